@@ -1,0 +1,144 @@
+/*
+ * m3scan.h -- C ABI of the Mamba-3 selective state-space scan on MI355X (gfx950).
+ *
+ * The operation ("Mamba-3: Improved Sequence Modeling using State Space
+ * Principles", intuitivepapers.ai):
+ *   For every batch b and head h (with group g = h * G / H of the shared B, C)
+ *   and token t, with a = exp(A_log[h]):
+ *     alpha = exp(-dt a),  beta = alpha dt (1 - lam),  gamma = lam dt
+ *         -- section "How the exponential-trapezoidal update works"
+ *     phi_i <- phi_i + dt theta_i            (i < npairs)
+ *     Bt = rot(B[g] + B_bias[h], phi),  Ct = rot(C[g] + C_bias[h], phi)
+ *         -- section "Computing the rotation as a data-dependent RoPE";
+ *            rot turns each adjacent pair (2i, 2i+1), i < npairs,
+ *            counter-clockwise by phi_i; dims >= 2 npairs are not turned
+ *     h <- alpha h + beta X_prev^T Bt_prev + gamma X^T Bt
+ *         -- h is P x N; X is R x P and Bt is R x N, so X^T Bt is the rank-R
+ *            write of section "MIMO: a rank-4 state update for the same state
+ *            size"
+ *     y_r = h Ct_r  (r < R),     (Bt_prev, X_prev) <- (Bt, X)
+ *   m3_scan_fwd evaluates this over a whole sequence in the chunked form
+ *   (section "The trapezoid term as a two-tap filter": the masked product
+ *   (L o C B^T) X inside a chunk, states carried between chunks, as in
+ *   "Diagonal Equivalence in State Space Models ..." (paperpeel.com),
+ *   section 2.4); m3_decode_step performs one token with the carry updated
+ *   in place (the decode listing of the RoPE section).
+ *
+ * Conventions
+ *   - All tensors are contiguous, row-major, in device memory (HBM) unless
+ *     stated.  Shapes below use b = batch, L = seqlen, H = nheads,
+ *     G = ngroups, P = headdim, N = dstate, R = rank, np = npairs.
+ *   - "io" tensors (x, B, C, y, B_prev, x_prev) are float32 or bfloat16 per
+ *     m3_desc.io_dtype; the state h is float32 or bfloat16 per
+ *     m3_desc.state_dtype; dt, lam, theta, A_log, biases and phi are float32.
+ *   - Every tensor base must be 16-byte aligned (128-bit vector access).
+ *   - The caller owns all memory.  The library never allocates, frees or
+ *     synchronises; work is enqueued on `stream` and runs asynchronously.
+ *   - Errors are returned as m3_status; nothing is launched when a call
+ *     returns an error found during argument checking.
+ *   - No mutable global state: calls are thread-safe.  Calls whose output
+ *     buffers overlap must not run concurrently.
+ */
+#ifndef M3SCAN_H
+#define M3SCAN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HIP's stream handle type (hipStream_t is `struct ihipStream_t*`);
+ * NULL selects the default stream. */
+struct ihipStream_t;
+typedef struct ihipStream_t* m3_stream_t;
+
+typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;
+
+typedef enum {
+    M3_OK = 0,
+    M3_ERR_INVALID_ARG = 1,   /* NULL pointer, bad shape, H % G != 0, npairs > N/2, small workspace, aliasing */
+    M3_ERR_UNSUPPORTED = 2,   /* valid but not implemented (shape or dtype out of the supported range) */
+    M3_ERR_ALIGNMENT = 3,     /* a tensor base is not 16-byte aligned */
+    M3_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} m3_status;
+
+/* Problem description.  All fields are logical sizes. */
+typedef struct {
+    int batch;        /* b >= 1 */
+    int seqlen;       /* L >= 0 tokens (m3_scan_fwd); ignored by m3_decode_step */
+    int nheads;       /* H >= 1 */
+    int ngroups;      /* G >= 1, H % G == 0; head h reads B, C group h * G / H */
+    int headdim;      /* P, 1..256 */
+    int dstate;       /* N, even, 2..256 */
+    int rank;         /* R, 1..8 */
+    int npairs;       /* rotating pairs, 0 <= npairs <= N/2 (0 = no rotation) */
+    int chunk;        /* Q: chunk length of the chunked scan, 1..256 (m3_scan_fwd only) */
+    m3_dtype io_dtype;     /* x, B, C, y, B_prev, x_prev */
+    m3_dtype state_dtype;  /* h */
+    int nsegments;    /* m3_scan_fwd schedule: 0 = library's choice; k > 0 asks for
+                         k sequence segments per (batch, head) stream, evaluated in
+                         parallel from zero-entry summaries (clamped to the number
+                         of chunks).  The result does not depend on it beyond
+                         rounding.  Ignored by m3_decode_step. */
+} m3_desc;
+
+/* The recurrence carry of section "Computing the rotation as a
+ * data-dependent RoPE" (decode listing: h, phi, B_prev, x_prev), as device
+ * pointers.  h is kept in the rotated frame (the frame in which B and C are
+ * turned rather than the state). */
+typedef struct {
+    void*  h;        /* [b, H, P, N]   state_dtype                              */
+    float* phi;      /* [b, H, np]     float32 accumulated angles, in [0, 2 pi)  */
+    void*  B_prev;   /* [b, H, R, N]   io_dtype: previous token's B, biased and turned */
+    void*  x_prev;   /* [b, H, R, P]   io_dtype: previous token's x             */
+} m3_carry;
+
+/* Bytes of device workspace m3_scan_fwd needs for *d (0 if none).
+ * Returns M3_ERR_INVALID_ARG for a NULL argument or an invalid descriptor. */
+m3_status m3_scan_workspace_size(const m3_desc* d, size_t* bytes);
+
+/* Chunked scan over a whole sequence.
+ *   x      [b, L, H, R, P] io          B, C [b, L, G, R, N] io
+ *   dt     [b, L, H] f32 (> 0, after softplus)
+ *   lam    [b, L, H] f32 (in [0, 1], after sigmoid)
+ *   theta  [b, L, H, np] f32 angular rate (each token adds dt * theta); NULL iff np == 0
+ *   A_log  [H] f32; the decay rate is A = -exp(A_log)
+ *   B_bias, C_bias [H, R, N] f32, or NULL for no bias (added before the turn)
+ *   init   carry at t = -1, or NULL for an all-zero carry; its phi may be NULL
+ *          when np == 0
+ *   y      [b, L, H, R, P] io (output; must not overlap any input)
+ *   final_ carry after the last token, or NULL; must not overlap init
+ *   workspace: device buffer of at least m3_scan_workspace_size(d) bytes
+ *          (may be NULL when that size is 0); its contents on entry do not
+ *          matter.
+ * With L == 0 nothing is launched except copying init to final_ (zeros if
+ * init is NULL). */
+m3_status m3_scan_fwd(const m3_desc* d,
+                      const void* x, const void* B, const void* C,
+                      const float* dt, const float* lam, const float* theta,
+                      const float* A_log, const float* B_bias, const float* C_bias,
+                      const m3_carry* init, void* y, const m3_carry* final_,
+                      void* workspace, size_t workspace_bytes, m3_stream_t stream);
+
+/* One token for every (batch, head), the carry updated in place.
+ *   x [b, H, R, P] io;  B, C [b, G, R, N] io;  dt, lam [b, H] f32;
+ *   theta [b, H, np] f32 (NULL iff np == 0); A_log [H]; B_bias, C_bias [H, R, N] or NULL
+ *   carry  in/out (all four pointers required; phi may be NULL iff np == 0)
+ *   y      [b, H, R, P] io (must not overlap inputs or the carry) */
+m3_status m3_decode_step(const m3_desc* d,
+                         const void* x, const void* B, const void* C,
+                         const float* dt, const float* lam, const float* theta,
+                         const float* A_log, const float* B_bias, const float* C_bias,
+                         const m3_carry* carry, void* y, m3_stream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* m3_status_string(m3_status s);
+
+/* Library version, (major << 16) | (minor << 8) | patch. */
+int m3_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* M3SCAN_H */

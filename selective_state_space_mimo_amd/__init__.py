@@ -1,0 +1,185 @@
+"""Mamba-3 selective state-space scan for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``include/m3scan.h`` (``libm3scan.so``,
+built in-tree by ``selective_state_space_mimo_amd.build``).  It only marshals
+arguments: every step of the scan and of the decode step runs in the HIP
+kernels of the library.  PyTorch supplies device memory and the current
+stream.  There is no fallback: without the built library this package does
+not import.
+
+    y, final = scan_fwd(x, B, C, dt, lam, theta, A_log, B_bias, C_bias,
+                        init=None, chunk=64)
+    y = decode_step(x, B, C, dt, lam, theta, A_log, B_bias, C_bias, carry)
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = ["scan_fwd", "decode_step", "scan_workspace_size", "new_carry", "M3Error",
+           "LIB_PATH", "lib", "Desc", "Carry", "M3_F32", "M3_BF16"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libm3scan.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libm3scan.so is not built: run __graft_entry__.build() "
+                      "(or python -m selective_state_space_mimo_amd.build)")
+
+M3_F32, M3_BF16 = 0, 1
+_STATUS = {0: "M3_OK", 1: "M3_ERR_INVALID_ARG", 2: "M3_ERR_UNSUPPORTED", 3: "M3_ERR_ALIGNMENT", 4: "M3_ERR_HIP"}
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int), ("seqlen", ctypes.c_int), ("nheads", ctypes.c_int),
+                ("ngroups", ctypes.c_int), ("headdim", ctypes.c_int), ("dstate", ctypes.c_int),
+                ("rank", ctypes.c_int), ("npairs", ctypes.c_int), ("chunk", ctypes.c_int),
+                ("io_dtype", ctypes.c_int), ("state_dtype", ctypes.c_int), ("nsegments", ctypes.c_int)]
+
+
+class Carry(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_void_p), ("phi", ctypes.c_void_p),
+                ("B_prev", ctypes.c_void_p), ("x_prev", ctypes.c_void_p)]
+
+
+lib = ctypes.CDLL(LIB_PATH)
+_vp, _sz = ctypes.c_void_p, ctypes.c_size_t
+lib.m3_scan_workspace_size.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(_sz)]
+lib.m3_scan_workspace_size.restype = ctypes.c_int
+lib.m3_scan_fwd.argtypes = [ctypes.POINTER(Desc)] + [_vp] * 9 + [ctypes.POINTER(Carry), _vp,
+                                                               ctypes.POINTER(Carry), _vp, _sz, _vp]
+lib.m3_scan_fwd.restype = ctypes.c_int
+lib.m3_decode_step.argtypes = [ctypes.POINTER(Desc)] + [_vp] * 9 + [ctypes.POINTER(Carry), _vp, _vp]
+lib.m3_decode_step.restype = ctypes.c_int
+lib.m3_status_string.argtypes = [ctypes.c_int]
+lib.m3_status_string.restype = ctypes.c_char_p
+lib.m3_version.restype = ctypes.c_int
+
+
+class M3Error(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = lib.m3_status_string(status).decode()
+        super().__init__("%s: %s (%s)" % (where, _STATUS.get(status, status), msg))
+
+
+def _check(st, where):
+    if st != 0:
+        raise M3Error(st, where)
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return M3_BF16
+    if t.dtype == torch.float32:
+        return M3_F32
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+def _ptr(t, dev, dtype=None, name=""):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != dev:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, dev))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t.data_ptr()
+
+
+def _stream(dev):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _carry(c, dev, io, st_dtype):
+    if c is None:
+        return None
+    return Carry(_ptr(c["h"], dev, st_dtype, "h"), _ptr(c.get("phi"), dev, torch.float32, "phi"),
+                 _ptr(c["B_prev"], dev, io, "B_prev"), _ptr(c["x_prev"], dev, io, "x_prev"))
+
+
+def make_desc(x, B, theta, *, chunk=64, state_dtype=None, nsegments=0, decode=False):
+    if decode:
+        b, H, R, P = x.shape
+        G, N = B.shape[1], B.shape[3]
+        L = 1
+    else:
+        b, L, H, R, P = x.shape
+        G, N = B.shape[2], B.shape[4]
+    npairs = 0 if theta is None else theta.shape[-1]
+    sd = _dt(x) if state_dtype is None else (M3_BF16 if state_dtype == torch.bfloat16 else M3_F32)
+    return Desc(b, L, H, G, P, N, R, npairs, chunk, _dt(x), sd, nsegments)
+
+
+def new_carry(batch, nheads, headdim, dstate, rank, npairs, io_dtype, state_dtype, device):
+    """An all-zero carry dict (h, phi, B_prev, x_prev) on ``device``."""
+    z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)  # noqa: E731
+    return {"h": z((batch, nheads, headdim, dstate), state_dtype),
+            "phi": z((batch, nheads, max(npairs, 0)), torch.float32),
+            "B_prev": z((batch, nheads, rank, dstate), io_dtype),
+            "x_prev": z((batch, nheads, rank, headdim), io_dtype)}
+
+
+def scan_workspace_size(desc):
+    n = _sz(0)
+    _check(lib.m3_scan_workspace_size(ctypes.byref(desc), ctypes.byref(n)), "m3_scan_workspace_size")
+    return n.value
+
+
+def scan_fwd(x, B, C, dt, lam, theta, A_log, B_bias=None, C_bias=None, init=None, *, chunk=64,
+             state_dtype=torch.float32, nsegments=0, y=None, final=True, workspace=None):
+    """Chunked scan (``m3_scan_fwd``).
+
+    x [b,L,H,R,P], B/C [b,L,G,R,N] (bf16 or f32, same dtype); dt, lam [b,L,H],
+    theta [b,L,H,np] or None, A_log [H], biases [H,R,N] or None (all f32).
+    init: None or dict(h [b,H,P,N] state_dtype, phi [b,H,np] f32, B_prev
+    [b,H,R,N], x_prev [b,H,R,P]).  final: True to allocate and return the final
+    carry, a dict to write into, or False/None to skip it.
+    Returns (y, final_carry_or_None).
+    """
+    dev = x.device
+    io = x.dtype
+    desc = make_desc(x, B, theta, chunk=chunk, state_dtype=state_dtype, nsegments=nsegments)
+    b, L, H, R, P = x.shape
+    N = B.shape[4]
+    if y is None:
+        y = torch.empty_like(x)
+    fin = None
+    if final is True:
+        fin = new_carry(b, H, P, N, R, desc.npairs, io, state_dtype, dev)
+    elif isinstance(final, dict):
+        fin = final
+    ws_bytes = scan_workspace_size(desc)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ci, cf = _carry(init, dev, io, state_dtype), _carry(fin, dev, io, state_dtype)
+    st = lib.m3_scan_fwd(ctypes.byref(desc), _ptr(x, dev, io, "x"), _ptr(B, dev, io, "B"), _ptr(C, dev, io, "C"),
+                         _ptr(dt, dev, torch.float32, "dt"), _ptr(lam, dev, torch.float32, "lam"),
+                         _ptr(theta, dev, torch.float32, "theta"), _ptr(A_log, dev, torch.float32, "A_log"),
+                         _ptr(B_bias, dev, torch.float32, "B_bias"), _ptr(C_bias, dev, torch.float32, "C_bias"),
+                         ctypes.byref(ci) if ci is not None else None, _ptr(y, dev, io, "y"),
+                         ctypes.byref(cf) if cf is not None else None,
+                         _ptr(workspace, dev, None, "workspace") if ws_bytes else None, ws_bytes, _stream(dev))
+    _check(st, "m3_scan_fwd")
+    return y, fin
+
+
+def decode_step(x, B, C, dt, lam, theta, A_log, B_bias, C_bias, carry, *, y=None):
+    """One decode step (``m3_decode_step``); ``carry`` (dict) is updated in place.
+
+    x [b,H,R,P], B/C [b,G,R,N]; dt, lam [b,H]; theta [b,H,np] or None.
+    Returns y [b,H,R,P]."""
+    dev = x.device
+    io = x.dtype
+    desc = make_desc(x, B, theta, state_dtype=carry["h"].dtype, decode=True)
+    if y is None:
+        y = torch.empty_like(x)
+    c = _carry(carry, dev, io, carry["h"].dtype)
+    st = lib.m3_decode_step(ctypes.byref(desc), _ptr(x, dev, io, "x"), _ptr(B, dev, io, "B"), _ptr(C, dev, io, "C"),
+                            _ptr(dt, dev, torch.float32, "dt"), _ptr(lam, dev, torch.float32, "lam"),
+                            _ptr(theta, dev, torch.float32, "theta"), _ptr(A_log, dev, torch.float32, "A_log"),
+                            _ptr(B_bias, dev, torch.float32, "B_bias"), _ptr(C_bias, dev, torch.float32, "C_bias"),
+                            ctypes.byref(c), _ptr(y, dev, io, "y"), _stream(dev))
+    _check(st, "m3_decode_step")
+    return y

@@ -1,0 +1,270 @@
+// Host side of the C ABI declared in include/m3scan.h: argument checking,
+// schedule choice and kernel dispatch.  Every check runs before the first
+// HIP call, so a call that returns an argument error has launched nothing.
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/m3scan.h"
+#include "m3_internal.h"
+
+using namespace m3;
+
+namespace {
+
+constexpr uintptr_t kAlign = 16;
+
+bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) % kAlign) != 0; }
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+Range rng(const void* p, size_t bytes) {
+    uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return {a, a + bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+size_t esize(m3_dtype t) { return t == M3_BF16 ? 2 : 4; }
+
+m3_status check_desc(const m3_desc* d, bool scan) {
+    if (!d) return M3_ERR_INVALID_ARG;
+    if (d->batch < 1 || d->nheads < 1 || d->ngroups < 1 || d->nheads % d->ngroups) return M3_ERR_INVALID_ARG;
+    if (d->headdim < 1 || d->dstate < 2 || (d->dstate & 1) || d->rank < 1) return M3_ERR_INVALID_ARG;
+    if (d->npairs < 0 || 2 * d->npairs > d->dstate) return M3_ERR_INVALID_ARG;
+    if ((d->io_dtype != M3_F32 && d->io_dtype != M3_BF16) ||
+        (d->state_dtype != M3_F32 && d->state_dtype != M3_BF16))
+        return M3_ERR_INVALID_ARG;
+    if (scan && (d->seqlen < 0 || d->chunk < 1 || d->nsegments < 0)) return M3_ERR_INVALID_ARG;
+    if (d->headdim > 256 || d->dstate > 256 || d->rank > 8) return M3_ERR_UNSUPPORTED;
+    if (scan && d->chunk > 256) return M3_ERR_UNSUPPORTED;
+    return M3_OK;
+}
+
+// Tensor sizes (bytes) of one call.
+struct Sizes {
+    size_t x, bc, tok, theta, alog, bias, h, phi, bp, xp;
+};
+Sizes sizes(const m3_desc* d, long long L) {
+    const size_t b = d->batch, H = d->nheads, G = d->ngroups, P = d->headdim, N = d->dstate, R = d->rank,
+                 np = d->npairs, io = esize(d->io_dtype), st = esize(d->state_dtype);
+    Sizes s;
+    s.x = b * L * H * R * P * io;
+    s.bc = b * L * G * R * N * io;
+    s.tok = b * L * H * 4;
+    s.theta = b * L * H * np * 4;
+    s.alog = H * 4;
+    s.bias = H * R * N * 4;
+    s.h = b * H * P * N * st;
+    s.phi = b * H * np * 4;
+    s.bp = b * H * R * N * io;
+    s.xp = b * H * R * P * io;
+    return s;
+}
+
+m3_status check_carry(const m3_carry* c, const m3_desc* d) {
+    if (!c->h || !c->B_prev || !c->x_prev) return M3_ERR_INVALID_ARG;
+    if (d->npairs > 0 && !c->phi) return M3_ERR_INVALID_ARG;
+    if (misaligned(c->h) || misaligned(c->phi) || misaligned(c->B_prev) || misaligned(c->x_prev))
+        return M3_ERR_ALIGNMENT;
+    return M3_OK;
+}
+
+void carry_ranges(const m3_carry* c, const Sizes& s, Range out[4]) {
+    out[0] = rng(c->h, s.h);
+    out[1] = rng(c->phi, c->phi ? s.phi : 0);
+    out[2] = rng(c->B_prev, s.bp);
+    out[3] = rng(c->x_prev, s.xp);
+}
+
+// Schedule: number of sequence segments per (batch, head) stream and their
+// length in tokens (a multiple of the chunk).
+void choose_segments(const m3_desc* d, int* nseg, int* seglen) {
+    const int L = d->seqlen, Q = d->chunk;
+    const int nchunks = (L + Q - 1) / Q;
+    int k = d->nsegments;
+    if (k == 0) {
+        const long long streams = (long long)d->batch * d->nheads;
+        // Fill the 256 compute units with >= ~1024 workgroups when the
+        // (batch, head) streams alone are too few.
+        k = streams >= 512 ? 1 : (int)((1024 + streams - 1) / streams);
+    }
+    k = std::max(1, std::min(k, std::max(1, nchunks)));
+    const int cps = (nchunks + k - 1) / k;       // chunks per segment
+    *seglen = cps * Q;
+    *nseg = std::max(1, (L + *seglen - 1) / *seglen);
+}
+
+ScanArgs make_scan_args(const m3_desc* d, const void* x, const void* B, const void* C, const float* dt,
+                        const float* lam, const float* theta, const float* A_log, const float* Bb,
+                        const float* Cb, const m3_carry* init, void* y, const m3_carry* fin) {
+    ScanArgs a{};
+    a.b = d->batch; a.L = d->seqlen; a.H = d->nheads; a.G = d->ngroups; a.P = d->headdim;
+    a.N = d->dstate; a.R = d->rank; a.np = d->npairs; a.Q = d->chunk;
+    a.io_bf16 = d->io_dtype == M3_BF16; a.st_bf16 = d->state_dtype == M3_BF16;
+    a.x = x; a.B = B; a.C = C; a.dt = dt; a.lam = lam; a.theta = d->npairs ? theta : nullptr;
+    a.A_log = A_log; a.Bb = Bb; a.Cb = Cb;
+    if (init) { a.h0 = init->h; a.phi0 = d->npairs ? init->phi : nullptr; a.Bp0 = init->B_prev; a.xp0 = init->x_prev; }
+    a.y = y;
+    if (fin) { a.h1 = fin->h; a.phi1 = d->npairs ? fin->phi : nullptr; a.Bp1 = fin->B_prev; a.xp1 = fin->x_prev; }
+    choose_segments(d, &a.nseg, &a.seglen);
+    return a;
+}
+
+// ---- L == 0: final carry = initial carry (zeros without one) -----------------------
+__global__ void copy_or_zero_kernel(const uint16_t* src, uint16_t* dst, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        dst[i] = src ? src[i] : (uint16_t)0;
+}
+hipError_t copy_or_zero(const void* src, void* dst, size_t bytes, hipStream_t s) {
+    if (!dst || bytes == 0) return hipSuccess;
+    const size_t n = bytes / 2;   // every carry tensor holds whole 2-byte units
+    const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(copy_or_zero_kernel, dim3(blocks), dim3(256), 0, s, (const uint16_t*)src, (uint16_t*)dst, n);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* m3_status_string(m3_status s) {
+    switch (s) {
+        case M3_OK: return "ok";
+        case M3_ERR_INVALID_ARG: return "invalid argument";
+        case M3_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case M3_ERR_ALIGNMENT: return "tensor base not 16-byte aligned";
+        case M3_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int m3_version(void) { return (0 << 16) | (1 << 8) | 0; }
+
+m3_status m3_scan_workspace_size(const m3_desc* d, size_t* bytes) {
+    if (!bytes) return M3_ERR_INVALID_ARG;
+    m3_status st = check_desc(d, true);
+    if (st != M3_OK) return st;
+    *bytes = 0;
+    if (d->seqlen == 0) return M3_OK;
+    ScanArgs a = make_scan_args(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, nullptr, nullptr);
+    if (a.io_bf16 && scan_mfma_supported(a)) *bytes = scan_mfma_workspace_bytes(a);
+    return M3_OK;
+}
+
+m3_status m3_scan_fwd(const m3_desc* d, const void* x, const void* B, const void* C, const float* dt,
+                      const float* lam, const float* theta, const float* A_log, const float* B_bias,
+                      const float* C_bias, const m3_carry* init, void* y, const m3_carry* final_,
+                      void* workspace, size_t workspace_bytes, m3_stream_t stream) {
+    m3_status st = check_desc(d, true);
+    if (st != M3_OK) return st;
+    const int L = d->seqlen;
+    if (init && (st = check_carry(init, d)) != M3_OK) return st;
+    if (final_ && (st = check_carry(final_, d)) != M3_OK) return st;
+    const Sizes s = sizes(d, L);
+    Range ri[4], rf[4];
+    if (init) carry_ranges(init, s, ri);
+    if (final_) {
+        carry_ranges(final_, s, rf);
+        for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 4; ++j)
+                if (init && overlap(rf[i], ri[j])) return M3_ERR_INVALID_ARG;
+        for (int i = 0; i < 4; ++i)
+            for (int j = i + 1; j < 4; ++j)
+                if (overlap(rf[i], rf[j])) return M3_ERR_INVALID_ARG;
+    }
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (L == 0) {
+        if (!final_) return M3_OK;
+        const Sizes s1 = sizes(d, 0);
+        hipError_t e = copy_or_zero(init ? init->h : nullptr, final_->h, s1.h, hs);
+        if (e == hipSuccess && d->npairs) e = copy_or_zero(init ? init->phi : nullptr, final_->phi, s1.phi, hs);
+        if (e == hipSuccess) e = copy_or_zero(init ? init->B_prev : nullptr, final_->B_prev, s1.bp, hs);
+        if (e == hipSuccess) e = copy_or_zero(init ? init->x_prev : nullptr, final_->x_prev, s1.xp, hs);
+        return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+    }
+    if (!x || !B || !C || !dt || !lam || !A_log || !y) return M3_ERR_INVALID_ARG;
+    if (d->npairs > 0 && !theta) return M3_ERR_INVALID_ARG;
+    const void* ptrs[] = {x, B, C, dt, lam, d->npairs ? theta : nullptr, A_log, B_bias, C_bias, y, workspace};
+    for (const void* p : ptrs)
+        if (misaligned(p)) return M3_ERR_ALIGNMENT;
+    const Range ry = rng(y, s.x);
+    const Range ins[] = {rng(x, s.x), rng(B, s.bc), rng(C, s.bc), rng(dt, s.tok), rng(lam, s.tok),
+                         rng(d->npairs ? theta : nullptr, d->npairs ? s.theta : 0), rng(A_log, s.alog),
+                         rng(B_bias, B_bias ? s.bias : 0), rng(C_bias, C_bias ? s.bias : 0)};
+    for (const Range& r : ins)
+        if (overlap(ry, r)) return M3_ERR_INVALID_ARG;
+    for (int i = 0; i < 4; ++i) {
+        if (init && overlap(ry, ri[i])) return M3_ERR_INVALID_ARG;
+        if (final_ && overlap(ry, rf[i])) return M3_ERR_INVALID_ARG;
+    }
+
+    ScanArgs a = make_scan_args(d, x, B, C, dt, lam, theta, A_log, B_bias, C_bias, init, y, final_);
+    hipError_t e;
+    if (a.io_bf16 && scan_mfma_supported(a)) {
+        const size_t need = scan_mfma_workspace_bytes(a);
+        if (need > 0) {
+            if (!workspace || workspace_bytes < need) return M3_ERR_INVALID_ARG;
+            const Range rw = rng(workspace, need);
+            for (const Range& r : ins)
+                if (overlap(rw, r)) return M3_ERR_INVALID_ARG;
+            if (overlap(rw, ry)) return M3_ERR_INVALID_ARG;
+        }
+        a.ws = static_cast<float*>(workspace);
+        e = launch_scan_mfma(a, hs);
+    } else {
+        if (scan_generic_chunk(a.P, a.N, a.R, a.np, a.Q) < 1) return M3_ERR_UNSUPPORTED;
+        e = launch_scan_generic(a, hs);
+    }
+    return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
+m3_status m3_decode_step(const m3_desc* d, const void* x, const void* B, const void* C, const float* dt,
+                         const float* lam, const float* theta, const float* A_log, const float* B_bias,
+                         const float* C_bias, const m3_carry* carry, void* y, m3_stream_t stream) {
+    m3_status st = check_desc(d, false);
+    if (st != M3_OK) return st;
+    if (!carry || !x || !B || !C || !dt || !lam || !A_log || !y) return M3_ERR_INVALID_ARG;
+    if (d->npairs > 0 && !theta) return M3_ERR_INVALID_ARG;
+    if ((st = check_carry(carry, d)) != M3_OK) return st;
+    const void* ptrs[] = {x, B, C, dt, lam, d->npairs ? theta : nullptr, A_log, B_bias, C_bias, y};
+    for (const void* p : ptrs)
+        if (misaligned(p)) return M3_ERR_ALIGNMENT;
+    const Sizes s = sizes(d, 1);
+    Range rc[4];
+    carry_ranges(carry, s, rc);
+    const Range ry = rng(y, s.x);
+    const Range ins[] = {rng(x, s.x), rng(B, s.bc), rng(C, s.bc), rng(dt, s.tok), rng(lam, s.tok),
+                         rng(d->npairs ? theta : nullptr, d->npairs ? s.theta : 0), rng(A_log, s.alog),
+                         rng(B_bias, B_bias ? s.bias : 0), rng(C_bias, C_bias ? s.bias : 0)};
+    for (const Range& r : ins) {
+        if (overlap(ry, r)) return M3_ERR_INVALID_ARG;
+        for (int i = 0; i < 4; ++i)
+            if (overlap(rc[i], r)) return M3_ERR_INVALID_ARG;
+    }
+    for (int i = 0; i < 4; ++i) {
+        if (overlap(ry, rc[i])) return M3_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(rc[i], rc[j])) return M3_ERR_INVALID_ARG;
+    }
+
+    DecodeArgs a{};
+    a.b = d->batch; a.H = d->nheads; a.G = d->ngroups; a.P = d->headdim; a.N = d->dstate; a.R = d->rank;
+    a.np = d->npairs; a.io_bf16 = d->io_dtype == M3_BF16; a.st_bf16 = d->state_dtype == M3_BF16;
+    a.x = x; a.B = B; a.C = C; a.dt = dt; a.lam = lam; a.theta = d->npairs ? theta : nullptr; a.A_log = A_log;
+    a.Bb = B_bias; a.Cb = C_bias;
+    a.h = carry->h; a.phi = d->npairs ? carry->phi : nullptr; a.Bp = carry->B_prev; a.xp = carry->x_prev;
+    a.y = y;
+    hipError_t e;
+    if (decode_fast_supported(a)) {
+        e = launch_decode_fast(a, reinterpret_cast<hipStream_t>(stream));
+    } else {
+        if (scan_generic_chunk(a.P, a.N, a.R, a.np, 1) < 1) return M3_ERR_UNSUPPORTED;
+        e = launch_decode_generic(a, reinterpret_cast<hipStream_t>(stream));
+    }
+    return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
+}  // extern "C"

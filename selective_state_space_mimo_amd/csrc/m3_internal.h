@@ -1,0 +1,78 @@
+// Internal declarations shared by the host entry points and the kernels of
+// libm3scan.  Not part of the public ABI (include/m3scan.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m3 {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr float kTwoPi = 6.283185307179586f;
+
+// Everything a scan launch needs; passed by value to the kernels.
+struct ScanArgs {
+    int b, L, H, G, P, N, R, np, Q;
+    int io_bf16, st_bf16;
+    const void* x; const void* B; const void* C;
+    const float* dt; const float* lam; const float* theta; const float* A_log;
+    const float* Bb; const float* Cb;
+    // initial carry (each may be null = zero)
+    const void* h0; const float* phi0; const void* Bp0; const void* xp0;
+    void* y;
+    // final carry (each may be null = not written)
+    void* h1; float* phi1; void* Bp1; void* xp1;
+    // segmented schedule: nseg segments of seglen tokens (seglen % Q == 0)
+    int nseg, seglen;
+    float* ws;   // workspace (segmented schedule only)
+};
+
+// Decode-step arguments (one token, carry in place).
+struct DecodeArgs {
+    int b, H, G, P, N, R, np;
+    int io_bf16, st_bf16;
+    const void* x; const void* B; const void* C;
+    const float* dt; const float* lam; const float* theta; const float* A_log;
+    const float* Bb; const float* Cb;
+    void* h; float* phi; void* Bp; void* xp;
+    void* y;
+};
+
+// ---- host-side launchers (return hipSuccess or the launch error) ----------
+hipError_t launch_scan_generic(const ScanArgs& a, hipStream_t s);
+size_t scan_generic_lds_bytes(int P, int N, int R, int np, int qg);
+int scan_generic_chunk(int P, int N, int R, int np, int Q);
+
+bool scan_mfma_supported(const ScanArgs& a);
+hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t s);
+size_t scan_mfma_workspace_bytes(const ScanArgs& a);
+
+bool decode_fast_supported(const DecodeArgs& a);
+hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t s);
+
+// ---- device helpers --------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t u) {
+    return __uint_as_float(((uint32_t)u) << 16);
+}
+__device__ __forceinline__ float ld_io(const void* p, size_t i, int is_bf16) {
+    if (is_bf16) return bf16_bits_to_f32(((const uint16_t*)p)[i]);
+    return ((const float*)p)[i];
+}
+__device__ __forceinline__ void st_io(void* p, size_t i, float v, int is_bf16) {
+    if (is_bf16) ((bf16*)p)[i] = (bf16)v;           // round to nearest even
+    else ((float*)p)[i] = v;
+}
+// Reduce an angle into [0, 2 pi).
+__device__ __forceinline__ float wrap_2pi(float v) {
+    float w = v - kTwoPi * floorf(v * (1.0f / kTwoPi));
+    return (w >= kTwoPi || w < 0.f) ? 0.f : w;
+}
+
+}  // namespace m3

@@ -1,0 +1,103 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol its header
+declares, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "m3scan.h")
+LIB = os.path.join(ROOT, "selective_state_space_mimo_amd", "libm3scan.so")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(m3_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("m3_scan_fwd", "m3_decode_step", "m3_scan_workspace_size", "m3_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    assert os.path.exists(LIB), "build the library first (__graft_entry__.build())"
+    lib = ctypes.CDLL(LIB)
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_header_compiles_as_c():
+    import shutil
+    import subprocess
+    import tempfile
+    if not shutil.which("gcc"):
+        pytest.skip("no gcc")
+    with tempfile.TemporaryDirectory() as td:
+        c = os.path.join(td, "t.c")
+        open(c, "w").write('#include "m3scan.h"\nint main(void){ m3_desc d; (void)d; return 0; }\n')
+        subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                               "-c", c, "-o", os.path.join(td, "t.o")])
+
+
+@pytest.fixture(scope="module")
+def m3():
+    import selective_state_space_mimo_amd as m
+    return m
+
+
+def _desc(m3, **kw):
+    d = dict(batch=2, seqlen=8, nheads=4, ngroups=2, headdim=16, dstate=16, rank=2, npairs=2,
+             chunk=4, io_dtype=m3.M3_F32, state_dtype=m3.M3_F32, nsegments=0)
+    d.update(kw)
+    return m3.Desc(**d)
+
+
+FAKE = 0x7f0000000000   # never dereferenced: every call below fails argument checks first
+
+
+def _scan(m3, desc, **ptrs):
+    p = dict(x=FAKE, B=FAKE + 0x100000, C=FAKE + 0x200000, dt=FAKE + 0x300000, lam=FAKE + 0x400000,
+             theta=FAKE + 0x500000, A_log=FAKE + 0x600000, Bb=None, Cb=None, y=FAKE + 0x700000)
+    p.update(ptrs)
+    return m3.lib.m3_scan_fwd(ctypes.byref(desc), p["x"], p["B"], p["C"], p["dt"], p["lam"], p["theta"],
+                              p["A_log"], p["Bb"], p["Cb"], None, p["y"], None, None, 0, None)
+
+
+def test_status_strings(m3):
+    for s in range(5):
+        assert m3.lib.m3_status_string(s)
+    assert m3.lib.m3_version() > 0
+
+
+def test_invalid_descriptors(m3):
+    n = ctypes.c_size_t(0)
+    assert m3.lib.m3_scan_workspace_size(None, ctypes.byref(n)) == 1
+    bad = [dict(nheads=3, ngroups=2), dict(npairs=9), dict(dstate=15), dict(batch=0), dict(chunk=0),
+           dict(rank=0), dict(io_dtype=7), dict(seqlen=-1)]
+    for kw in bad:
+        assert m3.lib.m3_scan_workspace_size(ctypes.byref(_desc(m3, **kw)), ctypes.byref(n)) == 1, kw
+        assert _scan(m3, _desc(m3, **kw)) == 1, kw
+    assert m3.lib.m3_scan_workspace_size(ctypes.byref(_desc(m3, dstate=512)), ctypes.byref(n)) == 2
+    assert m3.lib.m3_scan_workspace_size(ctypes.byref(_desc(m3)), ctypes.byref(n)) == 0
+
+
+def test_null_misaligned_and_aliased_pointers(m3):
+    d = _desc(m3)
+    assert _scan(m3, d, x=None) == 1
+    assert _scan(m3, d, theta=None) == 1                 # npairs > 0 needs theta
+    assert _scan(m3, d, y=None) == 1
+    assert _scan(m3, d, dt=FAKE + 0x300004) == 3         # not 16-byte aligned
+    assert _scan(m3, d, y=FAKE + 0x10) == 1              # y overlaps x
+    desc = _desc(m3, seqlen=1)
+    c = m3.Carry(FAKE + 0x800000, FAKE + 0x900000, FAKE + 0xa00000, FAKE + 0xb00000)
+    assert m3.lib.m3_decode_step(ctypes.byref(desc), FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000,
+                                 FAKE + 0x400000, None, FAKE + 0x600000, None, None, ctypes.byref(c),
+                                 FAKE + 0x700000, None) == 1     # theta missing
+    c2 = m3.Carry(FAKE + 0x800000, FAKE + 0x900000, FAKE + 0x800010, FAKE + 0xb00000)   # B_prev inside h
+    assert m3.lib.m3_decode_step(ctypes.byref(desc), FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000,
+                                 FAKE + 0x400000, FAKE + 0x500000, FAKE + 0x600000, None, None, ctypes.byref(c2),
+                                 FAKE + 0x700000, None) == 1

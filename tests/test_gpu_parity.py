@@ -1,0 +1,176 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Tolerances (normwise relative L2 per tensor): 1e-4 for f32 I/O, 2e-2 for
+bf16 I/O, as the workload statement fixes.  Phases are compared through
+(cos, sin) with an absolute bound.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from m3inputs import CONFIGS, config_by_name, make_decode_inputs, make_scan_inputs, make_small_case
+from oracle import ref_cpu
+from tests._util import host, phase_err, pooled_signed, rel_l2, to_device
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def m3():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_mimo_amd as m
+    return m
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _tol(io):
+    return 1e-4 if io == "f32" else 2e-2
+
+
+def _run_scan(m3, d, cfg, chunk=None, nsegments=0):
+    dev = torch.device("cuda:0")
+    io = torch.float32 if cfg.io_dtype == "f32" else torch.bfloat16
+    sd = torch.float32 if cfg.state_dtype == "f32" else torch.bfloat16
+    t = to_device(d, io, sd, dev)
+    y, fin = m3.scan_fwd(t["x"], t["B"], t["C"], t["dt"], t["lam"], t["theta"], t["A_log"], t["B_bias"],
+                         t["C_bias"], t["init"], chunk=chunk or cfg.chunk, state_dtype=sd, nsegments=nsegments)
+    torch.cuda.synchronize()
+    return y, fin
+
+
+def _compare(y, fin, yr, fr, io, sel=None, what=""):
+    tol = _tol(io)
+    yg = host(y)
+    if sel is not None:
+        yg = np.stack([yg[bi, :, h] for bi, h in sel])
+    e = rel_l2(yg, yr)
+    bias = pooled_signed(yg, yr)
+    _say("  %s y rel-L2 %.3e  pooled-signed %.2e" % (what, e, bias))
+    assert e <= tol, "y rel-L2 %.3e > %.1e" % (e, tol)
+    assert abs(bias) <= tol / 4
+    if fin is None:
+        return
+    for k in ("h", "B_prev", "x_prev"):
+        g = host(fin[k])
+        if sel is not None:
+            g = np.stack([g[bi, h] for bi, h in sel])
+        ek = rel_l2(g, fr[k])
+        _say("  %s %s rel-L2 %.3e" % (what, k, ek))
+        assert ek <= tol, k
+    if fr["phi"].size:
+        g = host(fin["phi"])
+        if sel is not None:
+            g = np.stack([g[bi, h] for bi, h in sel])
+        assert phase_err(g, fr["phi"]) < 1e-3
+        assert g.min() >= 0.0 and g.max() < 2 * np.pi + 1e-6
+
+
+# -----------------------------------------------------------------------------
+# small feature sweep (oracle on every stream)
+# -----------------------------------------------------------------------------
+SWEEP = [
+    # io,   P,  N, R, np, G, Q, L,  bias, lam1, init
+    ("f32", 16, 16, 1, 4, 2, 16, 64, False, False, False),
+    ("f32", 16, 16, 2, 8, 1, 16, 37, True, False, True),
+    ("f32", 8, 12, 3, 0, 1, 5, 23, True, True, True),
+    ("f32", 64, 128, 4, 32, 1, 64, 70, True, False, True),
+    ("f32", 64, 128, 1, 0, 1, 64, 129, False, True, False),
+    ("bf16", 16, 16, 1, 4, 2, 16, 64, False, False, False),
+    ("bf16", 64, 128, 1, 0, 1, 64, 130, False, True, False),
+    ("bf16", 64, 128, 2, 32, 1, 32, 100, True, False, True),
+    ("bf16", 64, 128, 4, 32, 1, 64, 150, True, False, True),
+    ("bf16", 64, 128, 4, 64, 2, 16, 77, True, False, True),
+    ("bf16", 64, 128, 4, 0, 1, 128, 300, True, False, True),
+    ("bf16", 32, 64, 2, 8, 1, 32, 64, False, False, True),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=lambda c: "%s-P%d-N%d-R%d-np%d-G%d-Q%d-L%d" % c[:8])
+def test_scan_sweep(m3, case):
+    io, P, N, R, npairs, G, Q, L, bias, lam1, init = case
+    _say("scan sweep", case)
+    cfg, d = make_small_case(1000 + P + N + R + Q + L, batch=2, seqlen=L, nheads=4, ngroups=G, headdim=P,
+                             dstate=N, rank=R, npairs=npairs, chunk=Q, io_dtype=io, state_dtype="f32",
+                             bias=bias, lam_one=lam1, rms_bc=(io == "bf16"), init_full=init)
+    yr, fr = ref_cpu.scan(d)
+    y, fin = _run_scan(m3, d, cfg)
+    _compare(y, fin, yr, fr, io, what="sweep")
+
+
+def test_config1_tiny_siso_f32(m3):
+    cfg = config_by_name("tiny_siso_f32")
+    d = make_scan_inputs(cfg)
+    yr, fr = ref_cpu.scan(d)
+    y, fin = _run_scan(m3, d, cfg)
+    _compare(y, fin, yr, fr, cfg.io_dtype, what="config1")
+
+
+def test_scan_empty_sequence(m3):
+    """L = 0: nothing but the carry copy (zeros without an initial carry)."""
+    cfg, d = make_small_case(5, batch=2, seqlen=0, nheads=2, headdim=8, dstate=8, rank=2, npairs=2,
+                             init_full=True)
+    y, fin = _run_scan(m3, d, cfg)
+    assert y.numel() == 0
+    for k in ("h", "phi", "B_prev", "x_prev"):
+        np.testing.assert_array_equal(host(fin[k]), d["init"][k].astype(np.float64))
+    d["init"] = None
+    y, fin = _run_scan(m3, d, cfg)
+    for k in ("h", "phi", "B_prev", "x_prev"):
+        assert not host(fin[k]).any()
+
+
+def test_scan_deterministic(m3):
+    cfg, d = make_small_case(7, batch=2, seqlen=150, nheads=4, ngroups=1, headdim=64, dstate=128, rank=4,
+                             npairs=32, chunk=64, io_dtype="bf16", rms_bc=True, init_full=True)
+    y1, f1 = _run_scan(m3, d, cfg)
+    y2, f2 = _run_scan(m3, d, cfg)
+    assert torch.equal(y1, y2) and torch.equal(f1["h"], f2["h"])
+
+
+# -----------------------------------------------------------------------------
+# decode step
+# -----------------------------------------------------------------------------
+DECODE = [
+    # io,   state, P,  N,  R, np, G, steps
+    ("f32", "f32", 16, 16, 1, 4, 2, 5),
+    ("bf16", "bf16", 64, 128, 4, 32, 1, 12),
+    ("bf16", "bf16", 64, 128, 2, 16, 2, 6),
+    ("bf16", "bf16", 64, 128, 1, 0, 1, 6),
+    ("bf16", "f32", 64, 128, 4, 32, 1, 5),
+    ("bf16", "bf16", 32, 64, 4, 8, 1, 5),
+]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=lambda c: "%s-%s-P%d-N%d-R%d-np%d-G%d-S%d" % c)
+def test_decode_steps(m3, case):
+    """k decode steps through m3_decode_step equal the oracle's recurrence over
+    k tokens (carried state, phase, previous write)."""
+    io, sdt, P, N, R, npairs, G, steps = case
+    _say("decode", case)
+    cfg, _ = make_small_case(0, batch=3, seqlen=steps, nheads=4, ngroups=G, headdim=P, dstate=N, rank=R,
+                             npairs=npairs, io_dtype=io, state_dtype=sdt, bias=True, rms_bc=(io == "bf16"))
+    cfg = cfg.with_(init_state=True, init_full=True)
+    d = make_decode_inputs(cfg, steps, seed=77)
+    yr, fr = ref_cpu.scan(d)
+    dev = torch.device("cuda:0")
+    iot = torch.float32 if io == "f32" else torch.bfloat16
+    sdt_t = torch.float32 if sdt == "f32" else torch.bfloat16
+    t = to_device(d, iot, sdt_t, dev)
+    carry = {k: v.clone() for k, v in t["init"].items()}
+    ys = []
+    for s in range(steps):
+        ys.append(m3.decode_step(t["x"][:, s].contiguous(), t["B"][:, s].contiguous(), t["C"][:, s].contiguous(),
+                                 t["dt"][:, s].contiguous(), t["lam"][:, s].contiguous(),
+                                 None if t["theta"] is None else t["theta"][:, s].contiguous(),
+                                 t["A_log"], t["B_bias"], t["C_bias"], carry))
+    torch.cuda.synchronize()
+    y = torch.stack(ys, dim=1)
+    _compare(y, carry, yr, fr, io, what="decode")
