@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""Benchmark of the Mamba-3 scan hot path on one MI355X.
+
+Prints ONE JSON line.  ``value`` is the chunked scan's throughput in tokens/s
+on the MIMO prefill workload (batch 8, 64 heads, P=64, N=128, R=4, L=2048,
+chunk 64, bf16 I/O), timed over ``--steps`` calls after ``--warmup`` calls with
+HIP events on the stream the kernels run on, inputs resident in HBM.  The same
+line carries the decode step (batch 256, 64 heads, bf16 state, 1000 consecutive
+steps) as GB/s against the 8 TB/s HBM peak, the other scan workloads, a
+roofline object per kernel, and the CPU oracle timed on a bounded sample.
+
+Algorithmic work (what the method must do; overheads are not credited):
+  scan FLOP per head-token   R^2 (N + P)(Q + 1) + 4 R N P   (causal-trimmed chunked form)
+  scan bytes per head-token  4 R P (x in, y out) + 4 R N G / H (B, C) + 8 (dt, lam) + 4 np (theta)
+                             + per stream: final carry (state f32, phase, previous write)
+  decode bytes per head-step 4 P N (bf16 state read + write) + 2 R P (x) + 4 R N G / H (B, C)
+                             + 8 (dt, lam) + 4 np (theta) + 8 np (phase r/w) + 4 R N (B_prev r/w)
+                             + 4 R P (x_prev r/w) + 2 R P (y)            = 37,288 B at R=4
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workloads", default="scan3,decode4,scan2,scan5")
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--json-out", default=None)
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic accounting
+# ---------------------------------------------------------------------------
+def scan_flops_per_head_token(cfg):
+    R, N, P, Q = cfg.rank, cfg.dstate, cfg.headdim, cfg.chunk
+    return R * R * (N + P) * (Q + 1) + 4 * R * N * P
+
+
+def scan_bytes(cfg, with_final=True):
+    R, N, P, H, G, NP = cfg.rank, cfg.dstate, cfg.headdim, cfg.nheads, cfg.ngroups, cfg.npairs
+    io = 2 if cfg.io_dtype == "bf16" else 4
+    per_ht = 2 * io * R * P + 2 * io * R * N * G / H + 8 + 4 * NP
+    streams = cfg.batch * H
+    total = per_ht * streams * cfg.seqlen
+    if cfg.init_state:
+        total += streams * P * N * 4
+    if with_final:
+        total += streams * (P * N * 4 + 4 * NP + io * R * (N + P))
+    if cfg.bias:
+        total += 2 * H * R * N * 4
+    return total
+
+
+def decode_bytes_per_head_step(cfg):
+    R, N, P, H, G, NP = cfg.rank, cfg.dstate, cfg.headdim, cfg.nheads, cfg.ngroups, cfg.npairs
+    return 4 * P * N + 2 * R * P + 4 * R * N * G / H + 8 + 4 * NP + 8 * NP + 4 * R * N + 4 * R * P + 2 * R * P
+
+
+# ---------------------------------------------------------------------------
+# timing helpers
+# ---------------------------------------------------------------------------
+def time_calls(torch, fn, steps, warmup):
+    """Mean ms per call over `steps` calls after `warmup`, HIP events on the
+    current stream (the stream the library launches on)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def per_launch_ms(torch, fn, n):
+    """Mean ms of single calls, each bracketed by its own events (launch gaps excluded)."""
+    s = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record(s)
+        fn()
+        b.record(s)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+def run_scan(torch, m3, cfg, steps, warmup):
+    from m3inputs import make_scan_inputs
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    d = make_scan_inputs(cfg)
+    io = torch.bfloat16 if cfg.io_dtype == "bf16" else torch.float32
+
+    def T(a, dt):
+        return None if a is None else torch.from_numpy(a).to(dev).to(dt).contiguous()
+    x, B, C = T(d["x"], io), T(d["B"], io), T(d["C"], io)
+    dt, lam, th, Al = T(d["dt"], torch.float32), T(d["lam"], torch.float32), T(d["theta"], torch.float32), \
+        T(d["A_log"], torch.float32)
+    Bb, Cb = T(d["B_bias"], torch.float32), T(d["C_bias"], torch.float32)
+    init = None
+    if d["init"] is not None:
+        init = {"h": T(d["init"]["h"], torch.float32), "phi": T(d["init"]["phi"], torch.float32),
+                "B_prev": T(d["init"]["B_prev"], io), "x_prev": T(d["init"]["x_prev"], io)}
+    del d
+    log("[bench] %s inputs ready in %.1fs" % (cfg.name, time.time() - t0))
+    b, L, H, R, P = x.shape
+    fin = m3.new_carry(b, H, P, cfg.dstate, R, cfg.npairs, io, torch.float32, dev)
+    y = torch.empty_like(x)
+    desc = m3.make_desc(x, B, th, chunk=cfg.chunk, state_dtype=torch.float32)
+    ws_bytes = m3.scan_workspace_size(desc)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def call():
+        m3.scan_fwd(x, B, C, dt, lam, th, Al, Bb, Cb, init, chunk=cfg.chunk, y=y, final=fin, workspace=ws)
+    ms = time_calls(torch, call, steps, warmup)
+    ms_launch = per_launch_ms(torch, call, max(3, min(steps, 10)))
+    toks = b * L
+    flops = scan_flops_per_head_token(cfg) * b * L * H
+    nbytes = scan_bytes(cfg)
+    out = {"workload": cfg.name, "batch": b, "seqlen": L, "nheads": H, "headdim": P, "dstate": cfg.dstate,
+           "rank": R, "chunk": cfg.chunk, "npairs": cfg.npairs, "ngroups": cfg.ngroups,
+           "ms_per_call": ms, "ms_per_launch": ms_launch, "tokens_per_s": toks / (ms * 1e-3),
+           "algo_tflops": flops / (ms_launch * 1e-3) / 1e12, "algo_gbs": nbytes / (ms_launch * 1e-3) / 1e9,
+           "flop_per_call": flops, "bytes_per_call": nbytes, "workspace_bytes": ws_bytes}
+    out["mfma_frac"] = out["algo_tflops"] / PEAK_BF16_TFLOPS
+    out["hbm_frac"] = out["algo_gbs"] / PEAK_HBM_GBS
+    log("[bench] %s: %.3f ms/call, %.2f M tok/s, %.1f TFLOP/s (%.1f%% MFMA), %.0f GB/s (%.1f%% HBM)" % (
+        cfg.name, ms, out["tokens_per_s"] / 1e6, out["algo_tflops"], 100 * out["mfma_frac"], out["algo_gbs"],
+        100 * out["hbm_frac"]))
+    del x, B, C, dt, lam, th, y, fin, init, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def decode_inputs_device(torch, cfg, nsteps, dev, seed):
+    """Per-step decode inputs for `nsteps` steps, drawn on the device from a
+    seeded torch generator (value laws as m3inputs; bf16 RNE storage)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    b, H, G, R, P, N, NP = cfg.batch, cfg.nheads, cfg.ngroups, cfg.rank, cfg.headdim, cfg.dstate, cfg.npairs
+    f32 = torch.float32
+    x = torch.randn((nsteps, b, H, R, P), generator=g, device=dev, dtype=f32).to(torch.bfloat16)
+
+    def bc():
+        v = torch.randn((nsteps, b, G, R, N), generator=g, device=dev, dtype=f32)
+        v = v * torch.rsqrt(v.square().mean(-1, keepdim=True) + 1e-6)
+        return v.to(torch.bfloat16)
+    B, C = bc(), bc()
+    dt = torch.nn.functional.softplus(torch.randn((nsteps, b, H), generator=g, device=dev, dtype=f32) * 0.5 - 2.0)
+    lam = torch.sigmoid(torch.randn((nsteps, b, H), generator=g, device=dev, dtype=f32))
+    th = torch.rand((nsteps, b, H, NP), generator=g, device=dev, dtype=f32) * (np.pi / N)
+    A_log = torch.log(torch.rand((H,), generator=g, device=dev, dtype=f32) * 15.0 + 1.0)
+    Bb = torch.randn((H, R, N), generator=g, device=dev, dtype=f32) * 0.1
+    Cb = torch.randn((H, R, N), generator=g, device=dev, dtype=f32) * 0.1
+    h0 = (torch.randn((b, H, P, N), generator=g, device=dev, dtype=f32) * 0.1).to(torch.bfloat16)
+    return dict(x=x, B=B, C=C, dt=dt, lam=lam, theta=th, A_log=A_log, B_bias=Bb, C_bias=Cb, h0=h0)
+
+
+def run_decode(torch, m3, cfg, nsteps):
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    d = decode_inputs_device(torch, cfg, nsteps, dev, cfg.seed)
+    torch.cuda.synchronize()
+    log("[bench] %s inputs (%d steps) ready in %.1fs" % (cfg.name, nsteps, time.time() - t0))
+    b, H, R, P, N = cfg.batch, cfg.nheads, cfg.rank, cfg.headdim, cfg.dstate
+    carry = m3.new_carry(b, H, P, N, R, cfg.npairs, torch.bfloat16, torch.bfloat16, dev)
+    ys = torch.empty((b, H, R, P), dtype=torch.bfloat16, device=dev)
+
+    def reset():
+        carry["h"].copy_(d["h0"])
+        for k in ("phi", "B_prev", "x_prev"):
+            carry[k].zero_()
+
+    def step(s):
+        m3.decode_step(d["x"][s], d["B"][s], d["C"][s], d["dt"][s], d["lam"][s], d["theta"][s], d["A_log"],
+                       d["B_bias"], d["C_bias"], carry, y=ys)
+    # warm-up pass, then the timed 1000 consecutive steps from the seeded state
+    reset()
+    for s in range(min(nsteps, 20)):
+        step(s)
+    reset()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for s in range(nsteps):
+        step(s)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / nsteps
+    # per-launch duration (events around single steps)
+    reset()
+    ms_launch = per_launch_ms(torch, lambda: step(0), 50)
+    per = decode_bytes_per_head_step(cfg)
+    nbytes = per * b * H
+    state_bytes = 4 * P * N * b * H
+    out = {"workload": cfg.name, "batch": b, "nheads": H, "headdim": P, "dstate": N, "rank": R,
+           "npairs": cfg.npairs, "steps": nsteps, "ms_per_step": ms, "ms_per_launch": ms_launch,
+           "bytes_per_head_step": per, "bytes_per_step": nbytes,
+           "gbs": nbytes / (ms_launch * 1e-3) / 1e9, "gbs_incl_gaps": nbytes / (ms * 1e-3) / 1e9,
+           "state_gbs": state_bytes / (ms_launch * 1e-3) / 1e9}
+    out["hbm_frac"] = out["gbs"] / PEAK_HBM_GBS
+    log("[bench] %s: %.1f us/step (%.1f us/launch), %.0f GB/s (%.1f%% HBM), state-only %.0f GB/s" % (
+        cfg.name, ms * 1e3, ms_launch * 1e3, out["gbs"], 100 * out["hbm_frac"], out["state_gbs"]))
+    del d, carry
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(cfg, budget_s):
+    """The fp64 C oracle, as it stands, on a bounded sample of the scan
+    workload: whole sequences of the first k (batch, head) streams."""
+    from m3inputs import make_scan_inputs
+    from oracle import ref_cpu
+    cores = len(os.sched_getaffinity(0))
+    d = make_scan_inputs(cfg, batch=1)
+    H = cfg.nheads
+    t0 = time.time()
+    ref_cpu.scan(d, sel=[(0, 0)], nthreads=1)
+    one = time.time() - t0                       # one stream, one thread
+    k = int(max(1, min(H, budget_s / max(one, 1e-3) * cores * 0.8)))
+    k = max(cores if k >= cores else k, 1)
+    k = min(k, H)
+    t0 = time.time()
+    ref_cpu.scan(d, sel=[(0, h) for h in range(k)], nthreads=cores)
+    dt = time.time() - t0
+    head_tokens = k * cfg.seqlen
+    tok_s = head_tokens / dt / H                # a token is H head-tokens
+    return {"value": tok_s, "unit": "tokens/s", "cores": min(cores, k), "kind": "oracle",
+            "sample": "%s: %d of %d heads of batch 0, full L=%d (%d head-tokens) in %.1fs, fp64 C recurrence" % (
+                cfg.name, k, H, cfg.seqlen, head_tokens, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; the (batch, head) streams would shard across "
+              "GPUs without communication, which is not built here. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import selective_state_space_mimo_amd as m3
+    from m3inputs import config_by_name
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    wl = [w.strip() for w in args.workloads.split(",") if w.strip()]
+    res = {}
+    names = {"scan2": "siso_bf16_mamba2", "scan3": "mimo_bf16_prefill", "scan5": "mimo_bf16_long",
+             "decode4": "mimo_bf16_decode"}
+    for w in wl:
+        cfg = config_by_name(names[w])
+        if w.startswith("scan"):
+            steps = args.steps if w != "scan5" else max(3, args.steps // 4)
+            res[w] = run_scan(torch, m3, cfg, steps, args.warmup)
+        else:
+            res[w] = run_decode(torch, m3, cfg, args.decode_steps)
+    main_w = "scan3" if "scan3" in res else wl[0]
+    prim = res[main_w]
+    cpu = None
+    if not args.no_cpu and main_w.startswith("scan"):
+        cpu = cpu_baseline(config_by_name(names[main_w]), args.cpu_seconds)
+        log("[bench] cpu oracle: %.1f tokens/s on %d cores (%s)" % (cpu["value"], cpu["cores"], cpu["sample"]))
+    line = {
+        "metric": "scan tokens/s (% MFMA peak) + decode state GB/s (% HBM peak), 1xMI355X",
+        "value": prim.get("tokens_per_s", prim.get("gbs")),
+        "unit": "tokens/s" if main_w.startswith("scan") else "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": prim.get("ms_per_call", prim.get("ms_per_step")),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded; shapes and value laws of the workloads)",
+        "config": {"workload": prim["workload"], **{k: prim[k] for k in
+                   ("batch", "seqlen", "nheads", "headdim", "dstate", "rank", "chunk", "npairs") if k in prim}},
+    }
+    if main_w.startswith("scan"):
+        line["roofline"] = {"bound": "mfma", "achieved": prim["algo_tflops"], "peak": PEAK_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": prim["mfma_frac"], "traffic": None,
+                            "hbm_achieved_gbs": prim["algo_gbs"], "hbm_frac": prim["hbm_frac"]}
+    if "decode4" in res:
+        dd = res["decode4"]
+        line["decode"] = {"workload": dd["workload"], "gbs": dd["gbs"], "hbm_frac": dd["hbm_frac"],
+                          "us_per_step": dd["ms_per_step"] * 1e3, "us_per_launch": dd["ms_per_launch"] * 1e3,
+                          "state_gbs": dd["state_gbs"], "bytes_per_head_step": dd["bytes_per_head_step"]}
+        line["roofline_decode"] = {"bound": "hbm", "achieved": dd["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": dd["hbm_frac"], "traffic": None}
+    others = {k: v for k, v in res.items() if k != main_w and k.startswith("scan")}
+    if others:
+        line["scan_other"] = {v["workload"]: {"tokens_per_s": v["tokens_per_s"], "ms_per_call": v["ms_per_call"],
+                                              "algo_tflops": v["algo_tflops"], "mfma_frac": v["mfma_frac"],
+                                              "algo_gbs": v["algo_gbs"], "hbm_frac": v["hbm_frac"]}
+                              for v in others.values()}
+    line["cpu_baseline"] = cpu
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(s + "\n")
+
+
+if __name__ == "__main__":
+    main()
