@@ -160,34 +160,11 @@ def run_scan(torch, m3, cfg, steps, warmup):
     return out
 
 
-def decode_inputs_device(torch, cfg, nsteps, dev, seed):
-    """Per-step decode inputs for `nsteps` steps, drawn on the device from a
-    seeded torch generator (value laws as m3inputs; bf16 RNE storage)."""
-    g = torch.Generator(device=dev)
-    g.manual_seed(seed)
-    b, H, G, R, P, N, NP = cfg.batch, cfg.nheads, cfg.ngroups, cfg.rank, cfg.headdim, cfg.dstate, cfg.npairs
-    f32 = torch.float32
-    x = torch.randn((nsteps, b, H, R, P), generator=g, device=dev, dtype=f32).to(torch.bfloat16)
-
-    def bc():
-        v = torch.randn((nsteps, b, G, R, N), generator=g, device=dev, dtype=f32)
-        v = v * torch.rsqrt(v.square().mean(-1, keepdim=True) + 1e-6)
-        return v.to(torch.bfloat16)
-    B, C = bc(), bc()
-    dt = torch.nn.functional.softplus(torch.randn((nsteps, b, H), generator=g, device=dev, dtype=f32) * 0.5 - 2.0)
-    lam = torch.sigmoid(torch.randn((nsteps, b, H), generator=g, device=dev, dtype=f32))
-    th = torch.rand((nsteps, b, H, NP), generator=g, device=dev, dtype=f32) * (np.pi / N)
-    A_log = torch.log(torch.rand((H,), generator=g, device=dev, dtype=f32) * 15.0 + 1.0)
-    Bb = torch.randn((H, R, N), generator=g, device=dev, dtype=f32) * 0.1
-    Cb = torch.randn((H, R, N), generator=g, device=dev, dtype=f32) * 0.1
-    h0 = (torch.randn((b, H, P, N), generator=g, device=dev, dtype=f32) * 0.1).to(torch.bfloat16)
-    return dict(x=x, B=B, C=C, dt=dt, lam=lam, theta=th, A_log=A_log, B_bias=Bb, C_bias=Cb, h0=h0)
-
-
 def run_decode(torch, m3, cfg, nsteps):
     dev = torch.device("cuda:0")
     t0 = time.time()
-    d = decode_inputs_device(torch, cfg, nsteps, dev, cfg.seed)
+    from m3inputs.gen_torch import decode_inputs_device
+    d = decode_inputs_device(cfg, nsteps, dev, cfg.seed)
     torch.cuda.synchronize()
     log("[bench] %s inputs (%d steps) ready in %.1fs" % (cfg.name, nsteps, time.time() - t0))
     b, H, R, P, N = cfg.batch, cfg.nheads, cfg.rank, cfg.headdim, cfg.dstate

@@ -105,6 +105,54 @@ def test_scan_sweep(m3, case):
     _compare(y, fin, yr, fr, io, what="sweep")
 
 
+# bf16, P = 64, N = 128: the MFMA route, every (R, Q) specialisation, one
+# sequence segment and several (the segmented schedule), ragged lengths.
+MFMA = [
+    # R, Q,   np, G, L,   bias, lam1, init, nseg
+    (1, 64, 0, 1, 130, False, True, False, 1),
+    (1, 64, 32, 1, 200, True, False, True, 3),
+    (1, 128, 16, 2, 300, True, False, True, 1),
+    (2, 32, 32, 1, 100, True, False, True, 1),
+    (2, 32, 8, 1, 161, True, False, True, 4),
+    (2, 64, 32, 1, 129, True, False, True, 2),
+    (2, 128, 32, 2, 260, False, False, True, 1),
+    (4, 16, 64, 2, 77, True, False, True, 1),
+    (4, 16, 32, 1, 96, True, False, True, 6),
+    (4, 32, 32, 1, 99, True, False, True, 2),
+    (4, 64, 32, 1, 150, True, False, True, 1),
+    (4, 64, 32, 1, 250, True, False, True, 3),
+    (4, 64, 0, 1, 64, True, True, False, 1),
+    (4, 128, 32, 1, 300, True, False, True, 1),
+    (4, 128, 32, 1, 520, True, False, True, 4),
+]
+
+
+@pytest.mark.parametrize("case", MFMA, ids=lambda c: "R%d-Q%d-np%d-G%d-L%d-seg%d" % (c[:5] + c[8:]))
+def test_scan_mfma(m3, case):
+    R, Q, npairs, G, L, bias, lam1, init, nseg = case
+    _say("mfma scan", case)
+    cfg, d = make_small_case(2000 + 7 * R + Q + L + nseg, batch=2, seqlen=L, nheads=4, ngroups=G, headdim=64,
+                             dstate=128, rank=R, npairs=npairs, chunk=Q, io_dtype="bf16", state_dtype="f32",
+                             bias=bias, lam_one=lam1, rms_bc=True, init_full=init)
+    yr, fr = ref_cpu.scan(d)
+    y, fin = _run_scan(m3, d, cfg, nsegments=nseg)
+    _compare(y, fin, yr, fr, "bf16", what="mfma")
+
+
+def test_scan_segments_agree(m3):
+    """The schedule (number of segments) changes rounding only."""
+    cfg, d = make_small_case(3003, batch=1, seqlen=512, nheads=2, ngroups=1, headdim=64, dstate=128, rank=4,
+                             npairs=32, chunk=64, io_dtype="bf16", rms_bc=True, init_full=True)
+    yr, fr = ref_cpu.scan(d)
+    ys = []
+    for k in (1, 2, 4, 8):
+        y, fin = _run_scan(m3, d, cfg, nsegments=k)
+        _compare(y, fin, yr, fr, "bf16", what="nseg=%d" % k)
+        ys.append(host(y))
+    for yk in ys[1:]:
+        assert rel_l2(yk, ys[0]) < 1e-2
+
+
 def test_config1_tiny_siso_f32(m3):
     cfg = config_by_name("tiny_siso_f32")
     d = make_scan_inputs(cfg)
