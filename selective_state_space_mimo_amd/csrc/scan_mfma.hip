@@ -19,15 +19,18 @@
 //            + sum_{s<=t} exp(l_t - l_s) (g_s + [s<t] dS_s) sum_r' (Ct_(t,r).Bt_(s,r')) x_(s,r')
 //   Hf_out   = exp(l_e) Hf_in + sum_s exp(l_e - l_s)(g_s + dS_s) X_s^T Bt_s
 //
-// Work decomposition (one workgroup = 8 waves per (batch, head, segment)):
+// Work decomposition (one workgroup of NW waves per (batch, head, segment);
+// NW = 4 up to 256 rows per chunk, so that two workgroups share a CU and hide
+// each other's memory waits, NW = 8 for 512 rows):
 //   * query rows of a chunk are split into 16-row tiles, dealt to the waves
 //     in a zig-zag so that causal work is balanced; each wave keeps its C
 //     tiles (biased, turned, bf16) in registers as MFMA B operands and its
 //     output tiles Y^T (P x 16) as fp32 accumulators;
-//   * key rows stream through LDS in blocks of 64 (double-buffered): every
-//     wave turns 8 rows of B into Bt (row-major, for the scores) and into
-//     (v * Bt)^T (for the state update), and stores X^T -- all swizzled so
-//     that the 16-byte MFMA operand reads are bank-conflict free;
+//   * key rows stream through LDS in blocks of 32 (double-buffered, the next
+//     block's global loads issued before the current block's MFMAs): every
+//     wave turns its rows of B into Bt (row-major, for the scores) and into
+//     (v * Bt)^T (for the state update), and stores X^T -- swizzled so that
+//     the 16-byte MFMA operand reads spread over the LDS banks;
 //   * scores S^T = Bt C^T come out of the MFMA with each lane holding one
 //     query column and four key rows; masked and rounded to bf16 they are
 //     directly the B operand of Y^T += X^T S'^T (the two key tiles of a pair
@@ -46,7 +49,7 @@ namespace m3 {
 
 namespace {
 
-constexpr int kP = 64, kN = 128, kWaves = 8, kThreads = 64 * kWaves, kKB = 64;
+constexpr int kP = 64, kN = 128, kKB = 32;
 constexpr float kLog2e = 1.4426950408889634f;
 
 enum Mode { kFull = 0, kSummary = 1 };
@@ -64,55 +67,48 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 }
 
 // ---- LDS layout ------------------------------------------------------------------
-// Per key-block buffer: Bn [64 j][128 n] bf16, BvT [128 n][64 j] bf16, XT [64 p][64 j] bf16.
-constexpr int kBnBytes = kKB * kN * 2;           // 16 KiB
-constexpr int kBvBytes = kN * kKB * 2;           // 16 KiB
-constexpr int kXtBytes = kP * kKB * 2;           //  8 KiB
+// Per key-block buffer: Bn [32 j][128 n] bf16, BvT [128 n][32 j] bf16, XT [64 p][32 j] bf16.
+constexpr int kBnBytes = kKB * kN * 2;           // 8 KiB
+constexpr int kBvBytes = kN * kKB * 2;           // 8 KiB
+constexpr int kXtBytes = kP * kKB * 2;           // 4 KiB
 constexpr int kBufBytes = kBnBytes + kBvBytes + kXtBytes;
 constexpr int kHsBytes = kP * kN * 2;            // bf16 snapshot of the folded state
 
 // 16-byte-group swizzles.  Bn and Hs rows hold 16 groups (256 B); BvT and XT
-// rows hold 8 groups (128 B).
-__device__ __forceinline__ int sw16(int row) { return row & 15; }
-__device__ __forceinline__ int sw8(int row) { return (row ^ (row >> 3)) & 7; }
-__device__ __forceinline__ int bn_off(int j, int grp) { return j * 256 + ((grp ^ sw16(j)) << 4); }
-__device__ __forceinline__ int hs_off(int p, int grp) { return p * 256 + ((grp ^ sw16(p)) << 4); }
-__device__ __forceinline__ int bv_off(int n, int grp) { return n * 128 + ((grp ^ sw8(n)) << 4); }
-__device__ __forceinline__ int xt_off(int p, int grp) { return p * 128 + ((grp ^ sw8(p)) << 4); }
+// rows hold 4 groups (64 B).
+__device__ __forceinline__ int bn_off(int j, int grp) { return j * 256 + ((grp ^ (j & 15)) << 4); }
+__device__ __forceinline__ int hs_off(int p, int grp) { return p * 256 + ((grp ^ (p & 15)) << 4); }
+__device__ __forceinline__ int q4_off(int row, int grp) { return row * 64 + ((grp ^ ((row >> 1) & 3)) << 4); }
 
-template <int Q, int NPMAX>
+template <int Q>
 struct Layout {
-    static constexpr int buf0 = 0;
     static constexpr int hs = 2 * kBufBytes;
-    static constexpr int cs = hs + kHsBytes;                  // float2 [Q][NPMAX]
-    static constexpr int cbias = cs + Q * NPMAX * 8;          // float [4][128]
-    static constexpr int l2 = cbias + 4 * kN * 4;             // float [Q]
+    static constexpr int cs = hs + kHsBytes;                  // float2 [Q][64]: (cos, sin) per token and pair
+    static constexpr int cbias = cs + Q * 64 * 8;             // float [4][128]
+    static constexpr int l2 = cbias + 4 * kN * 4;             // float [Q] each below
     static constexpr int gam = l2 + Q * 4;
     static constexpr int dels = gam + Q * 4;
     static constexpr int vs = dels + Q * 4;
-    static constexpr int phic = vs + Q * 4;                   // float [64]
+    static constexpr int dtv = vs + Q * 4;
+    static constexpr int phic = dtv + Q * 4;                  // float [64]
     static constexpr int misc = phic + 64 * 4;                // float [16]
     static constexpr int total = misc + 16 * 4;
 };
 
-struct Smem {
-    char* base;
-    __device__ char* buf(int i) const { return base + i * kBufBytes; }
-};
-
-// Query tile k of wave w (chunk-level tile index), or -1.
-template <int M>
+// Query tile k of wave w (chunk-level tile index), or -1.  Tiles are dealt in
+// groups of 2 NW: wave w takes tile w and tile 2 NW - 1 - w of each group, so
+// that the causal work (tile i meets i + 1 key tiles) is the same per wave.
+template <int NT, int NW>
 __device__ __forceinline__ int query_tile(int w, int k) {
-    constexpr int NT = M / 16;
-    if constexpr (NT >= 16) {
+    if constexpr (NT >= 2 * NW) {
         const int g = k >> 1;
-        return (k & 1) == 0 ? 16 * g + w : 16 * g + 15 - w;
+        return (k & 1) == 0 ? 2 * NW * g + w : 2 * NW * g + 2 * NW - 1 - w;
     } else {
         return (k == 0 && w < NT) ? w : -1;
     }
 }
 
-// Inclusive scan of v over lanes [0, W) groups of a wave (W a power of two <= 64).
+// Inclusive scan of v over groups of W lanes of a wave (W a power of two <= 64).
 template <int W>
 __device__ __forceinline__ float group_scan(float v, int lane_in_group) {
 #pragma unroll
@@ -123,23 +119,28 @@ __device__ __forceinline__ float group_scan(float v, int lane_in_group) {
     return v;
 }
 
-template <int R, int Q, int MODE>
-__global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
+template <int R, int Q, int NW, int MODE>
+__global__ __launch_bounds__(64 * NW) void scan_mfma_kernel(ScanArgs a) {
+    constexpr int kThreads = 64 * NW;
     constexpr int M = Q * R;                 // rows per chunk
     constexpr int NKB = M / kKB;             // key blocks per chunk
     constexpr int NT = M / 16;               // query tiles per chunk
-    constexpr int TPW = NT >= 16 ? NT / 8 : 1;
-    constexpr int NPMAX = 4096 / Q > 64 ? 64 : 4096 / Q;
-    using LY = Layout<Q, NPMAX>;
-    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-    Smem sm{smem_raw};
-    float* sL2 = reinterpret_cast<float*>(smem_raw + LY::l2);
-    float* sGam = reinterpret_cast<float*>(smem_raw + LY::gam);
-    float* sDelS = reinterpret_cast<float*>(smem_raw + LY::dels);
-    float* sV = reinterpret_cast<float*>(smem_raw + LY::vs);
-    float* sPhic = reinterpret_cast<float*>(smem_raw + LY::phic);
-    float2* sCS = reinterpret_cast<float2*>(smem_raw + LY::cs);
-    float* sCb = reinterpret_cast<float*>(smem_raw + LY::cbias);
+    constexpr int TPW = NT >= 2 * NW ? NT / NW : 1;   // query tiles per wave
+    constexpr int NNT = 8 / NW;              // 16-column state tiles per wave
+    constexpr int RPW = kKB / NW;            // producer rows per wave
+    constexpr bool kFullMode = MODE == kFull;
+    using LY = Layout<Q>;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    float* sL2 = reinterpret_cast<float*>(smem + LY::l2);
+    float* sGam = reinterpret_cast<float*>(smem + LY::gam);
+    float* sDelS = reinterpret_cast<float*>(smem + LY::dels);
+    float* sV = reinterpret_cast<float*>(smem + LY::vs);
+    float* sDt = reinterpret_cast<float*>(smem + LY::dtv);
+    float* sPhic = reinterpret_cast<float*>(smem + LY::phic);
+    float2* sCS = reinterpret_cast<float2*>(smem + LY::cs);
+    float* sCb = reinterpret_cast<float*>(smem + LY::cbias);
+    float* sMisc = reinterpret_cast<float*>(smem + LY::misc);
+    float* stage = reinterpret_cast<float*>(smem + kBufBytes);     // theta, aliased on buffer 1
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
     const int nblk = gridDim.x;
     const int bid = blockIdx.x;
     const int logical = (nblk % 8 == 0) ? (bid % 8) * (nblk / 8) + bid / 8 : bid;
-    // logical order: batch, then segment, then head (heads of one batch and
+    // logical order: batch, then segment, then head (the heads of one batch and
     // segment read the same B, C rows)
     const int h = logical % H;
     const int rest = logical / H;
@@ -162,43 +163,43 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
     const float ah = expf(a.A_log[h]);
     const size_t ss = (size_t)bh * nseg + seg;          // workspace slot
     const size_t S = (size_t)a.b * H * nseg;
-    float* wsHloc = a.ws;
-    float* wsHin = a.ws ? a.ws + S * kP * kN : nullptr;
-    float* wsLam = a.ws ? a.ws + 2 * S * kP * kN : nullptr;
-    float* wsDphi = a.ws ? wsLam + S : nullptr;
-    float* wsPhi = a.ws ? wsDphi + S * np : nullptr;
+    float* const wsHloc = a.ws;
+    float* const wsHin = a.ws + S * kP * kN;
+    float* const wsLam = a.ws + 2 * S * kP * kN;
+    float* const wsDphi = wsLam + S;
+    float* const wsPhi = wsDphi + S * np;
 
-    const uint16_t* Bg = static_cast<const uint16_t*>(a.B);
-    const uint16_t* Cg = static_cast<const uint16_t*>(a.C);
-    const uint16_t* Xg = static_cast<const uint16_t*>(a.x);
+    const uint16_t* const Bg = static_cast<const uint16_t*>(a.B);
+    const uint16_t* const Cg = static_cast<const uint16_t*>(a.C);
+    const uint16_t* const Xg = static_cast<const uint16_t*>(a.x);
+    const size_t tokbase = (size_t)bi * L;               // token index base of this batch
 
     // ---- per-workgroup set-up ------------------------------------------------------------
-    // B bias pair of this lane for every rank (producer lanes own n-pair (2 lane, 2 lane + 1))
-    float2 bb[R];
+    float2 bb[R];                                        // B bias of this lane's n-pair, per rank
 #pragma unroll
     for (int r = 0; r < R; ++r)
         bb[r] = a.Bb ? *reinterpret_cast<const float2*>(a.Bb + ((size_t)h * R + r) * kN + 2 * lane) : float2{0.f, 0.f};
-    if (MODE == kFull)
+    if (kFullMode)
         for (int e = tid; e < R * kN; e += kThreads) sCb[e] = a.Cb ? a.Cb[(size_t)h * R * kN + e] : 0.f;
-    // running angle at the segment start
     for (int i = tid; i < np; i += kThreads) {
         float v = 0.f;
-        if (MODE == kFull) {
-            if (seg == 0) v = a.phi0 ? a.phi0[(size_t)bh * np + i] : 0.f;
-            else v = wsPhi[ss * np + i];
-        }
+        if (kFullMode) v = seg == 0 ? (a.phi0 ? a.phi0[(size_t)bh * np + i] : 0.f) : wsPhi[ss * np + i];
         sPhic[i] = v;
     }
-    // folded state: this wave owns state columns n in [16w, 16w + 16), all P rows,
-    // as four H^T tiles (lane: p = 16 pt + l16, n = 16 w + 4 g4 + m)
-    f32x4 hacc[4];
-    {
-        const int nb = 16 * w + 4 * g4;
+    // pairs from np on do not turn: their table entries stay (cos, sin) = (1, 0)
+    for (int e = tid; e < Q * 64; e += kThreads)
+        if ((e & 63) >= np) sCS[e] = float2{1.f, 0.f};
+    // folded state: this wave owns state columns [16 NNT w, 16 NNT (w + 1)), all
+    // P rows, as H^T tiles (lane: p = 16 pt + l16, n = 16 (NNT w + i) + 4 g4 + m)
+    f32x4 hacc[NNT][4];
+#pragma unroll
+    for (int i = 0; i < NNT; ++i) {
+        const int nb = 16 * (NNT * w + i) + 4 * g4;
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
             const int p = 16 * pt + l16;
             f32x4 v = {0.f, 0.f, 0.f, 0.f};
-            if (MODE == kFull) {
+            if (kFullMode) {
                 if (seg == 0) {
                     if (a.h0) {
                         const size_t o = ((size_t)bh * kP + p) * kN + nb;
@@ -210,8 +211,8 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
                             v = f32x4{f.x, f.y, f.z, f.w};
                         }
                     }
-                    if (a.Bp0 && a.xp0 && L > 0) {
-                        const size_t t0 = (size_t)bi * L * H + h;     // token 0 of this stream
+                    if (a.Bp0 && a.xp0) {
+                        const size_t t0 = tokbase * H + h;     // token 0 of this stream
                         const float d0 = a.dt[t0] * (1.f - a.lam[t0]);
                         const uint16_t* bp = static_cast<const uint16_t*>(a.Bp0) + (size_t)bh * R * kN;
                         const uint16_t* xp = static_cast<const uint16_t*>(a.xp0) + (size_t)bh * R * kP;
@@ -227,36 +228,126 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
                     v = f32x4{f.x, f.y, f.z, f.w};
                 }
             }
-            hacc[pt] = v;
+            hacc[i][pt] = v;
         }
     }
-    float lam_sum = 0.f;                                        // summary: sum of log alpha
+    float lam_sum = 0.f;                                 // summary: segment sum of log alpha
 
     // ---- chunk loop ------------------------------------------------------------------------
+    bf16x8 cq[TPW][4];                                   // C tiles (raw bf16 first, then biased + turned)
+    f32x4 yacc[TPW][4];                                  // Y^T tiles
+    uint32_t pfB[RPW], pfX[RPW];                         // next key block's raw B and x pairs
+
     for (int c0 = T0; c0 < T1; c0 += Q) {
         const int nvalid = min(Q, T1 - c0);
-        // (A) the folded state snapshot (bf16) for the carry readout, and the
-        //     per-token angle increments staged in buffer 1
-        if (MODE == kFull) {
-            const int nb = 16 * w + 4 * g4;
+
+        // global loads of the producer rows of key block J into pfB / pfX
+        auto load_block = [&](int J) {
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                const int p = 16 * pt + l16;
-                const uint2 u = {pack2(hacc[pt][0], hacc[pt][1]), pack2(hacc[pt][2], hacc[pt][3])};
-                *reinterpret_cast<uint2*>(smem_raw + LY::hs + hs_off(p, nb >> 3) + ((nb >> 2) & 1) * 8) = u;
+            for (int rr = 0; rr < RPW; ++rr) {
+                const int j = kKB * J + RPW * w + rr;
+                const int t = j / R, r = j % R;
+                const bool valid = t < nvalid;
+                const size_t tok = tokbase + c0 + (valid ? t : 0);
+                pfB[rr] = valid ? *reinterpret_cast<const uint32_t*>(Bg + (((tok * a.G + g) * R + r) * kN + 2 * lane)) : 0u;
+                pfX[rr] = (valid && lane < 32) ? *reinterpret_cast<const uint32_t*>(Xg + (((tok * H + h) * R + r) * kP + 2 * lane)) : 0u;
+            }
+        };
+        // turn the prefetched rows and write key block J's LDS tiles
+        auto store_block = [&](int J) {
+            char* buf = smem + (J & 1) * kBufBytes;
+            uint32_t bv0[RPW / 2], bv1[RPW / 2], xt0[RPW / 2], xt1[RPW / 2];
+#pragma unroll
+            for (int rr = 0; rr < RPW; ++rr) {
+                const int jb = RPW * w + rr;             // row within the block
+                const int j = kKB * J + jb;
+                const int t = j / R, r = j % R;
+                const bool valid = t < nvalid;
+                float b0 = lo_f(pfB[rr]) + bb[r].x, b1 = hi_f(pfB[rr]) + bb[r].y;
+                {
+                    const float2 c = sCS[t * 64 + lane];
+                    const float e = b0, o = b1;
+                    b0 = valid ? e * c.x - o * c.y : 0.f;
+                    b1 = valid ? e * c.y + o * c.x : 0.f;
+                }
+                const uint32_t bt = pack2(b0, b1);
+                if (kFullMode) {
+                    *reinterpret_cast<uint32_t*>(buf + bn_off(jb, lane >> 2) + (lane & 3) * 4) = bt;
+                    if (valid && c0 + t == L - 1 && last_seg && a.Bp1) {
+                        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.Bp1) + ((size_t)bh * R + r) * kN + 2 * lane) = bt;
+                        if (lane < 32 && a.xp1)
+                            *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.xp1) + ((size_t)bh * R + r) * kP + 2 * lane) = pfX[rr];
+                    }
+                }
+                const float vv = sV[t];
+                const uint32_t bv = pack2(b0 * vv, b1 * vv);
+                const uint32_t xr = pfX[rr];
+                if (rr & 1) {
+                    bv0[rr >> 1] |= bv << 16;
+                    bv1[rr >> 1] |= bv & 0xffff0000u;
+                    xt0[rr >> 1] |= xr << 16;
+                    xt1[rr >> 1] |= xr & 0xffff0000u;
+                } else {
+                    bv0[rr >> 1] = bv & 0xffffu;
+                    bv1[rr >> 1] = bv >> 16;
+                    xt0[rr >> 1] = xr & 0xffffu;
+                    xt1[rr >> 1] = xr >> 16;
+                }
+            }
+            // this wave's rows form group (RPW w) / 8 of each 32-row line, half (RPW w / 4) & 1 when RPW = 4
+            const int grp = (RPW * w) >> 3, half = ((RPW * w) >> 2) & 1;
+            char* bvt = buf + kBnBytes;
+            char* xtt = buf + kBnBytes + kBvBytes;
+            if constexpr (RPW == 8) {
+                *reinterpret_cast<uint4*>(bvt + q4_off(2 * lane, grp)) = uint4{bv0[0], bv0[1], bv0[2], bv0[3]};
+                *reinterpret_cast<uint4*>(bvt + q4_off(2 * lane + 1, grp)) = uint4{bv1[0], bv1[1], bv1[2], bv1[3]};
+                if (lane < 32) {
+                    *reinterpret_cast<uint4*>(xtt + q4_off(2 * lane, grp)) = uint4{xt0[0], xt0[1], xt0[2], xt0[3]};
+                    *reinterpret_cast<uint4*>(xtt + q4_off(2 * lane + 1, grp)) = uint4{xt1[0], xt1[1], xt1[2], xt1[3]};
+                }
+            } else {
+                *reinterpret_cast<uint2*>(bvt + q4_off(2 * lane, grp) + 8 * half) = uint2{bv0[0], bv0[1]};
+                *reinterpret_cast<uint2*>(bvt + q4_off(2 * lane + 1, grp) + 8 * half) = uint2{bv1[0], bv1[1]};
+                if (lane < 32) {
+                    *reinterpret_cast<uint2*>(xtt + q4_off(2 * lane, grp) + 8 * half) = uint2{xt0[0], xt0[1]};
+                    *reinterpret_cast<uint2*>(xtt + q4_off(2 * lane + 1, grp) + 8 * half) = uint2{xt1[0], xt1[1]};
+                }
+            }
+        };
+
+        // (A) state snapshot; every global load of the chunk set-up in flight at once
+        if (kFullMode) {
+#pragma unroll
+            for (int i = 0; i < NNT; ++i) {
+                const int nb = 16 * (NNT * w + i) + 4 * g4;
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const int p = 16 * pt + l16;
+                    *reinterpret_cast<uint2*>(smem + LY::hs + hs_off(p, nb >> 3) + ((nb >> 2) & 1) * 8) =
+                        uint2{pack2(hacc[i][pt][0], hacc[i][pt][1]), pack2(hacc[i][pt][2], hacc[i][pt][3])};
+                }
+            }
+            // raw C rows of this wave's query tiles, straight into the operand registers
+#pragma unroll
+            for (int k = 0; k < TPW; ++k) {
+                const int qt = query_tile<NT, NW>(w, k);
+                const int qi = 16 * (qt < 0 ? 0 : qt) + l16;
+                const int t = qi / R, r = qi % R;
+                const bool valid = qt >= 0 && t < nvalid;
+                const size_t crow = (((tokbase + c0 + (valid ? t : 0)) * a.G + g) * R + r) * kN;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const uint4 raw = valid ? *reinterpret_cast<const uint4*>(Cg + crow + 32 * ks + 8 * g4) : uint4{0, 0, 0, 0};
+                    cq[k][ks] = __builtin_bit_cast(bf16x8, raw);
+                }
             }
         }
-        float* stage = reinterpret_cast<float*>(sm.buf(1));
+        load_block(0);
         for (int e = tid; e < Q * np; e += kThreads) {
             const int t = e / np, i = e - t * np;
-            float v = 0.f;
-            if (t < nvalid) {
-                const size_t ti = ((size_t)bi * L + c0 + t) * H + h;
-                v = a.dt[ti] * a.theta[ti * np + i];
-            }
-            stage[e] = v;
+            stage[e] = t < nvalid ? a.theta[((tokbase + c0 + t) * H + h) * np + i] : 0.f;
         }
-        // (B) scalars: wave 0 scans log alpha over the chunk's tokens
+        // (B) wave 0: step sizes, chunk-local cumulative log decay, trapezoid weights
         if (w == 0) {
             constexpr int TPL = Q > 64 ? Q / 64 : 1;          // tokens per lane
             float la[TPL], gm[TPL], dl[TPL];
@@ -265,277 +356,262 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
             for (int k = 0; k < TPL; ++k) {
                 const int t = lane * TPL + k;
                 la[k] = 0.f; gm[k] = 0.f; dl[k] = 0.f;
-                if (t < Q && t < nvalid) {
-                    const size_t ti = ((size_t)bi * L + c0 + t) * H + h;
-                    const float dt = a.dt[ti], lm = a.lam[ti];
+                float dt = 0.f;
+                if (t < nvalid) {
+                    const size_t ti = (tokbase + c0 + t) * H + h;
+                    dt = a.dt[ti];
+                    const float lm = a.lam[ti];
                     la[k] = -dt * ah;
                     gm[k] = lm * dt;
                     dl[k] = dt * (1.f - lm);
                 }
+                if (t < Q) sDt[t] = dt;
                 lsum += la[k];
                 la[k] = lsum;                                  // lane-local inclusive prefix
             }
             const float incl = group_scan<64>(lsum, lane);
             const float excl = incl - lsum;
-            // look-ahead: d of the token after the chunk (0 past the sequence end)
-            float dnext = 0.f;
+            float dnext = 0.f;                                 // d of the token after the chunk
             if (c0 + Q < L) {
-                const size_t ti = ((size_t)bi * L + c0 + Q) * H + h;
+                const size_t ti = (tokbase + c0 + Q) * H + h;
                 dnext = a.dt[ti] * (1.f - a.lam[ti]);
             }
-            const float le = __shfl(incl, 63) * kLog2e;         // l_e (padded tokens add 0)
+            const float tot = __shfl(incl, 63);
+            const float le = tot * kLog2e;                     // l_e (padded tokens add 0)
+            const float nx = __shfl_down(dl[0], 1);
 #pragma unroll
             for (int k = 0; k < TPL; ++k) {
                 const int t = lane * TPL + k;
+                const float dn = (k + 1 < TPL) ? dl[k + 1] : ((t + 1 < Q) ? nx : dnext);
                 if (t < Q) {
-                    sL2[t] = (excl + la[k]) * kLog2e;
+                    const float l2t = (excl + la[k]) * kLog2e;
+                    sL2[t] = l2t;
                     sGam[t] = gm[k];
-                }
-            }
-            // dS_t = d_{t+1}
-#pragma unroll
-            for (int k = 0; k < TPL; ++k) {
-                const int t = lane * TPL + k;
-                float dn;
-                if (k + 1 < TPL) dn = dl[k + 1];
-                else {
-                    const float nx = __shfl_down(dl[0], 1);
-                    dn = (t + 1 < Q) ? nx : dnext;
-                }
-                if (t < Q) {
                     sDelS[t] = dn;
-                    sV[t] = exp2f(le - (excl + la[k]) * kLog2e) * (gm[k] + dn);
+                    sV[t] = exp2f(le - l2t) * (gm[k] + dn);
                 }
             }
-            if (lane == 0) reinterpret_cast<float*>(smem_raw + LY::misc)[0] = le;
-            lam_sum += le * (1.f / kLog2e);                    // wave 0 keeps the segment total
+            if (lane == 0) sMisc[0] = le;
+            lam_sum += tot;
         }
         __syncthreads();
-        // (C) angles: threads (pair i, part k) scan the staged increments
+        // (C) angles: threads (pair i, part k) scan dt * theta over the chunk
         {
-            constexpr int TPP_BIG = 16;                        // threads per pair when np <= 32
-            const int tpp = np <= 32 ? TPP_BIG : 8;
+            const int tpp = np <= 32 ? 16 : 8;
             const int i = tid / tpp, k = tid % tpp;
-            if (i < np) {
-                const int tpt = Q / tpp;                       // tokens per thread (>= 1)
+            if (i < np && tid < kThreads) {
+                const int tpt = Q / tpp;
                 float loc = 0.f;
-                for (int t = k * tpt; t < (k + 1) * tpt; ++t) loc += stage[t * np + i];
-                float incl = tpp == 16 ? group_scan<16>(loc, k) : group_scan<8>(loc, k);
-                const float base = sPhic[i];
-                float run = base + incl - loc;
+                for (int t = k * tpt; t < (k + 1) * tpt; ++t) loc += sDt[t] * stage[t * np + i];
+                const float incl = tpp == 16 ? group_scan<16>(loc, k) : group_scan<8>(loc, k);
+                float run = sPhic[i] + incl - loc;
                 for (int t = k * tpt; t < (k + 1) * tpt; ++t) {
-                    run += stage[t * np + i];
+                    run += sDt[t] * stage[t * np + i];
                     float sn, cs;
                     __sincosf(run, &sn, &cs);
-                    sCS[t * np + i] = float2{cs, sn};
+                    sCS[t * 64 + i] = float2{cs, sn};
                 }
                 if (k == tpp - 1) sPhic[i] = wrap_2pi(run);
             }
+            if (NW == 4 && np > 32) {
+                // 8 threads per pair cover 32 pairs per 256 threads: the rest in a second round
+                const int i2 = i + kThreads / tpp;
+                if (i2 < np) {
+                    const int tpt = Q / tpp;
+                    float loc = 0.f;
+                    for (int t = k * tpt; t < (k + 1) * tpt; ++t) loc += sDt[t] * stage[t * np + i2];
+                    const float incl = group_scan<8>(loc, k);
+                    float run = sPhic[i2] + incl - loc;
+                    for (int t = k * tpt; t < (k + 1) * tpt; ++t) {
+                        run += sDt[t] * stage[t * np + i2];
+                        float sn, cs;
+                        __sincosf(run, &sn, &cs);
+                        sCS[t * 64 + i2] = float2{cs, sn};
+                    }
+                    if (k == tpp - 1) sPhic[i2] = wrap_2pi(run);
+                }
+            }
         }
         __syncthreads();
-        const float le2 = reinterpret_cast<float*>(smem_raw + LY::misc)[0];
+        const float le2 = sMisc[0];
 
-        // (D) per-wave query tiles: C (biased, turned, bf16) and the carry readout
-        bf16x8 cq[TPW][4];
-        f32x4 yacc[TPW][4];
-        if (MODE == kFull) {
+        // (D) C tiles: bias and turn in place; carry readout Y^T = exp(l_t) Hf Ct^T
+        if (kFullMode) {
 #pragma unroll
             for (int k = 0; k < TPW; ++k) {
-                const int qt = query_tile<M>(w, k);
-                const int qi = 16 * (qt < 0 ? 0 : qt) + l16;      // chunk row
+                const int qt = query_tile<NT, NW>(w, k);
+                const int qi = 16 * (qt < 0 ? 0 : qt) + l16;
                 const int t = qi / R, r = qi % R;
                 const bool valid = qt >= 0 && t < nvalid;
-                const size_t crow = ((((size_t)bi * L + c0 + (valid ? t : 0)) * a.G + g) * R + r) * kN;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const int n0 = 32 * ks + 8 * g4;
-                    uint4 raw = valid ? *reinterpret_cast<const uint4*>(Cg + crow + n0) : uint4{0, 0, 0, 0};
+                    const uint4 raw = __builtin_bit_cast(uint4, cq[k][ks]);
                     const float4 b0 = *reinterpret_cast<const float4*>(sCb + r * kN + n0);
                     const float4 b1 = *reinterpret_cast<const float4*>(sCb + r * kN + n0 + 4);
                     float v[8] = {lo_f(raw.x) + b0.x, hi_f(raw.x) + b0.y, lo_f(raw.y) + b0.z, hi_f(raw.y) + b0.w,
                                   lo_f(raw.z) + b1.x, hi_f(raw.z) + b1.y, lo_f(raw.w) + b1.z, hi_f(raw.w) + b1.w};
 #pragma unroll
                     for (int pp = 0; pp < 4; ++pp) {
-                        const int ip = n0 / 2 + pp;
-                        if (ip < np) {
-                            const float2 c = sCS[t * np + ip];
-                            const float e = v[2 * pp], o = v[2 * pp + 1];
-                            v[2 * pp] = e * c.x - o * c.y;
-                            v[2 * pp + 1] = e * c.y + o * c.x;
-                        }
+                        const float2 c = sCS[t * 64 + n0 / 2 + pp];
+                        const float e = v[2 * pp], o = v[2 * pp + 1];
+                        v[2 * pp] = e * c.x - o * c.y;
+                        v[2 * pp + 1] = e * c.y + o * c.x;
                     }
                     bf16x8 q;
 #pragma unroll
                     for (int m = 0; m < 8; ++m) q[m] = valid ? (bf16)v[m] : (bf16)0.f;
                     cq[k][ks] = q;
                 }
-                // Y^T = exp(l_t) * (Hf Ct^T)
-                const float sc = exp2f(sL2[t < Q ? t : Q - 1]);
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                    const int p = 16 * pt + l16;
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        const bf16x8 av = *reinterpret_cast<const bf16x8*>(smem_raw + LY::hs + hs_off(p, 4 * ks + g4));
-                        acc = mfma(av, cq[k][ks], acc);
-                    }
-                    yacc[k][pt] = acc * sc;
-                }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            float sc[TPW];
+#pragma unroll
+            for (int k = 0; k < TPW; ++k) {
+                const int qt = query_tile<NT, NW>(w, k);
+                sc[k] = exp2f(sL2[(16 * (qt < 0 ? 0 : qt) + l16) / R]);
+            }
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const int p = 16 * pt + l16;
+#pragma unroll
+                for (int k = 0; k < TPW; ++k) yacc[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const bf16x8 av = *reinterpret_cast<const bf16x8*>(smem + LY::hs + hs_off(p, 4 * ks + g4));
+#pragma unroll
+                    for (int k = 0; k < TPW; ++k) yacc[k][pt] = mfma(av, cq[k][ks], yacc[k][pt]);
+                }
+#pragma unroll
+                for (int k = 0; k < TPW; ++k) yacc[k][pt] = yacc[k][pt] * sc[k];
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
         // the state decays over the whole chunk before this chunk's writes land
         {
             const float f = exp2f(le2);
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt) hacc[pt] = hacc[pt] * f;
-        }
-
-        // (E) key blocks: produce block J into buffer J % 2, consume it
-        auto produce = [&](int J) {
-            char* buf = sm.buf(J & 1);
-            // wave w turns rows 8w .. 8w+7 of block J; lane owns n-pair (2 lane, 2 lane + 1)
-            uint32_t bvt0[4], bvt1[4];                      // 8 rows of (v Bt) for n = 2 lane, 2 lane + 1
-            uint32_t xt0[4], xt1[4];                        // 8 rows of x for p = 2 lane, 2 lane + 1 (lane < 32)
-            const int ip = lane;                            // pair index
+            for (int i = 0; i < NNT; ++i)
 #pragma unroll
-            for (int rr = 0; rr < 8; ++rr) {
-                const int j = kKB * J + 8 * w + rr;          // chunk row
-                const int t = j / R, r = j % R;
-                const int s = c0 + t;                        // token
-                const bool valid = t < nvalid;
-                const size_t tok = (size_t)bi * L + (valid ? s : c0);
-                uint32_t braw = 0, xraw = 0;
-                if (valid) {
-                    braw = *reinterpret_cast<const uint32_t*>(Bg + (((tok * a.G + g) * R + r) * kN + 2 * lane));
-                    if (lane < 32) xraw = *reinterpret_cast<const uint32_t*>(Xg + (((tok * H + h) * R + r) * kP + 2 * lane));
-                }
-                float b0 = valid ? lo_f(braw) + bb[r].x : 0.f;
-                float b1 = valid ? hi_f(braw) + bb[r].y : 0.f;
-                if (ip < np) {
-                    const float2 c = sCS[t * np + ip];
-                    const float e = b0, o = b1;
-                    b0 = e * c.x - o * c.y;
-                    b1 = e * c.y + o * c.x;
-                }
-                const uint32_t bt = pack2(b0, b1);
-                if (MODE == kFull) {
-                    *reinterpret_cast<uint32_t*>(buf + bn_off(8 * w + rr, lane >> 2) + (lane & 3) * 4) = bt;
-                    if (valid && s == L - 1 && last_seg && a.Bp1) {
-                        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.Bp1) + ((size_t)bh * R + r) * kN + 2 * lane) = bt;
-                        if (lane < 32 && a.xp1)
-                            *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.xp1) + ((size_t)bh * R + r) * kP + 2 * lane) = xraw;
-                    }
-                }
-                const float vv = sV[t];
-                const uint32_t bv = pack2(b0 * vv, b1 * vv);
-                // transpose in registers: (row rr) -> k-slot rr of the n = 2 lane / 2 lane + 1 rows
-                if (rr & 1) {
-                    bvt0[rr >> 1] |= bv << 16;
-                    bvt1[rr >> 1] |= bv & 0xffff0000u;
-                    xt0[rr >> 1] |= xraw << 16;
-                    xt1[rr >> 1] |= xraw & 0xffff0000u;
-                } else {
-                    bvt0[rr >> 1] = bv & 0xffffu;
-                    bvt1[rr >> 1] = bv >> 16;
-                    xt0[rr >> 1] = xraw & 0xffffu;
-                    xt1[rr >> 1] = xraw >> 16;
-                }
-            }
-            *reinterpret_cast<uint4*>(buf + kBnBytes + bv_off(2 * lane, w)) = uint4{bvt0[0], bvt0[1], bvt0[2], bvt0[3]};
-            *reinterpret_cast<uint4*>(buf + kBnBytes + bv_off(2 * lane + 1, w)) = uint4{bvt1[0], bvt1[1], bvt1[2], bvt1[3]};
-            if (lane < 32) {
-                *reinterpret_cast<uint4*>(buf + kBnBytes + kBvBytes + xt_off(2 * lane, w)) = uint4{xt0[0], xt0[1], xt0[2], xt0[3]};
-                *reinterpret_cast<uint4*>(buf + kBnBytes + kBvBytes + xt_off(2 * lane + 1, w)) = uint4{xt1[0], xt1[1], xt1[2], xt1[3]};
-            }
-        };
+                for (int pt = 0; pt < 4; ++pt) hacc[i][pt] = hacc[i][pt] * f;
+        }
+        store_block(0);
+        __syncthreads();
 
-        auto consume = [&](int J) {
-            const char* buf = sm.buf(J & 1);
+        // (E) key blocks: prefetch J + 1, consume J, write J + 1
+#pragma unroll 1
+        for (int J = 0; J < NKB; ++J) {
+            if (J + 1 < NKB) load_block(J + 1);
+            const char* buf = smem + (J & 1) * kBufBytes;
             const char* bvb = buf + kBnBytes;
             const char* xtb = buf + kBnBytes + kBvBytes;
-            if (MODE == kFull) {
+            if (kFullMode) {
+                // Operand loads are shared by this wave's query tiles, so the loops
+                // run operand-outer, tile-inner: each LDS operand is read once.
+                const int ka = 2 * J;                            // key tiles ka, ka + 1 of this block
+                bool act[TPW], hasb[TPW];
+                int tq[TPW];
 #pragma unroll
                 for (int k = 0; k < TPW; ++k) {
-                    const int qt = query_tile<M>(w, k);
-                    if (qt < 0) continue;
-                    const int qi = 16 * qt + l16;
-                    const int t = qi / R;
+                    const int qt = query_tile<NT, NW>(w, k);
+                    act[k] = qt >= ka;
+                    hasb[k] = qt >= ka + 1;
+                    tq[k] = (16 * (qt < 0 ? 0 : qt) + l16) / R;
+                }
+                // (1) scores S^T = Bt C^T for key tile a and b
+                f32x4 s0[TPW], s1[TPW];
+#pragma unroll
+                for (int k = 0; k < TPW; ++k) { s0[k] = f32x4{0.f, 0.f, 0.f, 0.f}; s1[k] = s0[k]; }
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const bf16x8 av = *reinterpret_cast<const bf16x8*>(buf + bn_off(l16, 4 * ks + g4));
+#pragma unroll
+                    for (int k = 0; k < TPW; ++k)
+                        if (act[k]) s0[k] = mfma(av, cq[k][ks], s0[k]);
+                }
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const bf16x8 av = *reinterpret_cast<const bf16x8*>(buf + bn_off(16 + l16, 4 * ks + g4));
+#pragma unroll
+                    for (int k = 0; k < TPW; ++k)
+                        if (hasb[k]) s1[k] = mfma(av, cq[k][ks], s1[k]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // (2) mask: key rows 16 ka + 4 g4 + m (tile a) and 16 ka + 16 + 4 g4 + m (tile b)
+                bf16x8 bop[TPW];
+#pragma unroll
+                for (int k = 0; k < TPW; ++k) {
+                    const int t = tq[k];
                     const float l2t = sL2[t];
+                    auto weight = [&](int sidx) {
+                        return sidx <= t ? exp2f(l2t - sL2[sidx]) * (sGam[sidx] + (sidx < t ? sDelS[sidx] : 0.f)) : 0.f;
+                    };
+                    float wa[4], wb[4];
+                    if constexpr (R == 4) {
+                        const float x0 = weight(8 * J + g4), x1 = weight(8 * J + 4 + g4);
 #pragma unroll
-                    for (int kp = 0; kp < 2; ++kp) {
-                        const int ka = 4 * J + 2 * kp;          // chunk-level key tiles ka, ka + 1
-                        if (ka > qt) continue;
-                        const bool has_b = ka + 1 <= qt;
-                        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+                        for (int m = 0; m < 4; ++m) { wa[m] = x0; wb[m] = x1; }
+                    } else if constexpr (R == 2) {
 #pragma unroll
-                        for (int ks = 0; ks < 4; ++ks) {
-                            const bf16x8 av = *reinterpret_cast<const bf16x8*>(buf + bn_off(32 * kp + l16, 4 * ks + g4));
-                            s0 = mfma(av, cq[k][ks], s0);
+                        for (int m = 0; m < 4; m += 2) {
+                            const float x0 = weight((32 * J + 4 * g4 + m) / 2);
+                            const float x1 = weight((32 * J + 16 + 4 * g4 + m) / 2);
+                            wa[m] = wa[m + 1] = x0;
+                            wb[m] = wb[m + 1] = x1;
                         }
-                        if (has_b) {
-#pragma unroll
-                            for (int ks = 0; ks < 4; ++ks) {
-                                const bf16x8 av = *reinterpret_cast<const bf16x8*>(buf + bn_off(32 * kp + 16 + l16, 4 * ks + g4));
-                                s1 = mfma(av, cq[k][ks], s1);
-                            }
-                        }
-                        // mask: key rows 16 ka + 4 g4 + m (tile a) and 16 (ka+1) + 4 g4 + m (tile b)
-                        bf16x8 bop;
+                    } else {
 #pragma unroll
                         for (int m = 0; m < 4; ++m) {
-                            const int sa = (16 * ka + 4 * g4 + m) / R;
-                            const int sb = (16 * ka + 16 + 4 * g4 + m) / R;
-                            float wa = 0.f, wb = 0.f;
-                            if (sa <= t) wa = exp2f(l2t - sL2[sa]) * (sGam[sa] + (sa < t ? sDelS[sa] : 0.f));
-                            if (has_b && sb <= t) wb = exp2f(l2t - sL2[sb]) * (sGam[sb] + (sb < t ? sDelS[sb] : 0.f));
-                            bop[m] = (bf16)(s0[m] * wa);
-                            bop[4 + m] = (bf16)(s1[m] * wb);
-                        }
-#pragma unroll
-                        for (int pt = 0; pt < 4; ++pt) {
-                            const int p = 16 * pt + l16;
-                            // k-slots: keys 4 g4 + 0..3 of tile a, then of tile b
-                            const int j0 = 32 * kp + 4 * g4, j1 = j0 + 16;
-                            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(xtb + xt_off(p, j0 >> 3) + ((j0 >> 2) & 1) * 8);
-                            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(xtb + xt_off(p, j1 >> 3) + ((j1 >> 2) & 1) * 8);
-                            const bf16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                            yacc[k][pt] = mfma(av, bop, yacc[k][pt]);
+                            wa[m] = weight(32 * J + 4 * g4 + m);
+                            wb[m] = weight(32 * J + 16 + 4 * g4 + m);
                         }
                     }
-                }
-            }
-            // state: Hf^T[n-tile w] += (v Bt)^T X over the block's 64 rows
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 av = *reinterpret_cast<const bf16x8*>(bvb + bv_off(16 * w + l16, 4 * ks + g4));
+                    for (int m = 0; m < 4; ++m) {
+                        bop[k][m] = (bf16)(s0[k][m] * wa[m]);
+                        bop[k][4 + m] = (bf16)(s1[k][m] * wb[m]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // (3) Y^T += X^T S'^T; X^T read with the k permutation of S'^T:
+                //     keys 4 g4 + 0..3 of tile a, then of tile b
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) {
-                    const bf16x8 bv = *reinterpret_cast<const bf16x8*>(xtb + xt_off(16 * pt + l16, 4 * ks + g4));
-                    hacc[pt] = mfma(av, bv, hacc[pt]);
+                    const int p = 16 * pt + l16;
+                    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(xtb + q4_off(p, g4 >> 1) + (g4 & 1) * 8);
+                    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(xtb + q4_off(p, 2 + (g4 >> 1)) + (g4 & 1) * 8);
+                    const bf16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+                    for (int k = 0; k < TPW; ++k)
+                        if (act[k]) yacc[k][pt] = mfma(av, bop[k], yacc[k][pt]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // state: Hf^T[wave's n-tiles] += (v Bt)^T X over the block's 32 rows
+#pragma unroll
+            for (int i = 0; i < NNT; ++i) {
+                const bf16x8 av = *reinterpret_cast<const bf16x8*>(bvb + q4_off(16 * (NNT * w + i) + l16, g4));
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const bf16x8 bv = *reinterpret_cast<const bf16x8*>(xtb + q4_off(16 * pt + l16, g4));
+                    hacc[i][pt] = mfma(av, bv, hacc[i][pt]);
                 }
             }
-        };
-
-        produce(0);
-        __syncthreads();
-        for (int J = 0; J < NKB; ++J) {
-            if (J + 1 < NKB) produce(J + 1);
-            consume(J);
+            if (J + 1 < NKB) store_block(J + 1);
             __syncthreads();
         }
 
         // (F) outputs of this chunk
-        if (MODE == kFull) {
+        if (kFullMode) {
             bf16* yg = static_cast<bf16*>(a.y);
 #pragma unroll
             for (int k = 0; k < TPW; ++k) {
-                const int qt = query_tile<M>(w, k);
+                const int qt = query_tile<NT, NW>(w, k);
                 if (qt < 0) continue;
                 const int qi = 16 * qt + l16;
                 const int t = qi / R, r = qi % R;
                 if (t >= nvalid) continue;
-                bf16* yrow = yg + ((((size_t)bi * L + c0 + t) * H + h) * R + r) * kP;
+                bf16* yrow = yg + (((tokbase + c0 + t) * H + h) * R + r) * kP;
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) {
                     bf16x4 o;
@@ -548,26 +624,34 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
     }
 
     // ---- end of the stream / segment ----------------------------------------------------------
-    const int nb = 16 * w + 4 * g4;
-    if (MODE == kSummary) {
+    if (!kFullMode) {
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-            const int p = 16 * pt + l16;
-            *reinterpret_cast<float4*>(wsHloc + (ss * kP + p) * kN + nb) = float4{hacc[pt][0], hacc[pt][1], hacc[pt][2], hacc[pt][3]};
+        for (int i = 0; i < NNT; ++i) {
+            const int nb = 16 * (NNT * w + i) + 4 * g4;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const int p = 16 * pt + l16;
+                *reinterpret_cast<float4*>(wsHloc + (ss * kP + p) * kN + nb) =
+                    float4{hacc[i][pt][0], hacc[i][pt][1], hacc[i][pt][2], hacc[i][pt][3]};
+            }
         }
         if (tid == 0) wsLam[ss] = lam_sum;
         for (int i = tid; i < np; i += kThreads) wsDphi[ss * np + i] = sPhic[i];
     } else if (last_seg) {
         if (a.h1) {
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                const int p = 16 * pt + l16;
-                const size_t o = ((size_t)bh * kP + p) * kN + nb;
-                if (a.st_bf16) {
-                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.h1) + o) =
-                        uint2{pack2(hacc[pt][0], hacc[pt][1]), pack2(hacc[pt][2], hacc[pt][3])};
-                } else {
-                    *reinterpret_cast<float4*>(static_cast<float*>(a.h1) + o) = float4{hacc[pt][0], hacc[pt][1], hacc[pt][2], hacc[pt][3]};
+            for (int i = 0; i < NNT; ++i) {
+                const int nb = 16 * (NNT * w + i) + 4 * g4;
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const int p = 16 * pt + l16;
+                    const size_t o = ((size_t)bh * kP + p) * kN + nb;
+                    if (a.st_bf16)
+                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.h1) + o) =
+                            uint2{pack2(hacc[i][pt][0], hacc[i][pt][1]), pack2(hacc[i][pt][2], hacc[i][pt][3])};
+                    else
+                        *reinterpret_cast<float4*>(static_cast<float*>(a.h1) + o) =
+                            float4{hacc[i][pt][0], hacc[i][pt][1], hacc[i][pt][2], hacc[i][pt][3]};
                 }
             }
         }
@@ -632,23 +716,23 @@ __global__ __launch_bounds__(256) void carry_pass_kernel(ScanArgs a) {
 
 template <int R, int Q>
 hipError_t launch_rq(const ScanArgs& a, hipStream_t st) {
-    constexpr int NPMAX = 4096 / Q > 64 ? 64 : 4096 / Q;
-    const size_t lds = Layout<Q, NPMAX>::total;
+    constexpr int NW = 8;
+    const size_t lds = Layout<Q>::total;
     const int nblk = a.b * a.H * a.nseg;
     hipError_t e;
     if (a.nseg > 1) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_mfma_kernel<R, Q, kSummary>),
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_mfma_kernel<R, Q, NW, kSummary>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((scan_mfma_kernel<R, Q, kSummary>), dim3(nblk), dim3(kThreads), lds, st, a);
+        hipLaunchKernelGGL((scan_mfma_kernel<R, Q, NW, kSummary>), dim3(nblk), dim3(64 * NW), lds, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL(carry_pass_kernel, dim3((kP * kN / 2 + 255) / 256, a.b * a.H), dim3(256), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_mfma_kernel<R, Q, kFull>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_mfma_kernel<R, Q, NW, kFull>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_mfma_kernel<R, Q, kFull>), dim3(nblk), dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((scan_mfma_kernel<R, Q, NW, kFull>), dim3(nblk), dim3(64 * NW), lds, st, a);
     return hipGetLastError();
 }
 
@@ -659,9 +743,7 @@ bool scan_mfma_supported(const ScanArgs& a) {
     const int M = a.Q * a.R;
     if (!(a.R == 1 || a.R == 2 || a.R == 4)) return false;
     if (!(a.Q == 16 || a.Q == 32 || a.Q == 64 || a.Q == 128)) return false;
-    if (M < 64 || M > 512) return false;
-    const int npmax = 4096 / a.Q > 64 ? 64 : 4096 / a.Q;
-    return a.np <= npmax;
+    return M >= 64 && M <= 512;
 }
 
 size_t scan_mfma_workspace_bytes(const ScanArgs& a) {
