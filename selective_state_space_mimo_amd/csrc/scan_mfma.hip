@@ -16,28 +16,30 @@
 // delivers, d_u = dt_u (1 - lam_u)).  Then, with l the chunk-local cumulative
 // log-decay, g_s = lam_s dt_s and dS_s = d_{s+1}:
 //   y_(t,r)  = exp(l_t) Hf_in Ct_(t,r)
-//            + sum_{s<=t} exp(l_t - l_s) (g_s + [s<t] dS_s) sum_r' (Ct_(t,r).Bt_(s,r')) x_(s,r')
-//   Hf_out   = exp(l_e) Hf_in + sum_s exp(l_e - l_s)(g_s + dS_s) X_s^T Bt_s
+//            + sum_{s<=t} W(t,s) sum_r' (Ct_(t,r).Bt_(s,r')) x_(s,r'),
+//     W(t,s) = exp(l_t - l_s) (g_s + [s<t] dS_s)
+//   Hf_out   = exp(l_e) Hf_in + sum_s v_s X_s^T Bt_s,  v_s = exp(l_e - l_s)(g_s + dS_s)
 //
-// Work decomposition (one workgroup of NW waves per (batch, head, segment);
-// NW = 4 up to 256 rows per chunk, so that two workgroups share a CU and hide
-// each other's memory waits, NW = 8 for 512 rows):
+// Work decomposition (one workgroup of 8 waves per (batch, head, segment)):
+//   * per chunk, the token-pair weights W (lower triangle, fp16), the (cos, sin)
+//     of every running angle (fp16) and v are tabled in LDS once;
 //   * query rows of a chunk are split into 16-row tiles, dealt to the waves
 //     in a zig-zag so that causal work is balanced; each wave keeps its C
 //     tiles (biased, turned, bf16) in registers as MFMA B operands and its
 //     output tiles Y^T (P x 16) as fp32 accumulators;
-//   * key rows stream through LDS in blocks of 32 (double-buffered, the next
-//     block's global loads issued before the current block's MFMAs): every
-//     wave turns its rows of B into Bt (row-major, for the scores) and into
-//     (v * Bt)^T (for the state update), and stores X^T -- swizzled so that
-//     the 16-byte MFMA operand reads spread over the LDS banks;
+//   * key rows stream through LDS in blocks of 32 (double-buffered); the raw
+//     rows of B and x are fetched into a register ring 2-4 blocks ahead of
+//     their use (across chunk boundaries), so that memory latency overlaps
+//     the MFMA work.  Every wave turns 4 rows of B into Bt (row-major, for
+//     the scores) and (v Bt)^T (for the state update) and stores X^T, all
+//     swizzled so that the 16-byte MFMA operand reads spread over the banks;
 //   * scores S^T = Bt C^T come out of the MFMA with each lane holding one
-//     query column and four key rows; masked and rounded to bf16 they are
-//     directly the B operand of Y^T += X^T S'^T (the two key tiles of a pair
+//     query column and four key rows; weighted and rounded to bf16 they are
+//     directly the B operand of Y^T += X^T S'^T (the two key tiles of a block
 //     give the 8 k-slots; X^T is read with the same k permutation);
 //   * the P x N state lives in MFMA accumulators (as H^T: each wave owns 16
 //     state columns), updated by Hf^T += (v Bt)^T X; a bf16 copy in LDS is
-//     the A operand of the carry readout Y^T = Hf Ct^T.
+//     the A operand of the carry readout Y^T = Hf Ct^T;
 //   * per-chunk prefix sums (log-decay, angles) use wave shuffles.
 // Segmented schedule (few streams, long sequences): pass 1 computes, per
 // segment, the folded state from a zero carry in a local angle frame; pass 2
@@ -49,10 +51,12 @@ namespace m3 {
 
 namespace {
 
-constexpr int kP = 64, kN = 128, kKB = 32;
+constexpr int kP = 64, kN = 128, kKB = 32, kNW = 8, kThreads = 64 * kNW, kRPW = kKB / kNW;
 constexpr float kLog2e = 1.4426950408889634f;
 
 enum Mode { kFull = 0, kSummary = 1 };
+
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -65,6 +69,7 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     v[1] = (bf16)hi;
     return __builtin_bit_cast(uint32_t, v);
 }
+__device__ __forceinline__ int tri(int t, int s) { return (t * (t + 1) >> 1) + s; }
 
 // ---- LDS layout ------------------------------------------------------------------
 // Per key-block buffer: Bn [32 j][128 n] bf16, BvT [128 n][32 j] bf16, XT [64 p][32 j] bf16.
@@ -83,8 +88,9 @@ __device__ __forceinline__ int q4_off(int row, int grp) { return row * 64 + ((gr
 template <int Q>
 struct Layout {
     static constexpr int hs = 2 * kBufBytes;
-    static constexpr int cs = hs + kHsBytes;                  // float2 [Q][64]: (cos, sin) per token and pair
-    static constexpr int cbias = cs + Q * 64 * 8;             // float [4][128]
+    static constexpr int cs = hs + kHsBytes;                  // half2 [Q][64]: (cos, sin) per token and pair
+    static constexpr int wt = cs + Q * 64 * 4;                // half [Q (Q + 1) / 2]: W(t, s), s <= t
+    static constexpr int cbias = wt + ((Q * (Q + 1) / 2 * 2 + 15) & ~15);   // float [4][128]
     static constexpr int l2 = cbias + 4 * kN * 4;             // float [Q] each below
     static constexpr int gam = l2 + Q * 4;
     static constexpr int dels = gam + Q * 4;
@@ -96,13 +102,13 @@ struct Layout {
 };
 
 // Query tile k of wave w (chunk-level tile index), or -1.  Tiles are dealt in
-// groups of 2 NW: wave w takes tile w and tile 2 NW - 1 - w of each group, so
-// that the causal work (tile i meets i + 1 key tiles) is the same per wave.
-template <int NT, int NW>
+// groups of 16: wave w takes tile w and tile 15 - w of each group, so that the
+// causal work (tile i meets i + 1 key tiles) is the same for every wave.
+template <int NT>
 __device__ __forceinline__ int query_tile(int w, int k) {
-    if constexpr (NT >= 2 * NW) {
+    if constexpr (NT >= 2 * kNW) {
         const int g = k >> 1;
-        return (k & 1) == 0 ? 2 * NW * g + w : 2 * NW * g + 2 * NW - 1 - w;
+        return (k & 1) == 0 ? 2 * kNW * g + w : 2 * kNW * g + 2 * kNW - 1 - w;
     } else {
         return (k == 0 && w < NT) ? w : -1;
     }
@@ -119,16 +125,21 @@ __device__ __forceinline__ float group_scan(float v, int lane_in_group) {
     return v;
 }
 
-template <int R, int Q, int NW, int MODE>
-__global__ __launch_bounds__(64 * NW) void scan_mfma_kernel(ScanArgs a) {
-    constexpr int kThreads = 64 * NW;
+template <int R, int Q, int MODE>
+__global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
     constexpr int M = Q * R;                 // rows per chunk
     constexpr int NKB = M / kKB;             // key blocks per chunk
     constexpr int NT = M / 16;               // query tiles per chunk
-    constexpr int TPW = NT >= 2 * NW ? NT / NW : 1;   // query tiles per wave
-    constexpr int NNT = 8 / NW;              // 16-column state tiles per wave
-    constexpr int RPW = kKB / NW;            // producer rows per wave
+    constexpr int TPW = NT >= 2 * kNW ? NT / kNW : 1;   // query tiles per wave
+    // prefetch distance (blocks) = ring size; shorter when 4 query tiles per wave
+    // already take the registers
+    constexpr int D = TPW >= 4 ? 2 : (NKB >= 4 ? 4 : NKB);
+    constexpr bool kPrefetchTheta = TPW < 4;
+    constexpr int TH = (Q * 64 + kThreads - 1) / kThreads;   // theta values per thread (np <= 64)
+    constexpr int TPL = Q > 64 ? Q / 64 : 1; // tokens per lane of wave 0
+    constexpr int RSTEP = R == 4 ? 4 : (R == 2 ? 2 : 1);
     constexpr bool kFullMode = MODE == kFull;
+    static_assert(NKB % D == 0, "ring size must divide the blocks per chunk");
     using LY = Layout<Q>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     float* sL2 = reinterpret_cast<float*>(smem + LY::l2);
@@ -137,12 +148,16 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma_kernel(ScanArgs a) {
     float* sV = reinterpret_cast<float*>(smem + LY::vs);
     float* sDt = reinterpret_cast<float*>(smem + LY::dtv);
     float* sPhic = reinterpret_cast<float*>(smem + LY::phic);
-    float2* sCS = reinterpret_cast<float2*>(smem + LY::cs);
+    f16x2* sCS = reinterpret_cast<f16x2*>(smem + LY::cs);
+    _Float16* sW = reinterpret_cast<_Float16*>(smem + LY::wt);
     float* sCb = reinterpret_cast<float*>(smem + LY::cbias);
     float* sMisc = reinterpret_cast<float*>(smem + LY::misc);
     float* stage = reinterpret_cast<float*>(smem + kBufBytes);     // theta, aliased on buffer 1
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // the wave index is the same for all lanes of a wave: say so, so that every
+    // decision derived from it is a scalar branch and its values live in SGPRs
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
     const int H = a.H, L = a.L, np = a.np, nseg = a.nseg;
 
@@ -169,10 +184,16 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma_kernel(ScanArgs a) {
     float* const wsDphi = wsLam + S;
     float* const wsPhi = wsDphi + S * np;
 
-    const uint16_t* const Bg = static_cast<const uint16_t*>(a.B);
-    const uint16_t* const Cg = static_cast<const uint16_t*>(a.C);
-    const uint16_t* const Xg = static_cast<const uint16_t*>(a.x);
     const size_t tokbase = (size_t)bi * L;               // token index base of this batch
+    // row pointers: token 0 of this batch, group g / head h, rank 0
+    const uint16_t* const Bg = static_cast<const uint16_t*>(a.B) + (tokbase * a.G + g) * R * kN;
+    const uint16_t* const Cg = static_cast<const uint16_t*>(a.C) + (tokbase * a.G + g) * R * kN;
+    const uint16_t* const Xg = static_cast<const uint16_t*>(a.x) + (tokbase * H + h) * R * kP;
+    const size_t bstride = (size_t)a.G * R * kN;          // elements between tokens in B, C
+    const size_t xstride = (size_t)H * R * kP;            // ... in x, y
+    const float* const dtg = a.dt + tokbase * H + h;      // dt of token t: dtg[t H]
+    const float* const lamg = a.lam + tokbase * H + h;
+    const float* const thg = np ? a.theta + (tokbase * H + h) * np : a.dt;   // theta[t][i]: thg[t H np + i]
 
     // ---- per-workgroup set-up ------------------------------------------------------------
     float2 bb[R];                                        // B bias of this lane's n-pair, per rank
@@ -188,183 +209,188 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma_kernel(ScanArgs a) {
     }
     // pairs from np on do not turn: their table entries stay (cos, sin) = (1, 0)
     for (int e = tid; e < Q * 64; e += kThreads)
-        if ((e & 63) >= np) sCS[e] = float2{1.f, 0.f};
-    // folded state: this wave owns state columns [16 NNT w, 16 NNT (w + 1)), all
-    // P rows, as H^T tiles (lane: p = 16 pt + l16, n = 16 (NNT w + i) + 4 g4 + m)
-    f32x4 hacc[NNT][4];
+        if ((e & 63) >= np) sCS[e] = f16x2{(_Float16)1.f, (_Float16)0.f};
+    // folded state: this wave owns state columns [16 w, 16 w + 16), all P rows,
+    // as four H^T tiles (lane: p = 16 pt + l16, n = 16 w + 4 g4 + m)
+    const int nb = 16 * w + 4 * g4;
+    f32x4 hacc[4];
 #pragma unroll
-    for (int i = 0; i < NNT; ++i) {
-        const int nb = 16 * (NNT * w + i) + 4 * g4;
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-            const int p = 16 * pt + l16;
-            f32x4 v = {0.f, 0.f, 0.f, 0.f};
-            if (kFullMode) {
-                if (seg == 0) {
-                    if (a.h0) {
-                        const size_t o = ((size_t)bh * kP + p) * kN + nb;
-                        if (a.st_bf16) {
-                            const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.h0) + o);
-                            v = f32x4{lo_f(u.x), hi_f(u.x), lo_f(u.y), hi_f(u.y)};
-                        } else {
-                            const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(a.h0) + o);
-                            v = f32x4{f.x, f.y, f.z, f.w};
-                        }
+    for (int pt = 0; pt < 4; ++pt) {
+        const int p = 16 * pt + l16;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (kFullMode) {
+            if (seg == 0) {
+                if (a.h0) {
+                    const size_t o = ((size_t)bh * kP + p) * kN + nb;
+                    if (a.st_bf16) {
+                        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.h0) + o);
+                        v = f32x4{lo_f(u.x), hi_f(u.x), lo_f(u.y), hi_f(u.y)};
+                    } else {
+                        const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(a.h0) + o);
+                        v = f32x4{f.x, f.y, f.z, f.w};
                     }
-                    if (a.Bp0 && a.xp0) {
-                        const size_t t0 = tokbase * H + h;     // token 0 of this stream
-                        const float d0 = a.dt[t0] * (1.f - a.lam[t0]);
-                        const uint16_t* bp = static_cast<const uint16_t*>(a.Bp0) + (size_t)bh * R * kN;
-                        const uint16_t* xp = static_cast<const uint16_t*>(a.xp0) + (size_t)bh * R * kP;
-#pragma unroll
-                        for (int r = 0; r < R; ++r) {
-                            const float xv = d0 * bf16_bits_to_f32(xp[r * kP + p]);
-#pragma unroll
-                            for (int m = 0; m < 4; ++m) v[m] += xv * bf16_bits_to_f32(bp[r * kN + nb + m]);
-                        }
-                    }
-                } else {
-                    const float4 f = *reinterpret_cast<const float4*>(wsHin + (ss * kP + p) * kN + nb);
-                    v = f32x4{f.x, f.y, f.z, f.w};
                 }
+                if (a.Bp0 && a.xp0) {
+                    const float d0 = dtg[0] * (1.f - lamg[0]);
+                    const uint16_t* bp = static_cast<const uint16_t*>(a.Bp0) + (size_t)bh * R * kN;
+                    const uint16_t* xp = static_cast<const uint16_t*>(a.xp0) + (size_t)bh * R * kP;
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const float xv = d0 * bf16_bits_to_f32(xp[r * kP + p]);
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) v[m] += xv * bf16_bits_to_f32(bp[r * kN + nb + m]);
+                    }
+                }
+            } else {
+                const float4 f = *reinterpret_cast<const float4*>(wsHin + (ss * kP + p) * kN + nb);
+                v = f32x4{f.x, f.y, f.z, f.w};
             }
-            hacc[i][pt] = v;
         }
+        hacc[pt] = v;
     }
     float lam_sum = 0.f;                                 // summary: segment sum of log alpha
 
-    // ---- chunk loop ------------------------------------------------------------------------
+    // ---- prefetch rings ------------------------------------------------------------------------
+    // Key block gb of the segment (chunk gb / NKB, block gb % NKB): this wave's
+    // rows jb = 4 w + rr of it are (token, rank) = ((32 J + jb) / R, (32 J + jb) % R).
+    uint32_t rgB[D][kRPW], rgX[D][kRPW];
+    auto fetch = [&](int gb, uint32_t (&pb)[kRPW], uint32_t (&px)[kRPW]) {
+        const int c = gb / NKB, J = gb % NKB;
+#pragma unroll
+        for (int rr = 0; rr < kRPW; ++rr) {
+            const int j = kKB * J + kRPW * w + rr;
+            const int t = T0 + c * Q + j / R;            // token (uniform)
+            const int r = j % R;
+            if (t < T1) {
+                pb[rr] = *reinterpret_cast<const uint32_t*>(Bg + (size_t)t * bstride + r * kN + 2 * lane);
+                px[rr] = *reinterpret_cast<const uint32_t*>(Xg + (size_t)t * xstride + r * kP + 2 * (lane & 31));
+            } else {
+                pb[rr] = 0u;
+                px[rr] = 0u;
+            }
+        }
+    };
+    // the next chunk's theta (staging layout) and dt, lam (wave 0: lanes over tokens)
+    float rgTh[kPrefetchTheta ? TH : 1], rgDt[TPL], rgLam[TPL];
+    auto fetch_scalars = [&](int cstart) {
+#pragma unroll
+        for (int k = 0; k < (kPrefetchTheta ? TH : 0); ++k) {
+            const int e = tid + k * kThreads;
+            const int t = np ? e / np : 0, i = e - t * np;
+            rgTh[k] = (e < Q * np && cstart + t < T1) ? thg[(size_t)(cstart + t) * H * np + i] : 0.f;
+        }
+        if (w == 0) {
+#pragma unroll
+            for (int k = 0; k < TPL; ++k) {
+                const int t = lane * TPL + k;
+                const bool ok = t < Q && cstart + t < T1;
+                rgDt[k] = ok ? dtg[(size_t)(cstart + t) * H] : 0.f;
+                rgLam[k] = ok ? lamg[(size_t)(cstart + t) * H] : 0.f;
+            }
+        }
+    };
+
+#pragma unroll
+    for (int d = 0; d < D; ++d) fetch(d, rgB[d], rgX[d]);
+    fetch_scalars(T0);
+
     bf16x8 cq[TPW][4];                                   // C tiles (raw bf16 first, then biased + turned)
     f32x4 yacc[TPW][4];                                  // Y^T tiles
-    uint32_t pfB[RPW], pfX[RPW];                         // next key block's raw B and x pairs
 
-    for (int c0 = T0; c0 < T1; c0 += Q) {
+    // turn a ring slot's rows and write key block J's LDS tiles
+    auto store_block = [&](int J, int c0, int nvalid, const uint32_t (&pb)[kRPW], const uint32_t (&px)[kRPW]) {
+        char* buf = smem + (J & 1) * kBufBytes;
+        uint32_t bv0[kRPW / 2], bv1[kRPW / 2], xt0[kRPW / 2], xt1[kRPW / 2];
+#pragma unroll
+        for (int rr = 0; rr < kRPW; ++rr) {
+            const int jb = kRPW * w + rr;                // row within the block
+            const int j = kKB * J + jb;
+            const int t = j / R, r = j % R;
+            const bool valid = t < nvalid;               // uniform
+            float b0 = 0.f, b1 = 0.f;
+            if (valid) {
+                const f16x2 c = sCS[t * 64 + lane];
+                const float cs = (float)c[0], sn = (float)c[1];
+                const float e = lo_f(pb[rr]) + bb[r].x, o = hi_f(pb[rr]) + bb[r].y;
+                b0 = e * cs - o * sn;
+                b1 = e * sn + o * cs;
+            }
+            const uint32_t bt = pack2(b0, b1);
+            if (kFullMode) *reinterpret_cast<uint32_t*>(buf + bn_off(jb, lane >> 2) + (lane & 3) * 4) = bt;
+            const float vv = sV[t];
+            const uint32_t bv = pack2(b0 * vv, b1 * vv);
+            const uint32_t xr = px[rr];
+            if (rr & 1) {
+                bv0[rr >> 1] |= bv << 16;
+                bv1[rr >> 1] |= bv & 0xffff0000u;
+                xt0[rr >> 1] |= xr << 16;
+                xt1[rr >> 1] |= xr & 0xffff0000u;
+            } else {
+                bv0[rr >> 1] = bv & 0xffffu;
+                bv1[rr >> 1] = bv >> 16;
+                xt0[rr >> 1] = xr & 0xffffu;
+                xt1[rr >> 1] = xr >> 16;
+            }
+        }
+        // this wave's 4 rows are half (w & 1) of 16-byte group w / 2 of each 32-row line
+        const int grp = w >> 1, half = w & 1;
+        char* bvt = buf + kBnBytes;
+        char* xtt = buf + kBnBytes + kBvBytes;
+        *reinterpret_cast<uint2*>(bvt + q4_off(2 * lane, grp) + 8 * half) = uint2{bv0[0], bv0[1]};
+        *reinterpret_cast<uint2*>(bvt + q4_off(2 * lane + 1, grp) + 8 * half) = uint2{bv1[0], bv1[1]};
+        if (lane < 32) {
+            *reinterpret_cast<uint2*>(xtt + q4_off(2 * lane, grp) + 8 * half) = uint2{xt0[0], xt0[1]};
+            *reinterpret_cast<uint2*>(xtt + q4_off(2 * lane + 1, grp) + 8 * half) = uint2{xt1[0], xt1[1]};
+        }
+    };
+
+    // ---- chunk loop ------------------------------------------------------------------------
+    int cidx = 0;
+    for (int c0 = T0; c0 < T1; c0 += Q, ++cidx) {
         const int nvalid = min(Q, T1 - c0);
 
-        // global loads of the producer rows of key block J into pfB / pfX
-        auto load_block = [&](int J) {
-#pragma unroll
-            for (int rr = 0; rr < RPW; ++rr) {
-                const int j = kKB * J + RPW * w + rr;
-                const int t = j / R, r = j % R;
-                const bool valid = t < nvalid;
-                const size_t tok = tokbase + c0 + (valid ? t : 0);
-                pfB[rr] = valid ? *reinterpret_cast<const uint32_t*>(Bg + (((tok * a.G + g) * R + r) * kN + 2 * lane)) : 0u;
-                pfX[rr] = (valid && lane < 32) ? *reinterpret_cast<const uint32_t*>(Xg + (((tok * H + h) * R + r) * kP + 2 * lane)) : 0u;
-            }
-        };
-        // turn the prefetched rows and write key block J's LDS tiles
-        auto store_block = [&](int J) {
-            char* buf = smem + (J & 1) * kBufBytes;
-            uint32_t bv0[RPW / 2], bv1[RPW / 2], xt0[RPW / 2], xt1[RPW / 2];
-#pragma unroll
-            for (int rr = 0; rr < RPW; ++rr) {
-                const int jb = RPW * w + rr;             // row within the block
-                const int j = kKB * J + jb;
-                const int t = j / R, r = j % R;
-                const bool valid = t < nvalid;
-                float b0 = lo_f(pfB[rr]) + bb[r].x, b1 = hi_f(pfB[rr]) + bb[r].y;
-                {
-                    const float2 c = sCS[t * 64 + lane];
-                    const float e = b0, o = b1;
-                    b0 = valid ? e * c.x - o * c.y : 0.f;
-                    b1 = valid ? e * c.y + o * c.x : 0.f;
-                }
-                const uint32_t bt = pack2(b0, b1);
-                if (kFullMode) {
-                    *reinterpret_cast<uint32_t*>(buf + bn_off(jb, lane >> 2) + (lane & 3) * 4) = bt;
-                    if (valid && c0 + t == L - 1 && last_seg && a.Bp1) {
-                        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.Bp1) + ((size_t)bh * R + r) * kN + 2 * lane) = bt;
-                        if (lane < 32 && a.xp1)
-                            *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.xp1) + ((size_t)bh * R + r) * kP + 2 * lane) = pfX[rr];
-                    }
-                }
-                const float vv = sV[t];
-                const uint32_t bv = pack2(b0 * vv, b1 * vv);
-                const uint32_t xr = pfX[rr];
-                if (rr & 1) {
-                    bv0[rr >> 1] |= bv << 16;
-                    bv1[rr >> 1] |= bv & 0xffff0000u;
-                    xt0[rr >> 1] |= xr << 16;
-                    xt1[rr >> 1] |= xr & 0xffff0000u;
-                } else {
-                    bv0[rr >> 1] = bv & 0xffffu;
-                    bv1[rr >> 1] = bv >> 16;
-                    xt0[rr >> 1] = xr & 0xffffu;
-                    xt1[rr >> 1] = xr >> 16;
-                }
-            }
-            // this wave's rows form group (RPW w) / 8 of each 32-row line, half (RPW w / 4) & 1 when RPW = 4
-            const int grp = (RPW * w) >> 3, half = ((RPW * w) >> 2) & 1;
-            char* bvt = buf + kBnBytes;
-            char* xtt = buf + kBnBytes + kBvBytes;
-            if constexpr (RPW == 8) {
-                *reinterpret_cast<uint4*>(bvt + q4_off(2 * lane, grp)) = uint4{bv0[0], bv0[1], bv0[2], bv0[3]};
-                *reinterpret_cast<uint4*>(bvt + q4_off(2 * lane + 1, grp)) = uint4{bv1[0], bv1[1], bv1[2], bv1[3]};
-                if (lane < 32) {
-                    *reinterpret_cast<uint4*>(xtt + q4_off(2 * lane, grp)) = uint4{xt0[0], xt0[1], xt0[2], xt0[3]};
-                    *reinterpret_cast<uint4*>(xtt + q4_off(2 * lane + 1, grp)) = uint4{xt1[0], xt1[1], xt1[2], xt1[3]};
-                }
-            } else {
-                *reinterpret_cast<uint2*>(bvt + q4_off(2 * lane, grp) + 8 * half) = uint2{bv0[0], bv0[1]};
-                *reinterpret_cast<uint2*>(bvt + q4_off(2 * lane + 1, grp) + 8 * half) = uint2{bv1[0], bv1[1]};
-                if (lane < 32) {
-                    *reinterpret_cast<uint2*>(xtt + q4_off(2 * lane, grp) + 8 * half) = uint2{xt0[0], xt0[1]};
-                    *reinterpret_cast<uint2*>(xtt + q4_off(2 * lane + 1, grp) + 8 * half) = uint2{xt1[0], xt1[1]};
-                }
-            }
-        };
-
-        // (A) state snapshot; every global load of the chunk set-up in flight at once
+        // (A) state snapshot; C rows straight into the operand registers; the
+        //     prefetched scalars into LDS; wave 0 scans log alpha
         if (kFullMode) {
 #pragma unroll
-            for (int i = 0; i < NNT; ++i) {
-                const int nb = 16 * (NNT * w + i) + 4 * g4;
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    const int p = 16 * pt + l16;
-                    *reinterpret_cast<uint2*>(smem + LY::hs + hs_off(p, nb >> 3) + ((nb >> 2) & 1) * 8) =
-                        uint2{pack2(hacc[i][pt][0], hacc[i][pt][1]), pack2(hacc[i][pt][2], hacc[i][pt][3])};
-                }
+            for (int pt = 0; pt < 4; ++pt) {
+                const int p = 16 * pt + l16;
+                *reinterpret_cast<uint2*>(smem + LY::hs + hs_off(p, nb >> 3) + ((nb >> 2) & 1) * 8) =
+                    uint2{pack2(hacc[pt][0], hacc[pt][1]), pack2(hacc[pt][2], hacc[pt][3])};
             }
-            // raw C rows of this wave's query tiles, straight into the operand registers
 #pragma unroll
             for (int k = 0; k < TPW; ++k) {
-                const int qt = query_tile<NT, NW>(w, k);
+                const int qt = query_tile<NT>(w, k);
                 const int qi = 16 * (qt < 0 ? 0 : qt) + l16;
                 const int t = qi / R, r = qi % R;
-                const bool valid = qt >= 0 && t < nvalid;
-                const size_t crow = (((tokbase + c0 + (valid ? t : 0)) * a.G + g) * R + r) * kN;
+                const uint16_t* crow = Cg + (size_t)(c0 + min(t, nvalid - 1)) * bstride + r * kN + 8 * g4;
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const uint4 raw = valid ? *reinterpret_cast<const uint4*>(Cg + crow + 32 * ks + 8 * g4) : uint4{0, 0, 0, 0};
-                    cq[k][ks] = __builtin_bit_cast(bf16x8, raw);
-                }
+                for (int ks = 0; ks < 4; ++ks)
+                    cq[k][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(crow + 32 * ks));
             }
         }
-        load_block(0);
-        for (int e = tid; e < Q * np; e += kThreads) {
-            const int t = e / np, i = e - t * np;
-            stage[e] = t < nvalid ? a.theta[((tokbase + c0 + t) * H + h) * np + i] : 0.f;
+        if constexpr (kPrefetchTheta) {
+#pragma unroll
+            for (int k = 0; k < TH; ++k) {
+                const int e = tid + k * kThreads;
+                if (e < Q * np) stage[e] = rgTh[k];
+            }
+        } else {
+            for (int e = tid; e < Q * np; e += kThreads) {
+                const int t = e / np, i = e - t * np;
+                stage[e] = t < nvalid ? thg[(size_t)(c0 + t) * H * np + i] : 0.f;
+            }
         }
-        // (B) wave 0: step sizes, chunk-local cumulative log decay, trapezoid weights
         if (w == 0) {
-            constexpr int TPL = Q > 64 ? Q / 64 : 1;          // tokens per lane
             float la[TPL], gm[TPL], dl[TPL];
             float lsum = 0.f;
 #pragma unroll
             for (int k = 0; k < TPL; ++k) {
                 const int t = lane * TPL + k;
-                la[k] = 0.f; gm[k] = 0.f; dl[k] = 0.f;
-                float dt = 0.f;
-                if (t < nvalid) {
-                    const size_t ti = (tokbase + c0 + t) * H + h;
-                    dt = a.dt[ti];
-                    const float lm = a.lam[ti];
-                    la[k] = -dt * ah;
-                    gm[k] = lm * dt;
-                    dl[k] = dt * (1.f - lm);
-                }
+                const float dt = rgDt[k], lm = rgLam[k];
+                la[k] = -dt * ah;
+                gm[k] = lm * dt;
+                dl[k] = dt * (1.f - lm);
                 if (t < Q) sDt[t] = dt;
                 lsum += la[k];
                 la[k] = lsum;                                  // lane-local inclusive prefix
@@ -372,10 +398,7 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma_kernel(ScanArgs a) {
             const float incl = group_scan<64>(lsum, lane);
             const float excl = incl - lsum;
             float dnext = 0.f;                                 // d of the token after the chunk
-            if (c0 + Q < L) {
-                const size_t ti = (tokbase + c0 + Q) * H + h;
-                dnext = a.dt[ti] * (1.f - a.lam[ti]);
-            }
+            if (c0 + Q < L) dnext = dtg[(size_t)(c0 + Q) * H] * (1.f - lamg[(size_t)(c0 + Q) * H]);
             const float tot = __shfl(incl, 63);
             const float le = tot * kLog2e;                     // l_e (padded tokens add 0)
             const float nx = __shfl_down(dl[0], 1);
@@ -394,13 +417,18 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma_kernel(ScanArgs a) {
             if (lane == 0) sMisc[0] = le;
             lam_sum += tot;
         }
+        // the next chunk's scalars are in flight during this chunk
+        fetch_scalars(c0 + Q);
         __syncthreads();
-        // (C) angles: threads (pair i, part k) scan dt * theta over the chunk
+
+        // (B) angles: threads (pair i, part k) scan dt * theta over the chunk;
+        //     pair weights W(t, s) for s <= t
         {
             const int tpp = np <= 32 ? 16 : 8;
-            const int i = tid / tpp, k = tid % tpp;
-            if (i < np && tid < kThreads) {
-                const int tpt = Q / tpp;
+            const int npr = kThreads / tpp;                    // pairs per round
+            const int k = tid % tpp;
+            const int tpt = Q / tpp;
+            for (int i = tid / tpp; i < np; i += npr) {
                 float loc = 0.f;
                 for (int t = k * tpt; t < (k + 1) * tpt; ++t) loc += sDt[t] * stage[t * np + i];
                 const float incl = tpp == 16 ? group_scan<16>(loc, k) : group_scan<8>(loc, k);
@@ -409,37 +437,25 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma_kernel(ScanArgs a) {
                     run += sDt[t] * stage[t * np + i];
                     float sn, cs;
                     __sincosf(run, &sn, &cs);
-                    sCS[t * 64 + i] = float2{cs, sn};
+                    sCS[t * 64 + i] = f16x2{(_Float16)cs, (_Float16)sn};
                 }
                 if (k == tpp - 1) sPhic[i] = wrap_2pi(run);
             }
-            if (NW == 4 && np > 32) {
-                // 8 threads per pair cover 32 pairs per 256 threads: the rest in a second round
-                const int i2 = i + kThreads / tpp;
-                if (i2 < np) {
-                    const int tpt = Q / tpp;
-                    float loc = 0.f;
-                    for (int t = k * tpt; t < (k + 1) * tpt; ++t) loc += sDt[t] * stage[t * np + i2];
-                    const float incl = group_scan<8>(loc, k);
-                    float run = sPhic[i2] + incl - loc;
-                    for (int t = k * tpt; t < (k + 1) * tpt; ++t) {
-                        run += sDt[t] * stage[t * np + i2];
-                        float sn, cs;
-                        __sincosf(run, &sn, &cs);
-                        sCS[t * 64 + i2] = float2{cs, sn};
-                    }
-                    if (k == tpp - 1) sPhic[i2] = wrap_2pi(run);
+            if (kFullMode) {
+                for (int e = tid; e < Q * Q; e += kThreads) {
+                    const int t = e / Q, s = e - t * Q;
+                    if (s <= t) sW[tri(t, s)] = (_Float16)(exp2f(sL2[t] - sL2[s]) * (sGam[s] + (s < t ? sDelS[s] : 0.f)));
                 }
             }
         }
         __syncthreads();
         const float le2 = sMisc[0];
 
-        // (D) C tiles: bias and turn in place; carry readout Y^T = exp(l_t) Hf Ct^T
+        // (C) C tiles: bias and turn in place; carry readout Y^T = exp(l_t) Hf Ct^T
         if (kFullMode) {
 #pragma unroll
             for (int k = 0; k < TPW; ++k) {
-                const int qt = query_tile<NT, NW>(w, k);
+                const int qt = query_tile<NT>(w, k);
                 const int qi = 16 * (qt < 0 ? 0 : qt) + l16;
                 const int t = qi / R, r = qi % R;
                 const bool valid = qt >= 0 && t < nvalid;
@@ -449,18 +465,19 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma_kernel(ScanArgs a) {
                     const uint4 raw = __builtin_bit_cast(uint4, cq[k][ks]);
                     const float4 b0 = *reinterpret_cast<const float4*>(sCb + r * kN + n0);
                     const float4 b1 = *reinterpret_cast<const float4*>(sCb + r * kN + n0 + 4);
-                    float v[8] = {lo_f(raw.x) + b0.x, hi_f(raw.x) + b0.y, lo_f(raw.y) + b0.z, hi_f(raw.y) + b0.w,
-                                  lo_f(raw.z) + b1.x, hi_f(raw.z) + b1.y, lo_f(raw.w) + b1.z, hi_f(raw.w) + b1.w};
-#pragma unroll
-                    for (int pp = 0; pp < 4; ++pp) {
-                        const float2 c = sCS[t * 64 + n0 / 2 + pp];
-                        const float e = v[2 * pp], o = v[2 * pp + 1];
-                        v[2 * pp] = e * c.x - o * c.y;
-                        v[2 * pp + 1] = e * c.y + o * c.x;
-                    }
+                    const uint4 csr = *reinterpret_cast<const uint4*>(sCS + t * 64 + n0 / 2);
+                    const uint32_t csw[4] = {csr.x, csr.y, csr.z, csr.w};
+                    const float v[8] = {lo_f(raw.x) + b0.x, hi_f(raw.x) + b0.y, lo_f(raw.y) + b0.z, hi_f(raw.y) + b0.w,
+                                        lo_f(raw.z) + b1.x, hi_f(raw.z) + b1.y, lo_f(raw.w) + b1.z, hi_f(raw.w) + b1.w};
                     bf16x8 q;
 #pragma unroll
-                    for (int m = 0; m < 8; ++m) q[m] = valid ? (bf16)v[m] : (bf16)0.f;
+                    for (int pp = 0; pp < 4; ++pp) {
+                        const f16x2 c = __builtin_bit_cast(f16x2, csw[pp]);
+                        const float cs = (float)c[0], sn = (float)c[1];
+                        const float e = v[2 * pp], o = v[2 * pp + 1];
+                        q[2 * pp] = valid ? (bf16)(e * cs - o * sn) : (bf16)0.f;
+                        q[2 * pp + 1] = valid ? (bf16)(e * sn + o * cs) : (bf16)0.f;
+                    }
                     cq[k][ks] = q;
                 }
             }
@@ -468,7 +485,7 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma_kernel(ScanArgs a) {
             float sc[TPW];
 #pragma unroll
             for (int k = 0; k < TPW; ++k) {
-                const int qt = query_tile<NT, NW>(w, k);
+                const int qt = query_tile<NT>(w, k);
                 sc[k] = exp2f(sL2[(16 * (qt < 0 ? 0 : qt) + l16) / R]);
             }
 #pragma unroll
@@ -491,127 +508,122 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma_kernel(ScanArgs a) {
         {
             const float f = exp2f(le2);
 #pragma unroll
-            for (int i = 0; i < NNT; ++i)
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt) hacc[i][pt] = hacc[i][pt] * f;
+            for (int pt = 0; pt < 4; ++pt) hacc[pt] = hacc[pt] * f;
         }
-        store_block(0);
+        store_block(0, c0, nvalid, rgB[0], rgX[0]);
         __syncthreads();
 
-        // (E) key blocks: prefetch J + 1, consume J, write J + 1
+        // (D) key blocks: ring slot J % D holds block J; once block J is in LDS
+        //     the slot is refilled with block J + D (which may be the next chunk's)
 #pragma unroll 1
-        for (int J = 0; J < NKB; ++J) {
-            if (J + 1 < NKB) load_block(J + 1);
-            const char* buf = smem + (J & 1) * kBufBytes;
-            const char* bvb = buf + kBnBytes;
-            const char* xtb = buf + kBnBytes + kBvBytes;
-            if (kFullMode) {
-                // Operand loads are shared by this wave's query tiles, so the loops
-                // run operand-outer, tile-inner: each LDS operand is read once.
-                const int ka = 2 * J;                            // key tiles ka, ka + 1 of this block
-                bool act[TPW], hasb[TPW];
-                int tq[TPW];
+        for (int J0 = 0; J0 < NKB; J0 += D) {
 #pragma unroll
-                for (int k = 0; k < TPW; ++k) {
-                    const int qt = query_tile<NT, NW>(w, k);
-                    act[k] = qt >= ka;
-                    hasb[k] = qt >= ka + 1;
-                    tq[k] = (16 * (qt < 0 ? 0 : qt) + l16) / R;
-                }
-                // (1) scores S^T = Bt C^T for key tile a and b
-                f32x4 s0[TPW], s1[TPW];
+            for (int d = 0; d < D; ++d) {
+                const int J = J0 + d;
+                fetch(cidx * NKB + J + D, rgB[d], rgX[d]);
+                const char* buf = smem + (J & 1) * kBufBytes;
+                const char* bvb = buf + kBnBytes;
+                const char* xtb = buf + kBnBytes + kBvBytes;
+                if (kFullMode) {
+                    // key tiles ka, ka + 1 (the block's rows) against this wave's query
+                    // tiles.  One key tile's operands are live at a time and shared by
+                    // the query tiles; fences keep the phases apart (register pressure).
+                    const int ka = 2 * J;
+                    f32x4 s0[TPW], s1[TPW];
+                    {
+                        bf16x8 op[4];
 #pragma unroll
-                for (int k = 0; k < TPW; ++k) { s0[k] = f32x4{0.f, 0.f, 0.f, 0.f}; s1[k] = s0[k]; }
+                        for (int ks = 0; ks < 4; ++ks)
+                            op[ks] = *reinterpret_cast<const bf16x8*>(buf + bn_off(l16, 4 * ks + g4));
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const bf16x8 av = *reinterpret_cast<const bf16x8*>(buf + bn_off(l16, 4 * ks + g4));
+                        for (int k = 0; k < TPW; ++k) {
+                            s0[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+                            if (query_tile<NT>(w, k) >= ka) {           // uniform
 #pragma unroll
-                    for (int k = 0; k < TPW; ++k)
-                        if (act[k]) s0[k] = mfma(av, cq[k][ks], s0[k]);
-                }
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const bf16x8 av = *reinterpret_cast<const bf16x8*>(buf + bn_off(16 + l16, 4 * ks + g4));
-#pragma unroll
-                    for (int k = 0; k < TPW; ++k)
-                        if (hasb[k]) s1[k] = mfma(av, cq[k][ks], s1[k]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                // (2) mask: key rows 16 ka + 4 g4 + m (tile a) and 16 ka + 16 + 4 g4 + m (tile b)
-                bf16x8 bop[TPW];
-#pragma unroll
-                for (int k = 0; k < TPW; ++k) {
-                    const int t = tq[k];
-                    const float l2t = sL2[t];
-                    auto weight = [&](int sidx) {
-                        return sidx <= t ? exp2f(l2t - sL2[sidx]) * (sGam[sidx] + (sidx < t ? sDelS[sidx] : 0.f)) : 0.f;
-                    };
-                    float wa[4], wb[4];
-                    if constexpr (R == 4) {
-                        const float x0 = weight(8 * J + g4), x1 = weight(8 * J + 4 + g4);
-#pragma unroll
-                        for (int m = 0; m < 4; ++m) { wa[m] = x0; wb[m] = x1; }
-                    } else if constexpr (R == 2) {
-#pragma unroll
-                        for (int m = 0; m < 4; m += 2) {
-                            const float x0 = weight((32 * J + 4 * g4 + m) / 2);
-                            const float x1 = weight((32 * J + 16 + 4 * g4 + m) / 2);
-                            wa[m] = wa[m + 1] = x0;
-                            wb[m] = wb[m + 1] = x1;
+                                for (int ks = 0; ks < 4; ++ks) s0[k] = mfma(op[ks], cq[k][ks], s0[k]);
+                            }
                         }
-                    } else {
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    {
+                        bf16x8 op[4];
+#pragma unroll
+                        for (int ks = 0; ks < 4; ++ks)
+                            op[ks] = *reinterpret_cast<const bf16x8*>(buf + bn_off(16 + l16, 4 * ks + g4));
+#pragma unroll
+                        for (int k = 0; k < TPW; ++k) {
+                            s1[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+                            if (query_tile<NT>(w, k) > ka) {            // uniform
+#pragma unroll
+                                for (int ks = 0; ks < 4; ++ks) s1[k] = mfma(op[ks], cq[k][ks], s1[k]);
+                            }
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    // S'^T = W o S^T: W of key rows 32 J + 4 g4 + m (tile a) and
+                    // 32 J + 16 + 4 g4 + m (tile b), rounded to bf16 as the B operand
+                    bf16x8 bop[TPW];
+#pragma unroll
+                    for (int k = 0; k < TPW; ++k) {
+                        const int qt = query_tile<NT>(w, k);
+                        const int t = (16 * (qt < 0 ? 0 : qt) + l16) / R;
+                        const int rt = tri(t, 0);
+                        float wa[4], wb[4];
+#pragma unroll
+                        for (int m = 0; m < 4; m += RSTEP) {
+                            const int sa = (32 * J + 4 * g4 + m) / R, sb = (32 * J + 16 + 4 * g4 + m) / R;
+                            const float xa = sa <= t ? (float)sW[rt + sa] : 0.f;
+                            const float xb = sb <= t ? (float)sW[rt + sb] : 0.f;
+#pragma unroll
+                            for (int q = 0; q < RSTEP; ++q) { wa[m + q] = xa; wb[m + q] = xb; }
+                        }
 #pragma unroll
                         for (int m = 0; m < 4; ++m) {
-                            wa[m] = weight(32 * J + 4 * g4 + m);
-                            wb[m] = weight(32 * J + 16 + 4 * g4 + m);
+                            bop[k][m] = (bf16)(s0[k][m] * wa[m]);
+                            bop[k][4 + m] = (bf16)(s1[k][m] * wb[m]);
                         }
                     }
+                    __builtin_amdgcn_sched_barrier(0);
+                    // Y^T += X^T S'^T, X^T read in the k order of S'^T:
+                    // keys 4 g4 + 0..3 of tile a, then of tile b
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        bop[k][m] = (bf16)(s0[k][m] * wa[m]);
-                        bop[k][4 + m] = (bf16)(s1[k][m] * wb[m]);
+                    for (int pt = 0; pt < 4; ++pt) {
+                        const int p = 16 * pt + l16;
+                        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(xtb + q4_off(p, g4 >> 1) + (g4 & 1) * 8);
+                        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(xtb + q4_off(p, 2 + (g4 >> 1)) + (g4 & 1) * 8);
+                        const bf16x8 xo = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+                        for (int k = 0; k < TPW; ++k)
+                            if (query_tile<NT>(w, k) >= ka) yacc[k][pt] = mfma(xo, bop[k], yacc[k][pt]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                // state: Hf^T[n-tile w] += (v Bt)^T X over the block's 32 rows
+                {
+                    const bf16x8 av = *reinterpret_cast<const bf16x8*>(bvb + q4_off(16 * w + l16, g4));
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt) {
+                        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(xtb + q4_off(16 * pt + l16, g4));
+                        hacc[pt] = mfma(av, bv, hacc[pt]);
                     }
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                // (3) Y^T += X^T S'^T; X^T read with the k permutation of S'^T:
-                //     keys 4 g4 + 0..3 of tile a, then of tile b
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    const int p = 16 * pt + l16;
-                    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(xtb + q4_off(p, g4 >> 1) + (g4 & 1) * 8);
-                    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(xtb + q4_off(p, 2 + (g4 >> 1)) + (g4 & 1) * 8);
-                    const bf16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-                    for (int k = 0; k < TPW; ++k)
-                        if (act[k]) yacc[k][pt] = mfma(av, bop[k], yacc[k][pt]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+                if (J + 1 < NKB) store_block(J + 1, c0, nvalid, rgB[(d + 1) % D], rgX[(d + 1) % D]);
+                __syncthreads();
             }
-            // state: Hf^T[wave's n-tiles] += (v Bt)^T X over the block's 32 rows
-#pragma unroll
-            for (int i = 0; i < NNT; ++i) {
-                const bf16x8 av = *reinterpret_cast<const bf16x8*>(bvb + q4_off(16 * (NNT * w + i) + l16, g4));
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    const bf16x8 bv = *reinterpret_cast<const bf16x8*>(xtb + q4_off(16 * pt + l16, g4));
-                    hacc[i][pt] = mfma(av, bv, hacc[i][pt]);
-                }
-            }
-            if (J + 1 < NKB) store_block(J + 1);
-            __syncthreads();
         }
+        // the next chunk's block 0 now sits in ring slot 0
 
-        // (F) outputs of this chunk
+        // (E) outputs of this chunk
         if (kFullMode) {
-            bf16* yg = static_cast<bf16*>(a.y);
+            bf16* yg = static_cast<bf16*>(a.y) + (tokbase * H + h) * R * kP;
 #pragma unroll
             for (int k = 0; k < TPW; ++k) {
-                const int qt = query_tile<NT, NW>(w, k);
+                const int qt = query_tile<NT>(w, k);
                 if (qt < 0) continue;
                 const int qi = 16 * qt + l16;
                 const int t = qi / R, r = qi % R;
                 if (t >= nvalid) continue;
-                bf16* yrow = yg + (((tokbase + c0 + t) * H + h) * R + r) * kP;
+                bf16* yrow = yg + (size_t)(c0 + t) * xstride + r * kP;
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) {
                     bf16x4 o;
@@ -626,37 +638,48 @@ __global__ __launch_bounds__(64 * NW) void scan_mfma_kernel(ScanArgs a) {
     // ---- end of the stream / segment ----------------------------------------------------------
     if (!kFullMode) {
 #pragma unroll
-        for (int i = 0; i < NNT; ++i) {
-            const int nb = 16 * (NNT * w + i) + 4 * g4;
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                const int p = 16 * pt + l16;
-                *reinterpret_cast<float4*>(wsHloc + (ss * kP + p) * kN + nb) =
-                    float4{hacc[i][pt][0], hacc[i][pt][1], hacc[i][pt][2], hacc[i][pt][3]};
-            }
+        for (int pt = 0; pt < 4; ++pt) {
+            const int p = 16 * pt + l16;
+            *reinterpret_cast<float4*>(wsHloc + (ss * kP + p) * kN + nb) = float4{hacc[pt][0], hacc[pt][1], hacc[pt][2], hacc[pt][3]};
         }
         if (tid == 0) wsLam[ss] = lam_sum;
         for (int i = tid; i < np; i += kThreads) wsDphi[ss * np + i] = sPhic[i];
     } else if (last_seg) {
         if (a.h1) {
 #pragma unroll
-            for (int i = 0; i < NNT; ++i) {
-                const int nb = 16 * (NNT * w + i) + 4 * g4;
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    const int p = 16 * pt + l16;
-                    const size_t o = ((size_t)bh * kP + p) * kN + nb;
-                    if (a.st_bf16)
-                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.h1) + o) =
-                            uint2{pack2(hacc[i][pt][0], hacc[i][pt][1]), pack2(hacc[i][pt][2], hacc[i][pt][3])};
-                    else
-                        *reinterpret_cast<float4*>(static_cast<float*>(a.h1) + o) =
-                            float4{hacc[i][pt][0], hacc[i][pt][1], hacc[i][pt][2], hacc[i][pt][3]};
-                }
+            for (int pt = 0; pt < 4; ++pt) {
+                const int p = 16 * pt + l16;
+                const size_t o = ((size_t)bh * kP + p) * kN + nb;
+                if (a.st_bf16)
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.h1) + o) =
+                        uint2{pack2(hacc[pt][0], hacc[pt][1]), pack2(hacc[pt][2], hacc[pt][3])};
+                else
+                    *reinterpret_cast<float4*>(static_cast<float*>(a.h1) + o) = float4{hacc[pt][0], hacc[pt][1], hacc[pt][2], hacc[pt][3]};
             }
         }
         if (a.phi1)
             for (int i = tid; i < np; i += kThreads) a.phi1[(size_t)bh * np + i] = sPhic[i];
+        // previous write after the last token: its biased, turned B (angle = the
+        // final phase) and its x
+        if (a.Bp1 && a.xp1) {
+            const int t = L - 1;
+            for (int e = tid; e < R * kN / 2; e += kThreads) {
+                const int r = e / (kN / 2), i = e % (kN / 2);
+                const uint32_t raw = *reinterpret_cast<const uint32_t*>(Bg + (size_t)t * bstride + r * kN + 2 * i);
+                float b0 = lo_f(raw) + (a.Bb ? a.Bb[((size_t)h * R + r) * kN + 2 * i] : 0.f);
+                float b1 = hi_f(raw) + (a.Bb ? a.Bb[((size_t)h * R + r) * kN + 2 * i + 1] : 0.f);
+                if (i < np) {
+                    float sn, cs;
+                    sincosf(sPhic[i], &sn, &cs);
+                    const float e0 = b0;
+                    b0 = e0 * cs - b1 * sn;
+                    b1 = e0 * sn + b1 * cs;
+                }
+                *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.Bp1) + ((size_t)bh * R + r) * kN + 2 * i) = pack2(b0, b1);
+            }
+            for (int e = tid; e < R * kP; e += kThreads)
+                static_cast<uint16_t*>(a.xp1)[(size_t)bh * R * kP + e] = Xg[(size_t)t * xstride + e];
+        }
     }
 }
 
@@ -716,23 +739,22 @@ __global__ __launch_bounds__(256) void carry_pass_kernel(ScanArgs a) {
 
 template <int R, int Q>
 hipError_t launch_rq(const ScanArgs& a, hipStream_t st) {
-    constexpr int NW = 8;
     const size_t lds = Layout<Q>::total;
     const int nblk = a.b * a.H * a.nseg;
     hipError_t e;
     if (a.nseg > 1) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_mfma_kernel<R, Q, NW, kSummary>),
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_mfma_kernel<R, Q, kSummary>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((scan_mfma_kernel<R, Q, NW, kSummary>), dim3(nblk), dim3(64 * NW), lds, st, a);
+        hipLaunchKernelGGL((scan_mfma_kernel<R, Q, kSummary>), dim3(nblk), dim3(kThreads), lds, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL(carry_pass_kernel, dim3((kP * kN / 2 + 255) / 256, a.b * a.H), dim3(256), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_mfma_kernel<R, Q, NW, kFull>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_mfma_kernel<R, Q, kFull>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_mfma_kernel<R, Q, NW, kFull>), dim3(nblk), dim3(64 * NW), lds, st, a);
+    hipLaunchKernelGGL((scan_mfma_kernel<R, Q, kFull>), dim3(nblk), dim3(kThreads), lds, st, a);
     return hipGetLastError();
 }
 
