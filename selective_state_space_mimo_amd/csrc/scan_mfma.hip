@@ -256,14 +256,17 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
     uint32_t rgB[D][kRPW], rgX[D][kRPW];
     auto fetch = [&](int gb, uint32_t (&pb)[kRPW], uint32_t (&px)[kRPW]) {
         const int c = gb / NKB, J = gb % NKB;
+        const int j0 = kKB * J + kRPW * w;                 // first row of this wave
+        const int t0 = T0 + c * Q + j0 / R;                // its token (uniform)
+        const uint16_t* bp = Bg + (size_t)t0 * bstride + 2 * lane;
+        const uint16_t* xq = Xg + (size_t)t0 * xstride + 2 * (lane & 31);
 #pragma unroll
         for (int rr = 0; rr < kRPW; ++rr) {
-            const int j = kKB * J + kRPW * w + rr;
-            const int t = T0 + c * Q + j / R;            // token (uniform)
-            const int r = j % R;
-            if (t < T1) {
-                pb[rr] = *reinterpret_cast<const uint32_t*>(Bg + (size_t)t * bstride + r * kN + 2 * lane);
-                px[rr] = *reinterpret_cast<const uint32_t*>(Xg + (size_t)t * xstride + r * kP + 2 * (lane & 31));
+            const int dt_ = (j0 % R + rr) / R;              // token offset from t0 (compile time for R = 4)
+            const int r = (j0 + rr) % R;
+            if (t0 + dt_ < T1) {
+                pb[rr] = *reinterpret_cast<const uint32_t*>(bp + dt_ * bstride + r * kN);
+                px[rr] = *reinterpret_cast<const uint32_t*>(xq + dt_ * xstride + r * kP);
             } else {
                 pb[rr] = 0u;
                 px[rr] = 0u;
@@ -297,40 +300,51 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
     bf16x8 cq[TPW][4];                                   // C tiles (raw bf16 first, then biased + turned)
     f32x4 yacc[TPW][4];                                  // Y^T tiles
 
-    // turn a ring slot's rows and write key block J's LDS tiles
-    auto store_block = [&](int J, int c0, int nvalid, const uint32_t (&pb)[kRPW], const uint32_t (&px)[kRPW]) {
+    // turn a ring slot's rows and write key block J's LDS tiles.  This wave's
+    // rows 4 w .. 4 w + 3 of the block cover TOKW tokens of R ranks each; the
+    // angle and v are read once per token.
+    constexpr int TOKW = kRPW / R > 0 ? kRPW / R : 1;     // tokens per wave and block
+    constexpr int RPT = kRPW / TOKW;                       // rows per token here (= R, or 4 when R > 4)
+    auto store_block = [&](int J, int nvalid, const uint32_t (&pb)[kRPW], const uint32_t (&px)[kRPW]) {
         char* buf = smem + (J & 1) * kBufBytes;
-        uint32_t bv0[kRPW / 2], bv1[kRPW / 2], xt0[kRPW / 2], xt1[kRPW / 2];
+        uint32_t bvw[kRPW];                                // (v Bt) pair of row rr, bf16x2
 #pragma unroll
-        for (int rr = 0; rr < kRPW; ++rr) {
-            const int jb = kRPW * w + rr;                // row within the block
-            const int j = kKB * J + jb;
-            const int t = j / R, r = j % R;
-            const bool valid = t < nvalid;               // uniform
-            float b0 = 0.f, b1 = 0.f;
-            if (valid) {
+        for (int tk = 0; tk < TOKW; ++tk) {
+            const int j0 = kKB * J + kRPW * w + tk * RPT;     // first row of this token
+            const int t = j0 / R;
+            if (t < nvalid) {                              // uniform
                 const f16x2 c = sCS[t * 64 + lane];
                 const float cs = (float)c[0], sn = (float)c[1];
-                const float e = lo_f(pb[rr]) + bb[r].x, o = hi_f(pb[rr]) + bb[r].y;
-                b0 = e * cs - o * sn;
-                b1 = e * sn + o * cs;
-            }
-            const uint32_t bt = pack2(b0, b1);
-            if (kFullMode) *reinterpret_cast<uint32_t*>(buf + bn_off(jb, lane >> 2) + (lane & 3) * 4) = bt;
-            const float vv = sV[t];
-            const uint32_t bv = pack2(b0 * vv, b1 * vv);
-            const uint32_t xr = px[rr];
-            if (rr & 1) {
-                bv0[rr >> 1] |= bv << 16;
-                bv1[rr >> 1] |= bv & 0xffff0000u;
-                xt0[rr >> 1] |= xr << 16;
-                xt1[rr >> 1] |= xr & 0xffff0000u;
+                const float vv = sV[t];
+#pragma unroll
+                for (int q = 0; q < RPT; ++q) {
+                    const int rr = tk * RPT + q, r = (j0 + q) % R;
+                    const float e = lo_f(pb[rr]) + bb[r].x, o = hi_f(pb[rr]) + bb[r].y;
+                    const float b0 = e * cs - o * sn;
+                    const float b1 = e * sn + o * cs;
+                    if (kFullMode)
+                        *reinterpret_cast<uint32_t*>(buf + bn_off(kRPW * w + rr, lane >> 2) + (lane & 3) * 4) = pack2(b0, b1);
+                    bvw[rr] = pack2(b0 * vv, b1 * vv);
+                }
             } else {
-                bv0[rr >> 1] = bv & 0xffffu;
-                bv1[rr >> 1] = bv >> 16;
-                xt0[rr >> 1] = xr & 0xffffu;
-                xt1[rr >> 1] = xr >> 16;
+#pragma unroll
+                for (int q = 0; q < RPT; ++q) {
+                    const int rr = tk * RPT + q;
+                    if (kFullMode)
+                        *reinterpret_cast<uint32_t*>(buf + bn_off(kRPW * w + rr, lane >> 2) + (lane & 3) * 4) = 0u;
+                    bvw[rr] = 0u;
+                }
             }
+        }
+        // transpose in registers: row rr of the n = 2 lane (2 lane + 1) line is the
+        // low (high) half of bvw[rr]; same for x with p = 2 lane (2 lane + 1)
+        uint32_t bv0[kRPW / 2], bv1[kRPW / 2], xt0[kRPW / 2], xt1[kRPW / 2];
+#pragma unroll
+        for (int q = 0; q < kRPW / 2; ++q) {
+            bv0[q] = __builtin_amdgcn_perm(bvw[2 * q + 1], bvw[2 * q], 0x05040100u);
+            bv1[q] = __builtin_amdgcn_perm(bvw[2 * q + 1], bvw[2 * q], 0x07060302u);
+            xt0[q] = __builtin_amdgcn_perm(px[2 * q + 1], px[2 * q], 0x05040100u);
+            xt1[q] = __builtin_amdgcn_perm(px[2 * q + 1], px[2 * q], 0x07060302u);
         }
         // this wave's 4 rows are half (w & 1) of 16-byte group w / 2 of each 32-row line
         const int grp = w >> 1, half = w & 1;
@@ -458,7 +472,8 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
                 const int qt = query_tile<NT>(w, k);
                 const int qi = 16 * (qt < 0 ? 0 : qt) + l16;
                 const int t = qi / R, r = qi % R;
-                const bool valid = qt >= 0 && t < nvalid;
+                // rows of padded tokens (t >= nvalid) hold a clamped copy of a valid
+                // row: finite, and their outputs are never stored
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const int n0 = 32 * ks + 8 * g4;
@@ -475,8 +490,8 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
                         const f16x2 c = __builtin_bit_cast(f16x2, csw[pp]);
                         const float cs = (float)c[0], sn = (float)c[1];
                         const float e = v[2 * pp], o = v[2 * pp + 1];
-                        q[2 * pp] = valid ? (bf16)(e * cs - o * sn) : (bf16)0.f;
-                        q[2 * pp + 1] = valid ? (bf16)(e * sn + o * cs) : (bf16)0.f;
+                        q[2 * pp] = (bf16)(e * cs - o * sn);
+                        q[2 * pp + 1] = (bf16)(e * sn + o * cs);
                     }
                     cq[k][ks] = q;
                 }
@@ -510,7 +525,7 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) hacc[pt] = hacc[pt] * f;
         }
-        store_block(0, c0, nvalid, rgB[0], rgX[0]);
+        store_block(0, nvalid, rgB[0], rgX[0]);
         __syncthreads();
 
         // (D) key blocks: ring slot J % D holds block J; once block J is in LDS
@@ -607,7 +622,7 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
                         hacc[pt] = mfma(av, bv, hacc[pt]);
                     }
                 }
-                if (J + 1 < NKB) store_block(J + 1, c0, nvalid, rgB[(d + 1) % D], rgX[(d + 1) % D]);
+                if (J + 1 < NKB) store_block(J + 1, nvalid, rgB[(d + 1) % D], rgX[(d + 1) % D]);
                 __syncthreads();
             }
         }
