@@ -47,6 +47,8 @@
 // the global frame); pass 3 evaluates every segment from its true carry.
 #include "m3_internal.h"
 
+#include <type_traits>
+
 namespace m3 {
 
 namespace {
@@ -61,6 +63,9 @@ typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 __device__ __forceinline__ float lo_f(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_f(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -69,7 +74,6 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     v[1] = (bf16)hi;
     return __builtin_bit_cast(uint32_t, v);
 }
-__device__ __forceinline__ int tri(int t, int s) { return (t * (t + 1) >> 1) + s; }
 
 // ---- LDS layout ------------------------------------------------------------------
 // Per key-block buffer: Bn [32 j][128 n] bf16, BvT [128 n][32 j] bf16, XT [64 p][32 j] bf16.
@@ -89,16 +93,17 @@ template <int Q>
 struct Layout {
     static constexpr int hs = 2 * kBufBytes;
     static constexpr int cs = hs + kHsBytes;                  // half2 [Q][64]: (cos, sin) per token and pair
-    static constexpr int wt = cs + Q * 64 * 4;                // half [Q (Q + 1) / 2]: W(t, s), s <= t
-    static constexpr int cbias = wt + ((Q * (Q + 1) / 2 * 2 + 15) & ~15);   // float [4][128]
+    static constexpr int cbias = cs + Q * 64 * 4;             // float [4][128]
     static constexpr int l2 = cbias + 4 * kN * 4;             // float [Q] each below
-    static constexpr int gam = l2 + Q * 4;
-    static constexpr int dels = gam + Q * 4;
-    static constexpr int vs = dels + Q * 4;
+    static constexpr int g1 = l2 + Q * 4;
+    static constexpr int gam = g1 + Q * 4;
+    static constexpr int vs = gam + Q * 4;
     static constexpr int dtv = vs + Q * 4;
     static constexpr int phic = dtv + Q * 4;                  // float [64]
     static constexpr int misc = phic + 64 * 4;                // float [16]
-    static constexpr int total = misc + 16 * 4;
+    static constexpr int stg = misc + 16 * 4;                 // float [64][Q + 1]: theta, pair-major
+    static constexpr int xsc = stg + ((64 * (Q + 1) * 4 + 15) & ~15);   // per wave 4 KiB: row <-> MFMA layout
+    static constexpr int total = xsc + kNW * 4096;
 };
 
 // Query tile k of wave w (chunk-level tile index), or -1.  Tiles are dealt in
@@ -114,13 +119,29 @@ __device__ __forceinline__ int query_tile(int w, int k) {
     }
 }
 
-// Inclusive scan of v over groups of W lanes of a wave (W a power of two <= 64).
+// DPP read of v from another lane; lanes whose source is outside the pattern (or
+// whose row is masked off) read 0.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_read(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, false));
+}
+
+// Inclusive scan of v over groups of W lanes of a wave (W a power of two, 8 <= W <= 64):
+// shifts within 16-lane rows, then the row broadcasts of lane 15 and lane 31.
 template <int W>
 __device__ __forceinline__ float group_scan(float v, int lane_in_group) {
-#pragma unroll
-    for (int off = 1; off < W; off <<= 1) {
-        const float u = __shfl_up(v, off, W);
-        if (lane_in_group >= off) v += u;
+    static_assert(W == 8 || W == 16 || W == 32 || W == 64, "group width");
+    if constexpr (W == 8) {
+        float u = dpp_read<0x111>(v); v = lane_in_group >= 1 ? v + u : v;
+        u = dpp_read<0x112>(v); v = lane_in_group >= 2 ? v + u : v;
+        u = dpp_read<0x114>(v); v = lane_in_group >= 4 ? v + u : v;
+    } else {
+        v += dpp_read<0x111>(v);        // row_shr:1, 2, 4, 8 (zero-filled at the row start)
+        v += dpp_read<0x112>(v);
+        v += dpp_read<0x114>(v);
+        v += dpp_read<0x118>(v);
+        if constexpr (W >= 32) v += dpp_read<0x142, 0xa>(v);   // row_bcast:15 into rows 1, 3
+        if constexpr (W == 64) v += dpp_read<0x143, 0xc>(v);   // row_bcast:31 into rows 2, 3
     }
     return v;
 }
@@ -133,26 +154,26 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
     constexpr int TPW = NT >= 2 * kNW ? NT / kNW : 1;   // query tiles per wave
     // prefetch distance (blocks) = ring size; shorter when 4 query tiles per wave
     // already take the registers
-    constexpr int D = TPW >= 4 ? 2 : (NKB >= 4 ? 4 : NKB);
+    constexpr int D = TPW >= 4 ? 2 : (NKB >= 2 ? 2 : NKB);
     constexpr bool kPrefetchTheta = TPW < 4;
-    constexpr int TH = (Q * 64 + kThreads - 1) / kThreads;   // theta values per thread (np <= 64)
+    constexpr int THP = (Q + 63) / 64;       // theta: passes of 64 tokens (thread: token tid / 8, 8 pairs)
     constexpr int TPL = Q > 64 ? Q / 64 : 1; // tokens per lane of wave 0
-    constexpr int RSTEP = R == 4 ? 4 : (R == 2 ? 2 : 1);
+    constexpr int KT = R >= 4 ? 1 : 4 / R;   // key tokens among a lane's 4 rows of a score tile
+    constexpr int TOKW = kRPW / R > 0 ? kRPW / R : 1;   // tokens of a wave's 4 rows of a key block
     constexpr bool kFullMode = MODE == kFull;
     static_assert(NKB % D == 0, "ring size must divide the blocks per chunk");
     using LY = Layout<Q>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     float* sL2 = reinterpret_cast<float*>(smem + LY::l2);
+    float* sG1 = reinterpret_cast<float*>(smem + LY::g1);
     float* sGam = reinterpret_cast<float*>(smem + LY::gam);
-    float* sDelS = reinterpret_cast<float*>(smem + LY::dels);
     float* sV = reinterpret_cast<float*>(smem + LY::vs);
     float* sDt = reinterpret_cast<float*>(smem + LY::dtv);
     float* sPhic = reinterpret_cast<float*>(smem + LY::phic);
     f16x2* sCS = reinterpret_cast<f16x2*>(smem + LY::cs);
-    _Float16* sW = reinterpret_cast<_Float16*>(smem + LY::wt);
     float* sCb = reinterpret_cast<float*>(smem + LY::cbias);
     float* sMisc = reinterpret_cast<float*>(smem + LY::misc);
-    float* stage = reinterpret_cast<float*>(smem + kBufBytes);     // theta, aliased on buffer 1
+    float* stage = reinterpret_cast<float*>(smem + LY::stg);
 
     const int tid = threadIdx.x, lane = tid & 63;
     // the wave index is the same for all lanes of a wave: say so, so that every
@@ -254,34 +275,48 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
     // Key block gb of the segment (chunk gb / NKB, block gb % NKB): this wave's
     // rows jb = 4 w + rr of it are (token, rank) = ((32 J + jb) / R, (32 J + jb) % R).
     uint32_t rgB[D][kRPW], rgX[D][kRPW];
+    // Raw buffer loads with the record count ending at the segment's last token:
+    // rows of later tokens (and whole blocks past the end) read as zero.
+    const uint32_t bsb = (uint32_t)bstride * 2u, xsb = (uint32_t)xstride * 2u;   // bytes per token
     auto fetch = [&](int gb, uint32_t (&pb)[kRPW], uint32_t (&px)[kRPW]) {
         const int c = gb / NKB, J = gb % NKB;
-        const int j0 = kKB * J + kRPW * w;                 // first row of this wave
-        const int t0 = T0 + c * Q + j0 / R;                // its token (uniform)
-        const uint16_t* bp = Bg + (size_t)t0 * bstride + 2 * lane;
-        const uint16_t* xq = Xg + (size_t)t0 * xstride + 2 * (lane & 31);
+        const int t0 = T0 + c * Q + (kKB * J + kRPW * w) / R;   // token of this wave's first row (uniform)
+        const int nt = __builtin_amdgcn_readfirstlane(min(max(T1 - t0, 0), TOKW));   // of the rows' tokens, those in the segment
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg + (size_t)t0 * bstride, (uint32_t)nt * bsb);
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xg + (size_t)t0 * xstride, (uint32_t)nt * xsb);
 #pragma unroll
         for (int rr = 0; rr < kRPW; ++rr) {
-            const int dt_ = (j0 % R + rr) / R;              // token offset from t0 (compile time for R = 4)
-            const int r = (j0 + rr) % R;
-            if (t0 + dt_ < T1) {
-                pb[rr] = *reinterpret_cast<const uint32_t*>(bp + dt_ * bstride + r * kN);
-                px[rr] = *reinterpret_cast<const uint32_t*>(xq + dt_ * xstride + r * kP);
-            } else {
-                pb[rr] = 0u;
-                px[rr] = 0u;
-            }
+            const int u = rr / R, r = rr % R;                    // token offset, rank (4 w is a multiple of R)
+            pb[rr] = __builtin_amdgcn_raw_buffer_load_b32(rb, (int)(u * bsb) + 4 * lane + 256 * r, 0, 0);
+            px[rr] = __builtin_amdgcn_raw_buffer_load_b32(rx, (int)(u * xsb) + 4 * (lane & 31) + 128 * r, 0, 0);
+        }
+    };
+    // theta of the chunk starting at cstart: thread (token tid / 8 + 64 p, pairs
+    // 8 (tid % 8) + u).  One buffer load per value, the record count ending at
+    // the segment end (later tokens read 0); pairs past np read neighbouring
+    // values that are never used.
+    const int th_t = tid >> 3, th_i = (tid & 7) * 8;
+    auto load_theta = [&](int cstart, float (&th)[kPrefetchTheta ? THP : 1][8]) {
+        const int nt = __builtin_amdgcn_readfirstlane(min(max(T1 - cstart, 0), Q));
+        const __amdgpu_buffer_rsrc_t rt = make_rsrc(thg + (size_t)cstart * H * np, (uint32_t)(nt * H * np) * 4u);
+#pragma unroll
+        for (int pp = 0; pp < (kPrefetchTheta ? THP : 1); ++pp) {
+            const int vo = ((th_t + 64 * pp) * H * np + th_i) * 4;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) th[pp][u] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rt, vo + 4 * u, 0, 0));
+        }
+    };
+    // pair-major staging, rows of Q + 1 floats (the odd stride spreads the banks)
+    auto stage_theta = [&](const float (&th)[8], int t) {
+        if (t < Q) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) stage[(th_i + u) * (Q + 1) + t] = th[u];
         }
     };
     // the next chunk's theta (staging layout) and dt, lam (wave 0: lanes over tokens)
-    float rgTh[kPrefetchTheta ? TH : 1], rgDt[TPL], rgLam[TPL];
+    float rgTh[kPrefetchTheta ? THP : 1][8], rgDt[TPL], rgLam[TPL], rgDnT = 0.f, rgDnL = 0.f;
     auto fetch_scalars = [&](int cstart) {
-#pragma unroll
-        for (int k = 0; k < (kPrefetchTheta ? TH : 0); ++k) {
-            const int e = tid + k * kThreads;
-            const int t = np ? e / np : 0, i = e - t * np;
-            rgTh[k] = (e < Q * np && cstart + t < T1) ? thg[(size_t)(cstart + t) * H * np + i] : 0.f;
-        }
+        if constexpr (kPrefetchTheta) load_theta(cstart, rgTh);
         if (w == 0) {
 #pragma unroll
             for (int k = 0; k < TPL; ++k) {
@@ -289,6 +324,12 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
                 const bool ok = t < Q && cstart + t < T1;
                 rgDt[k] = ok ? dtg[(size_t)(cstart + t) * H] : 0.f;
                 rgLam[k] = ok ? lamg[(size_t)(cstart + t) * H] : 0.f;
+            }
+            // the token after the chunk, in the lane that holds the chunk's last token
+            if (lane == (Q - 1) / TPL) {
+                const bool ok = cstart + Q < L;
+                rgDnT = ok ? dtg[(size_t)(cstart + Q) * H] : 0.f;
+                rgDnL = ok ? lamg[(size_t)(cstart + Q) * H] : 0.f;
             }
         }
     };
@@ -303,7 +344,6 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
     // turn a ring slot's rows and write key block J's LDS tiles.  This wave's
     // rows 4 w .. 4 w + 3 of the block cover TOKW tokens of R ranks each; the
     // angle and v are read once per token.
-    constexpr int TOKW = kRPW / R > 0 ? kRPW / R : 1;     // tokens per wave and block
     constexpr int RPT = kRPW / TOKW;                       // rows per token here (= R, or 4 when R > 4)
     auto store_block = [&](int J, int nvalid, const uint32_t (&pb)[kRPW], const uint32_t (&px)[kRPW]) {
         char* buf = smem + (J & 1) * kBufBytes;
@@ -358,6 +398,36 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
         }
     };
 
+    // (E) outputs of the chunk at cst (nv valid tokens).  Issued one chunk late, after
+    // the next chunk's staging waits, so that no wait for loaded data also waits
+    // for these stores.
+    auto store_y = [&](int cst, int nv) {
+        uint16_t* yg = static_cast<uint16_t*>(a.y) + (tokbase * H + h) * R * kP;
+        char* xs = smem + LY::xsc + w * 4096;                // rows of 144 bytes
+        // the lane index, opaque here so that the row offsets below are formed at
+        // the stores rather than kept live across the chunk loop
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+            const int qt = query_tile<NT>(w, k);
+            if (qt < 0) continue;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt)
+                *reinterpret_cast<uint2*>(xs + l16 * 144 + (16 * pt + 4 * g4) * 2) =
+                    uint2{pack2(yacc[k][pt][0], yacc[k][pt][1]), pack2(yacc[k][pt][2], yacc[k][pt][3])};
+            // rows 8 i + lane / 8, 16 bytes (p = 8 (lane % 8) ...) per lane
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int j = 8 * i + (ln >> 3);
+                const uint4 v = *reinterpret_cast<const uint4*>(xs + j * 144 + (ln & 7) * 16);
+                const int qi = 16 * qt + j;
+                const int t = qi / R, r = qi % R;
+                if (t < nv) *reinterpret_cast<uint4*>(yg + (size_t)(cst + t) * xstride + r * kP + 8 * (ln & 7)) = v;
+            }
+        }
+    };
+
     // ---- chunk loop ------------------------------------------------------------------------
     int cidx = 0;
     for (int c0 = T0; c0 < T1; c0 += Q, ++cidx) {
@@ -372,27 +442,30 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
                 *reinterpret_cast<uint2*>(smem + LY::hs + hs_off(p, nb >> 3) + ((nb >> 2) & 1) * 8) =
                     uint2{pack2(hacc[pt][0], hacc[pt][1]), pack2(hacc[pt][2], hacc[pt][3])};
             }
+            // raw C rows, contiguous: load i of tile k holds rows 4 i + lane / 16, 16 bytes
+            // (n = 8 (lane % 16) ...) per lane; padded tokens read the last valid row
+            int ln = lane;                                    // opaque: offsets formed here
+            asm volatile("" : "+v"(ln));
 #pragma unroll
             for (int k = 0; k < TPW; ++k) {
                 const int qt = query_tile<NT>(w, k);
-                const int qi = 16 * (qt < 0 ? 0 : qt) + l16;
-                const int t = qi / R, r = qi % R;
-                const uint16_t* crow = Cg + (size_t)(c0 + min(t, nvalid - 1)) * bstride + r * kN + 8 * g4;
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    cq[k][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(crow + 32 * ks));
+                for (int i = 0; i < 4; ++i) {
+                    const int qi = 16 * (qt < 0 ? 0 : qt) + 4 * i + (ln >> 4);
+                    const int t = qi / R, r = qi % R;
+                    const uint16_t* crow = Cg + (size_t)(c0 + min(t, nvalid - 1)) * bstride + r * kN + 8 * (ln & 15);
+                    cq[k][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(crow));
+                }
             }
         }
         if constexpr (kPrefetchTheta) {
 #pragma unroll
-            for (int k = 0; k < TH; ++k) {
-                const int e = tid + k * kThreads;
-                if (e < Q * np) stage[e] = rgTh[k];
-            }
+            for (int pp = 0; pp < THP; ++pp) stage_theta(rgTh[pp], th_t + 64 * pp);
         } else {
-            for (int e = tid; e < Q * np; e += kThreads) {
-                const int t = e / np, i = e - t * np;
-                stage[e] = t < nvalid ? thg[(size_t)(c0 + t) * H * np + i] : 0.f;
+            for (int pp = 0; pp < THP; ++pp) {
+                float th[1][8];
+                load_theta(c0 + 64 * pp, th);
+                stage_theta(th[0], th_t + 64 * pp);
             }
         }
         if (w == 0) {
@@ -411,11 +484,10 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
             }
             const float incl = group_scan<64>(lsum, lane);
             const float excl = incl - lsum;
-            float dnext = 0.f;                                 // d of the token after the chunk
-            if (c0 + Q < L) dnext = dtg[(size_t)(c0 + Q) * H] * (1.f - lamg[(size_t)(c0 + Q) * H]);
-            const float tot = __shfl(incl, 63);
+            const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
             const float le = tot * kLog2e;                     // l_e (padded tokens add 0)
-            const float nx = __shfl_down(dl[0], 1);
+            const float nx = dpp_read<0x130>(dl[0]);           // wave_shl:1: d of the next lane's first token
+            const float dnext = rgDnT * (1.f - rgDnL);         // d of the token after the chunk
 #pragma unroll
             for (int k = 0; k < TPL; ++k) {
                 const int t = lane * TPL + k;
@@ -423,9 +495,9 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
                 if (t < Q) {
                     const float l2t = (excl + la[k]) * kLog2e;
                     sL2[t] = l2t;
+                    sG1[t] = gm[k] + dn;
                     sGam[t] = gm[k];
-                    sDelS[t] = dn;
-                    sV[t] = exp2f(le - l2t) * (gm[k] + dn);
+                    sV[t] = __builtin_amdgcn_exp2f(le - l2t) * (gm[k] + dn);
                 }
             }
             if (lane == 0) sMisc[0] = le;
@@ -435,38 +507,63 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
         fetch_scalars(c0 + Q);
         __syncthreads();
 
-        // (B) angles: threads (pair i, part k) scan dt * theta over the chunk;
-        //     pair weights W(t, s) for s <= t
+        if (kFullMode && c0 > T0) store_y(c0 - Q, Q);
+
+        // (B) angles: TPP threads per pair scan dt * theta over the chunk (np <= 64)
         {
-            const int tpp = np <= 32 ? 16 : 8;
-            const int npr = kThreads / tpp;                    // pairs per round
-            const int k = tid % tpp;
-            const int tpt = Q / tpp;
-            for (int i = tid / tpp; i < np; i += npr) {
-                float loc = 0.f;
-                for (int t = k * tpt; t < (k + 1) * tpt; ++t) loc += sDt[t] * stage[t * np + i];
-                const float incl = tpp == 16 ? group_scan<16>(loc, k) : group_scan<8>(loc, k);
-                float run = sPhic[i] + incl - loc;
-                for (int t = k * tpt; t < (k + 1) * tpt; ++t) {
-                    run += sDt[t] * stage[t * np + i];
-                    float sn, cs;
-                    __sincosf(run, &sn, &cs);
-                    sCS[t * 64 + i] = f16x2{(_Float16)cs, (_Float16)sn};
+            auto angles = [&](auto tpp_c) {
+                constexpr int TPP = decltype(tpp_c)::value;
+                constexpr int TPT = Q / TPP;                   // tokens per thread
+                const int k = tid % TPP, i = tid / TPP;
+                if (i < np) {
+                    float inc[TPT];
+                    float loc = 0.f;
+#pragma unroll
+                    for (int u = 0; u < TPT; ++u) {
+                        const int t = k * TPT + u;
+                        loc += sDt[t] * stage[i * (Q + 1) + t];
+                        inc[u] = loc;
+                    }
+                    const float incl = group_scan<TPP>(loc, k);
+                    const float base = sPhic[i] + incl - loc;
+#pragma unroll
+                    for (int u = 0; u < TPT; ++u) {
+                        float sn, cs;
+                        __sincosf(base + inc[u], &sn, &cs);
+                        sCS[(k * TPT + u) * 64 + i] = f16x2{(_Float16)cs, (_Float16)sn};
+                    }
+                    if (k == TPP - 1) sPhic[i] = wrap_2pi(base + inc[TPT - 1]);
                 }
-                if (k == tpp - 1) sPhic[i] = wrap_2pi(run);
-            }
-            if (kFullMode) {
-                for (int e = tid; e < Q * Q; e += kThreads) {
-                    const int t = e / Q, s = e - t * Q;
-                    if (s <= t) sW[tri(t, s)] = (_Float16)(exp2f(sL2[t] - sL2[s]) * (sGam[s] + (s < t ? sDelS[s] : 0.f)));
-                }
-            }
+            };
+            if (np <= 32) angles(std::integral_constant<int, 16>{});
+            else angles(std::integral_constant<int, 8>{});
         }
         __syncthreads();
         const float le2 = sMisc[0];
+        // query token and its log-decay, per query tile of this wave
+        int tq[TPW];
+        float l2q[TPW];
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+            const int qt = query_tile<NT>(w, k);
+            tq[k] = (16 * (qt < 0 ? 0 : qt) + l16) / R;
+            l2q[k] = sL2[tq[k]];
+        }
 
-        // (C) C tiles: bias and turn in place; carry readout Y^T = exp(l_t) Hf Ct^T
+        // (C) C tiles: to the MFMA operand layout (lane: row l16, n = 32 ks + 8 g4 ...)
+        //     through this wave's scratch; bias and turn in place; carry readout
+        //     Y^T = exp(l_t) Hf Ct^T
         if (kFullMode) {
+            char* xs = smem + LY::xsc + w * 4096;
+#pragma unroll
+            for (int k = 0; k < TPW; ++k) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<bf16x8*>(xs + bn_off(4 * i + g4, l16)) = cq[k][i];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    cq[k][ks] = *reinterpret_cast<const bf16x8*>(xs + bn_off(l16, 4 * ks + g4));
+            }
 #pragma unroll
             for (int k = 0; k < TPW; ++k) {
                 const int qt = query_tile<NT>(w, k);
@@ -500,8 +597,7 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
             float sc[TPW];
 #pragma unroll
             for (int k = 0; k < TPW; ++k) {
-                const int qt = query_tile<NT>(w, k);
-                sc[k] = exp2f(sL2[(16 * (qt < 0 ? 0 : qt) + l16) / R]);
+                sc[k] = __builtin_amdgcn_exp2f(l2q[k]);
             }
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
@@ -544,6 +640,16 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
                     // tiles.  One key tile's operands are live at a time and shared by
                     // the query tiles; fences keep the phases apart (register pressure).
                     const int ka = 2 * J;
+                    // log-decay and weight of the key tokens of this lane's rows
+                    float kl2[2][KT], kg1[2][KT];
+#pragma unroll
+                    for (int ab = 0; ab < 2; ++ab)
+#pragma unroll
+                        for (int j = 0; j < KT; ++j) {
+                            const int ts = (16 * (ka + ab) + 4 * g4) / R + j;
+                            kl2[ab][j] = sL2[ts];
+                            kg1[ab][j] = sG1[ts];
+                        }
                     f32x4 s0[TPW], s1[TPW];
                     {
                         bf16x8 op[4];
@@ -575,27 +681,32 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
                         }
                     }
                     __builtin_amdgcn_sched_barrier(0);
-                    // S'^T = W o S^T: W of key rows 32 J + 4 g4 + m (tile a) and
-                    // 32 J + 16 + 4 g4 + m (tile b), rounded to bf16 as the B operand
+                    // S'^T = W o S^T, rounded to bf16 as the B operand.  Lane: query
+                    // token tq, key rows 16 kt + 4 g4 + m of key tiles ka (s0), ka + 1 (s1)
                     bf16x8 bop[TPW];
 #pragma unroll
                     for (int k = 0; k < TPW; ++k) {
                         const int qt = query_tile<NT>(w, k);
-                        const int t = (16 * (qt < 0 ? 0 : qt) + l16) / R;
-                        const int rt = tri(t, 0);
-                        float wa[4], wb[4];
+                        float wgt[2][KT];
 #pragma unroll
-                        for (int m = 0; m < 4; m += RSTEP) {
-                            const int sa = (32 * J + 4 * g4 + m) / R, sb = (32 * J + 16 + 4 * g4 + m) / R;
-                            const float xa = sa <= t ? (float)sW[rt + sa] : 0.f;
-                            const float xb = sb <= t ? (float)sW[rt + sb] : 0.f;
+                        for (int ab = 0; ab < 2; ++ab) {
 #pragma unroll
-                            for (int q = 0; q < RSTEP; ++q) { wa[m + q] = xa; wb[m + q] = xb; }
+                            for (int j = 0; j < KT; ++j) {
+                                const float e = __builtin_amdgcn_exp2f(l2q[k] - kl2[ab][j]);
+                                if (qt > ka + ab) {                      // uniform: key tile before the query tile
+                                    wgt[ab][j] = e * kg1[ab][j];
+                                } else if (qt == ka + ab) {              // the diagonal tile
+                                    const int ts = (16 * (ka + ab) + 4 * g4) / R + j;
+                                    wgt[ab][j] = ts < tq[k] ? e * kg1[ab][j] : (ts == tq[k] ? e * sGam[ts] : 0.f);
+                                } else {
+                                    wgt[ab][j] = 0.f;
+                                }
+                            }
                         }
 #pragma unroll
                         for (int m = 0; m < 4; ++m) {
-                            bop[k][m] = (bf16)(s0[k][m] * wa[m]);
-                            bop[k][4 + m] = (bf16)(s1[k][m] * wb[m]);
+                            bop[k][m] = (bf16)(s0[k][m] * wgt[0][m * KT / 4]);
+                            bop[k][4 + m] = (bf16)(s1[k][m] * wgt[1][m * KT / 4]);
                         }
                     }
                     __builtin_amdgcn_sched_barrier(0);
@@ -628,27 +739,9 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
         }
         // the next chunk's block 0 now sits in ring slot 0
 
-        // (E) outputs of this chunk
-        if (kFullMode) {
-            bf16* yg = static_cast<bf16*>(a.y) + (tokbase * H + h) * R * kP;
-#pragma unroll
-            for (int k = 0; k < TPW; ++k) {
-                const int qt = query_tile<NT>(w, k);
-                if (qt < 0) continue;
-                const int qi = 16 * qt + l16;
-                const int t = qi / R, r = qi % R;
-                if (t >= nvalid) continue;
-                bf16* yrow = yg + (size_t)(c0 + t) * xstride + r * kP;
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    bf16x4 o;
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) o[m] = (bf16)yacc[k][pt][m];
-                    *reinterpret_cast<bf16x4*>(yrow + 16 * pt + 4 * g4) = o;
-                }
-            }
-        }
     }
+    // the last chunk's outputs
+    if (kFullMode && T1 > T0) store_y(T0 + (T1 - T0 - 1) / Q * Q, (T1 - T0 - 1) % Q + 1);
 
     // ---- end of the stream / segment ----------------------------------------------------------
     if (!kFullMode) {

@@ -124,6 +124,9 @@ MFMA = [
     (4, 64, 0, 1, 64, True, True, False, 1),
     (4, 128, 32, 1, 300, True, False, True, 1),
     (4, 128, 32, 1, 520, True, False, True, 4),
+    # every pair turning at the longest chunk (the largest angle staging)
+    (4, 128, 64, 1, 200, True, False, True, 2),
+    (1, 128, 64, 2, 150, True, False, True, 1),
 ]
 
 
