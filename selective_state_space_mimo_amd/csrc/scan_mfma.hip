@@ -791,6 +791,682 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
     }
 }
 
+// ---- warp-specialised variant (chunks of at most 256 rows) ----------------------------------
+// Waves 0-3 are consumers: each keeps a quarter of the chunk's query tiles (C tiles in
+// registers, Y^T accumulators) and runs the scores, their weighting and Y^T += X^T S'^T.
+// Waves 4-7 are producers: each turns 8 of every key block's 32 rows into the LDS tiles
+// and owns 32 columns of the state (Hf^T += (v Bt)^T X).  A SIMD then holds one wave of
+// each kind, so that the producers' vector work overlaps the consumers' matrix work.
+// Both kinds pass the same barriers: one after each chunk section, one per key block.
+constexpr int kNC = 4;                                   // consumer waves
+
+// Query tile k of consumer c: tiles are dealt in groups of 8, consumer c taking tile c
+// and tile 7 - c of each group (equal causal work per consumer).
+__device__ __forceinline__ int ctile(int c, int k) { return 8 * (k >> 1) + ((k & 1) ? 7 - c : c); }
+
+template <int R, int Q, int MODE>
+__global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
+    constexpr int M = Q * R;                 // rows per chunk
+    constexpr int NKB = M / kKB;             // key blocks per chunk
+    constexpr int NT = M / 16;               // query tiles per chunk
+    constexpr int TPC = NT / kNC;            // query tiles per consumer
+    constexpr int TPL = Q > 64 ? Q / 64 : 1; // tokens per lane of the scanning wave
+    constexpr int KT = R >= 4 ? 1 : 4 / R;   // key tokens among a lane's 4 rows of a score tile
+    constexpr int PR = 8;                    // key rows per producer and block
+    constexpr bool kFullMode = MODE == kFull;
+    static_assert(TPC >= 1 && TPC <= 4 && NKB >= 2 && NKB % 2 == 0, "chunk shape");
+    using LY = Layout<Q>;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    float* sL2 = reinterpret_cast<float*>(smem + LY::l2);
+    float* sG1 = reinterpret_cast<float*>(smem + LY::g1);
+    float* sGam = reinterpret_cast<float*>(smem + LY::gam);
+    float* sV = reinterpret_cast<float*>(smem + LY::vs);
+    float* sDt = reinterpret_cast<float*>(smem + LY::dtv);
+    float* sPhic = reinterpret_cast<float*>(smem + LY::phic);
+    f16x2* sCS = reinterpret_cast<f16x2*>(smem + LY::cs);
+    float* sCb = reinterpret_cast<float*>(smem + LY::cbias);
+    float* sMisc = reinterpret_cast<float*>(smem + LY::misc);
+    float* stage = reinterpret_cast<float*>(smem + LY::stg);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int H = a.H, L = a.L, np = a.np, nseg = a.nseg;
+
+    const int nblk = gridDim.x;
+    const int bid = blockIdx.x;
+    const int logical = (nblk % 8 == 0) ? (bid % 8) * (nblk / 8) + bid / 8 : bid;
+    const int h = logical % H;
+    const int rest = logical / H;
+    const int seg = rest % nseg, bi = rest / nseg;
+    const int bh = bi * H + h;
+    const int g = h * a.G / H;
+    const int T0 = seg * a.seglen;
+    const int T1 = min(L, T0 + a.seglen);
+    const bool last_seg = (T1 == L);
+    const float ah = expf(a.A_log[h]);
+    const size_t ss = (size_t)bh * nseg + seg;
+    const size_t S = (size_t)a.b * H * nseg;
+    float* const wsHloc = a.ws;
+    float* const wsHin = a.ws + S * kP * kN;
+    float* const wsLam = a.ws + 2 * S * kP * kN;
+    float* const wsDphi = wsLam + S;
+    float* const wsPhi = wsDphi + S * np;
+
+    const size_t tokbase = (size_t)bi * L;
+    const uint16_t* const Bg = static_cast<const uint16_t*>(a.B) + (tokbase * a.G + g) * R * kN;
+    const uint16_t* const Cg = static_cast<const uint16_t*>(a.C) + (tokbase * a.G + g) * R * kN;
+    const uint16_t* const Xg = static_cast<const uint16_t*>(a.x) + (tokbase * H + h) * R * kP;
+    const size_t bstride = (size_t)a.G * R * kN;
+    const size_t xstride = (size_t)H * R * kP;
+    const float* const dtg = a.dt + tokbase * H + h;
+    const float* const lamg = a.lam + tokbase * H + h;
+    const float* const thg = np ? a.theta + (tokbase * H + h) * np : a.dt;
+
+    // ---- shared set-up ------------------------------------------------------------------------
+    if (kFullMode)
+        for (int e = tid; e < R * kN; e += kThreads) sCb[e] = a.Cb ? a.Cb[(size_t)h * R * kN + e] : 0.f;
+    for (int i = tid; i < np; i += kThreads) {
+        float v = 0.f;
+        if (kFullMode) v = seg == 0 ? (a.phi0 ? a.phi0[(size_t)bh * np + i] : 0.f) : wsPhi[ss * np + i];
+        sPhic[i] = v;
+    }
+    for (int e = tid; e < Q * 64; e += kThreads)
+        if ((e & 63) >= np) sCS[e] = f16x2{(_Float16)1.f, (_Float16)0.f};
+
+    // theta of the chunk at cstart (all threads: token tid / 8, pairs 8 (tid % 8) + u),
+    // one buffer load per value, bounded at the segment end
+    constexpr int THP = (Q + 63) / 64;
+    auto load_theta = [&](int cstart, float (&th)[THP][8]) {
+        int tt = tid;                                         // opaque: offsets formed here
+        asm volatile("" : "+v"(tt));
+        const int th_t = tt >> 3, th_i = (tt & 7) * 8;
+        const int nt = __builtin_amdgcn_readfirstlane(min(max(T1 - cstart, 0), Q));
+        const __amdgpu_buffer_rsrc_t rt = make_rsrc(thg + (size_t)cstart * H * np, (uint32_t)(nt * H * np) * 4u);
+#pragma unroll
+        for (int pp = 0; pp < THP; ++pp) {
+            const int vo = ((th_t + 64 * pp) * H * np + th_i) * 4;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) th[pp][u] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rt, vo + 4 * u, 0, 0));
+        }
+    };
+    auto stage_theta = [&](const float (&th)[THP][8]) {
+        int tt = tid;
+        asm volatile("" : "+v"(tt));
+        const int th_t = tt >> 3, th_i = (tt & 7) * 8;
+#pragma unroll
+        for (int pp = 0; pp < THP; ++pp) {
+            const int t = th_t + 64 * pp;
+            if (t < Q) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) stage[(th_i + u) * (Q + 1) + t] = th[pp][u];
+            }
+        }
+    };
+    // (B) angles, all threads: TPP threads per pair scan dt * theta over the chunk
+    auto angles = [&]() {
+        auto run = [&](auto tpp_c) {
+            constexpr int TPP = decltype(tpp_c)::value;
+            constexpr int TPT = Q / TPP;
+            int tt = tid;                                     // opaque: offsets formed here
+            asm volatile("" : "+v"(tt));
+            const int k = tt % TPP, i = tt / TPP;
+            if (i < np) {
+                float inc[TPT];
+                float loc = 0.f;
+#pragma unroll
+                for (int u = 0; u < TPT; ++u) {
+                    const int t = k * TPT + u;
+                    loc += sDt[t] * stage[i * (Q + 1) + t];
+                    inc[u] = loc;
+                }
+                const float incl = group_scan<TPP>(loc, k);
+                const float base = sPhic[i] + incl - loc;
+#pragma unroll
+                for (int u = 0; u < TPT; ++u) {
+                    float sn, cs;
+                    __sincosf(base + inc[u], &sn, &cs);
+                    sCS[(k * TPT + u) * 64 + i] = f16x2{(_Float16)cs, (_Float16)sn};
+                }
+                if (k == TPP - 1) sPhic[i] = wrap_2pi(base + inc[TPT - 1]);
+            }
+        };
+        if (np <= 32) run(std::integral_constant<int, 16>{});
+        else run(std::integral_constant<int, 8>{});
+    };
+    float rgTh[THP][8];
+    load_theta(T0, rgTh);
+    __syncthreads();
+
+    if (w < kNC) {
+        // =============================== consumers ===============================
+        const int c = w;
+        bf16x8 cq[TPC][4];
+        f32x4 yacc[TPC][4];
+        char* const xs = smem + LY::xsc + c * 4096;          // this wave's scratch
+        // outputs of the chunk at cst (nv valid tokens), through the scratch (rows of
+        // 144 bytes) so that every store writes whole rows
+        auto store_y = [&](int cst, int nv) {
+            uint16_t* yg = static_cast<uint16_t*>(a.y) + (tokbase * H + h) * R * kP;
+            int ln = lane;                                    // opaque: offsets formed here
+            asm volatile("" : "+v"(ln));
+#pragma unroll
+            for (int k = 0; k < TPC; ++k) {
+                const int qt = ctile(c, k);
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt)
+                    *reinterpret_cast<uint2*>(xs + (ln & 15) * 144 + (16 * pt + 4 * (ln >> 4)) * 2) =
+                        uint2{pack2(yacc[k][pt][0], yacc[k][pt][1]), pack2(yacc[k][pt][2], yacc[k][pt][3])};
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int j = 8 * i + (ln >> 3);
+                    const uint4 v = *reinterpret_cast<const uint4*>(xs + j * 144 + (ln & 7) * 16);
+                    const int qi = 16 * qt + j;
+                    const int t = qi / R, r = qi % R;
+                    if (t < nv) *reinterpret_cast<uint4*>(yg + (size_t)(cst + t) * xstride + r * kP + 8 * (ln & 7)) = v;
+                }
+            }
+        };
+
+        int cidx = 0;
+        for (int c0 = T0; c0 < T1; c0 += Q, ++cidx) {
+            const int nvalid = min(Q, T1 - c0);
+            // (A) raw C rows, contiguous (load i of tile k: rows 4 i + lane / 16, n = 8 (lane % 16) ...);
+            //     the previous chunk's outputs; theta into the staging area
+            if (kFullMode) {
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+#pragma unroll
+                for (int k = 0; k < TPC; ++k) {
+                    const int qt = ctile(c, k);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int qi = 16 * qt + 4 * i + (ln >> 4);
+                        const int t = qi / R, r = qi % R;
+                        const uint16_t* crow = Cg + (size_t)(c0 + min(t, nvalid - 1)) * bstride + r * kN + 8 * (ln & 15);
+                        cq[k][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(crow));
+                    }
+                }
+                if (c0 > T0) store_y(c0 - Q, Q);
+            }
+            stage_theta(rgTh);
+            load_theta(c0 + Q, rgTh);
+            __syncthreads();
+            angles();
+            __syncthreads();
+            // (C) C tiles to the operand layout (row l16, n = 32 ks + 8 g4 ...), bias and
+            //     turn; carry readout Y^T = exp(l_t) Hf Ct^T
+            int tq[TPC];
+            float l2q[TPC];
+            if (kFullMode) {
+                int ln = lane;                                // opaque: offsets formed here
+                asm volatile("" : "+v"(ln));
+                const int l16 = ln & 15, g4 = ln >> 4;
+#pragma unroll
+                for (int k = 0; k < TPC; ++k) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        *reinterpret_cast<bf16x8*>(xs + bn_off(4 * i + g4, l16)) = cq[k][i];
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        cq[k][ks] = *reinterpret_cast<const bf16x8*>(xs + bn_off(l16, 4 * ks + g4));
+                }
+#pragma unroll
+                for (int k = 0; k < TPC; ++k) {
+                    const int qi = 16 * ctile(c, k) + l16;
+                    const int t = qi / R, r = qi % R;
+                    tq[k] = t;
+                    l2q[k] = sL2[t];
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const int n0 = 32 * ks + 8 * g4;
+                        const uint4 raw = __builtin_bit_cast(uint4, cq[k][ks]);
+                        const float4 b0 = *reinterpret_cast<const float4*>(sCb + r * kN + n0);
+                        const float4 b1 = *reinterpret_cast<const float4*>(sCb + r * kN + n0 + 4);
+                        const uint4 csr = *reinterpret_cast<const uint4*>(sCS + t * 64 + n0 / 2);
+                        const uint32_t csw[4] = {csr.x, csr.y, csr.z, csr.w};
+                        const float v[8] = {lo_f(raw.x) + b0.x, hi_f(raw.x) + b0.y, lo_f(raw.y) + b0.z, hi_f(raw.y) + b0.w,
+                                            lo_f(raw.z) + b1.x, hi_f(raw.z) + b1.y, lo_f(raw.w) + b1.z, hi_f(raw.w) + b1.w};
+                        bf16x8 q;
+#pragma unroll
+                        for (int pp = 0; pp < 4; ++pp) {
+                            const f16x2 cc = __builtin_bit_cast(f16x2, csw[pp]);
+                            const float cs = (float)cc[0], sn = (float)cc[1];
+                            const float e = v[2 * pp], o = v[2 * pp + 1];
+                            q[2 * pp] = (bf16)(e * cs - o * sn);
+                            q[2 * pp + 1] = (bf16)(e * sn + o * cs);
+                        }
+                        cq[k][ks] = q;
+                    }
+                }
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const int p = 16 * pt + l16;
+#pragma unroll
+                    for (int k = 0; k < TPC; ++k) yacc[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const bf16x8 av = *reinterpret_cast<const bf16x8*>(smem + LY::hs + hs_off(p, 4 * ks + g4));
+#pragma unroll
+                        for (int k = 0; k < TPC; ++k) yacc[k][pt] = mfma(av, cq[k][ks], yacc[k][pt]);
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < TPC; ++k) {
+                    const float sc = __builtin_amdgcn_exp2f(l2q[k]);
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt) yacc[k][pt] = yacc[k][pt] * sc;
+                }
+            }
+            __syncthreads();
+            // (D) key blocks: scores against this wave's query tiles, weights, Y^T += X^T S'^T.
+            //     A wave's tiles ascend with k, so the tiles that meet key tile 2 J (2 J + 1)
+            //     are those from K0 (K1) on; each (K0, K1) has its own straight-line body.
+#pragma unroll 1
+            for (int J = 0; J < NKB; ++J) {
+                if (kFullMode) {
+                    const int ka = 2 * J;
+                    int k0 = 0;
+#pragma unroll
+                    for (int k = 0; k < TPC; ++k) k0 += ctile(c, k) < ka ? 1 : 0;
+                    const int k1 = k0 + ((k0 < TPC && ctile(c, k0) == ka) ? 1 : 0);
+                    const char* buf = smem + (J & 1) * kBufBytes;
+                    const char* xtb = buf + kBnBytes + kBvBytes;
+                    auto body = [&](auto k0c, auto k1c) {
+                        constexpr int K0 = decltype(k0c)::value, K1 = decltype(k1c)::value;
+                        if constexpr (K0 < TPC) {
+                            float kl2[2][KT], kg1[2][KT];
+#pragma unroll
+                            for (int ab = 0; ab < 2; ++ab)
+#pragma unroll
+                                for (int j = 0; j < KT; ++j) {
+                                    const int ts = (16 * (ka + ab) + 4 * g4) / R + j;
+                                    kl2[ab][j] = sL2[ts];
+                                    kg1[ab][j] = sG1[ts];
+                                }
+                            f32x4 s0[TPC], s1[TPC];
+                            {
+                                bf16x8 op[4];
+#pragma unroll
+                                for (int ks = 0; ks < 4; ++ks)
+                                    op[ks] = *reinterpret_cast<const bf16x8*>(buf + bn_off(l16, 4 * ks + g4));
+#pragma unroll
+                                for (int k = K0; k < TPC; ++k) {
+                                    s0[k] = mfma(op[0], cq[k][0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                                    for (int ks = 1; ks < 4; ++ks) s0[k] = mfma(op[ks], cq[k][ks], s0[k]);
+                                }
+                            }
+                            if constexpr (K1 < TPC) {
+                                bf16x8 op[4];
+#pragma unroll
+                                for (int ks = 0; ks < 4; ++ks)
+                                    op[ks] = *reinterpret_cast<const bf16x8*>(buf + bn_off(16 + l16, 4 * ks + g4));
+#pragma unroll
+                                for (int k = K1; k < TPC; ++k) {
+                                    s1[k] = mfma(op[0], cq[k][0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                                    for (int ks = 1; ks < 4; ++ks) s1[k] = mfma(op[ks], cq[k][ks], s1[k]);
+                                }
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
+                            // S'^T = W o S^T as bf16 B operands; the diagonal tile of key tile a
+                            // (b) can only be tile K0 (K1)
+                            bf16x8 bop[TPC];
+#pragma unroll
+                            for (int k = K0; k < TPC; ++k) {
+                                float wgt[2][KT];
+#pragma unroll
+                                for (int ab = 0; ab < 2; ++ab) {
+#pragma unroll
+                                    for (int j = 0; j < KT; ++j) {
+                                        if (ab == 1 && k < K1) {
+                                            wgt[ab][j] = 0.f;
+                                            continue;
+                                        }
+                                        const float e = __builtin_amdgcn_exp2f(l2q[k] - kl2[ab][j]);
+                                        wgt[ab][j] = e * kg1[ab][j];
+                                        if (k == (ab ? K1 : K0) && ctile(c, k) == ka + ab) {   // uniform
+                                            const int ts = (16 * (ka + ab) + 4 * g4) / R + j;
+                                            wgt[ab][j] = ts < tq[k] ? wgt[ab][j] : (ts == tq[k] ? e * sGam[ts] : 0.f);
+                                        }
+                                    }
+                                }
+#pragma unroll
+                                for (int m = 0; m < 4; ++m) {
+                                    bop[k][m] = (bf16)(s0[k][m] * wgt[0][m * KT / 4]);
+                                    bop[k][4 + m] = k < K1 ? (bf16)0.f : (bf16)(s1[k][m] * wgt[1][m * KT / 4]);
+                                }
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
+                            // X^T in the k order of S'^T: keys 4 g4 + 0..3 of tile a, then of tile b
+                            bf16x8 xo[4];
+#pragma unroll
+                            for (int pt = 0; pt < 4; ++pt)
+                                xo[pt] = *reinterpret_cast<const bf16x8*>(xtb + q4_off(16 * pt + l16, g4));
+#pragma unroll
+                            for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+                                for (int k = K0; k < TPC; ++k) yacc[k][pt] = mfma(xo[pt], bop[k], yacc[k][pt]);
+                        }
+                    };
+                    using std::integral_constant;
+#define M3_WS_CASE(A_, B_)                                                            \
+    case (A_) * 8 + (B_):                                                             \
+        if constexpr ((A_) <= TPC && (B_) <= TPC)                                     \
+            body(integral_constant<int, (A_)>{}, integral_constant<int, (B_)>{});     \
+        break;
+                    switch (k0 * 8 + k1) {
+                        M3_WS_CASE(0, 0) M3_WS_CASE(0, 1) M3_WS_CASE(1, 1) M3_WS_CASE(1, 2) M3_WS_CASE(2, 2)
+                        M3_WS_CASE(2, 3) M3_WS_CASE(3, 3) M3_WS_CASE(3, 4) M3_WS_CASE(4, 4)
+                        default: break;
+                    }
+#undef M3_WS_CASE
+                }
+                __syncthreads();
+            }
+        }
+        if (kFullMode && T1 > T0) store_y(T0 + (T1 - T0 - 1) / Q * Q, (T1 - T0 - 1) % Q + 1);
+    } else {
+        // =============================== producers ===============================
+        const int pw = w - kNC;
+        // key rows of producer pw in a block: 4 pw + i and 16 + 4 pw + i (i < 4), i.e. key
+        // group pw of both key tiles; row rr (< 8) is token offset tko(rr), rank rr % R,
+        // from the token of row 4 pw
+        auto tko = [](int rr) { return rr < 4 ? rr / R : 16 / R + (rr - 4) / R; };
+        constexpr int NTK = 16 / R + 3 / R + 1;              // tokens spanned by the 8 rows
+        // B bias of this lane's n-pair, per rank
+        float2 bb[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            bb[r] = a.Bb ? *reinterpret_cast<const float2*>(a.Bb + ((size_t)h * R + r) * kN + 2 * lane) : float2{0.f, 0.f};
+        // state columns [32 pw, 32 pw + 32): H^T tiles (n-tile 2 pw + u, p-tile pt), lane:
+        // p = 16 pt + l16, n = 32 pw + 16 u + 4 g4 + m
+        f32x4 hacc[2][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int nb = 32 * pw + 16 * u + 4 * g4;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const int p = 16 * pt + l16;
+                f32x4 v = {0.f, 0.f, 0.f, 0.f};
+                if (kFullMode) {
+                    if (seg == 0) {
+                        if (a.h0) {
+                            const size_t o = ((size_t)bh * kP + p) * kN + nb;
+                            if (a.st_bf16) {
+                                const uint2 q = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.h0) + o);
+                                v = f32x4{lo_f(q.x), hi_f(q.x), lo_f(q.y), hi_f(q.y)};
+                            } else {
+                                const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(a.h0) + o);
+                                v = f32x4{f.x, f.y, f.z, f.w};
+                            }
+                        }
+                        if (a.Bp0 && a.xp0) {
+                            const float d0 = dtg[0] * (1.f - lamg[0]);
+                            const uint16_t* bp = static_cast<const uint16_t*>(a.Bp0) + (size_t)bh * R * kN;
+                            const uint16_t* xp = static_cast<const uint16_t*>(a.xp0) + (size_t)bh * R * kP;
+#pragma unroll
+                            for (int r = 0; r < R; ++r) {
+                                const float xv = d0 * bf16_bits_to_f32(xp[r * kP + p]);
+#pragma unroll
+                                for (int m = 0; m < 4; ++m) v[m] += xv * bf16_bits_to_f32(bp[r * kN + nb + m]);
+                            }
+                        }
+                    } else {
+                        const float4 f = *reinterpret_cast<const float4*>(wsHin + (ss * kP + p) * kN + nb);
+                        v = f32x4{f.x, f.y, f.z, f.w};
+                    }
+                }
+                hacc[u][pt] = v;
+            }
+        }
+        float lam_sum = 0.f;
+
+        // raw key rows of block gb of the segment, through buffer loads bounded at the
+        // segment end (rows of later tokens read zero)
+        const uint32_t bsb = (uint32_t)bstride * 2u, xsb = (uint32_t)xstride * 2u;
+        // prefetch ring: slot J % DP holds block J's raw rows, fetched DP blocks ahead
+        constexpr int DP = NKB >= 4 ? 4 : 2;
+        uint32_t rgB[DP][PR], rgX[DP][PR];
+        auto fetch = [&](int gb, uint32_t (&pb)[PR], uint32_t (&px)[PR]) {
+            const int cc = gb / NKB, J = gb % NKB;
+            const int t0 = T0 + cc * Q + (kKB * J + 4 * pw) / R;
+            const int nt = __builtin_amdgcn_readfirstlane(min(max(T1 - t0, 0), NTK));
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg + (size_t)t0 * bstride, (uint32_t)nt * bsb);
+            const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xg + (size_t)t0 * xstride, (uint32_t)nt * xsb);
+#pragma unroll
+            for (int rr = 0; rr < PR; ++rr) {
+                const int u = tko(rr), r = rr % R;
+                pb[rr] = __builtin_amdgcn_raw_buffer_load_b32(rb, (int)(u * bsb) + 4 * lane + 256 * r, 0, 0);
+                px[rr] = __builtin_amdgcn_raw_buffer_load_b32(rx, (int)(u * xsb) + 4 * (lane & 31) + 128 * r, 0, 0);
+            }
+        };
+        // turn the rows of block J and write its tiles: Bn [32 j][128 n] (scores), and in
+        // the permuted key order (group q: keys 4 q .. 4 q + 3, then 16 + 4 q ..) BvT
+        // [128 n][32] = (v Bt)^T and XT [64 p][32].  Rows of tokens past the chunk's
+        // valid ones need no masking: their raw rows read zero and their weights and v
+        // are zero (dt = 0), so only finite values (the turned bias) reach the tiles.
+        auto store_block = [&](int J, const uint32_t (&pb)[PR], const uint32_t (&px)[PR]) {
+            char* buf = smem + (J & 1) * kBufBytes;
+            // per-row angle and v, all read before any tile write (rows of one token
+            // share the reads)
+            f16x2 csr[PR];
+            float vvr[PR];
+#pragma unroll
+            for (int rr = 0; rr < PR; ++rr) {
+                const int row = rr < 4 ? 4 * pw + rr : 12 + 4 * pw + rr;
+                const int t = (kKB * J + row) / R;
+                csr[rr] = sCS[t * 64 + lane];
+                vvr[rr] = sV[t];
+            }
+            uint32_t bvw[PR];
+#pragma unroll
+            for (int rr = 0; rr < PR; ++rr) {
+                const int row = rr < 4 ? 4 * pw + rr : 12 + 4 * pw + rr;
+                const int r = rr % R;
+                const float cs = (float)csr[rr][0], sn = (float)csr[rr][1];
+                const float e = lo_f(pb[rr]) + bb[r].x, o = hi_f(pb[rr]) + bb[r].y;
+                const float b0 = e * cs - o * sn;
+                const float b1 = e * sn + o * cs;
+                if (kFullMode)
+                    *reinterpret_cast<uint32_t*>(buf + bn_off(row, lane >> 2) + (lane & 3) * 4) = pack2(b0, b1);
+                bvw[rr] = pack2(b0 * vvr[rr], b1 * vvr[rr]);
+            }
+            uint32_t bv0[4], bv1[4], xt0[4], xt1[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                bv0[q] = __builtin_amdgcn_perm(bvw[2 * q + 1], bvw[2 * q], 0x05040100u);
+                bv1[q] = __builtin_amdgcn_perm(bvw[2 * q + 1], bvw[2 * q], 0x07060302u);
+                xt0[q] = __builtin_amdgcn_perm(px[2 * q + 1], px[2 * q], 0x05040100u);
+                xt1[q] = __builtin_amdgcn_perm(px[2 * q + 1], px[2 * q], 0x07060302u);
+            }
+            char* bvt = buf + kBnBytes;
+            char* xtt = buf + kBnBytes + kBvBytes;
+            *reinterpret_cast<uint4*>(bvt + q4_off(2 * lane, pw)) = uint4{bv0[0], bv0[1], bv0[2], bv0[3]};
+            *reinterpret_cast<uint4*>(bvt + q4_off(2 * lane + 1, pw)) = uint4{bv1[0], bv1[1], bv1[2], bv1[3]};
+            if (lane < 32) {
+                *reinterpret_cast<uint4*>(xtt + q4_off(2 * lane, pw)) = uint4{xt0[0], xt0[1], xt0[2], xt0[3]};
+                *reinterpret_cast<uint4*>(xtt + q4_off(2 * lane + 1, pw)) = uint4{xt1[0], xt1[1], xt1[2], xt1[3]};
+            }
+        };
+        // dt, lam of the chunk at cstart and of the token after it (wave 4: lanes over tokens)
+        float rgDt[TPL], rgLam[TPL], rgDnT = 0.f, rgDnL = 0.f;
+        auto fetch_scalars = [&](int cstart) {
+            if (pw == 0) {
+#pragma unroll
+                for (int k = 0; k < TPL; ++k) {
+                    const int t = lane * TPL + k;
+                    const bool ok = t < Q && cstart + t < T1;
+                    rgDt[k] = ok ? dtg[(size_t)(cstart + t) * H] : 0.f;
+                    rgLam[k] = ok ? lamg[(size_t)(cstart + t) * H] : 0.f;
+                }
+                if (lane == (Q - 1) / TPL) {
+                    const bool ok = cstart + Q < L;
+                    rgDnT = ok ? dtg[(size_t)(cstart + Q) * H] : 0.f;
+                    rgDnL = ok ? lamg[(size_t)(cstart + Q) * H] : 0.f;
+                }
+            }
+        };
+#pragma unroll
+        for (int d = 0; d < DP; ++d) fetch(d, rgB[d], rgX[d]);
+        fetch_scalars(T0);
+
+        int cidx = 0;
+        for (int c0 = T0; c0 < T1; c0 += Q, ++cidx) {
+            // (A) state snapshot (bf16, the carry readout's operand); theta staging; wave 4
+            //     scans the log-decays and tables the per-token scalars
+            if (kFullMode) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int nb = 32 * pw + 16 * u + 4 * g4;
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt) {
+                        const int p = 16 * pt + l16;
+                        *reinterpret_cast<uint2*>(smem + LY::hs + hs_off(p, nb >> 3) + ((nb >> 2) & 1) * 8) =
+                            uint2{pack2(hacc[u][pt][0], hacc[u][pt][1]), pack2(hacc[u][pt][2], hacc[u][pt][3])};
+                    }
+                }
+            }
+            stage_theta(rgTh);
+            load_theta(c0 + Q, rgTh);
+            if (pw == 0) {
+                float la[TPL], gm[TPL], dl[TPL];
+                float lsum = 0.f;
+#pragma unroll
+                for (int k = 0; k < TPL; ++k) {
+                    const int t = lane * TPL + k;
+                    const float dt = rgDt[k], lm = rgLam[k];
+                    la[k] = -dt * ah;
+                    gm[k] = lm * dt;
+                    dl[k] = dt * (1.f - lm);
+                    if (t < Q) sDt[t] = dt;
+                    lsum += la[k];
+                    la[k] = lsum;
+                }
+                const float incl = group_scan<64>(lsum, lane);
+                const float excl = incl - lsum;
+                const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
+                const float le = tot * kLog2e;
+                const float nx = dpp_read<0x130>(dl[0]);           // wave_shl:1
+                const float dnext = rgDnT * (1.f - rgDnL);
+#pragma unroll
+                for (int k = 0; k < TPL; ++k) {
+                    const int t = lane * TPL + k;
+                    const float dn = (k + 1 < TPL) ? dl[k + 1] : ((t + 1 < Q) ? nx : dnext);
+                    if (t < Q) {
+                        const float l2t = (excl + la[k]) * kLog2e;
+                        sL2[t] = l2t;
+                        sG1[t] = gm[k] + dn;
+                        sGam[t] = gm[k];
+                        sV[t] = __builtin_amdgcn_exp2f(le - l2t) * (gm[k] + dn);
+                    }
+                }
+                if (lane == 0) sMisc[0] = le;
+                lam_sum += tot;
+            }
+            fetch_scalars(c0 + Q);
+            __syncthreads();
+            angles();
+            __syncthreads();
+            // (C) the state decays over the whole chunk before its writes land; block 0
+            {
+                const float f = exp2f(sMisc[0]);
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt) hacc[u][pt] = hacc[u][pt] * f;
+            }
+            store_block(0, rgB[0], rgX[0]);
+            __syncthreads();
+            // (D) per block: the state update from block J; block J + 1's tiles; refill
+#pragma unroll 1
+            for (int J0 = 0; J0 < NKB; J0 += DP) {
+#pragma unroll
+                for (int d = 0; d < DP; ++d) {
+                    const int J = J0 + d;
+                    fetch(cidx * NKB + J + DP, rgB[d], rgX[d]);
+                    {
+                        const char* buf = smem + (J & 1) * kBufBytes;
+                        const char* bvb = buf + kBnBytes;
+                        const char* xtb = buf + kBnBytes + kBvBytes;
+                        bf16x8 av[2];
+#pragma unroll
+                        for (int u = 0; u < 2; ++u)
+                            av[u] = *reinterpret_cast<const bf16x8*>(bvb + q4_off(32 * pw + 16 * u + l16, g4));
+#pragma unroll
+                        for (int pt = 0; pt < 4; ++pt) {
+                            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(xtb + q4_off(16 * pt + l16, g4));
+#pragma unroll
+                            for (int u = 0; u < 2; ++u) hacc[u][pt] = mfma(av[u], bv, hacc[u][pt]);
+                        }
+                    }
+                    if (J + 1 < NKB) store_block(J + 1, rgB[(d + 1) % DP], rgX[(d + 1) % DP]);
+                    __syncthreads();
+                }
+            }
+        }
+        // ---- end of the stream / segment: the state ----
+        if (!kFullMode) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int nb = 32 * pw + 16 * u + 4 * g4;
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const int p = 16 * pt + l16;
+                    *reinterpret_cast<float4*>(wsHloc + (ss * kP + p) * kN + nb) =
+                        float4{hacc[u][pt][0], hacc[u][pt][1], hacc[u][pt][2], hacc[u][pt][3]};
+                }
+            }
+            if (pw == 0 && lane == 0) wsLam[ss] = lam_sum;
+        } else if (last_seg && a.h1) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int nb = 32 * pw + 16 * u + 4 * g4;
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const int p = 16 * pt + l16;
+                    const size_t o = ((size_t)bh * kP + p) * kN + nb;
+                    if (a.st_bf16)
+                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.h1) + o) =
+                            uint2{pack2(hacc[u][pt][0], hacc[u][pt][1]), pack2(hacc[u][pt][2], hacc[u][pt][3])};
+                    else
+                        *reinterpret_cast<float4*>(static_cast<float*>(a.h1) + o) =
+                            float4{hacc[u][pt][0], hacc[u][pt][1], hacc[u][pt][2], hacc[u][pt][3]};
+                }
+            }
+        }
+    }
+
+    // ---- end of the stream / segment: phase and previous write (all threads; sPhic holds
+    //      the final phase since the last chunk's angle section) ----
+    if (!kFullMode) {
+        for (int i = tid; i < np; i += kThreads) wsDphi[ss * np + i] = sPhic[i];
+    } else if (last_seg) {
+        if (a.phi1)
+            for (int i = tid; i < np; i += kThreads) a.phi1[(size_t)bh * np + i] = sPhic[i];
+        if (a.Bp1 && a.xp1) {
+            const int t = L - 1;
+            for (int e = tid; e < R * kN / 2; e += kThreads) {
+                const int r = e / (kN / 2), i = e % (kN / 2);
+                const uint32_t raw = *reinterpret_cast<const uint32_t*>(Bg + (size_t)t * bstride + r * kN + 2 * i);
+                float b0 = lo_f(raw) + (a.Bb ? a.Bb[((size_t)h * R + r) * kN + 2 * i] : 0.f);
+                float b1 = hi_f(raw) + (a.Bb ? a.Bb[((size_t)h * R + r) * kN + 2 * i + 1] : 0.f);
+                if (i < np) {
+                    float sn, cs;
+                    sincosf(sPhic[i], &sn, &cs);
+                    const float e0 = b0;
+                    b0 = e0 * cs - b1 * sn;
+                    b1 = e0 * sn + b1 * cs;
+                }
+                *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.Bp1) + ((size_t)bh * R + r) * kN + 2 * i) = pack2(b0, b1);
+            }
+            for (int e = tid; e < R * kP; e += kThreads)
+                static_cast<uint16_t*>(a.xp1)[(size_t)bh * R * kP + e] = Xg[(size_t)t * xstride + e];
+        }
+    }
+}
+
 // Pass 2 of the segmented schedule: the affine carry recurrence over segments.
 // Thread = one (p, n-pair) of one stream; loops over the segments in order.
 //   Hin[0]   = h0 + d_0 X_prev0^T Bt_prev0                (folded initial carry)
@@ -845,24 +1521,31 @@ __global__ __launch_bounds__(256) void carry_pass_kernel(ScanArgs a) {
     }
 }
 
-template <int R, int Q>
+template <int R, int Q, bool WS>
 hipError_t launch_rq(const ScanArgs& a, hipStream_t st) {
     const size_t lds = Layout<Q>::total;
     const int nblk = a.b * a.H * a.nseg;
+    void (*ksum)(ScanArgs);
+    void (*kfull)(ScanArgs);
+    if constexpr (WS) {
+        ksum = &scan_ws_kernel<R, Q, kSummary>;
+        kfull = &scan_ws_kernel<R, Q, kFull>;
+    } else {
+        ksum = &scan_mfma_kernel<R, Q, kSummary>;
+        kfull = &scan_mfma_kernel<R, Q, kFull>;
+    }
     hipError_t e;
     if (a.nseg > 1) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_mfma_kernel<R, Q, kSummary>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(ksum), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((scan_mfma_kernel<R, Q, kSummary>), dim3(nblk), dim3(kThreads), lds, st, a);
+        hipLaunchKernelGGL(ksum, dim3(nblk), dim3(kThreads), lds, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL(carry_pass_kernel, dim3((kP * kN / 2 + 255) / 256, a.b * a.H), dim3(256), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_mfma_kernel<R, Q, kFull>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfull), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_mfma_kernel<R, Q, kFull>), dim3(nblk), dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL(kfull, dim3(nblk), dim3(kThreads), lds, st, a);
     return hipGetLastError();
 }
 
@@ -884,15 +1567,16 @@ size_t scan_mfma_workspace_bytes(const ScanArgs& a) {
 
 hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t st) {
     switch (a.R * 1000 + a.Q) {
-        case 1064: return launch_rq<1, 64>(a, st);
-        case 1128: return launch_rq<1, 128>(a, st);
-        case 2032: return launch_rq<2, 32>(a, st);
-        case 2064: return launch_rq<2, 64>(a, st);
-        case 2128: return launch_rq<2, 128>(a, st);
-        case 4016: return launch_rq<4, 16>(a, st);
-        case 4032: return launch_rq<4, 32>(a, st);
-        case 4064: return launch_rq<4, 64>(a, st);
-        case 4128: return launch_rq<4, 128>(a, st);
+        // chunks of at most 256 rows: the warp-specialised kernel
+        case 1064: return launch_rq<1, 64, true>(a, st);
+        case 1128: return launch_rq<1, 128, true>(a, st);
+        case 2032: return launch_rq<2, 32, true>(a, st);
+        case 2064: return launch_rq<2, 64, true>(a, st);
+        case 2128: return launch_rq<2, 128, true>(a, st);
+        case 4016: return launch_rq<4, 16, true>(a, st);
+        case 4032: return launch_rq<4, 32, true>(a, st);
+        case 4064: return launch_rq<4, 64, true>(a, st);
+        case 4128: return launch_rq<4, 128, false>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
