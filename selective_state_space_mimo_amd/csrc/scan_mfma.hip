@@ -89,11 +89,19 @@ __device__ __forceinline__ int bn_off(int j, int grp) { return j * 256 + ((grp ^
 __device__ __forceinline__ int hs_off(int p, int grp) { return p * 256 + ((grp ^ (p & 15)) << 4); }
 __device__ __forceinline__ int q4_off(int row, int grp) { return row * 64 + ((grp ^ ((row >> 1) & 3)) << 4); }
 
+// (cos, sin) table entry: fp32 pairs where the chunk's table fits, fp16 pairs for 128
+template <int Q>
+using cs_t = typename std::conditional<(Q <= 64), float2, f16x2>::type;
+__device__ __forceinline__ float2 cs_get(float2 v) { return v; }
+__device__ __forceinline__ float2 cs_get(f16x2 v) { return float2{(float)v[0], (float)v[1]}; }
+__device__ __forceinline__ void cs_put(float2& d, float c, float s) { d = float2{c, s}; }
+__device__ __forceinline__ void cs_put(f16x2& d, float c, float s) { d = f16x2{(_Float16)c, (_Float16)s}; }
+
 template <int Q>
 struct Layout {
     static constexpr int hs = 2 * kBufBytes;
     static constexpr int cs = hs + kHsBytes;                  // half2 [Q][64]: (cos, sin) per token and pair
-    static constexpr int cbias = cs + Q * 64 * 4;             // float [4][128]
+    static constexpr int cbias = cs + Q * 64 * (int)sizeof(cs_t<Q>);   // float [4][128]
     static constexpr int l2 = cbias + 4 * kN * 4;             // float [Q] each below
     static constexpr int g1 = l2 + Q * 4;
     static constexpr int gam = g1 + Q * 4;
@@ -163,6 +171,7 @@ __global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
     constexpr bool kFullMode = MODE == kFull;
     static_assert(NKB % D == 0, "ring size must divide the blocks per chunk");
     using LY = Layout<Q>;
+    static_assert(std::is_same<cs_t<Q>, f16x2>::value, "this kernel reads fp16 (cos, sin) pairs");
     extern __shared__ __attribute__((aligned(16))) char smem[];
     float* sL2 = reinterpret_cast<float*>(smem + LY::l2);
     float* sG1 = reinterpret_cast<float*>(smem + LY::g1);
@@ -823,7 +832,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
     float* sV = reinterpret_cast<float*>(smem + LY::vs);
     float* sDt = reinterpret_cast<float*>(smem + LY::dtv);
     float* sPhic = reinterpret_cast<float*>(smem + LY::phic);
-    f16x2* sCS = reinterpret_cast<f16x2*>(smem + LY::cs);
+    cs_t<Q>* sCS = reinterpret_cast<cs_t<Q>*>(smem + LY::cs);
     float* sCb = reinterpret_cast<float*>(smem + LY::cbias);
     float* sMisc = reinterpret_cast<float*>(smem + LY::misc);
     float* stage = reinterpret_cast<float*>(smem + LY::stg);
@@ -872,7 +881,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
         sPhic[i] = v;
     }
     for (int e = tid; e < Q * 64; e += kThreads)
-        if ((e & 63) >= np) sCS[e] = f16x2{(_Float16)1.f, (_Float16)0.f};
+        if ((e & 63) >= np) cs_put(sCS[e], 1.f, 0.f);
 
     // theta of the chunk at cstart (all threads: token tid / 8, pairs 8 (tid % 8) + u),
     // one buffer load per value, bounded at the segment end
@@ -926,7 +935,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
                 for (int u = 0; u < TPT; ++u) {
                     float sn, cs;
                     __sincosf(base + inc[u], &sn, &cs);
-                    sCS[(k * TPT + u) * 64 + i] = f16x2{(_Float16)cs, (_Float16)sn};
+                    cs_put(sCS[(k * TPT + u) * 64 + i], cs, sn);
                 }
                 if (k == TPP - 1) sPhic[i] = wrap_2pi(base + inc[TPT - 1]);
             }
@@ -987,12 +996,13 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
                         cq[k][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(crow));
                     }
                 }
-                if (c0 > T0) store_y(c0 - Q, Q);
             }
             stage_theta(rgTh);
             load_theta(c0 + Q, rgTh);
             __syncthreads();
             angles();
+            // the previous chunk's outputs, after this chunk's loads are on their way
+            if (kFullMode && c0 > T0) store_y(c0 - Q, Q);
             __syncthreads();
             // (C) C tiles to the operand layout (row l16, n = 32 ks + 8 g4 ...), bias and
             //     turn; carry readout Y^T = exp(l_t) Hf Ct^T
@@ -1023,15 +1033,16 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
                         const uint4 raw = __builtin_bit_cast(uint4, cq[k][ks]);
                         const float4 b0 = *reinterpret_cast<const float4*>(sCb + r * kN + n0);
                         const float4 b1 = *reinterpret_cast<const float4*>(sCb + r * kN + n0 + 4);
-                        const uint4 csr = *reinterpret_cast<const uint4*>(sCS + t * 64 + n0 / 2);
-                        const uint32_t csw[4] = {csr.x, csr.y, csr.z, csr.w};
+                        cs_t<Q> csw[4];
+#pragma unroll
+                        for (int pp = 0; pp < 4; ++pp) csw[pp] = sCS[t * 64 + n0 / 2 + pp];
                         const float v[8] = {lo_f(raw.x) + b0.x, hi_f(raw.x) + b0.y, lo_f(raw.y) + b0.z, hi_f(raw.y) + b0.w,
                                             lo_f(raw.z) + b1.x, hi_f(raw.z) + b1.y, lo_f(raw.w) + b1.z, hi_f(raw.w) + b1.w};
                         bf16x8 q;
 #pragma unroll
                         for (int pp = 0; pp < 4; ++pp) {
-                            const f16x2 cc = __builtin_bit_cast(f16x2, csw[pp]);
-                            const float cs = (float)cc[0], sn = (float)cc[1];
+                            const float2 cc = cs_get(csw[pp]);
+                            const float cs = cc.x, sn = cc.y;
                             const float e = v[2 * pp], o = v[2 * pp + 1];
                             q[2 * pp] = (bf16)(e * cs - o * sn);
                             q[2 * pp + 1] = (bf16)(e * sn + o * cs);
@@ -1251,13 +1262,13 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
             char* buf = smem + (J & 1) * kBufBytes;
             // per-row angle and v, all read before any tile write (rows of one token
             // share the reads)
-            f16x2 csr[PR];
+            const int tb = (kKB * J + 4 * pw) / R;              // token of row 4 pw
+            float2 csr[PR];
             float vvr[PR];
 #pragma unroll
             for (int rr = 0; rr < PR; ++rr) {
-                const int row = rr < 4 ? 4 * pw + rr : 12 + 4 * pw + rr;
-                const int t = (kKB * J + row) / R;
-                csr[rr] = sCS[t * 64 + lane];
+                const int t = tb + tko(rr);
+                csr[rr] = cs_get(sCS[t * 64 + lane]);
                 vvr[rr] = sV[t];
             }
             uint32_t bvw[PR];
@@ -1265,7 +1276,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
             for (int rr = 0; rr < PR; ++rr) {
                 const int row = rr < 4 ? 4 * pw + rr : 12 + 4 * pw + rr;
                 const int r = rr % R;
-                const float cs = (float)csr[rr][0], sn = (float)csr[rr][1];
+                const float cs = csr[rr].x, sn = csr[rr].y;
                 const float e = lo_f(pb[rr]) + bb[r].x, o = hi_f(pb[rr]) + bb[r].y;
                 const float b0 = e * cs - o * sn;
                 const float b1 = e * sn + o * cs;
