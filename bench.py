@@ -31,6 +31,39 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+CSRC = os.path.join(ROOT, "selective_state_space_mimo_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+# sources that define each measured kernel (the counters stand only while these are unchanged)
+KERNEL_SOURCES = {"scan": ("scan_mfma.hip", "m3_internal.h"), "decode": ("decode.hip", "m3_internal.h")}
+
+
+def source_sha(kind):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kind, workload):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when
+    there is none or the kernel's sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            lines = fh.read().splitlines()
+    except OSError:
+        return None
+    sha = source_sha(kind)
+    for ln in lines:
+        ln = ln.strip()
+        if not ln.startswith("traffic:"):
+            continue
+        kv = dict(f.split("=", 1) for f in ln[len("traffic:"):].split() if "=" in f)
+        if kv.get("kind") == kind and kv.get("workload") == workload and kv.get("source_sha256") == sha:
+            return float(kv["bytes_per_launch"])
+    return None
 
 
 def parse():
@@ -43,6 +76,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--copy-mib", type=int, default=1024, help="size of the 'copy' calibration workload")
     return ap.parse_args()
 
 
@@ -212,28 +246,60 @@ def run_decode(torch, m3, cfg, nsteps):
     return out
 
 
+def run_copy(torch, mib):
+    """A plain device-to-device copy of a known size: the calibration kernel for
+    the HBM byte counters (not part of the method)."""
+    dev = torch.device("cuda:0")
+    src = torch.empty(mib * (1 << 20) // 4, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty_like(src)
+
+    def call():
+        dst.copy_(src)
+    ms = time_calls(torch, call, 5, 2)
+    nbytes = 2 * src.numel() * 4
+    log("[bench] copy %d MiB: %.3f ms, %.0f GB/s (read + write)" % (mib, ms, nbytes / (ms * 1e-3) / 1e9))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"workload": "copy", "bytes_read": mib << 20, "bytes_written": mib << 20, "ms_per_call": ms,
+            "gbs": nbytes / (ms * 1e-3) / 1e9}
+
+
+def cpu_cores():
+    """Host threads this process may use (affinity, capped by OMP_NUM_THREADS)."""
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
+
+
 def cpu_baseline(cfg, budget_s):
-    """The fp64 C oracle, as it stands, on a bounded sample of the scan
-    workload: whole sequences of the first k (batch, head) streams."""
+    """The fp64 C oracle, as it stands, on a bounded sample of the same scan
+    workload: whole sequences of the first k (batch, head) streams, k chosen so
+    that the timed run takes about ``budget_s`` seconds on the host cores."""
     from m3inputs import make_scan_inputs
     from oracle import ref_cpu
-    cores = len(os.sched_getaffinity(0))
-    d = make_scan_inputs(cfg, batch=1)
-    H = cfg.nheads
+    cores = cpu_cores()
+    d = make_scan_inputs(cfg)
+    H, b = cfg.nheads, cfg.batch
     t0 = time.time()
-    ref_cpu.scan(d, sel=[(0, 0)], nthreads=1)
+    ref_cpu.scan(d, sel=[(0, 0)], nthreads=1, want_y=True)
     one = time.time() - t0                       # one stream, one thread
-    k = int(max(1, min(H, budget_s / max(one, 1e-3) * cores * 0.8)))
-    k = max(cores if k >= cores else k, 1)
-    k = min(k, H)
+    k = int(budget_s * cores / max(one, 1e-4))
+    k = max(1, min(b * H, k))
+    if k >= cores:
+        k -= k % cores                           # whole rounds of the thread pool
+    sel = [(i // H, i % H) for i in range(k)]
     t0 = time.time()
-    ref_cpu.scan(d, sel=[(0, h) for h in range(k)], nthreads=cores)
+    ref_cpu.scan(d, sel=sel, nthreads=cores, want_y=True)
     dt = time.time() - t0
     head_tokens = k * cfg.seqlen
     tok_s = head_tokens / dt / H                # a token is H head-tokens
+    del d
     return {"value": tok_s, "unit": "tokens/s", "cores": min(cores, k), "kind": "oracle",
-            "sample": "%s: %d of %d heads of batch 0, full L=%d (%d head-tokens) in %.1fs, fp64 C recurrence" % (
-                cfg.name, k, H, cfg.seqlen, head_tokens, dt)}
+            "sample": "%s: the first %d of %d (batch, head) streams, full L=%d (%d head-tokens, %.2f%% of the "
+                      "workload) in %.1f s; fp64 sequential recurrence in C, one stream per thread" % (
+                cfg.name, k, b * H, cfg.seqlen, head_tokens, 100.0 * k / (b * H), dt)}
 
 
 def main():
@@ -251,15 +317,20 @@ def main():
     wl = [w.strip() for w in args.workloads.split(",") if w.strip()]
     res = {}
     names = {"scan2": "siso_bf16_mamba2", "scan3": "mimo_bf16_prefill", "scan5": "mimo_bf16_long",
-             "decode4": "mimo_bf16_decode"}
+             "decode4": "mimo_bf16_decode", "copy": None}
     for w in wl:
-        cfg = config_by_name(names[w])
-        if w.startswith("scan"):
+        cfg = config_by_name(names[w]) if names[w] else None
+        if w == "copy":
+            res[w] = run_copy(torch, args.copy_mib)
+        elif w.startswith("scan"):
             steps = args.steps if w != "scan5" else max(3, args.steps // 4)
             res[w] = run_scan(torch, m3, cfg, steps, args.warmup)
         else:
             res[w] = run_decode(torch, m3, cfg, args.decode_steps)
-    main_w = "scan3" if "scan3" in res else wl[0]
+    main_w = "scan3" if "scan3" in res else [w for w in wl if w != "copy"][0] if any(w != "copy" for w in wl) else "copy"
+    if main_w == "copy":
+        print(json.dumps({"metric": "copy calibration", "value": res["copy"]["gbs"], "unit": "GB/s"}), flush=True)
+        return
     prim = res[main_w]
     cpu = None
     if not args.no_cpu and main_w.startswith("scan"):
@@ -278,7 +349,9 @@ def main():
     }
     if main_w.startswith("scan"):
         line["roofline"] = {"bound": "mfma", "achieved": prim["algo_tflops"], "peak": PEAK_BF16_TFLOPS,
-                            "unit": "TFLOP/s", "frac": prim["mfma_frac"], "traffic": None,
+                            "unit": "TFLOP/s", "frac": prim["mfma_frac"],
+                            "traffic": measured_traffic("scan", prim["workload"]),
+                            "algorithmic_bytes": prim["bytes_per_call"],
                             "hbm_achieved_gbs": prim["algo_gbs"], "hbm_frac": prim["hbm_frac"]}
     if "decode4" in res:
         dd = res["decode4"]
@@ -286,7 +359,10 @@ def main():
                           "us_per_step": dd["ms_per_step"] * 1e3, "us_per_launch": dd["ms_per_launch"] * 1e3,
                           "state_gbs": dd["state_gbs"], "bytes_per_head_step": dd["bytes_per_head_step"]}
         line["roofline_decode"] = {"bound": "hbm", "achieved": dd["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                   "frac": dd["hbm_frac"], "traffic": None}
+                                   "frac": dd["hbm_frac"], "traffic": measured_traffic("decode", dd["workload"]),
+                                   "algorithmic_bytes": dd["bytes_per_step"]}
+    if "copy" in res:
+        line["copy_calibration"] = res["copy"]
     others = {k: v for k, v in res.items() if k != main_w and k.startswith("scan")}
     if others:
         line["scan_other"] = {v["workload"]: {"tokens_per_s": v["tokens_per_s"], "ms_per_call": v["ms_per_call"],

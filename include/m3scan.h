@@ -73,7 +73,11 @@ typedef struct {
     int dstate;       /* N, even, 2..256 */
     int rank;         /* R, 1..8 */
     int npairs;       /* rotating pairs, 0 <= npairs <= N/2 (0 = no rotation) */
-    int chunk;        /* Q: chunk length of the chunked scan, 1..256 (m3_scan_fwd only) */
+    int chunk;        /* Q: chunk length of the chunked scan, 1..256 (m3_scan_fwd only).
+                         A schedule parameter: the result does not depend on it beyond
+                         rounding.  The bf16 matrix-core path (P = 64, N = 128,
+                         R in {1, 2, 4}, Q in {16, 32, 64, 128}) runs chunks of at
+                         most 256 / R tokens and splits a longer request. */
     m3_dtype io_dtype;     /* x, B, C, y, B_prev, x_prev */
     m3_dtype state_dtype;  /* h */
     int nsegments;    /* m3_scan_fwd schedule: 0 = library's choice; k > 0 asks for

@@ -80,8 +80,8 @@ void carry_ranges(const m3_carry* c, const Sizes& s, Range out[4]) {
 
 // Schedule: number of sequence segments per (batch, head) stream and their
 // length in tokens (a multiple of the chunk).
-void choose_segments(const m3_desc* d, int* nseg, int* seglen) {
-    const int L = d->seqlen, Q = d->chunk;
+void choose_segments(const m3_desc* d, int Q, int* nseg, int* seglen) {
+    const int L = d->seqlen;
     const int nchunks = (L + Q - 1) / Q;
     int k = d->nsegments;
     if (k == 0) {
@@ -101,14 +101,15 @@ ScanArgs make_scan_args(const m3_desc* d, const void* x, const void* B, const vo
                         const float* Cb, const m3_carry* init, void* y, const m3_carry* fin) {
     ScanArgs a{};
     a.b = d->batch; a.L = d->seqlen; a.H = d->nheads; a.G = d->ngroups; a.P = d->headdim;
-    a.N = d->dstate; a.R = d->rank; a.np = d->npairs; a.Q = d->chunk;
+    a.N = d->dstate; a.R = d->rank; a.np = d->npairs;
     a.io_bf16 = d->io_dtype == M3_BF16; a.st_bf16 = d->state_dtype == M3_BF16;
+    a.Q = scan_mfma_chunk(a.io_bf16, a.P, a.N, a.R, d->chunk);
     a.x = x; a.B = B; a.C = C; a.dt = dt; a.lam = lam; a.theta = d->npairs ? theta : nullptr;
     a.A_log = A_log; a.Bb = Bb; a.Cb = Cb;
     if (init) { a.h0 = init->h; a.phi0 = d->npairs ? init->phi : nullptr; a.Bp0 = init->B_prev; a.xp0 = init->x_prev; }
     a.y = y;
     if (fin) { a.h1 = fin->h; a.phi1 = d->npairs ? fin->phi : nullptr; a.Bp1 = fin->B_prev; a.xp1 = fin->x_prev; }
-    choose_segments(d, &a.nseg, &a.seglen);
+    choose_segments(d, a.Q, &a.nseg, &a.seglen);
     return a;
 }
 

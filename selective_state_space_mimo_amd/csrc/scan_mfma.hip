@@ -53,7 +53,8 @@ namespace m3 {
 
 namespace {
 
-constexpr int kP = 64, kN = 128, kKB = 32, kNW = 8, kThreads = 64 * kNW, kRPW = kKB / kNW;
+constexpr int kP = 64, kN = 128, kKB = 32, kNW = 8, kThreads = 64 * kNW;
+constexpr int kMaxRows = 256;            // rows (tokens x ranks) per chunk
 constexpr float kLog2e = 1.4426950408889634f;
 
 enum Mode { kFull = 0, kSummary = 1 };
@@ -110,22 +111,9 @@ struct Layout {
     static constexpr int phic = dtv + Q * 4;                  // float [64]
     static constexpr int misc = phic + 64 * 4;                // float [16]
     static constexpr int stg = misc + 16 * 4;                 // float [64][Q + 1]: theta, pair-major
-    static constexpr int xsc = stg + ((64 * (Q + 1) * 4 + 15) & ~15);   // per wave 4 KiB: row <-> MFMA layout
-    static constexpr int total = xsc + kNW * 4096;
+    static constexpr int xsc = stg + ((64 * (Q + 1) * 4 + 15) & ~15);   // per consumer 4 KiB: row <-> MFMA layout
+    static constexpr int total = xsc + 4 * 4096;
 };
-
-// Query tile k of wave w (chunk-level tile index), or -1.  Tiles are dealt in
-// groups of 16: wave w takes tile w and tile 15 - w of each group, so that the
-// causal work (tile i meets i + 1 key tiles) is the same for every wave.
-template <int NT>
-__device__ __forceinline__ int query_tile(int w, int k) {
-    if constexpr (NT >= 2 * kNW) {
-        const int g = k >> 1;
-        return (k & 1) == 0 ? 2 * kNW * g + w : 2 * kNW * g + 2 * kNW - 1 - w;
-    } else {
-        return (k == 0 && w < NT) ? w : -1;
-    }
-}
 
 // DPP read of v from another lane; lanes whose source is outside the pattern (or
 // whose row is masked off) read 0.
@@ -152,652 +140,6 @@ __device__ __forceinline__ float group_scan(float v, int lane_in_group) {
         if constexpr (W == 64) v += dpp_read<0x143, 0xc>(v);   // row_bcast:31 into rows 2, 3
     }
     return v;
-}
-
-template <int R, int Q, int MODE>
-__global__ __launch_bounds__(kThreads) void scan_mfma_kernel(ScanArgs a) {
-    constexpr int M = Q * R;                 // rows per chunk
-    constexpr int NKB = M / kKB;             // key blocks per chunk
-    constexpr int NT = M / 16;               // query tiles per chunk
-    constexpr int TPW = NT >= 2 * kNW ? NT / kNW : 1;   // query tiles per wave
-    // prefetch distance (blocks) = ring size; shorter when 4 query tiles per wave
-    // already take the registers
-    constexpr int D = TPW >= 4 ? 2 : (NKB >= 2 ? 2 : NKB);
-    constexpr bool kPrefetchTheta = TPW < 4;
-    constexpr int THP = (Q + 63) / 64;       // theta: passes of 64 tokens (thread: token tid / 8, 8 pairs)
-    constexpr int TPL = Q > 64 ? Q / 64 : 1; // tokens per lane of wave 0
-    constexpr int KT = R >= 4 ? 1 : 4 / R;   // key tokens among a lane's 4 rows of a score tile
-    constexpr int TOKW = kRPW / R > 0 ? kRPW / R : 1;   // tokens of a wave's 4 rows of a key block
-    constexpr bool kFullMode = MODE == kFull;
-    static_assert(NKB % D == 0, "ring size must divide the blocks per chunk");
-    using LY = Layout<Q>;
-    static_assert(std::is_same<cs_t<Q>, f16x2>::value, "this kernel reads fp16 (cos, sin) pairs");
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    float* sL2 = reinterpret_cast<float*>(smem + LY::l2);
-    float* sG1 = reinterpret_cast<float*>(smem + LY::g1);
-    float* sGam = reinterpret_cast<float*>(smem + LY::gam);
-    float* sV = reinterpret_cast<float*>(smem + LY::vs);
-    float* sDt = reinterpret_cast<float*>(smem + LY::dtv);
-    float* sPhic = reinterpret_cast<float*>(smem + LY::phic);
-    f16x2* sCS = reinterpret_cast<f16x2*>(smem + LY::cs);
-    float* sCb = reinterpret_cast<float*>(smem + LY::cbias);
-    float* sMisc = reinterpret_cast<float*>(smem + LY::misc);
-    float* stage = reinterpret_cast<float*>(smem + LY::stg);
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    // the wave index is the same for all lanes of a wave: say so, so that every
-    // decision derived from it is a scalar branch and its values live in SGPRs
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l16 = lane & 15, g4 = lane >> 4;
-    const int H = a.H, L = a.L, np = a.np, nseg = a.nseg;
-
-    // ---- which (batch, head, segment): consecutive logical ids share an XCD --------
-    const int nblk = gridDim.x;
-    const int bid = blockIdx.x;
-    const int logical = (nblk % 8 == 0) ? (bid % 8) * (nblk / 8) + bid / 8 : bid;
-    // logical order: batch, then segment, then head (the heads of one batch and
-    // segment read the same B, C rows)
-    const int h = logical % H;
-    const int rest = logical / H;
-    const int seg = rest % nseg, bi = rest / nseg;
-    const int bh = bi * H + h;
-    const int g = h * a.G / H;
-    const int T0 = seg * a.seglen;
-    const int T1 = min(L, T0 + a.seglen);
-    const bool last_seg = (T1 == L);
-    const float ah = expf(a.A_log[h]);
-    const size_t ss = (size_t)bh * nseg + seg;          // workspace slot
-    const size_t S = (size_t)a.b * H * nseg;
-    float* const wsHloc = a.ws;
-    float* const wsHin = a.ws + S * kP * kN;
-    float* const wsLam = a.ws + 2 * S * kP * kN;
-    float* const wsDphi = wsLam + S;
-    float* const wsPhi = wsDphi + S * np;
-
-    const size_t tokbase = (size_t)bi * L;               // token index base of this batch
-    // row pointers: token 0 of this batch, group g / head h, rank 0
-    const uint16_t* const Bg = static_cast<const uint16_t*>(a.B) + (tokbase * a.G + g) * R * kN;
-    const uint16_t* const Cg = static_cast<const uint16_t*>(a.C) + (tokbase * a.G + g) * R * kN;
-    const uint16_t* const Xg = static_cast<const uint16_t*>(a.x) + (tokbase * H + h) * R * kP;
-    const size_t bstride = (size_t)a.G * R * kN;          // elements between tokens in B, C
-    const size_t xstride = (size_t)H * R * kP;            // ... in x, y
-    const float* const dtg = a.dt + tokbase * H + h;      // dt of token t: dtg[t H]
-    const float* const lamg = a.lam + tokbase * H + h;
-    const float* const thg = np ? a.theta + (tokbase * H + h) * np : a.dt;   // theta[t][i]: thg[t H np + i]
-
-    // ---- per-workgroup set-up ------------------------------------------------------------
-    float2 bb[R];                                        // B bias of this lane's n-pair, per rank
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-        bb[r] = a.Bb ? *reinterpret_cast<const float2*>(a.Bb + ((size_t)h * R + r) * kN + 2 * lane) : float2{0.f, 0.f};
-    if (kFullMode)
-        for (int e = tid; e < R * kN; e += kThreads) sCb[e] = a.Cb ? a.Cb[(size_t)h * R * kN + e] : 0.f;
-    for (int i = tid; i < np; i += kThreads) {
-        float v = 0.f;
-        if (kFullMode) v = seg == 0 ? (a.phi0 ? a.phi0[(size_t)bh * np + i] : 0.f) : wsPhi[ss * np + i];
-        sPhic[i] = v;
-    }
-    // pairs from np on do not turn: their table entries stay (cos, sin) = (1, 0)
-    for (int e = tid; e < Q * 64; e += kThreads)
-        if ((e & 63) >= np) sCS[e] = f16x2{(_Float16)1.f, (_Float16)0.f};
-    // folded state: this wave owns state columns [16 w, 16 w + 16), all P rows,
-    // as four H^T tiles (lane: p = 16 pt + l16, n = 16 w + 4 g4 + m)
-    const int nb = 16 * w + 4 * g4;
-    f32x4 hacc[4];
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-        const int p = 16 * pt + l16;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (kFullMode) {
-            if (seg == 0) {
-                if (a.h0) {
-                    const size_t o = ((size_t)bh * kP + p) * kN + nb;
-                    if (a.st_bf16) {
-                        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.h0) + o);
-                        v = f32x4{lo_f(u.x), hi_f(u.x), lo_f(u.y), hi_f(u.y)};
-                    } else {
-                        const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(a.h0) + o);
-                        v = f32x4{f.x, f.y, f.z, f.w};
-                    }
-                }
-                if (a.Bp0 && a.xp0) {
-                    const float d0 = dtg[0] * (1.f - lamg[0]);
-                    const uint16_t* bp = static_cast<const uint16_t*>(a.Bp0) + (size_t)bh * R * kN;
-                    const uint16_t* xp = static_cast<const uint16_t*>(a.xp0) + (size_t)bh * R * kP;
-#pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const float xv = d0 * bf16_bits_to_f32(xp[r * kP + p]);
-#pragma unroll
-                        for (int m = 0; m < 4; ++m) v[m] += xv * bf16_bits_to_f32(bp[r * kN + nb + m]);
-                    }
-                }
-            } else {
-                const float4 f = *reinterpret_cast<const float4*>(wsHin + (ss * kP + p) * kN + nb);
-                v = f32x4{f.x, f.y, f.z, f.w};
-            }
-        }
-        hacc[pt] = v;
-    }
-    float lam_sum = 0.f;                                 // summary: segment sum of log alpha
-
-    // ---- prefetch rings ------------------------------------------------------------------------
-    // Key block gb of the segment (chunk gb / NKB, block gb % NKB): this wave's
-    // rows jb = 4 w + rr of it are (token, rank) = ((32 J + jb) / R, (32 J + jb) % R).
-    uint32_t rgB[D][kRPW], rgX[D][kRPW];
-    // Raw buffer loads with the record count ending at the segment's last token:
-    // rows of later tokens (and whole blocks past the end) read as zero.
-    const uint32_t bsb = (uint32_t)bstride * 2u, xsb = (uint32_t)xstride * 2u;   // bytes per token
-    auto fetch = [&](int gb, uint32_t (&pb)[kRPW], uint32_t (&px)[kRPW]) {
-        const int c = gb / NKB, J = gb % NKB;
-        const int t0 = T0 + c * Q + (kKB * J + kRPW * w) / R;   // token of this wave's first row (uniform)
-        const int nt = __builtin_amdgcn_readfirstlane(min(max(T1 - t0, 0), TOKW));   // of the rows' tokens, those in the segment
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg + (size_t)t0 * bstride, (uint32_t)nt * bsb);
-        const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xg + (size_t)t0 * xstride, (uint32_t)nt * xsb);
-#pragma unroll
-        for (int rr = 0; rr < kRPW; ++rr) {
-            const int u = rr / R, r = rr % R;                    // token offset, rank (4 w is a multiple of R)
-            pb[rr] = __builtin_amdgcn_raw_buffer_load_b32(rb, (int)(u * bsb) + 4 * lane + 256 * r, 0, 0);
-            px[rr] = __builtin_amdgcn_raw_buffer_load_b32(rx, (int)(u * xsb) + 4 * (lane & 31) + 128 * r, 0, 0);
-        }
-    };
-    // theta of the chunk starting at cstart: thread (token tid / 8 + 64 p, pairs
-    // 8 (tid % 8) + u).  One buffer load per value, the record count ending at
-    // the segment end (later tokens read 0); pairs past np read neighbouring
-    // values that are never used.
-    const int th_t = tid >> 3, th_i = (tid & 7) * 8;
-    auto load_theta = [&](int cstart, float (&th)[kPrefetchTheta ? THP : 1][8]) {
-        const int nt = __builtin_amdgcn_readfirstlane(min(max(T1 - cstart, 0), Q));
-        const __amdgpu_buffer_rsrc_t rt = make_rsrc(thg + (size_t)cstart * H * np, (uint32_t)(nt * H * np) * 4u);
-#pragma unroll
-        for (int pp = 0; pp < (kPrefetchTheta ? THP : 1); ++pp) {
-            const int vo = ((th_t + 64 * pp) * H * np + th_i) * 4;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) th[pp][u] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rt, vo + 4 * u, 0, 0));
-        }
-    };
-    // pair-major staging, rows of Q + 1 floats (the odd stride spreads the banks)
-    auto stage_theta = [&](const float (&th)[8], int t) {
-        if (t < Q) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) stage[(th_i + u) * (Q + 1) + t] = th[u];
-        }
-    };
-    // the next chunk's theta (staging layout) and dt, lam (wave 0: lanes over tokens)
-    float rgTh[kPrefetchTheta ? THP : 1][8], rgDt[TPL], rgLam[TPL], rgDnT = 0.f, rgDnL = 0.f;
-    auto fetch_scalars = [&](int cstart) {
-        if constexpr (kPrefetchTheta) load_theta(cstart, rgTh);
-        if (w == 0) {
-#pragma unroll
-            for (int k = 0; k < TPL; ++k) {
-                const int t = lane * TPL + k;
-                const bool ok = t < Q && cstart + t < T1;
-                rgDt[k] = ok ? dtg[(size_t)(cstart + t) * H] : 0.f;
-                rgLam[k] = ok ? lamg[(size_t)(cstart + t) * H] : 0.f;
-            }
-            // the token after the chunk, in the lane that holds the chunk's last token
-            if (lane == (Q - 1) / TPL) {
-                const bool ok = cstart + Q < L;
-                rgDnT = ok ? dtg[(size_t)(cstart + Q) * H] : 0.f;
-                rgDnL = ok ? lamg[(size_t)(cstart + Q) * H] : 0.f;
-            }
-        }
-    };
-
-#pragma unroll
-    for (int d = 0; d < D; ++d) fetch(d, rgB[d], rgX[d]);
-    fetch_scalars(T0);
-
-    bf16x8 cq[TPW][4];                                   // C tiles (raw bf16 first, then biased + turned)
-    f32x4 yacc[TPW][4];                                  // Y^T tiles
-
-    // turn a ring slot's rows and write key block J's LDS tiles.  This wave's
-    // rows 4 w .. 4 w + 3 of the block cover TOKW tokens of R ranks each; the
-    // angle and v are read once per token.
-    constexpr int RPT = kRPW / TOKW;                       // rows per token here (= R, or 4 when R > 4)
-    auto store_block = [&](int J, int nvalid, const uint32_t (&pb)[kRPW], const uint32_t (&px)[kRPW]) {
-        char* buf = smem + (J & 1) * kBufBytes;
-        uint32_t bvw[kRPW];                                // (v Bt) pair of row rr, bf16x2
-#pragma unroll
-        for (int tk = 0; tk < TOKW; ++tk) {
-            const int j0 = kKB * J + kRPW * w + tk * RPT;     // first row of this token
-            const int t = j0 / R;
-            if (t < nvalid) {                              // uniform
-                const f16x2 c = sCS[t * 64 + lane];
-                const float cs = (float)c[0], sn = (float)c[1];
-                const float vv = sV[t];
-#pragma unroll
-                for (int q = 0; q < RPT; ++q) {
-                    const int rr = tk * RPT + q, r = (j0 + q) % R;
-                    const float e = lo_f(pb[rr]) + bb[r].x, o = hi_f(pb[rr]) + bb[r].y;
-                    const float b0 = e * cs - o * sn;
-                    const float b1 = e * sn + o * cs;
-                    if (kFullMode)
-                        *reinterpret_cast<uint32_t*>(buf + bn_off(kRPW * w + rr, lane >> 2) + (lane & 3) * 4) = pack2(b0, b1);
-                    bvw[rr] = pack2(b0 * vv, b1 * vv);
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < RPT; ++q) {
-                    const int rr = tk * RPT + q;
-                    if (kFullMode)
-                        *reinterpret_cast<uint32_t*>(buf + bn_off(kRPW * w + rr, lane >> 2) + (lane & 3) * 4) = 0u;
-                    bvw[rr] = 0u;
-                }
-            }
-        }
-        // transpose in registers: row rr of the n = 2 lane (2 lane + 1) line is the
-        // low (high) half of bvw[rr]; same for x with p = 2 lane (2 lane + 1)
-        uint32_t bv0[kRPW / 2], bv1[kRPW / 2], xt0[kRPW / 2], xt1[kRPW / 2];
-#pragma unroll
-        for (int q = 0; q < kRPW / 2; ++q) {
-            bv0[q] = __builtin_amdgcn_perm(bvw[2 * q + 1], bvw[2 * q], 0x05040100u);
-            bv1[q] = __builtin_amdgcn_perm(bvw[2 * q + 1], bvw[2 * q], 0x07060302u);
-            xt0[q] = __builtin_amdgcn_perm(px[2 * q + 1], px[2 * q], 0x05040100u);
-            xt1[q] = __builtin_amdgcn_perm(px[2 * q + 1], px[2 * q], 0x07060302u);
-        }
-        // this wave's 4 rows are half (w & 1) of 16-byte group w / 2 of each 32-row line
-        const int grp = w >> 1, half = w & 1;
-        char* bvt = buf + kBnBytes;
-        char* xtt = buf + kBnBytes + kBvBytes;
-        *reinterpret_cast<uint2*>(bvt + q4_off(2 * lane, grp) + 8 * half) = uint2{bv0[0], bv0[1]};
-        *reinterpret_cast<uint2*>(bvt + q4_off(2 * lane + 1, grp) + 8 * half) = uint2{bv1[0], bv1[1]};
-        if (lane < 32) {
-            *reinterpret_cast<uint2*>(xtt + q4_off(2 * lane, grp) + 8 * half) = uint2{xt0[0], xt0[1]};
-            *reinterpret_cast<uint2*>(xtt + q4_off(2 * lane + 1, grp) + 8 * half) = uint2{xt1[0], xt1[1]};
-        }
-    };
-
-    // (E) outputs of the chunk at cst (nv valid tokens).  Issued one chunk late, after
-    // the next chunk's staging waits, so that no wait for loaded data also waits
-    // for these stores.
-    auto store_y = [&](int cst, int nv) {
-        uint16_t* yg = static_cast<uint16_t*>(a.y) + (tokbase * H + h) * R * kP;
-        char* xs = smem + LY::xsc + w * 4096;                // rows of 144 bytes
-        // the lane index, opaque here so that the row offsets below are formed at
-        // the stores rather than kept live across the chunk loop
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-#pragma unroll
-        for (int k = 0; k < TPW; ++k) {
-            const int qt = query_tile<NT>(w, k);
-            if (qt < 0) continue;
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt)
-                *reinterpret_cast<uint2*>(xs + l16 * 144 + (16 * pt + 4 * g4) * 2) =
-                    uint2{pack2(yacc[k][pt][0], yacc[k][pt][1]), pack2(yacc[k][pt][2], yacc[k][pt][3])};
-            // rows 8 i + lane / 8, 16 bytes (p = 8 (lane % 8) ...) per lane
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int j = 8 * i + (ln >> 3);
-                const uint4 v = *reinterpret_cast<const uint4*>(xs + j * 144 + (ln & 7) * 16);
-                const int qi = 16 * qt + j;
-                const int t = qi / R, r = qi % R;
-                if (t < nv) *reinterpret_cast<uint4*>(yg + (size_t)(cst + t) * xstride + r * kP + 8 * (ln & 7)) = v;
-            }
-        }
-    };
-
-    // ---- chunk loop ------------------------------------------------------------------------
-    int cidx = 0;
-    for (int c0 = T0; c0 < T1; c0 += Q, ++cidx) {
-        const int nvalid = min(Q, T1 - c0);
-
-        // (A) state snapshot; C rows straight into the operand registers; the
-        //     prefetched scalars into LDS; wave 0 scans log alpha
-        if (kFullMode) {
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                const int p = 16 * pt + l16;
-                *reinterpret_cast<uint2*>(smem + LY::hs + hs_off(p, nb >> 3) + ((nb >> 2) & 1) * 8) =
-                    uint2{pack2(hacc[pt][0], hacc[pt][1]), pack2(hacc[pt][2], hacc[pt][3])};
-            }
-            // raw C rows, contiguous: load i of tile k holds rows 4 i + lane / 16, 16 bytes
-            // (n = 8 (lane % 16) ...) per lane; padded tokens read the last valid row
-            int ln = lane;                                    // opaque: offsets formed here
-            asm volatile("" : "+v"(ln));
-#pragma unroll
-            for (int k = 0; k < TPW; ++k) {
-                const int qt = query_tile<NT>(w, k);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int qi = 16 * (qt < 0 ? 0 : qt) + 4 * i + (ln >> 4);
-                    const int t = qi / R, r = qi % R;
-                    const uint16_t* crow = Cg + (size_t)(c0 + min(t, nvalid - 1)) * bstride + r * kN + 8 * (ln & 15);
-                    cq[k][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(crow));
-                }
-            }
-        }
-        if constexpr (kPrefetchTheta) {
-#pragma unroll
-            for (int pp = 0; pp < THP; ++pp) stage_theta(rgTh[pp], th_t + 64 * pp);
-        } else {
-            for (int pp = 0; pp < THP; ++pp) {
-                float th[1][8];
-                load_theta(c0 + 64 * pp, th);
-                stage_theta(th[0], th_t + 64 * pp);
-            }
-        }
-        if (w == 0) {
-            float la[TPL], gm[TPL], dl[TPL];
-            float lsum = 0.f;
-#pragma unroll
-            for (int k = 0; k < TPL; ++k) {
-                const int t = lane * TPL + k;
-                const float dt = rgDt[k], lm = rgLam[k];
-                la[k] = -dt * ah;
-                gm[k] = lm * dt;
-                dl[k] = dt * (1.f - lm);
-                if (t < Q) sDt[t] = dt;
-                lsum += la[k];
-                la[k] = lsum;                                  // lane-local inclusive prefix
-            }
-            const float incl = group_scan<64>(lsum, lane);
-            const float excl = incl - lsum;
-            const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
-            const float le = tot * kLog2e;                     // l_e (padded tokens add 0)
-            const float nx = dpp_read<0x130>(dl[0]);           // wave_shl:1: d of the next lane's first token
-            const float dnext = rgDnT * (1.f - rgDnL);         // d of the token after the chunk
-#pragma unroll
-            for (int k = 0; k < TPL; ++k) {
-                const int t = lane * TPL + k;
-                const float dn = (k + 1 < TPL) ? dl[k + 1] : ((t + 1 < Q) ? nx : dnext);
-                if (t < Q) {
-                    const float l2t = (excl + la[k]) * kLog2e;
-                    sL2[t] = l2t;
-                    sG1[t] = gm[k] + dn;
-                    sGam[t] = gm[k];
-                    sV[t] = __builtin_amdgcn_exp2f(le - l2t) * (gm[k] + dn);
-                }
-            }
-            if (lane == 0) sMisc[0] = le;
-            lam_sum += tot;
-        }
-        // the next chunk's scalars are in flight during this chunk
-        fetch_scalars(c0 + Q);
-        __syncthreads();
-
-        if (kFullMode && c0 > T0) store_y(c0 - Q, Q);
-
-        // (B) angles: TPP threads per pair scan dt * theta over the chunk (np <= 64)
-        {
-            auto angles = [&](auto tpp_c) {
-                constexpr int TPP = decltype(tpp_c)::value;
-                constexpr int TPT = Q / TPP;                   // tokens per thread
-                const int k = tid % TPP, i = tid / TPP;
-                if (i < np) {
-                    float inc[TPT];
-                    float loc = 0.f;
-#pragma unroll
-                    for (int u = 0; u < TPT; ++u) {
-                        const int t = k * TPT + u;
-                        loc += sDt[t] * stage[i * (Q + 1) + t];
-                        inc[u] = loc;
-                    }
-                    const float incl = group_scan<TPP>(loc, k);
-                    const float base = sPhic[i] + incl - loc;
-#pragma unroll
-                    for (int u = 0; u < TPT; ++u) {
-                        float sn, cs;
-                        __sincosf(base + inc[u], &sn, &cs);
-                        sCS[(k * TPT + u) * 64 + i] = f16x2{(_Float16)cs, (_Float16)sn};
-                    }
-                    if (k == TPP - 1) sPhic[i] = wrap_2pi(base + inc[TPT - 1]);
-                }
-            };
-            if (np <= 32) angles(std::integral_constant<int, 16>{});
-            else angles(std::integral_constant<int, 8>{});
-        }
-        __syncthreads();
-        const float le2 = sMisc[0];
-        // query token and its log-decay, per query tile of this wave
-        int tq[TPW];
-        float l2q[TPW];
-#pragma unroll
-        for (int k = 0; k < TPW; ++k) {
-            const int qt = query_tile<NT>(w, k);
-            tq[k] = (16 * (qt < 0 ? 0 : qt) + l16) / R;
-            l2q[k] = sL2[tq[k]];
-        }
-
-        // (C) C tiles: to the MFMA operand layout (lane: row l16, n = 32 ks + 8 g4 ...)
-        //     through this wave's scratch; bias and turn in place; carry readout
-        //     Y^T = exp(l_t) Hf Ct^T
-        if (kFullMode) {
-            char* xs = smem + LY::xsc + w * 4096;
-#pragma unroll
-            for (int k = 0; k < TPW; ++k) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    *reinterpret_cast<bf16x8*>(xs + bn_off(4 * i + g4, l16)) = cq[k][i];
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    cq[k][ks] = *reinterpret_cast<const bf16x8*>(xs + bn_off(l16, 4 * ks + g4));
-            }
-#pragma unroll
-            for (int k = 0; k < TPW; ++k) {
-                const int qt = query_tile<NT>(w, k);
-                const int qi = 16 * (qt < 0 ? 0 : qt) + l16;
-                const int t = qi / R, r = qi % R;
-                // rows of padded tokens (t >= nvalid) hold a clamped copy of a valid
-                // row: finite, and their outputs are never stored
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const int n0 = 32 * ks + 8 * g4;
-                    const uint4 raw = __builtin_bit_cast(uint4, cq[k][ks]);
-                    const float4 b0 = *reinterpret_cast<const float4*>(sCb + r * kN + n0);
-                    const float4 b1 = *reinterpret_cast<const float4*>(sCb + r * kN + n0 + 4);
-                    const uint4 csr = *reinterpret_cast<const uint4*>(sCS + t * 64 + n0 / 2);
-                    const uint32_t csw[4] = {csr.x, csr.y, csr.z, csr.w};
-                    const float v[8] = {lo_f(raw.x) + b0.x, hi_f(raw.x) + b0.y, lo_f(raw.y) + b0.z, hi_f(raw.y) + b0.w,
-                                        lo_f(raw.z) + b1.x, hi_f(raw.z) + b1.y, lo_f(raw.w) + b1.z, hi_f(raw.w) + b1.w};
-                    bf16x8 q;
-#pragma unroll
-                    for (int pp = 0; pp < 4; ++pp) {
-                        const f16x2 c = __builtin_bit_cast(f16x2, csw[pp]);
-                        const float cs = (float)c[0], sn = (float)c[1];
-                        const float e = v[2 * pp], o = v[2 * pp + 1];
-                        q[2 * pp] = (bf16)(e * cs - o * sn);
-                        q[2 * pp + 1] = (bf16)(e * sn + o * cs);
-                    }
-                    cq[k][ks] = q;
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            float sc[TPW];
-#pragma unroll
-            for (int k = 0; k < TPW; ++k) {
-                sc[k] = __builtin_amdgcn_exp2f(l2q[k]);
-            }
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                const int p = 16 * pt + l16;
-#pragma unroll
-                for (int k = 0; k < TPW; ++k) yacc[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const bf16x8 av = *reinterpret_cast<const bf16x8*>(smem + LY::hs + hs_off(p, 4 * ks + g4));
-#pragma unroll
-                    for (int k = 0; k < TPW; ++k) yacc[k][pt] = mfma(av, cq[k][ks], yacc[k][pt]);
-                }
-#pragma unroll
-                for (int k = 0; k < TPW; ++k) yacc[k][pt] = yacc[k][pt] * sc[k];
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // the state decays over the whole chunk before this chunk's writes land
-        {
-            const float f = exp2f(le2);
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt) hacc[pt] = hacc[pt] * f;
-        }
-        store_block(0, nvalid, rgB[0], rgX[0]);
-        __syncthreads();
-
-        // (D) key blocks: ring slot J % D holds block J; once block J is in LDS
-        //     the slot is refilled with block J + D (which may be the next chunk's)
-#pragma unroll 1
-        for (int J0 = 0; J0 < NKB; J0 += D) {
-#pragma unroll
-            for (int d = 0; d < D; ++d) {
-                const int J = J0 + d;
-                fetch(cidx * NKB + J + D, rgB[d], rgX[d]);
-                const char* buf = smem + (J & 1) * kBufBytes;
-                const char* bvb = buf + kBnBytes;
-                const char* xtb = buf + kBnBytes + kBvBytes;
-                if (kFullMode) {
-                    // key tiles ka, ka + 1 (the block's rows) against this wave's query
-                    // tiles.  One key tile's operands are live at a time and shared by
-                    // the query tiles; fences keep the phases apart (register pressure).
-                    const int ka = 2 * J;
-                    // log-decay and weight of the key tokens of this lane's rows
-                    float kl2[2][KT], kg1[2][KT];
-#pragma unroll
-                    for (int ab = 0; ab < 2; ++ab)
-#pragma unroll
-                        for (int j = 0; j < KT; ++j) {
-                            const int ts = (16 * (ka + ab) + 4 * g4) / R + j;
-                            kl2[ab][j] = sL2[ts];
-                            kg1[ab][j] = sG1[ts];
-                        }
-                    f32x4 s0[TPW], s1[TPW];
-                    {
-                        bf16x8 op[4];
-#pragma unroll
-                        for (int ks = 0; ks < 4; ++ks)
-                            op[ks] = *reinterpret_cast<const bf16x8*>(buf + bn_off(l16, 4 * ks + g4));
-#pragma unroll
-                        for (int k = 0; k < TPW; ++k) {
-                            s0[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-                            if (query_tile<NT>(w, k) >= ka) {           // uniform
-#pragma unroll
-                                for (int ks = 0; ks < 4; ++ks) s0[k] = mfma(op[ks], cq[k][ks], s0[k]);
-                            }
-                        }
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    {
-                        bf16x8 op[4];
-#pragma unroll
-                        for (int ks = 0; ks < 4; ++ks)
-                            op[ks] = *reinterpret_cast<const bf16x8*>(buf + bn_off(16 + l16, 4 * ks + g4));
-#pragma unroll
-                        for (int k = 0; k < TPW; ++k) {
-                            s1[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-                            if (query_tile<NT>(w, k) > ka) {            // uniform
-#pragma unroll
-                                for (int ks = 0; ks < 4; ++ks) s1[k] = mfma(op[ks], cq[k][ks], s1[k]);
-                            }
-                        }
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    // S'^T = W o S^T, rounded to bf16 as the B operand.  Lane: query
-                    // token tq, key rows 16 kt + 4 g4 + m of key tiles ka (s0), ka + 1 (s1)
-                    bf16x8 bop[TPW];
-#pragma unroll
-                    for (int k = 0; k < TPW; ++k) {
-                        const int qt = query_tile<NT>(w, k);
-                        float wgt[2][KT];
-#pragma unroll
-                        for (int ab = 0; ab < 2; ++ab) {
-#pragma unroll
-                            for (int j = 0; j < KT; ++j) {
-                                const float e = __builtin_amdgcn_exp2f(l2q[k] - kl2[ab][j]);
-                                if (qt > ka + ab) {                      // uniform: key tile before the query tile
-                                    wgt[ab][j] = e * kg1[ab][j];
-                                } else if (qt == ka + ab) {              // the diagonal tile
-                                    const int ts = (16 * (ka + ab) + 4 * g4) / R + j;
-                                    wgt[ab][j] = ts < tq[k] ? e * kg1[ab][j] : (ts == tq[k] ? e * sGam[ts] : 0.f);
-                                } else {
-                                    wgt[ab][j] = 0.f;
-                                }
-                            }
-                        }
-#pragma unroll
-                        for (int m = 0; m < 4; ++m) {
-                            bop[k][m] = (bf16)(s0[k][m] * wgt[0][m * KT / 4]);
-                            bop[k][4 + m] = (bf16)(s1[k][m] * wgt[1][m * KT / 4]);
-                        }
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    // Y^T += X^T S'^T, X^T read in the k order of S'^T:
-                    // keys 4 g4 + 0..3 of tile a, then of tile b
-#pragma unroll
-                    for (int pt = 0; pt < 4; ++pt) {
-                        const int p = 16 * pt + l16;
-                        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(xtb + q4_off(p, g4 >> 1) + (g4 & 1) * 8);
-                        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(xtb + q4_off(p, 2 + (g4 >> 1)) + (g4 & 1) * 8);
-                        const bf16x8 xo = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-                        for (int k = 0; k < TPW; ++k)
-                            if (query_tile<NT>(w, k) >= ka) yacc[k][pt] = mfma(xo, bop[k], yacc[k][pt]);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                // state: Hf^T[n-tile w] += (v Bt)^T X over the block's 32 rows
-                {
-                    const bf16x8 av = *reinterpret_cast<const bf16x8*>(bvb + q4_off(16 * w + l16, g4));
-#pragma unroll
-                    for (int pt = 0; pt < 4; ++pt) {
-                        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(xtb + q4_off(16 * pt + l16, g4));
-                        hacc[pt] = mfma(av, bv, hacc[pt]);
-                    }
-                }
-                if (J + 1 < NKB) store_block(J + 1, nvalid, rgB[(d + 1) % D], rgX[(d + 1) % D]);
-                __syncthreads();
-            }
-        }
-        // the next chunk's block 0 now sits in ring slot 0
-
-    }
-    // the last chunk's outputs
-    if (kFullMode && T1 > T0) store_y(T0 + (T1 - T0 - 1) / Q * Q, (T1 - T0 - 1) % Q + 1);
-
-    // ---- end of the stream / segment ----------------------------------------------------------
-    if (!kFullMode) {
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-            const int p = 16 * pt + l16;
-            *reinterpret_cast<float4*>(wsHloc + (ss * kP + p) * kN + nb) = float4{hacc[pt][0], hacc[pt][1], hacc[pt][2], hacc[pt][3]};
-        }
-        if (tid == 0) wsLam[ss] = lam_sum;
-        for (int i = tid; i < np; i += kThreads) wsDphi[ss * np + i] = sPhic[i];
-    } else if (last_seg) {
-        if (a.h1) {
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                const int p = 16 * pt + l16;
-                const size_t o = ((size_t)bh * kP + p) * kN + nb;
-                if (a.st_bf16)
-                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.h1) + o) =
-                        uint2{pack2(hacc[pt][0], hacc[pt][1]), pack2(hacc[pt][2], hacc[pt][3])};
-                else
-                    *reinterpret_cast<float4*>(static_cast<float*>(a.h1) + o) = float4{hacc[pt][0], hacc[pt][1], hacc[pt][2], hacc[pt][3]};
-            }
-        }
-        if (a.phi1)
-            for (int i = tid; i < np; i += kThreads) a.phi1[(size_t)bh * np + i] = sPhic[i];
-        // previous write after the last token: its biased, turned B (angle = the
-        // final phase) and its x
-        if (a.Bp1 && a.xp1) {
-            const int t = L - 1;
-            for (int e = tid; e < R * kN / 2; e += kThreads) {
-                const int r = e / (kN / 2), i = e % (kN / 2);
-                const uint32_t raw = *reinterpret_cast<const uint32_t*>(Bg + (size_t)t * bstride + r * kN + 2 * i);
-                float b0 = lo_f(raw) + (a.Bb ? a.Bb[((size_t)h * R + r) * kN + 2 * i] : 0.f);
-                float b1 = hi_f(raw) + (a.Bb ? a.Bb[((size_t)h * R + r) * kN + 2 * i + 1] : 0.f);
-                if (i < np) {
-                    float sn, cs;
-                    sincosf(sPhic[i], &sn, &cs);
-                    const float e0 = b0;
-                    b0 = e0 * cs - b1 * sn;
-                    b1 = e0 * sn + b1 * cs;
-                }
-                *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.Bp1) + ((size_t)bh * R + r) * kN + 2 * i) = pack2(b0, b1);
-            }
-            for (int e = tid; e < R * kP; e += kThreads)
-                static_cast<uint16_t*>(a.xp1)[(size_t)bh * R * kP + e] = Xg[(size_t)t * xstride + e];
-        }
-    }
 }
 
 // ---- warp-specialised variant (chunks of at most 256 rows) ----------------------------------
@@ -1532,42 +874,40 @@ __global__ __launch_bounds__(256) void carry_pass_kernel(ScanArgs a) {
     }
 }
 
-template <int R, int Q, bool WS>
+template <int R, int Q>
 hipError_t launch_rq(const ScanArgs& a, hipStream_t st) {
     const size_t lds = Layout<Q>::total;
     const int nblk = a.b * a.H * a.nseg;
-    void (*ksum)(ScanArgs);
-    void (*kfull)(ScanArgs);
-    if constexpr (WS) {
-        ksum = &scan_ws_kernel<R, Q, kSummary>;
-        kfull = &scan_ws_kernel<R, Q, kFull>;
-    } else {
-        ksum = &scan_mfma_kernel<R, Q, kSummary>;
-        kfull = &scan_mfma_kernel<R, Q, kFull>;
-    }
     hipError_t e;
     if (a.nseg > 1) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(ksum), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_ws_kernel<R, Q, kSummary>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(ksum, dim3(nblk), dim3(kThreads), lds, st, a);
+        hipLaunchKernelGGL((scan_ws_kernel<R, Q, kSummary>), dim3(nblk), dim3(kThreads), lds, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL(carry_pass_kernel, dim3((kP * kN / 2 + 255) / 256, a.b * a.H), dim3(256), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfull), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_ws_kernel<R, Q, kFull>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kfull, dim3(nblk), dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((scan_ws_kernel<R, Q, kFull>), dim3(nblk), dim3(kThreads), lds, st, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
+int scan_mfma_chunk(int io_bf16, int P, int N, int R, int Q) {
+    if (!io_bf16 || P != kP || N != kN || !(R == 1 || R == 2 || R == 4)) return Q;
+    return Q * R > kMaxRows ? kMaxRows / R : Q;
+}
+
 bool scan_mfma_supported(const ScanArgs& a) {
     if (!a.io_bf16 || a.P != kP || a.N != kN) return false;
-    const int M = a.Q * a.R;
     if (!(a.R == 1 || a.R == 2 || a.R == 4)) return false;
     if (!(a.Q == 16 || a.Q == 32 || a.Q == 64 || a.Q == 128)) return false;
-    return M >= 64 && M <= 512;
+    const int M = a.Q * a.R;
+    return M >= 64 && M <= kMaxRows;
 }
 
 size_t scan_mfma_workspace_bytes(const ScanArgs& a) {
@@ -1578,16 +918,14 @@ size_t scan_mfma_workspace_bytes(const ScanArgs& a) {
 
 hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t st) {
     switch (a.R * 1000 + a.Q) {
-        // chunks of at most 256 rows: the warp-specialised kernel
-        case 1064: return launch_rq<1, 64, true>(a, st);
-        case 1128: return launch_rq<1, 128, true>(a, st);
-        case 2032: return launch_rq<2, 32, true>(a, st);
-        case 2064: return launch_rq<2, 64, true>(a, st);
-        case 2128: return launch_rq<2, 128, true>(a, st);
-        case 4016: return launch_rq<4, 16, true>(a, st);
-        case 4032: return launch_rq<4, 32, true>(a, st);
-        case 4064: return launch_rq<4, 64, true>(a, st);
-        case 4128: return launch_rq<4, 128, false>(a, st);
+        case 1064: return launch_rq<1, 64>(a, st);
+        case 1128: return launch_rq<1, 128>(a, st);
+        case 2032: return launch_rq<2, 32>(a, st);
+        case 2064: return launch_rq<2, 64>(a, st);
+        case 2128: return launch_rq<2, 128>(a, st);
+        case 4016: return launch_rq<4, 16>(a, st);
+        case 4032: return launch_rq<4, 32>(a, st);
+        case 4064: return launch_rq<4, 64>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

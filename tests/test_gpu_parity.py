@@ -156,6 +156,17 @@ def test_scan_segments_agree(m3):
         assert rel_l2(yk, ys[0]) < 1e-2
 
 
+def test_long_chunk_request_is_split(m3):
+    """A chunk longer than the matrix-core path's 256 rows (R = 4, Q = 128) runs
+    as chunks of 64 tokens: the same schedule, hence the same bits, as asking
+    for 64."""
+    cfg, d = make_small_case(3011, batch=2, seqlen=300, nheads=2, ngroups=1, headdim=64, dstate=128, rank=4,
+                             npairs=32, chunk=128, io_dtype="bf16", rms_bc=True, init_full=True)
+    y128, f128 = _run_scan(m3, d, cfg, chunk=128)
+    y64, f64 = _run_scan(m3, d, cfg, chunk=64)
+    assert torch.equal(y128, y64) and torch.equal(f128["h"], f64["h"])
+
+
 def test_config1_tiny_siso_f32(m3):
     cfg = config_by_name("tiny_siso_f32")
     d = make_scan_inputs(cfg)
