@@ -20,27 +20,30 @@
 //     W(t,s) = exp(l_t - l_s) (g_s + [s<t] dS_s)
 //   Hf_out   = exp(l_e) Hf_in + sum_s v_s X_s^T Bt_s,  v_s = exp(l_e - l_s)(g_s + dS_s)
 //
-// Work decomposition (one workgroup of 8 waves per (batch, head, segment)):
-//   * per chunk, the token-pair weights W (lower triangle, fp16), the (cos, sin)
-//     of every running angle (fp16) and v are tabled in LDS once;
-//   * query rows of a chunk are split into 16-row tiles, dealt to the waves
-//     in a zig-zag so that causal work is balanced; each wave keeps its C
-//     tiles (biased, turned, bf16) in registers as MFMA B operands and its
-//     output tiles Y^T (P x 16) as fp32 accumulators;
-//   * key rows stream through LDS in blocks of 32 (double-buffered); the raw
-//     rows of B and x are fetched into a register ring 2-4 blocks ahead of
-//     their use (across chunk boundaries), so that memory latency overlaps
-//     the MFMA work.  Every wave turns 4 rows of B into Bt (row-major, for
-//     the scores) and (v Bt)^T (for the state update) and stores X^T, all
-//     swizzled so that the 16-byte MFMA operand reads spread over the banks;
-//   * scores S^T = Bt C^T come out of the MFMA with each lane holding one
-//     query column and four key rows; weighted and rounded to bf16 they are
-//     directly the B operand of Y^T += X^T S'^T (the two key tiles of a block
-//     give the 8 k-slots; X^T is read with the same k permutation);
-//   * the P x N state lives in MFMA accumulators (as H^T: each wave owns 16
-//     state columns), updated by Hf^T += (v Bt)^T X; a bf16 copy in LDS is
-//     the A operand of the carry readout Y^T = Hf Ct^T;
-//   * per-chunk prefix sums (log-decay, angles) use wave shuffles.
+// Work decomposition: one workgroup of 8 waves per (batch, head, segment),
+// chunks of M = Q R <= 256 rows, split by role so that each SIMD holds one wave
+// of each kind and vector work overlaps matrix work:
+//   * 4 consumer waves own the chunk's query tiles (16 rows each, dealt so
+//     that the causal work is equal).  Each keeps its C tiles (biased, turned,
+//     bf16) in registers as MFMA B operands and its output tiles Y^T (P x 16) as
+//     fp32 accumulators; per key block it forms the scores S^T = Bt C^T (each
+//     lane: one query column, four key rows), weights them with W -- computed
+//     per lane from the tabled log-decays, exact, never factored -- and feeds
+//     them as bf16 B operands straight into Y^T += X^T S'^T.  The tiles a key
+//     block meets are a suffix of the wave's (ascending) tiles, so each block
+//     runs a straight-line body chosen by that suffix.
+//   * 4 producer waves stream key rows: raw B and x rows are fetched with
+//     bounded buffer loads into a register ring DP blocks ahead (across chunk
+//     boundaries); each producer turns 8 rows of every 32-row block into Bt
+//     (row-major, for the scores) and (v Bt)^T, and stores X^T, in LDS tiles
+//     swizzled for conflict-free 16-byte operand reads.  The producers own the
+//     P x N state as MFMA accumulators (H^T, 32 columns each) and update it with
+//     Hf^T += (v Bt)^T X; a bf16 snapshot in LDS is the consumers' A operand for
+//     the carry readout Y^T = Hf Ct^T.
+//   * per chunk, all waves compute the running angles (fp32 (cos, sin) table
+//     for Q <= 64); one producer scans the log-decays with DPP.
+//   * key blocks are double-buffered in LDS with one barrier per block; both
+//     roles pass the same barriers.
 // Segmented schedule (few streams, long sequences): pass 1 computes, per
 // segment, the folded state from a zero carry in a local angle frame; pass 2
 // runs the affine carry recurrence across segments (turning each summary into
