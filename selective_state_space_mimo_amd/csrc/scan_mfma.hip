@@ -63,6 +63,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 enum Mode { kFull = 0, kSummary = 1 };
 
 typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -213,6 +214,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
     const uint16_t* const Xg = static_cast<const uint16_t*>(a.x) + (tokbase * H + h) * R * kP;
     const size_t bstride = (size_t)a.G * R * kN;
     const size_t xstride = (size_t)H * R * kP;
+    const uint32_t bsb = (uint32_t)bstride * 2u, xsb = (uint32_t)xstride * 2u;   // bytes per token
     const float* const dtg = a.dt + tokbase * H + h;
     const float* const lamg = a.lam + tokbase * H + h;
     const float* const thg = np ? a.theta + (tokbase * H + h) * np : a.dt;
@@ -234,6 +236,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
     auto load_theta = [&](int cstart, float (&th)[THP][8]) {
         int tt = tid;                                         // opaque: offsets formed here
         asm volatile("" : "+v"(tt));
+            tt &= kThreads - 1;                               // a thread index: non-negative
         const int th_t = tt >> 3, th_i = (tt & 7) * 8;
         const int nt = __builtin_amdgcn_readfirstlane(min(max(T1 - cstart, 0), Q));
         const __amdgpu_buffer_rsrc_t rt = make_rsrc(thg + (size_t)cstart * H * np, (uint32_t)(nt * H * np) * 4u);
@@ -247,6 +250,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
     auto stage_theta = [&](const float (&th)[THP][8]) {
         int tt = tid;
         asm volatile("" : "+v"(tt));
+            tt &= kThreads - 1;                               // a thread index: non-negative
         const int th_t = tt >> 3, th_i = (tt & 7) * 8;
 #pragma unroll
         for (int pp = 0; pp < THP; ++pp) {
@@ -264,6 +268,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
             constexpr int TPT = Q / TPP;
             int tt = tid;                                     // opaque: offsets formed here
             asm volatile("" : "+v"(tt));
+            tt &= kThreads - 1;                               // a thread index: non-negative
             const int k = tt % TPP, i = tt / TPP;
             if (i < np) {
                 float inc[TPT];
@@ -301,23 +306,26 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
         // outputs of the chunk at cst (nv valid tokens), through the scratch (rows of
         // 144 bytes) so that every store writes whole rows
         auto store_y = [&](int cst, int nv) {
-            uint16_t* yg = static_cast<uint16_t*>(a.y) + (tokbase * H + h) * R * kP;
-            int ln = lane;                                    // opaque: offsets formed here
+            // rows of tokens at or past nv fall outside the record count: dropped
+            const __amdgpu_buffer_rsrc_t ry = make_rsrc(static_cast<uint16_t*>(a.y) + ((tokbase + cst) * H + h) * R * kP,
+                                                        (uint32_t)nv * xsb);
+            unsigned ln = lane;                               // opaque: offsets formed here
             asm volatile("" : "+v"(ln));
+            ln &= 63u;
 #pragma unroll
             for (int k = 0; k < TPC; ++k) {
                 const int qt = ctile(c, k);
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt)
-                    *reinterpret_cast<uint2*>(xs + (ln & 15) * 144 + (16 * pt + 4 * (ln >> 4)) * 2) =
+                    *reinterpret_cast<uint2*>(xs + (ln & 15u) * 144 + (16 * pt + 4 * (ln >> 4)) * 2) =
                         uint2{pack2(yacc[k][pt][0], yacc[k][pt][1]), pack2(yacc[k][pt][2], yacc[k][pt][3])};
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    const int j = 8 * i + (ln >> 3);
-                    const uint4 v = *reinterpret_cast<const uint4*>(xs + j * 144 + (ln & 7) * 16);
-                    const int qi = 16 * qt + j;
-                    const int t = qi / R, r = qi % R;
-                    if (t < nv) *reinterpret_cast<uint4*>(yg + (size_t)(cst + t) * xstride + r * kP + 8 * (ln & 7)) = v;
+                    const unsigned j = 8 * i + (ln >> 3);
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(xs + j * 144 + (ln & 7u) * 16);
+                    const unsigned qi = 16 * qt + j;
+                    const unsigned t = qi / R, r = qi % R;
+                    __builtin_amdgcn_raw_buffer_store_b128(v, ry, (int)(t * xsb + r * (kP * 2) + 16 * (ln & 7u)), 0, 0);
                 }
             }
         };
@@ -328,17 +336,20 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
             // (A) raw C rows, contiguous (load i of tile k: rows 4 i + lane / 16, n = 8 (lane % 16) ...);
             //     the previous chunk's outputs; theta into the staging area
             if (kFullMode) {
-                int ln = lane;
+                // rows of tokens at or past nvalid read zero (their outputs are never stored)
+                const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cg + (size_t)c0 * bstride, (uint32_t)nvalid * bsb);
+                unsigned ln = lane;                           // opaque: offsets formed here
                 asm volatile("" : "+v"(ln));
+                ln &= 63u;
 #pragma unroll
                 for (int k = 0; k < TPC; ++k) {
                     const int qt = ctile(c, k);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int qi = 16 * qt + 4 * i + (ln >> 4);
-                        const int t = qi / R, r = qi % R;
-                        const uint16_t* crow = Cg + (size_t)(c0 + min(t, nvalid - 1)) * bstride + r * kN + 8 * (ln & 15);
-                        cq[k][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(crow));
+                        const unsigned qi = 16 * qt + 4 * i + (ln >> 4);
+                        const unsigned t = qi / R, r = qi % R;
+                        cq[k][i] = __builtin_bit_cast(
+                            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(t * bsb + r * (kN * 2) + 16 * (ln & 15u)), 0, 0));
                     }
                 }
             }
@@ -356,6 +367,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
             if (kFullMode) {
                 int ln = lane;                                // opaque: offsets formed here
                 asm volatile("" : "+v"(ln));
+                ln &= 63;
                 const int l16 = ln & 15, g4 = ln >> 4;
 #pragma unroll
                 for (int k = 0; k < TPC; ++k) {
@@ -581,7 +593,6 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
 
         // raw key rows of block gb of the segment, through buffer loads bounded at the
         // segment end (rows of later tokens read zero)
-        const uint32_t bsb = (uint32_t)bstride * 2u, xsb = (uint32_t)xstride * 2u;
         // prefetch ring: slot J % DP holds block J's raw rows, fetched DP blocks ahead
         constexpr int DP = NKB >= 4 ? 4 : 2;
         uint32_t rgB[DP][PR], rgX[DP][PR];
