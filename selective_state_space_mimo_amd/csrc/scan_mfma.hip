@@ -428,111 +428,103 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
             }
             __syncthreads();
             // (D) key blocks: scores against this wave's query tiles, weights, Y^T += X^T S'^T.
-            //     A wave's tiles ascend with k, so the tiles that meet key tile 2 J (2 J + 1)
-            //     are those from K0 (K1) on; each (K0, K1) has its own straight-line body.
-#pragma unroll 1
-            for (int J = 0; J < NKB; ++J) {
-                if (kFullMode) {
-                    const int ka = 2 * J;
-                    int k0 = 0;
+            //     A wave's tiles ascend with k, so the tiles that meet key block J are those
+            //     from some K0 on; the blocks run in phases of constant K0, each phase a loop
+            //     over one straight-line body.
+            auto block_body = [&](auto k0c, int J) {
+                constexpr int K0 = decltype(k0c)::value;
+                const int ka = 2 * J;
+                const char* buf = smem + (J & 1) * kBufBytes;
+                const char* xtb = buf + kBnBytes + kBvBytes;
+                float kl2[2][KT], kg1[2][KT];
 #pragma unroll
-                    for (int k = 0; k < TPC; ++k) k0 += ctile(c, k) < ka ? 1 : 0;
-                    const int k1 = k0 + ((k0 < TPC && ctile(c, k0) == ka) ? 1 : 0);
-                    const char* buf = smem + (J & 1) * kBufBytes;
-                    const char* xtb = buf + kBnBytes + kBvBytes;
-                    auto body = [&](auto k0c, auto k1c) {
-                        constexpr int K0 = decltype(k0c)::value, K1 = decltype(k1c)::value;
-                        if constexpr (K0 < TPC) {
-                            float kl2[2][KT], kg1[2][KT];
+                for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
-                            for (int ab = 0; ab < 2; ++ab)
-#pragma unroll
-                                for (int j = 0; j < KT; ++j) {
-                                    const int ts = (16 * (ka + ab) + 4 * g4) / R + j;
-                                    kl2[ab][j] = sL2[ts];
-                                    kg1[ab][j] = sG1[ts];
-                                }
-                            f32x4 s0[TPC], s1[TPC];
-                            {
-                                bf16x8 op[4];
-#pragma unroll
-                                for (int ks = 0; ks < 4; ++ks)
-                                    op[ks] = *reinterpret_cast<const bf16x8*>(buf + bn_off(l16, 4 * ks + g4));
-#pragma unroll
-                                for (int k = K0; k < TPC; ++k) {
-                                    s0[k] = mfma(op[0], cq[k][0], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                                    for (int ks = 1; ks < 4; ++ks) s0[k] = mfma(op[ks], cq[k][ks], s0[k]);
-                                }
-                            }
-                            if constexpr (K1 < TPC) {
-                                bf16x8 op[4];
-#pragma unroll
-                                for (int ks = 0; ks < 4; ++ks)
-                                    op[ks] = *reinterpret_cast<const bf16x8*>(buf + bn_off(16 + l16, 4 * ks + g4));
-#pragma unroll
-                                for (int k = K1; k < TPC; ++k) {
-                                    s1[k] = mfma(op[0], cq[k][0], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                                    for (int ks = 1; ks < 4; ++ks) s1[k] = mfma(op[ks], cq[k][ks], s1[k]);
-                                }
-                            }
-                            __builtin_amdgcn_sched_barrier(0);
-                            // S'^T = W o S^T as bf16 B operands; the diagonal tile of key tile a
-                            // (b) can only be tile K0 (K1)
-                            bf16x8 bop[TPC];
-#pragma unroll
-                            for (int k = K0; k < TPC; ++k) {
-                                float wgt[2][KT];
-#pragma unroll
-                                for (int ab = 0; ab < 2; ++ab) {
-#pragma unroll
-                                    for (int j = 0; j < KT; ++j) {
-                                        if (ab == 1 && k < K1) {
-                                            wgt[ab][j] = 0.f;
-                                            continue;
-                                        }
-                                        const float e = __builtin_amdgcn_exp2f(l2q[k] - kl2[ab][j]);
-                                        wgt[ab][j] = e * kg1[ab][j];
-                                        if (k == (ab ? K1 : K0) && ctile(c, k) == ka + ab) {   // uniform
-                                            const int ts = (16 * (ka + ab) + 4 * g4) / R + j;
-                                            wgt[ab][j] = ts < tq[k] ? wgt[ab][j] : (ts == tq[k] ? e * sGam[ts] : 0.f);
-                                        }
-                                    }
-                                }
-#pragma unroll
-                                for (int m = 0; m < 4; ++m) {
-                                    bop[k][m] = (bf16)(s0[k][m] * wgt[0][m * KT / 4]);
-                                    bop[k][4 + m] = k < K1 ? (bf16)0.f : (bf16)(s1[k][m] * wgt[1][m * KT / 4]);
-                                }
-                            }
-                            __builtin_amdgcn_sched_barrier(0);
-                            // X^T in the k order of S'^T: keys 4 g4 + 0..3 of tile a, then of tile b
-                            bf16x8 xo[4];
-#pragma unroll
-                            for (int pt = 0; pt < 4; ++pt)
-                                xo[pt] = *reinterpret_cast<const bf16x8*>(xtb + q4_off(16 * pt + l16, g4));
-#pragma unroll
-                            for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-                                for (int k = K0; k < TPC; ++k) yacc[k][pt] = mfma(xo[pt], bop[k], yacc[k][pt]);
-                        }
-                    };
-                    using std::integral_constant;
-#define M3_WS_CASE(A_, B_)                                                            \
-    case (A_) * 8 + (B_):                                                             \
-        if constexpr ((A_) <= TPC && (B_) <= TPC)                                     \
-            body(integral_constant<int, (A_)>{}, integral_constant<int, (B_)>{});     \
-        break;
-                    switch (k0 * 8 + k1) {
-                        M3_WS_CASE(0, 0) M3_WS_CASE(0, 1) M3_WS_CASE(1, 1) M3_WS_CASE(1, 2) M3_WS_CASE(2, 2)
-                        M3_WS_CASE(2, 3) M3_WS_CASE(3, 3) M3_WS_CASE(3, 4) M3_WS_CASE(4, 4)
-                        default: break;
+                    for (int j = 0; j < KT; ++j) {
+                        const int ts = (16 * (ka + ab) + 4 * g4) / R + j;
+                        kl2[ab][j] = sL2[ts];
+                        kg1[ab][j] = sG1[ts];
                     }
-#undef M3_WS_CASE
+                f32x4 s0[TPC], s1[TPC];
+                {
+                    bf16x8 op[4];
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) op[ks] = *reinterpret_cast<const bf16x8*>(buf + bn_off(l16, 4 * ks + g4));
+#pragma unroll
+                    for (int k = K0; k < TPC; ++k) {
+                        s0[k] = mfma(op[0], cq[k][0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                        for (int ks = 1; ks < 4; ++ks) s0[k] = mfma(op[ks], cq[k][ks], s0[k]);
+                    }
                 }
-                __syncthreads();
-            }
+                {
+                    bf16x8 op[4];
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        op[ks] = *reinterpret_cast<const bf16x8*>(buf + bn_off(16 + l16, 4 * ks + g4));
+#pragma unroll
+                    for (int k = K0; k < TPC; ++k) {
+                        s1[k] = mfma(op[0], cq[k][0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                        for (int ks = 1; ks < 4; ++ks) s1[k] = mfma(op[ks], cq[k][ks], s1[k]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // S'^T = W o S^T as bf16 B operands.  A tile that reaches the block's
+                // diagonal (query tile ka or ka + 1) masks per element; key rows after
+                // its query rows get weight 0 (also the whole of key tile b when the
+                // query tile is ka).
+                bf16x8 bop[TPC];
+#pragma unroll
+                for (int k = K0; k < TPC; ++k) {
+                    const bool diag = ctile(c, k) <= ka + 1;          // uniform
+                    float wgt[2][KT];
+#pragma unroll
+                    for (int ab = 0; ab < 2; ++ab) {
+#pragma unroll
+                        for (int j = 0; j < KT; ++j) {
+                            const float e = __builtin_amdgcn_exp2f(l2q[k] - kl2[ab][j]);
+                            wgt[ab][j] = e * kg1[ab][j];
+                            if (diag) {
+                                const int ts = (16 * (ka + ab) + 4 * g4) / R + j;
+                                wgt[ab][j] = ts < tq[k] ? wgt[ab][j] : (ts == tq[k] ? e * sGam[ts] : 0.f);
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        bop[k][m] = (bf16)(s0[k][m] * wgt[0][m * KT / 4]);
+                        bop[k][4 + m] = (bf16)(s1[k][m] * wgt[1][m * KT / 4]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // X^T in the k order of S'^T: keys 4 g4 + 0..3 of tile a, then of tile b
+                bf16x8 xo[4];
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) xo[pt] = *reinterpret_cast<const bf16x8*>(xtb + q4_off(16 * pt + l16, g4));
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+                    for (int k = K0; k < TPC; ++k) yacc[k][pt] = mfma(xo[pt], bop[k], yacc[k][pt]);
+            };
+            int Jb = 0;
+            auto phase = [&](auto mc) {
+                constexpr int K0 = decltype(mc)::value;
+                const int Je = K0 < TPC ? min(NKB, ctile(c, K0 < TPC ? K0 : 0) / 2 + 1) : NKB;
+#pragma unroll 1
+                for (int J = Jb; J < Je; ++J) {
+                    if constexpr (K0 < TPC) {
+                        if (kFullMode) block_body(mc, J);
+                    }
+                    __syncthreads();
+                }
+                Jb = max(Jb, Je);
+            };
+            phase(std::integral_constant<int, 0>{});
+            if constexpr (TPC >= 1) phase(std::integral_constant<int, 1>{});
+            if constexpr (TPC >= 2) phase(std::integral_constant<int, 2>{});
+            if constexpr (TPC >= 3) phase(std::integral_constant<int, 3>{});
+            if constexpr (TPC >= 4) phase(std::integral_constant<int, 4>{});
         }
         if (kFullMode && T1 > T0) store_y(T0 + (T1 - T0 - 1) / Q * Q, (T1 - T0 - 1) % Q + 1);
     } else {
