@@ -588,18 +588,25 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
         // prefetch ring: slot J % DP holds block J's raw rows, fetched DP blocks ahead
         constexpr int DP = NKB >= 4 ? 4 : 2;
         uint32_t rgB[DP][PR], rgX[DP][PR];
-        auto fetch = [&](int gb, uint32_t (&pb)[PR], uint32_t (&px)[PR]) {
-            const int cc = gb / NKB, J = gb % NKB;
-            const int t0 = T0 + cc * Q + (kKB * J + 4 * pw) / R;
-            const int nt = __builtin_amdgcn_readfirstlane(min(max(T1 - t0, 0), NTK));
-            const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg + (size_t)t0 * bstride, (uint32_t)nt * bsb);
-            const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xg + (size_t)t0 * xstride, (uint32_t)nt * xsb);
+        // Blocks are fetched in order; consecutive blocks (also across a chunk boundary)
+        // start 32 / R tokens apart, so the fetch keeps running row pointers.
+        constexpr int TPB = kKB / R;                         // tokens per block
+        int f_rem = T1 - (T0 + 4 * pw / R);                  // tokens from row 4 pw to the segment end
+        const uint16_t* f_b = Bg + (size_t)(T0 + 4 * pw / R) * bstride;
+        const uint16_t* f_x = Xg + (size_t)(T0 + 4 * pw / R) * xstride;
+        auto fetch = [&](uint32_t (&pb)[PR], uint32_t (&px)[PR]) {
+            const int nt = __builtin_amdgcn_readfirstlane(min(max(f_rem, 0), NTK));
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(f_b, (uint32_t)nt * bsb);
+            const __amdgpu_buffer_rsrc_t rx = make_rsrc(f_x, (uint32_t)nt * xsb);
 #pragma unroll
             for (int rr = 0; rr < PR; ++rr) {
                 const int u = tko(rr), r = rr % R;
                 pb[rr] = __builtin_amdgcn_raw_buffer_load_b32(rb, (int)(u * bsb) + 4 * lane + 256 * r, 0, 0);
                 px[rr] = __builtin_amdgcn_raw_buffer_load_b32(rx, (int)(u * xsb) + 4 * (lane & 31) + 128 * r, 0, 0);
             }
+            f_rem -= TPB;
+            f_b += (size_t)TPB * bstride;
+            f_x += (size_t)TPB * xstride;
         };
         // turn the rows of block J and write its tiles: Bn [32 j][128 n] (scores), and in
         // the permuted key order (group q: keys 4 q .. 4 q + 3, then 16 + 4 q ..) BvT
@@ -668,7 +675,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
             }
         };
 #pragma unroll
-        for (int d = 0; d < DP; ++d) fetch(d, rgB[d], rgX[d]);
+        for (int d = 0; d < DP; ++d) fetch(rgB[d], rgX[d]);
         fetch_scalars(T0);
 
         int cidx = 0;
@@ -744,7 +751,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
 #pragma unroll
                 for (int d = 0; d < DP; ++d) {
                     const int J = J0 + d;
-                    fetch(cidx * NKB + J + DP, rgB[d], rgX[d]);
+                    fetch(rgB[d], rgX[d]);
                     {
                         const char* buf = smem + (J & 1) * kBufBytes;
                         const char* bvb = buf + kBnBytes;
