@@ -231,7 +231,10 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
         if ((e & 63) >= np) cs_put(sCS[e], 1.f, 0.f);
 
     // theta of the chunk at cstart (all threads: token tid / 8, pairs 8 (tid % 8) + u),
-    // one buffer load per value, bounded at the segment end
+    // one buffer load per value.  Token t's np angles of this head start t H np after the
+    // chunk's first; the record count ends at this head's last angle of the last valid
+    // token, so nothing past the segment end or past the tensor is read.  Lanes of pairs
+    // at or past np read zero (those values are never used).
     constexpr int THP = (Q + 63) / 64;
     auto load_theta = [&](int cstart, float (&th)[THP][8]) {
         int tt = tid;                                         // opaque: offsets formed here
@@ -239,10 +242,12 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
             tt &= kThreads - 1;                               // a thread index: non-negative
         const int th_t = tt >> 3, th_i = (tt & 7) * 8;
         const int nt = __builtin_amdgcn_readfirstlane(min(max(T1 - cstart, 0), Q));
-        const __amdgpu_buffer_rsrc_t rt = make_rsrc(thg + (size_t)cstart * H * np, (uint32_t)(nt * H * np) * 4u);
+        const uint32_t nrec = nt > 0 ? (uint32_t)((nt - 1) * H * np + np) * 4u : 0u;
+        const __amdgpu_buffer_rsrc_t rt = make_rsrc(thg + (size_t)cstart * H * np, nrec);
 #pragma unroll
         for (int pp = 0; pp < THP; ++pp) {
-            const int vo = ((th_t + 64 * pp) * H * np + th_i) * 4;
+            // a group wholly past np gets an offset beyond every record count
+            const int vo = th_i < np ? ((th_t + 64 * pp) * H * np + th_i) * 4 : 0x7fffff00;
 #pragma unroll
             for (int u = 0; u < 8; ++u) th[pp][u] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rt, vo + 4 * u, 0, 0));
         }
