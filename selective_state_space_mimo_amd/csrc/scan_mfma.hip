@@ -157,7 +157,17 @@ constexpr int kNC = 4;                                   // consumer waves
 
 // Query tile k of consumer c: tiles are dealt in groups of 8, consumer c taking tile c
 // and tile 7 - c of each group (equal causal work per consumer).
-__device__ __forceinline__ int ctile(int c, int k) { return 8 * (k >> 1) + ((k & 1) ? 7 - c : c); }
+__host__ __device__ constexpr int ctile(int c, int k) { return 8 * (k >> 1) + ((k & 1) ? 7 - c : c); }
+// Query tile t meets key blocks 0 .. t / 2 and reaches the diagonal in the last of them.  A
+// consumer's tiles end in strictly increasing blocks, so in any key block at most one of its
+// tiles is on the diagonal: the first active one, in the last block before it retires.
+constexpr bool ctile_blocks_increase() {
+    for (int c = 0; c < 4; ++c)
+        for (int k = 0; k + 1 < 4; ++k)
+            if (ctile(c, k + 1) / 2 <= ctile(c, k) / 2) return false;
+    return true;
+}
+static_assert(ctile_blocks_increase(), "one diagonal tile per key block and consumer");
 
 template <int R, int Q, int MODE>
 __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
@@ -167,6 +177,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
     constexpr int TPC = NT / kNC;            // query tiles per consumer
     constexpr int TPL = Q > 64 ? Q / 64 : 1; // tokens per lane of the scanning wave
     constexpr int KT = R >= 4 ? 1 : 4 / R;   // key tokens among a lane's 4 rows of a score tile
+    constexpr bool kEarlyExp = KT == 1;      // decay exps ahead of the score MFMAs (registers allow)
     constexpr int PR = 8;                    // key rows per producer and block
     constexpr bool kFullMode = MODE == kFull;
     static_assert(TPC >= 1 && TPC <= 4 && NKB >= 2 && NKB % 2 == 0, "chunk shape");
@@ -436,8 +447,10 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
             //     A wave's tiles ascend with k, so the tiles that meet key block J are those
             //     from some K0 on; the blocks run in phases of constant K0, each phase a loop
             //     over one straight-line body.
-            auto block_body = [&](auto k0c, int J) {
+            auto block_body = [&](auto k0c, auto dgc, int J) {
                 constexpr int K0 = decltype(k0c)::value;
+                // 0: no tile on the diagonal; 1: tile K0 on it; 2: every tile checks
+                constexpr int kDiag = decltype(dgc)::value;
                 const int ka = 2 * J;
                 const char* buf = smem + (J & 1) * kBufBytes;
                 const char* xtb = buf + kBnBytes + kBvBytes;
@@ -450,6 +463,19 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
                         kl2[ab][j] = sL2[ts];
                         kg1[ab][j] = sG1[ts];
                     }
+                // The decay factors of W: they need only the tabled log-decays, so with one
+                // key token per lane and key tile (R = 4) their exps go before the score
+                // MFMAs and overlap them; with more they stay after (registers).
+                float ex[TPC][2][KT];
+                auto decays = [&]() {
+#pragma unroll
+                    for (int k = K0; k < TPC; ++k)
+#pragma unroll
+                        for (int ab = 0; ab < 2; ++ab)
+#pragma unroll
+                            for (int j = 0; j < KT; ++j) ex[k][ab][j] = __builtin_amdgcn_exp2f(l2q[k] - kl2[ab][j]);
+                };
+                if constexpr (kEarlyExp) decays();
                 f32x4 s0[TPC], s1[TPC];
                 {
                     bf16x8 op[4];
@@ -475,20 +501,20 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                // S'^T = W o S^T as bf16 B operands.  A tile that reaches the block's
-                // diagonal (query tile ka or ka + 1) masks per element; key rows after
-                // its query rows get weight 0 (also the whole of key tile b when the
-                // query tile is ka).
+                if constexpr (!kEarlyExp) decays();
+                // S'^T = W o S^T as bf16 B operands.  The tile on the block's diagonal
+                // (query tile ka or ka + 1) masks per element; key rows after its query
+                // rows get weight 0 (also the whole of key tile b when the query tile is ka).
                 bf16x8 bop[TPC];
 #pragma unroll
                 for (int k = K0; k < TPC; ++k) {
-                    const bool diag = ctile(c, k) <= ka + 1;          // uniform
+                    const bool diag = kDiag == 2 ? ctile(c, k) <= ka + 1 : (kDiag == 1 && k == K0);   // uniform
                     float wgt[2][KT];
 #pragma unroll
                     for (int ab = 0; ab < 2; ++ab) {
 #pragma unroll
                         for (int j = 0; j < KT; ++j) {
-                            const float e = __builtin_amdgcn_exp2f(l2q[k] - kl2[ab][j]);
+                            const float e = ex[k][ab][j];
                             wgt[ab][j] = e * kg1[ab][j];
                             if (diag) {
                                 const int ts = (16 * (ka + ab) + 4 * g4) / R + j;
@@ -516,12 +542,26 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
             auto phase = [&](auto mc) {
                 constexpr int K0 = decltype(mc)::value;
                 const int Je = K0 < TPC ? min(NKB, ctile(c, K0 < TPC ? K0 : 0) / 2 + 1) : NKB;
+                if constexpr (K0 < TPC && kEarlyExp) {
+                    // blocks before the last of tile K0, then its diagonal block
 #pragma unroll 1
-                for (int J = Jb; J < Je; ++J) {
-                    if constexpr (K0 < TPC) {
-                        if (kFullMode) block_body(mc, J);
+                    for (int J = Jb; J < Je - 1; ++J) {
+                        if (kFullMode) block_body(mc, std::integral_constant<int, 0>{}, J);
+                        __syncthreads();
                     }
-                    __syncthreads();
+                    if (Je > Jb) {
+                        if (kFullMode) block_body(mc, std::integral_constant<int, 1>{}, Je - 1);
+                        __syncthreads();
+                    }
+                } else if constexpr (K0 < TPC) {
+#pragma unroll 1
+                    for (int J = Jb; J < Je; ++J) {
+                        if (kFullMode) block_body(mc, std::integral_constant<int, 2>{}, J);
+                        __syncthreads();
+                    }
+                } else {
+#pragma unroll 1
+                    for (int J = Jb; J < Je; ++J) __syncthreads();
                 }
                 Jb = max(Jb, Je);
             };
