@@ -40,8 +40,9 @@
 //     P x N state as MFMA accumulators (H^T, 32 columns each) and update it with
 //     Hf^T += (v Bt)^T X; a bf16 snapshot in LDS is the consumers' A operand for
 //     the carry readout Y^T = Hf Ct^T.
-//   * per chunk, all waves compute the running angles (fp32 (cos, sin) table
-//     for Q <= 64); one producer scans the log-decays with DPP.
+//   * per chunk, all waves compute the running angles into a table of bf16
+//     pairs (the B and C rows are turned with packed-bf16 dot products, fp32
+//     sums); one producer scans the log-decays with DPP.
 //   * key blocks are double-buffered in LDS with one barrier per block; both
 //     roles pass the same barriers.
 // Segmented schedule (few streams, long sequences): pass 1 computes, per
@@ -62,7 +63,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 enum Mode { kFull = 0, kSummary = 1 };
 
-typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -94,28 +94,35 @@ __device__ __forceinline__ int bn_off(int j, int grp) { return j * 256 + ((grp ^
 __device__ __forceinline__ int hs_off(int p, int grp) { return p * 256 + ((grp ^ (p & 15)) << 4); }
 __device__ __forceinline__ int q4_off(int row, int grp) { return row * 64 + ((grp ^ ((row >> 1) & 3)) << 4); }
 
-// (cos, sin) table entry: fp32 pairs where the chunk's table fits, fp16 pairs for 128
-template <int Q>
-using cs_t = typename std::conditional<(Q <= 64), float2, f16x2>::type;
-__device__ __forceinline__ float2 cs_get(float2 v) { return v; }
-__device__ __forceinline__ float2 cs_get(f16x2 v) { return float2{(float)v[0], (float)v[1]}; }
-__device__ __forceinline__ void cs_put(float2& d, float c, float s) { d = float2{c, s}; }
-__device__ __forceinline__ void cs_put(f16x2& d, float c, float s) { d = f16x2{(_Float16)c, (_Float16)s}; }
+// Rotation of an (even, odd) pair by a tabled angle, on packed-bf16 dot products with fp32
+// sums.  An angle's table entry holds two bf16 pairs, (cos, -sin) and (sin, cos); a bias is
+// a bf16 pair; rot(v + b) = rot(v) + rot(b), each half of the result two dot products.
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+__device__ __forceinline__ float2 rot_pair(uint32_t v, uint32_t bias, uint2 cs) {
+    return float2{dot2(v, cs.x, dot2(bias, cs.x, 0.f)), dot2(v, cs.y, dot2(bias, cs.y, 0.f))};
+}
+__device__ __forceinline__ uint2 cs_entry(float c, float s) { return uint2{pack2(c, -s), pack2(s, c)}; }
 
 template <int Q>
 struct Layout {
     static constexpr int hs = 2 * kBufBytes;
-    static constexpr int cs = hs + kHsBytes;                  // half2 [Q][64]: (cos, sin) per token and pair
-    static constexpr int cbias = cs + Q * 64 * (int)sizeof(cs_t<Q>);   // float [4][128]
-    static constexpr int l2 = cbias + 4 * kN * 4;             // float [Q] each below
+    static constexpr int cs = hs + kHsBytes;                  // [Q][64] two bf16 pairs: (cos, -sin), (sin, cos)
+    static constexpr int cbias = cs + Q * 64 * 8;             // bf16 pairs [4][64]: C bias
+    static constexpr int l2 = cbias + 4 * 64 * 4;             // float [Q] each below
     static constexpr int g1 = l2 + Q * 4;
     static constexpr int gam = g1 + Q * 4;
     static constexpr int vs = gam + Q * 4;
     static constexpr int dtv = vs + Q * 4;
     static constexpr int phic = dtv + Q * 4;                  // float [64]
     static constexpr int misc = phic + 64 * 4;                // float [16]
-    static constexpr int stg = misc + 16 * 4;                 // float [64][Q + 1]: theta, pair-major
-    static constexpr int xsc = stg + ((64 * (Q + 1) * 4 + 15) & ~15);   // per consumer 4 KiB: row <-> MFMA layout
+    // float [64][Q + 1]: theta, pair-major.  It shares the key-block buffers, which hold
+    // nothing from the last key block of a chunk to the next chunk's block-0 tiles (the
+    // theta staging and the angles fall in between).
+    static constexpr int stg = 0;
+    static_assert(64 * (Q + 1) * 4 <= 2 * kBufBytes, "theta staging fits the key-block buffers");
+    static constexpr int xsc = misc + 16 * 4;                 // per consumer 4 KiB: row <-> MFMA layout
     static constexpr int total = xsc + 4 * 4096;
 };
 
@@ -189,8 +196,8 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
     float* sV = reinterpret_cast<float*>(smem + LY::vs);
     float* sDt = reinterpret_cast<float*>(smem + LY::dtv);
     float* sPhic = reinterpret_cast<float*>(smem + LY::phic);
-    cs_t<Q>* sCS = reinterpret_cast<cs_t<Q>*>(smem + LY::cs);
-    float* sCb = reinterpret_cast<float*>(smem + LY::cbias);
+    uint2* sCS = reinterpret_cast<uint2*>(smem + LY::cs);
+    uint32_t* sCb = reinterpret_cast<uint32_t*>(smem + LY::cbias);
     float* sMisc = reinterpret_cast<float*>(smem + LY::misc);
     float* stage = reinterpret_cast<float*>(smem + LY::stg);
 
@@ -232,14 +239,15 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
 
     // ---- shared set-up ------------------------------------------------------------------------
     if (kFullMode)
-        for (int e = tid; e < R * kN; e += kThreads) sCb[e] = a.Cb ? a.Cb[(size_t)h * R * kN + e] : 0.f;
+        for (int e = tid; e < R * kN / 2; e += kThreads)
+            sCb[e] = a.Cb ? pack2(a.Cb[(size_t)h * R * kN + 2 * e], a.Cb[(size_t)h * R * kN + 2 * e + 1]) : 0u;
     for (int i = tid; i < np; i += kThreads) {
         float v = 0.f;
         if (kFullMode) v = seg == 0 ? (a.phi0 ? a.phi0[(size_t)bh * np + i] : 0.f) : wsPhi[ss * np + i];
         sPhic[i] = v;
     }
     for (int e = tid; e < Q * 64; e += kThreads)
-        if ((e & 63) >= np) cs_put(sCS[e], 1.f, 0.f);
+        if ((e & 63) >= np) sCS[e] = cs_entry(1.f, 0.f);
 
     // theta of the chunk at cstart (all threads: token tid / 8, pairs 8 (tid % 8) + u),
     // one buffer load per value.  Token t's np angles of this head start t H np after the
@@ -301,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
                 for (int u = 0; u < TPT; ++u) {
                     float sn, cs;
                     __sincosf(base + inc[u], &sn, &cs);
-                    cs_put(sCS[(k * TPT + u) * 64 + i], cs, sn);
+                    sCS[(k * TPT + u) * 64 + i] = cs_entry(cs, sn);
                 }
                 if (k == TPP - 1) sPhic[i] = wrap_2pi(base + inc[TPT - 1]);
             }
@@ -349,8 +357,8 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
         int cidx = 0;
         for (int c0 = T0; c0 < T1; c0 += Q, ++cidx) {
             const int nvalid = min(Q, T1 - c0);
-            // (A) raw C rows, contiguous (load i of tile k: rows 4 i + lane / 16, n = 8 (lane % 16) ...);
-            //     the previous chunk's outputs; theta into the staging area
+            // (A) raw C rows straight into the operand layout (tile k, slice ks: row 16 qt + lane % 16,
+            //     n = 32 ks + 8 (lane / 16) ...); the previous chunk's outputs; theta into the staging area
             if (kFullMode) {
                 // rows of tokens at or past nvalid read zero (their outputs are never stored)
                 const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cg + (size_t)c0 * bstride, (uint32_t)nvalid * bsb);
@@ -360,13 +368,12 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
 #pragma unroll
                 for (int k = 0; k < TPC; ++k) {
                     const int qt = ctile(c, k);
+                    const unsigned qi = 16 * qt + (ln & 15u);
+                    const unsigned t = qi / R, r = qi % R;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const unsigned qi = 16 * qt + 4 * i + (ln >> 4);
-                        const unsigned t = qi / R, r = qi % R;
-                        cq[k][i] = __builtin_bit_cast(
-                            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(t * bsb + r * (kN * 2) + 16 * (ln & 15u)), 0, 0));
-                    }
+                    for (int ks = 0; ks < 4; ++ks)
+                        cq[k][ks] = __builtin_bit_cast(
+                            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(t * bsb + r * (kN * 2) + 64 * ks + 16 * (ln >> 4)), 0, 0));
                 }
             }
             stage_theta(rgTh);
@@ -376,8 +383,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
             // the previous chunk's outputs, after this chunk's loads are on their way
             if (kFullMode && c0 > T0) store_y(c0 - Q, Q);
             __syncthreads();
-            // (C) C tiles to the operand layout (row l16, n = 32 ks + 8 g4 ...), bias and
-            //     turn; carry readout Y^T = exp(l_t) Hf Ct^T
+            // (C) C tiles: bias and turn; carry readout Y^T = exp(l_t) Hf Ct^T
             int tq[TPC];
             float l2q[TPC];
             if (kFullMode) {
@@ -387,53 +393,38 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
                 const int l16 = ln & 15, g4 = ln >> 4;
 #pragma unroll
                 for (int k = 0; k < TPC; ++k) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        *reinterpret_cast<bf16x8*>(xs + bn_off(4 * i + g4, l16)) = cq[k][i];
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks)
-                        cq[k][ks] = *reinterpret_cast<const bf16x8*>(xs + bn_off(l16, 4 * ks + g4));
-                }
-#pragma unroll
-                for (int k = 0; k < TPC; ++k) {
                     const int qi = 16 * ctile(c, k) + l16;
                     const int t = qi / R, r = qi % R;
                     tq[k] = t;
                     l2q[k] = sL2[t];
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks) {
-                        const int n0 = 32 * ks + 8 * g4;
+                        const int i0 = 16 * ks + 4 * g4;             // first pair
                         const uint4 raw = __builtin_bit_cast(uint4, cq[k][ks]);
-                        const float4 b0 = *reinterpret_cast<const float4*>(sCb + r * kN + n0);
-                        const float4 b1 = *reinterpret_cast<const float4*>(sCb + r * kN + n0 + 4);
-                        cs_t<Q> csw[4];
-#pragma unroll
-                        for (int pp = 0; pp < 4; ++pp) csw[pp] = sCS[t * 64 + n0 / 2 + pp];
-                        const float v[8] = {lo_f(raw.x) + b0.x, hi_f(raw.x) + b0.y, lo_f(raw.y) + b0.z, hi_f(raw.y) + b0.w,
-                                            lo_f(raw.z) + b1.x, hi_f(raw.z) + b1.y, lo_f(raw.w) + b1.z, hi_f(raw.w) + b1.w};
-                        bf16x8 q;
-#pragma unroll
-                        for (int pp = 0; pp < 4; ++pp) {
-                            const float2 cc = cs_get(csw[pp]);
-                            const float cs = cc.x, sn = cc.y;
-                            const float e = v[2 * pp], o = v[2 * pp + 1];
-                            q[2 * pp] = (bf16)(e * cs - o * sn);
-                            q[2 * pp + 1] = (bf16)(e * sn + o * cs);
-                        }
-                        cq[k][ks] = q;
+                        const uint4 bi = *reinterpret_cast<const uint4*>(sCb + r * 64 + i0);
+                        const uint4 c01 = *reinterpret_cast<const uint4*>(sCS + t * 64 + i0);
+                        const uint4 c23 = *reinterpret_cast<const uint4*>(sCS + t * 64 + i0 + 2);
+                        const float2 p0 = rot_pair(raw.x, bi.x, uint2{c01.x, c01.y});
+                        const float2 p1 = rot_pair(raw.y, bi.y, uint2{c01.z, c01.w});
+                        const float2 p2 = rot_pair(raw.z, bi.z, uint2{c23.x, c23.y});
+                        const float2 p3 = rot_pair(raw.w, bi.w, uint2{c23.z, c23.w});
+                        cq[k][ks] = __builtin_bit_cast(bf16x8, uint4{pack2(p0.x, p0.y), pack2(p1.x, p1.y),
+                                                                     pack2(p2.x, p2.y), pack2(p3.x, p3.y)});
                     }
                 }
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) {
                     const int p = 16 * pt + l16;
+                    bf16x8 av[4];
 #pragma unroll
-                    for (int k = 0; k < TPC; ++k) yacc[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int ks = 0; ks < 4; ++ks)
+                        av[ks] = *reinterpret_cast<const bf16x8*>(smem + LY::hs + hs_off(p, 4 * ks + g4));
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        const bf16x8 av = *reinterpret_cast<const bf16x8*>(smem + LY::hs + hs_off(p, 4 * ks + g4));
+                    for (int k = 0; k < TPC; ++k) yacc[k][pt] = mfma(av[0], cq[k][0], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                        for (int k = 0; k < TPC; ++k) yacc[k][pt] = mfma(av, cq[k][ks], yacc[k][pt]);
-                    }
+                    for (int ks = 1; ks < 4; ++ks)
+#pragma unroll
+                        for (int k = 0; k < TPC; ++k) yacc[k][pt] = mfma(av[ks], cq[k][ks], yacc[k][pt]);
                 }
 #pragma unroll
                 for (int k = 0; k < TPC; ++k) {
@@ -580,11 +571,16 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
         // from the token of row 4 pw
         auto tko = [](int rr) { return rr < 4 ? rr / R : 16 / R + (rr - 4) / R; };
         constexpr int NTK = 16 / R + 3 / R + 1;              // tokens spanned by the 8 rows
-        // B bias of this lane's n-pair, per rank
-        float2 bb[R];
+        // B bias of this lane's n-pair, per rank (bf16 pair)
+        uint32_t bb[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-            bb[r] = a.Bb ? *reinterpret_cast<const float2*>(a.Bb + ((size_t)h * R + r) * kN + 2 * lane) : float2{0.f, 0.f};
+        for (int r = 0; r < R; ++r) {
+            bb[r] = 0u;
+            if (a.Bb) {
+                const float2 v = *reinterpret_cast<const float2*>(a.Bb + ((size_t)h * R + r) * kN + 2 * lane);
+                bb[r] = pack2(v.x, v.y);
+            }
+        }
         // state columns [32 pw, 32 pw + 32): H^T tiles (n-tile 2 pw + u, p-tile pt), lane:
         // p = 16 pt + l16, n = 32 pw + 16 u + 4 g4 + m
         f32x4 hacc[2][4];
@@ -663,23 +659,20 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
             // per-row angle and v, all read before any tile write (rows of one token
             // share the reads)
             const int tb = (kKB * J + 4 * pw) / R;              // token of row 4 pw
-            float2 csr[PR];
+            uint2 csr[PR];
             float vvr[PR];
 #pragma unroll
             for (int rr = 0; rr < PR; ++rr) {
                 const int t = tb + tko(rr);
-                csr[rr] = cs_get(sCS[t * 64 + lane]);
+                csr[rr] = sCS[t * 64 + lane];
                 vvr[rr] = sV[t];
             }
             uint32_t bvw[PR];
 #pragma unroll
             for (int rr = 0; rr < PR; ++rr) {
                 const int row = rr < 4 ? 4 * pw + rr : 12 + 4 * pw + rr;
-                const int r = rr % R;
-                const float cs = csr[rr].x, sn = csr[rr].y;
-                const float e = lo_f(pb[rr]) + bb[r].x, o = hi_f(pb[rr]) + bb[r].y;
-                const float b0 = e * cs - o * sn;
-                const float b1 = e * sn + o * cs;
+                const float2 bt = rot_pair(pb[rr], bb[rr % R], csr[rr]);
+                const float b0 = bt.x, b1 = bt.y;
                 if (kFullMode)
                     *reinterpret_cast<uint32_t*>(buf + bn_off(row, lane >> 2) + (lane & 3) * 4) = pack2(b0, b1);
                 bvw[rr] = pack2(b0 * vvr[rr], b1 * vvr[rr]);
