@@ -122,8 +122,14 @@ struct Layout {
     // theta staging and the angles fall in between).
     static constexpr int stg = 0;
     static_assert(64 * (Q + 1) * 4 <= 2 * kBufBytes, "theta staging fits the key-block buffers");
-    static constexpr int xsc = misc + 16 * 4;                 // per consumer 4 KiB: row <-> MFMA layout
-    static constexpr int total = xsc + 4 * 4096;
+    // Output tiles leave through LDS so that every store writes whole rows.  With Q <= 64 a
+    // chunk's outputs are staged (rows of 144 bytes, query row q at q * 144) at its end and
+    // stored during the next chunk's key blocks; with Q = 128 (no room) each consumer stores
+    // a tile at a time through a 4 KiB scratch.
+    static constexpr bool kYStage = Q <= 64;
+    static constexpr int xsc = misc + 16 * 4;                 // per consumer 4 KiB (Q = 128)
+    static constexpr int ysg = xsc + (kYStage ? 0 : 4 * 4096);
+    static constexpr int total = ysg + (kYStage ? kMaxRows * 144 : 0);
 };
 
 // DPP read of v from another lane; lanes whose source is outside the pattern (or
@@ -326,7 +332,8 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
         const int c = w;
         bf16x8 cq[TPC][4];
         f32x4 yacc[TPC][4];
-        char* const xs = smem + LY::xsc + c * 4096;          // this wave's scratch
+        char* const xs = smem + LY::xsc + c * 4096;          // this wave's scratch (Q = 128)
+        char* const ys = smem + LY::ysg;                      // output staging (Q <= 64)
         // outputs of the chunk at cst (nv valid tokens), through the scratch (rows of
         // 144 bytes) so that every store writes whole rows
         auto store_y = [&](int cst, int nv) {
@@ -354,34 +361,74 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
             }
         };
 
+        // (Q <= 64) this wave's output tiles into their staging rows
+        auto stage_y = [&]() {
+            unsigned ln = lane;                               // opaque: offsets formed here
+            asm volatile("" : "+v"(ln));
+            ln &= 63u;
+#pragma unroll
+            for (int k = 0; k < TPC; ++k) {
+                const unsigned qt = ctile(c, k);
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt)
+                    *reinterpret_cast<uint2*>(ys + (16 * qt + (ln & 15u)) * 144 + (16 * pt + 4 * (ln >> 4)) * 2) =
+                        uint2{pack2(yacc[k][pt][0], yacc[k][pt][1]), pack2(yacc[k][pt][2], yacc[k][pt][3])};
+            }
+        };
+        // (Q <= 64) staged rows 16 qt + 8 i .. + 7 (a tile of this wave) to the outputs of the
+        // chunk at cst with nv valid tokens; rows of later tokens fall outside the record count
+        auto store_rows = [&](int cst, int nv, int qt, int i) {
+            const __amdgpu_buffer_rsrc_t ry = make_rsrc(static_cast<uint16_t*>(a.y) + ((tokbase + cst) * H + h) * R * kP,
+                                                        (uint32_t)nv * xsb);
+            unsigned ln = lane;                               // opaque: offsets formed here
+            asm volatile("" : "+v"(ln));
+            ln &= 63u;
+            const unsigned qi = 16 * (unsigned)qt + 8 * (unsigned)i + (ln >> 3);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(ys + qi * 144 + (ln & 7u) * 16);
+            const unsigned t = qi / R, r = qi % R;
+            __builtin_amdgcn_raw_buffer_store_b128(v, ry, (int)(t * xsb + r * (kP * 2) + 16 * (ln & 7u)), 0, 0);
+        };
+        // raw C rows of tiles KB .. KE - 1 of the chunk at cst straight into the operand layout
+        // (tile k, slice ks: row 16 qt + lane % 16, n = 32 ks + 8 (lane / 16) ...); rows of
+        // tokens past the segment end read zero (their outputs are never stored)
+        auto load_c = [&](int cst, auto kbc, auto kec) {
+            constexpr int KB = decltype(kbc)::value, KE = decltype(kec)::value;
+            const int nv = min(Q, T1 - cst);
+            const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cg + (size_t)cst * bstride, (uint32_t)nv * bsb);
+            unsigned ln = lane;                               // opaque: offsets formed here
+            asm volatile("" : "+v"(ln));
+            ln &= 63u;
+#pragma unroll
+            for (int k = KB; k < KE; ++k) {
+                const int qt = ctile(c, k);
+                const unsigned qi = 16 * qt + (ln & 15u);
+                const unsigned t = qi / R, r = qi % R;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    cq[k][ks] = __builtin_bit_cast(
+                        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(t * bsb + r * (kN * 2) + 64 * ks + 16 * (ln >> 4)), 0, 0));
+            }
+        };
+
+        // Tiles 0 .. TPC - 2 of a chunk are retired before its last phase of key blocks; their
+        // C rows for the next chunk are loaded then, and only tile TPC - 1 at the chunk start.
+        bool pre = false;
         int cidx = 0;
         for (int c0 = T0; c0 < T1; c0 += Q, ++cidx) {
-            const int nvalid = min(Q, T1 - c0);
-            // (A) raw C rows straight into the operand layout (tile k, slice ks: row 16 qt + lane % 16,
-            //     n = 32 ks + 8 (lane / 16) ...); the previous chunk's outputs; theta into the staging area
+            // (A) the chunk's C rows; theta into the staging area
             if (kFullMode) {
-                // rows of tokens at or past nvalid read zero (their outputs are never stored)
-                const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cg + (size_t)c0 * bstride, (uint32_t)nvalid * bsb);
-                unsigned ln = lane;                           // opaque: offsets formed here
-                asm volatile("" : "+v"(ln));
-                ln &= 63u;
-#pragma unroll
-                for (int k = 0; k < TPC; ++k) {
-                    const int qt = ctile(c, k);
-                    const unsigned qi = 16 * qt + (ln & 15u);
-                    const unsigned t = qi / R, r = qi % R;
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks)
-                        cq[k][ks] = __builtin_bit_cast(
-                            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(t * bsb + r * (kN * 2) + 64 * ks + 16 * (ln >> 4)), 0, 0));
-                }
+                if (pre) load_c(c0, std::integral_constant<int, TPC - 1>{}, std::integral_constant<int, TPC>{});
+                else load_c(c0, std::integral_constant<int, 0>{}, std::integral_constant<int, TPC>{});
             }
             stage_theta(rgTh);
             load_theta(c0 + Q, rgTh);
             __syncthreads();
             angles();
-            // the previous chunk's outputs, after this chunk's loads are on their way
-            if (kFullMode && c0 > T0) store_y(c0 - Q, Q);
+            // the previous chunk's outputs: staged (stored during this chunk's key blocks) or stored
+            if (kFullMode && c0 > T0) {
+                if constexpr (LY::kYStage) stage_y();
+                else store_y(c0 - Q, Q);
+            }
             __syncthreads();
             // (C) C tiles: bias and turn; carry readout Y^T = exp(l_t) Hf Ct^T
             int tq[TPC];
@@ -529,30 +576,41 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
 #pragma unroll
                     for (int k = K0; k < TPC; ++k) yacc[k][pt] = mfma(xo[pt], bop[k], yacc[k][pt]);
             };
+            // per key block (Q <= 64): rows 8 (J % 2) .. + 7 of this wave's tile J / 2 of the
+            // previous chunk's staged outputs
+            const bool have_prev = kFullMode && c0 > T0;
+            auto block_end = [&](int J) {
+                if constexpr (LY::kYStage)
+                    if (have_prev) store_rows(c0 - Q, Q, ctile(c, J >> 1), J & 1);
+                __syncthreads();
+            };
             int Jb = 0;
             auto phase = [&](auto mc) {
                 constexpr int K0 = decltype(mc)::value;
                 const int Je = K0 < TPC ? min(NKB, ctile(c, K0 < TPC ? K0 : 0) / 2 + 1) : NKB;
+                if constexpr (TPC > 1 && K0 == TPC - 1)
+                    if (kFullMode && c0 + Q < T1)
+                        load_c(c0 + Q, std::integral_constant<int, 0>{}, std::integral_constant<int, TPC - 1>{});
                 if constexpr (K0 < TPC && kEarlyExp) {
                     // blocks before the last of tile K0, then its diagonal block
 #pragma unroll 1
                     for (int J = Jb; J < Je - 1; ++J) {
                         if (kFullMode) block_body(mc, std::integral_constant<int, 0>{}, J);
-                        __syncthreads();
+                        block_end(J);
                     }
                     if (Je > Jb) {
                         if (kFullMode) block_body(mc, std::integral_constant<int, 1>{}, Je - 1);
-                        __syncthreads();
+                        block_end(Je - 1);
                     }
                 } else if constexpr (K0 < TPC) {
 #pragma unroll 1
                     for (int J = Jb; J < Je; ++J) {
                         if (kFullMode) block_body(mc, std::integral_constant<int, 2>{}, J);
-                        __syncthreads();
+                        block_end(J);
                     }
                 } else {
 #pragma unroll 1
-                    for (int J = Jb; J < Je; ++J) __syncthreads();
+                    for (int J = Jb; J < Je; ++J) block_end(J);
                 }
                 Jb = max(Jb, Je);
             };
@@ -561,8 +619,21 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
             if constexpr (TPC >= 2) phase(std::integral_constant<int, 2>{});
             if constexpr (TPC >= 3) phase(std::integral_constant<int, 3>{});
             if constexpr (TPC >= 4) phase(std::integral_constant<int, 4>{});
+            pre = TPC > 1 && c0 + Q < T1;
         }
-        if (kFullMode && T1 > T0) store_y(T0 + (T1 - T0 - 1) / Q * Q, (T1 - T0 - 1) % Q + 1);
+        // the last chunk's outputs
+        if (kFullMode && T1 > T0) {
+            const int cst = T0 + (T1 - T0 - 1) / Q * Q, nv = (T1 - T0 - 1) % Q + 1;
+            if constexpr (LY::kYStage) {
+                stage_y();
+#pragma unroll
+                for (int k = 0; k < TPC; ++k)
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) store_rows(cst, nv, ctile(c, k), i);
+            } else {
+                store_y(cst, nv);
+            }
+        }
     } else {
         // =============================== producers ===============================
         const int pw = w - kNC;
@@ -628,6 +699,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
         // segment end (rows of later tokens read zero)
         // prefetch ring: slot J % DP holds block J's raw rows, fetched DP blocks ahead
         constexpr int DP = NKB >= 4 ? 4 : 2;
+        static_assert(NKB % DP == 0, "whole ring groups per chunk");
         uint32_t rgB[DP][PR], rgX[DP][PR];
         // Blocks are fetched in order; consecutive blocks (also across a chunk boundary)
         // start 32 / R tokens apart, so the fetch keeps running row pointers.
@@ -654,19 +726,20 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
         // [128 n][32] = (v Bt)^T and XT [64 p][32].  Rows of tokens past the chunk's
         // valid ones need no masking: their raw rows read zero and their weights and v
         // are zero (dt = 0), so only finite values (the turned bias) reach the tiles.
-        auto store_block = [&](int J, const uint32_t (&pb)[PR], const uint32_t (&px)[PR]) {
-            char* buf = smem + (J & 1) * kBufBytes;
-            // per-row angle and v, all read before any tile write (rows of one token
-            // share the reads)
+        // per-row angle table entry and v of block J (rows of one token share the reads);
+        // read ahead of the block's state MFMAs
+        auto block_scalars = [&](int J, uint2 (&csr)[PR], float (&vvr)[PR]) {
             const int tb = (kKB * J + 4 * pw) / R;              // token of row 4 pw
-            uint2 csr[PR];
-            float vvr[PR];
 #pragma unroll
             for (int rr = 0; rr < PR; ++rr) {
                 const int t = tb + tko(rr);
                 csr[rr] = sCS[t * 64 + lane];
                 vvr[rr] = sV[t];
             }
+        };
+        auto store_block = [&](int J, const uint32_t (&pb)[PR], const uint32_t (&px)[PR], const uint2 (&csr)[PR],
+                               const float (&vvr)[PR]) {
+            char* buf = smem + (J & 1) * kBufBytes;
             uint32_t bvw[PR];
 #pragma unroll
             for (int rr = 0; rr < PR; ++rr) {
@@ -781,7 +854,12 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
 #pragma unroll
                     for (int pt = 0; pt < 4; ++pt) hacc[u][pt] = hacc[u][pt] * f;
             }
-            store_block(0, rgB[0], rgX[0]);
+            {
+                uint2 csr[PR];
+                float vvr[PR];
+                block_scalars(0, csr, vvr);
+                store_block(0, rgB[0], rgX[0], csr, vvr);
+            }
             __syncthreads();
             // (D) per block: the state update from block J; block J + 1's tiles; refill
 #pragma unroll 1
@@ -790,22 +868,37 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
                 for (int d = 0; d < DP; ++d) {
                     const int J = J0 + d;
                     fetch(rgB[d], rgX[d]);
-                    {
-                        const char* buf = smem + (J & 1) * kBufBytes;
-                        const char* bvb = buf + kBnBytes;
-                        const char* xtb = buf + kBnBytes + kBvBytes;
-                        bf16x8 av[2];
+                    // every LDS read of the iteration first (block J's operands, block J + 1's
+                    // angles and v), then the state MFMAs, then block J + 1's tiles
+                    const char* buf = smem + (J & 1) * kBufBytes;
+                    const char* bvb = buf + kBnBytes;
+                    const char* xtb = buf + kBnBytes + kBvBytes;
+                    bf16x8 av[2], bv[4];
 #pragma unroll
-                        for (int u = 0; u < 2; ++u)
-                            av[u] = *reinterpret_cast<const bf16x8*>(bvb + q4_off(32 * pw + 16 * u + l16, g4));
+                    for (int u = 0; u < 2; ++u)
+                        av[u] = *reinterpret_cast<const bf16x8*>(bvb + q4_off(32 * pw + 16 * u + l16, g4));
 #pragma unroll
-                        for (int pt = 0; pt < 4; ++pt) {
-                            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(xtb + q4_off(16 * pt + l16, g4));
+                    for (int pt = 0; pt < 4; ++pt) bv[pt] = *reinterpret_cast<const bf16x8*>(xtb + q4_off(16 * pt + l16, g4));
+                    // a next block exists within the ring group (d < DP - 1: NKB % DP == 0)
+                    const bool more = d + 1 < DP || J + 1 < NKB;
+                    uint2 csr[PR];
+                    float vvr[PR];
+                    if (more) block_scalars(J + 1, csr, vvr);
 #pragma unroll
-                            for (int u = 0; u < 2; ++u) hacc[u][pt] = mfma(av[u], bv, hacc[u][pt]);
-                        }
+                    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) hacc[u][pt] = mfma(av[u], bv[pt], hacc[u][pt]);
+                    if (more) store_block(J + 1, rgB[(d + 1) % DP], rgX[(d + 1) % DP], csr, vvr);
+                    // schedule: the LDS reads, then the row fetches, then the MFMAs each
+                    // followed by a share of the row turning, then the tile writes
+                    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
                     }
-                    if (J + 1 < NKB) store_block(J + 1, rgB[(d + 1) % DP], rgX[(d + 1) % DP]);
+                    __builtin_amdgcn_sched_group_barrier(0x200, 12, 0);
                     __syncthreads();
                 }
             }
