@@ -81,18 +81,42 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 }
 
 // ---- LDS layout ------------------------------------------------------------------
-// Per key-block buffer: Bn [32 j][128 n] bf16, BvT [128 n][32 j] bf16, XT [64 p][32 j] bf16.
+// Per key-block buffer: Bn [32 j][128 n] (turned B) and Bv [32 j][128 n] (v times turned B),
+// row-major over the block's 32 key rows j; XT [64 p][32 j] bf16, keys in the scores'
+// permuted order (group q: keys 4 q .. 4 q + 3, then 16 + 4 q ..).
 constexpr int kBnBytes = kKB * kN * 2;           // 8 KiB
-constexpr int kBvBytes = kN * kKB * 2;           // 8 KiB
+constexpr int kBvBytes = kKB * kN * 2;           // 8 KiB
 constexpr int kXtBytes = kP * kKB * 2;           // 4 KiB
 constexpr int kBufBytes = kBnBytes + kBvBytes + kXtBytes;
 constexpr int kHsBytes = kP * kN * 2;            // bf16 snapshot of the folded state
 
-// 16-byte-group swizzles.  Bn and Hs rows hold 16 groups (256 B); BvT and XT
-// rows hold 4 groups (64 B).
+// 16-byte-group swizzles.  Bn, Bv and Hs rows hold 16 groups (256 B); XT rows 4 (64 B).
 __device__ __forceinline__ int bn_off(int j, int grp) { return j * 256 + ((grp ^ (j & 15)) << 4); }
 __device__ __forceinline__ int hs_off(int p, int grp) { return p * 256 + ((grp ^ (p & 15)) << 4); }
 __device__ __forceinline__ int q4_off(int row, int grp) { return row * 64 + ((grp ^ ((row >> 1) & 3)) << 4); }
+
+// The state update's A operand, (v Bt)^T (k over a block's keys), comes from the row-major
+// Bv tile by transposed reads (ds_read_b64_tr_b16).  Within each 16-lane group the instruction treats
+// the lanes' 8-byte chunks as a 16 x 4 matrix M (lane s: M[s][0..3]) and returns to lane i
+// the column M[4 j + i / 4][i % 4], j = 0..3.  So when lane s points at key row kb + s / 4,
+// columns c0 + 4 (s % 4) .. + 3, lane i receives column c0 + i at keys kb .. kb + 3.
+// The operand's k order is the scores' permuted one (lane group g: keys 4 g .. 4 g + 3 of
+// key tile a, then of key tile b), so each operand is two reads, kb = 4 g and 16 + 4 g.
+typedef short tr_v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 ds_tr(const char* p) {
+    const tr_v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) tr_v4i16*)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+// operand over (16 columns from c0) x (the block's 32 keys) of a 256-byte-row tile (Bv)
+__device__ __forceinline__ bf16x8 key_operand_256(const char* tile, int c0, int lane) {
+    const int g = lane >> 4, s = lane & 15;
+    const int col = c0 + 4 * (s & 3), kr = 4 * g + (s >> 2);
+    const int off = (col & 7) * 2;
+    const uint2 lo = ds_tr(tile + bn_off(kr, col >> 3) + off);
+    const uint2 hi = ds_tr(tile + bn_off(16 + kr, col >> 3) + off);
+    return __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
+}
 
 // Rotation of an (even, odd) pair by a tabled angle, on packed-bf16 dot products with fp32
 // sums.  An angle's table entry holds two bf16 pairs, (cos, -sin) and (sin, cos); a bias is
@@ -191,7 +215,6 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
     constexpr int TPL = Q > 64 ? Q / 64 : 1; // tokens per lane of the scanning wave
     constexpr int KT = R >= 4 ? 1 : 4 / R;   // key tokens among a lane's 4 rows of a score tile
     constexpr bool kEarlyExp = KT == 1;      // decay exps ahead of the score MFMAs (registers allow)
-    constexpr int PR = 8;                    // key rows per producer and block
     constexpr bool kFullMode = MODE == kFull;
     static_assert(TPC >= 1 && TPC <= 4 && NKB >= 2 && NKB % 2 == 0, "chunk shape");
     using LY = Layout<Q>;
@@ -637,19 +660,22 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
     } else {
         // =============================== producers ===============================
         const int pw = w - kNC;
-        // key rows of producer pw in a block: 4 pw + i and 16 + 4 pw + i (i < 4), i.e. key
-        // group pw of both key tiles; row rr (< 8) is token offset tko(rr), rank rr % R,
-        // from the token of row 4 pw
-        auto tko = [](int rr) { return rr < 4 ? rr / R : 16 / R + (rr - 4) / R; };
+        // Key rows of producer pw in a block: key group pw of both key tiles.  For B, half-wave
+        // hh = lane / 32 takes rows 16 hh + 4 pw + i (i < 4): token offset hh 16 / R + i / R
+        // from the token of row 4 pw, rank i % R, and lane lq = lane % 32 its n = 4 lq ..
+        // 4 lq + 3 (pairs 2 lq, 2 lq + 1).  For x, lane lq takes p = 2 lq, 2 lq + 1 of all 8
+        // rows rr = 4 hh' + i (both half-waves load the same).
         constexpr int NTK = 16 / R + 3 / R + 1;              // tokens spanned by the 8 rows
-        // B bias of this lane's n-pair, per rank (bf16 pair)
-        uint32_t bb[R];
+        const int hh = lane >> 5, lq = lane & 31;
+        // B bias of this lane's two pairs, per rank (bf16 pairs)
+        uint32_t bb[R][2];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            bb[r] = 0u;
+            bb[r][0] = bb[r][1] = 0u;
             if (a.Bb) {
-                const float2 v = *reinterpret_cast<const float2*>(a.Bb + ((size_t)h * R + r) * kN + 2 * lane);
-                bb[r] = pack2(v.x, v.y);
+                const float4 v = *reinterpret_cast<const float4*>(a.Bb + ((size_t)h * R + r) * kN + 4 * lq);
+                bb[r][0] = pack2(v.x, v.y);
+                bb[r][1] = pack2(v.z, v.w);
             }
         }
         // state columns [32 pw, 32 pw + 32): H^T tiles (n-tile 2 pw + u, p-tile pt), lane:
@@ -700,71 +726,75 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
         // prefetch ring: slot J % DP holds block J's raw rows, fetched DP blocks ahead
         constexpr int DP = NKB >= 4 ? 4 : 2;
         static_assert(NKB % DP == 0, "whole ring groups per chunk");
-        uint32_t rgB[DP][PR], rgX[DP][PR];
+        uint2 rgB[DP][4];
+        uint32_t rgX[DP][8];
         // Blocks are fetched in order; consecutive blocks (also across a chunk boundary)
         // start 32 / R tokens apart, so the fetch keeps running row pointers.
         constexpr int TPB = kKB / R;                         // tokens per block
         int f_rem = T1 - (T0 + 4 * pw / R);                  // tokens from row 4 pw to the segment end
         const uint16_t* f_b = Bg + (size_t)(T0 + 4 * pw / R) * bstride;
         const uint16_t* f_x = Xg + (size_t)(T0 + 4 * pw / R) * xstride;
-        auto fetch = [&](uint32_t (&pb)[PR], uint32_t (&px)[PR]) {
+        auto fetch = [&](uint2 (&pb)[4], uint32_t (&px)[8]) {
             const int nt = __builtin_amdgcn_readfirstlane(min(max(f_rem, 0), NTK));
             const __amdgpu_buffer_rsrc_t rb = make_rsrc(f_b, (uint32_t)nt * bsb);
             const __amdgpu_buffer_rsrc_t rx = make_rsrc(f_x, (uint32_t)nt * xsb);
+            unsigned ln = lane;                               // opaque: offsets formed here
+            asm volatile("" : "+v"(ln));
+            ln &= 63u;
+            const unsigned h2 = ln >> 5, l2 = ln & 31u;
 #pragma unroll
-            for (int rr = 0; rr < PR; ++rr) {
-                const int u = tko(rr), r = rr % R;
-                pb[rr] = __builtin_amdgcn_raw_buffer_load_b32(rb, (int)(u * bsb) + 4 * lane + 256 * r, 0, 0);
-                px[rr] = __builtin_amdgcn_raw_buffer_load_b32(rx, (int)(u * xsb) + 4 * (lane & 31) + 128 * r, 0, 0);
+            for (int i = 0; i < 4; ++i) {
+                const unsigned u = h2 * (16 / R) + i / R, r = i % R;
+                pb[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rb, (int)(u * bsb + 256 * r + 8 * l2), 0, 0));
+            }
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr) {
+                const unsigned u = (rr >> 2) * (16 / R) + (rr & 3) / R, r = (rr & 3) % R;
+                px[rr] = __builtin_amdgcn_raw_buffer_load_b32(rx, (int)(u * xsb + 128 * r + 4 * l2), 0, 0);
             }
             f_rem -= TPB;
             f_b += (size_t)TPB * bstride;
             f_x += (size_t)TPB * xstride;
         };
-        // turn the rows of block J and write its tiles: Bn [32 j][128 n] (scores), and in
-        // the permuted key order (group q: keys 4 q .. 4 q + 3, then 16 + 4 q ..) BvT
-        // [128 n][32] = (v Bt)^T and XT [64 p][32].  Rows of tokens past the chunk's
-        // valid ones need no masking: their raw rows read zero and their weights and v
-        // are zero (dt = 0), so only finite values (the turned bias) reach the tiles.
-        // per-row angle table entry and v of block J (rows of one token share the reads);
-        // read ahead of the block's state MFMAs
-        auto block_scalars = [&](int J, uint2 (&csr)[PR], float (&vvr)[PR]) {
+        // turn the rows of block J and write its tiles, row-major over the key rows: Bn (the
+        // scores' operand), Bv = v Bt and X (read back by transposed reads).  Rows of tokens
+        // past the chunk's valid ones need no masking: their raw rows read zero and their v is
+        // zero (dt = 0), so only finite values (the turned bias) reach the tiles.
+        // per-row angle table entries (this lane's two pairs) and v of block J (rows of one
+        // token share the reads); read ahead of the block's state MFMAs
+        auto block_scalars = [&](int J, uint4 (&csr)[4], float (&vvr)[4]) {
             const int tb = (kKB * J + 4 * pw) / R;              // token of row 4 pw
 #pragma unroll
-            for (int rr = 0; rr < PR; ++rr) {
-                const int t = tb + tko(rr);
-                csr[rr] = sCS[t * 64 + lane];
-                vvr[rr] = sV[t];
+            for (int i = 0; i < 4; ++i) {
+                const int t = tb + hh * (16 / R) + i / R;
+                csr[i] = *reinterpret_cast<const uint4*>(sCS + t * 64 + 2 * lq);
+                vvr[i] = sV[t];
             }
         };
-        auto store_block = [&](int J, const uint32_t (&pb)[PR], const uint32_t (&px)[PR], const uint2 (&csr)[PR],
-                               const float (&vvr)[PR]) {
+        auto store_block = [&](int J, const uint2 (&pb)[4], const uint32_t (&px)[8], const uint4 (&csr)[4],
+                               const float (&vvr)[4]) {
             char* buf = smem + (J & 1) * kBufBytes;
-            uint32_t bvw[PR];
 #pragma unroll
-            for (int rr = 0; rr < PR; ++rr) {
-                const int row = rr < 4 ? 4 * pw + rr : 12 + 4 * pw + rr;
-                const float2 bt = rot_pair(pb[rr], bb[rr % R], csr[rr]);
-                const float b0 = bt.x, b1 = bt.y;
-                if (kFullMode)
-                    *reinterpret_cast<uint32_t*>(buf + bn_off(row, lane >> 2) + (lane & 3) * 4) = pack2(b0, b1);
-                bvw[rr] = pack2(b0 * vvr[rr], b1 * vvr[rr]);
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * hh + 4 * pw + i;
+                const int o = bn_off(row, lq >> 1) + (lq & 1) * 8;
+                const float2 p0 = rot_pair(pb[i].x, bb[i % R][0], uint2{csr[i].x, csr[i].y});
+                const float2 p1 = rot_pair(pb[i].y, bb[i % R][1], uint2{csr[i].z, csr[i].w});
+                if (kFullMode) *reinterpret_cast<uint2*>(buf + o) = uint2{pack2(p0.x, p0.y), pack2(p1.x, p1.y)};
+                const float v = vvr[i];
+                *reinterpret_cast<uint2*>(buf + kBnBytes + o) = uint2{pack2(p0.x * v, p0.y * v), pack2(p1.x * v, p1.y * v)};
             }
-            uint32_t bv0[4], bv1[4], xt0[4], xt1[4];
+            // XT rows p = 2 lq, 2 lq + 1, key group pw (lanes of the first half-wave)
+            uint32_t xt0[4], xt1[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                bv0[q] = __builtin_amdgcn_perm(bvw[2 * q + 1], bvw[2 * q], 0x05040100u);
-                bv1[q] = __builtin_amdgcn_perm(bvw[2 * q + 1], bvw[2 * q], 0x07060302u);
                 xt0[q] = __builtin_amdgcn_perm(px[2 * q + 1], px[2 * q], 0x05040100u);
                 xt1[q] = __builtin_amdgcn_perm(px[2 * q + 1], px[2 * q], 0x07060302u);
             }
-            char* bvt = buf + kBnBytes;
             char* xtt = buf + kBnBytes + kBvBytes;
-            *reinterpret_cast<uint4*>(bvt + q4_off(2 * lane, pw)) = uint4{bv0[0], bv0[1], bv0[2], bv0[3]};
-            *reinterpret_cast<uint4*>(bvt + q4_off(2 * lane + 1, pw)) = uint4{bv1[0], bv1[1], bv1[2], bv1[3]};
-            if (lane < 32) {
-                *reinterpret_cast<uint4*>(xtt + q4_off(2 * lane, pw)) = uint4{xt0[0], xt0[1], xt0[2], xt0[3]};
-                *reinterpret_cast<uint4*>(xtt + q4_off(2 * lane + 1, pw)) = uint4{xt1[0], xt1[1], xt1[2], xt1[3]};
+            if (hh == 0) {
+                *reinterpret_cast<uint4*>(xtt + q4_off(2 * lq, pw)) = uint4{xt0[0], xt0[1], xt0[2], xt0[3]};
+                *reinterpret_cast<uint4*>(xtt + q4_off(2 * lq + 1, pw)) = uint4{xt1[0], xt1[1], xt1[2], xt1[3]};
             }
         };
         // dt, lam of the chunk at cstart and of the token after it (wave 4: lanes over tokens)
@@ -855,8 +885,8 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
                     for (int pt = 0; pt < 4; ++pt) hacc[u][pt] = hacc[u][pt] * f;
             }
             {
-                uint2 csr[PR];
-                float vvr[PR];
+                uint4 csr[4];
+                float vvr[4];
                 block_scalars(0, csr, vvr);
                 store_block(0, rgB[0], rgX[0], csr, vvr);
             }
@@ -873,16 +903,16 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
                     const char* buf = smem + (J & 1) * kBufBytes;
                     const char* bvb = buf + kBnBytes;
                     const char* xtb = buf + kBnBytes + kBvBytes;
+                    // A: (v Bt)^T rows n = 32 pw + 16 u + l16; B: XT row p = 16 pt + l16
                     bf16x8 av[2], bv[4];
 #pragma unroll
-                    for (int u = 0; u < 2; ++u)
-                        av[u] = *reinterpret_cast<const bf16x8*>(bvb + q4_off(32 * pw + 16 * u + l16, g4));
+                    for (int u = 0; u < 2; ++u) av[u] = key_operand_256(bvb, 32 * pw + 16 * u, lane);
 #pragma unroll
                     for (int pt = 0; pt < 4; ++pt) bv[pt] = *reinterpret_cast<const bf16x8*>(xtb + q4_off(16 * pt + l16, g4));
                     // a next block exists within the ring group (d < DP - 1: NKB % DP == 0)
                     const bool more = d + 1 < DP || J + 1 < NKB;
-                    uint2 csr[PR];
-                    float vvr[PR];
+                    uint4 csr[4];
+                    float vvr[4];
                     if (more) block_scalars(J + 1, csr, vvr);
 #pragma unroll
                     for (int pt = 0; pt < 4; ++pt)
@@ -891,8 +921,8 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
                     if (more) store_block(J + 1, rgB[(d + 1) % DP], rgX[(d + 1) % DP], csr, vvr);
                     // schedule: the LDS reads, then the row fetches, then the MFMAs each
                     // followed by a share of the row turning, then the tile writes
-                    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 12, 0);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
