@@ -132,7 +132,10 @@ __device__ __forceinline__ uint2 cs_entry(float c, float s) { return uint2{pack2
 template <int Q>
 struct Layout {
     static constexpr int hs = 2 * kBufBytes;
-    static constexpr int cs = hs + kHsBytes;                  // [Q][64] two bf16 pairs: (cos, -sin), (sin, cos)
+    // [Q][64] two bf16 pairs, (cos, -sin) and (sin, cos); pair i of token t sits in column
+    // i ^ (t & 60), which keeps aligned groups of four pairs together and spreads the angle
+    // writes (one token row per lane group) over the banks
+    static constexpr int cs = hs + kHsBytes;
     static constexpr int cbias = cs + Q * 64 * 8;             // bf16 pairs [4][64]: C bias
     static constexpr int l2 = cbias + 4 * 64 * 4;             // float [Q] each below
     static constexpr int g1 = l2 + Q * 4;
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
         sPhic[i] = v;
     }
     for (int e = tid; e < Q * 64; e += kThreads)
-        if ((e & 63) >= np) sCS[e] = cs_entry(1.f, 0.f);
+        if ((e & 63) >= np) sCS[(e & ~63) + ((e & 63) ^ ((e >> 6) & 60))] = cs_entry(1.f, 0.f);
 
     // theta of the chunk at cstart (all threads: token tid / 8, pairs 8 (tid % 8) + u),
     // one buffer load per value.  Token t's np angles of this head start t H np after the
@@ -338,7 +341,8 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
                 for (int u = 0; u < TPT; ++u) {
                     float sn, cs;
                     __sincosf(base + inc[u], &sn, &cs);
-                    sCS[(k * TPT + u) * 64 + i] = cs_entry(cs, sn);
+                    const int t = k * TPT + u;
+                    sCS[t * 64 + (i ^ (t & 60))] = cs_entry(cs, sn);
                 }
                 if (k == TPP - 1) sPhic[i] = wrap_2pi(base + inc[TPT - 1]);
             }
@@ -472,8 +476,9 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
                         const int i0 = 16 * ks + 4 * g4;             // first pair
                         const uint4 raw = __builtin_bit_cast(uint4, cq[k][ks]);
                         const uint4 bi = *reinterpret_cast<const uint4*>(sCb + r * 64 + i0);
-                        const uint4 c01 = *reinterpret_cast<const uint4*>(sCS + t * 64 + i0);
-                        const uint4 c23 = *reinterpret_cast<const uint4*>(sCS + t * 64 + i0 + 2);
+                        const uint2* ce = sCS + t * 64 + (i0 ^ (t & 60));   // pairs i0 .. i0 + 3
+                        const uint4 c01 = *reinterpret_cast<const uint4*>(ce);
+                        const uint4 c23 = *reinterpret_cast<const uint4*>(ce + 2);
                         const float2 p0 = rot_pair(raw.x, bi.x, uint2{c01.x, c01.y});
                         const float2 p1 = rot_pair(raw.y, bi.y, uint2{c01.z, c01.w});
                         const float2 p2 = rot_pair(raw.z, bi.z, uint2{c23.x, c23.y});
@@ -767,7 +772,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = tb + hh * (16 / R) + i / R;
-                csr[i] = *reinterpret_cast<const uint4*>(sCS + t * 64 + 2 * lq);
+                csr[i] = *reinterpret_cast<const uint4*>(sCS + t * 64 + ((2 * lq) ^ (t & 60)));
                 vvr[i] = sV[t];
             }
         };
