@@ -4,8 +4,8 @@
  * The operation ("Mamba-3: Improved Sequence Modeling using State Space
  * Principles", intuitivepapers.ai):
  *   For every batch b and head h (with group g = h * G / H of the shared B, C)
- *   and token t, with a = exp(A_log[h]):
- *     alpha = exp(-dt a),  beta = alpha dt (1 - lam),  gamma = lam dt
+ *   and token t, with the decay rate A < 0 (see m3_rate_law):
+ *     alpha = exp(dt A),  beta = alpha dt (1 - lam),  gamma = lam dt
  *         -- section "How the exponential-trapezoidal update works"
  *     phi_i <- phi_i + dt theta_i            (i < npairs)
  *     Bt = rot(B[g] + B_bias[h], phi),  Ct = rot(C[g] + C_bias[h], phi)
@@ -55,6 +55,18 @@ typedef struct ihipStream_t* m3_stream_t;
 
 typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;
 
+/* The decay rate A (< 0) of a token.
+ *   M3_RATE_STATIC: one rate per head, A = -exp(A_log[h]); the A_log argument
+ *     is [H] f32.
+ *   M3_RATE_HEAVY_TAIL: a rate per token, A = min(-ht(u), -1e-4) with ht(u) =
+ *     1 + u for u >= 0 and 1 / (1 - u) for u < 0, the rate activation the
+ *     Mamba-3 code applies to its rate projection ("Mamba-3: Improved Sequence
+ *     Modeling using State Space Principles", the remarks after the decode
+ *     listing on the layer's remaining nonlinearities); the A_log argument then
+ *     carries the input u: [b, L, H] f32 for m3_scan_fwd, [b, H] for
+ *     m3_decode_step. */
+typedef enum { M3_RATE_STATIC = 0, M3_RATE_HEAVY_TAIL = 1 } m3_rate_law;
+
 typedef enum {
     M3_OK = 0,
     M3_ERR_INVALID_ARG = 1,   /* NULL pointer, bad shape, H % G != 0, npairs > N/2, small workspace, aliasing */
@@ -85,6 +97,7 @@ typedef struct {
                          parallel from zero-entry summaries (clamped to the number
                          of chunks).  The result does not depend on it beyond
                          rounding.  Ignored by m3_decode_step. */
+    int rate_law;     /* m3_rate_law: how the A_log argument gives the decay rate */
 } m3_desc;
 
 /* The recurrence carry of section "Computing the rotation as a
@@ -107,7 +120,8 @@ m3_status m3_scan_workspace_size(const m3_desc* d, size_t* bytes);
  *   dt     [b, L, H] f32 (> 0, after softplus)
  *   lam    [b, L, H] f32 (in [0, 1], after sigmoid)
  *   theta  [b, L, H, np] f32 angular rate (each token adds dt * theta); NULL iff np == 0
- *   A_log  [H] f32; the decay rate is A = -exp(A_log)
+ *   A_log  [H] f32, the decay rate A = -exp(A_log) (M3_RATE_STATIC), or
+ *          [b, L, H] f32, the per-token rate input u (M3_RATE_HEAVY_TAIL)
  *   B_bias, C_bias [H, R, N] f32, or NULL for no bias (added before the turn)
  *   init   carry at t = -1, or NULL for an all-zero carry; its phi may be NULL
  *          when np == 0
@@ -127,7 +141,8 @@ m3_status m3_scan_fwd(const m3_desc* d,
 
 /* One token for every (batch, head), the carry updated in place.
  *   x [b, H, R, P] io;  B, C [b, G, R, N] io;  dt, lam [b, H] f32;
- *   theta [b, H, np] f32 (NULL iff np == 0); A_log [H]; B_bias, C_bias [H, R, N] or NULL
+ *   theta [b, H, np] f32 (NULL iff np == 0); A_log [H], or [b, H] with M3_RATE_HEAVY_TAIL;
+ *   B_bias, C_bias [H, R, N] or NULL
  *   carry  in/out (all four pointers required; phi may be NULL iff np == 0)
  *   y      [b, H, R, P] io (must not overlap inputs or the carry) */
 m3_status m3_decode_step(const m3_desc* d,

@@ -31,6 +31,7 @@ class Config:
     init_state: bool     # h0 ~ N(0, 0.1); otherwise the carry starts at zero
     init_full: bool = False  # also random phi0 / B_prev0 / x_prev0 (tests only)
     decode_steps: int = 0    # > 0: a decode workload of that many steps
+    rate_dyn: bool = False   # per-token decay rates (heavy-tail law of a rate input)
     seed_index: int = 0      # k in SeedSequence(20260000 + k)
 
     @property

@@ -8,7 +8,8 @@ upcasts the float32 values exactly, the GPU path takes the bf16 bit patterns.
 
 Value laws (per workload text): x ~ N(0,1); B, C ~ N(0,1), optionally RMS-
 normalised over the state axis (eps 1e-6) before rounding; dt =
-softplus(N(-2, 0.5)); A_log = log U(1, 16) per head; lambda = sigmoid(N(0,1))
+softplus(N(-2, 0.5)); A_log = log U(1, 16) per head, or (per-token rates) a
+rate input u ~ N(0, 1) per token; lambda = sigmoid(N(0,1))
 or exactly 1; theta = U(0, pi) / N per rotating pair; bias ~ N(0, 0.1) (std);
 h0 ~ N(0, 0.1).  These are input preparation only (the block's activations and
 BCNorm sit outside the scan), not the scan's arithmetic.
@@ -20,7 +21,7 @@ import numpy as np
 from .configs import Config
 
 _ORDER = ("A_log", "dt", "lam", "theta", "x", "B", "C", "B_bias", "C_bias",
-          "h0", "phi0", "B_prev0", "x_prev0")
+          "h0", "phi0", "B_prev0", "x_prev0", "A_raw")
 
 
 def bf16_bits(a) -> np.ndarray:
@@ -67,7 +68,8 @@ def make_scan_inputs(cfg: Config, seed=None, *, batch=None, seqlen=None, spawn_k
     """All inputs of one scan call, as float32 arrays of storage-exact values.
 
     Returns a dict with x [b,L,H,R,P], B, C [b,L,G,R,N], dt, lam [b,L,H],
-    theta [b,L,H,npairs] (None if npairs == 0), A_log [H], B_bias, C_bias
+    theta [b,L,H,npairs] (None if npairs == 0), A_log [H], A_raw [b,L,H]
+    (per-token rate inputs, None unless ``cfg.rate_dyn``), B_bias, C_bias
     [H,R,N] (None without bias) and init (None, or a dict h [b,H,P,N],
     phi [b,H,npairs], B_prev [b,H,R,N], x_prev [b,H,R,P]).
     """
@@ -77,6 +79,7 @@ def make_scan_inputs(cfg: Config, seed=None, *, batch=None, seqlen=None, spawn_k
     g = _rngs(cfg.seed if seed is None else seed, spawn_key)
     out = {}
     out["A_log"] = np.log(g["A_log"].uniform(1.0, 16.0, size=H)).astype(np.float32)
+    out["A_raw"] = g["A_raw"].standard_normal((b, L, H)).astype(np.float32) if cfg.rate_dyn else None
     z = g["dt"].normal(-2.0, 0.5, size=(b, L, H))
     out["dt"] = np.logaddexp(0.0, z).astype(np.float32)          # softplus
     if cfg.lam_one:
@@ -137,14 +140,14 @@ def make_decode_inputs(cfg: Config, nsteps: int, seed=None, *, batch=None):
 def make_small_case(seed, *, batch=1, seqlen=16, nheads=2, ngroups=None, headdim=4,
                     dstate=6, rank=2, npairs=2, chunk=4, io_dtype="f32",
                     state_dtype="f32", bias=True, lam_one=False, rms_bc=False,
-                    init_full=True, dt_scale=1.0):
+                    init_full=True, dt_scale=1.0, rate_dyn=False):
     """A small random case for oracle self-tests and small GPU parity cases."""
     cfg = Config("small", batch=batch, seqlen=seqlen, nheads=nheads,
                  ngroups=nheads if ngroups is None else ngroups, headdim=headdim,
                  dstate=dstate, rank=rank, npairs=npairs, chunk=chunk,
                  io_dtype=io_dtype, state_dtype=state_dtype, bias=bias,
                  lam_one=lam_one, rms_bc=rms_bc, init_state=init_full,
-                 init_full=init_full, seed_index=0)
+                 init_full=init_full, rate_dyn=rate_dyn, seed_index=0)
     d = make_scan_inputs(cfg, seed=seed)
     if dt_scale != 1.0:
         d["dt"] = (d["dt"] * np.float32(dt_scale)).astype(np.float32)

@@ -22,6 +22,10 @@ Sources (web pages, cited by title and section):
       - "MIMO: a rank-4 state update for the same state size": x_t is P x R,
         B_t is N x R, R writes share one decay and are summed into one state,
         which is read R times.
+      - The remarks after the decode listing on the layer's remaining
+        nonlinearities: the rate activation the code calls heavy_tail, 1 + u
+        for u >= 0 and 1 / (1 - u) for u < 0, negated and clamped at -1e-4
+        (the per-token rate A_t = -heavy_tail(A_r) of the listing).
 [D]   "Diagonal Equivalence in State Space Models: Characterization,
       Retrieval Rank, and Selective Extensions" (paperpeel.com).
       - Section 2.4: chunked evaluation with chunk-local cumulative
@@ -73,6 +77,25 @@ def rot(v, phi):
     return v
 
 
+def heavy_tail_rate(u):
+    """Per-token decay rate A_t (< 0) from the rate input u (float or array).
+
+    [M3] remarks after the decode listing: heavy_tail(u) is 1 + u for u >= 0
+    and 1 / (1 - u) for u < 0; the rate is its negation, clamped at -1e-4.
+    """
+    u = np.asarray(u, dtype=np.float64)
+    ht = np.where(u >= 0.0, 1.0 + u, 1.0 / (1.0 - np.minimum(u, 0.0)))
+    return np.minimum(-ht, -1e-4)
+
+
+def _rate_mag(inp, bi, h, L):
+    """a_t = -A_t > 0 for the L tokens of stream (bi, h): exp(A_log[h]) for the
+    static law, or -heavy_tail_rate(A_raw[bi, t, h]) for per-token rates."""
+    if inp.get("A_raw") is not None:
+        return -heavy_tail_rate(inp["A_raw"][bi, :, h])
+    return np.full(L, math.exp(float(inp["A_log"][h])))
+
+
 def _dims(inp):
     b, L, H, R, P = inp["x"].shape
     G, N = inp["B"].shape[2], inp["B"].shape[4]
@@ -95,7 +118,7 @@ def _stream(inp, bi, h):
     dt = f(inp["dt"][bi, :, h])
     lam = f(inp["lam"][bi, :, h])
     th = f(inp["theta"][bi, :, h]) if npairs else np.zeros((L, 0))
-    a = math.exp(float(inp["A_log"][h]))            # A = -exp(A_log)
+    a = _rate_mag(inp, bi, h, L)                     # [L]: A_t = -a_t
     init = inp.get("init")
     if init is not None:
         H0 = f(init["h"][bi, h])
@@ -143,7 +166,7 @@ def scan_seq(inp):
             Hs, phi, Bp, Xp = s["H0"].copy(), s["phi0"].copy(), s["Bp0"].copy(), s["xp0"].copy()
             for t in range(L):
                 dt, lam = s["dt"][t], s["lam"][t]
-                alpha = math.exp(-dt * s["a"])
+                alpha = math.exp(-dt * s["a"][t])
                 beta = alpha * dt * (1.0 - lam)
                 gamma = lam * dt
                 phi = phi + dt * s["theta"][t]
@@ -160,7 +183,7 @@ def scan_seq(inp):
 # ----------------------------------------------------------------------------
 # 2. one decode step (the page's listing, restricted to the scan core)
 # ----------------------------------------------------------------------------
-def decode_step(carry, x, B, C, dt, lam, theta, A_log, B_bias=None, C_bias=None):
+def decode_step(carry, x, B, C, dt, lam, theta, A_log, B_bias=None, C_bias=None, A_raw=None):
     """One token for every (batch, head); returns (y [b,H,R,P], new carry).
 
     [M3] "Computing the rotation as a data-dependent RoPE", decode listing:
@@ -169,7 +192,8 @@ def decode_step(carry, x, B, C, dt, lam, theta, A_log, B_bias=None, C_bias=None)
     projections, activations, D skip and gate around it are outside the scan.
 
     carry: dict h [b,H,P,N], phi [b,H,np], B_prev [b,H,R,N], x_prev [b,H,R,P]
-    x [b,H,R,P]; B, C [b,G,R,N]; dt, lam [b,H]; theta [b,H,np] or None.
+    x [b,H,R,P]; B, C [b,G,R,N]; dt, lam [b,H]; theta [b,H,np] or None;
+    A_raw [b,H] per-token rate inputs (heavy-tail law) or None (A = -exp(A_log)).
     """
     f = lambda a: np.asarray(a, dtype=np.float64)  # noqa: E731
     h, phi = f(carry["h"]), f(carry["phi"])
@@ -183,7 +207,9 @@ def decode_step(carry, x, B, C, dt, lam, theta, A_log, B_bias=None, C_bias=None)
         for hh in range(H):
             g = hh * G // H
             d = float(dt[bi, hh])
-            alpha = math.exp(d * -math.exp(float(A_log[hh])))
+            rate = (float(heavy_tail_rate(A_raw[bi, hh])) if A_raw is not None
+                    else -math.exp(float(A_log[hh])))
+            alpha = math.exp(d * rate)
             lm = float(lam[bi, hh])
             beta = alpha * d * (1.0 - lm)
             gamma = lm * d
@@ -332,7 +358,7 @@ def scan_seq_unrotated(inp):
             phi = s["phi0"].copy()
             for t in range(L):
                 dt, lam = s["dt"][t], s["lam"][t]
-                alpha = math.exp(-dt * s["a"])
+                alpha = math.exp(-dt * s["a"][t])
                 beta = alpha * dt * (1.0 - lam)
                 gamma = lam * dt
                 step = dt * s["theta"][t]

@@ -10,7 +10,10 @@
  * Principles" (intuitivepapers.ai):
  *   - "How the exponential-trapezoidal update works":
  *       h_t = a_t h_{t-1} + b_t X_{t-1}^T B_{t-1} + g_t X_t^T B_t,
- *       a_t = exp(-dt_t exp(A_log)),  b_t = a_t dt_t (1 - lam_t),  g_t = lam_t dt_t
+ *       a_t = exp(dt_t A_t),  b_t = a_t dt_t (1 - lam_t),  g_t = lam_t dt_t,
+ *     with the rate A_t = -exp(A_log) per head, or per token the negated
+ *     heavy-tail activation of a rate input u (1 + u for u >= 0, 1 / (1 - u)
+ *     for u < 0), clamped at -1e-4 (remarks after the decode listing)
  *   - "Computing the rotation as a data-dependent RoPE": phi_t = phi_{t-1} +
  *     dt_t theta_t per pair; B and C (bias added first) turned by phi_t on
  *     adjacent pairs (2i, 2i+1), counter-clockwise; the lagged term uses the
@@ -34,7 +37,8 @@
 /* Layouts (row-major, contiguous):
  *   x      [b][L][H][R][P]      B, C  [b][L][G][R][N]
  *   dt,lam [b][L][H]            theta [b][L][H][npairs]  (NULL if npairs == 0)
- *   A_log  [H]                  B_bias, C_bias [H][R][N] (NULL = no bias)
+ *   A_log  [H]                  A_raw [b][L][H] per-token rate inputs (NULL = static rates)
+ *   B_bias, C_bias [H][R][N] (NULL = no bias)
  *   h0 [b][H][P][N], phi0 [b][H][npairs], Bp0 [b][H][R][N], xp0 [b][H][R][P] (each may be NULL = 0)
  * Outputs, for selected stream k (k < nsel, stream (sel_b[k], sel_h[k])):
  *   y [k][L][R][P], h_out [k][P][N], phi_out [k][npairs] (in [0, 2pi)),
@@ -44,7 +48,7 @@
 int m3ref_scan(int batch, int L, int H, int G, int P, int N, int R, int npairs,
                const float* x, const float* B, const float* C,
                const float* dt, const float* lam, const float* theta,
-               const float* A_log, const float* B_bias, const float* C_bias,
+               const float* A_log, const float* A_raw, const float* B_bias, const float* C_bias,
                const float* h0, const float* phi0, const float* Bp0, const float* xp0,
                int nsel, const int* sel_b, const int* sel_h,
                double* y, double* h_out, double* phi_out, double* Bp_out, double* xp_out,
@@ -79,12 +83,18 @@ int m3ref_scan(int batch, int L, int H, int G, int P, int N, int R, int npairs,
         if (phi0) for (int i = 0; i < npairs; ++i) phi[i] = phi0[sh * npairs + i];
         if (Bp0)  for (int i = 0; i < R * N; ++i) Bp[i] = Bp0[sh * R * N + i];
         if (xp0)  for (int i = 0; i < R * P; ++i) Xp[i] = xp0[sh * R * P + i];
-        const double a = exp((double)A_log[h]);
+        const double a_static = A_raw ? 0.0 : exp((double)A_log[h]);
 
         for (int t = 0; t < L; ++t) {
             const size_t tok = ((size_t)bi * L + t) * H + h;      /* index into [b][L][H] */
             const double d = dt[tok], lm = lam[tok];
-            const double alpha = exp(-d * a);
+            double rate = -a_static;
+            if (A_raw) {
+                const double u = A_raw[tok];
+                const double ht = u >= 0.0 ? 1.0 + u : 1.0 / (1.0 - u);
+                rate = -ht < -1e-4 ? -ht : -1e-4;
+            }
+            const double alpha = exp(d * rate);
             const double beta = alpha * d * (1.0 - lm);
             const double gamma = lm * d;
             for (int i = 0; i < npairs; ++i) phi[i] += d * (double)theta[tok * npairs + i];

@@ -35,7 +35,7 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         I = ctypes.c_int
-        lib.m3ref_scan.argtypes = [I] * 8 + [P] * 13 + [I, P, P] + [P] * 5 + [I]
+        lib.m3ref_scan.argtypes = [I] * 8 + [P] * 14 + [I, P, P] + [P] * 5 + [I]
         lib.m3ref_scan.restype = I
         lib.m3ref_max_threads.restype = I
         _lib = lib
@@ -73,7 +73,7 @@ def scan(inp, sel=None, nthreads=0, want_y=True):
     init = inp.get("init") or {}
     keep = [x, Bm, Cm]
     args = {}
-    for k in ("dt", "lam", "A_log", "B_bias", "C_bias"):
+    for k in ("dt", "lam", "A_log", "A_raw", "B_bias", "C_bias"):
         args[k] = _f32(inp.get(k))
     ini = {k: _f32(init.get(k)) for k in ("h", "phi", "B_prev", "x_prev")}
     full = sel is None
@@ -89,7 +89,7 @@ def scan(inp, sel=None, nthreads=0, want_y=True):
     xf = np.zeros((k, R, P))
     rc = lib.m3ref_scan(b, L, H, G, P, N, R, npairs,
                         _ptr(x), _ptr(Bm), _ptr(Cm), _ptr(args["dt"]), _ptr(args["lam"]), _ptr(th),
-                        _ptr(args["A_log"]), _ptr(args["B_bias"]), _ptr(args["C_bias"]),
+                        _ptr(args["A_log"]), _ptr(args["A_raw"]), _ptr(args["B_bias"]), _ptr(args["C_bias"]),
                         _ptr(ini["h"]), _ptr(ini["phi"]), _ptr(ini["B_prev"]), _ptr(ini["x_prev"]),
                         k, _ptr(sb), _ptr(sh), _ptr(y), _ptr(hf), _ptr(pf), _ptr(bf), _ptr(xf),
                         int(nthreads))

@@ -10,6 +10,10 @@ not import.
     y, final = scan_fwd(x, B, C, dt, lam, theta, A_log, B_bias, C_bias,
                         init=None, chunk=64)
     y = decode_step(x, B, C, dt, lam, theta, A_log, B_bias, C_bias, carry)
+
+With ``A_raw=`` (a per-token rate input [b,L,H], or [b,H] for a decode step)
+the decay rate of each token is the heavy-tail law (M3_RATE_HEAVY_TAIL) and
+``A_log`` is not used.
 """
 import ctypes
 import os
@@ -17,7 +21,7 @@ import os
 import torch
 
 __all__ = ["scan_fwd", "decode_step", "scan_workspace_size", "new_carry", "M3Error",
-           "LIB_PATH", "lib", "Desc", "Carry", "M3_F32", "M3_BF16"]
+           "LIB_PATH", "lib", "Desc", "Carry", "M3_F32", "M3_BF16", "M3_RATE_STATIC", "M3_RATE_HEAVY_TAIL"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libm3scan.so")
 if not os.path.exists(LIB_PATH):
@@ -25,6 +29,7 @@ if not os.path.exists(LIB_PATH):
                       "(or python -m selective_state_space_mimo_amd.build)")
 
 M3_F32, M3_BF16 = 0, 1
+M3_RATE_STATIC, M3_RATE_HEAVY_TAIL = 0, 1
 _STATUS = {0: "M3_OK", 1: "M3_ERR_INVALID_ARG", 2: "M3_ERR_UNSUPPORTED", 3: "M3_ERR_ALIGNMENT", 4: "M3_ERR_HIP"}
 
 
@@ -32,7 +37,8 @@ class Desc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int), ("seqlen", ctypes.c_int), ("nheads", ctypes.c_int),
                 ("ngroups", ctypes.c_int), ("headdim", ctypes.c_int), ("dstate", ctypes.c_int),
                 ("rank", ctypes.c_int), ("npairs", ctypes.c_int), ("chunk", ctypes.c_int),
-                ("io_dtype", ctypes.c_int), ("state_dtype", ctypes.c_int), ("nsegments", ctypes.c_int)]
+                ("io_dtype", ctypes.c_int), ("state_dtype", ctypes.c_int), ("nsegments", ctypes.c_int),
+                ("rate_law", ctypes.c_int)]
 
 
 class Carry(ctypes.Structure):
@@ -99,7 +105,7 @@ def _carry(c, dev, io, st_dtype):
                  _ptr(c["B_prev"], dev, io, "B_prev"), _ptr(c["x_prev"], dev, io, "x_prev"))
 
 
-def make_desc(x, B, theta, *, chunk=64, state_dtype=None, nsegments=0, decode=False):
+def make_desc(x, B, theta, *, chunk=64, state_dtype=None, nsegments=0, decode=False, rate_law=M3_RATE_STATIC):
     if decode:
         b, H, R, P = x.shape
         G, N = B.shape[1], B.shape[3]
@@ -109,7 +115,7 @@ def make_desc(x, B, theta, *, chunk=64, state_dtype=None, nsegments=0, decode=Fa
         G, N = B.shape[2], B.shape[4]
     npairs = 0 if theta is None else theta.shape[-1]
     sd = _dt(x) if state_dtype is None else (M3_BF16 if state_dtype == torch.bfloat16 else M3_F32)
-    return Desc(b, L, H, G, P, N, R, npairs, chunk, _dt(x), sd, nsegments)
+    return Desc(b, L, H, G, P, N, R, npairs, chunk, _dt(x), sd, nsegments, rate_law)
 
 
 def new_carry(batch, nheads, headdim, dstate, rank, npairs, io_dtype, state_dtype, device):
@@ -128,19 +134,23 @@ def scan_workspace_size(desc):
 
 
 def scan_fwd(x, B, C, dt, lam, theta, A_log, B_bias=None, C_bias=None, init=None, *, chunk=64,
-             state_dtype=torch.float32, nsegments=0, y=None, final=True, workspace=None):
+             state_dtype=torch.float32, nsegments=0, y=None, final=True, workspace=None, A_raw=None):
     """Chunked scan (``m3_scan_fwd``).
 
     x [b,L,H,R,P], B/C [b,L,G,R,N] (bf16 or f32, same dtype); dt, lam [b,L,H],
     theta [b,L,H,np] or None, A_log [H], biases [H,R,N] or None (all f32).
     init: None or dict(h [b,H,P,N] state_dtype, phi [b,H,np] f32, B_prev
     [b,H,R,N], x_prev [b,H,R,P]).  final: True to allocate and return the final
-    carry, a dict to write into, or False/None to skip it.
+    carry, a dict to write into, or False/None to skip it.  A_raw: None for the
+    static rates -exp(A_log), or the per-token rate input [b,L,H] f32 (the
+    heavy-tail law; A_log is then ignored and may be None).
     Returns (y, final_carry_or_None).
     """
     dev = x.device
     io = x.dtype
-    desc = make_desc(x, B, theta, chunk=chunk, state_dtype=state_dtype, nsegments=nsegments)
+    law = M3_RATE_STATIC if A_raw is None else M3_RATE_HEAVY_TAIL
+    desc = make_desc(x, B, theta, chunk=chunk, state_dtype=state_dtype, nsegments=nsegments, rate_law=law)
+    rate = A_log if A_raw is None else A_raw
     b, L, H, R, P = x.shape
     N = B.shape[4]
     if y is None:
@@ -156,7 +166,7 @@ def scan_fwd(x, B, C, dt, lam, theta, A_log, B_bias=None, C_bias=None, init=None
     ci, cf = _carry(init, dev, io, state_dtype), _carry(fin, dev, io, state_dtype)
     st = lib.m3_scan_fwd(ctypes.byref(desc), _ptr(x, dev, io, "x"), _ptr(B, dev, io, "B"), _ptr(C, dev, io, "C"),
                          _ptr(dt, dev, torch.float32, "dt"), _ptr(lam, dev, torch.float32, "lam"),
-                         _ptr(theta, dev, torch.float32, "theta"), _ptr(A_log, dev, torch.float32, "A_log"),
+                         _ptr(theta, dev, torch.float32, "theta"), _ptr(rate, dev, torch.float32, "A_log/A_raw"),
                          _ptr(B_bias, dev, torch.float32, "B_bias"), _ptr(C_bias, dev, torch.float32, "C_bias"),
                          ctypes.byref(ci) if ci is not None else None, _ptr(y, dev, io, "y"),
                          ctypes.byref(cf) if cf is not None else None,
@@ -165,20 +175,22 @@ def scan_fwd(x, B, C, dt, lam, theta, A_log, B_bias=None, C_bias=None, init=None
     return y, fin
 
 
-def decode_step(x, B, C, dt, lam, theta, A_log, B_bias, C_bias, carry, *, y=None):
+def decode_step(x, B, C, dt, lam, theta, A_log, B_bias, C_bias, carry, *, y=None, A_raw=None):
     """One decode step (``m3_decode_step``); ``carry`` (dict) is updated in place.
 
     x [b,H,R,P], B/C [b,G,R,N]; dt, lam [b,H]; theta [b,H,np] or None.
     Returns y [b,H,R,P]."""
     dev = x.device
     io = x.dtype
-    desc = make_desc(x, B, theta, state_dtype=carry["h"].dtype, decode=True)
+    law = M3_RATE_STATIC if A_raw is None else M3_RATE_HEAVY_TAIL
+    desc = make_desc(x, B, theta, state_dtype=carry["h"].dtype, decode=True, rate_law=law)
+    rate = A_log if A_raw is None else A_raw
     if y is None:
         y = torch.empty_like(x)
     c = _carry(carry, dev, io, carry["h"].dtype)
     st = lib.m3_decode_step(ctypes.byref(desc), _ptr(x, dev, io, "x"), _ptr(B, dev, io, "B"), _ptr(C, dev, io, "C"),
                             _ptr(dt, dev, torch.float32, "dt"), _ptr(lam, dev, torch.float32, "lam"),
-                            _ptr(theta, dev, torch.float32, "theta"), _ptr(A_log, dev, torch.float32, "A_log"),
+                            _ptr(theta, dev, torch.float32, "theta"), _ptr(rate, dev, torch.float32, "A_log/A_raw"),
                             _ptr(B_bias, dev, torch.float32, "B_bias"), _ptr(C_bias, dev, torch.float32, "C_bias"),
                             ctypes.byref(c), _ptr(y, dev, io, "y"), _stream(dev))
     _check(st, "m3_decode_step")

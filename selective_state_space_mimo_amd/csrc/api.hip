@@ -37,6 +37,7 @@ m3_status check_desc(const m3_desc* d, bool scan) {
         (d->state_dtype != M3_F32 && d->state_dtype != M3_BF16))
         return M3_ERR_INVALID_ARG;
     if (scan && (d->seqlen < 0 || d->chunk < 1 || d->nsegments < 0)) return M3_ERR_INVALID_ARG;
+    if (d->rate_law != M3_RATE_STATIC && d->rate_law != M3_RATE_HEAVY_TAIL) return M3_ERR_INVALID_ARG;
     if (d->headdim > 256 || d->dstate > 256 || d->rank > 8) return M3_ERR_UNSUPPORTED;
     if (scan && d->chunk > 256) return M3_ERR_UNSUPPORTED;
     return M3_OK;
@@ -54,7 +55,7 @@ Sizes sizes(const m3_desc* d, long long L) {
     s.bc = b * L * G * R * N * io;
     s.tok = b * L * H * 4;
     s.theta = b * L * H * np * 4;
-    s.alog = H * 4;
+    s.alog = d->rate_law == M3_RATE_HEAVY_TAIL ? b * L * H * 4 : H * 4;
     s.bias = H * R * N * 4;
     s.h = b * H * P * N * st;
     s.phi = b * H * np * 4;
@@ -105,7 +106,7 @@ ScanArgs make_scan_args(const m3_desc* d, const void* x, const void* B, const vo
     a.io_bf16 = d->io_dtype == M3_BF16; a.st_bf16 = d->state_dtype == M3_BF16;
     a.Q = scan_mfma_chunk(a.io_bf16, a.P, a.N, a.R, d->chunk);
     a.x = x; a.B = B; a.C = C; a.dt = dt; a.lam = lam; a.theta = d->npairs ? theta : nullptr;
-    a.A_log = A_log; a.Bb = Bb; a.Cb = Cb;
+    a.A_log = A_log; a.rate_law = d->rate_law; a.Bb = Bb; a.Cb = Cb;
     if (init) { a.h0 = init->h; a.phi0 = d->npairs ? init->phi : nullptr; a.Bp0 = init->B_prev; a.xp0 = init->x_prev; }
     a.y = y;
     if (fin) { a.h1 = fin->h; a.phi1 = d->npairs ? fin->phi : nullptr; a.Bp1 = fin->B_prev; a.xp1 = fin->x_prev; }
@@ -255,6 +256,7 @@ m3_status m3_decode_step(const m3_desc* d, const void* x, const void* B, const v
     a.b = d->batch; a.H = d->nheads; a.G = d->ngroups; a.P = d->headdim; a.N = d->dstate; a.R = d->rank;
     a.np = d->npairs; a.io_bf16 = d->io_dtype == M3_BF16; a.st_bf16 = d->state_dtype == M3_BF16;
     a.x = x; a.B = B; a.C = C; a.dt = dt; a.lam = lam; a.theta = d->npairs ? theta : nullptr; a.A_log = A_log;
+    a.rate_law = d->rate_law;
     a.Bb = B_bias; a.Cb = C_bias;
     a.h = carry->h; a.phi = d->npairs ? carry->phi : nullptr; a.Bp = carry->B_prev; a.xp = carry->x_prev;
     a.y = y;

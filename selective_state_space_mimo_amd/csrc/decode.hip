@@ -95,7 +95,8 @@ __global__ __launch_bounds__(kThreads) void decode_fast_kernel(DecodeArgs a) {
     const int n0 = (tid & 15) * 8, prow = tid >> 4;
 
     // ---- 1. every global load this thread needs, issued before any use -------------
-    const float dt = a.dt[bh], lam = a.lam[bh], alog = a.A_log[h];
+    // the rate input: A_log [H] (static) or the per-token input [b][H]
+    const float dt = a.dt[bh], lam = a.lam[bh], alog = a.A_log[a.rate_law ? bh : h];
     // pair work (tid < R*N/2): rank r, pair i.  Addresses are clamped or
     // redirected to a zero word instead of branching, so that all loads are
     // in flight together.
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void decode_fast_kernel(DecodeArgs a) {
     for (int k = 0; k < 4; ++k) st[k] = __builtin_nontemporal_load(&hs[((prow + 16 * k) * kN + n0) / 8]);
 
     // ---- 2. per-head scalars ------------------------------------------------------------
-    const float alpha = expf(-dt * expf(alog));
+    const float alpha = expf(dt * (a.rate_law ? heavy_tail_rate(alog) : -expf(alog)));
     const float beta = alpha * dt * (1.f - lam), gamma = lam * dt;
 
     // ---- 3. biased, turned B and C (one adjacent pair per thread) -----------------------

@@ -22,6 +22,7 @@ struct ScanArgs {
     int io_bf16, st_bf16;
     const void* x; const void* B; const void* C;
     const float* dt; const float* lam; const float* theta; const float* A_log;
+    int rate_law;   // 0: A_log [H] static rates; 1: A_log holds the per-token rate input [b,L,H]
     const float* Bb; const float* Cb;
     // initial carry (each may be null = zero)
     const void* h0; const float* phi0; const void* Bp0; const void* xp0;
@@ -39,6 +40,7 @@ struct DecodeArgs {
     int io_bf16, st_bf16;
     const void* x; const void* B; const void* C;
     const float* dt; const float* lam; const float* theta; const float* A_log;
+    int rate_law;   // 0: A_log [H]; 1: A_log holds the per-token rate input [b,H]
     const float* Bb; const float* Cb;
     void* h; float* phi; void* Bp; void* xp;
     void* y;
@@ -71,6 +73,12 @@ __device__ __forceinline__ float ld_io(const void* p, size_t i, int is_bf16) {
 __device__ __forceinline__ void st_io(void* p, size_t i, float v, int is_bf16) {
     if (is_bf16) ((bf16*)p)[i] = (bf16)v;           // round to nearest even
     else ((float*)p)[i] = v;
+}
+// Decay rate (< 0) from a per-token input u: the heavy-tail activation, negated and
+// kept at or below -1e-4 (1 + u for u >= 0, 1 / (1 - u) for u < 0).
+__device__ __forceinline__ float heavy_tail_rate(float u) {
+    const float ht = u >= 0.f ? 1.f + u : 1.f / (1.f - u);
+    return fminf(-ht, -1e-4f);
 }
 // Reduce an angle into [0, 2 pi).
 __device__ __forceinline__ float wrap_2pi(float v) {

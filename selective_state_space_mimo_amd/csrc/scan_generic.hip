@@ -52,7 +52,8 @@ __global__ __launch_bounds__(kThreads) void scan_generic_kernel(ScanArgs a, int 
     const int bi = blockIdx.x / H, h = blockIdx.x % H, g = h * a.G / H;
     const int tid = threadIdx.x;
     GenLds s = carve(sm, P, N, R, np, qg);
-    const float ah = expf(a.A_log[h]);
+    const bool dyn = a.rate_law != 0;                // per-token rate input, [b][L][H]
+    const float ah = dyn ? 0.f : expf(a.A_log[h]);
     const size_t sh = (size_t)bi * H + h;           // stream index into [b][H]
     const size_t tok0 = (size_t)bi * L;              // token base into [b][L]
 
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void scan_generic_kernel(ScanArgs a, int 
             if (t < n) {
                 const size_t ti = (tok0 + c0 + t) * H + h;
                 const float dt = a.dt[ti], lm = a.lam[ti];
-                s.ell[t] = -dt * ah;
+                s.ell[t] = dyn ? dt * heavy_tail_rate(a.A_log[ti]) : -dt * ah;
                 s.gam[t] = lm * dt;
                 s.del[t] = dt * (1.f - lm);
             } else {
@@ -215,6 +216,7 @@ hipError_t launch_decode_generic(const DecodeArgs& d, hipStream_t st) {
     a.b = d.b; a.L = 1; a.H = d.H; a.G = d.G; a.P = d.P; a.N = d.N; a.R = d.R; a.np = d.np; a.Q = 1;
     a.io_bf16 = d.io_bf16; a.st_bf16 = d.st_bf16;
     a.x = d.x; a.B = d.B; a.C = d.C; a.dt = d.dt; a.lam = d.lam; a.theta = d.theta; a.A_log = d.A_log;
+    a.rate_law = d.rate_law;
     a.Bb = d.Bb; a.Cb = d.Cb;
     a.h0 = d.h; a.phi0 = d.phi; a.Bp0 = d.Bp; a.xp0 = d.xp;
     a.y = d.y;

@@ -249,7 +249,8 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
     const int T0 = seg * a.seglen;
     const int T1 = min(L, T0 + a.seglen);
     const bool last_seg = (T1 == L);
-    const float ah = expf(a.A_log[h]);
+    const bool dyn_rate = a.rate_law != 0;               // A_log holds the per-token rate input
+    const float ah = dyn_rate ? 0.f : expf(a.A_log[h]);
     const size_t ss = (size_t)bh * nseg + seg;
     const size_t S = (size_t)a.b * H * nseg;
     float* const wsHloc = a.ws;
@@ -267,6 +268,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
     const uint32_t bsb = (uint32_t)bstride * 2u, xsb = (uint32_t)xstride * 2u;   // bytes per token
     const float* const dtg = a.dt + tokbase * H + h;
     const float* const lamg = a.lam + tokbase * H + h;
+    const float* const rateg = a.A_log + (dyn_rate ? tokbase * H + h : 0);
     const float* const thg = np ? a.theta + (tokbase * H + h) * np : a.dt;
 
     // ---- shared set-up ------------------------------------------------------------------------
@@ -802,8 +804,9 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
                 *reinterpret_cast<uint4*>(xtt + q4_off(2 * lq + 1, pw)) = uint4{xt1[0], xt1[1], xt1[2], xt1[3]};
             }
         };
-        // dt, lam of the chunk at cstart and of the token after it (wave 4: lanes over tokens)
-        float rgDt[TPL], rgLam[TPL], rgDnT = 0.f, rgDnL = 0.f;
+        // dt, lam (and the rate input, per-token rates) of the chunk at cstart, and dt, lam
+        // of the token after it (wave 4: lanes over tokens)
+        float rgDt[TPL], rgLam[TPL], rgA[TPL], rgDnT = 0.f, rgDnL = 0.f;
         auto fetch_scalars = [&](int cstart) {
             if (pw == 0) {
 #pragma unroll
@@ -812,6 +815,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
                     const bool ok = t < Q && cstart + t < T1;
                     rgDt[k] = ok ? dtg[(size_t)(cstart + t) * H] : 0.f;
                     rgLam[k] = ok ? lamg[(size_t)(cstart + t) * H] : 0.f;
+                    rgA[k] = ok && dyn_rate ? rateg[(size_t)(cstart + t) * H] : 0.f;
                 }
                 if (lane == (Q - 1) / TPL) {
                     const bool ok = cstart + Q < L;
@@ -849,7 +853,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
                 for (int k = 0; k < TPL; ++k) {
                     const int t = lane * TPL + k;
                     const float dt = rgDt[k], lm = rgLam[k];
-                    la[k] = -dt * ah;
+                    la[k] = dt * (dyn_rate ? heavy_tail_rate(rgA[k]) : -ah);
                     gm[k] = lm * dt;
                     dl[k] = dt * (1.f - lm);
                     if (t < Q) sDt[t] = dt;

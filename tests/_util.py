@@ -30,7 +30,7 @@ def to_device(d, io_dtype, state_dtype, dev):
     out = {}
     for k in ("x", "B", "C"):
         out[k] = tdev(d[k], io_dtype, dev)
-    for k in ("dt", "lam", "theta", "A_log", "B_bias", "C_bias"):
+    for k in ("dt", "lam", "theta", "A_log", "A_raw", "B_bias", "C_bias"):
         out[k] = tdev(d.get(k), torch.float32, dev)
     if d.get("init") is not None:
         i = d["init"]

@@ -51,7 +51,7 @@ def m3():
 
 def _desc(m3, **kw):
     d = dict(batch=2, seqlen=8, nheads=4, ngroups=2, headdim=16, dstate=16, rank=2, npairs=2,
-             chunk=4, io_dtype=m3.M3_F32, state_dtype=m3.M3_F32, nsegments=0)
+             chunk=4, io_dtype=m3.M3_F32, state_dtype=m3.M3_F32, nsegments=0, rate_law=m3.M3_RATE_STATIC)
     d.update(kw)
     return m3.Desc(**d)
 
@@ -77,7 +77,7 @@ def test_invalid_descriptors(m3):
     n = ctypes.c_size_t(0)
     assert m3.lib.m3_scan_workspace_size(None, ctypes.byref(n)) == 1
     bad = [dict(nheads=3, ngroups=2), dict(npairs=9), dict(dstate=15), dict(batch=0), dict(chunk=0),
-           dict(rank=0), dict(io_dtype=7), dict(seqlen=-1)]
+           dict(rank=0), dict(io_dtype=7), dict(seqlen=-1), dict(rate_law=2)]
     for kw in bad:
         assert m3.lib.m3_scan_workspace_size(ctypes.byref(_desc(m3, **kw)), ctypes.byref(n)) == 1, kw
         assert _scan(m3, _desc(m3, **kw)) == 1, kw
@@ -97,6 +97,8 @@ def test_null_misaligned_and_aliased_pointers(m3):
     assert m3.lib.m3_decode_step(ctypes.byref(desc), FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000,
                                  FAKE + 0x400000, None, FAKE + 0x600000, None, None, ctypes.byref(c),
                                  FAKE + 0x700000, None) == 1     # theta missing
+    # per-token rates: the rate input spans [b, L, H], here reaching into y
+    assert _scan(m3, _desc(m3, rate_law=m3.M3_RATE_HEAVY_TAIL), A_log=FAKE + 0x700000 - 64) == 1
     c2 = m3.Carry(FAKE + 0x800000, FAKE + 0x900000, FAKE + 0x800010, FAKE + 0xb00000)   # B_prev inside h
     assert m3.lib.m3_decode_step(ctypes.byref(desc), FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000,
                                  FAKE + 0x400000, FAKE + 0x500000, FAKE + 0x600000, None, None, ctypes.byref(c2),

@@ -41,7 +41,8 @@ def _run_scan(m3, d, cfg, chunk=None, nsegments=0):
     sd = torch.float32 if cfg.state_dtype == "f32" else torch.bfloat16
     t = to_device(d, io, sd, dev)
     y, fin = m3.scan_fwd(t["x"], t["B"], t["C"], t["dt"], t["lam"], t["theta"], t["A_log"], t["B_bias"],
-                         t["C_bias"], t["init"], chunk=chunk or cfg.chunk, state_dtype=sd, nsegments=nsegments)
+                         t["C_bias"], t["init"], chunk=chunk or cfg.chunk, state_dtype=sd, nsegments=nsegments,
+                         A_raw=t["A_raw"])
     torch.cuda.synchronize()
     return y, fin
 
@@ -197,6 +198,44 @@ def test_scan_deterministic(m3):
     assert torch.equal(y1, y2) and torch.equal(f1["h"], f2["h"])
 
 
+# per-token (heavy-tail) decay rates: the generic route (f32), the MFMA route
+# (bf16, one and several segments) and the decode step
+RATE_DYN = [
+    # io,   P,  N,   R, np, G, Q,  L,   nseg
+    ("f32", 16, 16, 2, 4, 1, 16, 45, 0),
+    ("f32", 64, 128, 4, 32, 1, 64, 70, 0),
+    ("bf16", 64, 128, 4, 32, 1, 64, 150, 1),
+    ("bf16", 64, 128, 4, 32, 1, 64, 250, 3),
+    ("bf16", 64, 128, 1, 0, 2, 128, 200, 1),
+    ("bf16", 64, 128, 2, 16, 1, 32, 161, 2),
+]
+
+
+@pytest.mark.parametrize("case", RATE_DYN, ids=lambda c: "%s-P%d-N%d-R%d-np%d-G%d-Q%d-L%d-seg%d" % c)
+def test_scan_dynamic_rate(m3, case):
+    """Per-token rates A_t = min(-heavy_tail(u_t), -1e-4) (M3_RATE_HEAVY_TAIL);
+    u ~ N(0, 1) spans both branches of the law."""
+    io, P, N, R, npairs, G, Q, L, nseg = case
+    _say("dynamic-rate scan", case)
+    cfg, d = make_small_case(4000 + P + R + Q + L + nseg, batch=2, seqlen=L, nheads=4, ngroups=G, headdim=P,
+                             dstate=N, rank=R, npairs=npairs, chunk=Q, io_dtype=io, state_dtype="f32",
+                             bias=True, rms_bc=(io == "bf16"), init_full=True, rate_dyn=True)
+    yr, fr = ref_cpu.scan(d)
+    y, fin = _run_scan(m3, d, cfg, nsegments=nseg)
+    _compare(y, fin, yr, fr, io, what="dyn-rate")
+
+
+def test_scan_dynamic_rate_floor(m3):
+    """Very negative rate inputs hit the -1e-4 floor: long memory, through the
+    MFMA route, against the oracle."""
+    cfg, d = make_small_case(4100, batch=1, seqlen=200, nheads=2, ngroups=1, headdim=64, dstate=128, rank=4,
+                             npairs=32, chunk=64, io_dtype="bf16", rms_bc=True, init_full=True, rate_dyn=True)
+    d["A_raw"][:, ::2] = np.float32(-3e4)      # |A| = 1/(1 + 3e4) < 1e-4: floored
+    yr, fr = ref_cpu.scan(d)
+    y, fin = _run_scan(m3, d, cfg)
+    _compare(y, fin, yr, fr, "bf16", what="dyn-rate floor")
+
+
 # -----------------------------------------------------------------------------
 # decode step
 # -----------------------------------------------------------------------------
@@ -208,17 +247,23 @@ DECODE = [
     ("bf16", "bf16", 64, 128, 1, 0, 1, 6),
     ("bf16", "f32", 64, 128, 4, 32, 1, 5),
     ("bf16", "bf16", 32, 64, 4, 8, 1, 5),
+    # per-token (heavy-tail) rates
+    ("f32", "f32", 16, 16, 2, 4, 1, 5, True),
+    ("bf16", "f32", 64, 128, 4, 32, 1, 6, True),
 ]
 
 
-@pytest.mark.parametrize("case", DECODE, ids=lambda c: "%s-%s-P%d-N%d-R%d-np%d-G%d-S%d" % c)
+@pytest.mark.parametrize("case", DECODE, ids=lambda c: "%s-%s-P%d-N%d-R%d-np%d-G%d-S%d" % c[:8]
+                         + ("-dyn" if len(c) > 8 else ""))
 def test_decode_steps(m3, case):
     """k decode steps through m3_decode_step equal the oracle's recurrence over
     k tokens (carried state, phase, previous write)."""
-    io, sdt, P, N, R, npairs, G, steps = case
+    io, sdt, P, N, R, npairs, G, steps = case[:8]
+    dyn = len(case) > 8 and case[8]
     _say("decode", case)
     cfg, _ = make_small_case(0, batch=3, seqlen=steps, nheads=4, ngroups=G, headdim=P, dstate=N, rank=R,
-                             npairs=npairs, io_dtype=io, state_dtype=sdt, bias=True, rms_bc=(io == "bf16"))
+                             npairs=npairs, io_dtype=io, state_dtype=sdt, bias=True, rms_bc=(io == "bf16"),
+                             rate_dyn=dyn)
     cfg = cfg.with_(init_state=True, init_full=True)
     d = make_decode_inputs(cfg, steps, seed=77)
     yr, fr = ref_cpu.scan(d)
@@ -232,7 +277,8 @@ def test_decode_steps(m3, case):
         ys.append(m3.decode_step(t["x"][:, s].contiguous(), t["B"][:, s].contiguous(), t["C"][:, s].contiguous(),
                                  t["dt"][:, s].contiguous(), t["lam"][:, s].contiguous(),
                                  None if t["theta"] is None else t["theta"][:, s].contiguous(),
-                                 t["A_log"], t["B_bias"], t["C_bias"], carry))
+                                 t["A_log"], t["B_bias"], t["C_bias"], carry,
+                                 A_raw=None if t["A_raw"] is None else t["A_raw"][:, s].contiguous()))
     torch.cuda.synchronize()
     y = torch.stack(ys, dim=1)
     _compare(y, carry, yr, fr, io, what="decode")

@@ -422,6 +422,110 @@ def test_counted_decode_step(P, N, R):
 
 
 # --------------------------------------------------------------------------
+# pin 14: per-token decay rates (the heavy-tail law)
+# --------------------------------------------------------------------------
+def test_heavy_tail_rate_closed_form():
+    """[M3] remarks after the decode listing: heavy_tail(u) is 1 + u for
+    u >= 0 and 1 / (1 - u) for u < 0; the rate is its negation clamped at
+    -1e-4.  Values by hand, the floor, and the joint at u = 0 (value and slope
+    1 from both sides)."""
+    u = np.array([0.0, 2.0, 0.5, -1.0, -3.0, -1e5, -1e9, 7.0])
+    want = np.array([-1.0, -3.0, -1.5, -0.5, -0.25, -1e-4, -1e-4, -8.0])
+    assert np.array_equal(ref.heavy_tail_rate(u), want)
+    assert float(ref.heavy_tail_rate(-9998.0)) == pytest.approx(-1.0 / 9999.0, rel=1e-15)  # just above the floor
+    e = 1e-7
+    left = (ref.heavy_tail_rate(0.0) - ref.heavy_tail_rate(-e)) / e
+    right = (ref.heavy_tail_rate(e) - ref.heavy_tail_rate(0.0)) / e
+    assert left == pytest.approx(-1.0, abs=1e-6) and right == pytest.approx(-1.0, abs=1e-6)
+    grid = np.linspace(-50.0, 50.0, 2001)
+    assert np.all(np.diff(ref.heavy_tail_rate(grid)) < 0)      # strictly decreasing above the floor
+
+
+def _case_scalar_dyn(dts, lams, xs, us):
+    d = _case_scalar(dts, lams, xs)
+    d["A_raw"] = np.array(us, np.float32).reshape(1, len(xs), 1)
+    d["A_log"] = np.array([123.0], np.float32)       # must not be read
+    return d
+
+
+@pytest.mark.parametrize("form", sorted(ALL_FORMS))
+def test_dynamic_rate_worked_example(form):
+    """[M3] worked step with the rate input u = 0 (heavy_tail = 1, A = -1)
+    reproduces the page's 0.35, 0.303, 0.184; with u = (0, 1, -1) token t's
+    own rate decays the state entering token t: 0.35, e^{-1} 0.5 and
+    e^{-1/4} e^{-1} 0.5 by hand."""
+    g = json.load(open(os.path.join(GOLD, "worked_example.json")))
+    fn = ALL_FORMS[form]
+    y, _ = fn(_case_scalar_dyn([0.5] * 3, [0.7] * 3, [1.0, 0.0, 0.0], [0.0, 0.0, 0.0]))
+    tol = 0.5 * 10.0 ** -g["printed_decimals"]
+    np.testing.assert_allclose(y.reshape(-1), g["mamba3_states"], atol=tol)
+    y, _ = fn(_case_scalar_dyn([0.5] * 3, [0.7] * 3, [1.0, 0.0, 0.0], [0.0, 1.0, -1.0]))
+    h1 = math.exp(0.5 * -2.0) * 0.5          # a_1 (gamma_0 + delta_1) x_0, A_1 = -2
+    h2 = math.exp(0.5 * -0.5) * h1           # A_2 = -1/2
+    assert np.allclose(y.reshape(-1), [0.35, h1, h2], rtol=1e-6, atol=0)
+
+
+def test_dynamic_rate_equals_static():
+    """A per-token rate input that is constant per head, u = exp(A_log) - 1
+    (heavy_tail(u) = exp(A_log) on the u >= 0 branch), gives the static-rate
+    result; and so does u = 1 - exp(-A_log) on the u < 0 branch for heads
+    whose rate magnitude is below 1."""
+    _, d = make_small_case(131, batch=2, seqlen=14, nheads=3, ngroups=1, headdim=3, dstate=6, rank=2,
+                           npairs=2, init_full=True, dt_scale=2.0)
+    d["A_log"] = np.array([0.3, 1.7, -0.9])          # exp: 1.35, 5.47, 0.41
+    y0, f0 = ref.scan_seq(d)
+    a = np.exp(d["A_log"])
+    u = np.where(a >= 1.0, a - 1.0, 1.0 - 1.0 / a)
+    dd = dict(d, A_raw=np.broadcast_to(u, (2, 14, 3)).copy(), A_log=None)
+    for fn in (ref.scan_seq, ref.scan_quadratic, lambda z: ref.scan_chunked(z, 4), ref.scan_seq_unrotated):
+        y1, f1 = fn(dd)
+        assert _rel(y1, y0) < 1e-12
+        assert _rel(f1["h"], f0["h"]) < 1e-12
+
+
+@pytest.mark.parametrize("seed,R,npairs,L", [(141, 1, 0, 11), (142, 3, 2, 13), (143, 4, 3, 10)])
+def test_dynamic_rate_forms_agree(seed, R, npairs, L):
+    """With rates that change every token (u ~ N(0, 4), both branches and some
+    at the floor): the explicit decay products of the masked form, the
+    sequential recurrence, the chunk-local log-sums at every chunk size, the
+    unrotated state and the C recurrence all agree."""
+    _, d = make_small_case(seed, batch=2, seqlen=L, nheads=2, ngroups=1, headdim=3, dstate=6, rank=R,
+                           npairs=npairs, init_full=True, dt_scale=2.0, rate_dyn=True)
+    d["A_raw"] = (d["A_raw"] * 2.0).astype(np.float32)
+    d["A_raw"][0, 1, 0] = -2e4                        # one floored token
+    y0, f0 = ref.scan_seq(d)
+    yq, fq = ref.scan_quadratic(d)
+    assert _rel(yq, y0) < 1e-12 and _rel(fq["h"], f0["h"]) < 1e-12
+    for q in range(1, L + 1):
+        yc, fc = ref.scan_chunked(d, q)
+        assert _rel(yc, y0) < 1e-12 and _rel(fc["h"], f0["h"]) < 1e-12, q
+    yu, fu = ref.scan_seq_unrotated(d)
+    assert _rel(yu, y0) < 1e-12
+    yc, fc = ref_cpu.scan(d)
+    assert _rel(yc, y0) < 1e-12 and _rel(fc["h"], f0["h"]) < 1e-12
+    # a rate that differs from the static one changes the result
+    ys, _ = ref.scan_seq(dict(d, A_raw=None))
+    assert _rel(ys, y0) > 1e-2
+
+
+def test_dynamic_rate_decode_continuation():
+    """[M3] decode listing (A = -heavy_tail(A_r) per token): token-by-token
+    decode with per-token rate inputs equals the whole-sequence scan."""
+    _, d = make_small_case(151, batch=2, seqlen=9, nheads=2, ngroups=1, headdim=3, dstate=6, rank=2,
+                           npairs=2, init_full=True, rate_dyn=True)
+    y, f = ref.scan_seq(d)
+    carry = {k: np.asarray(v, np.float64) for k, v in d["init"].items()}
+    ys = []
+    for t in range(9):
+        yt, carry = ref.decode_step(carry, d["x"][:, t], d["B"][:, t], d["C"][:, t], d["dt"][:, t],
+                                    d["lam"][:, t], d["theta"][:, t], None, d["B_bias"], d["C_bias"],
+                                    A_raw=d["A_raw"][:, t])
+        ys.append(yt)
+    assert _rel(np.stack(ys, axis=1), y) < 1e-12
+    assert _rel(carry["h"], f["h"]) < 1e-12
+
+
+# --------------------------------------------------------------------------
 # the C oracle against the numpy oracle
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("seed,G,R,npairs,bias", [
@@ -478,6 +582,18 @@ def test_planted_mistakes_are_caught(monkeypatch):
     y_bad, _ = ref.scan_seq(d)
     monkeypatch.setattr(ref, "rot", orig)
     assert _rel(y_bad, y_ok) > 1e-3
+    # (d) the decay of token t taken from token t - 1's rate input: breaks the
+    # per-token worked example (0.303 instead of e^{-1} 0.5 = 0.184)
+    orig_rate = ref._rate_mag
+
+    def lagged_rate(inp, bi, h, L):
+        a = orig_rate(inp, bi, h, L)
+        return np.concatenate([a[:1], a[:-1]])
+    dd = _case_scalar_dyn([0.5] * 3, [0.7] * 3, [1.0, 0.0, 0.0], [0.0, 1.0, -1.0])
+    monkeypatch.setattr(ref, "_rate_mag", lagged_rate)
+    y_bad, _ = ref.scan_seq(dd)
+    monkeypatch.setattr(ref, "_rate_mag", orig_rate)
+    assert abs(y_bad.reshape(-1)[1] - math.exp(-1.0) * 0.5) > 0.1
     # (c) a dropped lagged term: breaks the worked example
     s2 = _case_scalar([0.5] * 3, [0.7] * 3, [1.0, 0.0, 0.0])
     y2, _ = ref.scan_seq(s2)
