@@ -129,7 +129,7 @@ __device__ __forceinline__ float2 rot_pair(uint32_t v, uint32_t bias, uint2 cs) 
 }
 __device__ __forceinline__ uint2 cs_entry(float c, float s) { return uint2{pack2(c, -s), pack2(s, c)}; }
 
-template <int Q>
+template <int R, int Q>
 struct Layout {
     static constexpr int hs = 2 * kBufBytes;
     // [Q][64] two bf16 pairs, (cos, -sin) and (sin, cos); pair i of token t sits in column
@@ -156,7 +156,7 @@ struct Layout {
     static constexpr bool kYStage = Q <= 64;
     static constexpr int xsc = misc + 16 * 4;                 // per consumer 4 KiB (Q = 128)
     static constexpr int ysg = xsc + (kYStage ? 0 : 4 * 4096);
-    static constexpr int total = ysg + (kYStage ? kMaxRows * 144 : 0);
+    static constexpr int total = ysg + (kYStage ? R * Q * 144 : 0);
 };
 
 // DPP read of v from another lane; lanes whose source is outside the pattern (or
@@ -209,8 +209,14 @@ constexpr bool ctile_blocks_increase() {
 }
 static_assert(ctile_blocks_increase(), "one diagonal tile per key block and consumer");
 
+// Chunks of 16 tokens at R = 4 (64 rows: the small-chunk MIMO schedule) fit two workgroups
+// per CU: at most 128 registers per lane (four waves per SIMD) and half the LDS.  The extra
+// waves hide the latencies that one workgroup's two waves per SIMD leave exposed.
+template <int R, int Q>
+constexpr int waves_per_simd() { return (R == 4 && Q == 16) ? 4 : 2; }
+
 template <int R, int Q, int MODE>
-__global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
+__global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_kernel(ScanArgs a) {
     constexpr int M = Q * R;                 // rows per chunk
     constexpr int NKB = M / kKB;             // key blocks per chunk
     constexpr int NT = M / 16;               // query tiles per chunk
@@ -220,7 +226,8 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
     constexpr bool kEarlyExp = KT == 1;      // decay exps ahead of the score MFMAs (registers allow)
     constexpr bool kFullMode = MODE == kFull;
     static_assert(TPC >= 1 && TPC <= 4 && NKB >= 2 && NKB % 2 == 0, "chunk shape");
-    using LY = Layout<Q>;
+    using LY = Layout<R, Q>;
+    static_assert(waves_per_simd<R, Q>() == 2 || LY::total <= 80 * 1024, "two workgroups per CU fit the LDS");
     extern __shared__ __attribute__((aligned(16))) char smem[];
     float* sL2 = reinterpret_cast<float*>(smem + LY::l2);
     float* sG1 = reinterpret_cast<float*>(smem + LY::g1);
@@ -283,17 +290,19 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
     for (int e = tid; e < Q * 64; e += kThreads)
         if ((e & 63) >= np) sCS[(e & ~63) + ((e & 63) ^ ((e >> 6) & 60))] = cs_entry(1.f, 0.f);
 
-    // theta of the chunk at cstart (all threads: token tid / 8, pairs 8 (tid % 8) + u),
-    // one buffer load per value.  Token t's np angles of this head start t H np after the
+    // theta of the chunk at cstart (all threads: THU consecutive pairs of one token each,
+    // THP times), one buffer load per value.  Token t's np angles of this head start t H np after the
     // chunk's first; the record count ends at this head's last angle of the last valid
     // token, so nothing past the segment end or past the tensor is read.  Lanes of pairs
     // at or past np read zero (those values are never used).
-    constexpr int THP = (Q + 63) / 64;
-    auto load_theta = [&](int cstart, float (&th)[THP][8]) {
+    constexpr int THP = (Q + 63) / 64;                    // token rounds
+    constexpr int THU = Q >= 64 ? 8 : Q / 8;              // pairs per thread and round
+    constexpr int THG = 64 / THU;                         // threads per token
+    auto load_theta = [&](int cstart, float (&th)[THP][THU]) {
         int tt = tid;                                         // opaque: offsets formed here
         asm volatile("" : "+v"(tt));
             tt &= kThreads - 1;                               // a thread index: non-negative
-        const int th_t = tt >> 3, th_i = (tt & 7) * 8;
+        const int th_t = tt / THG, th_i = (tt % THG) * THU;
         const int nt = __builtin_amdgcn_readfirstlane(min(max(T1 - cstart, 0), Q));
         const uint32_t nrec = nt > 0 ? (uint32_t)((nt - 1) * H * np + np) * 4u : 0u;
         const __amdgpu_buffer_rsrc_t rt = make_rsrc(thg + (size_t)cstart * H * np, nrec);
@@ -302,20 +311,20 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
             // a group wholly past np gets an offset beyond every record count
             const int vo = th_i < np ? ((th_t + 64 * pp) * H * np + th_i) * 4 : 0x7fffff00;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) th[pp][u] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rt, vo + 4 * u, 0, 0));
+            for (int u = 0; u < THU; ++u) th[pp][u] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rt, vo + 4 * u, 0, 0));
         }
     };
-    auto stage_theta = [&](const float (&th)[THP][8]) {
+    auto stage_theta = [&](const float (&th)[THP][THU]) {
         int tt = tid;
         asm volatile("" : "+v"(tt));
             tt &= kThreads - 1;                               // a thread index: non-negative
-        const int th_t = tt >> 3, th_i = (tt & 7) * 8;
+        const int th_t = tt / THG, th_i = (tt % THG) * THU;
 #pragma unroll
         for (int pp = 0; pp < THP; ++pp) {
             const int t = th_t + 64 * pp;
             if (t < Q) {
 #pragma unroll
-                for (int u = 0; u < 8; ++u) stage[(th_i + u) * (Q + 1) + t] = th[pp][u];
+                for (int u = 0; u < THU; ++u) stage[(th_i + u) * (Q + 1) + t] = th[pp][u];
             }
         }
     };
@@ -352,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
         if (np <= 32) run(std::integral_constant<int, 16>{});
         else run(std::integral_constant<int, 8>{});
     };
-    float rgTh[THP][8];
+    float rgTh[THP][THU];
     load_theta(T0, rgTh);
     __syncthreads();
 
@@ -444,12 +453,12 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
         bool pre = false;
         int cidx = 0;
         for (int c0 = T0; c0 < T1; c0 += Q, ++cidx) {
-            // (A) the chunk's C rows; theta into the staging area
+            // (A) theta into the staging area (loaded a chunk ago), then the chunk's C rows
+            stage_theta(rgTh);
             if (kFullMode) {
                 if (pre) load_c(c0, std::integral_constant<int, TPC - 1>{}, std::integral_constant<int, TPC>{});
                 else load_c(c0, std::integral_constant<int, 0>{}, std::integral_constant<int, TPC>{});
             }
-            stage_theta(rgTh);
             load_theta(c0 + Q, rgTh);
             __syncthreads();
             angles();
@@ -470,23 +479,32 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(ScanArgs a) {
 #pragma unroll
                 for (int k = 0; k < TPC; ++k) {
                     const int qi = 16 * ctile(c, k) + l16;
-                    const int t = qi / R, r = qi % R;
+                    const int t = qi / R;
                     tq[k] = t;
                     l2q[k] = sL2[t];
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks) {
                         const int i0 = 16 * ks + 4 * g4;             // first pair
                         const uint4 raw = __builtin_bit_cast(uint4, cq[k][ks]);
-                        const uint4 bi = *reinterpret_cast<const uint4*>(sCb + r * 64 + i0);
-                        const uint2* ce = sCS + t * 64 + (i0 ^ (t & 60));   // pairs i0 .. i0 + 3
-                        const uint4 c01 = *reinterpret_cast<const uint4*>(ce);
-                        const uint4 c23 = *reinterpret_cast<const uint4*>(ce + 2);
-                        const float2 p0 = rot_pair(raw.x, bi.x, uint2{c01.x, c01.y});
-                        const float2 p1 = rot_pair(raw.y, bi.y, uint2{c01.z, c01.w});
-                        const float2 p2 = rot_pair(raw.z, bi.z, uint2{c23.x, c23.y});
-                        const float2 p3 = rot_pair(raw.w, bi.w, uint2{c23.z, c23.w});
-                        cq[k][ks] = __builtin_bit_cast(bf16x8, uint4{pack2(p0.x, p0.y), pack2(p1.x, p1.y),
-                                                                     pack2(p2.x, p2.y), pack2(p3.x, p3.y)});
+                        // a lane's rows have rank l16 % R in every tile (16 % R == 0)
+                        const uint4 bi = *reinterpret_cast<const uint4*>(sCb + (l16 % R) * 64 + i0);
+                        uint4 o;
+                        if (16 * ks >= np) {                          // no pair of this slice turns
+                            o = uint4{pack2(lo_f(raw.x) + lo_f(bi.x), hi_f(raw.x) + hi_f(bi.x)),
+                                      pack2(lo_f(raw.y) + lo_f(bi.y), hi_f(raw.y) + hi_f(bi.y)),
+                                      pack2(lo_f(raw.z) + lo_f(bi.z), hi_f(raw.z) + hi_f(bi.z)),
+                                      pack2(lo_f(raw.w) + lo_f(bi.w), hi_f(raw.w) + hi_f(bi.w))};
+                        } else {
+                            const uint2* ce = sCS + t * 64 + (i0 ^ (t & 60));   // pairs i0 .. i0 + 3
+                            const uint4 c01 = *reinterpret_cast<const uint4*>(ce);
+                            const uint4 c23 = *reinterpret_cast<const uint4*>(ce + 2);
+                            const float2 p0 = rot_pair(raw.x, bi.x, uint2{c01.x, c01.y});
+                            const float2 p1 = rot_pair(raw.y, bi.y, uint2{c01.z, c01.w});
+                            const float2 p2 = rot_pair(raw.z, bi.z, uint2{c23.x, c23.y});
+                            const float2 p3 = rot_pair(raw.w, bi.w, uint2{c23.z, c23.w});
+                            o = uint4{pack2(p0.x, p0.y), pack2(p1.x, p1.y), pack2(p2.x, p2.y), pack2(p3.x, p3.y)};
+                        }
+                        cq[k][ks] = __builtin_bit_cast(bf16x8, o);
                     }
                 }
 #pragma unroll
@@ -1059,7 +1077,7 @@ __global__ __launch_bounds__(256) void carry_pass_kernel(ScanArgs a) {
 
 template <int R, int Q>
 hipError_t launch_rq(const ScanArgs& a, hipStream_t st) {
-    const size_t lds = Layout<Q>::total;
+    const size_t lds = Layout<R, Q>::total;
     const int nblk = a.b * a.H * a.nseg;
     hipError_t e;
     if (a.nseg > 1) {
@@ -1082,7 +1100,7 @@ hipError_t launch_rq(const ScanArgs& a, hipStream_t st) {
 
 int scan_mfma_chunk(int io_bf16, int P, int N, int R, int Q) {
     if (!io_bf16 || P != kP || N != kN || !(R == 1 || R == 2 || R == 4)) return Q;
-    return Q * R > kMaxRows ? kMaxRows / R : Q;
+    return Q * R > kMaxRows ? 64 / R : Q;        // oversize: the small-chunk schedule
 }
 
 bool scan_mfma_supported(const ScanArgs& a) {

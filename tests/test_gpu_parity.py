@@ -159,13 +159,15 @@ def test_scan_segments_agree(m3):
 
 def test_long_chunk_request_is_split(m3):
     """A chunk longer than the matrix-core path's 256 rows (R = 4, Q = 128) runs
-    as chunks of 64 tokens: the same schedule, hence the same bits, as asking
-    for 64."""
+    on the small-chunk schedule (16 tokens): the same schedule, hence the same
+    bits, as asking for 16."""
     cfg, d = make_small_case(3011, batch=2, seqlen=300, nheads=2, ngroups=1, headdim=64, dstate=128, rank=4,
                              npairs=32, chunk=128, io_dtype="bf16", rms_bc=True, init_full=True)
     y128, f128 = _run_scan(m3, d, cfg, chunk=128)
-    y64, f64 = _run_scan(m3, d, cfg, chunk=64)
-    assert torch.equal(y128, y64) and torch.equal(f128["h"], f64["h"])
+    y16, f16 = _run_scan(m3, d, cfg, chunk=16)
+    assert torch.equal(y128, y16) and torch.equal(f128["h"], f16["h"])
+    yr, fr = ref_cpu.scan(d)
+    _compare(y128, f128, yr, fr, "bf16", what="Q128 -> 16")
 
 
 def test_config1_tiny_siso_f32(m3):
@@ -208,6 +210,7 @@ RATE_DYN = [
     ("bf16", 64, 128, 4, 32, 1, 64, 250, 3),
     ("bf16", 64, 128, 1, 0, 2, 128, 200, 1),
     ("bf16", 64, 128, 2, 16, 1, 32, 161, 2),
+    ("bf16", 64, 128, 4, 32, 1, 16, 90, 2),
 ]
 
 
