@@ -141,8 +141,12 @@ struct Layout {
     static constexpr int g1 = l2 + Q * 4;
     static constexpr int gam = g1 + Q * 4;
     static constexpr int vs = gam + Q * 4;
+    // raw per-token inputs of the chunk, staged by the consumers: dt and lambda of its Q
+    // tokens and of the token after it ([Q + 4], 16-byte multiples), the rate input [Q]
     static constexpr int dtv = vs + Q * 4;
-    static constexpr int phic = dtv + Q * 4;                  // float [64]
+    static constexpr int lmv = dtv + (Q + 4) * 4;
+    static constexpr int arv = lmv + (Q + 4) * 4;
+    static constexpr int phic = arv + Q * 4;                  // float [64]
     static constexpr int misc = phic + 64 * 4;                // float [16]
     // float [64][Q + 1]: theta, pair-major.  It shares the key-block buffers, which hold
     // nothing from the last key block of a chunk to the next chunk's block-0 tiles (the
@@ -234,6 +238,8 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
     float* sGam = reinterpret_cast<float*>(smem + LY::gam);
     float* sV = reinterpret_cast<float*>(smem + LY::vs);
     float* sDt = reinterpret_cast<float*>(smem + LY::dtv);
+    float* sLm = reinterpret_cast<float*>(smem + LY::lmv);
+    float* sAr = reinterpret_cast<float*>(smem + LY::arv);
     float* sPhic = reinterpret_cast<float*>(smem + LY::phic);
     uint2* sCS = reinterpret_cast<uint2*>(smem + LY::cs);
     uint32_t* sCb = reinterpret_cast<uint32_t*>(smem + LY::cbias);
@@ -361,8 +367,44 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
         if (np <= 32) run(std::integral_constant<int, 16>{});
         else run(std::integral_constant<int, 8>{});
     };
+    // A chunk's raw per-token inputs (dt and lambda of its tokens and of the next one, the
+    // rate input), loaded by the producer threads at the previous chunk's start (value e:
+    // dt of token e, then lambda, then the rate input) and staged in LDS at its first key
+    // block ahead of that block's row fetches, when they have long arrived; the wave that
+    // scans them then reads LDS only and never waits on the row fetches.
+    constexpr int NSV = (3 * Q + 2 + kNC * 64 - 1) / (kNC * 64);
+    float rgS[NSV];
+    auto load_scalars = [&](int cstart) {
+#pragma unroll
+        for (int j = 0; j < NSV; ++j) {
+            const int e = tid - kNC * 64 + kNC * 64 * j;
+            float v = 0.f;
+            if (e < 2 * Q + 2) {
+                const int t = e <= Q ? e : e - (Q + 1);
+                const bool ok = t < Q ? cstart + t < T1 : cstart + Q < L;
+                if (ok) v = (e <= Q ? dtg : lamg)[(size_t)(cstart + t) * H];
+            } else if (e < 3 * Q + 2 && dyn_rate) {
+                const int t = e - (2 * Q + 2);
+                if (cstart + t < T1) v = rateg[(size_t)(cstart + t) * H];
+            }
+            rgS[j] = v;
+        }
+    };
+    auto stage_scalars = [&]() {
+#pragma unroll
+        for (int j = 0; j < NSV; ++j) {
+            const int e = tid - kNC * 64 + kNC * 64 * j;
+            if (e <= Q) sDt[e] = rgS[j];
+            else if (e < 2 * Q + 2) sLm[e - (Q + 1)] = rgS[j];
+            else if (e < 3 * Q + 2) sAr[e - (2 * Q + 2)] = rgS[j];
+        }
+    };
     float rgTh[THP][THU];
     load_theta(T0, rgTh);
+    if (w >= kNC) {
+        load_scalars(T0);
+        stage_scalars();
+    }
     __syncthreads();
 
     if (w < kNC) {
@@ -453,7 +495,8 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
         bool pre = false;
         int cidx = 0;
         for (int c0 = T0; c0 < T1; c0 += Q, ++cidx) {
-            // (A) theta into the staging area (loaded a chunk ago), then the chunk's C rows
+            // (A) theta into LDS (loaded a chunk ago), then the chunk's C rows, the next
+            //     chunk's theta and per-token inputs
             stage_theta(rgTh);
             if (kFullMode) {
                 if (pre) load_c(c0, std::integral_constant<int, TPC - 1>{}, std::integral_constant<int, TPC>{});
@@ -822,34 +865,12 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
                 *reinterpret_cast<uint4*>(xtt + q4_off(2 * lq + 1, pw)) = uint4{xt1[0], xt1[1], xt1[2], xt1[3]};
             }
         };
-        // dt, lam (and the rate input, per-token rates) of the chunk at cstart, and dt, lam
-        // of the token after it (wave 4: lanes over tokens)
-        float rgDt[TPL], rgLam[TPL], rgA[TPL], rgDnT = 0.f, rgDnL = 0.f;
-        auto fetch_scalars = [&](int cstart) {
-            if (pw == 0) {
-#pragma unroll
-                for (int k = 0; k < TPL; ++k) {
-                    const int t = lane * TPL + k;
-                    const bool ok = t < Q && cstart + t < T1;
-                    rgDt[k] = ok ? dtg[(size_t)(cstart + t) * H] : 0.f;
-                    rgLam[k] = ok ? lamg[(size_t)(cstart + t) * H] : 0.f;
-                    rgA[k] = ok && dyn_rate ? rateg[(size_t)(cstart + t) * H] : 0.f;
-                }
-                if (lane == (Q - 1) / TPL) {
-                    const bool ok = cstart + Q < L;
-                    rgDnT = ok ? dtg[(size_t)(cstart + Q) * H] : 0.f;
-                    rgDnL = ok ? lamg[(size_t)(cstart + Q) * H] : 0.f;
-                }
-            }
-        };
 #pragma unroll
         for (int d = 0; d < DP; ++d) fetch(rgB[d], rgX[d]);
-        fetch_scalars(T0);
 
         int cidx = 0;
         for (int c0 = T0; c0 < T1; c0 += Q, ++cidx) {
-            // (A) state snapshot (bf16, the carry readout's operand); theta staging; wave 4
-            //     scans the log-decays and tables the per-token scalars
+            // (A) state snapshot (bf16, the carry readout's operand); theta staging
             if (kFullMode) {
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
@@ -864,17 +885,21 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
             }
             stage_theta(rgTh);
             load_theta(c0 + Q, rgTh);
+            load_scalars(c0 + Q);
+            // wave 4 scans the log-decays from the staged inputs and tables the per-token scalars
             if (pw == 0) {
                 float la[TPL], gm[TPL], dl[TPL];
                 float lsum = 0.f;
 #pragma unroll
                 for (int k = 0; k < TPL; ++k) {
                     const int t = lane * TPL + k;
-                    const float dt = rgDt[k], lm = rgLam[k];
-                    la[k] = dt * (dyn_rate ? heavy_tail_rate(rgA[k]) : -ah);
+                    const bool in = t < Q;
+                    const float dt = in ? sDt[t] : 0.f, lm = in ? sLm[t] : 0.f;
+                    float rate = -ah;
+                    if (dyn_rate) rate = heavy_tail_rate(in ? sAr[t] : 0.f);
+                    la[k] = dt * rate;
                     gm[k] = lm * dt;
                     dl[k] = dt * (1.f - lm);
-                    if (t < Q) sDt[t] = dt;
                     lsum += la[k];
                     la[k] = lsum;
                 }
@@ -883,7 +908,7 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
                 const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
                 const float le = tot * kLog2e;
                 const float nx = dpp_read<0x130>(dl[0]);           // wave_shl:1
-                const float dnext = rgDnT * (1.f - rgDnL);
+                const float dnext = sDt[Q] * (1.f - sLm[Q]);
 #pragma unroll
                 for (int k = 0; k < TPL; ++k) {
                     const int t = lane * TPL + k;
@@ -899,7 +924,6 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
                 if (lane == 0) sMisc[0] = le;
                 lam_sum += tot;
             }
-            fetch_scalars(c0 + Q);
             __syncthreads();
             angles();
             __syncthreads();
@@ -924,6 +948,7 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
 #pragma unroll
                 for (int d = 0; d < DP; ++d) {
                     const int J = J0 + d;
+                    if (J == 0) stage_scalars();              // the next chunk's inputs
                     fetch(rgB[d], rgX[d]);
                     // every LDS read of the iteration first (block J's operands, block J + 1's
                     // angles and v), then the state MFMAs, then block J + 1's tiles
