@@ -128,9 +128,17 @@ def decode_bytes_per_head_step(cfg):
 # ---------------------------------------------------------------------------
 # timing helpers
 # ---------------------------------------------------------------------------
-def time_calls(torch, fn, steps, warmup):
+def time_calls(torch, fn, steps, warmup, ramp_s=0.25):
     """Mean ms per call over `steps` calls after `warmup`, HIP events on the
-    current stream (the stream the library launches on)."""
+    current stream (the stream the library launches on).  Before the warm-up
+    calls the workload runs untimed for `ramp_s` seconds: an idle GPU raises its
+    clocks over the first tens of milliseconds of load, and a serving or training
+    loop runs at the raised clocks."""
+    t0 = time.time()
+    while time.time() - t0 < ramp_s:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()

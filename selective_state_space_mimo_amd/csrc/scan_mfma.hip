@@ -57,7 +57,8 @@ namespace m3 {
 
 namespace {
 
-constexpr int kP = 64, kN = 128, kKB = 32, kNW = 8, kThreads = 64 * kNW;
+constexpr int kP = 64, kN = 128, kKB = 32;
+constexpr int kNP = 4;                   // producer waves
 constexpr int kMaxRows = 256;            // rows (tokens x ranks) per chunk
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -193,45 +194,62 @@ __device__ __forceinline__ float group_scan(float v, int lane_in_group) {
 // ---- warp-specialised variant (chunks of at most 256 rows) ----------------------------------
 // Waves 0-3 are consumers: each keeps a quarter of the chunk's query tiles (C tiles in
 // registers, Y^T accumulators) and runs the scores, their weighting and Y^T += X^T S'^T.
-// Waves 4-7 are producers: each turns 8 of every key block's 32 rows into the LDS tiles
-// and owns 32 columns of the state (Hf^T += (v Bt)^T X).  A SIMD then holds one wave of
-// each kind, so that the producers' vector work overlaps the consumers' matrix work.
+// The last 4 waves are producers: each turns 8 of every key block's 32 rows into the LDS
+// tiles and owns 32 columns of the state (Hf^T += (v Bt)^T X).  Every SIMD holds producer
+// and consumer waves, so that the producers' vector work overlaps the consumers' matrix work.
 // Both kinds pass the same barriers: one after each chunk section, one per key block.
-constexpr int kNC = 4;                                   // consumer waves
+//
+// Consumer waves: 4, or 8 at R = 4, Q = 64 (256 rows): there each consumer keeps two query
+// tiles, which fits 168 registers per lane, and the workgroup's 12 waves put three on each
+// SIMD (two consumers and a producer) to hide more of the latency of a wave's LDS reads,
+// fetches and barriers.
+template <int R, int Q>
+constexpr int n_consumers() { return (R == 4 && Q == 64) ? 8 : 4; }
+template <int R, int Q>
+constexpr int n_threads() { return 64 * (n_consumers<R, Q>() + kNP); }
 
-// Query tile k of consumer c: tiles are dealt in groups of 8, consumer c taking tile c
-// and tile 7 - c of each group (equal causal work per consumer).
-__host__ __device__ constexpr int ctile(int c, int k) { return 8 * (k >> 1) + ((k & 1) ? 7 - c : c); }
+// Query tile k of consumer c (NC consumers): tiles are dealt in groups of 2 NC, consumer c
+// taking tile c and tile 2 NC - 1 - c of each group (equal causal work per consumer).
+template <int NC>
+__host__ __device__ constexpr int ctile(int c, int k) {
+    return 2 * NC * (k >> 1) + ((k & 1) ? 2 * NC - 1 - c : c);
+}
 // Query tile t meets key blocks 0 .. t / 2 and reaches the diagonal in the last of them.  A
 // consumer's tiles end in strictly increasing blocks, so in any key block at most one of its
 // tiles is on the diagonal: the first active one, in the last block before it retires.
+template <int NC, int TPC>
 constexpr bool ctile_blocks_increase() {
-    for (int c = 0; c < 4; ++c)
-        for (int k = 0; k + 1 < 4; ++k)
-            if (ctile(c, k + 1) / 2 <= ctile(c, k) / 2) return false;
+    for (int c = 0; c < NC; ++c)
+        for (int k = 0; k + 1 < TPC; ++k)
+            if (ctile<NC>(c, k + 1) / 2 <= ctile<NC>(c, k) / 2) return false;
     return true;
 }
-static_assert(ctile_blocks_increase(), "one diagonal tile per key block and consumer");
+static_assert(ctile_blocks_increase<4, 4>() && ctile_blocks_increase<8, 2>(), "one diagonal tile per key block and consumer");
 
-// Chunks of 16 tokens at R = 4 (64 rows: the small-chunk MIMO schedule) fit two workgroups
-// per CU: at most 128 registers per lane (four waves per SIMD) and half the LDS.  The extra
-// waves hide the latencies that one workgroup's two waves per SIMD leave exposed.
+// Waves per SIMD the kernel is built for.  Chunks of 16 tokens at R = 4 (64 rows: the
+// small-chunk MIMO schedule) fit two workgroups per CU: at most 128 registers per lane (four
+// waves per SIMD) and half the LDS; the extra waves hide the latencies that one workgroup's
+// two waves per SIMD leave exposed.  R = 4, Q = 64 runs 12 waves (three per SIMD).
 template <int R, int Q>
-constexpr int waves_per_simd() { return (R == 4 && Q == 16) ? 4 : 2; }
+constexpr int waves_per_simd() { return (R == 4 && Q == 16) ? 4 : n_threads<R, Q>() / 256; }
 
 template <int R, int Q, int MODE>
-__global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_kernel(ScanArgs a) {
+__global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void scan_ws_kernel(ScanArgs a) {
+    constexpr int kNC = n_consumers<R, Q>();                // consumer waves
+    constexpr int kThreads = n_threads<R, Q>();
     constexpr int M = Q * R;                 // rows per chunk
     constexpr int NKB = M / kKB;             // key blocks per chunk
     constexpr int NT = M / 16;               // query tiles per chunk
     constexpr int TPC = NT / kNC;            // query tiles per consumer
+    constexpr int RPB = 32 / kNC;            // staged output rows a consumer stores per key block
+    static_assert(RPB * NKB == 16 * TPC, "a chunk's staged rows leave over its key blocks");
     constexpr int TPL = Q > 64 ? Q / 64 : 1; // tokens per lane of the scanning wave
     constexpr int KT = R >= 4 ? 1 : 4 / R;   // key tokens among a lane's 4 rows of a score tile
     constexpr bool kEarlyExp = KT == 1;      // decay exps ahead of the score MFMAs (registers allow)
     constexpr bool kFullMode = MODE == kFull;
     static_assert(TPC >= 1 && TPC <= 4 && NKB >= 2 && NKB % 2 == 0, "chunk shape");
     using LY = Layout<R, Q>;
-    static_assert(waves_per_simd<R, Q>() == 2 || LY::total <= 80 * 1024, "two workgroups per CU fit the LDS");
+    static_assert(waves_per_simd<R, Q>() != 4 || LY::total <= 80 * 1024, "two workgroups per CU fit the LDS");
     extern __shared__ __attribute__((aligned(16))) char smem[];
     float* sL2 = reinterpret_cast<float*>(smem + LY::l2);
     float* sG1 = reinterpret_cast<float*>(smem + LY::g1);
@@ -307,7 +325,7 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
     auto load_theta = [&](int cstart, float (&th)[THP][THU]) {
         int tt = tid;                                         // opaque: offsets formed here
         asm volatile("" : "+v"(tt));
-            tt &= kThreads - 1;                               // a thread index: non-negative
+            tt &= 1023;                                      // a thread index: non-negative
         const int th_t = tt / THG, th_i = (tt % THG) * THU;
         const int nt = __builtin_amdgcn_readfirstlane(min(max(T1 - cstart, 0), Q));
         const uint32_t nrec = nt > 0 ? (uint32_t)((nt - 1) * H * np + np) * 4u : 0u;
@@ -323,7 +341,7 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
     auto stage_theta = [&](const float (&th)[THP][THU]) {
         int tt = tid;
         asm volatile("" : "+v"(tt));
-            tt &= kThreads - 1;                               // a thread index: non-negative
+            tt &= 1023;                                      // a thread index: non-negative
         const int th_t = tt / THG, th_i = (tt % THG) * THU;
 #pragma unroll
         for (int pp = 0; pp < THP; ++pp) {
@@ -341,7 +359,7 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
             constexpr int TPT = Q / TPP;
             int tt = tid;                                     // opaque: offsets formed here
             asm volatile("" : "+v"(tt));
-            tt &= kThreads - 1;                               // a thread index: non-negative
+            tt &= 1023;                                      // a thread index: non-negative
             const int k = tt % TPP, i = tt / TPP;
             if (i < np) {
                 float inc[TPT];
@@ -372,12 +390,12 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
     // dt of token e, then lambda, then the rate input) and staged in LDS at its first key
     // block ahead of that block's row fetches, when they have long arrived; the wave that
     // scans them then reads LDS only and never waits on the row fetches.
-    constexpr int NSV = (3 * Q + 2 + kNC * 64 - 1) / (kNC * 64);
+    constexpr int NSV = (3 * Q + 2 + kNP * 64 - 1) / (kNP * 64);
     float rgS[NSV];
     auto load_scalars = [&](int cstart) {
 #pragma unroll
         for (int j = 0; j < NSV; ++j) {
-            const int e = tid - kNC * 64 + kNC * 64 * j;
+            const int e = tid - kNC * 64 + kNP * 64 * j;
             float v = 0.f;
             if (e < 2 * Q + 2) {
                 const int t = e <= Q ? e : e - (Q + 1);
@@ -393,7 +411,7 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
     auto stage_scalars = [&]() {
 #pragma unroll
         for (int j = 0; j < NSV; ++j) {
-            const int e = tid - kNC * 64 + kNC * 64 * j;
+            const int e = tid - kNC * 64 + kNP * 64 * j;
             if (e <= Q) sDt[e] = rgS[j];
             else if (e < 2 * Q + 2) sLm[e - (Q + 1)] = rgS[j];
             else if (e < 3 * Q + 2) sAr[e - (2 * Q + 2)] = rgS[j];
@@ -425,7 +443,7 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
             ln &= 63u;
 #pragma unroll
             for (int k = 0; k < TPC; ++k) {
-                const int qt = ctile(c, k);
+                const int qt = ctile<kNC>(c, k);
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt)
                     *reinterpret_cast<uint2*>(xs + (ln & 15u) * 144 + (16 * pt + 4 * (ln >> 4)) * 2) =
@@ -448,25 +466,29 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
             ln &= 63u;
 #pragma unroll
             for (int k = 0; k < TPC; ++k) {
-                const unsigned qt = ctile(c, k);
+                const unsigned qt = ctile<kNC>(c, k);
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt)
                     *reinterpret_cast<uint2*>(ys + (16 * qt + (ln & 15u)) * 144 + (16 * pt + 4 * (ln >> 4)) * 2) =
                         uint2{pack2(yacc[k][pt][0], yacc[k][pt][1]), pack2(yacc[k][pt][2], yacc[k][pt][3])};
             }
         };
-        // (Q <= 64) staged rows 16 qt + 8 i .. + 7 (a tile of this wave) to the outputs of the
-        // chunk at cst with nv valid tokens; rows of later tokens fall outside the record count
-        auto store_rows = [&](int cst, int nv, int qt, int i) {
+        // (Q <= 64) NR staged rows 16 qt + r0 .. + NR - 1 (of a tile of this wave; NR = 8 or
+        // 4, eight lanes a row) to the outputs of the chunk at cst with nv valid tokens; rows of
+        // later tokens fall outside the record count
+        auto store_rows = [&](int cst, int nv, int qt, int r0, auto nrc) {
+            constexpr unsigned NR = decltype(nrc)::value;
             const __amdgpu_buffer_rsrc_t ry = make_rsrc(static_cast<uint16_t*>(a.y) + ((tokbase + cst) * H + h) * R * kP,
                                                         (uint32_t)nv * xsb);
             unsigned ln = lane;                               // opaque: offsets formed here
             asm volatile("" : "+v"(ln));
             ln &= 63u;
-            const unsigned qi = 16 * (unsigned)qt + 8 * (unsigned)i + (ln >> 3);
-            const u32x4 v = *reinterpret_cast<const u32x4*>(ys + qi * 144 + (ln & 7u) * 16);
-            const unsigned t = qi / R, r = qi % R;
-            __builtin_amdgcn_raw_buffer_store_b128(v, ry, (int)(t * xsb + r * (kP * 2) + 16 * (ln & 7u)), 0, 0);
+            if (NR == 8 || ln < 8 * NR) {
+                const unsigned qi = 16 * (unsigned)qt + (unsigned)r0 + (ln >> 3);
+                const u32x4 v = *reinterpret_cast<const u32x4*>(ys + qi * 144 + (ln & 7u) * 16);
+                const unsigned t = qi / R, r = qi % R;
+                __builtin_amdgcn_raw_buffer_store_b128(v, ry, (int)(t * xsb + r * (kP * 2) + 16 * (ln & 7u)), 0, 0);
+            }
         };
         // raw C rows of tiles KB .. KE - 1 of the chunk at cst straight into the operand layout
         // (tile k, slice ks: row 16 qt + lane % 16, n = 32 ks + 8 (lane / 16) ...); rows of
@@ -480,7 +502,7 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
             ln &= 63u;
 #pragma unroll
             for (int k = KB; k < KE; ++k) {
-                const int qt = ctile(c, k);
+                const int qt = ctile<kNC>(c, k);
                 const unsigned qi = 16 * qt + (ln & 15u);
                 const unsigned t = qi / R, r = qi % R;
 #pragma unroll
@@ -521,7 +543,7 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
                 const int l16 = ln & 15, g4 = ln >> 4;
 #pragma unroll
                 for (int k = 0; k < TPC; ++k) {
-                    const int qi = 16 * ctile(c, k) + l16;
+                    const int qi = 16 * ctile<kNC>(c, k) + l16;
                     const int t = qi / R;
                     tq[k] = t;
                     l2q[k] = sL2[t];
@@ -637,7 +659,7 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
                 bf16x8 bop[TPC];
 #pragma unroll
                 for (int k = K0; k < TPC; ++k) {
-                    const bool diag = kDiag == 2 ? ctile(c, k) <= ka + 1 : (kDiag == 1 && k == K0);   // uniform
+                    const bool diag = kDiag == 2 ? ctile<kNC>(c, k) <= ka + 1 : (kDiag == 1 && k == K0);   // uniform
                     float wgt[2][KT];
 #pragma unroll
                     for (int ab = 0; ab < 2; ++ab) {
@@ -667,18 +689,19 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
 #pragma unroll
                     for (int k = K0; k < TPC; ++k) yacc[k][pt] = mfma(xo[pt], bop[k], yacc[k][pt]);
             };
-            // per key block (Q <= 64): rows 8 (J % 2) .. + 7 of this wave's tile J / 2 of the
-            // previous chunk's staged outputs
+            // per key block (Q <= 64): rows RPB J .. RPB J + RPB - 1 of this wave's staged outputs
+            // of the previous chunk (tile RPB J / 16)
             const bool have_prev = kFullMode && c0 > T0;
             auto block_end = [&](int J) {
                 if constexpr (LY::kYStage)
-                    if (have_prev) store_rows(c0 - Q, Q, ctile(c, J >> 1), J & 1);
+                    if (have_prev)
+                        store_rows(c0 - Q, Q, ctile<kNC>(c, RPB * J / 16), RPB * J % 16, std::integral_constant<unsigned, RPB>{});
                 __syncthreads();
             };
             int Jb = 0;
             auto phase = [&](auto mc) {
                 constexpr int K0 = decltype(mc)::value;
-                const int Je = K0 < TPC ? min(NKB, ctile(c, K0 < TPC ? K0 : 0) / 2 + 1) : NKB;
+                const int Je = K0 < TPC ? min(NKB, ctile<kNC>(c, K0 < TPC ? K0 : 0) / 2 + 1) : NKB;
                 if constexpr (TPC > 1 && K0 == TPC - 1)
                     if (kFullMode && c0 + Q < T1)
                         load_c(c0 + Q, std::integral_constant<int, 0>{}, std::integral_constant<int, TPC - 1>{});
@@ -720,7 +743,7 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
 #pragma unroll
                 for (int k = 0; k < TPC; ++k)
 #pragma unroll
-                    for (int i = 0; i < 2; ++i) store_rows(cst, nv, ctile(c, k), i);
+                    for (int i = 0; i < 2; ++i) store_rows(cst, nv, ctile<kNC>(c, k), 8 * i, std::integral_constant<unsigned, 8>{});
             } else {
                 store_y(cst, nv);
             }
@@ -792,7 +815,7 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
         // raw key rows of block gb of the segment, through buffer loads bounded at the
         // segment end (rows of later tokens read zero)
         // prefetch ring: slot J % DP holds block J's raw rows, fetched DP blocks ahead
-        constexpr int DP = NKB >= 4 ? 4 : 2;
+        constexpr int DP = (NKB >= 4 && kNC == 4) ? 4 : 2;      // 12 waves: 168 registers
         static_assert(NKB % DP == 0, "whole ring groups per chunk");
         uint2 rgB[DP][4];
         uint32_t rgX[DP][8];
@@ -888,11 +911,16 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
             load_scalars(c0 + Q);
             // wave 4 scans the log-decays from the staged inputs and tables the per-token scalars
             if (pw == 0) {
+                // lane index made opaque here: the table addresses are formed per chunk rather
+                // than kept live (or spilled) across the chunk loop
+                int lns = lane;
+                asm volatile("" : "+v"(lns));
+                lns &= 63;
                 float la[TPL], gm[TPL], dl[TPL];
                 float lsum = 0.f;
 #pragma unroll
                 for (int k = 0; k < TPL; ++k) {
-                    const int t = lane * TPL + k;
+                    const int t = lns * TPL + k;
                     const bool in = t < Q;
                     const float dt = in ? sDt[t] : 0.f, lm = in ? sLm[t] : 0.f;
                     float rate = -ah;
@@ -911,7 +939,7 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<R, Q>())) void scan_ws_ke
                 const float dnext = sDt[Q] * (1.f - sLm[Q]);
 #pragma unroll
                 for (int k = 0; k < TPL; ++k) {
-                    const int t = lane * TPL + k;
+                    const int t = lns * TPL + k;
                     const float dn = (k + 1 < TPL) ? dl[k + 1] : ((t + 1 < Q) ? nx : dnext);
                     if (t < Q) {
                         const float l2t = (excl + la[k]) * kLog2e;
@@ -1109,7 +1137,7 @@ hipError_t launch_rq(const ScanArgs& a, hipStream_t st) {
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_ws_kernel<R, Q, kSummary>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((scan_ws_kernel<R, Q, kSummary>), dim3(nblk), dim3(kThreads), lds, st, a);
+        hipLaunchKernelGGL((scan_ws_kernel<R, Q, kSummary>), dim3(nblk), dim3(n_threads<R, Q>()), lds, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL(carry_pass_kernel, dim3((kP * kN / 2 + 255) / 256, a.b * a.H), dim3(256), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1117,7 +1145,7 @@ hipError_t launch_rq(const ScanArgs& a, hipStream_t st) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_ws_kernel<R, Q, kFull>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_ws_kernel<R, Q, kFull>), dim3(nblk), dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((scan_ws_kernel<R, Q, kFull>), dim3(nblk), dim3(n_threads<R, Q>()), lds, st, a);
     return hipGetLastError();
 }
 
