@@ -152,3 +152,55 @@ def make_small_case(seed, *, batch=1, seqlen=16, nheads=2, ngroups=None, headdim
     if dt_scale != 1.0:
         d["dt"] = (d["dt"] * np.float32(dt_scale)).astype(np.float32)
     return cfg, d
+
+
+_BLOCK_ORDER = ("z", "x", "B_raw", "C_raw", "dt_raw", "A_raw", "lam_raw", "th_raw",
+                "dt_bias", "B_gain", "C_gain", "lift", "comb", "D", "B_bias", "C_bias", "init")
+
+
+def make_block_inputs(cfg: Config, seed=None, *, batch=None, seqlen=None, init=True):
+    """Inputs of one layer call (the steps around the scan), float32 arrays of
+    storage-exact values.
+
+    Raw projections: z, x [b,L,H,P] ~ N(0,1); B_raw, C_raw [b,L,G,R,N] ~ 2 N(0,1)
+    (not normalised: the layer normalises them); dt_raw, A_raw, lam_raw [b,L,H] ~
+    N(0,1) (dt_raw with std 0.5); th_raw [b,L,H,npairs] ~ N(0,1).  Parameters:
+    dt_bias [H] ~ N(-3, 1) (steps of a few hundredths); B_gain,
+    C_gain [N] ~ 1 + N(0, 0.1); lift, comb [H,R,P] ~ 1 + N(0, 0.1) (comb divided
+    by R); D [H] ~ 1 + N(0, 0.1); B_bias, C_bias [H,R,N] ~ 1 + N(0, 0.1) (the
+    biases start at ones).  init: a scan carry (x_prev is the lifted x) or None.
+    The io tensors (z, x, B_raw, C_raw, and the carry's B_prev, x_prev) are
+    rounded to the config's io dtype.
+    """
+    b = cfg.batch if batch is None else batch
+    L = cfg.seqlen if seqlen is None else seqlen
+    H, G, P, N, R, NP = cfg.nheads, cfg.ngroups, cfg.headdim, cfg.dstate, cfg.rank, cfg.npairs
+    ss = np.random.SeedSequence(cfg.seed if seed is None else seed, spawn_key=(11,))
+    g = {k: np.random.Generator(np.random.PCG64(c)) for k, c in zip(_BLOCK_ORDER, ss.spawn(len(_BLOCK_ORDER)))}
+    io = cfg.io_dtype
+    out = {"z": _round_io(_normal(g["z"], (b, L, H, P)), io),
+           "x": _round_io(_normal(g["x"], (b, L, H, P)), io),
+           "B_raw": _round_io(_normal(g["B_raw"], (b, L, G, R, N), 2.0), io),
+           "C_raw": _round_io(_normal(g["C_raw"], (b, L, G, R, N), 2.0), io),
+           "dt_raw": _normal(g["dt_raw"], (b, L, H), 0.5),
+           "A_raw": _normal(g["A_raw"], (b, L, H)),
+           "lam_raw": _normal(g["lam_raw"], (b, L, H)),
+           "th_raw": _normal(g["th_raw"], (b, L, H, NP)) if NP > 0 else None}
+    p = {"dt_bias": _normal(g["dt_bias"], (H,), 1.0) - np.float32(3.0),
+         "B_gain": (1.0 + _normal(g["B_gain"], (N,), 0.1)).astype(np.float32),
+         "C_gain": (1.0 + _normal(g["C_gain"], (N,), 0.1)).astype(np.float32),
+         "lift": (1.0 + _normal(g["lift"], (H, R, P), 0.1)).astype(np.float32),
+         "comb": ((1.0 + _normal(g["comb"], (H, R, P), 0.1)) / R).astype(np.float32),
+         "D": (1.0 + _normal(g["D"], (H,), 0.1)).astype(np.float32),
+         "B_bias": (1.0 + _normal(g["B_bias"], (H, R, N), 0.1)).astype(np.float32),
+         "C_bias": (1.0 + _normal(g["C_bias"], (H, R, N), 0.1)).astype(np.float32)}
+    out["params"] = p
+    if init:
+        gi = g["init"]
+        out["init"] = {"h": _round_io(_normal(gi, (b, H, P, N), 0.1), cfg.state_dtype),
+                       "phi": gi.uniform(0.0, 2 * math.pi, size=(b, H, NP)).astype(np.float32),
+                       "B_prev": _round_io(_normal(gi, (b, H, R, N)), io),
+                       "x_prev": _round_io(_normal(gi, (b, H, R, P)), io)}
+    else:
+        out["init"] = None
+    return out

@@ -9,6 +9,9 @@ meet only through the seeded inputs of ``m3inputs``.
                forms, one decode step, and an op-counting decode step.
 - ``ref_cpu``  plain C fp64 sequential recurrence (OpenMP over streams).
 - ``model``    the pages' byte / operation accounting of a decode step.
+- ``block``    the layer steps around the scan (activations, BCNorm, x lift,
+               readout recombination, D skip, gate), whole sequence and one
+               decode step, on top of ``ref``.
 
 Parity status of every function is pinned by ``tests/test_oracle.py``; no
 function here is "parity unpinned".

@@ -228,6 +228,21 @@ def test_scan_dynamic_rate(m3, case):
     _compare(y, fin, yr, fr, io, what="dyn-rate")
 
 
+@pytest.mark.parametrize("Q", [16, 64])
+@pytest.mark.parametrize("dt_scale", [40.0, 1e-3])
+def test_scan_extreme_decay(m3, Q, dt_scale):
+    """Steps 40x the workload law (per-token log-decays down to about -1e3, so a
+    chunk's decay underflows fp32) and 1e-3x (decays within 1e-3 of one): the
+    weights are exps of non-positive log-decay differences, so neither end
+    overflows or loses the diagonal terms."""
+    cfg, d = make_small_case(4200 + Q, batch=2, seqlen=150, nheads=2, ngroups=1, headdim=64, dstate=128, rank=4,
+                             npairs=32, chunk=Q, io_dtype="bf16", rms_bc=True, init_full=True, dt_scale=dt_scale)
+    yr, fr = ref_cpu.scan(d)
+    y, fin = _run_scan(m3, d, cfg)
+    assert torch.isfinite(y.float()).all() and torch.isfinite(fin["h"]).all()
+    _compare(y, fin, yr, fr, "bf16", what="dt x %g" % dt_scale)
+
+
 def test_scan_dynamic_rate_floor(m3):
     """Very negative rate inputs hit the -1e-4 floor: long memory, through the
     MFMA route, against the oracle."""
