@@ -154,6 +154,67 @@ m3_status m3_decode_step(const m3_desc* d,
                          const float* A_log, const float* B_bias, const float* C_bias,
                          const m3_carry* carry, void* y, m3_stream_t stream);
 
+/* ---- The layer steps on either side of the scan ------------------------------------
+ * "Mamba-3: Improved Sequence Modeling using State Space Principles": the decode
+ * listing of section "Computing the rotation as a data-dependent RoPE", section
+ * "MIMO: a rank-4 state update for the same state size" (x keeps its P-wide
+ * projection, lifted into R copies by a learned data-independent vector) and section
+ * "The Mamba-3 block, layer by layer" (BCNorm; the bias after the norm):
+ *   dt = softplus(dt_raw + dt_bias[h]),  lam = sigmoid(lam_raw),
+ *   theta = pi tanh(th_raw)                        (each token adds dt theta to phi)
+ *   B = rms_norm(B_raw) B_gain,  C = rms_norm(C_raw) C_gain    (over the N axis)
+ *       then + B_bias[h], C_bias[h] and the rotation, inside the scan
+ *   x_r = lift[h, r] x                             (elementwise over P, r < R)
+ *   the scan (m3_scan_fwd / m3_decode_step, with the descriptor's rate law) -> y_r
+ *   out = (sum_r comb[h, r] y_r + D[h] x) silu(z)
+ * with rms_norm(v) = v / sqrt(mean(v^2) + eps).  The pages do not say how the R
+ * readouts recombine; comb is the mirror of the lift.  The steps before and after
+ * the scan run as element-map kernels around it; the scan's inputs and readouts pass
+ * through the workspace. */
+typedef struct {
+    const float* dt_bias;  /* [H], or NULL for 0 */
+    const float* B_gain;   /* [N] RMSNorm gain of B, or NULL for 1 */
+    const float* C_gain;   /* [N] RMSNorm gain of C, or NULL for 1 */
+    const float* B_bias;   /* [H, R, N], or NULL: added after the norm, before the turn */
+    const float* C_bias;   /* [H, R, N], or NULL */
+    const float* lift;     /* [H, R, P], required */
+    const float* comb;     /* [H, R, P], required */
+    const float* D;        /* [H], or NULL for no skip */
+    float eps;             /* RMSNorm epsilon, > 0 */
+} m3_block_params;
+
+/* Bytes of device workspace that m3_block_fwd (decode = 0) or m3_block_decode_step
+ * (decode = 1) needs for *d: the scan's inputs and readouts and the scan's own
+ * workspace.  Returns M3_ERR_INVALID_ARG for a NULL argument or a bad descriptor. */
+m3_status m3_block_workspace_size(const m3_desc* d, int decode, size_t* bytes);
+
+/* The layer over whole sequences.
+ *   z, x           [b, L, H, P] io
+ *   B_raw, C_raw   [b, L, G, R, N] io, before the norm
+ *   dt_raw, lam_raw [b, L, H] f32;  th_raw [b, L, H, np] f32 (NULL iff np == 0)
+ *   A              as m3_scan_fwd's A_log argument: [H] (M3_RATE_STATIC) or the
+ *                  per-token rate input [b, L, H] (M3_RATE_HEAVY_TAIL)
+ *   init, final_   scan carries as for m3_scan_fwd; x_prev holds the lifted x
+ *   out            [b, L, H, P] io (must not overlap an input or the workspace)
+ *   workspace      at least m3_block_workspace_size(d, 0, .) bytes, 16-byte aligned;
+ *                  its contents on entry do not matter.
+ * Errors as m3_scan_fwd; nothing is launched when an argument check fails. */
+m3_status m3_block_fwd(const m3_desc* d, const m3_block_params* p,
+                       const void* z, const void* x, const void* B_raw, const void* C_raw,
+                       const float* dt_raw, const float* A, const float* lam_raw, const float* th_raw,
+                       const m3_carry* init, void* out, const m3_carry* final_,
+                       void* workspace, size_t workspace_bytes, m3_stream_t stream);
+
+/* One token of the layer for every (batch, head), the carry updated in place.
+ * Shapes as m3_block_fwd without the L axis: z, x [b, H, P]; B_raw, C_raw
+ * [b, G, R, N]; dt_raw, lam_raw [b, H]; th_raw [b, H, np]; A [H] or [b, H];
+ * out [b, H, P]; workspace at least m3_block_workspace_size(d, 1, .) bytes. */
+m3_status m3_block_decode_step(const m3_desc* d, const m3_block_params* p,
+                               const void* z, const void* x, const void* B_raw, const void* C_raw,
+                               const float* dt_raw, const float* A, const float* lam_raw, const float* th_raw,
+                               const m3_carry* carry, void* out, void* workspace, size_t workspace_bytes,
+                               m3_stream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* m3_status_string(m3_status s);
 

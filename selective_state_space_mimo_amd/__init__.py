@@ -195,3 +195,119 @@ def decode_step(x, B, C, dt, lam, theta, A_log, B_bias, C_bias, carry, *, y=None
                             ctypes.byref(c), _ptr(y, dev, io, "y"), _stream(dev))
     _check(st, "m3_decode_step")
     return y
+
+
+# ---------------------------------------------------------------------------
+# the layer steps around the scan (m3_block_fwd, m3_block_decode_step)
+# ---------------------------------------------------------------------------
+class BlockParams(ctypes.Structure):
+    _fields_ = [("dt_bias", ctypes.c_void_p), ("B_gain", ctypes.c_void_p), ("C_gain", ctypes.c_void_p),
+                ("B_bias", ctypes.c_void_p), ("C_bias", ctypes.c_void_p), ("lift", ctypes.c_void_p),
+                ("comb", ctypes.c_void_p), ("D", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
+lib.m3_block_workspace_size.argtypes = [ctypes.POINTER(Desc), ctypes.c_int, ctypes.POINTER(_sz)]
+lib.m3_block_workspace_size.restype = ctypes.c_int
+lib.m3_block_fwd.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(BlockParams)] + [_vp] * 8 + [
+    ctypes.POINTER(Carry), _vp, ctypes.POINTER(Carry), _vp, _sz, _vp]
+lib.m3_block_fwd.restype = ctypes.c_int
+lib.m3_block_decode_step.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(BlockParams)] + [_vp] * 8 + [
+    ctypes.POINTER(Carry), _vp, _vp, _sz, _vp]
+lib.m3_block_decode_step.restype = ctypes.c_int
+__all__ += ["block_fwd", "block_decode_step", "block_workspace_size", "BlockParams"]
+
+
+def _block_params(p, dev):
+    f = lambda k: _ptr(p.get(k), dev, torch.float32, k)  # noqa: E731
+    return BlockParams(f("dt_bias"), f("B_gain"), f("C_gain"), f("B_bias"), f("C_bias"), f("lift"), f("comb"),
+                       f("D"), float(p.get("eps", 1e-6)))
+
+
+def _block_desc(x, B_raw, R, th_raw, *, decode, chunk=64, state_dtype=None, nsegments=0, rate_law):
+    if decode:
+        b, H, P = x.shape
+        G, N = B_raw.shape[1], B_raw.shape[3]
+        L = 1
+    else:
+        b, L, H, P = x.shape
+        G, N = B_raw.shape[2], B_raw.shape[4]
+    npairs = 0 if th_raw is None else th_raw.shape[-1]
+    sd = _dt(x) if state_dtype is None else (M3_BF16 if state_dtype == torch.bfloat16 else M3_F32)
+    return Desc(b, L, H, G, P, N, R, npairs, chunk, _dt(x), sd, nsegments, rate_law)
+
+
+def block_workspace_size(desc, decode=False):
+    n = _sz(0)
+    _check(lib.m3_block_workspace_size(ctypes.byref(desc), int(bool(decode)), ctypes.byref(n)),
+           "m3_block_workspace_size")
+    return n.value
+
+
+def block_fwd(z, x, B_raw, C_raw, dt_raw, A, lam_raw, th_raw, params, init=None, *, chunk=64,
+              state_dtype=torch.float32, nsegments=0, rate_law=M3_RATE_HEAVY_TAIL, out=None, final=True,
+              workspace=None):
+    """The layer steps around the scan over whole sequences (``m3_block_fwd``).
+
+    z, x [b,L,H,P]; B_raw, C_raw [b,L,G,R,N] (bf16 or f32, same dtype); dt_raw,
+    lam_raw [b,L,H] f32; A: the per-token rate input [b,L,H] (heavy-tail law) or
+    A_log [H] with rate_law=M3_RATE_STATIC; th_raw [b,L,H,np] or None.  params:
+    dict of f32 tensors lift, comb [H,R,P] (required), dt_bias [H], B_gain, C_gain
+    [N], B_bias, C_bias [H,R,N], D [H] (each optional) and eps (float).
+    Returns (out [b,L,H,P], final carry or None); the carry's x_prev holds the
+    lifted x [b,H,R,P].
+    """
+    dev = x.device
+    io = x.dtype
+    R = B_raw.shape[3]
+    desc = _block_desc(x, B_raw, R, th_raw, decode=False, chunk=chunk, state_dtype=state_dtype,
+                       nsegments=nsegments, rate_law=rate_law)
+    b, L, H, P = x.shape
+    N = B_raw.shape[4]
+    if out is None:
+        out = torch.empty_like(x)
+    fin = None
+    if final is True:
+        fin = new_carry(b, H, P, N, R, desc.npairs, io, state_dtype, dev)
+    elif isinstance(final, dict):
+        fin = final
+    ws_bytes = block_workspace_size(desc)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    bp = _block_params(params, dev)
+    ci, cf = _carry(init, dev, io, state_dtype), _carry(fin, dev, io, state_dtype)
+    st = lib.m3_block_fwd(ctypes.byref(desc), ctypes.byref(bp), _ptr(z, dev, io, "z"), _ptr(x, dev, io, "x"),
+                          _ptr(B_raw, dev, io, "B_raw"), _ptr(C_raw, dev, io, "C_raw"),
+                          _ptr(dt_raw, dev, torch.float32, "dt_raw"), _ptr(A, dev, torch.float32, "A"),
+                          _ptr(lam_raw, dev, torch.float32, "lam_raw"), _ptr(th_raw, dev, torch.float32, "th_raw"),
+                          ctypes.byref(ci) if ci is not None else None, _ptr(out, dev, io, "out"),
+                          ctypes.byref(cf) if cf is not None else None,
+                          _ptr(workspace, dev, None, "workspace") if ws_bytes else None, ws_bytes, _stream(dev))
+    _check(st, "m3_block_fwd")
+    return out, fin
+
+
+def block_decode_step(z, x, B_raw, C_raw, dt_raw, A, lam_raw, th_raw, params, carry, *,
+                      rate_law=M3_RATE_HEAVY_TAIL, out=None, workspace=None):
+    """One token of the layer (``m3_block_decode_step``); ``carry`` is updated in
+    place.  z, x [b,H,P]; B_raw, C_raw [b,G,R,N]; dt_raw, lam_raw [b,H]; A [b,H]
+    (or A_log [H] with rate_law=M3_RATE_STATIC); th_raw [b,H,np] or None.
+    Returns out [b,H,P]."""
+    dev = x.device
+    io = x.dtype
+    R = B_raw.shape[2]
+    desc = _block_desc(x, B_raw, R, th_raw, decode=True, state_dtype=carry["h"].dtype, rate_law=rate_law)
+    if out is None:
+        out = torch.empty_like(x)
+    ws_bytes = block_workspace_size(desc, decode=True)
+    if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    bp = _block_params(params, dev)
+    c = _carry(carry, dev, io, carry["h"].dtype)
+    st = lib.m3_block_decode_step(ctypes.byref(desc), ctypes.byref(bp), _ptr(z, dev, io, "z"), _ptr(x, dev, io, "x"),
+                                  _ptr(B_raw, dev, io, "B_raw"), _ptr(C_raw, dev, io, "C_raw"),
+                                  _ptr(dt_raw, dev, torch.float32, "dt_raw"), _ptr(A, dev, torch.float32, "A"),
+                                  _ptr(lam_raw, dev, torch.float32, "lam_raw"),
+                                  _ptr(th_raw, dev, torch.float32, "th_raw"), ctypes.byref(c), _ptr(out, dev, io, "out"),
+                                  _ptr(workspace, dev, None, "workspace"), ws_bytes, _stream(dev))
+    _check(st, "m3_block_decode_step")
+    return out

@@ -127,6 +127,83 @@ hipError_t copy_or_zero(const void* src, void* dst, size_t bytes, hipStream_t s)
     return hipGetLastError();
 }
 
+// Workspace of the layer entry points: the scan's inputs (lifted x, normalised B
+// and C, dt, lambda, angular rates), its readouts and its own workspace, each part
+// starting on a 256-byte boundary.
+struct BlockWs {
+    size_t xl, bn, cn, dt, lam, th, y, scan, scan_bytes, total;
+};
+BlockWs block_ws(const m3_desc* d, int decode) {
+    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    const size_t L = decode ? 1 : (size_t)d->seqlen;
+    const size_t b = d->batch, H = d->nheads, G = d->ngroups, P = d->headdim, N = d->dstate, R = d->rank,
+                 np = d->npairs, io = esize(d->io_dtype);
+    BlockWs w{};
+    size_t o = 0;
+    w.xl = o;  o += up(b * L * H * R * P * io);
+    w.bn = o;  o += up(b * L * G * R * N * io);
+    w.cn = o;  o += up(b * L * G * R * N * io);
+    w.dt = o;  o += up(b * L * H * 4);
+    w.lam = o; o += up(b * L * H * 4);
+    w.th = o;  o += up(b * L * H * np * 4);
+    w.y = o;   o += up(b * L * H * R * P * io);
+    w.scan = o;
+    w.scan_bytes = 0;
+    if (!decode && L > 0) {
+        ScanArgs a = make_scan_args(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                    nullptr, nullptr, nullptr, nullptr);
+        if (a.io_bf16 && scan_mfma_supported(a)) w.scan_bytes = scan_mfma_workspace_bytes(a);
+    }
+    w.total = o + w.scan_bytes;
+    return w;
+}
+
+// Checks shared by the two layer entry points (pointers, alignment, parameters,
+// workspace size, overlaps of the output and the workspace with the inputs).
+m3_status check_block(const m3_desc* d, const m3_block_params* p, int decode, const void* z, const void* x,
+                      const void* Braw, const void* Craw, const float* dt_raw, const float* A,
+                      const float* lam_raw, const float* th_raw, const void* out, const void* ws, size_t wsb) {
+    if (!p || !p->lift || !p->comb || !(p->eps > 0.f) || !(p->eps < 1e30f)) return M3_ERR_INVALID_ARG;
+    if (!z || !x || !Braw || !Craw || !dt_raw || !A || !lam_raw || !out) return M3_ERR_INVALID_ARG;
+    if (d->npairs > 0 && !th_raw) return M3_ERR_INVALID_ARG;
+    const void* ptrs[] = {z, x, Braw, Craw, dt_raw, A, lam_raw, d->npairs ? th_raw : nullptr, out, ws,
+                          p->dt_bias, p->B_gain, p->C_gain, p->B_bias, p->C_bias, p->lift, p->comb, p->D};
+    for (const void* q : ptrs)
+        if (misaligned(q)) return M3_ERR_ALIGNMENT;
+    const BlockWs w = block_ws(d, decode);
+    if (w.total > 0 && (!ws || wsb < w.total)) return M3_ERR_INVALID_ARG;
+    const Sizes s = sizes(d, decode ? 1 : d->seqlen);
+    const size_t io = esize(d->io_dtype);
+    const size_t zx = s.x / d->rank;                      // [b, L, H, P]
+    (void)io;
+    const Range ro = rng(out, zx), rw = rng(ws, w.total);
+    const Range ins[] = {rng(z, zx), rng(x, zx), rng(Braw, s.bc), rng(Craw, s.bc), rng(dt_raw, s.tok), rng(A, s.alog),
+                         rng(lam_raw, s.tok), rng(d->npairs ? th_raw : nullptr, d->npairs ? s.theta : 0)};
+    for (const Range& r : ins)
+        if (overlap(ro, r) || overlap(rw, r)) return M3_ERR_INVALID_ARG;
+    if (overlap(ro, rw)) return M3_ERR_INVALID_ARG;
+    return M3_OK;
+}
+
+BlockArgs make_block_args(const m3_desc* d, const m3_block_params* p, int L, const void* z, const void* x,
+                          const void* Braw, const void* Craw, const float* dt_raw, const float* lam_raw,
+                          const float* th_raw, void* out, void* ws, const BlockWs& w) {
+    BlockArgs a{};
+    a.b = d->batch; a.L = L; a.H = d->nheads; a.G = d->ngroups; a.P = d->headdim; a.N = d->dstate;
+    a.R = d->rank; a.np = d->npairs; a.io_bf16 = d->io_dtype == M3_BF16;
+    a.z = z; a.x = x; a.Braw = Braw; a.Craw = Craw; a.dt_raw = dt_raw; a.lam_raw = lam_raw;
+    a.th_raw = d->npairs ? th_raw : nullptr;
+    a.dt_bias = p->dt_bias; a.Bg = p->B_gain; a.Cg = p->C_gain; a.lift = p->lift; a.comb = p->comb; a.D = p->D;
+    a.eps = p->eps;
+    char* base = static_cast<char*>(ws);
+    a.xl = base + w.xl; a.Bn = base + w.bn; a.Cn = base + w.cn;
+    a.dt = reinterpret_cast<float*>(base + w.dt); a.lam = reinterpret_cast<float*>(base + w.lam);
+    a.th = reinterpret_cast<float*>(base + w.th);
+    a.y = base + w.y;
+    a.out = out;
+    return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -268,6 +345,59 @@ m3_status m3_decode_step(const m3_desc* d, const void* x, const void* B, const v
         e = launch_decode_generic(a, reinterpret_cast<hipStream_t>(stream));
     }
     return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
+m3_status m3_block_workspace_size(const m3_desc* d, int decode, size_t* bytes) {
+    if (!bytes) return M3_ERR_INVALID_ARG;
+    m3_status st = check_desc(d, !decode);
+    if (st != M3_OK) return st;
+    *bytes = block_ws(d, decode).total;
+    return M3_OK;
+}
+
+m3_status m3_block_fwd(const m3_desc* d, const m3_block_params* p, const void* z, const void* x,
+                       const void* B_raw, const void* C_raw, const float* dt_raw, const float* A,
+                       const float* lam_raw, const float* th_raw, const m3_carry* init, void* out,
+                       const m3_carry* final_, void* workspace, size_t workspace_bytes, m3_stream_t stream) {
+    m3_status st = check_desc(d, true);
+    if (st != M3_OK) return st;
+    if (d->seqlen == 0)      // nothing but the carry copy
+        return m3_scan_fwd(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                           init, nullptr, final_, nullptr, 0, stream);
+    if ((st = check_block(d, p, 0, z, x, B_raw, C_raw, dt_raw, A, lam_raw, th_raw, out, workspace,
+                          workspace_bytes)) != M3_OK)
+        return st;
+    const BlockWs w = block_ws(d, 0);
+    const BlockArgs a = make_block_args(d, p, d->seqlen, z, x, B_raw, C_raw, dt_raw, lam_raw, th_raw, out,
+                                        workspace, w);
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (launch_block_prologue(a, hs) != hipSuccess) return M3_ERR_HIP;
+    char* base = static_cast<char*>(workspace);
+    st = m3_scan_fwd(d, a.xl, a.Bn, a.Cn, a.dt, a.lam, d->npairs ? a.th : nullptr, A, p->B_bias, p->C_bias, init,
+                     base + w.y, final_, w.scan_bytes ? base + w.scan : nullptr, w.scan_bytes, stream);
+    if (st != M3_OK) return st;
+    return launch_block_epilogue(a, hs) == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
+m3_status m3_block_decode_step(const m3_desc* d, const m3_block_params* p, const void* z, const void* x,
+                               const void* B_raw, const void* C_raw, const float* dt_raw, const float* A,
+                               const float* lam_raw, const float* th_raw, const m3_carry* carry, void* out,
+                               void* workspace, size_t workspace_bytes, m3_stream_t stream) {
+    m3_status st = check_desc(d, false);
+    if (st != M3_OK) return st;
+    if (!carry) return M3_ERR_INVALID_ARG;
+    if ((st = check_block(d, p, 1, z, x, B_raw, C_raw, dt_raw, A, lam_raw, th_raw, out, workspace,
+                          workspace_bytes)) != M3_OK)
+        return st;
+    const BlockWs w = block_ws(d, 1);
+    const BlockArgs a = make_block_args(d, p, 1, z, x, B_raw, C_raw, dt_raw, lam_raw, th_raw, out, workspace, w);
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (launch_block_prologue(a, hs) != hipSuccess) return M3_ERR_HIP;
+    char* base = static_cast<char*>(workspace);
+    st = m3_decode_step(d, a.xl, a.Bn, a.Cn, a.dt, a.lam, d->npairs ? a.th : nullptr, A, p->B_bias, p->C_bias,
+                        carry, base + w.y, stream);
+    if (st != M3_OK) return st;
+    return launch_block_epilogue(a, hs) == hipSuccess ? M3_OK : M3_ERR_HIP;
 }
 
 }  // extern "C"

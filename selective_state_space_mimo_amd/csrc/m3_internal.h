@@ -46,7 +46,25 @@ struct DecodeArgs {
     void* y;
 };
 
+// The layer steps around the scan (block.hip): raw projections and parameters in,
+// the scan's inputs (lifted x, normalised B and C, dt, lambda, angular rates) out
+// (prologue); the scan's readouts in, the gated layer output out (epilogue).
+struct BlockArgs {
+    int b, L, H, G, P, N, R, np;
+    int io_bf16;
+    const void* z; const void* x; const void* Braw; const void* Craw;
+    const float* dt_raw; const float* lam_raw; const float* th_raw;
+    const float* dt_bias; const float* Bg; const float* Cg;
+    const float* lift; const float* comb; const float* D;
+    float eps;
+    void* xl; void* Bn; void* Cn; float* dt; float* lam; float* th;   // prologue outputs
+    const void* y;                                                    // scan readouts [.., R, P]
+    void* out;                                                        // layer output [.., P]
+};
+
 // ---- host-side launchers (return hipSuccess or the launch error) ----------
+hipError_t launch_block_prologue(const BlockArgs& a, hipStream_t s);
+hipError_t launch_block_epilogue(const BlockArgs& a, hipStream_t s);
 hipError_t launch_scan_generic(const ScanArgs& a, hipStream_t s);
 size_t scan_generic_lds_bytes(int P, int N, int R, int np, int qg);
 int scan_generic_chunk(int P, int N, int R, int np, int Q);

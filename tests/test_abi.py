@@ -103,3 +103,37 @@ def test_null_misaligned_and_aliased_pointers(m3):
     assert m3.lib.m3_decode_step(ctypes.byref(desc), FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000,
                                  FAKE + 0x400000, FAKE + 0x500000, FAKE + 0x600000, None, None, ctypes.byref(c2),
                                  FAKE + 0x700000, None) == 1
+
+
+def _block(m3, d, p=None, ws_bytes=None, **kw):
+    a = dict(z=FAKE, x=FAKE + 0x100000, B=FAKE + 0x200000, C=FAKE + 0x300000, dt=FAKE + 0x400000,
+             A=FAKE + 0x500000, lam=FAKE + 0x600000, th=FAKE + 0x680000, out=FAKE + 0x700000, ws=FAKE + 0x1000000)
+    a.update(kw)
+    if p is None:
+        p = m3.BlockParams(None, None, None, None, None, FAKE + 0x900000, FAKE + 0x940000, None, 1e-6)
+    n = ctypes.c_size_t(0)
+    assert m3.lib.m3_block_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == 0
+    return m3.lib.m3_block_fwd(ctypes.byref(d), ctypes.byref(p), a["z"], a["x"], a["B"], a["C"], a["dt"], a["A"],
+                               a["lam"], a["th"], None, a["out"], None, a["ws"],
+                               n.value if ws_bytes is None else ws_bytes, None)
+
+
+def test_block_entry_points_reject_bad_arguments(m3):
+    """The layer entry points check parameters, pointers, alignment, the
+    workspace size and overlaps before launching anything."""
+    d = _desc(m3, rate_law=m3.M3_RATE_HEAVY_TAIL)
+    n = ctypes.c_size_t(0)
+    assert m3.lib.m3_block_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == 0 and n.value > 0
+    n1 = ctypes.c_size_t(0)
+    assert m3.lib.m3_block_workspace_size(ctypes.byref(d), 1, ctypes.byref(n1)) == 0 and 0 < n1.value < n.value
+    assert m3.lib.m3_block_workspace_size(None, 0, ctypes.byref(n)) == 1
+    no_lift = m3.BlockParams(None, None, None, None, None, None, FAKE + 0x940000, None, 1e-6)
+    assert _block(m3, d, p=no_lift) == 1
+    zero_eps = m3.BlockParams(None, None, None, None, None, FAKE + 0x900000, FAKE + 0x940000, None, 0.0)
+    assert _block(m3, d, p=zero_eps) == 1
+    assert _block(m3, d, z=None) == 1
+    assert _block(m3, d, th=None) == 1                    # npairs > 0 needs the raw angles
+    assert _block(m3, d, z=FAKE + 8) == 3                 # not 16-byte aligned
+    assert _block(m3, d, ws_bytes=64) == 1                # workspace too small
+    assert _block(m3, d, out=FAKE + 0x100010) == 1        # out overlaps x
+    assert _block(m3, d, ws=FAKE + 0x400000) == 1         # workspace overlaps dt_raw
