@@ -71,7 +71,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="scan3,decode4,scan2,scan5,scan3r,scan3q")
+    ap.add_argument("--workloads", default="scan3,decode4,scan2,scan5,scan3r,scan3q,layer3")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -217,6 +217,63 @@ def run_scan(torch, m3, cfg, steps, warmup):
     return out
 
 
+def layer_bytes(cfg):
+    """Algorithmic bytes of one layer call (the steps around the scan included):
+    z, x and the output (P each per head-token), the raw B and C (shared by the
+    heads of a group), the raw step, lambda and rate input, the raw angles, and the
+    carries."""
+    R, N, P, H, G, NP = cfg.rank, cfg.dstate, cfg.headdim, cfg.nheads, cfg.ngroups, cfg.npairs
+    io = 2 if cfg.io_dtype == "bf16" else 4
+    per_ht = 3 * io * P + 2 * io * R * N * G / H + 12 + 4 * NP
+    streams = cfg.batch * H
+    total = per_ht * streams * cfg.seqlen
+    total += streams * (P * N * 4 + 4 * NP + io * R * (N + P)) * 2      # carry in and out
+    return total
+
+
+def run_layer(torch, m3, cfg, steps, warmup):
+    """The layer entry point (m3_block_fwd) at a scan workload's shape."""
+    from m3inputs import make_block_inputs
+    dev = torch.device("cuda:0")
+    d = make_block_inputs(cfg)
+    io = torch.bfloat16 if cfg.io_dtype == "bf16" else torch.float32
+
+    def T(a, dt):
+        return None if a is None else torch.from_numpy(a).to(dev).to(dt).contiguous()
+    t = {k: T(d[k], io) for k in ("z", "x", "B_raw", "C_raw")}
+    for k in ("dt_raw", "A_raw", "lam_raw", "th_raw"):
+        t[k] = T(d.get(k), torch.float32)
+    params = {k: T(v, torch.float32) for k, v in d["params"].items()}
+    params["eps"] = 1e-6
+    init = {"h": T(d["init"]["h"], torch.float32), "phi": T(d["init"]["phi"], torch.float32),
+            "B_prev": T(d["init"]["B_prev"], io), "x_prev": T(d["init"]["x_prev"], io)}
+    del d
+    b, L, H, P = t["x"].shape
+    R = cfg.rank
+    out = torch.empty_like(t["x"])
+    fin = m3.new_carry(b, H, P, cfg.dstate, R, cfg.npairs, io, torch.float32, dev)
+    ws = None
+
+    def call():
+        nonlocal ws
+        _, _ = m3.block_fwd(t["z"], t["x"], t["B_raw"], t["C_raw"], t["dt_raw"], t["A_raw"], t["lam_raw"],
+                            t["th_raw"], params, init, chunk=cfg.chunk, out=out, final=fin, workspace=ws)
+    desc = m3._block_desc(t["x"], t["B_raw"], R, t["th_raw"], decode=False, chunk=cfg.chunk,
+                          state_dtype=torch.float32, rate_law=m3.M3_RATE_HEAVY_TAIL)
+    ws = torch.empty(max(m3.block_workspace_size(desc), 1), dtype=torch.uint8, device=dev)
+    ms = time_calls(torch, call, steps, warmup)
+    nbytes = layer_bytes(cfg)
+    res = {"workload": cfg.name, "ms_per_call": ms, "tokens_per_s": b * L / (ms * 1e-3),
+           "algo_gbs": nbytes / (ms * 1e-3) / 1e9, "bytes_per_call": nbytes,
+           "workspace_bytes": int(ws.numel())}
+    res["hbm_frac"] = res["algo_gbs"] / PEAK_HBM_GBS
+    log("[bench] %s: %.3f ms/call, %.2f M tok/s, %.0f GB/s of layer I/O (%.1f%% HBM), workspace %.2f GB" % (
+        cfg.name, ms, res["tokens_per_s"] / 1e6, res["algo_gbs"], 100 * res["hbm_frac"], ws.numel() / 1e9))
+    del t, params, init, out, fin, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_decode(torch, m3, cfg, nsteps):
     dev = torch.device("cuda:0")
     t0 = time.time()
@@ -341,15 +398,19 @@ def main():
     res = {}
     names = {"scan2": "siso_bf16_mamba2", "scan3": "mimo_bf16_prefill", "scan5": "mimo_bf16_long",
              "decode4": "mimo_bf16_decode", "scan3r": "mimo_bf16_prefill", "scan3q": "mimo_bf16_prefill",
-             "copy": None}
+             "layer3": "mimo_bf16_prefill", "copy": None}
     for w in wl:
         cfg = config_by_name(names[w]) if names[w] else None
         if w == "scan3r":      # the headline prefill with per-token heavy-tail rates
             cfg = cfg.with_(name="mimo_bf16_prefill_heavytail", rate_dyn=True)
         if w == "scan3q":      # the headline prefill on the small-chunk MIMO schedule (Q = 64 / R)
             cfg = cfg.with_(name="mimo_bf16_prefill_q16", chunk=64 // cfg.rank)
+        if w == "layer3":      # the layer entry point (steps around the scan) at the prefill shape
+            cfg = cfg.with_(name="mimo_bf16_layer")
         if w == "copy":
             res[w] = run_copy(torch, args.copy_mib)
+        elif w.startswith("layer"):
+            res[w] = run_layer(torch, m3, cfg, args.steps, args.warmup)
         elif w.startswith("scan"):
             steps = args.steps if w != "scan5" else max(3, args.steps // 4)
             res[w] = run_scan(torch, m3, cfg, steps, args.warmup)
@@ -402,6 +463,10 @@ def main():
                                    "algorithmic_bytes": dd["bytes_per_step"]}
     if "copy" in res:
         line["copy_calibration"] = res["copy"]
+    layers = {k: v for k, v in res.items() if k.startswith("layer")}
+    if layers:
+        line["layer"] = {v["workload"]: {k2: v[k2] for k2 in ("tokens_per_s", "ms_per_call", "algo_gbs", "hbm_frac")}
+                         for v in layers.values()}
     others = {k: v for k, v in res.items() if k != main_w and k.startswith("scan")}
     if others:
         line["scan_other"] = {v["workload"]: {"tokens_per_s": v["tokens_per_s"], "ms_per_call": v["ms_per_call"],

@@ -95,6 +95,126 @@ __global__ __launch_bounds__(64 * kWaves) void epilogue_kernel(BlockArgs a) {
     }
 }
 
+// ---- vectorised forms: 16-byte pieces of V io elements (V = 8 bf16 or 4 f32) per lane ----
+template <int V> struct Vec;
+template <> struct Vec<8> {          // bf16
+    typedef uint4 T;
+    __device__ static void unpack(const T& t, float (&f)[8]) {
+        const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(w[i] << 16);
+            f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    __device__ static T pack(const float (&f)[8]) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bf16x2 v;
+            v[0] = (bf16)f[2 * i];
+            v[1] = (bf16)f[2 * i + 1];
+            w[i] = __builtin_bit_cast(uint32_t, v);
+        }
+        return T{w[0], w[1], w[2], w[3]};
+    }
+};
+template <> struct Vec<4> {          // f32
+    typedef float4 T;
+    __device__ static void unpack(const T& t, float (&f)[4]) { f[0] = t.x; f[1] = t.y; f[2] = t.z; f[3] = t.w; }
+    __device__ static T pack(const float (&f)[4]) { return T{f[0], f[1], f[2], f[3]}; }
+};
+
+// BCNorm, vectorised: G = N / V lanes per row, 64 / G rows per wave (N / V a power of
+// two dividing 64).
+template <int V>
+__global__ __launch_bounds__(64 * kWaves) void bcnorm_vec_kernel(BlockArgs a) {
+    typedef typename Vec<V>::T T;
+    const int lane = threadIdx.x & 63;
+    const int G = a.N / V, RPW = 64 / G;
+    const long long rows = (long long)a.b * a.L * a.G * a.R;
+    const long long ri = ((long long)blockIdx.x * kWaves + (threadIdx.x >> 6)) * RPW + lane / G;
+    const bool ok = ri < 2 * rows;
+    const int which = (int)(ri & 1);
+    const size_t row = ok ? (size_t)(ri >> 1) : 0;
+    const int j = lane % G;                                   // piece of the row
+    const T* src = reinterpret_cast<const T*>(which ? a.Craw : a.Braw);
+    float f[V];
+    Vec<V>::unpack(ok ? src[row * G + j] : T{}, f);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) ss += f[i] * f[i];
+    for (int o = G >> 1; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);    // within the row's lanes
+    const float sc = 1.f / sqrtf(ss / (float)a.N + a.eps);
+    const float* gain = which ? a.Cg : a.Bg;
+#pragma unroll
+    for (int i = 0; i < V; ++i) f[i] *= sc * (gain ? gain[j * V + i] : 1.f);
+    if (ok) reinterpret_cast<T*>(which ? a.Cn : a.Bn)[row * G + j] = Vec<V>::pack(f);
+}
+
+// Per (token, head), vectorised: the lifted x (G = P / V lanes per token-head); the
+// scalars and angular rates by the first lane of each token-head.
+template <int V>
+__global__ __launch_bounds__(64 * kWaves) void prologue_vec_kernel(BlockArgs a) {
+    typedef typename Vec<V>::T T;
+    const int lane = threadIdx.x & 63;
+    const int G = a.P / V, TPW = 64 / G;
+    const long long nth = (long long)a.b * a.L * a.H;
+    const long long ti = ((long long)blockIdx.x * kWaves + (threadIdx.x >> 6)) * TPW + lane / G;
+    if (ti >= nth) return;
+    const int h = (int)(ti % a.H), j = lane % G;
+    if (j == 0) {
+        a.dt[ti] = softplus(a.dt_raw[ti] + (a.dt_bias ? a.dt_bias[h] : 0.f));
+        a.lam[ti] = sigmoid(a.lam_raw[ti]);
+    }
+    for (int i = j; i < a.np; i += G) a.th[(size_t)ti * a.np + i] = kPi * tanhf(a.th_raw[(size_t)ti * a.np + i]);
+    float xv[V];
+    Vec<V>::unpack(reinterpret_cast<const T*>(a.x)[(size_t)ti * G + j], xv);
+    for (int r = 0; r < a.R; ++r) {
+        const float* l = a.lift + ((size_t)h * a.R + r) * a.P + j * V;
+        float o[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) o[i] = l[i] * xv[i];
+        reinterpret_cast<T*>(a.xl)[((size_t)ti * a.R + r) * G + j] = Vec<V>::pack(o);
+    }
+}
+
+// Per (token, head), vectorised epilogue.
+template <int V>
+__global__ __launch_bounds__(64 * kWaves) void epilogue_vec_kernel(BlockArgs a) {
+    typedef typename Vec<V>::T T;
+    const int lane = threadIdx.x & 63;
+    const int G = a.P / V, TPW = 64 / G;
+    const long long nth = (long long)a.b * a.L * a.H;
+    const long long ti = ((long long)blockIdx.x * kWaves + (threadIdx.x >> 6)) * TPW + lane / G;
+    if (ti >= nth) return;
+    const int h = (int)(ti % a.H), j = lane % G;
+    const float dh = a.D ? a.D[h] : 0.f;
+    float acc[V], t[V];
+    Vec<V>::unpack(reinterpret_cast<const T*>(a.x)[(size_t)ti * G + j], t);
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = dh * t[i];
+    for (int r = 0; r < a.R; ++r) {
+        Vec<V>::unpack(reinterpret_cast<const T*>(a.y)[((size_t)ti * a.R + r) * G + j], t);
+        const float* w = a.comb + ((size_t)h * a.R + r) * a.P + j * V;
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] += w[i] * t[i];
+    }
+    Vec<V>::unpack(reinterpret_cast<const T*>(a.z)[(size_t)ti * G + j], t);
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] *= t[i] * sigmoid(t[i]);
+    reinterpret_cast<T*>(a.out)[(size_t)ti * G + j] = Vec<V>::pack(acc);
+}
+
+// The vectorised forms need the row (N) and token-head (P) widths to be whole numbers
+// of 16-byte pieces whose count per row divides the wave.
+bool pow2_divides_64(int g) { return g >= 1 && g <= 64 && (g & (g - 1)) == 0; }
+int vec_width(const BlockArgs& a) { return a.io_bf16 ? 8 : 4; }
+bool vec_ok(const BlockArgs& a, int n) {
+    const int v = vec_width(a);
+    return n % v == 0 && pow2_divides_64(n / v);
+}
+
 unsigned blocks_for(long long waves) { return (unsigned)((waves + kWaves - 1) / kWaves); }
 
 }  // namespace
@@ -102,18 +222,42 @@ unsigned blocks_for(long long waves) { return (unsigned)((waves + kWaves - 1) / 
 hipError_t launch_block_prologue(const BlockArgs& a, hipStream_t s) {
     const long long rows = 2LL * a.b * a.L * a.G * a.R;
     const long long toks = (long long)a.b * a.L * a.H;
+    const int v = vec_width(a);
     if (rows > 0) {
-        hipLaunchKernelGGL(bcnorm_kernel, dim3(blocks_for(rows)), dim3(64 * kWaves), 0, s, a);
+        if (vec_ok(a, a.N)) {
+            const int rpw = 64 / (a.N / v);
+            if (v == 8) hipLaunchKernelGGL(bcnorm_vec_kernel<8>, dim3(blocks_for((rows + rpw - 1) / rpw)), dim3(64 * kWaves), 0, s, a);
+            else hipLaunchKernelGGL(bcnorm_vec_kernel<4>, dim3(blocks_for((rows + rpw - 1) / rpw)), dim3(64 * kWaves), 0, s, a);
+        } else {
+            hipLaunchKernelGGL(bcnorm_kernel, dim3(blocks_for(rows)), dim3(64 * kWaves), 0, s, a);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (toks > 0) hipLaunchKernelGGL(prologue_kernel, dim3(blocks_for(toks)), dim3(64 * kWaves), 0, s, a);
+    if (toks > 0) {
+        if (vec_ok(a, a.P)) {
+            const int tpw = 64 / (a.P / v);
+            if (v == 8) hipLaunchKernelGGL(prologue_vec_kernel<8>, dim3(blocks_for((toks + tpw - 1) / tpw)), dim3(64 * kWaves), 0, s, a);
+            else hipLaunchKernelGGL(prologue_vec_kernel<4>, dim3(blocks_for((toks + tpw - 1) / tpw)), dim3(64 * kWaves), 0, s, a);
+        } else {
+            hipLaunchKernelGGL(prologue_kernel, dim3(blocks_for(toks)), dim3(64 * kWaves), 0, s, a);
+        }
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_block_epilogue(const BlockArgs& a, hipStream_t s) {
     const long long toks = (long long)a.b * a.L * a.H;
-    if (toks > 0) hipLaunchKernelGGL(epilogue_kernel, dim3(blocks_for(toks)), dim3(64 * kWaves), 0, s, a);
+    const int v = vec_width(a);
+    if (toks > 0) {
+        if (vec_ok(a, a.P)) {
+            const int tpw = 64 / (a.P / v);
+            if (v == 8) hipLaunchKernelGGL(epilogue_vec_kernel<8>, dim3(blocks_for((toks + tpw - 1) / tpw)), dim3(64 * kWaves), 0, s, a);
+            else hipLaunchKernelGGL(epilogue_vec_kernel<4>, dim3(blocks_for((toks + tpw - 1) / tpw)), dim3(64 * kWaves), 0, s, a);
+        } else {
+            hipLaunchKernelGGL(epilogue_kernel, dim3(blocks_for(toks)), dim3(64 * kWaves), 0, s, a);
+        }
+    }
     return hipGetLastError();
 }
 
