@@ -367,15 +367,37 @@ m3_status m3_block_fwd(const m3_desc* d, const m3_block_params* p, const void* z
     if ((st = check_block(d, p, 0, z, x, B_raw, C_raw, dt_raw, A, lam_raw, th_raw, out, workspace,
                           workspace_bytes)) != M3_OK)
         return st;
+    if (init && (st = check_carry(init, d)) != M3_OK) return st;
+    if (final_) {
+        if ((st = check_carry(final_, d)) != M3_OK) return st;
+        const Sizes cs = sizes(d, d->seqlen);
+        Range ri[4], rf[4];
+        carry_ranges(final_, cs, rf);
+        if (init) carry_ranges(init, cs, ri);
+        for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 4; ++j)
+                if ((init && overlap(rf[i], ri[j])) || (j > i && overlap(rf[i], rf[j]))) return M3_ERR_INVALID_ARG;
+    }
     const BlockWs w = block_ws(d, 0);
-    const BlockArgs a = make_block_args(d, p, d->seqlen, z, x, B_raw, C_raw, dt_raw, lam_raw, th_raw, out,
-                                        workspace, w);
+    BlockArgs a = make_block_args(d, p, d->seqlen, z, x, B_raw, C_raw, dt_raw, lam_raw, th_raw, out, workspace, w);
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    if (launch_block_prologue(a, hs) != hipSuccess) return M3_ERR_HIP;
     char* base = static_cast<char*>(workspace);
-    st = m3_scan_fwd(d, a.xl, a.Bn, a.Cn, a.dt, a.lam, d->npairs ? a.th : nullptr, A, p->B_bias, p->C_bias, init,
-                     base + w.y, final_, w.scan_bytes ? base + w.scan : nullptr, w.scan_bytes, stream);
-    if (st != M3_OK) return st;
+    // The matrix-core scan lifts x as it fetches the rows; elsewhere the prologue writes
+    // the lifted rows and the scan reads them.
+    ScanArgs sa = make_scan_args(d, x, a.Bn, a.Cn, a.dt, a.lam, d->npairs ? a.th : nullptr, A, p->B_bias,
+                                 p->C_bias, init, base + w.y, final_);
+    const bool fused_lift = sa.io_bf16 && scan_mfma_supported(sa);
+    if (fused_lift) a.xl = nullptr;
+    if (launch_block_prologue(a, hs) != hipSuccess) return M3_ERR_HIP;
+    if (fused_lift) {
+        sa.lift = p->lift;
+        sa.ws = w.scan_bytes ? reinterpret_cast<float*>(base + w.scan) : nullptr;
+        if (launch_scan_mfma(sa, hs) != hipSuccess) return M3_ERR_HIP;
+    } else {
+        st = m3_scan_fwd(d, a.xl, a.Bn, a.Cn, a.dt, a.lam, d->npairs ? a.th : nullptr, A, p->B_bias, p->C_bias,
+                         init, base + w.y, final_, w.scan_bytes ? base + w.scan : nullptr, w.scan_bytes, stream);
+        if (st != M3_OK) return st;
+    }
     return launch_block_epilogue(a, hs) == hipSuccess ? M3_OK : M3_ERR_HIP;
 }
 

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(64 * kWaves) void prologue_kernel(BlockArgs a) {
         a.lam[ti] = sigmoid(a.lam_raw[ti]);
     }
     for (int i = lane; i < a.np; i += 64) a.th[(size_t)ti * a.np + i] = kPi * tanhf(a.th_raw[(size_t)ti * a.np + i]);
-    for (int p = lane; p < a.P; p += 64) {
+    for (int p = lane; p < a.P && a.xl; p += 64) {
         const float xv = ld_io(a.x, (size_t)ti * a.P + p, a.io_bf16);
         for (int r = 0; r < a.R; ++r)
             st_io(a.xl, ((size_t)ti * a.R + r) * a.P + p, a.lift[((size_t)h * a.R + r) * a.P + p] * xv, a.io_bf16);
@@ -168,6 +168,7 @@ __global__ __launch_bounds__(64 * kWaves) void prologue_vec_kernel(BlockArgs a) 
         a.lam[ti] = sigmoid(a.lam_raw[ti]);
     }
     for (int i = j; i < a.np; i += G) a.th[(size_t)ti * a.np + i] = kPi * tanhf(a.th_raw[(size_t)ti * a.np + i]);
+    if (!a.xl) return;                                   // the scan lifts x itself
     float xv[V];
     Vec<V>::unpack(reinterpret_cast<const T*>(a.x)[(size_t)ti * G + j], xv);
     for (int r = 0; r < a.R; ++r) {

@@ -32,6 +32,9 @@ struct ScanArgs {
     // segmented schedule: nseg segments of seglen tokens (seglen % Q == 0)
     int nseg, seglen;
     float* ws;   // workspace (segmented schedule only)
+    // matrix-core path only: non-null when x is the un-lifted [b, L, H, P] and key row
+    // (t, r) is lift[h, r, :] * x[t] (the layer's P x R lift, applied as rows are fetched)
+    const float* lift;
 };
 
 // Decode-step arguments (one token, carry in place).

@@ -293,10 +293,13 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
     const size_t tokbase = (size_t)bi * L;
     const uint16_t* const Bg = static_cast<const uint16_t*>(a.B) + (tokbase * a.G + g) * R * kN;
     const uint16_t* const Cg = static_cast<const uint16_t*>(a.C) + (tokbase * a.G + g) * R * kN;
-    const uint16_t* const Xg = static_cast<const uint16_t*>(a.x) + (tokbase * H + h) * R * kP;
+    const bool lifted = a.lift != nullptr;                // x rows lifted as they are fetched
+    const int xrows = lifted ? 1 : R;                      // x rows per (token, head) in memory
+    const uint16_t* const Xg = static_cast<const uint16_t*>(a.x) + (tokbase * H + h) * xrows * kP;
     const size_t bstride = (size_t)a.G * R * kN;
-    const size_t xstride = (size_t)H * R * kP;
+    const size_t xstride = (size_t)H * xrows * kP;
     const uint32_t bsb = (uint32_t)bstride * 2u, xsb = (uint32_t)xstride * 2u;   // bytes per token
+    const uint32_t ysb = (uint32_t)H * R * kP * 2u;                               // y: bytes per token
     const float* const dtg = a.dt + tokbase * H + h;
     const float* const lamg = a.lam + tokbase * H + h;
     const float* const rateg = a.A_log + (dyn_rate ? tokbase * H + h : 0);
@@ -437,7 +440,7 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
         auto store_y = [&](int cst, int nv) {
             // rows of tokens at or past nv fall outside the record count: dropped
             const __amdgpu_buffer_rsrc_t ry = make_rsrc(static_cast<uint16_t*>(a.y) + ((tokbase + cst) * H + h) * R * kP,
-                                                        (uint32_t)nv * xsb);
+                                                        (uint32_t)nv * ysb);
             unsigned ln = lane;                               // opaque: offsets formed here
             asm volatile("" : "+v"(ln));
             ln &= 63u;
@@ -454,7 +457,7 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
                     const u32x4 v = *reinterpret_cast<const u32x4*>(xs + j * 144 + (ln & 7u) * 16);
                     const unsigned qi = 16 * qt + j;
                     const unsigned t = qi / R, r = qi % R;
-                    __builtin_amdgcn_raw_buffer_store_b128(v, ry, (int)(t * xsb + r * (kP * 2) + 16 * (ln & 7u)), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(v, ry, (int)(t * ysb + r * (kP * 2) + 16 * (ln & 7u)), 0, 0);
                 }
             }
         };
@@ -479,7 +482,7 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
         auto store_rows = [&](int cst, int nv, int qt, int r0, auto nrc) {
             constexpr unsigned NR = decltype(nrc)::value;
             const __amdgpu_buffer_rsrc_t ry = make_rsrc(static_cast<uint16_t*>(a.y) + ((tokbase + cst) * H + h) * R * kP,
-                                                        (uint32_t)nv * xsb);
+                                                        (uint32_t)nv * ysb);
             unsigned ln = lane;                               // opaque: offsets formed here
             asm volatile("" : "+v"(ln));
             ln &= 63u;
@@ -487,7 +490,7 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
                 const unsigned qi = 16 * (unsigned)qt + (unsigned)r0 + (ln >> 3);
                 const u32x4 v = *reinterpret_cast<const u32x4*>(ys + qi * 144 + (ln & 7u) * 16);
                 const unsigned t = qi / R, r = qi % R;
-                __builtin_amdgcn_raw_buffer_store_b128(v, ry, (int)(t * xsb + r * (kP * 2) + 16 * (ln & 7u)), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(v, ry, (int)(t * ysb + r * (kP * 2) + 16 * (ln & 7u)), 0, 0);
             }
         };
         // raw C rows of tiles KB .. KE - 1 of the chunk at cst straight into the operand layout
@@ -769,6 +772,13 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
                 bb[r][1] = pack2(v.z, v.w);
             }
         }
+        // lift factors of this lane's two x elements p = 2 lq, 2 lq + 1, per rank
+        float lf[R][2];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            lf[r][0] = lifted ? a.lift[((size_t)h * R + r) * kP + 2 * lq] : 0.f;
+            lf[r][1] = lifted ? a.lift[((size_t)h * R + r) * kP + 2 * lq + 1] : 0.f;
+        }
         // state columns [32 pw, 32 pw + 32): H^T tiles (n-tile 2 pw + u, p-tile pt), lane:
         // p = 16 pt + l16, n = 32 pw + 16 u + 4 g4 + m
         f32x4 hacc[2][4];
@@ -838,10 +848,13 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
                 const unsigned u = h2 * (16 / R) + i / R, r = i % R;
                 pb[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rb, (int)(u * bsb + 256 * r + 8 * l2), 0, 0));
             }
+            // row rr = (token u, rank r); an un-lifted x has one row per token, which every
+            // rank's slot loads (the lift is applied when the rows are turned into tiles)
+            const unsigned rstride = lifted ? 0u : 128u;
 #pragma unroll
             for (int rr = 0; rr < 8; ++rr) {
                 const unsigned u = (rr >> 2) * (16 / R) + (rr & 3) / R, r = (rr & 3) % R;
-                px[rr] = __builtin_amdgcn_raw_buffer_load_b32(rx, (int)(u * xsb + 128 * r + 4 * l2), 0, 0);
+                px[rr] = __builtin_amdgcn_raw_buffer_load_b32(rx, (int)(u * xsb + rstride * r + 4 * l2), 0, 0);
             }
             f_rem -= TPB;
             f_b += (size_t)TPB * bstride;
@@ -875,12 +888,19 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
                 const float v = vvr[i];
                 *reinterpret_cast<uint2*>(buf + kBnBytes + o) = uint2{pack2(p0.x * v, p0.y * v), pack2(p1.x * v, p1.y * v)};
             }
+            // the 8 x rows (lifted here when x is un-lifted: row rr of rank r is lift[r] * x)
+            uint32_t xv[8];
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr) {
+                const int r = (rr & 3) % R;
+                xv[rr] = lifted ? pack2(lf[r][0] * lo_f(px[rr]), lf[r][1] * hi_f(px[rr])) : px[rr];
+            }
             // XT rows p = 2 lq, 2 lq + 1, key group pw (lanes of the first half-wave)
             uint32_t xt0[4], xt1[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                xt0[q] = __builtin_amdgcn_perm(px[2 * q + 1], px[2 * q], 0x05040100u);
-                xt1[q] = __builtin_amdgcn_perm(px[2 * q + 1], px[2 * q], 0x07060302u);
+                xt0[q] = __builtin_amdgcn_perm(xv[2 * q + 1], xv[2 * q], 0x05040100u);
+                xt1[q] = __builtin_amdgcn_perm(xv[2 * q + 1], xv[2 * q], 0x07060302u);
             }
             char* xtt = buf + kBnBytes + kBvBytes;
             if (hh == 0) {
@@ -1068,8 +1088,11 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
                 }
                 *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.Bp1) + ((size_t)bh * R + r) * kN + 2 * i) = pack2(b0, b1);
             }
-            for (int e = tid; e < R * kP; e += kThreads)
-                static_cast<uint16_t*>(a.xp1)[(size_t)bh * R * kP + e] = Xg[(size_t)t * xstride + e];
+            for (int e = tid; e < R * kP; e += kThreads) {
+                uint16_t v = Xg[(size_t)t * xstride + (lifted ? e % kP : e)];
+                if (lifted) v = __builtin_bit_cast(uint16_t, (bf16)(a.lift[(size_t)h * R * kP + e] * bf16_bits_to_f32(v)));
+                static_cast<uint16_t*>(a.xp1)[(size_t)bh * R * kP + e] = v;
+            }
         }
     }
 }
