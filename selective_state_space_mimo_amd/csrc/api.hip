@@ -382,15 +382,21 @@ m3_status m3_block_fwd(const m3_desc* d, const m3_block_params* p, const void* z
     BlockArgs a = make_block_args(d, p, d->seqlen, z, x, B_raw, C_raw, dt_raw, lam_raw, th_raw, out, workspace, w);
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     char* base = static_cast<char*>(workspace);
-    // The matrix-core scan lifts x as it fetches the rows; elsewhere the prologue writes
-    // the lifted rows and the scan reads them.
-    ScanArgs sa = make_scan_args(d, x, a.Bn, a.Cn, a.dt, a.lam, d->npairs ? a.th : nullptr, A, p->B_bias,
+    // The matrix-core scan lifts x as it fetches the rows and activates the raw step,
+    // blend and angle inputs as it stages them; elsewhere the prologue writes the lifted
+    // rows and the activated inputs and the scan reads them.  BCNorm always runs first
+    // (B and C are shared by the heads of a group).
+    ScanArgs sa = make_scan_args(d, x, a.Bn, a.Cn, dt_raw, lam_raw, d->npairs ? th_raw : nullptr, A, p->B_bias,
                                  p->C_bias, init, base + w.y, final_);
-    const bool fused_lift = sa.io_bf16 && scan_mfma_supported(sa);
-    if (fused_lift) a.xl = nullptr;
+    const bool fused = sa.io_bf16 && scan_mfma_supported(sa);
+    if (fused) {
+        a.xl = nullptr;
+        a.dt = a.lam = a.th = nullptr;
+    }
     if (launch_block_prologue(a, hs) != hipSuccess) return M3_ERR_HIP;
-    if (fused_lift) {
+    if (fused) {
         sa.lift = p->lift;
+        sa.dt_bias = p->dt_bias;
         sa.ws = w.scan_bytes ? reinterpret_cast<float*>(base + w.scan) : nullptr;
         if (launch_scan_mfma(sa, hs) != hipSuccess) return M3_ERR_HIP;
     } else {

@@ -26,8 +26,8 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ float softplus(float v) { return fmaxf(v, 0.f) + log1pf(expf(-fabsf(v))); }
-__device__ __forceinline__ float sigmoid(float v) { return 1.f / (1.f + expf(-v)); }
+__device__ __forceinline__ float softplus(float v) { return softplus_f(v); }
+__device__ __forceinline__ float sigmoid(float v) { return sigmoid_f(v); }
 
 // BCNorm: row (token, group, rank) of B (which = 0) or C (which = 1).
 __global__ __launch_bounds__(64 * kWaves) void bcnorm_kernel(BlockArgs a) {
@@ -163,11 +163,13 @@ __global__ __launch_bounds__(64 * kWaves) void prologue_vec_kernel(BlockArgs a) 
     const long long ti = ((long long)blockIdx.x * kWaves + (threadIdx.x >> 6)) * TPW + lane / G;
     if (ti >= nth) return;
     const int h = (int)(ti % a.H), j = lane % G;
-    if (j == 0) {
-        a.dt[ti] = softplus(a.dt_raw[ti] + (a.dt_bias ? a.dt_bias[h] : 0.f));
-        a.lam[ti] = sigmoid(a.lam_raw[ti]);
+    if (a.dt) {                                          // (else the scan activates them itself)
+        if (j == 0) {
+            a.dt[ti] = softplus(a.dt_raw[ti] + (a.dt_bias ? a.dt_bias[h] : 0.f));
+            a.lam[ti] = sigmoid(a.lam_raw[ti]);
+        }
+        for (int i = j; i < a.np; i += G) a.th[(size_t)ti * a.np + i] = kPi * tanhf(a.th_raw[(size_t)ti * a.np + i]);
     }
-    for (int i = j; i < a.np; i += G) a.th[(size_t)ti * a.np + i] = kPi * tanhf(a.th_raw[(size_t)ti * a.np + i]);
     if (!a.xl) return;                                   // the scan lifts x itself
     float xv[V];
     Vec<V>::unpack(reinterpret_cast<const T*>(a.x)[(size_t)ti * G + j], xv);
@@ -235,7 +237,7 @@ hipError_t launch_block_prologue(const BlockArgs& a, hipStream_t s) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (toks > 0) {
+    if (toks > 0 && (a.dt || a.xl)) {
         if (vec_ok(a, a.P)) {
             const int tpw = 64 / (a.P / v);
             if (v == 8) hipLaunchKernelGGL(prologue_vec_kernel<8>, dim3(blocks_for((toks + tpw - 1) / tpw)), dim3(64 * kWaves), 0, s, a);

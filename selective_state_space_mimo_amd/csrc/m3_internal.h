@@ -32,9 +32,13 @@ struct ScanArgs {
     // segmented schedule: nseg segments of seglen tokens (seglen % Q == 0)
     int nseg, seglen;
     float* ws;   // workspace (segmented schedule only)
-    // matrix-core path only: non-null when x is the un-lifted [b, L, H, P] and key row
-    // (t, r) is lift[h, r, :] * x[t] (the layer's P x R lift, applied as rows are fetched)
+    // Matrix-core path only, the layer entry point: when lift is non-null, x is the
+    // un-lifted [b, L, H, P] and key row (t, r) is lift[h, r, :] * x[t] (the layer's P x R
+    // lift, applied as the rows are fetched), and dt, lam, theta hold the layer's raw
+    // projections, activated as they are staged: dt = softplus(dt + dt_bias[h]),
+    // lam = sigmoid(lam), theta = pi tanh(theta).
     const float* lift;
+    const float* dt_bias;
 };
 
 // Decode-step arguments (one token, carry in place).
@@ -101,6 +105,10 @@ __device__ __forceinline__ float heavy_tail_rate(float u) {
     const float ht = u >= 0.f ? 1.f + u : 1.f / (1.f - u);
     return fminf(-ht, -1e-4f);
 }
+// The layer's activations of its raw step, blend and angle projections.
+__device__ __forceinline__ float softplus_f(float v) { return fmaxf(v, 0.f) + log1pf(expf(-fabsf(v))); }
+__device__ __forceinline__ float sigmoid_f(float v) { return 1.f / (1.f + expf(-v)); }
+constexpr float kPiF = 3.14159265358979f;
 // Reduce an angle into [0, 2 pi).
 __device__ __forceinline__ float wrap_2pi(float v) {
     float w = v - kTwoPi * floorf(v * (1.0f / kTwoPi));

@@ -233,7 +233,10 @@ static_assert(ctile_blocks_increase<4, 4>() && ctile_blocks_increase<8, 2>(), "o
 template <int R, int Q>
 constexpr int waves_per_simd() { return (R == 4 && Q == 16) ? 4 : n_threads<R, Q>() / 256; }
 
-template <int R, int Q, int MODE>
+// LAYER: the kernel runs inside the layer entry point, so x is un-lifted (lift applied as
+// the rows are fetched) and dt, lam, theta are the raw projections (activated as they are
+// staged); a compile-time switch, so the scan on its own carries none of it.
+template <int R, int Q, int MODE, bool LAYER>
 __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void scan_ws_kernel(ScanArgs a) {
     constexpr int kNC = n_consumers<R, Q>();                // consumer waves
     constexpr int kThreads = n_threads<R, Q>();
@@ -282,6 +285,7 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
     const bool last_seg = (T1 == L);
     const bool dyn_rate = a.rate_law != 0;               // A_log holds the per-token rate input
     const float ah = dyn_rate ? 0.f : expf(a.A_log[h]);
+    const float dtb = LAYER && a.dt_bias ? a.dt_bias[h] : 0.f;   // raw projections: step bias
     const size_t ss = (size_t)bh * nseg + seg;
     const size_t S = (size_t)a.b * H * nseg;
     float* const wsHloc = a.ws;
@@ -293,7 +297,7 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
     const size_t tokbase = (size_t)bi * L;
     const uint16_t* const Bg = static_cast<const uint16_t*>(a.B) + (tokbase * a.G + g) * R * kN;
     const uint16_t* const Cg = static_cast<const uint16_t*>(a.C) + (tokbase * a.G + g) * R * kN;
-    const bool lifted = a.lift != nullptr;                // x rows lifted as they are fetched
+    constexpr bool lifted = LAYER;                        // x rows lifted as they are fetched
     const int xrows = lifted ? 1 : R;                      // x rows per (token, head) in memory
     const uint16_t* const Xg = static_cast<const uint16_t*>(a.x) + (tokbase * H + h) * xrows * kP;
     const size_t bstride = (size_t)a.G * R * kN;
@@ -351,7 +355,8 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
             const int t = th_t + 64 * pp;
             if (t < Q) {
 #pragma unroll
-                for (int u = 0; u < THU; ++u) stage[(th_i + u) * (Q + 1) + t] = th[pp][u];
+                for (int u = 0; u < THU; ++u)
+                    stage[(th_i + u) * (Q + 1) + t] = LAYER ? kPiF * tanhf(th[pp][u]) : th[pp][u];
             }
         }
     };
@@ -411,20 +416,31 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
             rgS[j] = v;
         }
     };
-    auto stage_scalars = [&]() {
+    // (raw projections: the step and the blend are activated here, for valid tokens only;
+    // the others stay 0)
+    auto stage_scalars = [&](int cstart) {
+        int tt = tid;                                         // opaque: the LDS addresses are
+        asm volatile("" : "+v"(tt));                          // formed here, not kept live
+        tt &= 1023;
 #pragma unroll
         for (int j = 0; j < NSV; ++j) {
-            const int e = tid - kNC * 64 + kNP * 64 * j;
-            if (e <= Q) sDt[e] = rgS[j];
-            else if (e < 2 * Q + 2) sLm[e - (Q + 1)] = rgS[j];
-            else if (e < 3 * Q + 2) sAr[e - (2 * Q + 2)] = rgS[j];
+            const int e = tt - kNC * 64 + kNP * 64 * j;
+            float v = rgS[j];
+            if (LAYER && e < 2 * Q + 2) {
+                const int t = e <= Q ? e : e - (Q + 1);
+                const bool ok = t < Q ? cstart + t < T1 : cstart + Q < L;
+                if (ok) v = e <= Q ? softplus_f(v + dtb) : sigmoid_f(v);
+            }
+            if (e <= Q) sDt[e] = v;
+            else if (e < 2 * Q + 2) sLm[e - (Q + 1)] = v;
+            else if (e < 3 * Q + 2) sAr[e - (2 * Q + 2)] = v;
         }
     };
     float rgTh[THP][THU];
     load_theta(T0, rgTh);
     if (w >= kNC) {
         load_scalars(T0);
-        stage_scalars();
+        stage_scalars(T0);
     }
     __syncthreads();
 
@@ -802,7 +818,8 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
                             }
                         }
                         if (a.Bp0 && a.xp0) {
-                            const float d0 = dtg[0] * (1.f - lamg[0]);
+                            const float dt0 = LAYER ? softplus_f(dtg[0] + dtb) : dtg[0];
+                            const float d0 = dt0 * (1.f - (LAYER ? sigmoid_f(lamg[0]) : lamg[0]));
                             const uint16_t* bp = static_cast<const uint16_t*>(a.Bp0) + (size_t)bh * R * kN;
                             const uint16_t* xp = static_cast<const uint16_t*>(a.xp0) + (size_t)bh * R * kP;
 #pragma unroll
@@ -996,7 +1013,7 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
 #pragma unroll
                 for (int d = 0; d < DP; ++d) {
                     const int J = J0 + d;
-                    if (J == 0) stage_scalars();              // the next chunk's inputs
+                    if (J == 0) stage_scalars(c0 + Q);        // the next chunk's inputs
                     fetch(rgB[d], rgX[d]);
                     // every LDS read of the iteration first (block J's operands, block J + 1's
                     // angles and v), then the state MFMAs, then block J + 1's tiles
@@ -1122,7 +1139,9 @@ __global__ __launch_bounds__(256) void carry_pass_kernel(ScanArgs a) {
     }
     if (a.Bp0 && a.xp0) {
         const size_t t0 = (size_t)bi * L * H + (bh % H);
-        const float d0 = a.dt[t0] * (1.f - a.lam[t0]);
+        const bool raw = a.lift != nullptr;                 // the layer's raw projections
+        const float dt0 = raw ? softplus_f(a.dt[t0] + (a.dt_bias ? a.dt_bias[bh % H] : 0.f)) : a.dt[t0];
+        const float d0 = dt0 * (1.f - (raw ? sigmoid_f(a.lam[t0]) : a.lam[t0]));
         for (int r = 0; r < a.R; ++r) {
             const float xv = d0 * ld_io(a.xp0, ((size_t)bh * a.R + r) * kP + p, 1);
             h0 += xv * ld_io(a.Bp0, ((size_t)bh * a.R + r) * kN + n, 1);
@@ -1151,25 +1170,30 @@ __global__ __launch_bounds__(256) void carry_pass_kernel(ScanArgs a) {
     }
 }
 
-template <int R, int Q>
-hipError_t launch_rq(const ScanArgs& a, hipStream_t st) {
+template <int R, int Q, bool LAYER>
+hipError_t launch_rql(const ScanArgs& a, hipStream_t st) {
     const size_t lds = Layout<R, Q>::total;
     const int nblk = a.b * a.H * a.nseg;
     hipError_t e;
     if (a.nseg > 1) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_ws_kernel<R, Q, kSummary>),
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_ws_kernel<R, Q, kSummary, LAYER>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((scan_ws_kernel<R, Q, kSummary>), dim3(nblk), dim3(n_threads<R, Q>()), lds, st, a);
+        hipLaunchKernelGGL((scan_ws_kernel<R, Q, kSummary, LAYER>), dim3(nblk), dim3(n_threads<R, Q>()), lds, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL(carry_pass_kernel, dim3((kP * kN / 2 + 255) / 256, a.b * a.H), dim3(256), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_ws_kernel<R, Q, kFull>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_ws_kernel<R, Q, kFull, LAYER>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_ws_kernel<R, Q, kFull>), dim3(nblk), dim3(n_threads<R, Q>()), lds, st, a);
+    hipLaunchKernelGGL((scan_ws_kernel<R, Q, kFull, LAYER>), dim3(nblk), dim3(n_threads<R, Q>()), lds, st, a);
     return hipGetLastError();
+}
+
+template <int R, int Q>
+hipError_t launch_rq(const ScanArgs& a, hipStream_t st) {
+    return a.lift ? launch_rql<R, Q, true>(a, st) : launch_rql<R, Q, false>(a, st);
 }
 
 }  // namespace
