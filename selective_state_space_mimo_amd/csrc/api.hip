@@ -388,7 +388,7 @@ m3_status m3_block_fwd(const m3_desc* d, const m3_block_params* p, const void* z
     // (B and C are shared by the heads of a group).
     ScanArgs sa = make_scan_args(d, x, a.Bn, a.Cn, dt_raw, lam_raw, d->npairs ? th_raw : nullptr, A, p->B_bias,
                                  p->C_bias, init, base + w.y, final_);
-    const bool fused = sa.io_bf16 && scan_mfma_supported(sa);
+    const bool fused = sa.io_bf16 && scan_mfma_supported(sa) && sa.Q <= 64;
     if (fused) {
         a.xl = nullptr;
         a.dt = a.lam = a.th = nullptr;
@@ -397,8 +397,11 @@ m3_status m3_block_fwd(const m3_desc* d, const m3_block_params* p, const void* z
     if (fused) {
         sa.lift = p->lift;
         sa.dt_bias = p->dt_bias;
+        sa.comb = p->comb;                      // y: the recombined readout [b, L, H, P]
         sa.ws = w.scan_bytes ? reinterpret_cast<float*>(base + w.scan) : nullptr;
         if (launch_scan_mfma(sa, hs) != hipSuccess) return M3_ERR_HIP;
+        a.R = 1;
+        a.comb = nullptr;
     } else {
         st = m3_scan_fwd(d, a.xl, a.Bn, a.Cn, a.dt, a.lam, d->npairs ? a.th : nullptr, A, p->B_bias, p->C_bias,
                          init, base + w.y, final_, w.scan_bytes ? base + w.scan : nullptr, w.scan_bytes, stream);

@@ -88,7 +88,8 @@ __global__ __launch_bounds__(64 * kWaves) void epilogue_kernel(BlockArgs a) {
     for (int p = lane; p < a.P; p += 64) {
         float acc = 0.f;
         for (int r = 0; r < a.R; ++r)
-            acc += a.comb[((size_t)h * a.R + r) * a.P + p] * ld_io(a.y, ((size_t)ti * a.R + r) * a.P + p, a.io_bf16);
+            acc += (a.comb ? a.comb[((size_t)h * a.R + r) * a.P + p] : 1.f) *
+                   ld_io(a.y, ((size_t)ti * a.R + r) * a.P + p, a.io_bf16);
         acc += dh * ld_io(a.x, (size_t)ti * a.P + p, a.io_bf16);
         const float zz = ld_io(a.z, (size_t)ti * a.P + p, a.io_bf16);
         st_io(a.out, (size_t)ti * a.P + p, acc * zz * sigmoid(zz), a.io_bf16);
@@ -199,9 +200,14 @@ __global__ __launch_bounds__(64 * kWaves) void epilogue_vec_kernel(BlockArgs a) 
     for (int i = 0; i < V; ++i) acc[i] = dh * t[i];
     for (int r = 0; r < a.R; ++r) {
         Vec<V>::unpack(reinterpret_cast<const T*>(a.y)[((size_t)ti * a.R + r) * G + j], t);
-        const float* w = a.comb + ((size_t)h * a.R + r) * a.P + j * V;
+        if (a.comb) {
+            const float* w = a.comb + ((size_t)h * a.R + r) * a.P + j * V;
 #pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] += w[i] * t[i];
+            for (int i = 0; i < V; ++i) acc[i] += w[i] * t[i];
+        } else {                                         // y already recombined (R = 1)
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[i] += t[i];
+        }
     }
     Vec<V>::unpack(reinterpret_cast<const T*>(a.z)[(size_t)ti * G + j], t);
 #pragma unroll

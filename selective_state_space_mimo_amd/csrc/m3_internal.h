@@ -39,6 +39,9 @@ struct ScanArgs {
     // lam = sigmoid(lam), theta = pi tanh(theta).
     const float* lift;
     const float* dt_bias;
+    // with lift: the readout weights [H, R, P]; y is then the recombined readout
+    // sum_r comb[h, r] y_r, [b, L, H, P] (chunks of at most 64 tokens only)
+    const float* comb;
 };
 
 // Decode-step arguments (one token, carry in place).

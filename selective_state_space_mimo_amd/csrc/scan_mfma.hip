@@ -159,7 +159,8 @@ struct Layout {
     // stored during the next chunk's key blocks; with Q = 128 (no room) each consumer stores
     // a tile at a time through a 4 KiB scratch.
     static constexpr bool kYStage = Q <= 64;
-    static constexpr int xsc = misc + 16 * 4;                 // per consumer 4 KiB (Q = 128)
+    static constexpr int cmb = misc + 16 * 4;                 // float [R][64]: readout weights (layer)
+    static constexpr int xsc = cmb + R * 64 * 4;              // per consumer 4 KiB (Q = 128)
     static constexpr int ysg = xsc + (kYStage ? 0 : 4 * 4096);
     static constexpr int total = ysg + (kYStage ? R * Q * 144 : 0);
 };
@@ -252,6 +253,7 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
     constexpr bool kFullMode = MODE == kFull;
     static_assert(TPC >= 1 && TPC <= 4 && NKB >= 2 && NKB % 2 == 0, "chunk shape");
     using LY = Layout<R, Q>;
+    static_assert(!LAYER || LY::kYStage, "the layer variant stages its outputs");
     static_assert(waves_per_simd<R, Q>() != 4 || LY::total <= 80 * 1024, "two workgroups per CU fit the LDS");
     extern __shared__ __attribute__((aligned(16))) char smem[];
     float* sL2 = reinterpret_cast<float*>(smem + LY::l2);
@@ -320,6 +322,10 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
     }
     for (int e = tid; e < Q * 64; e += kThreads)
         if ((e & 63) >= np) sCS[(e & ~63) + ((e & 63) ^ ((e >> 6) & 60))] = cs_entry(1.f, 0.f);
+    if constexpr (LAYER)
+        if (kFullMode)
+            for (int e = tid; e < R * kP; e += kThreads)
+                reinterpret_cast<float*>(smem + LY::cmb)[e] = a.comb[(size_t)h * R * kP + e];
 
     // theta of the chunk at cstart (all threads: THU consecutive pairs of one token each,
     // THP times), one buffer load per value.  Token t's np angles of this head start t H np after the
@@ -497,11 +503,37 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
         // later tokens fall outside the record count
         auto store_rows = [&](int cst, int nv, int qt, int r0, auto nrc) {
             constexpr unsigned NR = decltype(nrc)::value;
-            const __amdgpu_buffer_rsrc_t ry = make_rsrc(static_cast<uint16_t*>(a.y) + ((tokbase + cst) * H + h) * R * kP,
-                                                        (uint32_t)nv * ysb);
             unsigned ln = lane;                               // opaque: offsets formed here
             asm volatile("" : "+v"(ln));
             ln &= 63u;
+            if constexpr (LAYER) {
+                // the layer: the R readouts of each token recombined, sum_r comb[r] y_r, one
+                // P-wide row per token (NR / R tokens, eight lanes a token)
+                const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<uint16_t*>(a.y) + ((tokbase + cst) * H + h) * kP,
+                                                            (uint32_t)nv * (uint32_t)(H * kP * 2));
+                if (ln < 8 * (NR / R)) {
+                    const unsigned qi0 = 16 * (unsigned)qt + (unsigned)r0 + R * (ln >> 3), k = ln & 7u;
+                    const float* cw = reinterpret_cast<const float*>(smem + LY::cmb);
+                    float acc[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const u32x4 v = *reinterpret_cast<const u32x4*>(ys + (qi0 + r) * 144 + k * 16);
+                        const float4 w0 = *reinterpret_cast<const float4*>(cw + r * kP + 8 * k);
+                        const float4 w1 = *reinterpret_cast<const float4*>(cw + r * kP + 8 * k + 4);
+                        acc[0] += w0.x * lo_f(v[0]); acc[1] += w0.y * hi_f(v[0]);
+                        acc[2] += w0.z * lo_f(v[1]); acc[3] += w0.w * hi_f(v[1]);
+                        acc[4] += w1.x * lo_f(v[2]); acc[5] += w1.y * hi_f(v[2]);
+                        acc[6] += w1.z * lo_f(v[3]); acc[7] += w1.w * hi_f(v[3]);
+                    }
+                    const u32x4 o = {pack2(acc[0], acc[1]), pack2(acc[2], acc[3]), pack2(acc[4], acc[5]), pack2(acc[6], acc[7])};
+                    __builtin_amdgcn_raw_buffer_store_b128(o, ro, (int)((qi0 / R) * (unsigned)(H * kP * 2) + 16 * k), 0, 0);
+                }
+                return;
+            }
+            const __amdgpu_buffer_rsrc_t ry = make_rsrc(static_cast<uint16_t*>(a.y) + ((tokbase + cst) * H + h) * R * kP,
+                                                        (uint32_t)nv * ysb);
             if (NR == 8 || ln < 8 * NR) {
                 const unsigned qi = 16 * (unsigned)qt + (unsigned)r0 + (ln >> 3);
                 const u32x4 v = *reinterpret_cast<const u32x4*>(ys + qi * 144 + (ln & 7u) * 16);
@@ -1193,7 +1225,12 @@ hipError_t launch_rql(const ScanArgs& a, hipStream_t st) {
 
 template <int R, int Q>
 hipError_t launch_rq(const ScanArgs& a, hipStream_t st) {
-    return a.lift ? launch_rql<R, Q, true>(a, st) : launch_rql<R, Q, false>(a, st);
+    if constexpr (Q <= 64) {                 // the layer variant stages its outputs (Q <= 64)
+        if (a.lift) return launch_rql<R, Q, true>(a, st);
+    } else {
+        if (a.lift) return hipErrorInvalidValue;
+    }
+    return launch_rql<R, Q, false>(a, st);
 }
 
 }  // namespace
