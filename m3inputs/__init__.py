@@ -11,6 +11,7 @@ from .gen import (  # noqa: F401
     bf16_bits,
     bits_to_f32,
     make_block_inputs,
+    make_cotangents,
     make_scan_inputs,
     make_decode_inputs,
     make_small_case,

@@ -204,3 +204,21 @@ def make_block_inputs(cfg: Config, seed=None, *, batch=None, seqlen=None, init=T
     else:
         out["init"] = None
     return out
+
+
+def make_cotangents(cfg: Config, seed=None, *, batch=None, seqlen=None, final=True):
+    """Seeded output cotangents of one scan call (the backward pass's inputs):
+    dy [b,L,H,R,P] ~ N(0,1) rounded to the I/O dtype, and (``final``) float32
+    sensitivities of the final carry: h [b,H,P,N], phi [b,H,npairs],
+    B_prev [b,H,R,N], x_prev [b,H,R,P], each ~ N(0,1) (None without ``final``)."""
+    b = cfg.batch if batch is None else batch
+    L = cfg.seqlen if seqlen is None else seqlen
+    H, P, N, R, NP = cfg.nheads, cfg.headdim, cfg.dstate, cfg.rank, cfg.npairs
+    ss = np.random.SeedSequence(cfg.seed if seed is None else seed, spawn_key=(13,))
+    k = [np.random.Generator(np.random.PCG64(c)) for c in ss.spawn(5)]
+    dy = _round_io(_normal(k[0], (b, L, H, R, P)), cfg.io_dtype)
+    if not final:
+        return dy, None
+    dfin = {"h": _normal(k[1], (b, H, P, N)), "phi": _normal(k[2], (b, H, NP)),
+            "B_prev": _normal(k[3], (b, H, R, N)), "x_prev": _normal(k[4], (b, H, R, P))}
+    return dy, dfin
