@@ -215,6 +215,62 @@ m3_status m3_block_decode_step(const m3_desc* d, const m3_block_params* p,
                                const m3_carry* carry, void* out, void* workspace, size_t workspace_bytes,
                                m3_stream_t stream);
 
+/* ---- Backward pass of the scan -------------------------------------------------------
+ * "Diagonal Equivalence in State Space Models: Characterization, Retrieval Rank, and
+ * Selective Extensions" (paperpeel.com), section 2.5 "Parallel scan and gradients"
+ * (the adjoint recurrence: the state sensitivity runs backward through the transposed
+ * transition; the initial carry's gradient is what is left at the start; a final-state
+ * sensitivity enters as the terminal condition) and appendix C.2 (every carry is
+ * differentiable, so calls on consecutive segments chain their gradients).
+ *
+ * The loss is sum(dy * y) + <dfinal.h, h_L> + <dfinal.phi, phi_L> + <dfinal.B_prev,
+ * B_prev_L> + <dfinal.x_prev, x_prev_L> for the y and final carry that m3_scan_fwd
+ * returns on the same inputs (phi_L before its reduction into [0, 2 pi)). */
+
+/* Sensitivities of (or gradients with respect to) a carry: all float32, any member may
+ * be NULL (a zero sensitivity on input; not written on output). */
+typedef struct {
+    float* h;        /* [b, H, P, N] */
+    float* phi;      /* [b, H, np]   */
+    float* B_prev;   /* [b, H, R, N]  (of the biased, turned B_prev the carry holds) */
+    float* x_prev;   /* [b, H, R, P] */
+} m3_carry_grad;
+
+/* Where m3_scan_bwd writes the gradients (device pointers, overwritten, never
+ * accumulated into; none may overlap another or any input). */
+typedef struct {
+    void*  dx;       /* [b, L, H, R, P] io_dtype                                  required */
+    void*  dB;       /* [b, L, G, R, N] io_dtype, summed over the heads of a group  required */
+    void*  dC;       /* [b, L, G, R, N] io_dtype                                  required */
+    float* ddt;      /* [b, L, H]                                                 required */
+    float* dlam;     /* [b, L, H]                                                 required */
+    float* dtheta;   /* [b, L, H, np]                                 required iff np > 0 */
+    float* dA;       /* [H] d A_log (M3_RATE_STATIC) or [b, L, H] d u (M3_RATE_HEAVY_TAIL)  required */
+    float* dB_bias;  /* [H, R, N], or NULL (not computed) */
+    float* dC_bias;  /* [H, R, N], or NULL */
+    m3_carry_grad dinit;   /* gradients of the initial carry (members may be NULL) */
+} m3_scan_grads;
+
+/* Bytes of device workspace m3_scan_bwd needs for *d (float32 sums of the shared B and
+ * C gradients, per-token angles and replay terms). */
+m3_status m3_scan_bwd_workspace_size(const m3_desc* d, size_t* bytes);
+
+/* Gradients of the scan.  The forward inputs are those of m3_scan_fwd (init may be
+ * NULL: an all-zero carry); dy [b, L, H, R, P] io_dtype; dfinal NULL or the final
+ * carry's sensitivities.  d->chunk and d->nsegments are ignored: the backward replays
+ * the recurrence token by token (fp32 state in registers), so its result does not
+ * depend on the forward's chunking beyond rounding.  Supported: P <= 64, N <= 128,
+ * R <= 4 (M3_ERR_UNSUPPORTED otherwise).  With L == 0 the initial carry's gradients
+ * are the final carry's sensitivities and the parameter gradients are zero.
+ * Asynchronous on stream; the workspace's contents on entry do not matter. */
+m3_status m3_scan_bwd(const m3_desc* d,
+                      const void* x, const void* B, const void* C,
+                      const float* dt, const float* lam, const float* theta,
+                      const float* A_log, const float* B_bias, const float* C_bias,
+                      const m3_carry* init, const void* dy, const m3_carry_grad* dfinal,
+                      const m3_scan_grads* grads, void* workspace, size_t workspace_bytes,
+                      m3_stream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* m3_status_string(m3_status s);
 

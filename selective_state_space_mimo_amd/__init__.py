@@ -10,6 +10,8 @@ not import.
     y, final = scan_fwd(x, B, C, dt, lam, theta, A_log, B_bias, C_bias,
                         init=None, chunk=64)
     y = decode_step(x, B, C, dt, lam, theta, A_log, B_bias, C_bias, carry)
+    grads = scan_bwd(x, B, C, dt, lam, theta, A_log, B_bias, C_bias, init, dy,
+                     dfinal=None)
 
 With ``A_raw=`` (a per-token rate input [b,L,H], or [b,H] for a decode step)
 the decay rate of each token is the heavy-tail law (M3_RATE_HEAVY_TAIL) and
@@ -20,7 +22,7 @@ import os
 
 import torch
 
-__all__ = ["scan_fwd", "decode_step", "scan_workspace_size", "new_carry", "M3Error",
+__all__ = ["scan_fwd", "scan_bwd", "decode_step", "scan_workspace_size", "new_carry", "M3Error",
            "LIB_PATH", "lib", "Desc", "Carry", "M3_F32", "M3_BF16", "M3_RATE_STATIC", "M3_RATE_HEAVY_TAIL"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libm3scan.so")
@@ -173,6 +175,96 @@ def scan_fwd(x, B, C, dt, lam, theta, A_log, B_bias=None, C_bias=None, init=None
                          _ptr(workspace, dev, None, "workspace") if ws_bytes else None, ws_bytes, _stream(dev))
     _check(st, "m3_scan_fwd")
     return y, fin
+
+
+class CarryGrad(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_void_p), ("phi", ctypes.c_void_p),
+                ("B_prev", ctypes.c_void_p), ("x_prev", ctypes.c_void_p)]
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [("dx", ctypes.c_void_p), ("dB", ctypes.c_void_p), ("dC", ctypes.c_void_p),
+                ("ddt", ctypes.c_void_p), ("dlam", ctypes.c_void_p), ("dtheta", ctypes.c_void_p),
+                ("dA", ctypes.c_void_p), ("dB_bias", ctypes.c_void_p), ("dC_bias", ctypes.c_void_p),
+                ("dinit", CarryGrad)]
+
+
+lib.m3_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(_sz)]
+lib.m3_scan_bwd_workspace_size.restype = ctypes.c_int
+lib.m3_scan_bwd.argtypes = [ctypes.POINTER(Desc)] + [_vp] * 9 + [ctypes.POINTER(Carry), _vp, ctypes.POINTER(CarryGrad),
+                                                               ctypes.POINTER(Grads), _vp, _sz, _vp]
+lib.m3_scan_bwd.restype = ctypes.c_int
+
+
+def scan_bwd_workspace_size(desc):
+    n = _sz(0)
+    _check(lib.m3_scan_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(n)), "m3_scan_bwd_workspace_size")
+    return n.value
+
+
+def _carry_grad(c, dev, name):
+    if c is None:
+        return CarryGrad(None, None, None, None)
+    return CarryGrad(*[_ptr(c.get(k), dev, torch.float32, name + "." + k) for k in ("h", "phi", "B_prev", "x_prev")])
+
+
+def scan_bwd(x, B, C, dt, lam, theta, A_log, B_bias, C_bias, init, dy, *, dfinal=None, state_dtype=torch.float32,
+             A_raw=None, grads=None, want_init=True, workspace=None):
+    """Gradients of the scan (``m3_scan_bwd``) for the loss sum(dy * y) plus the
+    final carry's sensitivities ``dfinal`` (dict h, phi, B_prev, x_prev of float32
+    tensors, any missing, or None).
+
+    Forward inputs as for :func:`scan_fwd`.  Returns a dict: x, B, C (I/O dtype),
+    dt, lam, theta (or None), A (d A_log [H], or d A_raw [b,L,H] with ``A_raw``),
+    B_bias, C_bias (None without a bias), init (dict h, phi, B_prev, x_prev of
+    float32, or None without ``want_init``).  ``grads`` may hold preallocated
+    output tensors under the same keys."""
+    dev = x.device
+    io = x.dtype
+    law = M3_RATE_STATIC if A_raw is None else M3_RATE_HEAVY_TAIL
+    desc = make_desc(x, B, theta, state_dtype=state_dtype, rate_law=law)
+    rate = A_log if A_raw is None else A_raw
+    b, L, H, R, P = x.shape
+    G, N = B.shape[2], B.shape[4]
+    npairs = desc.npairs
+    f32 = torch.float32
+    out = dict(grads or {})
+    e = lambda k, shape, dt=f32: out[k] if out.get(k) is not None else torch.empty(shape, dtype=dt, device=dev)  # noqa: E731
+    out["x"] = e("x", x.shape, io)
+    out["B"] = e("B", B.shape, io)
+    out["C"] = e("C", C.shape, io)
+    out["dt"] = e("dt", (b, L, H))
+    out["lam"] = e("lam", (b, L, H))
+    out["theta"] = e("theta", (b, L, H, npairs)) if npairs else None
+    out["A"] = e("A", (b, L, H) if A_raw is not None else (H,))
+    out["B_bias"] = e("B_bias", (H, R, N)) if B_bias is not None else None
+    out["C_bias"] = e("C_bias", (H, R, N)) if C_bias is not None else None
+    if want_init:
+        di = dict(out.get("init") or {})
+        out["init"] = {"h": di.get("h", torch.empty((b, H, P, N), dtype=f32, device=dev)),
+                       "phi": di.get("phi", torch.empty((b, H, npairs), dtype=f32, device=dev)),
+                       "B_prev": di.get("B_prev", torch.empty((b, H, R, N), dtype=f32, device=dev)),
+                       "x_prev": di.get("x_prev", torch.empty((b, H, R, P), dtype=f32, device=dev))}
+    else:
+        out["init"] = None
+    g = Grads(_ptr(out["x"], dev, io, "dx"), _ptr(out["B"], dev, io, "dB"), _ptr(out["C"], dev, io, "dC"),
+              _ptr(out["dt"], dev, f32, "ddt"), _ptr(out["lam"], dev, f32, "dlam"),
+              _ptr(out["theta"], dev, f32, "dtheta"), _ptr(out["A"], dev, f32, "dA"),
+              _ptr(out["B_bias"], dev, f32, "dB_bias"), _ptr(out["C_bias"], dev, f32, "dC_bias"),
+              _carry_grad(out["init"], dev, "dinit"))
+    ws_bytes = scan_bwd_workspace_size(desc)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ci = _carry(init, dev, io, state_dtype)
+    df = _carry_grad(dfinal, dev, "dfinal") if dfinal is not None else None
+    st = lib.m3_scan_bwd(ctypes.byref(desc), _ptr(x, dev, io, "x"), _ptr(B, dev, io, "B"), _ptr(C, dev, io, "C"),
+                         _ptr(dt, dev, f32, "dt"), _ptr(lam, dev, f32, "lam"), _ptr(theta, dev, f32, "theta"),
+                         _ptr(rate, dev, f32, "A_log/A_raw"), _ptr(B_bias, dev, f32, "B_bias"),
+                         _ptr(C_bias, dev, f32, "C_bias"), ctypes.byref(ci) if ci is not None else None,
+                         _ptr(dy, dev, io, "dy"), ctypes.byref(df) if df is not None else None, ctypes.byref(g),
+                         _ptr(workspace, dev, None, "workspace") if ws_bytes else None, ws_bytes, _stream(dev))
+    _check(st, "m3_scan_bwd")
+    return out
 
 
 def decode_step(x, B, C, dt, lam, theta, A_log, B_bias, C_bias, carry, *, y=None, A_raw=None):

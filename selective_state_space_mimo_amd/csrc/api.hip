@@ -431,4 +431,96 @@ m3_status m3_block_decode_step(const m3_desc* d, const m3_block_params* p, const
     return launch_block_epilogue(a, hs) == hipSuccess ? M3_OK : M3_ERR_HIP;
 }
 
+m3_status m3_scan_bwd_workspace_size(const m3_desc* d, size_t* bytes) {
+    if (!bytes) return M3_ERR_INVALID_ARG;
+    m3_status st = check_desc(d, true);
+    if (st != M3_OK) return st;
+    if (!scan_bwd_supported(d->headdim, d->dstate, d->rank, d->npairs)) return M3_ERR_UNSUPPORTED;
+    *bytes = d->seqlen == 0 ? 0
+                            : scan_bwd_workspace(d->batch, d->seqlen, d->nheads, d->ngroups, d->rank, d->dstate,
+                                                 d->npairs).total;
+    return M3_OK;
+}
+
+m3_status m3_scan_bwd(const m3_desc* d, const void* x, const void* B, const void* C, const float* dt,
+                      const float* lam, const float* theta, const float* A_log, const float* B_bias,
+                      const float* C_bias, const m3_carry* init, const void* dy, const m3_carry_grad* dfinal,
+                      const m3_scan_grads* g, void* workspace, size_t workspace_bytes, m3_stream_t stream) {
+    m3_status st = check_desc(d, true);
+    if (st != M3_OK) return st;
+    if (!scan_bwd_supported(d->headdim, d->dstate, d->rank, d->npairs)) return M3_ERR_UNSUPPORTED;
+    if (!g) return M3_ERR_INVALID_ARG;
+    const int L = d->seqlen;
+    const size_t b = d->batch, H = d->nheads, P = d->headdim, N = d->dstate, R = d->rank, np = d->npairs;
+    const Sizes s = sizes(d, L);
+    if (init && (st = check_carry(init, d)) != M3_OK) return st;
+    if (L > 0) {
+        if (!x || !B || !C || !dt || !lam || !A_log || !dy) return M3_ERR_INVALID_ARG;
+        if (np > 0 && !theta) return M3_ERR_INVALID_ARG;
+        if (!g->dx || !g->dB || !g->dC || !g->ddt || !g->dlam || !g->dA) return M3_ERR_INVALID_ARG;
+        if (np > 0 && !g->dtheta) return M3_ERR_INVALID_ARG;
+    }
+    const m3_carry_grad zero{};
+    const m3_carry_grad& df = dfinal ? *dfinal : zero;
+    const void* ptrs[] = {x, B, C, dt, lam, np ? theta : nullptr, A_log, B_bias, C_bias, dy, workspace,
+                          g->dx, g->dB, g->dC, g->ddt, g->dlam, np ? g->dtheta : nullptr, g->dA, g->dB_bias,
+                          g->dC_bias, g->dinit.h, g->dinit.phi, g->dinit.B_prev, g->dinit.x_prev,
+                          df.h, df.phi, df.B_prev, df.x_prev};
+    for (const void* p : ptrs)
+        if (misaligned(p)) return M3_ERR_ALIGNMENT;
+    // inputs (forward inputs, init carry, dy, dfinal) and outputs (every gradient, workspace)
+    const size_t f4 = 4;
+    const BwdWs w = scan_bwd_workspace(d->batch, L, d->nheads, d->ngroups, d->rank, d->dstate, d->npairs);
+    const size_t wsb = L > 0 ? w.total : 0;
+    if (wsb > 0 && (!workspace || workspace_bytes < wsb)) return M3_ERR_INVALID_ARG;
+    Range ri[4] = {};
+    if (init) carry_ranges(init, s, ri);
+    const Range ins[] = {rng(x, s.x), rng(B, s.bc), rng(C, s.bc), rng(dt, s.tok), rng(lam, s.tok),
+                         rng(np ? theta : nullptr, np ? s.theta : 0), rng(A_log, s.alog),
+                         rng(B_bias, B_bias ? s.bias : 0), rng(C_bias, C_bias ? s.bias : 0), rng(dy, s.x),
+                         ri[0], ri[1], ri[2], ri[3],
+                         rng(df.h, df.h ? b * H * P * N * f4 : 0), rng(df.phi, df.phi ? b * H * np * f4 : 0),
+                         rng(df.B_prev, df.B_prev ? b * H * R * N * f4 : 0),
+                         rng(df.x_prev, df.x_prev ? b * H * R * P * f4 : 0)};
+    const Range outs[] = {rng(g->dx, g->dx ? s.x : 0), rng(g->dB, g->dB ? s.bc : 0), rng(g->dC, g->dC ? s.bc : 0),
+                          rng(g->ddt, g->ddt ? s.tok : 0), rng(g->dlam, g->dlam ? s.tok : 0),
+                          rng(np ? g->dtheta : nullptr, np && g->dtheta ? s.theta : 0),
+                          rng(g->dA, g->dA ? s.alog : 0), rng(g->dB_bias, g->dB_bias ? s.bias : 0),
+                          rng(g->dC_bias, g->dC_bias ? s.bias : 0),
+                          rng(g->dinit.h, g->dinit.h ? b * H * P * N * f4 : 0),
+                          rng(g->dinit.phi, g->dinit.phi ? b * H * np * f4 : 0),
+                          rng(g->dinit.B_prev, g->dinit.B_prev ? b * H * R * N * f4 : 0),
+                          rng(g->dinit.x_prev, g->dinit.x_prev ? b * H * R * P * f4 : 0), rng(workspace, wsb)};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return M3_ERR_INVALID_ARG;
+        for (size_t k = i + 1; k < sizeof(outs) / sizeof(outs[0]); ++k)
+            if (overlap(outs[i], outs[k])) return M3_ERR_INVALID_ARG;
+    }
+
+    BwdArgs a{};
+    a.b = d->batch; a.L = L; a.H = d->nheads; a.G = d->ngroups; a.P = d->headdim; a.N = d->dstate;
+    a.R = d->rank; a.np = d->npairs;
+    a.io_bf16 = d->io_dtype == M3_BF16; a.st_bf16 = d->state_dtype == M3_BF16; a.rate_law = d->rate_law;
+    a.x = x; a.B = B; a.C = C; a.dt = dt; a.lam = lam; a.theta = np ? theta : nullptr; a.A = A_log;
+    a.Bb = B_bias; a.Cb = C_bias;
+    if (init) { a.h0 = init->h; a.phi0 = np ? init->phi : nullptr; a.Bp0 = init->B_prev; a.xp0 = init->x_prev; }
+    a.dy = dy;
+    a.dh1 = df.h; a.dphi1 = np ? df.phi : nullptr; a.dBp1 = df.B_prev; a.dxp1 = df.x_prev;
+    a.dx = g->dx; a.ddt = g->ddt; a.dlam = g->dlam; a.dtheta = np ? g->dtheta : nullptr; a.dA = g->dA;
+    a.dBb = g->dB_bias; a.dCb = g->dC_bias;
+    a.dh0 = g->dinit.h; a.dphi0 = np ? g->dinit.phi : nullptr; a.dBp0 = g->dinit.B_prev; a.dxp0 = g->dinit.x_prev;
+    if (L > 0) {
+        char* base = static_cast<char*>(workspace);
+        a.accB = reinterpret_cast<float*>(base + w.accB);
+        a.accC = reinterpret_cast<float*>(base + w.accC);
+        a.wphi = reinterpret_cast<float*>(base + w.phi);
+        a.wdphi = reinterpret_cast<float*>(base + w.dphi);
+        a.wdl = reinterpret_cast<float*>(base + w.dl);
+        a.wdlf = reinterpret_cast<float*>(base + w.dlf);
+    }
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    return launch_scan_bwd(a, g->dB, g->dC, hs) == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
 }  // extern "C"

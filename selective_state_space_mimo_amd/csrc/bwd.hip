@@ -1,0 +1,706 @@
+// Backward pass of the scan: the gradients of a loss with respect to every input of
+// the scan (x, B, C, dt, lambda, theta, the rate input, the biases and the initial
+// carry), given the loss's gradients with respect to its outputs (dy and, optionally,
+// the final carry).
+//
+// "Diagonal Equivalence in State Space Models: Characterization, Retrieval Rank, and
+// Selective Extensions" (paperpeel.com), section 2.5 "Parallel scan and gradients":
+// the state sensitivity G_t = d loss / d H_t runs backward through the transposed
+// transition (a scalar decay here), G_t = alpha_{t+1} G_{t+1} + sum_r dy_t[r] (x) Ct_t[r];
+// the initial carry's gradient is what is left at the start; a sensitivity for the
+// final state enters as the terminal condition (section 5.5 and appendix C.2: every
+// carry is differentiable).  The recurrence differentiated is the three-term update
+// of "Mamba-3: Improved Sequence Modeling using State Space Principles"
+// (intuitivepapers.ai), sections "How the exponential-trapezoidal update works",
+// "Computing the rotation as a data-dependent RoPE" and "MIMO: a rank-4 state update".
+//
+// Two sweeps per (batch, head) stream, one workgroup (4 waves) each; the P x N fp32
+// state (P <= 64, N <= 128) lives in registers: wave w holds rows 16 w .. 16 w + 15,
+// lane (lg = lane / 16, l16 = lane % 16) rows 16 w + 4 lg + v (v < 4) of columns
+// 16 nt + l16 (nt < 8).  Tokens are staged kT at a time in LDS; the per-token work is
+// wave-local (no barrier), the per-token outputs are formed after each group.
+//
+//   replay (forward): H_t again, token by token (never stored), read against dy:
+//     dCt_t[r] = H_t^T dy_t[r], <dy_t, y_t> = sum_r Ct_t[r] . dCt_t[r]; the running
+//     angles phi_t (kept for the reverse sweep) and the C side of the angle gradient.
+//   adjoint (reverse): G from the last token back, with per token
+//     v[r] = G_{t+1} Bt_t[r] (P values) and w[r] = G_{t+1}^T X_t[r] (N values);
+//     with K_t = sum_r dy_t[r] (x) Ct_t[r] and G_t = alpha_{t+1} G_{t+1} + K_t:
+//       dX_t  = (gamma_t alpha_{t+1} + beta_{t+1}) v + gamma_t K_t Bt_t   (+ d x_prev at the end)
+//       dBt_t = (gamma_t alpha_{t+1} + beta_{t+1}) w + gamma_t K_t^T X_t  (+ d B_prev at the end)
+//       d gamma_t = alpha_{t+1} X_t . v + sum_{r,r'} (dy_t[r'] . X_t[r]) (Ct_t[r'] . Bt_t[r])
+//       d beta_{t+1} = X_t . v
+//     (the K_t terms are R x R dot products: no second pass over the state).
+// The decay's gradient uses the cumulative log-decay l_t = sum_{k <= t} log alpha_k:
+// l_k multiplies every term read at k and divides every term written at k, so
+//   d loss / d l_k = <dy_k, y_k> (+ <dH_L, H_L> at the last token) - <dX_k, X_k>_writes
+// with <dX_k, X_k>_writes = gamma_k d gamma_k + beta_{k+1} d beta_{k+1}, and
+// d loss / d log alpha_t = sum_{k >= t} d loss / d l_k: the reverse sweep never needs H_t.
+// Shared B and C (G < H): the per-head gradients are summed into fp32 buffers by
+// atomic adds and converted to the I/O dtype at the end.
+#include <algorithm>
+
+#include "m3_internal.h"
+
+namespace m3 {
+
+namespace {
+
+constexpr int kT = 8;                 // tokens per staged group
+constexpr int kR4 = 4, kPP = 64, kNN = 128, kThreads = 256;
+
+// turned B and C rows are kept with column n at (n % 16) * 8 + n / 16, so that a lane's
+// eight columns 16 nt + l16 are one 32-byte run
+__device__ __forceinline__ int colpos(int n) { return (n & 15) * 8 + (n >> 4); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// involutions inside a row of 16 lanes pairing the two halves of each level
+template <int LEVEL>
+__device__ __forceinline__ float row_partner(float v) {
+    if constexpr (LEVEL == 8) return dpp_mov<0x140>(v);        // row mirror
+    else if constexpr (LEVEL == 4) return dpp_mov<0x141>(v);   // row half mirror
+    else if constexpr (LEVEL == 2) return dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+    else return dpp_mov<0xB1>(v);                              // quad_perm [1,0,3,2]
+}
+template <int LEVEL, int CNT>
+__device__ __forceinline__ void rs_row_level(float* v, bool up) {
+    constexpr int HALF = CNT / 2;
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) {
+        const float keep = up ? v[i + HALF] : v[i];
+        const float send = up ? v[i] : v[i + HALF];
+        v[i] = keep + row_partner<LEVEL>(send);
+    }
+}
+// Sum of v[16] over the 16 lanes of a row, scattered: lane l16 returns entry l16.
+__device__ __forceinline__ float rs_row16(float (&v)[16], int l16) {
+    rs_row_level<8, 16>(v, l16 & 8);
+    rs_row_level<4, 8>(v, l16 & 4);
+    rs_row_level<2, 4>(v, l16 & 2);
+    rs_row_level<1, 2>(v, l16 & 1);
+    return v[0];
+}
+// Sum of part[r][nt] over the four 16-lane groups, scattered: group lg keeps tiles
+// nt = 2 lg + i (i < 2) in out[r][i].
+template <int R>
+__device__ __forceinline__ void rs_groups(const float (&part)[R][8], float (&out)[R][2], int lg) {
+    const bool h2 = lg & 2, h1 = lg & 1;
+    float k4[R][4];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float keep = h2 ? part[r][4 + i] : part[r][i];
+            const float send = h2 ? part[r][i] : part[r][4 + i];
+            k4[r][i] = keep + __shfl_xor(send, 32);
+        }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float keep = h1 ? k4[r][2 + i] : k4[r][i];
+            const float send = h1 ? k4[r][i] : k4[r][2 + i];
+            out[r][i] = keep + __shfl_xor(send, 16);
+        }
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    return v;
+}
+// Sum of v[8] over the wave, scattered: lanes with lane % 8 == 0 return entry
+// 4 (lane >> 5 & 1) + 2 (lane >> 4 & 1) + (lane >> 3 & 1).
+__device__ __forceinline__ float rs_wave8(float (&v)[8], int lane) {
+    float a[4], b[2];
+    const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = (h5 ? v[4 + i] : v[i]) + __shfl_xor(h5 ? v[i] : v[4 + i], 32);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) b[i] = (h4 ? a[2 + i] : a[i]) + __shfl_xor(h4 ? a[i] : a[2 + i], 16);
+    float c = (h3 ? b[1] : b[0]) + __shfl_xor(h3 ? b[0] : b[1], 8);
+    c += __shfl_xor(c, 4);
+    c += __shfl_xor(c, 2);
+    c += __shfl_xor(c, 1);
+    return c;
+}
+__device__ __forceinline__ void lds_add(float* p, float v) {
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+__device__ __forceinline__ float rate_of(const BwdArgs& a, int h, size_t tok_h) {
+    return a.rate_law ? heavy_tail_rate(a.A[tok_h]) : -expf(a.A[h]);
+}
+// d rate / d u of the heavy-tail law (0 where the clamp at -1e-4 holds)
+__device__ __forceinline__ float heavy_tail_rate_grad(float u) {
+    const float ht = u >= 0.f ? 1.f + u : 1.f / (1.f - u);
+    const float d = u >= 0.f ? 1.f : 1.f / ((1.f - u) * (1.f - u));
+    return -ht < -1e-4f ? -d : 0.f;
+}
+
+// One staged token pair (rank r, pair j) of B or C: biased, turned by (c, s).
+__device__ __forceinline__ float2 turned_pair(const void* M, size_t idx, int io_bf16, float bias0, float bias1,
+                                              bool turns, float c, float s) {
+    const float m0 = ld_io(M, idx, io_bf16) + bias0, m1 = ld_io(M, idx + 1, io_bf16) + bias1;
+    if (!turns) return make_float2(m0, m1);
+    return make_float2(m0 * c - m1 * s, m0 * s + m1 * c);
+}
+
+// ============================== forward replay ==============================
+template <int R>
+__global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
+    __shared__ __align__(16) float sX[kT + 1][kR4][kPP];     // slot 0: the previous token's x
+    __shared__ __align__(16) float sBt[kT + 1][kR4][kNN];    // turned B (column order colpos); slot 0: previous
+    __shared__ __align__(16) float sDY[kT][kR4][kPP];
+    __shared__ __align__(16) float sCt[kT][kR4][kNN];        // turned C (colpos)
+    __shared__ float sDC[kT][kR4][kNN];        // dCt (natural column order), summed over waves
+    __shared__ float sDPH[kT][64];
+    __shared__ float sDL[kT];
+    __shared__ float sAl[kT], sBe[kT], sGa[kT];
+    __shared__ float sRed[4];
+
+    const int bh = blockIdx.x, H = a.H, bi = bh / H, h = bh % H, g = h * a.G / H;
+    const int L = a.L, P = a.P, N = a.N, np = a.np, io = a.io_bf16;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lg = lane >> 4, l16 = lane & 15;
+    // staging / output role: rank r = w, pair j (columns 2 j, 2 j + 1) and row j
+    const int r = w, j = lane;
+    const bool pok = r < R && 2 * j < N, xok = r < R && j < P, turns = pok && j < np;
+    const int prow = 16 * w + 4 * lg;
+
+    float S[4][8];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            const int p = prow + v, n = 16 * nt + l16;
+            S[v][nt] = (a.h0 && p < P && n < N) ? ld_io(a.h0, ((size_t)bh * P + p) * N + n, a.st_bf16) : 0.f;
+        }
+    float bb0 = 0.f, bb1 = 0.f, cb0 = 0.f, cb1 = 0.f;
+    if (pok && a.Bb) { bb0 = a.Bb[((size_t)h * R + r) * N + 2 * j]; bb1 = a.Bb[((size_t)h * R + r) * N + 2 * j + 1]; }
+    if (pok && a.Cb) { cb0 = a.Cb[((size_t)h * R + r) * N + 2 * j]; cb1 = a.Cb[((size_t)h * R + r) * N + 2 * j + 1]; }
+    float phi = (turns && a.phi0) ? a.phi0[(size_t)bh * np + j] : 0.f;
+    float gC0 = 0.f, gC1 = 0.f;                 // C bias gradient partials
+    // slot 0: the carried previous write (x_prev, turned B_prev)
+    sX[0][r][j] = (xok && a.xp0) ? ld_io(a.xp0, ((size_t)bh * R + r) * P + j, io) : 0.f;
+    {
+        const bool ok = pok && a.Bp0;
+        sBt[0][r][colpos(2 * j)] = ok ? ld_io(a.Bp0, ((size_t)bh * R + r) * N + 2 * j, io) : 0.f;
+        sBt[0][r][colpos(2 * j + 1)] = ok ? ld_io(a.Bp0, ((size_t)bh * R + r) * N + 2 * j + 1, io) : 0.f;
+    }
+
+    for (int t0 = 0; t0 < L; t0 += kT) {
+        const int nv = min(kT, L - t0);
+        // ---- stage kT tokens: angles, turned B and C, x, dy, per-token scalars ----
+        float cs[kT], sn[kT];
+#pragma unroll
+        for (int k = 0; k < kT; ++k) {
+            const bool valid = k < nv;
+            const size_t tok = (size_t)bi * L + t0 + k;
+            cs[k] = 1.f; sn[k] = 0.f;
+            if (valid && turns) {
+                const float dtv = a.dt[tok * H + h];
+                phi = wrap_2pi(phi + dtv * a.theta[(tok * H + h) * np + j]);
+                sincosf(phi, &sn[k], &cs[k]);
+                if (r == 0) a.wphi[(tok * H + h) * np + j] = phi;
+            }
+            float2 bt = make_float2(0.f, 0.f), ct = bt;
+            if (valid && pok) {
+                const size_t bc = ((tok * a.G + g) * R + r) * N + 2 * j;
+                bt = turned_pair(a.B, bc, io, bb0, bb1, turns, cs[k], sn[k]);
+                ct = turned_pair(a.C, bc, io, cb0, cb1, turns, cs[k], sn[k]);
+            }
+            sBt[k + 1][r][colpos(2 * j)] = bt.x;
+            sBt[k + 1][r][colpos(2 * j + 1)] = bt.y;
+            sCt[k][r][colpos(2 * j)] = ct.x;
+            sCt[k][r][colpos(2 * j + 1)] = ct.y;
+            const size_t xi = ((tok * H + h) * R + r) * P + j;
+            sX[k + 1][r][j] = (valid && xok) ? ld_io(a.x, xi, io) : 0.f;
+            sDY[k][r][j] = (valid && xok) ? ld_io(a.dy, xi, io) : 0.f;
+            sDC[k][r][2 * j] = 0.f;
+            sDC[k][r][2 * j + 1] = 0.f;
+            if (w == 0) sDPH[k][j] = 0.f;
+        }
+        if (tid < kT) {
+            float al = 1.f, be = 0.f, ga = 0.f;
+            if (tid < nv) {
+                const size_t th = ((size_t)bi * L + t0 + tid) * H + h;
+                const float dtv = a.dt[th], lm = a.lam[th];
+                al = expf(dtv * rate_of(a, h, th));
+                be = al * dtv * (1.f - lm);
+                ga = lm * dtv;
+            }
+            sAl[tid] = al; sBe[tid] = be; sGa[tid] = ga;
+            sDL[tid] = 0.f;
+        }
+        __syncthreads();
+        // ---- per token (wave-local): H_t, then dCt_t = H_t^T dy_t ----
+        for (int k = 0; k < nv; ++k) {
+            const float al = sAl[k], be = sBe[k], ga = sGa[k];
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) S[v][nt] *= al;
+#pragma unroll
+            for (int q = 0; q < R; ++q) {
+                const float4 xp = ld4(&sX[k][q][prow]), xc = ld4(&sX[k + 1][q][prow]);
+                const float4 p0 = ld4(&sBt[k][q][l16 * 8]), p1 = ld4(&sBt[k][q][l16 * 8 + 4]);
+                const float4 c0 = ld4(&sBt[k + 1][q][l16 * 8]), c1 = ld4(&sBt[k + 1][q][l16 * 8 + 4]);
+                const float bp[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+                const float bc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+                const float ap[4] = {be * xp.x, be * xp.y, be * xp.z, be * xp.w};
+                const float ac[4] = {ga * xc.x, ga * xc.y, ga * xc.z, ga * xc.w};
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+#pragma unroll
+                    for (int nt = 0; nt < 8; ++nt) S[v][nt] = fmaf(ap[v], bp[nt], fmaf(ac[v], bc[nt], S[v][nt]));
+            }
+            float part[R][8];
+#pragma unroll
+            for (int q = 0; q < R; ++q) {
+                const float4 d = ld4(&sDY[k][q][prow]);
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt)
+                    part[q][nt] = S[0][nt] * d.x + S[1][nt] * d.y + S[2][nt] * d.z + S[3][nt] * d.w;
+            }
+            float red[R][2];
+            rs_groups<R>(part, red, lg);
+#pragma unroll
+            for (int q = 0; q < R; ++q)
+#pragma unroll
+                for (int i = 0; i < 2; ++i) lds_add(&sDC[k][q][16 * (2 * lg + i) + l16], red[q][i]);
+        }
+        __syncthreads();
+        // ---- per token outputs: dC (turned back), bias partials, angle and <dy, y> terms ----
+        for (int k = 0; k < nv; ++k) {
+            const size_t tok = (size_t)bi * L + t0 + k;
+            float dl = 0.f;
+            if (pok) {
+                const float d0 = sDC[k][r][2 * j], d1 = sDC[k][r][2 * j + 1];
+                const float c0 = sCt[k][r][colpos(2 * j)], c1 = sCt[k][r][colpos(2 * j + 1)];
+                dl = c0 * d0 + c1 * d1;
+                float e0 = d0, e1 = d1;
+                if (turns) {
+                    lds_add(&sDPH[k][j], -d0 * c1 + d1 * c0);
+                    e0 = d0 * cs[k] + d1 * sn[k];
+                    e1 = -d0 * sn[k] + d1 * cs[k];
+                }
+                float* acc = a.accC + ((tok * a.G + g) * R + r) * N + 2 * j;
+                unsafeAtomicAdd(acc, e0);
+                unsafeAtomicAdd(acc + 1, e1);
+                gC0 += e0;
+                gC1 += e1;
+            }
+            dl = wave_sum(dl);
+            if (lane == 0 && r < R) lds_add(&sDL[k], dl);
+        }
+        __syncthreads();
+        if (w == 0 && j < np)
+            for (int k = 0; k < nv; ++k) a.wdphi[(((size_t)bi * L + t0 + k) * H + h) * np + j] = sDPH[k][j];
+        if (tid < nv) a.wdl[((size_t)bi * L + t0 + tid) * H + h] = sDL[tid];
+        // the group's last token is the next group's previous write
+        sX[0][r][j] = sX[nv][r][j];
+        sBt[0][r][2 * j] = sBt[nv][r][2 * j];
+        sBt[0][r][2 * j + 1] = sBt[nv][r][2 * j + 1];
+        __syncthreads();
+    }
+    // <dH_L, H_L>, the final state's reader term of the last token
+    float fin = 0.f;
+    if (a.dh1) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) {
+                const int p = prow + v, n = 16 * nt + l16;
+                if (p < P && n < N) fin += S[v][nt] * a.dh1[((size_t)bh * P + p) * N + n];
+            }
+    }
+    fin = wave_sum(fin);
+    if (lane == 0) sRed[w] = fin;
+    __syncthreads();
+    if (tid == 0) a.wdlf[bh] = sRed[0] + sRed[1] + sRed[2] + sRed[3];
+    if (pok && a.dCb) {
+        unsafeAtomicAdd(a.dCb + ((size_t)h * R + r) * N + 2 * j, gC0);
+        unsafeAtomicAdd(a.dCb + ((size_t)h * R + r) * N + 2 * j + 1, gC1);
+    }
+}
+
+// ============================== reverse adjoint ==============================
+// v and w of one token against the state S (G_{t+1}): v[r][row] stored to sv, w summed
+// into sw (both [R4][..] rows of that token)
+template <int R>
+__device__ __forceinline__ void contract(const float (&S)[4][8], const float (*sx)[kPP], const float (*sb)[kNN],
+                                         float (*sv)[kPP], float (*sw)[kNN], int prow, int lg, int l16) {
+    float vp[16];
+    float wp[R][8];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) vp[i] = 0.f;
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const float4 b0 = ld4(&sb[q][l16 * 8]), b1 = ld4(&sb[q][l16 * 8 + 4]);
+        const float bq[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        const float4 xv = ld4(&sx[q][prow]);
+        const float xq[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float s = 0.f;
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) s = fmaf(S[v][nt], bq[nt], s);
+            vp[4 * q + v] = s;
+        }
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+            wp[q][nt] = S[0][nt] * xq[0] + S[1][nt] * xq[1] + S[2][nt] * xq[2] + S[3][nt] * xq[3];
+    }
+    const float vr = rs_row16(vp, l16);
+    const int q = l16 >> 2;
+    if (q < R) sv[q][prow + (l16 & 3)] = vr;
+    float red[R][2];
+    rs_groups<R>(wp, red, lg);
+#pragma unroll
+    for (int qq = 0; qq < R; ++qq)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) lds_add(&sw[qq][16 * (2 * lg + i) + l16], red[qq][i]);
+}
+
+template <int R>
+__global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
+    __shared__ __align__(16) float sX[kT][kR4][kPP];
+    __shared__ __align__(16) float sBt[kT][kR4][kNN];        // turned B (colpos)
+    __shared__ __align__(16) float sDY[kT][kR4][kPP];
+    __shared__ __align__(16) float sCt[kT][kR4][kNN];        // turned C (colpos)
+    __shared__ float sV[kT][kR4][kPP];         // v = G_{t+1} Bt_t
+    __shared__ float sW[kT][kR4][kNN];         // w = G_{t+1}^T X_t (natural order)
+    __shared__ float sDot[kT][kR4][8];         // [r][r'] = Ct[r'] . Bt[r], [r][4 + r'] = dy[r'] . X[r]
+    __shared__ float sXV[kT];                  // X_t . v
+    __shared__ float sDPH[kT][64];
+    __shared__ float sAl[kT + 1], sBe[kT + 1], sGa[kT + 1], sDt[kT + 1], sLm[kT + 1], sRt[kT + 1], sU[kT + 1];
+
+    const int bh = blockIdx.x, H = a.H, bi = bh / H, h = bh % H, g = h * a.G / H;
+    const int L = a.L, P = a.P, N = a.N, np = a.np, io = a.io_bf16;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lg = lane >> 4, l16 = lane & 15;
+    const int r = w, j = lane;
+    const bool pok = r < R && 2 * j < N, xok = r < R && j < P, turns = pok && j < np;
+    const int prow = 16 * w + 4 * lg;
+
+    float S[4][8];                             // G_{t+1}: the final state's sensitivity first
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            const int p = prow + v, n = 16 * nt + l16;
+            S[v][nt] = (a.dh1 && p < P && n < N) ? a.dh1[((size_t)bh * P + p) * N + n] : 0.f;
+        }
+    float bb0 = 0.f, bb1 = 0.f, cb0 = 0.f, cb1 = 0.f;
+    if (pok && a.Bb) { bb0 = a.Bb[((size_t)h * R + r) * N + 2 * j]; bb1 = a.Bb[((size_t)h * R + r) * N + 2 * j + 1]; }
+    if (pok && a.Cb) { cb0 = a.Cb[((size_t)h * R + r) * N + 2 * j]; cb1 = a.Cb[((size_t)h * R + r) * N + 2 * j + 1]; }
+    float gB0 = 0.f, gB1 = 0.f;                // B bias gradient partials
+    // wave 0, lane j < np: the angle sensitivity sum_{k >= t} d loss / d phi_k
+    float Phi = (w == 0 && j < np && a.dphi1) ? a.dphi1[(size_t)bh * np + j] : 0.f;
+    // lane 0 of wave 0: the scalar chain (running log-decay sensitivity, token t+1's
+    // pending step / blend gradients, the static rate's sum)
+    float Sl = 0.f, pend_dt = 0.f, pend_lm = 0.f, dA_sum = 0.f;
+
+    for (int t0 = ((L - 1) / kT) * kT; t0 >= 0; t0 -= kT) {
+        const int nv = min(kT, L - t0);
+        float cs[kT], sn[kT];
+#pragma unroll
+        for (int k = 0; k < kT; ++k) {
+            const bool valid = k < nv;
+            const size_t tok = (size_t)bi * L + t0 + k;
+            cs[k] = 1.f; sn[k] = 0.f;
+            if (valid && turns) sincosf(a.wphi[(tok * H + h) * np + j], &sn[k], &cs[k]);
+            float2 bt = make_float2(0.f, 0.f), ct = bt;
+            if (valid && pok) {
+                const size_t bc = ((tok * a.G + g) * R + r) * N + 2 * j;
+                bt = turned_pair(a.B, bc, io, bb0, bb1, turns, cs[k], sn[k]);
+                ct = turned_pair(a.C, bc, io, cb0, cb1, turns, cs[k], sn[k]);
+            }
+            sBt[k][r][colpos(2 * j)] = bt.x;
+            sBt[k][r][colpos(2 * j + 1)] = bt.y;
+            sCt[k][r][colpos(2 * j)] = ct.x;
+            sCt[k][r][colpos(2 * j + 1)] = ct.y;
+            const size_t xi = ((tok * H + h) * R + r) * P + j;
+            sX[k][r][j] = (valid && xok) ? ld_io(a.x, xi, io) : 0.f;
+            sDY[k][r][j] = (valid && xok) ? ld_io(a.dy, xi, io) : 0.f;
+            sW[k][r][2 * j] = 0.f;
+            sW[k][r][2 * j + 1] = 0.f;
+            if (w == 0) sDPH[k][j] = 0.f;
+        }
+        if (tid <= kT) {
+            // slot kT is token t0 + kT (the first of the group done before), or past the end:
+            // there alpha = 1 and beta = 0 stand for the final carry
+            float al = 1.f, be = 0.f, ga = 0.f, dtv = 0.f, lm = 0.f, rt = 0.f, u = 0.f;
+            if (t0 + tid < L) {
+                const size_t th = ((size_t)bi * L + t0 + tid) * H + h;
+                dtv = a.dt[th]; lm = a.lam[th];
+                u = a.rate_law ? a.A[th] : 0.f;
+                rt = rate_of(a, h, th);
+                al = expf(dtv * rt);
+                be = al * dtv * (1.f - lm);
+                ga = lm * dtv;
+            }
+            sAl[tid] = al; sBe[tid] = be; sGa[tid] = ga; sDt[tid] = dtv; sLm[tid] = lm; sRt[tid] = rt; sU[tid] = u;
+            if (tid < kT) sXV[tid] = 0.f;
+        }
+        __syncthreads();
+        // ---- per token, last first (wave-local): v, w against G_{t+1}, then G_t ----
+        for (int k = nv - 1; k >= 0; --k) {
+            contract<R>(S, sX[k], sBt[k], sV[k], sW[k], prow, lg, l16);
+            const float al1 = sAl[k + 1];
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) S[v][nt] *= al1;
+#pragma unroll
+            for (int q = 0; q < R; ++q) {
+                const float4 d = ld4(&sDY[k][q][prow]);
+                const float dq[4] = {d.x, d.y, d.z, d.w};
+                const float4 c0 = ld4(&sCt[k][q][l16 * 8]), c1 = ld4(&sCt[k][q][l16 * 8 + 4]);
+                const float cq[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+#pragma unroll
+                    for (int nt = 0; nt < 8; ++nt) S[v][nt] = fmaf(dq[v], cq[nt], S[v][nt]);
+            }
+        }
+        __syncthreads();
+        // ---- per token R x R dot products and X . v ----
+        for (int k = 0; k < nv; ++k) {
+            if (r < R) {
+                float d8[8];
+                const float b0 = sBt[k][r][colpos(2 * j)], b1 = sBt[k][r][colpos(2 * j + 1)];
+                const float xr = sX[k][r][j];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    d8[q] = (q < R && pok) ? sCt[k][q][colpos(2 * j)] * b0 + sCt[k][q][colpos(2 * j + 1)] * b1 : 0.f;
+                    d8[4 + q] = (q < R && xok) ? sDY[k][q][j] * xr : 0.f;
+                }
+                const float d = rs_wave8(d8, lane);
+                if ((lane & 7) == 0) sDot[k][r][lane >> 3] = d;
+                const float xv = wave_sum(xok ? xr * sV[k][r][j] : 0.f);
+                if (lane == 0) lds_add(&sXV[k], xv);
+            }
+        }
+        __syncthreads();
+        // ---- per token outputs: dx, dB (turned back), bias partials, angle terms ----
+        for (int k = 0; k < nv; ++k) {
+            const int t = t0 + k;
+            const size_t tok = (size_t)bi * L + t;
+            const bool last = t == L - 1;
+            const float ga = sGa[k], kap = ga * sAl[k + 1] + sBe[k + 1];
+            if (xok) {
+                float dxv = kap * sV[k][r][j];
+#pragma unroll
+                for (int q = 0; q < R; ++q) dxv = fmaf(ga * sDY[k][q][j], sDot[k][r][q], dxv);
+                if (last && a.dxp1) dxv += a.dxp1[((size_t)bh * R + r) * P + j];
+                st_io(a.dx, ((tok * H + h) * R + r) * P + j, dxv, io);
+            }
+            if (pok) {
+                float d0 = kap * sW[k][r][2 * j], d1 = kap * sW[k][r][2 * j + 1];
+#pragma unroll
+                for (int q = 0; q < R; ++q) {
+                    const float m = ga * sDot[k][r][4 + q];
+                    d0 = fmaf(m, sCt[k][q][colpos(2 * j)], d0);
+                    d1 = fmaf(m, sCt[k][q][colpos(2 * j + 1)], d1);
+                }
+                if (last && a.dBp1) {
+                    d0 += a.dBp1[((size_t)bh * R + r) * N + 2 * j];
+                    d1 += a.dBp1[((size_t)bh * R + r) * N + 2 * j + 1];
+                }
+                float e0 = d0, e1 = d1;
+                if (turns) {
+                    const float b0 = sBt[k][r][colpos(2 * j)], b1 = sBt[k][r][colpos(2 * j + 1)];
+                    lds_add(&sDPH[k][j], -d0 * b1 + d1 * b0);
+                    e0 = d0 * cs[k] + d1 * sn[k];
+                    e1 = -d0 * sn[k] + d1 * cs[k];
+                }
+                float* acc = a.accB + ((tok * a.G + g) * R + r) * N + 2 * j;
+                unsafeAtomicAdd(acc, e0);
+                unsafeAtomicAdd(acc + 1, e1);
+                gB0 += e0;
+                gB1 += e1;
+            }
+        }
+        __syncthreads();
+        // ---- wave 0: angle sensitivities, then lane 0's scalar chain, last token first ----
+        if (w == 0) {
+            for (int k = nv - 1; k >= 0; --k) {
+                const int t = t0 + k;
+                const size_t th = ((size_t)bi * L + t) * H + h;
+                float tp = 0.f;
+                if (j < np) {
+                    Phi += sDPH[k][j] + a.wdphi[th * np + j];
+                    a.dtheta[th * np + j] = sDt[k] * Phi;
+                    tp = a.theta[th * np + j] * Phi;
+                }
+                tp = wave_sum(tp);
+                if (lane == 0) {
+                    float dots = 0.f;
+#pragma unroll
+                    for (int q = 0; q < R; ++q)
+#pragma unroll
+                        for (int q2 = 0; q2 < R; ++q2) dots += sDot[k][q][q2] * sDot[k][q][4 + q2];
+                    const bool has_next = t + 1 < L;
+                    const float al1 = sAl[k + 1], be1 = sBe[k + 1];
+                    const float dbe1 = has_next ? sXV[k] : 0.f;       // d beta_{t+1}
+                    const float dga = al1 * sXV[k] + dots;             // d gamma_t
+                    float dl = a.wdl[th] - sGa[k] * dga - be1 * dbe1;
+                    if (t == L - 1) dl += a.wdlf[bh];
+                    Sl += dl;                                          // d loss / d log alpha_t
+                    if (has_next) {
+                        const float dde = al1 * dbe1;                  // beta = alpha delta
+                        a.ddt[th + H] = pend_dt + (1.f - sLm[k + 1]) * dde;
+                        a.dlam[th + H] = pend_lm - sDt[k + 1] * dde;
+                    }
+                    pend_dt = sRt[k] * Sl + sLm[k] * dga + tp;
+                    pend_lm = sDt[k] * dga;
+                    const float dA = sDt[k] * Sl;                      // log alpha = dt A
+                    if (a.rate_law) a.dA[th] = dA * heavy_tail_rate_grad(sU[k]);
+                    else dA_sum += dA;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // ---- the carried previous write at t = 0 (x_prev, turned B_prev) against G_0 ----
+    if (L > 0) {
+        sX[0][r][j] = (xok && a.xp0) ? ld_io(a.xp0, ((size_t)bh * R + r) * P + j, io) : 0.f;
+        const bool ok = pok && a.Bp0;
+        sBt[0][r][colpos(2 * j)] = ok ? ld_io(a.Bp0, ((size_t)bh * R + r) * N + 2 * j, io) : 0.f;
+        sBt[0][r][colpos(2 * j + 1)] = ok ? ld_io(a.Bp0, ((size_t)bh * R + r) * N + 2 * j + 1, io) : 0.f;
+        sW[0][r][2 * j] = 0.f;
+        sW[0][r][2 * j + 1] = 0.f;
+        if (tid == 0) sXV[0] = 0.f;
+        __syncthreads();
+        contract<R>(S, sX[0], sBt[0], sV[0], sW[0], prow, lg, l16);
+        __syncthreads();
+        // sAl[0], sBe[0], ... still hold token 0 (the last group staged)
+        const float al0 = sAl[0], be0 = sBe[0];
+        if (r < R) {
+            const float xv = wave_sum(xok ? sX[0][r][j] * sV[0][r][j] : 0.f);
+            if (lane == 0) lds_add(&sXV[0], xv);
+        }
+        if (xok && a.dxp0) a.dxp0[((size_t)bh * R + r) * P + j] = be0 * sV[0][r][j];
+        if (pok && a.dBp0) {
+            a.dBp0[((size_t)bh * R + r) * N + 2 * j] = be0 * sW[0][r][2 * j];
+            a.dBp0[((size_t)bh * R + r) * N + 2 * j + 1] = be0 * sW[0][r][2 * j + 1];
+        }
+        if (a.dh0) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) {
+                    const int p = prow + v, n = 16 * nt + l16;
+                    if (p < P && n < N) a.dh0[((size_t)bh * P + p) * N + n] = al0 * S[v][nt];
+                }
+        }
+        __syncthreads();
+        if (tid == 0) {
+            const size_t th = (size_t)bi * L * H + h;                 // token 0
+            const float dde = al0 * sXV[0];
+            a.ddt[th] = pend_dt + (1.f - sLm[0]) * dde;
+            a.dlam[th] = pend_lm - sDt[0] * dde;
+            if (!a.rate_law) unsafeAtomicAdd(a.dA + h, dA_sum * -expf(a.A[h]));
+        }
+    }
+    if (w == 0 && j < np && a.dphi0) a.dphi0[(size_t)bh * np + j] = Phi;
+    if (pok && a.dBb) {
+        unsafeAtomicAdd(a.dBb + ((size_t)h * R + r) * N + 2 * j, gB0);
+        unsafeAtomicAdd(a.dBb + ((size_t)h * R + r) * N + 2 * j + 1, gB1);
+    }
+}
+
+__global__ void fill_zero_kernel(float* p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0.f;
+}
+__global__ void copy_f32_kernel(const float* src, float* dst, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        dst[i] = src ? src[i] : 0.f;
+}
+__global__ void acc_convert_kernel(const float* acc, void* out, size_t n, int io_bf16) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        st_io(out, i, acc[i], io_bf16);
+}
+hipError_t fill_zero(float* p, size_t n, hipStream_t s) {
+    if (!p || n == 0) return hipSuccess;
+    const int blocks = (int)std::min<size_t>((n + 255) / 256, 8192);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+template <int R>
+hipError_t launch_r(const BwdArgs& a, hipStream_t s) {
+    const dim3 grid((unsigned)(a.b * a.H));
+    hipLaunchKernelGGL(bwd_replay_kernel<R>, grid, dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_adjoint_kernel<R>, grid, dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool scan_bwd_supported(int P, int N, int R, int np) {
+    return P >= 1 && P <= kPP && N >= 2 && N <= kNN && (N % 2) == 0 && R >= 1 && R <= kR4 && 2 * np <= N;
+}
+
+BwdWs scan_bwd_workspace(int b, int L, int H, int G, int R, int N, int np) {
+    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    BwdWs w{};
+    size_t o = 0;
+    const size_t tokbc = (size_t)b * L * G * R * N, tokh = (size_t)b * L * H;
+    w.accB = o; o += up(tokbc * 4);
+    w.accC = o; o += up(tokbc * 4);
+    w.phi = o;  o += up(tokh * np * 4);
+    w.dphi = o; o += up(tokh * np * 4);
+    w.dl = o;   o += up(tokh * 4);
+    w.dlf = o;  o += up((size_t)b * H * 4);
+    w.total = o;
+    return w;
+}
+
+hipError_t launch_scan_bwd(const BwdArgs& a, void* dB, void* dC, hipStream_t s) {
+    if (a.L == 0) {
+        // no token: the initial carry's gradients are the final carry's sensitivities
+        hipError_t e = hipSuccess;
+        if (!a.rate_law) e = fill_zero(a.dA, (size_t)a.H, s);
+        if (e == hipSuccess) e = fill_zero(a.dBb, (size_t)a.H * a.R * a.N, s);
+        if (e == hipSuccess) e = fill_zero(a.dCb, (size_t)a.H * a.R * a.N, s);
+        const size_t bh = (size_t)a.b * a.H;
+        const float* src[4] = {a.dh1, a.dphi1, a.dBp1, a.dxp1};
+        float* dst[4] = {a.dh0, a.dphi0, a.dBp0, a.dxp0};
+        const size_t n[4] = {bh * a.P * a.N, bh * a.np, bh * a.R * a.N, bh * a.R * a.P};
+        for (int i = 0; i < 4 && e == hipSuccess; ++i) {
+            if (!dst[i] || n[i] == 0) continue;
+            const int blocks = (int)std::min<size_t>((n[i] + 255) / 256, 8192);
+            hipLaunchKernelGGL(copy_f32_kernel, dim3(blocks), dim3(256), 0, s, src[i], dst[i], n[i]);
+            e = hipGetLastError();
+        }
+        return e;
+    }
+    const size_t nbc = (size_t)a.b * a.L * a.G * a.R * a.N;
+    hipError_t e = fill_zero(a.accB, nbc, s);
+    if (e == hipSuccess) e = fill_zero(a.accC, nbc, s);
+    if (e == hipSuccess && !a.rate_law) e = fill_zero(a.dA, (size_t)a.H, s);
+    if (e == hipSuccess) e = fill_zero(a.dBb, (size_t)a.H * a.R * a.N, s);
+    if (e == hipSuccess) e = fill_zero(a.dCb, (size_t)a.H * a.R * a.N, s);
+    if (e != hipSuccess) return e;
+    switch (a.R) {
+        case 1: e = launch_r<1>(a, s); break;
+        case 2: e = launch_r<2>(a, s); break;
+        case 3: e = launch_r<3>(a, s); break;
+        case 4: e = launch_r<4>(a, s); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess || nbc == 0) return e;
+    const int blocks = (int)std::min<size_t>((nbc + 255) / 256, 8192);
+    hipLaunchKernelGGL(acc_convert_kernel, dim3(blocks), dim3(256), 0, s, a.accB, dB, nbc, a.io_bf16);
+    hipLaunchKernelGGL(acc_convert_kernel, dim3(blocks), dim3(256), 0, s, a.accC, dC, nbc, a.io_bf16);
+    return hipGetLastError();
+}
+
+}  // namespace m3

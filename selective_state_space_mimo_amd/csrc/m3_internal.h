@@ -72,6 +72,31 @@ struct BlockArgs {
     void* out;                                                        // layer output [.., P]
 };
 
+// Backward pass of the scan (bwd.hip): forward inputs, output sensitivities in, the
+// gradients out; fp32 workspace for the shared B / C sums and the replay's per-token terms.
+struct BwdArgs {
+    int b, L, H, G, P, N, R, np;
+    int io_bf16, st_bf16, rate_law;
+    const void* x; const void* B; const void* C;
+    const float* dt; const float* lam; const float* theta; const float* A;
+    const float* Bb; const float* Cb;
+    const void* h0; const float* phi0; const void* Bp0; const void* xp0;   // initial carry (null = 0)
+    const void* dy;                                                        // [b, L, H, R, P] io
+    const float* dh1; const float* dphi1; const float* dBp1; const float* dxp1;   // final-carry sensitivities
+    void* dx; float* ddt; float* dlam; float* dtheta; float* dA; float* dBb; float* dCb;
+    float* dh0; float* dphi0; float* dBp0; float* dxp0;                    // initial-carry gradients
+    float* accB; float* accC;          // [b, L, G, R, N] fp32 sums over the heads of a group
+    float* wphi; float* wdphi;         // [b, L, H, np] running angles, C side of the angle gradient
+    float* wdl;                        // [b, L, H] <dy_t, y_t>
+    float* wdlf;                       // [b, H] <dh_L, h_L>
+};
+struct BwdWs {
+    size_t accB, accC, phi, dphi, dl, dlf, total;   // byte offsets of the workspace parts
+};
+bool scan_bwd_supported(int P, int N, int R, int np);
+BwdWs scan_bwd_workspace(int b, int L, int H, int G, int R, int N, int np);
+hipError_t launch_scan_bwd(const BwdArgs& a, void* dB, void* dC, hipStream_t s);
+
 // ---- host-side launchers (return hipSuccess or the launch error) ----------
 hipError_t launch_block_prologue(const BlockArgs& a, hipStream_t s);
 hipError_t launch_block_epilogue(const BlockArgs& a, hipStream_t s);

@@ -137,3 +137,42 @@ def test_block_entry_points_reject_bad_arguments(m3):
     assert _block(m3, d, ws_bytes=64) == 1                # workspace too small
     assert _block(m3, d, out=FAKE + 0x100010) == 1        # out overlaps x
     assert _block(m3, d, ws=FAKE + 0x400000) == 1         # workspace overlaps dt_raw
+
+
+def _bwd(m3, d, ws_bytes=None, grads=None, **kw):
+    a = dict(x=FAKE, B=FAKE + 0x100000, C=FAKE + 0x200000, dt=FAKE + 0x300000, lam=FAKE + 0x400000,
+             theta=FAKE + 0x500000, A=FAKE + 0x600000, dy=FAKE + 0x700000, ws=FAKE + 0x4000000)
+    a.update(kw)
+    if grads is None:
+        grads = m3.Grads(FAKE + 0x1000000, FAKE + 0x1100000, FAKE + 0x1200000, FAKE + 0x1300000, FAKE + 0x1400000,
+                         FAKE + 0x1500000, FAKE + 0x1600000, None, None, m3.CarryGrad(None, None, None, None))
+    n = ctypes.c_size_t(0)
+    assert m3.lib.m3_scan_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    return m3.lib.m3_scan_bwd(ctypes.byref(d), a["x"], a["B"], a["C"], a["dt"], a["lam"], a["theta"], a["A"],
+                              None, None, None, a["dy"], None, ctypes.byref(grads), a["ws"],
+                              n.value if ws_bytes is None else ws_bytes, None)
+
+
+def test_backward_entry_point_rejects_bad_arguments(m3):
+    """m3_scan_bwd checks shapes, pointers, alignment, the workspace size and
+    overlaps (outputs with inputs and with each other) before launching."""
+    d = _desc(m3)
+    n = ctypes.c_size_t(0)
+    assert m3.lib.m3_scan_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0 and n.value > 0
+    assert m3.lib.m3_scan_bwd_workspace_size(None, ctypes.byref(n)) == 1
+    assert m3.lib.m3_scan_bwd_workspace_size(ctypes.byref(_desc(m3, headdim=80)), ctypes.byref(n)) == 2
+    assert m3.lib.m3_scan_bwd_workspace_size(ctypes.byref(_desc(m3, rank=5)), ctypes.byref(n)) == 2
+    assert _bwd(m3, d, dy=None) == 1
+    assert _bwd(m3, d, theta=None) == 1                    # npairs > 0 needs theta
+    assert _bwd(m3, d, dt=FAKE + 0x300004) == 3            # not 16-byte aligned
+    assert _bwd(m3, d, ws_bytes=64) == 1                   # workspace too small
+    assert _bwd(m3, d, ws=FAKE + 0x700000) == 1            # workspace overlaps dy
+    g = m3.Grads(FAKE + 0x1000000, FAKE + 0x1100000, FAKE + 0x1200000, FAKE + 0x1300000, FAKE + 0x1400000,
+                 None, FAKE + 0x1600000, None, None, m3.CarryGrad(None, None, None, None))
+    assert _bwd(m3, d, grads=g) == 1                       # dtheta required when npairs > 0
+    g = m3.Grads(FAKE + 0x10, FAKE + 0x1100000, FAKE + 0x1200000, FAKE + 0x1300000, FAKE + 0x1400000,
+                 FAKE + 0x1500000, FAKE + 0x1600000, None, None, m3.CarryGrad(None, None, None, None))
+    assert _bwd(m3, d, grads=g) == 1                       # dx overlaps x
+    g = m3.Grads(FAKE + 0x1000000, FAKE + 0x1000010, FAKE + 0x1200000, FAKE + 0x1300000, FAKE + 0x1400000,
+                 FAKE + 0x1500000, FAKE + 0x1600000, None, None, m3.CarryGrad(None, None, None, None))
+    assert _bwd(m3, d, grads=g) == 1                       # dB overlaps dx

@@ -1,0 +1,137 @@
+"""GPU parity of the scan's backward pass (``m3_scan_bwd`` through the C ABI)
+against the fp64 backward oracle (``oracle.grad``), every gradient tensor.
+
+Tolerances (normwise relative L2 per tensor): 1e-4 for f32 I/O, 2e-2 for bf16
+I/O (inputs and dy rounded to bf16 on both sides; the kernels accumulate in
+fp32 and round dx, dB, dC to bf16).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from m3inputs import config_by_name, make_cotangents, make_scan_inputs, make_small_case
+from oracle import grad
+from tests._util import host, rel_l2, tdev, to_device
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def m3():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_mimo_amd as m
+    return m
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _run(m3, d, dy, dfin, io):
+    dev = torch.device("cuda:0")
+    iot = torch.float32 if io == "f32" else torch.bfloat16
+    t = to_device(d, iot, torch.float32, dev)
+    dyt = tdev(dy, iot, dev)
+    dft = None if dfin is None else {k: tdev(v, torch.float32, dev) for k, v in dfin.items()}
+    g = m3.scan_bwd(t["x"], t["B"], t["C"], t["dt"], t["lam"], t["theta"], t["A_log"], t["B_bias"], t["C_bias"],
+                    t["init"], dyt, dfinal=dft, A_raw=t["A_raw"])
+    torch.cuda.synchronize()
+    return g
+
+
+def _compare(g, want, d, tol, npairs):
+    keys = [("x", "x"), ("B", "B"), ("C", "C"), ("dt", "dt"), ("lam", "lam")]
+    if npairs:
+        keys.append(("theta", "theta"))
+    keys.append(("A", "A_raw" if d.get("A_raw") is not None else "A_log"))
+    if d.get("B_bias") is not None:
+        keys += [("B_bias", "B_bias"), ("C_bias", "C_bias")]
+    errs = {}
+    for gk, wk in keys:
+        errs[gk] = rel_l2(host(g[gk]), want[wk])
+    for k in ("h", "B_prev", "x_prev") + (("phi",) if npairs else ()):
+        errs["init." + k] = rel_l2(host(g["init"][k]), want["init"][k])
+    _say("  " + " ".join("%s %.1e" % kv for kv in errs.items()))
+    for k, e in errs.items():
+        assert e <= tol, (k, e)
+
+
+CASES = [
+    # name, small-case kwargs, io, final-carry sensitivities
+    ("f32-P16N16-R2-G=H", dict(batch=2, seqlen=37, nheads=2, headdim=16, dstate=16, rank=2, npairs=4), "f32", True),
+    ("f32-P8N12-R3-G1", dict(batch=1, seqlen=23, nheads=2, ngroups=1, headdim=8, dstate=12, rank=3, npairs=2),
+     "f32", True),
+    ("f32-heavy-R1-nocarry", dict(batch=2, seqlen=9, nheads=3, headdim=5, dstate=6, rank=1, npairs=0,
+                                  init_full=False, bias=False, rate_dyn=True), "f32", False),
+    ("f32-one-token", dict(batch=1, seqlen=1, nheads=2, headdim=4, dstate=8, rank=4, npairs=3), "f32", True),
+    ("f32-R4-full-width", dict(batch=1, seqlen=19, nheads=2, ngroups=1, headdim=64, dstate=128, rank=4,
+                               npairs=64), "f32", True),
+    ("bf16-P64N128-R4-G1", dict(batch=2, seqlen=70, nheads=4, ngroups=1, headdim=64, dstate=128, rank=4,
+                                npairs=32, rms_bc=True), "bf16", True),
+    ("bf16-heavy-R2", dict(batch=1, seqlen=41, nheads=3, ngroups=1, headdim=64, dstate=128, rank=2, npairs=32,
+                           rms_bc=True, rate_dyn=True), "bf16", False),
+]
+
+
+@pytest.mark.parametrize("name,kw,io,final", CASES, ids=[c[0] for c in CASES])
+def test_scan_bwd_parity(m3, name, kw, io, final):
+    _say("scan bwd", name)
+    cfg, d = make_small_case(900 + len(name), io_dtype=io, **kw)
+    dy, dfin = make_cotangents(cfg, seed=31, final=final)
+    want = grad.scan_bwd(d, dy, dfin)
+    g = _run(m3, d, dy, dfin, io)
+    _compare(g, want, d, 1e-4 if io == "f32" else 2e-2, cfg.npairs)
+
+
+def test_scan_bwd_empty_sequence(m3):
+    """L = 0: the initial carry's gradients are the final carry's sensitivities."""
+    cfg, d = make_small_case(5, batch=2, seqlen=0, nheads=2, headdim=4, dstate=8, rank=2, npairs=2)
+    _, dfin = make_cotangents(cfg, seed=3)
+    g = _run(m3, d, np.zeros((2, 0, 2, 2, 4), np.float32), dfin, "f32")
+    for k in ("h", "phi", "B_prev", "x_prev"):
+        assert np.array_equal(host(g["init"][k]), np.asarray(dfin[k], np.float64)), k
+    assert np.all(host(g["A"]) == 0.0) and np.all(host(g["B_bias"]) == 0.0)
+
+
+def _one_stream(d, bi, h):
+    """The inputs of stream (bi, h) alone (G = 1: B and C are shared)."""
+    s = {}
+    for k in ("x", "dt", "lam", "theta", "A_raw"):
+        v = d.get(k)
+        s[k] = None if v is None else np.ascontiguousarray(v[bi:bi + 1, :, h:h + 1])
+    s["B"] = d["B"][bi:bi + 1]
+    s["C"] = d["C"][bi:bi + 1]
+    s["A_log"] = d["A_log"][h:h + 1]
+    for k in ("B_bias", "C_bias"):
+        s[k] = None if d.get(k) is None else d[k][h:h + 1]
+    s["init"] = None if d.get("init") is None else {k: v[bi:bi + 1, h:h + 1] for k, v in d["init"].items()}
+    return s
+
+
+def test_scan_bwd_prefill_full_size(m3):
+    """The rank-4 prefill workload at full size (b 8, L 2048, H 64): the
+    per-stream gradients (dx, dt, lambda, theta, initial carry) of sampled
+    streams against the oracle run on those streams alone."""
+    cfg = config_by_name("mimo_bf16_prefill")
+    d = make_scan_inputs(cfg)
+    dy, dfin = make_cotangents(cfg, seed=77)
+    _say("scan bwd full size: inputs ready")
+    g = _run(m3, d, dy, dfin, "bf16")
+    for bi, h in [(0, 0), (5, 41), (7, 63)]:
+        s = _one_stream(d, bi, h)
+        sf = {k: v[bi:bi + 1, h:h + 1] for k, v in dfin.items()}
+        want = grad.scan_bwd(s, dy[bi:bi + 1, :, h:h + 1], sf)
+        errs = {"x": rel_l2(host(g["x"][bi, :, h]), want["x"][0, :, 0]),
+                "dt": rel_l2(host(g["dt"][bi, :, h]), want["dt"][0, :, 0]),
+                "lam": rel_l2(host(g["lam"][bi, :, h]), want["lam"][0, :, 0]),
+                "theta": rel_l2(host(g["theta"][bi, :, h]), want["theta"][0, :, 0])}
+        for k in ("h", "phi", "B_prev", "x_prev"):
+            errs["init." + k] = rel_l2(host(g["init"][k][bi, h]), want["init"][k][0, 0])
+        _say("  stream (%d, %d): " % (bi, h) + " ".join("%s %.1e" % kv for kv in errs.items()))
+        for k, e in errs.items():
+            assert e <= 2e-2, (bi, h, k, e)
