@@ -31,10 +31,12 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_FP32_VALU_TFLOPS = 157.3 # MI355X fp32 vector: 256 CUs x 4 SIMDs x 2.4 GHz x 64 flop (packed FMA)
 CSRC = os.path.join(ROOT, "selective_state_space_mimo_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 # sources that define each measured kernel (the counters stand only while these are unchanged)
-KERNEL_SOURCES = {"scan": ("scan_mfma.hip", "m3_internal.h"), "decode": ("decode.hip", "m3_internal.h")}
+KERNEL_SOURCES = {"scan": ("scan_mfma.hip", "m3_internal.h"), "decode": ("decode.hip", "m3_internal.h"),
+                  "bwd": ("bwd.hip", "m3_internal.h")}
 
 
 def source_sha(kind):
@@ -71,7 +73,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="scan3,decode4,scan2,scan5,scan3r,scan3q,layer3")
+    ap.add_argument("--workloads", default="scan3,decode4,scan2,scan5,scan3r,scan3q,layer3,bwd3")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -117,6 +119,32 @@ def scan_bytes(cfg, with_final=True):
         total += streams * (P * N * 4 + 4 * NP + io * R * (N + P))
     if cfg.bias:
         total += 2 * H * R * N * 4
+    return total
+
+
+def bwd_flops_per_head_token(cfg):
+    """Products with the P x N state per (head, token) of the backward recurrence:
+    the readout's transpose dC = H^T dy (2 R P N), the sensitivity update G = alpha G
+    + sum_r dy_r (x) C_r (2 R P N + P N), and v = G B, w = G^T X (2 R P N each).
+    Reconstructing the forward states (4 R P N + P N more) is recomputation, not
+    credited."""
+    R, N, P = cfg.rank, cfg.dstate, cfg.headdim
+    return 8 * R * P * N + P * N
+
+
+def bwd_bytes(cfg):
+    """Inputs read once (x, dy, B, C, dt, lambda, theta), gradients written once (dx,
+    dB, dC, dt, lambda, theta), the initial and final carries and their sensitivities."""
+    R, N, P, H, G, NP = cfg.rank, cfg.dstate, cfg.headdim, cfg.nheads, cfg.ngroups, cfg.npairs
+    io = 2 if cfg.io_dtype == "bf16" else 4
+    per_ht = 3 * io * R * P + 4 * io * R * N * G / H + 16 + 8 * NP + (8 if cfg.rate_dyn else 0)
+    streams = cfg.batch * H
+    total = per_ht * streams * cfg.seqlen
+    total += streams * 2 * (P * N * 4 + 4 * NP + 4 * R * (N + P))   # final sensitivities in, initial gradients out
+    if cfg.init_state:
+        total += streams * P * N * 4
+    if cfg.bias:
+        total += 4 * H * R * N * 4
     return total
 
 
@@ -274,6 +302,60 @@ def run_layer(torch, m3, cfg, steps, warmup):
     return res
 
 
+def run_bwd(torch, m3, cfg, steps, warmup):
+    """The backward pass (m3_scan_bwd) at a scan workload's shape, with output and
+    final-carry sensitivities."""
+    from m3inputs import make_cotangents, make_scan_inputs
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    d = make_scan_inputs(cfg)
+    dy, dfin = make_cotangents(cfg, seed=77)
+    io = torch.bfloat16 if cfg.io_dtype == "bf16" else torch.float32
+
+    def T(a, dt):
+        return None if a is None else torch.from_numpy(a).to(dev).to(dt).contiguous()
+    x, B, C = T(d["x"], io), T(d["B"], io), T(d["C"], io)
+    dt, lam, th, Al = T(d["dt"], torch.float32), T(d["lam"], torch.float32), T(d["theta"], torch.float32), \
+        T(d["A_log"], torch.float32)
+    Bb, Cb = T(d["B_bias"], torch.float32), T(d["C_bias"], torch.float32)
+    Ar = T(d["A_raw"], torch.float32)
+    init = None
+    if d["init"] is not None:
+        init = {"h": T(d["init"]["h"], torch.float32), "phi": T(d["init"]["phi"], torch.float32),
+                "B_prev": T(d["init"]["B_prev"], io), "x_prev": T(d["init"]["x_prev"], io)}
+    dyt = T(dy, io)
+    dft = {k: T(v, torch.float32) for k, v in dfin.items()}
+    del d, dy, dfin
+    log("[bench] %s backward inputs ready in %.1fs" % (cfg.name, time.time() - t0))
+    b, L, H, R, P = x.shape
+    desc = m3.make_desc(x, B, th, state_dtype=torch.float32,
+                        rate_law=m3.M3_RATE_STATIC if Ar is None else m3.M3_RATE_HEAVY_TAIL)
+    ws_bytes = m3.scan_bwd_workspace_size(desc)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    grads = m3.scan_bwd(x, B, C, dt, lam, th, Al, Bb, Cb, init, dyt, dfinal=dft, A_raw=Ar, workspace=ws)
+
+    def call():
+        m3.scan_bwd(x, B, C, dt, lam, th, Al, Bb, Cb, init, dyt, dfinal=dft, A_raw=Ar, grads=grads, workspace=ws)
+    ms = time_calls(torch, call, steps, warmup)
+    ms_launch = per_launch_ms(torch, call, max(3, min(steps, 10)))
+    flops = bwd_flops_per_head_token(cfg) * b * L * H
+    nbytes = bwd_bytes(cfg)
+    out = {"workload": cfg.name + "_backward", "batch": b, "seqlen": L, "nheads": H, "headdim": P,
+           "dstate": cfg.dstate, "rank": R, "npairs": cfg.npairs, "ms_per_call": ms, "ms_per_launch": ms_launch,
+           "tokens_per_s": b * L / (ms * 1e-3), "algo_tflops": flops / (ms_launch * 1e-3) / 1e12,
+           "algo_gbs": nbytes / (ms_launch * 1e-3) / 1e9, "flop_per_call": flops, "bytes_per_call": nbytes,
+           "workspace_bytes": ws_bytes}
+    out["valu_frac"] = out["algo_tflops"] / PEAK_FP32_VALU_TFLOPS
+    out["hbm_frac"] = out["algo_gbs"] / PEAK_HBM_GBS
+    log("[bench] %s: %.3f ms/call, %.2f M tok/s, %.1f TFLOP/s fp32 (%.1f%% of the VALU peak), %.0f GB/s "
+        "(%.1f%% HBM), workspace %.2f GB" % (out["workload"], ms, out["tokens_per_s"] / 1e6, out["algo_tflops"],
+                                             100 * out["valu_frac"], out["algo_gbs"], 100 * out["hbm_frac"],
+                                             ws_bytes / 1e9))
+    del x, B, C, dt, lam, th, Ar, init, dyt, dft, grads, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_decode(torch, m3, cfg, nsteps):
     dev = torch.device("cuda:0")
     t0 = time.time()
@@ -398,7 +480,7 @@ def main():
     res = {}
     names = {"scan2": "siso_bf16_mamba2", "scan3": "mimo_bf16_prefill", "scan5": "mimo_bf16_long",
              "decode4": "mimo_bf16_decode", "scan3r": "mimo_bf16_prefill", "scan3q": "mimo_bf16_prefill",
-             "layer3": "mimo_bf16_prefill", "copy": None}
+             "layer3": "mimo_bf16_prefill", "bwd3": "mimo_bf16_prefill", "copy": None}
     for w in wl:
         cfg = config_by_name(names[w]) if names[w] else None
         if w == "scan3r":      # the headline prefill with per-token heavy-tail rates
@@ -411,6 +493,8 @@ def main():
             res[w] = run_copy(torch, args.copy_mib)
         elif w.startswith("layer"):
             res[w] = run_layer(torch, m3, cfg, args.steps, args.warmup)
+        elif w.startswith("bwd"):
+            res[w] = run_bwd(torch, m3, cfg, max(3, args.steps // 2), args.warmup)
         elif w.startswith("scan"):
             steps = args.steps if w != "scan5" else max(3, args.steps // 4)
             res[w] = run_scan(torch, m3, cfg, steps, args.warmup)
@@ -467,6 +551,15 @@ def main():
     if layers:
         line["layer"] = {v["workload"]: {k2: v[k2] for k2 in ("tokens_per_s", "ms_per_call", "algo_gbs", "hbm_frac")}
                          for v in layers.values()}
+    if "bwd3" in res:
+        bw = res["bwd3"]
+        line["backward"] = {k2: bw[k2] for k2 in ("workload", "tokens_per_s", "ms_per_call", "ms_per_launch",
+                                                  "algo_tflops", "algo_gbs", "hbm_frac")}
+        line["roofline_backward"] = {"bound": "alu", "achieved": bw["algo_tflops"], "peak": PEAK_FP32_VALU_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": bw["valu_frac"],
+                                     "traffic": measured_traffic("bwd", bw["workload"]),
+                                     "algorithmic_flops": bw["flop_per_call"],
+                                     "algorithmic_bytes": bw["bytes_per_call"]}
     others = {k: v for k, v in res.items() if k != main_w and k.startswith("scan")}
     if others:
         line["scan_other"] = {v["workload"]: {"tokens_per_s": v["tokens_per_s"], "ms_per_call": v["ms_per_call"],

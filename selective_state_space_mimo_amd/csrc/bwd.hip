@@ -46,12 +46,18 @@ namespace m3 {
 
 namespace {
 
-constexpr int kT = 8;                 // tokens per staged group
+constexpr int kT = 8;                 // tokens per staged group (replay)
+constexpr int kTA = 7;                // tokens per staged group (adjoint: its LDS fits two groups per CU)
 constexpr int kR4 = 4, kPP = 64, kNN = 128, kThreads = 256;
 
-// turned B and C rows are kept with column n at (n % 16) * 8 + n / 16, so that a lane's
-// eight columns 16 nt + l16 are one 32-byte run
-__device__ __forceinline__ int colpos(int n) { return (n & 15) * 8 + (n >> 4); }
+// Turned B and C rows keep column n = 16 nt + l16 at 64 (nt / 4) + 4 l16 + nt % 4: a lane's
+// eight columns are two 16-byte runs, and the 16 lanes of a row group read 64 consecutive
+// words per access (no bank conflict; the four row groups read the same words).
+__device__ __forceinline__ int bpos(int n) { return ((n >> 6) << 6) + ((n & 15) << 2) + ((n >> 4) & 3); }
+// Rows summed over the waves by LDS adds keep column n at n + 16 (n / 32): the four 16-lane
+// groups of one add (columns 32 lg + 16 i + l16) then fall on distinct banks.
+constexpr int kDPad = kNN + 48;
+__device__ __forceinline__ int dpos(int n) { return n + ((n >> 5) << 4); }
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
@@ -83,6 +89,28 @@ __device__ __forceinline__ float rs_row16(float (&v)[16], int l16) {
     rs_row_level<1, 2>(v, l16 & 1);
     return v[0];
 }
+// Lane swaps across wave halves and across 16-lane rows (VALU, no LDS round trip):
+// swap32(a, b) returns (a with its upper 32 lanes replaced by b's lower 32, b with its lower
+// 32 lanes replaced by a's upper 32); swap16 does the same between the odd rows of a and
+// the even rows of b.
+__device__ __forceinline__ float2 swap32(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float2 swap16(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// One reduce-scatter level across halves: the lower half keeps lo, the upper half keeps hi,
+// each adding its partner's copy.
+__device__ __forceinline__ float rs32(float lo, float hi, bool upper) {
+    const float2 w = swap32(lo, hi);
+    return upper ? hi + w.x : lo + w.y;
+}
+__device__ __forceinline__ float rs16(float lo, float hi, bool odd) {
+    const float2 w = swap16(lo, hi);
+    return odd ? hi + w.x : lo + w.y;
+}
 // Sum of part[r][nt] over the four 16-lane groups, scattered: group lg keeps tiles
 // nt = 2 lg + i (i < 2) in out[r][i].
 template <int R>
@@ -92,24 +120,26 @@ __device__ __forceinline__ void rs_groups(const float (&part)[R][8], float (&out
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float keep = h2 ? part[r][4 + i] : part[r][i];
-            const float send = h2 ? part[r][i] : part[r][4 + i];
-            k4[r][i] = keep + __shfl_xor(send, 32);
-        }
+        for (int i = 0; i < 4; ++i) k4[r][i] = rs32(part[r][i], part[r][4 + i], h2);
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const float keep = h1 ? k4[r][2 + i] : k4[r][i];
-            const float send = h1 ? k4[r][i] : k4[r][2 + i];
-            out[r][i] = keep + __shfl_xor(send, 16);
-        }
+        for (int i = 0; i < 2; ++i) out[r][i] = rs16(k4[r][i], k4[r][2 + i], h1);
+}
+// all-reduce inside each 8-lane half-row (involutions generating the group of 8)
+__device__ __forceinline__ float sum8(float c) {
+    c += row_partner<4>(c);
+    c += row_partner<2>(c);
+    c += row_partner<1>(c);
+    return c;
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-    return v;
+    float2 w = swap32(v, v);
+    v = w.x + w.y;
+    w = swap16(v, v);
+    v = w.x + w.y;
+    v += row_partner<8>(v);
+    return sum8(v);
 }
 // Sum of v[8] over the wave, scattered: lanes with lane % 8 == 0 return entry
 // 4 (lane >> 5 & 1) + 2 (lane >> 4 & 1) + (lane >> 3 & 1).
@@ -117,14 +147,21 @@ __device__ __forceinline__ float rs_wave8(float (&v)[8], int lane) {
     float a[4], b[2];
     const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = (h5 ? v[4 + i] : v[i]) + __shfl_xor(h5 ? v[i] : v[4 + i], 32);
+    for (int i = 0; i < 4; ++i) a[i] = rs32(v[i], v[4 + i], h5);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) b[i] = (h4 ? a[2 + i] : a[i]) + __shfl_xor(h4 ? a[i] : a[2 + i], 16);
-    float c = (h3 ? b[1] : b[0]) + __shfl_xor(h3 ? b[0] : b[1], 8);
-    c += __shfl_xor(c, 4);
-    c += __shfl_xor(c, 2);
-    c += __shfl_xor(c, 1);
-    return c;
+    for (int i = 0; i < 2; ++i) b[i] = rs16(a[i], a[2 + i], h4);
+    float c = (h3 ? b[1] : b[0]) + row_partner<8>(h3 ? b[0] : b[1]);
+    return sum8(c);
+}
+// Sum of v[4] over the wave, scattered: lanes with lane % 16 == 0 return entry lane / 16.
+__device__ __forceinline__ float rs_wave4(float (&v)[4], int lane) {
+    const bool h5 = lane & 32, h4 = lane & 16;
+    float a[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a[i] = rs32(v[i], v[2 + i], h5);
+    float c = rs16(a[0], a[1], h4);
+    c += row_partner<8>(c);
+    return sum8(c);
 }
 __device__ __forceinline__ void lds_add(float* p, float v) {
     __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -141,25 +178,67 @@ __device__ __forceinline__ float heavy_tail_rate_grad(float u) {
     return -ht < -1e-4f ? -d : 0.f;
 }
 
-// One staged token pair (rank r, pair j) of B or C: biased, turned by (c, s).
-__device__ __forceinline__ float2 turned_pair(const void* M, size_t idx, int io_bf16, float bias0, float bias1,
-                                              bool turns, float c, float s) {
-    const float m0 = ld_io(M, idx, io_bf16) + bias0, m1 = ld_io(M, idx + 1, io_bf16) + bias1;
+template <bool BF>
+__device__ __forceinline__ float ldt(const void* p, size_t i) {
+    if constexpr (BF) return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
+    else return static_cast<const float*>(p)[i];
+}
+// The raw inputs one thread stages for a group of KT tokens (rank r, pair j, row j), all
+// loaded before any of them is used; indices are clamped into the tensors, and the values of
+// slots that are not staged (past the group's tokens, ranks or pairs) are ignored.
+template <int KT>
+struct RawGroup {
+    float b0[KT], b1[KT], c0[KT], c1[KT], x[KT], dy[KT], dt[KT], ang[KT];
+};
+template <int KT, bool BF>
+__device__ __forceinline__ void load_group(RawGroup<KT>& g, const BwdArgs& a, int bi, int h, int gr, int r, int j,
+                                           int t0, int nv, const float* ang, bool with_dt) {
+    const int R = a.R, N = a.N, P = a.P, H = a.H, np = a.np;
+    const int rr = min(r, R - 1), jb = min(j, N / 2 - 1), jx = min(j, P - 1), ja = np > 0 ? min(j, np - 1) : 0;
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+        const size_t tok = (size_t)bi * a.L + t0 + min(k, nv - 1);
+        const size_t bc = ((tok * a.G + gr) * R + rr) * N + 2 * jb;
+        const size_t xi = ((tok * H + h) * R + rr) * P + jx;
+        g.b0[k] = ldt<BF>(a.B, bc);
+        g.b1[k] = ldt<BF>(a.B, bc + 1);
+        g.c0[k] = ldt<BF>(a.C, bc);
+        g.c1[k] = ldt<BF>(a.C, bc + 1);
+        g.x[k] = ldt<BF>(a.x, xi);
+        g.dy[k] = ldt<BF>(a.dy, xi);
+        g.dt[k] = with_dt ? a.dt[tok * H + h] : 0.f;
+        g.ang[k] = np > 0 ? ang[(tok * H + h) * np + ja] : 0.f;
+    }
+}
+template <int KT>
+__device__ __forceinline__ void load_group_io(RawGroup<KT>& g, const BwdArgs& a, int bi, int h, int gr, int r, int j,
+                                              int t0, int nv, const float* ang, bool with_dt) {
+    if (a.io_bf16) load_group<KT, true>(g, a, bi, h, gr, r, j, t0, nv, ang, with_dt);
+    else load_group<KT, false>(g, a, bi, h, gr, r, j, t0, nv, ang, with_dt);
+}
+__device__ __forceinline__ float2 turn(float m0, float m1, bool turns, float c, float s) {
     if (!turns) return make_float2(m0, m1);
     return make_float2(m0 * c - m1 * s, m0 * s + m1 * c);
 }
 
+
 // ============================== forward replay ==============================
+// The replay carries the folded state U_t = H_t + delta_{t+1} X_t^T Bt_t (delta = dt (1 - lam),
+// beta = alpha delta), whose recurrence has one rank-R write per token:
+//   U_t = alpha_t U_{t-1} + (gamma_t + delta_{t+1}) X_t^T Bt_t,   U_{-1} = H_0 + delta_0 X_prev^T B_prev,
+// so dCt_t[r] = H_t^T dy_t[r] = U_t^T dy_t[r] - delta_{t+1} sum_r' (X_t[r'] . dy_t[r]) Bt_t[r']
+// (an R x R correction formed after each group; delta_L = 0 at the last token).
 template <int R>
 __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
-    __shared__ __align__(16) float sX[kT + 1][kR4][kPP];     // slot 0: the previous token's x
-    __shared__ __align__(16) float sBt[kT + 1][kR4][kNN];    // turned B (column order colpos); slot 0: previous
+    __shared__ __align__(16) float sX[kT + 1][kR4][kPP];     // slot 0: x_prev (initial fold only)
+    __shared__ __align__(16) float sBt[kT + 1][kR4][kNN];    // turned B (bpos order); slot 0: B_prev
     __shared__ __align__(16) float sDY[kT][kR4][kPP];
-    __shared__ __align__(16) float sCt[kT][kR4][kNN];        // turned C (colpos)
-    __shared__ float sDC[kT][kR4][kNN];        // dCt (natural column order), summed over waves
+    __shared__ __align__(16) float sCt[kT][kR4][kNN];        // turned C (bpos order)
+    __shared__ float sDC[kT][kR4][kDPad];                   // U^T dy (dpos order), summed over waves
+    __shared__ float sDot[kT][kR4][4];                      // [r][r'] = X[r'] . dy[r]
     __shared__ float sDPH[kT][64];
     __shared__ float sDL[kT];
-    __shared__ float sAl[kT], sBe[kT], sGa[kT];
+    __shared__ float sAl[kT], sCo[kT], sDn[kT];             // alpha_t, gamma_t + delta_{t+1}, delta_{t+1}
     __shared__ float sRed[4];
 
     const int bh = blockIdx.x, H = a.H, bi = bh / H, h = bh % H, g = h * a.G / H;
@@ -183,84 +262,119 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
     if (pok && a.Cb) { cb0 = a.Cb[((size_t)h * R + r) * N + 2 * j]; cb1 = a.Cb[((size_t)h * R + r) * N + 2 * j + 1]; }
     float phi = (turns && a.phi0) ? a.phi0[(size_t)bh * np + j] : 0.f;
     float gC0 = 0.f, gC1 = 0.f;                 // C bias gradient partials
-    // slot 0: the carried previous write (x_prev, turned B_prev)
+    // the initial fold U_{-1} = H_0 + delta_0 X_prev^T B_prev
     sX[0][r][j] = (xok && a.xp0) ? ld_io(a.xp0, ((size_t)bh * R + r) * P + j, io) : 0.f;
     {
         const bool ok = pok && a.Bp0;
-        sBt[0][r][colpos(2 * j)] = ok ? ld_io(a.Bp0, ((size_t)bh * R + r) * N + 2 * j, io) : 0.f;
-        sBt[0][r][colpos(2 * j + 1)] = ok ? ld_io(a.Bp0, ((size_t)bh * R + r) * N + 2 * j + 1, io) : 0.f;
+        sBt[0][r][bpos(2 * j)] = ok ? ld_io(a.Bp0, ((size_t)bh * R + r) * N + 2 * j, io) : 0.f;
+        sBt[0][r][bpos(2 * j + 1)] = ok ? ld_io(a.Bp0, ((size_t)bh * R + r) * N + 2 * j + 1, io) : 0.f;
     }
+    if (tid == 0 && L > 0) {
+        const size_t th = (size_t)bi * L * H + h;
+        sDn[0] = a.dt[th] * (1.f - a.lam[th]);
+    }
+    __syncthreads();
+    if (L > 0) {
+        const float d0 = sDn[0];
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const float4 xv = ld4(&sX[0][q][prow]);
+            const float4 b0 = ld4(&sBt[0][q][l16 * 4]), b1 = ld4(&sBt[0][q][64 + l16 * 4]);
+            const float bq[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+            const float xq[4] = {d0 * xv.x, d0 * xv.y, d0 * xv.z, d0 * xv.w};
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) S[v][nt] = fmaf(xq[v], bq[nt], S[v][nt]);
+        }
+    }
+    __syncthreads();
 
     for (int t0 = 0; t0 < L; t0 += kT) {
         const int nv = min(kT, L - t0);
         // ---- stage kT tokens: angles, turned B and C, x, dy, per-token scalars ----
         float cs[kT], sn[kT];
+        {
+            RawGroup<kT> rg;
+            load_group_io<kT>(rg, a, bi, h, g, r, j, t0, nv, a.theta, true);
 #pragma unroll
-        for (int k = 0; k < kT; ++k) {
-            const bool valid = k < nv;
-            const size_t tok = (size_t)bi * L + t0 + k;
-            cs[k] = 1.f; sn[k] = 0.f;
-            if (valid && turns) {
-                const float dtv = a.dt[tok * H + h];
-                phi = wrap_2pi(phi + dtv * a.theta[(tok * H + h) * np + j]);
-                sincosf(phi, &sn[k], &cs[k]);
-                if (r == 0) a.wphi[(tok * H + h) * np + j] = phi;
+            for (int k = 0; k < kT; ++k) {
+                const bool valid = k < nv;
+                const size_t tok = (size_t)bi * L + t0 + k;
+                cs[k] = 1.f; sn[k] = 0.f;
+                if (valid && turns) {
+                    phi = wrap_2pi(phi + rg.dt[k] * rg.ang[k]);
+                    sincosf(phi, &sn[k], &cs[k]);
+                    if (r == 0) a.wphi[(tok * H + h) * np + j] = phi;
+                }
+                const bool ok = valid && pok;
+                const float2 bt = turn(rg.b0[k] + bb0, rg.b1[k] + bb1, turns, cs[k], sn[k]);
+                const float2 ct = turn(rg.c0[k] + cb0, rg.c1[k] + cb1, turns, cs[k], sn[k]);
+                sBt[k + 1][r][bpos(2 * j)] = ok ? bt.x : 0.f;
+                sBt[k + 1][r][bpos(2 * j + 1)] = ok ? bt.y : 0.f;
+                sCt[k][r][bpos(2 * j)] = ok ? ct.x : 0.f;
+                sCt[k][r][bpos(2 * j + 1)] = ok ? ct.y : 0.f;
+                sX[k + 1][r][j] = (valid && xok) ? rg.x[k] : 0.f;
+                sDY[k][r][j] = (valid && xok) ? rg.dy[k] : 0.f;
+                sDC[k][r][dpos(2 * j)] = 0.f;
+                sDC[k][r][dpos(2 * j + 1)] = 0.f;
+                if (w == 0) sDPH[k][j] = 0.f;
             }
-            float2 bt = make_float2(0.f, 0.f), ct = bt;
-            if (valid && pok) {
-                const size_t bc = ((tok * a.G + g) * R + r) * N + 2 * j;
-                bt = turned_pair(a.B, bc, io, bb0, bb1, turns, cs[k], sn[k]);
-                ct = turned_pair(a.C, bc, io, cb0, cb1, turns, cs[k], sn[k]);
-            }
-            sBt[k + 1][r][colpos(2 * j)] = bt.x;
-            sBt[k + 1][r][colpos(2 * j + 1)] = bt.y;
-            sCt[k][r][colpos(2 * j)] = ct.x;
-            sCt[k][r][colpos(2 * j + 1)] = ct.y;
-            const size_t xi = ((tok * H + h) * R + r) * P + j;
-            sX[k + 1][r][j] = (valid && xok) ? ld_io(a.x, xi, io) : 0.f;
-            sDY[k][r][j] = (valid && xok) ? ld_io(a.dy, xi, io) : 0.f;
-            sDC[k][r][2 * j] = 0.f;
-            sDC[k][r][2 * j + 1] = 0.f;
-            if (w == 0) sDPH[k][j] = 0.f;
         }
         if (tid < kT) {
-            float al = 1.f, be = 0.f, ga = 0.f;
+            // alpha_t and gamma_t + delta_{t+1} of token t = t0 + tid (delta_L = 0)
+            float al = 1.f, ga = 0.f, dn = 0.f;
             if (tid < nv) {
                 const size_t th = ((size_t)bi * L + t0 + tid) * H + h;
                 const float dtv = a.dt[th], lm = a.lam[th];
                 al = expf(dtv * rate_of(a, h, th));
-                be = al * dtv * (1.f - lm);
                 ga = lm * dtv;
+                if (t0 + tid + 1 < L) dn = a.dt[th + H] * (1.f - a.lam[th + H]);
             }
-            sAl[tid] = al; sBe[tid] = be; sGa[tid] = ga;
+            sAl[tid] = al; sCo[tid] = ga + dn; sDn[tid] = dn;
             sDL[tid] = 0.f;
         }
         __syncthreads();
-        // ---- per token (wave-local): H_t, then dCt_t = H_t^T dy_t ----
+        // ---- per token (wave-local): U_t, then U_t^T dy_t; each token's operands are read
+        //      from LDS one token ahead, so the reads overlap the previous token's arithmetic ----
+        float4 nx[R], nb[R][2], nd[R];
+        float nal = 1.f, nco = 0.f;
+        auto fetch_tok = [&](int k) {
+#pragma unroll
+            for (int q = 0; q < R; ++q) {
+                nx[q] = ld4(&sX[k + 1][q][prow]);
+                nb[q][0] = ld4(&sBt[k + 1][q][l16 * 4]);
+                nb[q][1] = ld4(&sBt[k + 1][q][64 + l16 * 4]);
+                nd[q] = ld4(&sDY[k][q][prow]);
+            }
+            nal = sAl[k];
+            nco = sCo[k];
+        };
+        if (nv > 0) fetch_tok(0);
         for (int k = 0; k < nv; ++k) {
-            const float al = sAl[k], be = sBe[k], ga = sGa[k];
+            float4 cx[R], cb[R][2], cd[R];
+#pragma unroll
+            for (int q = 0; q < R; ++q) { cx[q] = nx[q]; cb[q][0] = nb[q][0]; cb[q][1] = nb[q][1]; cd[q] = nd[q]; }
+            const float al = nal, co = nco;
+            if (k + 1 < nv) fetch_tok(k + 1);
 #pragma unroll
             for (int v = 0; v < 4; ++v)
 #pragma unroll
                 for (int nt = 0; nt < 8; ++nt) S[v][nt] *= al;
 #pragma unroll
             for (int q = 0; q < R; ++q) {
-                const float4 xp = ld4(&sX[k][q][prow]), xc = ld4(&sX[k + 1][q][prow]);
-                const float4 p0 = ld4(&sBt[k][q][l16 * 8]), p1 = ld4(&sBt[k][q][l16 * 8 + 4]);
-                const float4 c0 = ld4(&sBt[k + 1][q][l16 * 8]), c1 = ld4(&sBt[k + 1][q][l16 * 8 + 4]);
-                const float bp[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-                const float bc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-                const float ap[4] = {be * xp.x, be * xp.y, be * xp.z, be * xp.w};
-                const float ac[4] = {ga * xc.x, ga * xc.y, ga * xc.z, ga * xc.w};
+                const float bc[8] = {cb[q][0].x, cb[q][0].y, cb[q][0].z, cb[q][0].w,
+                                     cb[q][1].x, cb[q][1].y, cb[q][1].z, cb[q][1].w};
+                const float ac[4] = {co * cx[q].x, co * cx[q].y, co * cx[q].z, co * cx[q].w};
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
 #pragma unroll
-                    for (int nt = 0; nt < 8; ++nt) S[v][nt] = fmaf(ap[v], bp[nt], fmaf(ac[v], bc[nt], S[v][nt]));
+                    for (int nt = 0; nt < 8; ++nt) S[v][nt] = fmaf(ac[v], bc[nt], S[v][nt]);
             }
             float part[R][8];
 #pragma unroll
             for (int q = 0; q < R; ++q) {
-                const float4 d = ld4(&sDY[k][q][prow]);
+                const float4 d = cd[q];
 #pragma unroll
                 for (int nt = 0; nt < 8; ++nt)
                     part[q][nt] = S[0][nt] * d.x + S[1][nt] * d.y + S[2][nt] * d.z + S[3][nt] * d.w;
@@ -270,16 +384,35 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
 #pragma unroll
             for (int q = 0; q < R; ++q)
 #pragma unroll
-                for (int i = 0; i < 2; ++i) lds_add(&sDC[k][q][16 * (2 * lg + i) + l16], red[q][i]);
+                for (int i = 0; i < 2; ++i) lds_add(&sDC[k][q][dpos(16 * (2 * lg + i) + l16)], red[q][i]);
         }
         __syncthreads();
-        // ---- per token outputs: dC (turned back), bias partials, angle and <dy, y> terms ----
+        // ---- per token R x R dots X[r'] . dy[r] (wave r) ----
+        if (r < R) {
+            for (int k = 0; k < nv; ++k) {
+                float d4[4];
+                const float dyr = xok ? sDY[k][r][j] : 0.f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) d4[q] = (q < R && xok) ? sX[k + 1][q][j] * dyr : 0.f;
+                const float d = rs_wave4(d4, lane);
+                if ((lane & 15) == 0) sDot[k][r][lane >> 4] = d;
+            }
+        }
+        __syncthreads();
+        // ---- per token outputs: dC (corrected, turned back), bias partials, angle and <dy, y> terms ----
         for (int k = 0; k < nv; ++k) {
             const size_t tok = (size_t)bi * L + t0 + k;
             float dl = 0.f;
             if (pok) {
-                const float d0 = sDC[k][r][2 * j], d1 = sDC[k][r][2 * j + 1];
-                const float c0 = sCt[k][r][colpos(2 * j)], c1 = sCt[k][r][colpos(2 * j + 1)];
+                float d0 = sDC[k][r][dpos(2 * j)], d1 = sDC[k][r][dpos(2 * j + 1)];
+                const float dn = sDn[k];
+#pragma unroll
+                for (int q = 0; q < R; ++q) {
+                    const float m = -dn * sDot[k][r][q];
+                    d0 = fmaf(m, sBt[k + 1][q][bpos(2 * j)], d0);
+                    d1 = fmaf(m, sBt[k + 1][q][bpos(2 * j + 1)], d1);
+                }
+                const float c0 = sCt[k][r][bpos(2 * j)], c1 = sCt[k][r][bpos(2 * j + 1)];
                 dl = c0 * d0 + c1 * d1;
                 float e0 = d0, e1 = d1;
                 if (turns) {
@@ -300,13 +433,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
         if (w == 0 && j < np)
             for (int k = 0; k < nv; ++k) a.wdphi[(((size_t)bi * L + t0 + k) * H + h) * np + j] = sDPH[k][j];
         if (tid < nv) a.wdl[((size_t)bi * L + t0 + tid) * H + h] = sDL[tid];
-        // the group's last token is the next group's previous write
-        sX[0][r][j] = sX[nv][r][j];
-        sBt[0][r][2 * j] = sBt[nv][r][2 * j];
-        sBt[0][r][2 * j + 1] = sBt[nv][r][2 * j + 1];
-        __syncthreads();
     }
-    // <dH_L, H_L>, the final state's reader term of the last token
+    // <dH_L, H_L>, the final state's reader term of the last token (U_{L-1} = H_{L-1})
     float fin = 0.f;
     if (a.dh1) {
 #pragma unroll
@@ -332,14 +460,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
 // into sw (both [R4][..] rows of that token)
 template <int R>
 __device__ __forceinline__ void contract(const float (&S)[4][8], const float (*sx)[kPP], const float (*sb)[kNN],
-                                         float (*sv)[kPP], float (*sw)[kNN], int prow, int lg, int l16) {
+                                         float (*sv)[kPP], float (*sw)[kDPad], int prow, int lg, int l16) {
     float vp[16];
     float wp[R][8];
 #pragma unroll
     for (int i = 0; i < 16; ++i) vp[i] = 0.f;
 #pragma unroll
     for (int q = 0; q < R; ++q) {
-        const float4 b0 = ld4(&sb[q][l16 * 8]), b1 = ld4(&sb[q][l16 * 8 + 4]);
+        const float4 b0 = ld4(&sb[q][l16 * 4]), b1 = ld4(&sb[q][64 + l16 * 4]);
         const float bq[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
         const float4 xv = ld4(&sx[q][prow]);
         const float xq[4] = {xv.x, xv.y, xv.z, xv.w};
@@ -362,21 +490,21 @@ __device__ __forceinline__ void contract(const float (&S)[4][8], const float (*s
 #pragma unroll
     for (int qq = 0; qq < R; ++qq)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) lds_add(&sw[qq][16 * (2 * lg + i) + l16], red[qq][i]);
+        for (int i = 0; i < 2; ++i) lds_add(&sw[qq][dpos(16 * (2 * lg + i) + l16)], red[qq][i]);
 }
 
 template <int R>
 __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
-    __shared__ __align__(16) float sX[kT][kR4][kPP];
-    __shared__ __align__(16) float sBt[kT][kR4][kNN];        // turned B (colpos)
-    __shared__ __align__(16) float sDY[kT][kR4][kPP];
-    __shared__ __align__(16) float sCt[kT][kR4][kNN];        // turned C (colpos)
-    __shared__ float sV[kT][kR4][kPP];         // v = G_{t+1} Bt_t
-    __shared__ float sW[kT][kR4][kNN];         // w = G_{t+1}^T X_t (natural order)
-    __shared__ float sDot[kT][kR4][8];         // [r][r'] = Ct[r'] . Bt[r], [r][4 + r'] = dy[r'] . X[r]
-    __shared__ float sXV[kT];                  // X_t . v
-    __shared__ float sDPH[kT][64];
-    __shared__ float sAl[kT + 1], sBe[kT + 1], sGa[kT + 1], sDt[kT + 1], sLm[kT + 1], sRt[kT + 1], sU[kT + 1];
+    __shared__ __align__(16) float sX[kTA][kR4][kPP];
+    __shared__ __align__(16) float sBt[kTA][kR4][kNN];        // turned B (bpos order)
+    __shared__ __align__(16) float sDY[kTA][kR4][kPP];
+    __shared__ __align__(16) float sCt[kTA][kR4][kNN];        // turned C (bpos order)
+    __shared__ float sV[kTA][kR4][kPP];         // v = G_{t+1} Bt_t
+    __shared__ float sW[kTA][kR4][kDPad];       // w = G_{t+1}^T X_t (dpos order)
+    __shared__ float sDot[kTA][kR4][8];         // [r][r'] = Ct[r'] . Bt[r], [r][4 + r'] = dy[r'] . X[r]
+    __shared__ float sXV[kTA];                  // X_t . v
+    __shared__ float sDPH[kTA][64];
+    __shared__ float sAl[kTA + 1], sBe[kTA + 1], sGa[kTA + 1], sDt[kTA + 1], sLm[kTA + 1], sRt[kTA + 1], sU[kTA + 1];
 
     const int bh = blockIdx.x, H = a.H, bi = bh / H, h = bh % H, g = h * a.G / H;
     const int L = a.L, P = a.P, N = a.N, np = a.np, io = a.io_bf16;
@@ -403,34 +531,33 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
     // pending step / blend gradients, the static rate's sum)
     float Sl = 0.f, pend_dt = 0.f, pend_lm = 0.f, dA_sum = 0.f;
 
-    for (int t0 = ((L - 1) / kT) * kT; t0 >= 0; t0 -= kT) {
-        const int nv = min(kT, L - t0);
-        float cs[kT], sn[kT];
+    for (int t0 = ((L - 1) / kTA) * kTA; t0 >= 0; t0 -= kTA) {
+        const int nv = min(kTA, L - t0);
+        float cs[kTA], sn[kTA];
+        {
+            RawGroup<kTA> rg;
+            load_group_io<kTA>(rg, a, bi, h, g, r, j, t0, nv, a.wphi, false);
 #pragma unroll
-        for (int k = 0; k < kT; ++k) {
-            const bool valid = k < nv;
-            const size_t tok = (size_t)bi * L + t0 + k;
-            cs[k] = 1.f; sn[k] = 0.f;
-            if (valid && turns) sincosf(a.wphi[(tok * H + h) * np + j], &sn[k], &cs[k]);
-            float2 bt = make_float2(0.f, 0.f), ct = bt;
-            if (valid && pok) {
-                const size_t bc = ((tok * a.G + g) * R + r) * N + 2 * j;
-                bt = turned_pair(a.B, bc, io, bb0, bb1, turns, cs[k], sn[k]);
-                ct = turned_pair(a.C, bc, io, cb0, cb1, turns, cs[k], sn[k]);
+            for (int k = 0; k < kTA; ++k) {
+                const bool valid = k < nv;
+                cs[k] = 1.f; sn[k] = 0.f;
+                if (valid && turns) sincosf(rg.ang[k], &sn[k], &cs[k]);
+                const bool ok = valid && pok;
+                const float2 bt = turn(rg.b0[k] + bb0, rg.b1[k] + bb1, turns, cs[k], sn[k]);
+                const float2 ct = turn(rg.c0[k] + cb0, rg.c1[k] + cb1, turns, cs[k], sn[k]);
+                sBt[k][r][bpos(2 * j)] = ok ? bt.x : 0.f;
+                sBt[k][r][bpos(2 * j + 1)] = ok ? bt.y : 0.f;
+                sCt[k][r][bpos(2 * j)] = ok ? ct.x : 0.f;
+                sCt[k][r][bpos(2 * j + 1)] = ok ? ct.y : 0.f;
+                sX[k][r][j] = (valid && xok) ? rg.x[k] : 0.f;
+                sDY[k][r][j] = (valid && xok) ? rg.dy[k] : 0.f;
+                sW[k][r][dpos(2 * j)] = 0.f;
+                sW[k][r][dpos(2 * j + 1)] = 0.f;
+                if (w == 0) sDPH[k][j] = 0.f;
             }
-            sBt[k][r][colpos(2 * j)] = bt.x;
-            sBt[k][r][colpos(2 * j + 1)] = bt.y;
-            sCt[k][r][colpos(2 * j)] = ct.x;
-            sCt[k][r][colpos(2 * j + 1)] = ct.y;
-            const size_t xi = ((tok * H + h) * R + r) * P + j;
-            sX[k][r][j] = (valid && xok) ? ld_io(a.x, xi, io) : 0.f;
-            sDY[k][r][j] = (valid && xok) ? ld_io(a.dy, xi, io) : 0.f;
-            sW[k][r][2 * j] = 0.f;
-            sW[k][r][2 * j + 1] = 0.f;
-            if (w == 0) sDPH[k][j] = 0.f;
         }
-        if (tid <= kT) {
-            // slot kT is token t0 + kT (the first of the group done before), or past the end:
+        if (tid <= kTA) {
+            // slot kTA is token t0 + kTA (the first of the group done before), or past the end:
             // there alpha = 1 and beta = 0 stand for the final carry
             float al = 1.f, be = 0.f, ga = 0.f, dtv = 0.f, lm = 0.f, rt = 0.f, u = 0.f;
             if (t0 + tid < L) {
@@ -443,7 +570,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
                 ga = lm * dtv;
             }
             sAl[tid] = al; sBe[tid] = be; sGa[tid] = ga; sDt[tid] = dtv; sLm[tid] = lm; sRt[tid] = rt; sU[tid] = u;
-            if (tid < kT) sXV[tid] = 0.f;
+            if (tid < kTA) sXV[tid] = 0.f;
         }
         __syncthreads();
         // ---- per token, last first (wave-local): v, w against G_{t+1}, then G_t ----
@@ -458,7 +585,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
             for (int q = 0; q < R; ++q) {
                 const float4 d = ld4(&sDY[k][q][prow]);
                 const float dq[4] = {d.x, d.y, d.z, d.w};
-                const float4 c0 = ld4(&sCt[k][q][l16 * 8]), c1 = ld4(&sCt[k][q][l16 * 8 + 4]);
+                const float4 c0 = ld4(&sCt[k][q][l16 * 4]), c1 = ld4(&sCt[k][q][64 + l16 * 4]);
                 const float cq[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
@@ -471,11 +598,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
         for (int k = 0; k < nv; ++k) {
             if (r < R) {
                 float d8[8];
-                const float b0 = sBt[k][r][colpos(2 * j)], b1 = sBt[k][r][colpos(2 * j + 1)];
+                const float b0 = sBt[k][r][bpos(2 * j)], b1 = sBt[k][r][bpos(2 * j + 1)];
                 const float xr = sX[k][r][j];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    d8[q] = (q < R && pok) ? sCt[k][q][colpos(2 * j)] * b0 + sCt[k][q][colpos(2 * j + 1)] * b1 : 0.f;
+                    d8[q] = (q < R && pok) ? sCt[k][q][bpos(2 * j)] * b0 + sCt[k][q][bpos(2 * j + 1)] * b1 : 0.f;
                     d8[4 + q] = (q < R && xok) ? sDY[k][q][j] * xr : 0.f;
                 }
                 const float d = rs_wave8(d8, lane);
@@ -499,12 +626,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
                 st_io(a.dx, ((tok * H + h) * R + r) * P + j, dxv, io);
             }
             if (pok) {
-                float d0 = kap * sW[k][r][2 * j], d1 = kap * sW[k][r][2 * j + 1];
+                float d0 = kap * sW[k][r][dpos(2 * j)], d1 = kap * sW[k][r][dpos(2 * j + 1)];
 #pragma unroll
                 for (int q = 0; q < R; ++q) {
                     const float m = ga * sDot[k][r][4 + q];
-                    d0 = fmaf(m, sCt[k][q][colpos(2 * j)], d0);
-                    d1 = fmaf(m, sCt[k][q][colpos(2 * j + 1)], d1);
+                    d0 = fmaf(m, sCt[k][q][bpos(2 * j)], d0);
+                    d1 = fmaf(m, sCt[k][q][bpos(2 * j + 1)], d1);
                 }
                 if (last && a.dBp1) {
                     d0 += a.dBp1[((size_t)bh * R + r) * N + 2 * j];
@@ -512,7 +639,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
                 }
                 float e0 = d0, e1 = d1;
                 if (turns) {
-                    const float b0 = sBt[k][r][colpos(2 * j)], b1 = sBt[k][r][colpos(2 * j + 1)];
+                    const float b0 = sBt[k][r][bpos(2 * j)], b1 = sBt[k][r][bpos(2 * j + 1)];
                     lds_add(&sDPH[k][j], -d0 * b1 + d1 * b0);
                     e0 = d0 * cs[k] + d1 * sn[k];
                     e1 = -d0 * sn[k] + d1 * cs[k];
@@ -569,10 +696,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
     if (L > 0) {
         sX[0][r][j] = (xok && a.xp0) ? ld_io(a.xp0, ((size_t)bh * R + r) * P + j, io) : 0.f;
         const bool ok = pok && a.Bp0;
-        sBt[0][r][colpos(2 * j)] = ok ? ld_io(a.Bp0, ((size_t)bh * R + r) * N + 2 * j, io) : 0.f;
-        sBt[0][r][colpos(2 * j + 1)] = ok ? ld_io(a.Bp0, ((size_t)bh * R + r) * N + 2 * j + 1, io) : 0.f;
-        sW[0][r][2 * j] = 0.f;
-        sW[0][r][2 * j + 1] = 0.f;
+        sBt[0][r][bpos(2 * j)] = ok ? ld_io(a.Bp0, ((size_t)bh * R + r) * N + 2 * j, io) : 0.f;
+        sBt[0][r][bpos(2 * j + 1)] = ok ? ld_io(a.Bp0, ((size_t)bh * R + r) * N + 2 * j + 1, io) : 0.f;
+        sW[0][r][dpos(2 * j)] = 0.f;
+        sW[0][r][dpos(2 * j + 1)] = 0.f;
         if (tid == 0) sXV[0] = 0.f;
         __syncthreads();
         contract<R>(S, sX[0], sBt[0], sV[0], sW[0], prow, lg, l16);
@@ -585,8 +712,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
         }
         if (xok && a.dxp0) a.dxp0[((size_t)bh * R + r) * P + j] = be0 * sV[0][r][j];
         if (pok && a.dBp0) {
-            a.dBp0[((size_t)bh * R + r) * N + 2 * j] = be0 * sW[0][r][2 * j];
-            a.dBp0[((size_t)bh * R + r) * N + 2 * j + 1] = be0 * sW[0][r][2 * j + 1];
+            a.dBp0[((size_t)bh * R + r) * N + 2 * j] = be0 * sW[0][r][dpos(2 * j)];
+            a.dBp0[((size_t)bh * R + r) * N + 2 * j + 1] = be0 * sW[0][r][dpos(2 * j + 1)];
         }
         if (a.dh0) {
 #pragma unroll
