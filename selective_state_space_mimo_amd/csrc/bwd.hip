@@ -231,10 +231,10 @@ __device__ __forceinline__ float2 turn(float m0, float m1, bool turns, float c, 
 template <int R>
 __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
     __shared__ __align__(16) float sX[kT + 1][kR4][kPP];     // slot 0: x_prev (initial fold only)
-    __shared__ __align__(16) float sBt[kT + 1][kR4][kNN];    // turned B (bpos order); slot 0: B_prev
+    __shared__ __align__(16) float sBt[kT + 1][kR4][kNN];    // turned B; slot 0: B_prev
     __shared__ __align__(16) float sDY[kT][kR4][kPP];
-    __shared__ __align__(16) float sCt[kT][kR4][kNN];        // turned C (bpos order)
-    __shared__ float sDC[kT][kR4][kDPad];                   // U^T dy (dpos order), summed over waves
+    __shared__ __align__(16) float sCt[kT][kR4][kNN];        // turned C
+    __shared__ float sDC[kT][kR4][kNN];                     // U^T dy
     __shared__ float sDot[kT][kR4][4];                      // [r][r'] = X[r'] . dy[r]
     __shared__ float sDPH[kT][64];
     __shared__ float sDL[kT];
@@ -242,52 +242,62 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
     __shared__ float sRed[4];
 
     const int bh = blockIdx.x, H = a.H, bi = bh / H, h = bh % H, g = h * a.G / H;
-    const int L = a.L, P = a.P, N = a.N, np = a.np, io = a.io_bf16;
+    const int L = a.L, P = a.P, N = a.N, np = a.np;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lg = lane >> 4, l16 = lane & 15;
     // staging / output role: rank r = w, pair j (columns 2 j, 2 j + 1) and row j
     const int r = w, j = lane;
     const bool pok = r < R && 2 * j < N, xok = r < R && j < P, turns = pok && j < np;
-    const int prow = 16 * w + 4 * lg;
+    // The replay's state layout: wave w owns columns 32 w .. 32 w + 31 of every row, lane
+    // (lg, l16) rows 16 pt + 4 lg + v of columns 32 w + 16 c + l16, so the readout U^T dy
+    // (a sum over rows) finishes inside the wave.
+    const int ncol = 32 * w + l16;
 
-    float S[4][8];
+    float S[4][4][2];
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
+    for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            const int p = prow + v, n = 16 * nt + l16;
-            S[v][nt] = (a.h0 && p < P && n < N) ? ld_io(a.h0, ((size_t)bh * P + p) * N + n, a.st_bf16) : 0.f;
-        }
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int p = 16 * pt + 4 * lg + v, n = ncol + 16 * c;
+                S[pt][v][c] = (a.h0 && p < P && n < N) ? ld_io(a.h0, ((size_t)bh * P + p) * N + n, a.st_bf16) : 0.f;
+            }
     float bb0 = 0.f, bb1 = 0.f, cb0 = 0.f, cb1 = 0.f;
     if (pok && a.Bb) { bb0 = a.Bb[((size_t)h * R + r) * N + 2 * j]; bb1 = a.Bb[((size_t)h * R + r) * N + 2 * j + 1]; }
     if (pok && a.Cb) { cb0 = a.Cb[((size_t)h * R + r) * N + 2 * j]; cb1 = a.Cb[((size_t)h * R + r) * N + 2 * j + 1]; }
     float phi = (turns && a.phi0) ? a.phi0[(size_t)bh * np + j] : 0.f;
     float gC0 = 0.f, gC1 = 0.f;                 // C bias gradient partials
+
+    // rank-R write S += sum_q (f x_q[rows]) (x) b_q[cols] from staged rows
+    auto write = [&](const float (*sx)[kPP], const float (*sb)[kNN], float f) {
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const float b0 = sb[q][ncol], b1 = sb[q][ncol + 16];
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const float4 xv = ld4(&sx[q][16 * pt + 4 * lg]);
+                const float xq[4] = {f * xv.x, f * xv.y, f * xv.z, f * xv.w};
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    S[pt][v][0] = fmaf(xq[v], b0, S[pt][v][0]);
+                    S[pt][v][1] = fmaf(xq[v], b1, S[pt][v][1]);
+                }
+            }
+        }
+    };
     // the initial fold U_{-1} = H_0 + delta_0 X_prev^T B_prev
-    sX[0][r][j] = (xok && a.xp0) ? ld_io(a.xp0, ((size_t)bh * R + r) * P + j, io) : 0.f;
+    sX[0][r][j] = (xok && a.xp0) ? ld_io(a.xp0, ((size_t)bh * R + r) * P + j, a.io_bf16) : 0.f;
     {
         const bool ok = pok && a.Bp0;
-        sBt[0][r][bpos(2 * j)] = ok ? ld_io(a.Bp0, ((size_t)bh * R + r) * N + 2 * j, io) : 0.f;
-        sBt[0][r][bpos(2 * j + 1)] = ok ? ld_io(a.Bp0, ((size_t)bh * R + r) * N + 2 * j + 1, io) : 0.f;
+        sBt[0][r][2 * j] = ok ? ld_io(a.Bp0, ((size_t)bh * R + r) * N + 2 * j, a.io_bf16) : 0.f;
+        sBt[0][r][2 * j + 1] = ok ? ld_io(a.Bp0, ((size_t)bh * R + r) * N + 2 * j + 1, a.io_bf16) : 0.f;
     }
     if (tid == 0 && L > 0) {
         const size_t th = (size_t)bi * L * H + h;
         sDn[0] = a.dt[th] * (1.f - a.lam[th]);
     }
     __syncthreads();
-    if (L > 0) {
-        const float d0 = sDn[0];
-#pragma unroll
-        for (int q = 0; q < R; ++q) {
-            const float4 xv = ld4(&sX[0][q][prow]);
-            const float4 b0 = ld4(&sBt[0][q][l16 * 4]), b1 = ld4(&sBt[0][q][64 + l16 * 4]);
-            const float bq[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-            const float xq[4] = {d0 * xv.x, d0 * xv.y, d0 * xv.z, d0 * xv.w};
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-#pragma unroll
-                for (int nt = 0; nt < 8; ++nt) S[v][nt] = fmaf(xq[v], bq[nt], S[v][nt]);
-        }
-    }
+    if (L > 0) write(sX[0], sBt[0], sDn[0]);
     __syncthreads();
 
     for (int t0 = 0; t0 < L; t0 += kT) {
@@ -310,14 +320,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
                 const bool ok = valid && pok;
                 const float2 bt = turn(rg.b0[k] + bb0, rg.b1[k] + bb1, turns, cs[k], sn[k]);
                 const float2 ct = turn(rg.c0[k] + cb0, rg.c1[k] + cb1, turns, cs[k], sn[k]);
-                sBt[k + 1][r][bpos(2 * j)] = ok ? bt.x : 0.f;
-                sBt[k + 1][r][bpos(2 * j + 1)] = ok ? bt.y : 0.f;
-                sCt[k][r][bpos(2 * j)] = ok ? ct.x : 0.f;
-                sCt[k][r][bpos(2 * j + 1)] = ok ? ct.y : 0.f;
+                sBt[k + 1][r][2 * j] = ok ? bt.x : 0.f;
+                sBt[k + 1][r][2 * j + 1] = ok ? bt.y : 0.f;
+                sCt[k][r][2 * j] = ok ? ct.x : 0.f;
+                sCt[k][r][2 * j + 1] = ok ? ct.y : 0.f;
                 sX[k + 1][r][j] = (valid && xok) ? rg.x[k] : 0.f;
                 sDY[k][r][j] = (valid && xok) ? rg.dy[k] : 0.f;
-                sDC[k][r][dpos(2 * j)] = 0.f;
-                sDC[k][r][dpos(2 * j + 1)] = 0.f;
                 if (w == 0) sDPH[k][j] = 0.f;
             }
         }
@@ -335,56 +343,44 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
             sDL[tid] = 0.f;
         }
         __syncthreads();
-        // ---- per token (wave-local): U_t, then U_t^T dy_t; each token's operands are read
-        //      from LDS one token ahead, so the reads overlap the previous token's arithmetic ----
-        float4 nx[R], nb[R][2], nd[R];
-        float nal = 1.f, nco = 0.f;
-        auto fetch_tok = [&](int k) {
-#pragma unroll
-            for (int q = 0; q < R; ++q) {
-                nx[q] = ld4(&sX[k + 1][q][prow]);
-                nb[q][0] = ld4(&sBt[k + 1][q][l16 * 4]);
-                nb[q][1] = ld4(&sBt[k + 1][q][64 + l16 * 4]);
-                nd[q] = ld4(&sDY[k][q][prow]);
-            }
-            nal = sAl[k];
-            nco = sCo[k];
-        };
-        if (nv > 0) fetch_tok(0);
+        // ---- per token (wave-local): U_t, then U_t^T dy_t (complete per wave: plain stores) ----
         for (int k = 0; k < nv; ++k) {
-            float4 cx[R], cb[R][2], cd[R];
+            const float al = sAl[k];
 #pragma unroll
-            for (int q = 0; q < R; ++q) { cx[q] = nx[q]; cb[q][0] = nb[q][0]; cb[q][1] = nb[q][1]; cd[q] = nd[q]; }
-            const float al = nal, co = nco;
-            if (k + 1 < nv) fetch_tok(k + 1);
+            for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
+                for (int v = 0; v < 4; ++v) {
+                    S[pt][v][0] *= al;
+                    S[pt][v][1] *= al;
+                }
+            write(sX[k + 1], sBt[k + 1], sCo[k]);
+            float part[4][2];
 #pragma unroll
-                for (int nt = 0; nt < 8; ++nt) S[v][nt] *= al;
+            for (int q = 0; q < 4; ++q) {
+                part[q][0] = part[q][1] = 0.f;
+                if (q < R) {
 #pragma unroll
-            for (int q = 0; q < R; ++q) {
-                const float bc[8] = {cb[q][0].x, cb[q][0].y, cb[q][0].z, cb[q][0].w,
-                                     cb[q][1].x, cb[q][1].y, cb[q][1].z, cb[q][1].w};
-                const float ac[4] = {co * cx[q].x, co * cx[q].y, co * cx[q].z, co * cx[q].w};
+                    for (int pt = 0; pt < 4; ++pt) {
+                        const float4 d = ld4(&sDY[k][q][16 * pt + 4 * lg]);
+                        const float dq[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-#pragma unroll
-                    for (int nt = 0; nt < 8; ++nt) S[v][nt] = fmaf(ac[v], bc[nt], S[v][nt]);
+                        for (int v = 0; v < 4; ++v) {
+                            part[q][0] = fmaf(S[pt][v][0], dq[v], part[q][0]);
+                            part[q][1] = fmaf(S[pt][v][1], dq[v], part[q][1]);
+                        }
+                    }
+                }
             }
-            float part[R][8];
+            // sum over the four 16-lane groups, scattered: group lg keeps rank lg's two columns
+            float k4[4];
+            const bool h2 = lg & 2, h1 = lg & 1;
 #pragma unroll
-            for (int q = 0; q < R; ++q) {
-                const float4 d = cd[q];
-#pragma unroll
-                for (int nt = 0; nt < 8; ++nt)
-                    part[q][nt] = S[0][nt] * d.x + S[1][nt] * d.y + S[2][nt] * d.z + S[3][nt] * d.w;
+            for (int i = 0; i < 4; ++i) k4[i] = rs32(part[i >> 1][i & 1], part[2 + (i >> 1)][i & 1], h2);
+            const float o0 = rs16(k4[0], k4[2], h1), o1 = rs16(k4[1], k4[3], h1);
+            if (lg < R) {
+                sDC[k][lg][ncol] = o0;
+                sDC[k][lg][ncol + 16] = o1;
             }
-            float red[R][2];
-            rs_groups<R>(part, red, lg);
-#pragma unroll
-            for (int q = 0; q < R; ++q)
-#pragma unroll
-                for (int i = 0; i < 2; ++i) lds_add(&sDC[k][q][dpos(16 * (2 * lg + i) + l16)], red[q][i]);
         }
         __syncthreads();
         // ---- per token R x R dots X[r'] . dy[r] (wave r) ----
@@ -404,15 +400,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
             const size_t tok = (size_t)bi * L + t0 + k;
             float dl = 0.f;
             if (pok) {
-                float d0 = sDC[k][r][dpos(2 * j)], d1 = sDC[k][r][dpos(2 * j + 1)];
+                float d0 = sDC[k][r][2 * j], d1 = sDC[k][r][2 * j + 1];
                 const float dn = sDn[k];
 #pragma unroll
                 for (int q = 0; q < R; ++q) {
                     const float m = -dn * sDot[k][r][q];
-                    d0 = fmaf(m, sBt[k + 1][q][bpos(2 * j)], d0);
-                    d1 = fmaf(m, sBt[k + 1][q][bpos(2 * j + 1)], d1);
+                    d0 = fmaf(m, sBt[k + 1][q][2 * j], d0);
+                    d1 = fmaf(m, sBt[k + 1][q][2 * j + 1], d1);
                 }
-                const float c0 = sCt[k][r][bpos(2 * j)], c1 = sCt[k][r][bpos(2 * j + 1)];
+                const float c0 = sCt[k][r][2 * j], c1 = sCt[k][r][2 * j + 1];
                 dl = c0 * d0 + c1 * d1;
                 float e0 = d0, e1 = d1;
                 if (turns) {
@@ -438,12 +434,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
     float fin = 0.f;
     if (a.dh1) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+        for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
-                const int p = prow + v, n = 16 * nt + l16;
-                if (p < P && n < N) fin += S[v][nt] * a.dh1[((size_t)bh * P + p) * N + n];
-            }
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const int p = 16 * pt + 4 * lg + v, n = ncol + 16 * c;
+                    if (p < P && n < N) fin += S[pt][v][c] * a.dh1[((size_t)bh * P + p) * N + n];
+                }
     }
     fin = wave_sum(fin);
     if (lane == 0) sRed[w] = fin;
