@@ -47,17 +47,14 @@ namespace m3 {
 namespace {
 
 constexpr int kT = 8;                 // tokens per staged group (replay)
-constexpr int kTA = 7;                // tokens per staged group (adjoint: its LDS fits two groups per CU)
+constexpr int kTA = 4;                // tokens per staged group (adjoint: per-wave partial rows fit two groups per CU)
 constexpr int kR4 = 4, kPP = 64, kNN = 128, kThreads = 256;
 
 // Turned B and C rows keep column n = 16 nt + l16 at 64 (nt / 4) + 4 l16 + nt % 4: a lane's
 // eight columns are two 16-byte runs, and the 16 lanes of a row group read 64 consecutive
 // words per access (no bank conflict; the four row groups read the same words).
 __device__ __forceinline__ int bpos(int n) { return ((n >> 6) << 6) + ((n & 15) << 2) + ((n >> 4) & 3); }
-// Rows summed over the waves by LDS adds keep column n at n + 16 (n / 32): the four 16-lane
-// groups of one add (columns 32 lg + 16 i + l16) then fall on distinct banks.
-constexpr int kDPad = kNN + 48;
-__device__ __forceinline__ int dpos(int n) { return n + ((n >> 5) << 4); }
+
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
@@ -458,7 +455,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
 // into sw (both [R4][..] rows of that token)
 template <int R>
 __device__ __forceinline__ void contract(const float (&S)[4][8], const float (*sx)[kPP], const float (*sb)[kNN],
-                                         float (*sv)[kPP], float (*sw)[kDPad], int prow, int lg, int l16) {
+                                         float (*sv)[kPP], float (*sw)[kNN], int prow, int lg, int l16) {
     float vp[16];
     float wp[R][8];
 #pragma unroll
@@ -488,7 +485,7 @@ __device__ __forceinline__ void contract(const float (&S)[4][8], const float (*s
 #pragma unroll
     for (int qq = 0; qq < R; ++qq)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) lds_add(&sw[qq][dpos(16 * (2 * lg + i) + l16)], red[qq][i]);
+        for (int i = 0; i < 2; ++i) sw[qq][16 * (2 * lg + i) + l16] = red[qq][i];
 }
 
 template <int R>
@@ -498,7 +495,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
     __shared__ __align__(16) float sDY[kTA][kR4][kPP];
     __shared__ __align__(16) float sCt[kTA][kR4][kNN];        // turned C (bpos order)
     __shared__ float sV[kTA][kR4][kPP];         // v = G_{t+1} Bt_t
-    __shared__ float sW[kTA][kR4][kDPad];       // w = G_{t+1}^T X_t (dpos order)
+    __shared__ float sW[kTA][4][kR4][kNN];      // w = G_{t+1}^T X_t: each wave's partial (its 16 rows)
     __shared__ float sDot[kTA][kR4][8];         // [r][r'] = Ct[r'] . Bt[r], [r][4 + r'] = dy[r'] . X[r]
     __shared__ float sXV[kTA];                  // X_t . v
     __shared__ float sDPH[kTA][64];
@@ -549,8 +546,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
                 sCt[k][r][bpos(2 * j + 1)] = ok ? ct.y : 0.f;
                 sX[k][r][j] = (valid && xok) ? rg.x[k] : 0.f;
                 sDY[k][r][j] = (valid && xok) ? rg.dy[k] : 0.f;
-                sW[k][r][dpos(2 * j)] = 0.f;
-                sW[k][r][dpos(2 * j + 1)] = 0.f;
                 if (w == 0) sDPH[k][j] = 0.f;
             }
         }
@@ -573,7 +568,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
         __syncthreads();
         // ---- per token, last first (wave-local): v, w against G_{t+1}, then G_t ----
         for (int k = nv - 1; k >= 0; --k) {
-            contract<R>(S, sX[k], sBt[k], sV[k], sW[k], prow, lg, l16);
+            contract<R>(S, sX[k], sBt[k], sV[k], sW[k][w], prow, lg, l16);
             const float al1 = sAl[k + 1];
 #pragma unroll
             for (int v = 0; v < 4; ++v)
@@ -624,7 +619,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
                 st_io(a.dx, ((tok * H + h) * R + r) * P + j, dxv, io);
             }
             if (pok) {
-                float d0 = kap * sW[k][r][dpos(2 * j)], d1 = kap * sW[k][r][dpos(2 * j + 1)];
+                const float w0 = sW[k][0][r][2 * j] + sW[k][1][r][2 * j] + sW[k][2][r][2 * j] + sW[k][3][r][2 * j];
+                const float w1 = sW[k][0][r][2 * j + 1] + sW[k][1][r][2 * j + 1] + sW[k][2][r][2 * j + 1] +
+                                 sW[k][3][r][2 * j + 1];
+                float d0 = kap * w0, d1 = kap * w1;
 #pragma unroll
                 for (int q = 0; q < R; ++q) {
                     const float m = ga * sDot[k][r][4 + q];
@@ -696,11 +694,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
         const bool ok = pok && a.Bp0;
         sBt[0][r][bpos(2 * j)] = ok ? ld_io(a.Bp0, ((size_t)bh * R + r) * N + 2 * j, io) : 0.f;
         sBt[0][r][bpos(2 * j + 1)] = ok ? ld_io(a.Bp0, ((size_t)bh * R + r) * N + 2 * j + 1, io) : 0.f;
-        sW[0][r][dpos(2 * j)] = 0.f;
-        sW[0][r][dpos(2 * j + 1)] = 0.f;
         if (tid == 0) sXV[0] = 0.f;
         __syncthreads();
-        contract<R>(S, sX[0], sBt[0], sV[0], sW[0], prow, lg, l16);
+        contract<R>(S, sX[0], sBt[0], sV[0], sW[0][w], prow, lg, l16);
         __syncthreads();
         // sAl[0], sBe[0], ... still hold token 0 (the last group staged)
         const float al0 = sAl[0], be0 = sBe[0];
@@ -710,8 +706,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
         }
         if (xok && a.dxp0) a.dxp0[((size_t)bh * R + r) * P + j] = be0 * sV[0][r][j];
         if (pok && a.dBp0) {
-            a.dBp0[((size_t)bh * R + r) * N + 2 * j] = be0 * sW[0][r][dpos(2 * j)];
-            a.dBp0[((size_t)bh * R + r) * N + 2 * j + 1] = be0 * sW[0][r][dpos(2 * j + 1)];
+            a.dBp0[((size_t)bh * R + r) * N + 2 * j] =
+                be0 * (sW[0][0][r][2 * j] + sW[0][1][r][2 * j] + sW[0][2][r][2 * j] + sW[0][3][r][2 * j]);
+            a.dBp0[((size_t)bh * R + r) * N + 2 * j + 1] =
+                be0 * (sW[0][0][r][2 * j + 1] + sW[0][1][r][2 * j + 1] + sW[0][2][r][2 * j + 1] + sW[0][3][r][2 * j + 1]);
         }
         if (a.dh0) {
 #pragma unroll
