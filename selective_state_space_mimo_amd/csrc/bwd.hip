@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
     __shared__ __align__(16) float sCt[kT][kR4][kNN];        // turned C
     __shared__ float sDC[kT][kR4][kNN];                     // U^T dy
     __shared__ float sDot[kT][kR4][4];                      // [r][r'] = X[r'] . dy[r]
-    __shared__ float sDPH[kT][64];
+    __shared__ float sDPH[kT][kR4][64];                     // C side of the angle gradient, per rank
     __shared__ float sDL[kT];
     __shared__ float sAl[kT], sCo[kT], sDn[kT];             // alpha_t, gamma_t + delta_{t+1}, delta_{t+1}
     __shared__ float sRed[4];
@@ -323,7 +323,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
                 sCt[k][r][2 * j + 1] = ok ? ct.y : 0.f;
                 sX[k + 1][r][j] = (valid && xok) ? rg.x[k] : 0.f;
                 sDY[k][r][j] = (valid && xok) ? rg.dy[k] : 0.f;
-                if (w == 0) sDPH[k][j] = 0.f;
             }
         }
         if (tid < kT) {
@@ -395,7 +394,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
         // ---- per token outputs: dC (corrected, turned back), bias partials, angle and <dy, y> terms ----
         for (int k = 0; k < nv; ++k) {
             const size_t tok = (size_t)bi * L + t0 + k;
-            float dl = 0.f;
+            float dl = 0.f, dph = 0.f;
             if (pok) {
                 float d0 = sDC[k][r][2 * j], d1 = sDC[k][r][2 * j + 1];
                 const float dn = sDn[k];
@@ -409,7 +408,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
                 dl = c0 * d0 + c1 * d1;
                 float e0 = d0, e1 = d1;
                 if (turns) {
-                    lds_add(&sDPH[k][j], -d0 * c1 + d1 * c0);
+                    dph = -d0 * c1 + d1 * c0;
                     e0 = d0 * cs[k] + d1 * sn[k];
                     e1 = -d0 * sn[k] + d1 * cs[k];
                 }
@@ -419,12 +418,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
                 gC0 += e0;
                 gC1 += e1;
             }
+            sDPH[k][r][j] = dph;
             dl = wave_sum(dl);
             if (lane == 0 && r < R) lds_add(&sDL[k], dl);
         }
         __syncthreads();
         if (w == 0 && j < np)
-            for (int k = 0; k < nv; ++k) a.wdphi[(((size_t)bi * L + t0 + k) * H + h) * np + j] = sDPH[k][j];
+            for (int k = 0; k < nv; ++k)
+                a.wdphi[(((size_t)bi * L + t0 + k) * H + h) * np + j] =
+                    sDPH[k][0][j] + sDPH[k][1][j] + sDPH[k][2][j] + sDPH[k][3][j];
         if (tid < nv) a.wdl[((size_t)bi * L + t0 + tid) * H + h] = sDL[tid];
     }
     // <dH_L, H_L>, the final state's reader term of the last token (U_{L-1} = H_{L-1})
@@ -498,7 +500,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
     __shared__ float sW[kTA][4][kR4][kNN];      // w = G_{t+1}^T X_t: each wave's partial (its 16 rows)
     __shared__ float sDot[kTA][kR4][8];         // [r][r'] = Ct[r'] . Bt[r], [r][4 + r'] = dy[r'] . X[r]
     __shared__ float sXV[kTA];                  // X_t . v
-    __shared__ float sDPH[kTA][64];
+    __shared__ float sDPH[kTA][kR4][64];        // B side of the angle gradient, per rank
+    __shared__ float sPC[kTA][64], sTh[kTA][64]; // C side (from the replay) and the rates, per pair
+    __shared__ float sDLp[kTA];                 // <dy_t, y_t> (from the replay)
     __shared__ float sAl[kTA + 1], sBe[kTA + 1], sGa[kTA + 1], sDt[kTA + 1], sLm[kTA + 1], sRt[kTA + 1], sU[kTA + 1];
 
     const int bh = blockIdx.x, H = a.H, bi = bh / H, h = bh % H, g = h * a.G / H;
@@ -546,7 +550,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
                 sCt[k][r][bpos(2 * j + 1)] = ok ? ct.y : 0.f;
                 sX[k][r][j] = (valid && xok) ? rg.x[k] : 0.f;
                 sDY[k][r][j] = (valid && xok) ? rg.dy[k] : 0.f;
-                if (w == 0) sDPH[k][j] = 0.f;
             }
         }
         if (tid <= kTA) {
@@ -563,7 +566,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
                 ga = lm * dtv;
             }
             sAl[tid] = al; sBe[tid] = be; sGa[tid] = ga; sDt[tid] = dtv; sLm[tid] = lm; sRt[tid] = rt; sU[tid] = u;
-            if (tid < kTA) sXV[tid] = 0.f;
+            if (tid < kTA) {
+                sXV[tid] = 0.f;
+                sDLp[tid] = t0 + tid < L ? a.wdl[((size_t)bi * L + t0 + tid) * H + h] : 0.f;
+            }
+        }
+        if (w == 0 && j < np) {
+            // the replay's angle terms and the rates, read here rather than in the sequential chain below
+#pragma unroll
+            for (int k = 0; k < kTA; ++k) {
+                const size_t th = ((size_t)bi * L + t0 + min(k, nv - 1)) * H + h;
+                sPC[k][j] = a.wdphi[th * np + j];
+                sTh[k][j] = a.theta[th * np + j];
+            }
         }
         __syncthreads();
         // ---- per token, last first (wave-local): v, w against G_{t+1}, then G_t ----
@@ -611,6 +626,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
             const size_t tok = (size_t)bi * L + t;
             const bool last = t == L - 1;
             const float ga = sGa[k], kap = ga * sAl[k + 1] + sBe[k + 1];
+            float dph = 0.f;
             if (xok) {
                 float dxv = kap * sV[k][r][j];
 #pragma unroll
@@ -636,7 +652,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
                 float e0 = d0, e1 = d1;
                 if (turns) {
                     const float b0 = sBt[k][r][bpos(2 * j)], b1 = sBt[k][r][bpos(2 * j + 1)];
-                    lds_add(&sDPH[k][j], -d0 * b1 + d1 * b0);
+                    dph = -d0 * b1 + d1 * b0;
                     e0 = d0 * cs[k] + d1 * sn[k];
                     e1 = -d0 * sn[k] + d1 * cs[k];
                 }
@@ -646,6 +662,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
                 gB0 += e0;
                 gB1 += e1;
             }
+            sDPH[k][r][j] = dph;
         }
         __syncthreads();
         // ---- wave 0: angle sensitivities, then lane 0's scalar chain, last token first ----
@@ -655,9 +672,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
                 const size_t th = ((size_t)bi * L + t) * H + h;
                 float tp = 0.f;
                 if (j < np) {
-                    Phi += sDPH[k][j] + a.wdphi[th * np + j];
+                    Phi += sDPH[k][0][j] + sDPH[k][1][j] + sDPH[k][2][j] + sDPH[k][3][j] + sPC[k][j];
                     a.dtheta[th * np + j] = sDt[k] * Phi;
-                    tp = a.theta[th * np + j] * Phi;
+                    tp = sTh[k][j] * Phi;
                 }
                 tp = wave_sum(tp);
                 if (lane == 0) {
@@ -670,7 +687,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
                     const float al1 = sAl[k + 1], be1 = sBe[k + 1];
                     const float dbe1 = has_next ? sXV[k] : 0.f;       // d beta_{t+1}
                     const float dga = al1 * sXV[k] + dots;             // d gamma_t
-                    float dl = a.wdl[th] - sGa[k] * dga - be1 * dbe1;
+                    float dl = sDLp[k] - sGa[k] * dga - be1 * dbe1;
                     if (t == L - 1) dl += a.wdlf[bh];
                     Sl += dl;                                          // d loss / d log alpha_t
                     if (has_next) {
