@@ -530,12 +530,42 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
     // pending step / blend gradients, the static rate's sum)
     float Sl = 0.f, pend_dt = 0.f, pend_lm = 0.f, dA_sum = 0.f;
 
+    // The next group's raw inputs are loaded into registers while the current group computes:
+    // its rows (every thread), the replay's angle terms and the rates (wave 0), the per-token
+    // scalars and <dy, y> (threads 0 .. kTA).
+    RawGroup<kTA> nrg;
+    float npc[kTA], nth[kTA], ndt = 0.f, nlm = 0.f, nu = 0.f, ndl = 0.f;
+    auto prefetch = [&](int t0n) {
+        const int nvn = min(kTA, L - t0n);
+        load_group_io<kTA>(nrg, a, bi, h, g, r, j, t0n, nvn, a.wphi, false);
+        if (w == 0 && j < np) {
+#pragma unroll
+            for (int k = 0; k < kTA; ++k) {
+                const size_t th = ((size_t)bi * L + t0n + min(k, nvn - 1)) * H + h;
+                npc[k] = a.wdphi[th * np + j];
+                nth[k] = a.theta[th * np + j];
+            }
+        }
+        if (tid <= kTA && t0n + tid < L) {
+            const size_t th = ((size_t)bi * L + t0n + tid) * H + h;
+            ndt = a.dt[th];
+            nlm = a.lam[th];
+            nu = a.A[a.rate_law ? th : (size_t)h];
+            ndl = a.wdl[th];
+        }
+    };
+    if (L > 0) prefetch(((L - 1) / kTA) * kTA);
+
     for (int t0 = ((L - 1) / kTA) * kTA; t0 >= 0; t0 -= kTA) {
         const int nv = min(kTA, L - t0);
         float cs[kTA], sn[kTA];
         {
-            RawGroup<kTA> rg;
-            load_group_io<kTA>(rg, a, bi, h, g, r, j, t0, nv, a.wphi, false);
+            const RawGroup<kTA> rg = nrg;
+            float pc[kTA], thr[kTA];
+#pragma unroll
+            for (int k = 0; k < kTA; ++k) { pc[k] = npc[k]; thr[k] = nth[k]; }
+            const float dtv0 = ndt, lm0 = nlm, u0 = nu, dl0 = ndl;
+            if (t0 >= kTA) prefetch(t0 - kTA);
 #pragma unroll
             for (int k = 0; k < kTA; ++k) {
                 const bool valid = k < nv;
@@ -551,33 +581,30 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
                 sX[k][r][j] = (valid && xok) ? rg.x[k] : 0.f;
                 sDY[k][r][j] = (valid && xok) ? rg.dy[k] : 0.f;
             }
-        }
-        if (tid <= kTA) {
-            // slot kTA is token t0 + kTA (the first of the group done before), or past the end:
-            // there alpha = 1 and beta = 0 stand for the final carry
-            float al = 1.f, be = 0.f, ga = 0.f, dtv = 0.f, lm = 0.f, rt = 0.f, u = 0.f;
-            if (t0 + tid < L) {
-                const size_t th = ((size_t)bi * L + t0 + tid) * H + h;
-                dtv = a.dt[th]; lm = a.lam[th];
-                u = a.rate_law ? a.A[th] : 0.f;
-                rt = rate_of(a, h, th);
-                al = expf(dtv * rt);
-                be = al * dtv * (1.f - lm);
-                ga = lm * dtv;
-            }
-            sAl[tid] = al; sBe[tid] = be; sGa[tid] = ga; sDt[tid] = dtv; sLm[tid] = lm; sRt[tid] = rt; sU[tid] = u;
-            if (tid < kTA) {
-                sXV[tid] = 0.f;
-                sDLp[tid] = t0 + tid < L ? a.wdl[((size_t)bi * L + t0 + tid) * H + h] : 0.f;
-            }
-        }
-        if (w == 0 && j < np) {
-            // the replay's angle terms and the rates, read here rather than in the sequential chain below
+            if (w == 0 && j < np) {
 #pragma unroll
-            for (int k = 0; k < kTA; ++k) {
-                const size_t th = ((size_t)bi * L + t0 + min(k, nv - 1)) * H + h;
-                sPC[k][j] = a.wdphi[th * np + j];
-                sTh[k][j] = a.theta[th * np + j];
+                for (int k = 0; k < kTA; ++k) {
+                    sPC[k][j] = pc[k];
+                    sTh[k][j] = thr[k];
+                }
+            }
+            if (tid <= kTA) {
+                // slot kTA is token t0 + kTA (the first of the group done before), or past the end:
+                // there alpha = 1 and beta = 0 stand for the final carry
+                float al = 1.f, be = 0.f, ga = 0.f, dtv = 0.f, lm = 0.f, rt = 0.f, u = 0.f;
+                if (t0 + tid < L) {
+                    dtv = dtv0; lm = lm0;
+                    u = a.rate_law ? u0 : 0.f;
+                    rt = a.rate_law ? heavy_tail_rate(u0) : -expf(u0);
+                    al = expf(dtv * rt);
+                    be = al * dtv * (1.f - lm);
+                    ga = lm * dtv;
+                }
+                sAl[tid] = al; sBe[tid] = be; sGa[tid] = ga; sDt[tid] = dtv; sLm[tid] = lm; sRt[tid] = rt; sU[tid] = u;
+                if (tid < kTA) {
+                    sXV[tid] = 0.f;
+                    sDLp[tid] = t0 + tid < L ? dl0 : 0.f;
+                }
             }
         }
         __syncthreads();
