@@ -15,10 +15,13 @@
 // "Computing the rotation as a data-dependent RoPE" and "MIMO: a rank-4 state update".
 //
 // Two sweeps per (batch, head) stream, one workgroup (4 waves) each; the P x N fp32
-// state (P <= 64, N <= 128) lives in registers: wave w holds rows 16 w .. 16 w + 15,
-// lane (lg = lane / 16, l16 = lane % 16) rows 16 w + 4 lg + v (v < 4) of columns
-// 16 nt + l16 (nt < 8).  Tokens are staged kT at a time in LDS; the per-token work is
-// wave-local (no barrier), the per-token outputs are formed after each group.
+// state (P <= 64, N <= 128) lives in registers, 32 values per lane (lg = lane / 16,
+// l16 = lane % 16).  The replay gives wave w the columns 32 w .. 32 w + 31 of every row
+// (its readout, a sum over rows, then finishes inside the wave); the sensitivity sweep gives
+// wave w the rows 16 w .. 16 w + 15 (its v, a sum over columns, finishes inside the wave,
+// and w = G^T X is kept as one partial row per wave, summed when a group's outputs are
+// formed).  Tokens are staged a group at a time in LDS; the per-token work is wave-local
+// (no barrier, no LDS atomics), the per-token outputs are formed after each group.
 //
 //   replay (forward): H_t again, token by token (never stored), read against dy:
 //     dCt_t[r] = H_t^T dy_t[r], <dy_t, y_t> = sum_r Ct_t[r] . dCt_t[r]; the running
