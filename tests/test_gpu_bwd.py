@@ -135,3 +135,58 @@ def test_scan_bwd_prefill_full_size(m3):
         _say("  stream (%d, %d): " % (bi, h) + " ".join("%s %.1e" % kv for kv in errs.items()))
         for k, e in errs.items():
             assert e <= 2e-2, (bi, h, k, e)
+
+
+def test_scan_bwd_continuation(m3):
+    """[DE] App C.2: gradients chain through the carries.  The backward of the
+    second segment, with the whole sequence's final-carry sensitivities, gives the
+    sensitivities of its initial carry; fed as the first segment's final-carry
+    sensitivities, the two segments' gradients equal the whole sequence's (f32,
+    rank 4, rotation, bias, 2 of 4 heads per group)."""
+    cfg, d = make_small_case(77, batch=2, seqlen=150, nheads=4, ngroups=2, headdim=64, dstate=128, rank=4,
+                             npairs=32, io_dtype="f32", rms_bc=True)
+    dy, dfin = make_cotangents(cfg, seed=8)
+    dev = torch.device("cuda:0")
+    f32 = torch.float32
+    t = to_device(d, f32, f32, dev)
+    dyt = tdev(dy, f32, dev)
+    dft = {k: tdev(v, f32, dev) for k, v in dfin.items()}
+    whole = m3.scan_bwd(t["x"], t["B"], t["C"], t["dt"], t["lam"], t["theta"], t["A_log"], t["B_bias"], t["C_bias"],
+                        t["init"], dyt, dfinal=dft)
+    cut = 64
+    sl = lambda v, a, b: None if v is None else v[:, a:b].contiguous()  # noqa: E731
+    seg = [{k: sl(t[k], 0, cut) for k in ("x", "B", "C", "dt", "lam", "theta")},
+           {k: sl(t[k], cut, 150) for k in ("x", "B", "C", "dt", "lam", "theta")}]
+    _, mid = m3.scan_fwd(seg[0]["x"], seg[0]["B"], seg[0]["C"], seg[0]["dt"], seg[0]["lam"], seg[0]["theta"],
+                         t["A_log"], t["B_bias"], t["C_bias"], t["init"], chunk=16, state_dtype=f32)
+    g2 = m3.scan_bwd(seg[1]["x"], seg[1]["B"], seg[1]["C"], seg[1]["dt"], seg[1]["lam"], seg[1]["theta"], t["A_log"],
+                     t["B_bias"], t["C_bias"], mid, dyt[:, cut:].contiguous(), dfinal=dft)
+    g1 = m3.scan_bwd(seg[0]["x"], seg[0]["B"], seg[0]["C"], seg[0]["dt"], seg[0]["lam"], seg[0]["theta"], t["A_log"],
+                     t["B_bias"], t["C_bias"], t["init"], dyt[:, :cut].contiguous(), dfinal=g2["init"])
+    torch.cuda.synchronize()
+    errs = {}
+    for k in ("x", "B", "C", "dt", "lam", "theta"):
+        errs[k] = rel_l2(np.concatenate([host(g1[k]), host(g2[k])], axis=1), host(whole[k]))
+    for k in ("A", "B_bias", "C_bias"):
+        errs[k] = rel_l2(host(g1[k]) + host(g2[k]), host(whole[k]))
+    for k in ("h", "phi", "B_prev", "x_prev"):
+        errs["init." + k] = rel_l2(host(g1["init"][k]), host(whole["init"][k]))
+    _say("  continuation: " + " ".join("%s %.1e" % kv for kv in errs.items()))
+    for k, e in errs.items():
+        assert e <= 1e-4, (k, e)
+
+
+def test_scan_bwd_bf16_state_and_groups(m3):
+    """A bf16 initial state (the decode workload's state dtype) and two groups of
+    two heads, against the oracle."""
+    cfg, d = make_small_case(404, batch=2, seqlen=33, nheads=4, ngroups=2, headdim=64, dstate=128, rank=2,
+                             npairs=16, io_dtype="bf16", state_dtype="bf16", rms_bc=True)
+    dy, dfin = make_cotangents(cfg, seed=9)
+    want = grad.scan_bwd(d, dy, dfin)
+    dev = torch.device("cuda:0")
+    t = to_device(d, torch.bfloat16, torch.bfloat16, dev)
+    g = m3.scan_bwd(t["x"], t["B"], t["C"], t["dt"], t["lam"], t["theta"], t["A_log"], t["B_bias"], t["C_bias"],
+                    t["init"], tdev(dy, torch.bfloat16, dev),
+                    dfinal={k: tdev(v, torch.float32, dev) for k, v in dfin.items()}, state_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    _compare(g, want, d, 2e-2, cfg.npairs)
