@@ -88,8 +88,8 @@ typedef struct {
     int chunk;        /* Q: chunk length of the chunked scan, 1..256 (m3_scan_fwd only).
                          A schedule parameter: the result does not depend on it beyond
                          rounding.  The bf16 matrix-core path (P = 64, N = 128,
-                         R in {1, 2, 4}, Q in {16, 32, 64, 128}) holds at most 256
-                         rows (Q R) per chunk; a longer request runs the
+                         R in {1, 2, 4}) runs chunks of 64 to 256 rows (Q R) with
+                         Q in {16, 32, 64, 128}; any other request there runs the
                          small-chunk schedule Q = 64 / R (64 rows per chunk; at
                          R = 4, 16 tokens, which also runs two workgroups per
                          compute unit). */

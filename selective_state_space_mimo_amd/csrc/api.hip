@@ -86,10 +86,13 @@ void choose_segments(const m3_desc* d, int Q, int* nseg, int* seglen) {
     const int nchunks = (L + Q - 1) / Q;
     int k = d->nsegments;
     if (k == 0) {
+        // When the (batch, head) streams alone cannot fill the compute units' workgroup
+        // slots (256 units, each holding one or two of the scan's workgroups), split each
+        // stream into just enough segments to fill them: every further segment costs a
+        // summary pass and a re-evaluation, and a partial wave of workgroups a tail.
         const long long streams = (long long)d->batch * d->nheads;
-        // Fill the 256 compute units with >= ~1024 workgroups when the
-        // (batch, head) streams alone are too few.
-        k = streams >= 512 ? 1 : (int)((1024 + streams - 1) / streams);
+        const long long slots = 256LL * scan_mfma_groups_per_cu(d->rank, Q);
+        k = streams >= slots ? 1 : (int)((slots + streams - 1) / streams);
     }
     k = std::max(1, std::min(k, std::max(1, nchunks)));
     const int cps = (nchunks + k - 1) / k;       // chunks per segment

@@ -107,6 +107,8 @@ int scan_generic_chunk(int P, int N, int R, int np, int Q);
 // The chunk the MFMA path runs for a requested chunk Q: at most 256 rows (Q R) per
 // chunk; a longer request is split, which changes rounding only.
 int scan_mfma_chunk(int io_bf16, int P, int N, int R, int Q);
+// Workgroups of the matrix-core scan that one compute unit holds at once for (R, Q).
+int scan_mfma_groups_per_cu(int R, int Q);
 bool scan_mfma_supported(const ScanArgs& a);
 hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t s);
 size_t scan_mfma_workspace_bytes(const ScanArgs& a);

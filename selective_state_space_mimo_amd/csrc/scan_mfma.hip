@@ -1237,8 +1237,11 @@ hipError_t launch_rq(const ScanArgs& a, hipStream_t st) {
 
 int scan_mfma_chunk(int io_bf16, int P, int N, int R, int Q) {
     if (!io_bf16 || P != kP || N != kN || !(R == 1 || R == 2 || R == 4)) return Q;
-    return Q * R > kMaxRows ? 64 / R : Q;        // oversize: the small-chunk schedule
+    const bool built = (Q == 16 || Q == 32 || Q == 64 || Q == 128) && Q * R >= 64 && Q * R <= kMaxRows;
+    return built ? Q : 64 / R;                   // otherwise the small-chunk schedule
 }
+
+int scan_mfma_groups_per_cu(int R, int Q) { return (R == 4 && Q == 16) ? 2 : 1; }
 
 bool scan_mfma_supported(const ScanArgs& a) {
     if (!a.io_bf16 || a.P != kP || a.N != kN) return false;
