@@ -12,7 +12,7 @@ import pytest
 
 from m3inputs import config_by_name, make_cotangents, make_scan_inputs, make_small_case
 from oracle import grad
-from tests._util import host, rel_l2, tdev, to_device
+from tests._util import host, pooled_signed, rel_l2, tdev, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -190,3 +190,55 @@ def test_scan_bwd_bf16_state_and_groups(m3):
                     dfinal={k: tdev(v, torch.float32, dev) for k, v in dfin.items()}, state_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     _compare(g, want, d, 2e-2, cfg.npairs)
+
+
+def _sweep_cases(n=12, seed=2027):
+    """Seeded random small shapes over what the backward supports (P <= 64, N <= 128,
+    R <= 4, any npairs <= N/2, groups dividing the heads, both rate laws, carries or
+    not, ragged lengths, both I/O dtypes)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        P = int(rng.choice([3, 8, 16, 33, 64]))
+        N = int(rng.choice([2, 6, 16, 40, 128]))
+        R = int(rng.integers(1, 5))
+        H = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([g for g in (1, 2, 4) if H % g == 0]))
+        c = dict(P=P, N=N, R=R, H=H, G=G, npairs=int(rng.integers(0, N // 2 + 1)),
+                 L=int(rng.integers(1, 41)), io=str(rng.choice(["f32", "bf16"])),
+                 heavy=bool(rng.integers(0, 2)), init=bool(rng.integers(0, 2)), final=bool(rng.integers(0, 2)))
+        if c["L"] == 1:
+            # one token and no carry: the angle gradient is zero by rotation invariance
+            # (test_scan_bwd_angle_invariance); keep a carry so that it is not
+            c["init"] = True
+        out.append(c)
+    return out
+
+
+@pytest.mark.parametrize("c", _sweep_cases(), ids=lambda c: "P%(P)d-N%(N)d-R%(R)d-H%(H)d-G%(G)d-np%(npairs)d-L%(L)d-%(io)s" % c)
+def test_scan_bwd_random_shapes(m3, c):
+    """Every gradient against the oracle on a seeded random shape, plus the
+    pooled signed error sum(gpu - oracle) / ||oracle||_1 as a bias check ([DE]
+    App C.4), at a quarter of the normwise tolerance."""
+    cfg, d = make_small_case(7000 + c["P"] + 3 * c["N"] + c["L"], batch=2, seqlen=c["L"], nheads=c["H"],
+                             ngroups=c["G"], headdim=c["P"], dstate=c["N"], rank=c["R"], npairs=c["npairs"],
+                             io_dtype=c["io"], init_full=c["init"], rate_dyn=c["heavy"])
+    dy, dfin = make_cotangents(cfg, seed=12, final=c["final"])
+    want = grad.scan_bwd(d, dy, dfin)
+    g = _run(m3, d, dy, dfin, c["io"])
+    tol = 1e-4 if c["io"] == "f32" else 2e-2
+    _compare(g, want, d, tol, cfg.npairs)
+    for gk, wk in (("x", "x"), ("B", "B"), ("dt", "dt")):
+        assert abs(pooled_signed(host(g[gk]), want[wk])) <= tol / 4, gk
+
+
+def test_scan_bwd_angle_invariance(m3):
+    """One token and no carry: B and C turn by the same angle, so every C . B product
+    and the output do not depend on it, and the angle gradients vanish (to rounding)."""
+    cfg, d = make_small_case(11, batch=2, seqlen=1, nheads=2, headdim=33, dstate=128, rank=2, npairs=45,
+                             io_dtype="f32", init_full=False)
+    dy, _ = make_cotangents(cfg, seed=4, final=False)
+    g = _run(m3, d, dy, None, "f32")
+    scale = float(np.abs(host(g["B"])).max())
+    assert float(np.abs(host(g["theta"])).max()) <= 1e-5 * scale
+    assert float(np.abs(host(g["init"]["phi"])).max()) <= 1e-5 * scale

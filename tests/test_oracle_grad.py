@@ -126,3 +126,17 @@ def test_heavy_tail_rate_grad():
     for v in (0.7, -0.4, -5.0):
         fd = (ref.heavy_tail_rate(v + h) - ref.heavy_tail_rate(v - h)) / (2 * h)
         assert grad.heavy_tail_rate_grad(v) == pytest.approx(float(fd), rel=1e-7)
+
+
+def test_angle_invariance_single_token():
+    """[M3] "Computing the rotation as a data-dependent RoPE": B and C turn by the same
+    angle, so with one token and no carry every C . B product is unchanged by it and
+    the angle gradients are zero (here to fp64 rounding), while the B, C gradients are not."""
+    cfg, inp = make_small_case(8, batch=1, seqlen=1, nheads=2, headdim=3, dstate=8, rank=2, npairs=4,
+                               init_full=False)
+    dy, _ = make_cotangents(cfg, seed=2, final=False)
+    g = grad.scan_bwd(inp, dy)
+    scale = float(np.abs(g["B"]).max())
+    assert scale > 1e-3
+    assert float(np.abs(g["theta"]).max()) <= 1e-13 * scale
+    assert float(np.abs(g["init"]["phi"]).max()) <= 1e-13 * scale
