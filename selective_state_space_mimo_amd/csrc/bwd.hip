@@ -383,8 +383,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
         }
         __syncthreads();
         // ---- per token R x R dots X[r'] . dy[r] (wave r) ----
+        // (the per-token loops of the dots and outputs run over the group's fixed size, tokens
+        // past the valid ones skipped, so that the wave reductions of different tokens interleave)
         if (r < R) {
-            for (int k = 0; k < nv; ++k) {
+#pragma unroll
+            for (int k = 0; k < kT; ++k) {
+                if (k >= nv) break;
                 float d4[4];
                 const float dyr = xok ? sDY[k][r][j] : 0.f;
 #pragma unroll
@@ -395,7 +399,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
         }
         __syncthreads();
         // ---- per token outputs: dC (corrected, turned back), bias partials, angle and <dy, y> terms ----
-        for (int k = 0; k < nv; ++k) {
+#pragma unroll
+        for (int k = 0; k < kT; ++k) {
+            if (k >= nv) break;
             const size_t tok = (size_t)bi * L + t0 + k;
             float dl = 0.f, dph = 0.f;
             if (pok) {
@@ -633,8 +639,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
         }
         __syncthreads();
         // ---- per token R x R dot products and X . v ----
-        for (int k = 0; k < nv; ++k) {
-            if (r < R) {
+        // (these per-token loops and wave 0's run over the group's fixed size, tokens past the
+        // valid ones skipped, so that the reductions and loads of different tokens interleave)
+#pragma unroll
+        for (int k = 0; k < kTA; ++k) {
+            if (k < nv && r < R) {
                 float d8[8];
                 const float b0 = sBt[k][r][bpos(2 * j)], b1 = sBt[k][r][bpos(2 * j + 1)];
                 const float xr = sX[k][r][j];
@@ -651,7 +660,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
         }
         __syncthreads();
         // ---- per token outputs: dx, dB (turned back), bias partials, angle terms ----
-        for (int k = 0; k < nv; ++k) {
+#pragma unroll
+        for (int k = 0; k < kTA; ++k) {
+            if (k >= nv) break;
             const int t = t0 + k;
             const size_t tok = (size_t)bi * L + t;
             const bool last = t == L - 1;
@@ -697,7 +708,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
         __syncthreads();
         // ---- wave 0: angle sensitivities, then lane 0's scalar chain, last token first ----
         if (w == 0) {
-            for (int k = nv - 1; k >= 0; --k) {
+#pragma unroll
+            for (int k = kTA - 1; k >= 0; --k) {
+                if (k >= nv) continue;
                 const int t = t0 + k;
                 const size_t th = ((size_t)bi * L + t) * H + h;
                 float tp = 0.f;
