@@ -216,6 +216,12 @@ __device__ __forceinline__ void load_group_io(RawGroup<KT>& g, const BwdArgs& a,
     if (a.io_bf16) load_group<KT, true>(g, a, bi, h, gr, r, j, t0, nv, ang, with_dt);
     else load_group<KT, false>(g, a, bi, h, gr, r, j, t0, nv, ang, with_dt);
 }
+// sin and cos of a phase in [0, 2 pi), as the forward pass turns B and C: the hardware form for
+// bf16 I/O (the matrix-core forward's), the full-precision one for f32 I/O (the f32 forward's)
+__device__ __forceinline__ void phase_sincos(float phi, bool fast, float* s, float* c) {
+    if (fast) __sincosf(phi, s, c);
+    else sincosf(phi, s, c);
+}
 __device__ __forceinline__ float2 turn(float m0, float m1, bool turns, float c, float s) {
     if (!turns) return make_float2(m0, m1);
     return make_float2(m0 * c - m1 * s, m0 * s + m1 * c);
@@ -314,7 +320,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_replay_kernel(BwdArgs a) {
                 cs[k] = 1.f; sn[k] = 0.f;
                 if (valid && turns) {
                     phi = wrap_2pi(phi + rg.dt[k] * rg.ang[k]);
-                    sincosf(phi, &sn[k], &cs[k]);
+                    phase_sincos(phi, a.io_bf16, &sn[k], &cs[k]);
                     if (r == 0) a.wphi[(tok * H + h) * np + j] = phi;
                 }
                 const bool ok = valid && pok;
@@ -579,7 +585,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_adjoint_kernel(BwdArgs a) {
             for (int k = 0; k < kTA; ++k) {
                 const bool valid = k < nv;
                 cs[k] = 1.f; sn[k] = 0.f;
-                if (valid && turns) sincosf(rg.ang[k], &sn[k], &cs[k]);
+                if (valid && turns) phase_sincos(rg.ang[k], io, &sn[k], &cs[k]);   // phases wrapped into [0, 2 pi)
                 const bool ok = valid && pok;
                 const float2 bt = turn(rg.b0[k] + bb0, rg.b1[k] + bb1, turns, cs[k], sn[k]);
                 const float2 ct = turn(rg.c0[k] + cb0, rg.c1[k] + cb1, turns, cs[k], sn[k]);
