@@ -28,7 +28,7 @@ __all__ = ["scan_fwd", "scan_bwd", "decode_step", "scan_workspace_size", "new_ca
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libm3scan.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError("libm3scan.so is not built: run __graft_entry__.build() "
-                      "(or python -m selective_state_space_mimo_amd.build)")
+                      "(or python selective_state_space_mimo_amd/build.py)")
 
 M3_F32, M3_BF16 = 0, 1
 M3_RATE_STATIC, M3_RATE_HEAVY_TAIL = 0, 1
