@@ -52,3 +52,20 @@ def phase_err(gpu_phi, ref_phi):
     if g.size == 0:
         return 0.0
     return float(max(np.abs(np.cos(g) - np.cos(r)).max(), np.abs(np.sin(g) - np.sin(r)).max()))
+
+
+ROW_TOL = 5e-2        # per-row bound for bf16 I/O (see row_errors)
+ROW_FLOOR = 0.5       # denominator floor, as a fraction of the RMS row norm
+
+
+def row_errors(g, r, floor_frac=None):
+    """Per-row errors of one stream's outputs [L, R, P]: ||g - r|| over P, divided
+    by max(||r||, ROW_FLOOR * the RMS row norm).  The floor keeps rows whose exact
+    value nearly cancels from being judged by relative rounding noise; a wrong
+    or dropped row still scores about 1."""
+    floor_frac = ROW_FLOOR if floor_frac is None else floor_frac
+    g = np.asarray(g, np.float64).reshape(-1, g.shape[-1])
+    r = np.asarray(r, np.float64).reshape(-1, r.shape[-1])
+    rn = np.linalg.norm(r, axis=1)
+    floor = floor_frac * float(np.sqrt(np.mean(rn * rn))) if rn.size else 0.0
+    return np.linalg.norm(g - r, axis=1) / np.maximum(rn, max(floor, 1e-30))

@@ -137,6 +137,30 @@ def test_scan_bwd_prefill_full_size(m3):
             assert e <= 2e-2, (bi, h, k, e)
 
 
+def test_scan_bwd_all_heads_shared_gradients(m3):
+    """One group shared by 64 heads (b 1, H 64, G 1, L 256, rank 4, bf16, rotation,
+    bias, carries): the gradients summed across heads -- dB, dC (over the 64 heads
+    of the group), d A_log (over tokens), the bias gradients -- and every per-head
+    gradient, against the oracle over all heads.  The kernels sum dB and dC over
+    heads with float atomics, so the order of the sums may change between runs:
+    a second run must agree to float rounding (bounded), and so must a third."""
+    cfg, d = make_small_case(31, batch=1, seqlen=256, nheads=64, ngroups=1, headdim=64, dstate=128, rank=4,
+                             npairs=32, io_dtype="bf16", rms_bc=True, init_full=True)
+    dy, dfin = make_cotangents(cfg, seed=3)
+    want = grad.scan_bwd(d, dy, dfin)
+    _say("  oracle done")
+    g = _run(m3, d, dy, dfin, "bf16")
+    _compare(g, want, d, 2e-2, cfg.npairs)
+    for gk, wk in (("B", "B"), ("C", "C"), ("A", "A_log"), ("B_bias", "B_bias"), ("C_bias", "C_bias")):
+        assert abs(pooled_signed(host(g[gk]), want[wk])) <= 5e-3, gk
+    for _ in range(2):
+        g2 = _run(m3, d, dy, dfin, "bf16")
+        drift = {k: rel_l2(host(g2[k]), host(g[k])) for k in ("B", "C", "A", "B_bias", "C_bias", "x", "dt")}
+        _say("  run-to-run drift: " + " ".join("%s %.1e" % kv for kv in drift.items()))
+        for k, e in drift.items():
+            assert e <= 2e-3, (k, e)
+
+
 def test_scan_bwd_continuation(m3):
     """[DE] App C.2: gradients chain through the carries.  The backward of the
     second segment, with the whole sequence's final-carry sensitivities, gives the
