@@ -281,6 +281,10 @@ m3_status m3_scan_fwd(const m3_desc* d, const void* x, const void* B, const void
     for (int i = 0; i < 4; ++i) {
         if (init && overlap(ry, ri[i])) return M3_ERR_INVALID_ARG;
         if (final_ && overlap(ry, rf[i])) return M3_ERR_INVALID_ARG;
+        // the final carry is written while other workgroups still read the inputs
+        if (final_)
+            for (const Range& r : ins)
+                if (overlap(rf[i], r)) return M3_ERR_INVALID_ARG;
     }
 
     ScanArgs a = make_scan_args(d, x, B, C, dt, lam, theta, A_log, B_bias, C_bias, init, y, final_);
@@ -293,6 +297,8 @@ m3_status m3_scan_fwd(const m3_desc* d, const void* x, const void* B, const void
             for (const Range& r : ins)
                 if (overlap(rw, r)) return M3_ERR_INVALID_ARG;
             if (overlap(rw, ry)) return M3_ERR_INVALID_ARG;
+            for (int i = 0; i < 4; ++i)
+                if ((init && overlap(rw, ri[i])) || (final_ && overlap(rw, rf[i]))) return M3_ERR_INVALID_ARG;
         }
         a.ws = static_cast<float*>(workspace);
         e = launch_scan_mfma(a, hs);
@@ -380,6 +386,15 @@ m3_status m3_block_fwd(const m3_desc* d, const m3_block_params* p, const void* z
         for (int i = 0; i < 4; ++i)
             for (int j = 0; j < 4; ++j)
                 if ((init && overlap(rf[i], ri[j])) || (j > i && overlap(rf[i], rf[j]))) return M3_ERR_INVALID_ARG;
+        // nor the raw inputs, the output or the workspace (written while they are read)
+        const size_t zx = cs.x / d->rank;
+        const Range others[] = {rng(z, zx), rng(x, zx), rng(B_raw, cs.bc), rng(C_raw, cs.bc), rng(dt_raw, cs.tok),
+                                rng(A, cs.alog), rng(lam_raw, cs.tok), rng(d->npairs ? th_raw : nullptr,
+                                                                             d->npairs ? cs.theta : 0),
+                                rng(out, zx), rng(workspace, block_ws(d, 0).total)};
+        for (int i = 0; i < 4; ++i)
+            for (const Range& r : others)
+                if (overlap(rf[i], r)) return M3_ERR_INVALID_ARG;
     }
     const BlockWs w = block_ws(d, 0);
     BlockArgs a = make_block_args(d, p, d->seqlen, z, x, B_raw, C_raw, dt_raw, lam_raw, th_raw, out, workspace, w);

@@ -176,3 +176,32 @@ def test_backward_entry_point_rejects_bad_arguments(m3):
     g = m3.Grads(FAKE + 0x1000000, FAKE + 0x1000010, FAKE + 0x1200000, FAKE + 0x1300000, FAKE + 0x1400000,
                  FAKE + 0x1500000, FAKE + 0x1600000, None, None, m3.CarryGrad(None, None, None, None))
     assert _bwd(m3, d, grads=g) == 1                       # dB overlaps dx
+
+
+def test_final_carry_must_not_overlap_inputs(m3):
+    """The final carry is written while other workgroups still read the inputs:
+    m3_scan_fwd and m3_block_fwd reject a final carry that overlaps any input,
+    the output or the workspace."""
+    d = _desc(m3)
+    p = dict(x=FAKE, B=FAKE + 0x100000, C=FAKE + 0x200000, dt=FAKE + 0x300000, lam=FAKE + 0x400000,
+             theta=FAKE + 0x500000, A_log=FAKE + 0x600000, y=FAKE + 0x700000)
+
+    def scan_with_final(fin):
+        return m3.lib.m3_scan_fwd(ctypes.byref(d), p["x"], p["B"], p["C"], p["dt"], p["lam"], p["theta"],
+                                  p["A_log"], None, None, None, p["y"], ctypes.byref(fin), None, 0, None)
+    ok = m3.Carry(FAKE + 0x800000, FAKE + 0x900000, FAKE + 0xa00000, FAKE + 0xb00000)
+    for k, bad in (("h", FAKE + 0x100000), ("phi", FAKE + 0x300000), ("B_prev", FAKE + 0x10),
+                   ("x_prev", FAKE + 0x600000)):
+        f = m3.Carry(ok.h, ok.phi, ok.B_prev, ok.x_prev)
+        setattr(f, k, bad)
+        assert scan_with_final(f) == 1, k
+    db = _desc(m3, rate_law=m3.M3_RATE_HEAVY_TAIL)
+    n = ctypes.c_size_t(0)
+    assert m3.lib.m3_block_workspace_size(ctypes.byref(db), 0, ctypes.byref(n)) == 0
+    prm = m3.BlockParams(None, None, None, None, None, FAKE + 0x900000, FAKE + 0x940000, None, 1e-6)
+    for bad in (FAKE + 0x200000, FAKE + 0x700000, FAKE + 0x1000000):      # B_raw, out, workspace
+        f = m3.Carry(bad, FAKE + 0x2900000, FAKE + 0x2a00000, FAKE + 0x2b00000)
+        assert m3.lib.m3_block_fwd(ctypes.byref(db), ctypes.byref(prm), FAKE, FAKE + 0x100000, FAKE + 0x200000,
+                                   FAKE + 0x300000, FAKE + 0x400000, FAKE + 0x500000, FAKE + 0x600000,
+                                   FAKE + 0x680000, None, FAKE + 0x700000, ctypes.byref(f), FAKE + 0x1000000,
+                                   n.value, None) == 1, hex(bad)
