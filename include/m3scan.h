@@ -36,8 +36,9 @@
  *     synchronises; work is enqueued on `stream` and runs asynchronously.
  *   - Errors are returned as m3_status; nothing is launched when a call
  *     returns an error found during argument checking.
- *   - No mutable global state: calls are thread-safe.  Calls whose output
- *     buffers overlap must not run concurrently.
+ *   - Calls are thread-safe.  The only mutable global state is the per-GPU
+ *     address of m3_scan_fwd_noalloc's scratch, set once under a lock.  Calls
+ *     whose output buffers overlap must not run concurrently.
  */
 #ifndef M3SCAN_H
 #define M3SCAN_H
@@ -72,7 +73,8 @@ typedef enum {
     M3_ERR_INVALID_ARG = 1,   /* NULL pointer, bad shape, H % G != 0, npairs > N/2, small workspace, aliasing */
     M3_ERR_UNSUPPORTED = 2,   /* valid but not implemented (shape or dtype out of the supported range) */
     M3_ERR_ALIGNMENT = 3,     /* a tensor base is not 16-byte aligned */
-    M3_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+    M3_ERR_HIP = 4,           /* a HIP runtime call or kernel launch failed */
+    M3_ERR_TOO_LARGE = 5      /* m3_scan_fwd_noalloc: the schedule needs more scratch than it holds */
 } m3_status;
 
 /* Problem description.  All fields are logical sizes. */
@@ -141,6 +143,30 @@ m3_status m3_scan_fwd(const m3_desc* d,
                       const float* A_log, const float* B_bias, const float* C_bias,
                       const m3_carry* init, void* y, const m3_carry* final_,
                       void* workspace, size_t workspace_bytes, m3_stream_t stream);
+
+/* m3_scan_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * arguments, results and errors are those of m3_scan_fwd, without the workspace:
+ * the schedule's workspace (the segmented schedule's per-segment summaries,
+ * incoming states and phases) lives in a device array of the library, one per
+ * GPU, of m3_scan_noalloc_max_workspace() bytes (64 MiB), held from the first
+ * call on that GPU until the process ends.  A call whose schedule would need
+ * more (m3_scan_workspace_size(d) above that limit) returns M3_ERR_TOO_LARGE and
+ * launches nothing.  The call allocates and frees nothing.  Every call on one GPU
+ * uses that GPU's one array, so calls on one GPU whose work may overlap in time
+ * (different streams, different host threads) race and must be serialised by
+ * the caller; calls on one stream are ordered and safe.  The array needs no
+ * clearing between calls.  The current device (hipSetDevice) must be the device
+ * of `stream`. */
+m3_status m3_scan_fwd_noalloc(const m3_desc* d,
+                              const void* x, const void* B, const void* C,
+                              const float* dt, const float* lam, const float* theta,
+                              const float* A_log, const float* B_bias, const float* C_bias,
+                              const m3_carry* init, void* y, const m3_carry* final_,
+                              m3_stream_t stream);
+
+/* Bytes of device scratch m3_scan_fwd_noalloc holds per GPU (its limit). */
+size_t m3_scan_noalloc_max_workspace(void);
 
 /* One token for every (batch, head), the carry updated in place.
  *   x [b, H, R, P] io;  B, C [b, G, R, N] io;  dt, lam [b, H] f32;

@@ -22,7 +22,7 @@ import os
 
 import torch
 
-__all__ = ["scan_fwd", "scan_bwd", "decode_step", "scan_workspace_size", "new_carry", "M3Error",
+__all__ = ["scan_fwd", "scan_fwd_noalloc", "scan_bwd", "decode_step", "scan_workspace_size", "new_carry", "M3Error",
            "LIB_PATH", "lib", "Desc", "Carry", "M3_F32", "M3_BF16", "M3_RATE_STATIC", "M3_RATE_HEAVY_TAIL"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libm3scan.so")
@@ -32,7 +32,9 @@ if not os.path.exists(LIB_PATH):
 
 M3_F32, M3_BF16 = 0, 1
 M3_RATE_STATIC, M3_RATE_HEAVY_TAIL = 0, 1
-_STATUS = {0: "M3_OK", 1: "M3_ERR_INVALID_ARG", 2: "M3_ERR_UNSUPPORTED", 3: "M3_ERR_ALIGNMENT", 4: "M3_ERR_HIP"}
+M3_ERR_TOO_LARGE = 5
+_STATUS = {0: "M3_OK", 1: "M3_ERR_INVALID_ARG", 2: "M3_ERR_UNSUPPORTED", 3: "M3_ERR_ALIGNMENT", 4: "M3_ERR_HIP",
+           5: "M3_ERR_TOO_LARGE"}
 
 
 class Desc(ctypes.Structure):
@@ -175,6 +177,36 @@ def scan_fwd(x, B, C, dt, lam, theta, A_log, B_bias=None, C_bias=None, init=None
                          _ptr(workspace, dev, None, "workspace") if ws_bytes else None, ws_bytes, _stream(dev))
     _check(st, "m3_scan_fwd")
     return y, fin
+
+
+lib.m3_scan_fwd_noalloc.argtypes = [ctypes.POINTER(Desc)] + [_vp] * 9 + [ctypes.POINTER(Carry), _vp,
+                                                                       ctypes.POINTER(Carry), _vp]
+lib.m3_scan_fwd_noalloc.restype = ctypes.c_int
+lib.m3_scan_noalloc_max_workspace.argtypes = []
+lib.m3_scan_noalloc_max_workspace.restype = _sz
+
+
+def scan_fwd_noalloc(x, B, C, dt, lam, theta, A_log, B_bias=None, C_bias=None, init=None, *, y, final=None,
+                     chunk=64, state_dtype=torch.float32, nsegments=0, A_raw=None):
+    """Chunked scan without device allocation (``m3_scan_fwd_noalloc``): the
+    caller passes the output ``y`` and, optionally, the final carry dict
+    ``final``; the schedule's workspace is the library's per-GPU scratch.
+    Arguments otherwise as for :func:`scan_fwd`.  Returns (y, final)."""
+    dev = x.device
+    io = x.dtype
+    law = M3_RATE_STATIC if A_raw is None else M3_RATE_HEAVY_TAIL
+    desc = make_desc(x, B, theta, chunk=chunk, state_dtype=state_dtype, nsegments=nsegments, rate_law=law)
+    rate = A_log if A_raw is None else A_raw
+    ci, cf = _carry(init, dev, io, state_dtype), _carry(final, dev, io, state_dtype)
+    st = lib.m3_scan_fwd_noalloc(ctypes.byref(desc), _ptr(x, dev, io, "x"), _ptr(B, dev, io, "B"),
+                                 _ptr(C, dev, io, "C"), _ptr(dt, dev, torch.float32, "dt"),
+                                 _ptr(lam, dev, torch.float32, "lam"), _ptr(theta, dev, torch.float32, "theta"),
+                                 _ptr(rate, dev, torch.float32, "A_log/A_raw"),
+                                 _ptr(B_bias, dev, torch.float32, "B_bias"), _ptr(C_bias, dev, torch.float32, "C_bias"),
+                                 ctypes.byref(ci) if ci is not None else None, _ptr(y, dev, io, "y"),
+                                 ctypes.byref(cf) if cf is not None else None, _stream(dev))
+    _check(st, "m3_scan_fwd_noalloc")
+    return y, final
 
 
 class CarryGrad(ctypes.Structure):

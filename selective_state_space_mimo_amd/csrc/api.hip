@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/m3scan.h"
 #include "m3_internal.h"
@@ -14,6 +15,37 @@ using namespace m3;
 namespace {
 
 constexpr uintptr_t kAlign = 16;
+
+// Device scratch of m3_scan_fwd_noalloc: the segmented schedule's workspace for
+// callers that cannot allocate.  Each GPU the library runs on holds one copy until
+// the process ends.  Host code never passes `scratch` itself to a kernel (on the
+// host it names a stand-in, not a device address): scratch_address() looks up each
+// device's address once with hipGetSymbolAddress and keeps it.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+// The current device's address of `scratch` (looked up on the first call on that device).
+m3_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return M3_ERR_HIP;
+    if (dev >= kMaxDevices) return M3_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return M3_ERR_HIP;
+        g_scratch_addr[dev] = ptr;
+    }
+    *out = g_scratch_addr[dev];
+    return M3_OK;
+}
 
 bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) % kAlign) != 0; }
 
@@ -218,6 +250,7 @@ const char* m3_status_string(m3_status s) {
         case M3_ERR_UNSUPPORTED: return "unsupported shape or dtype";
         case M3_ERR_ALIGNMENT: return "tensor base not 16-byte aligned";
         case M3_ERR_HIP: return "HIP runtime error";
+        case M3_ERR_TOO_LARGE: return "schedule needs more than the no-allocation scratch (64 MiB per GPU)";
     }
     return "unknown status";
 }
@@ -236,10 +269,16 @@ m3_status m3_scan_workspace_size(const m3_desc* d, size_t* bytes) {
     return M3_OK;
 }
 
-m3_status m3_scan_fwd(const m3_desc* d, const void* x, const void* B, const void* C, const float* dt,
-                      const float* lam, const float* theta, const float* A_log, const float* B_bias,
-                      const float* C_bias, const m3_carry* init, void* y, const m3_carry* final_,
-                      void* workspace, size_t workspace_bytes, m3_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// m3_scan_fwd, or with use_scratch m3_scan_fwd_noalloc (the workspace argument is
+// ignored and the segmented schedule runs in the device scratch).
+m3_status scan_fwd_impl(const m3_desc* d, const void* x, const void* B, const void* C, const float* dt,
+                        const float* lam, const float* theta, const float* A_log, const float* B_bias,
+                        const float* C_bias, const m3_carry* init, void* y, const m3_carry* final_,
+                        void* workspace, size_t workspace_bytes, m3_stream_t stream, bool use_scratch) {
     m3_status st = check_desc(d, true);
     if (st != M3_OK) return st;
     const int L = d->seqlen;
@@ -291,7 +330,13 @@ m3_status m3_scan_fwd(const m3_desc* d, const void* x, const void* B, const void
     hipError_t e;
     if (a.io_bf16 && scan_mfma_supported(a)) {
         const size_t need = scan_mfma_workspace_bytes(a);
-        if (need > 0) {
+        if (use_scratch) {
+            // every summary, incoming state and phase is written before it is read, so the
+            // scratch needs no clearing; what a previous call left there does not matter
+            if (need > kScratchBytes) return M3_ERR_TOO_LARGE;
+            workspace = nullptr;
+            if (need > 0 && (st = scratch_address(&workspace)) != M3_OK) return st;
+        } else if (need > 0) {
             if (!workspace || workspace_bytes < need) return M3_ERR_INVALID_ARG;
             const Range rw = rng(workspace, need);
             for (const Range& r : ins)
@@ -308,6 +353,28 @@ m3_status m3_scan_fwd(const m3_desc* d, const void* x, const void* B, const void
     }
     return e == hipSuccess ? M3_OK : M3_ERR_HIP;
 }
+
+}  // namespace
+
+extern "C" {
+
+m3_status m3_scan_fwd(const m3_desc* d, const void* x, const void* B, const void* C, const float* dt,
+                      const float* lam, const float* theta, const float* A_log, const float* B_bias,
+                      const float* C_bias, const m3_carry* init, void* y, const m3_carry* final_,
+                      void* workspace, size_t workspace_bytes, m3_stream_t stream) {
+    return scan_fwd_impl(d, x, B, C, dt, lam, theta, A_log, B_bias, C_bias, init, y, final_, workspace,
+                         workspace_bytes, stream, false);
+}
+
+m3_status m3_scan_fwd_noalloc(const m3_desc* d, const void* x, const void* B, const void* C, const float* dt,
+                              const float* lam, const float* theta, const float* A_log, const float* B_bias,
+                              const float* C_bias, const m3_carry* init, void* y, const m3_carry* final_,
+                              m3_stream_t stream) {
+    return scan_fwd_impl(d, x, B, C, dt, lam, theta, A_log, B_bias, C_bias, init, y, final_, nullptr, 0, stream,
+                         true);
+}
+
+size_t m3_scan_noalloc_max_workspace(void) { return kScratchBytes; }
 
 m3_status m3_decode_step(const m3_desc* d, const void* x, const void* B, const void* C, const float* dt,
                          const float* lam, const float* theta, const float* A_log, const float* B_bias,

@@ -68,7 +68,7 @@ def _scan(m3, desc, **ptrs):
 
 
 def test_status_strings(m3):
-    for s in range(5):
+    for s in range(6):
         assert m3.lib.m3_status_string(s)
     assert m3.lib.m3_version() > 0
 
@@ -205,3 +205,19 @@ def test_final_carry_must_not_overlap_inputs(m3):
                                    FAKE + 0x300000, FAKE + 0x400000, FAKE + 0x500000, FAKE + 0x600000,
                                    FAKE + 0x680000, None, FAKE + 0x700000, ctypes.byref(f), FAKE + 0x1000000,
                                    n.value, None) == 1, hex(bad)
+
+
+def test_noalloc_rejects_a_schedule_beyond_its_scratch(m3):
+    """m3_scan_fwd_noalloc refuses, before any HIP call, a schedule whose workspace
+    exceeds its per-GPU scratch (here the long-context shape split into 64
+    segments per stream), and names the limit."""
+    G4 = 1 << 32
+    d = _desc(m3, batch=1, seqlen=65536, nheads=64, ngroups=1, headdim=64, dstate=128, rank=4, npairs=32,
+              chunk=16, io_dtype=m3.M3_BF16, nsegments=64)
+    n = ctypes.c_size_t(0)
+    assert m3.lib.m3_scan_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    assert n.value > m3.lib.m3_scan_noalloc_max_workspace() == 64 << 20
+    st = m3.lib.m3_scan_fwd_noalloc(ctypes.byref(d), FAKE, FAKE + G4, FAKE + 2 * G4, FAKE + 3 * G4, FAKE + 4 * G4,
+                                    FAKE + 5 * G4, FAKE + 6 * G4, None, None, None, FAKE + 7 * G4, None, None)
+    assert st == m3.M3_ERR_TOO_LARGE == 5
+    assert b"64 MiB" in m3.lib.m3_status_string(st)
