@@ -112,6 +112,8 @@ int scan_mfma_groups_per_cu(int R, int Q);
 bool scan_mfma_supported(const ScanArgs& a);
 hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t s);
 size_t scan_mfma_workspace_bytes(const ScanArgs& a);
+// Pass 2 of the segmented schedule (the carry recurrence across segments).
+hipError_t launch_carry_pass(const ScanArgs& a, hipStream_t s);
 
 bool decode_fast_supported(const DecodeArgs& a);
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s);

@@ -49,86 +49,13 @@
 // segment, the folded state from a zero carry in a local angle frame; pass 2
 // runs the affine carry recurrence across segments (turning each summary into
 // the global frame); pass 3 evaluates every segment from its true carry.
-#include "m3_internal.h"
+#include "scan_common.h"
 
 #include <type_traits>
 
 namespace m3 {
 
 namespace {
-
-constexpr int kP = 64, kN = 128, kKB = 32;
-constexpr int kNP = 4;                   // producer waves
-constexpr int kMaxRows = 256;            // rows (tokens x ranks) per chunk
-constexpr float kLog2e = 1.4426950408889634f;
-
-enum Mode { kFull = 0, kSummary = 1 };
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ float lo_f(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float hi_f(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    bf16x2 v;
-    v[0] = (bf16)lo;
-    v[1] = (bf16)hi;
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-// ---- LDS layout ------------------------------------------------------------------
-// Per key-block buffer: Bn [32 j][128 n] (turned B) and Bv [32 j][128 n] (v times turned B),
-// row-major over the block's 32 key rows j; XT [64 p][32 j] bf16, keys in the scores'
-// permuted order (group q: keys 4 q .. 4 q + 3, then 16 + 4 q ..).
-constexpr int kBnBytes = kKB * kN * 2;           // 8 KiB
-constexpr int kBvBytes = kKB * kN * 2;           // 8 KiB
-constexpr int kXtBytes = kP * kKB * 2;           // 4 KiB
-constexpr int kBufBytes = kBnBytes + kBvBytes + kXtBytes;
-constexpr int kHsBytes = kP * kN * 2;            // bf16 snapshot of the folded state
-
-// 16-byte-group swizzles.  Bn, Bv and Hs rows hold 16 groups (256 B); XT rows 4 (64 B).
-__device__ __forceinline__ int bn_off(int j, int grp) { return j * 256 + ((grp ^ (j & 15)) << 4); }
-__device__ __forceinline__ int hs_off(int p, int grp) { return p * 256 + ((grp ^ (p & 15)) << 4); }
-__device__ __forceinline__ int q4_off(int row, int grp) { return row * 64 + ((grp ^ ((row >> 1) & 3)) << 4); }
-
-// The state update's A operand, (v Bt)^T (k over a block's keys), comes from the row-major
-// Bv tile by transposed reads (ds_read_b64_tr_b16).  Within each 16-lane group the instruction treats
-// the lanes' 8-byte chunks as a 16 x 4 matrix M (lane s: M[s][0..3]) and returns to lane i
-// the column M[4 j + i / 4][i % 4], j = 0..3.  So when lane s points at key row kb + s / 4,
-// columns c0 + 4 (s % 4) .. + 3, lane i receives column c0 + i at keys kb .. kb + 3.
-// The operand's k order is the scores' permuted one (lane group g: keys 4 g .. 4 g + 3 of
-// key tile a, then of key tile b), so each operand is two reads, kb = 4 g and 16 + 4 g.
-typedef short tr_v4i16 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint2 ds_tr(const char* p) {
-    const tr_v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) tr_v4i16*)(p));
-    return __builtin_bit_cast(uint2, v);
-}
-// operand over (16 columns from c0) x (the block's 32 keys) of a 256-byte-row tile (Bv)
-__device__ __forceinline__ bf16x8 key_operand_256(const char* tile, int c0, int lane) {
-    const int g = lane >> 4, s = lane & 15;
-    const int col = c0 + 4 * (s & 3), kr = 4 * g + (s >> 2);
-    const int off = (col & 7) * 2;
-    const uint2 lo = ds_tr(tile + bn_off(kr, col >> 3) + off);
-    const uint2 hi = ds_tr(tile + bn_off(16 + kr, col >> 3) + off);
-    return __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
-}
-
-// Rotation of an (even, odd) pair by a tabled angle, on packed-bf16 dot products with fp32
-// sums.  An angle's table entry holds two bf16 pairs, (cos, -sin) and (sin, cos); a bias is
-// a bf16 pair; rot(v + b) = rot(v) + rot(b), each half of the result two dot products.
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
-__device__ __forceinline__ float2 rot_pair(uint32_t v, uint32_t bias, uint2 cs) {
-    return float2{dot2(v, cs.x, dot2(bias, cs.x, 0.f)), dot2(v, cs.y, dot2(bias, cs.y, 0.f))};
-}
-__device__ __forceinline__ uint2 cs_entry(float c, float s) { return uint2{pack2(c, -s), pack2(s, c)}; }
 
 template <int R, int Q>
 struct Layout {
@@ -164,33 +91,6 @@ struct Layout {
     static constexpr int ysg = xsc + (kYStage ? 0 : 4 * 4096);
     static constexpr int total = ysg + (kYStage ? R * Q * 144 : 0);
 };
-
-// DPP read of v from another lane; lanes whose source is outside the pattern (or
-// whose row is masked off) read 0.
-template <int CTRL, int ROWS = 0xf>
-__device__ __forceinline__ float dpp_read(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, false));
-}
-
-// Inclusive scan of v over groups of W lanes of a wave (W a power of two, 8 <= W <= 64):
-// shifts within 16-lane rows, then the row broadcasts of lane 15 and lane 31.
-template <int W>
-__device__ __forceinline__ float group_scan(float v, int lane_in_group) {
-    static_assert(W == 8 || W == 16 || W == 32 || W == 64, "group width");
-    if constexpr (W == 8) {
-        float u = dpp_read<0x111>(v); v = lane_in_group >= 1 ? v + u : v;
-        u = dpp_read<0x112>(v); v = lane_in_group >= 2 ? v + u : v;
-        u = dpp_read<0x114>(v); v = lane_in_group >= 4 ? v + u : v;
-    } else {
-        v += dpp_read<0x111>(v);        // row_shr:1, 2, 4, 8 (zero-filled at the row start)
-        v += dpp_read<0x112>(v);
-        v += dpp_read<0x114>(v);
-        v += dpp_read<0x118>(v);
-        if constexpr (W >= 32) v += dpp_read<0x142, 0xa>(v);   // row_bcast:15 into rows 1, 3
-        if constexpr (W == 64) v += dpp_read<0x143, 0xc>(v);   // row_bcast:31 into rows 2, 3
-    }
-    return v;
-}
 
 // ---- warp-specialised variant (chunks of at most 256 rows) ----------------------------------
 // Waves 0-3 are consumers: each keeps a quarter of the chunk's query tiles (C tiles in
@@ -546,8 +446,8 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
         // tokens past the segment end read zero (their outputs are never stored)
         auto load_c = [&](int cst, auto kbc, auto kec) {
             constexpr int KB = decltype(kbc)::value, KE = decltype(kec)::value;
-            const int nv = min(Q, T1 - cst);
-            const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cg + (size_t)cst * bstride, (uint32_t)nv * bsb);
+            const int nv = max(0, min(Q, T1 - cst));
+            const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cg + (size_t)(nv > 0 ? cst : 0) * bstride, (uint32_t)nv * bsb);
             unsigned ln = lane;                               // opaque: offsets formed here
             asm volatile("" : "+v"(ln));
             ln &= 63u;
@@ -564,17 +464,17 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
         };
 
         // Tiles 0 .. TPC - 2 of a chunk are retired before its last phase of key blocks; their
-        // C rows for the next chunk are loaded then, and only tile TPC - 1 at the chunk start.
-        bool pre = false;
+        // C rows for the next chunk are loaded then (for the first chunk, here), and only tile
+        // TPC - 1 at the chunk start.  Every chunk issues the same global loads and stores in
+        // the same order (rows past the segment end fall outside the record counts), so a wait
+        // for a load counts exactly the later ones and never the output stores just issued.
+        if (kFullMode && TPC > 1) load_c(T0, std::integral_constant<int, 0>{}, std::integral_constant<int, TPC - 1>{});
         int cidx = 0;
         for (int c0 = T0; c0 < T1; c0 += Q, ++cidx) {
             // (A) theta into LDS (loaded a chunk ago), then the chunk's C rows, the next
             //     chunk's theta and per-token inputs
             stage_theta(rgTh);
-            if (kFullMode) {
-                if (pre) load_c(c0, std::integral_constant<int, TPC - 1>{}, std::integral_constant<int, TPC>{});
-                else load_c(c0, std::integral_constant<int, 0>{}, std::integral_constant<int, TPC>{});
-            }
+            if (kFullMode) load_c(c0, std::integral_constant<int, TPC - 1>{}, std::integral_constant<int, TPC>{});
             load_theta(c0 + Q, rgTh);
             __syncthreads();
             angles();
@@ -598,29 +498,28 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
                     const int t = qi / R;
                     tq[k] = t;
                     l2q[k] = sL2[t];
+                    // Pairs at or past np have identity table entries, so every slice takes the
+                    // same path (a per-slice branch on np serialised the table reads); all of the
+                    // tile's table and bias reads are issued before its math.
+                    uint4 ce[4][2], bi[4];
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks) {
                         const int i0 = 16 * ks + 4 * g4;             // first pair
-                        const uint4 raw = __builtin_bit_cast(uint4, cq[k][ks]);
+                        const uint2* e = sCS + t * 64 + (i0 ^ (t & 60));   // pairs i0 .. i0 + 3
+                        ce[ks][0] = *reinterpret_cast<const uint4*>(e);
+                        ce[ks][1] = *reinterpret_cast<const uint4*>(e + 2);
                         // a lane's rows have rank l16 % R in every tile (16 % R == 0)
-                        const uint4 bi = *reinterpret_cast<const uint4*>(sCb + (l16 % R) * 64 + i0);
-                        uint4 o;
-                        if (16 * ks >= np) {                          // no pair of this slice turns
-                            o = uint4{pack2(lo_f(raw.x) + lo_f(bi.x), hi_f(raw.x) + hi_f(bi.x)),
-                                      pack2(lo_f(raw.y) + lo_f(bi.y), hi_f(raw.y) + hi_f(bi.y)),
-                                      pack2(lo_f(raw.z) + lo_f(bi.z), hi_f(raw.z) + hi_f(bi.z)),
-                                      pack2(lo_f(raw.w) + lo_f(bi.w), hi_f(raw.w) + hi_f(bi.w))};
-                        } else {
-                            const uint2* ce = sCS + t * 64 + (i0 ^ (t & 60));   // pairs i0 .. i0 + 3
-                            const uint4 c01 = *reinterpret_cast<const uint4*>(ce);
-                            const uint4 c23 = *reinterpret_cast<const uint4*>(ce + 2);
-                            const float2 p0 = rot_pair(raw.x, bi.x, uint2{c01.x, c01.y});
-                            const float2 p1 = rot_pair(raw.y, bi.y, uint2{c01.z, c01.w});
-                            const float2 p2 = rot_pair(raw.z, bi.z, uint2{c23.x, c23.y});
-                            const float2 p3 = rot_pair(raw.w, bi.w, uint2{c23.z, c23.w});
-                            o = uint4{pack2(p0.x, p0.y), pack2(p1.x, p1.y), pack2(p2.x, p2.y), pack2(p3.x, p3.y)};
-                        }
-                        cq[k][ks] = __builtin_bit_cast(bf16x8, o);
+                        bi[ks] = *reinterpret_cast<const uint4*>(sCb + (l16 % R) * 64 + i0);
+                    }
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const uint4 raw = __builtin_bit_cast(uint4, cq[k][ks]);
+                        const float2 p0 = rot_pair(raw.x, bi[ks].x, uint2{ce[ks][0].x, ce[ks][0].y});
+                        const float2 p1 = rot_pair(raw.y, bi[ks].y, uint2{ce[ks][0].z, ce[ks][0].w});
+                        const float2 p2 = rot_pair(raw.z, bi[ks].z, uint2{ce[ks][1].x, ce[ks][1].y});
+                        const float2 p3 = rot_pair(raw.w, bi[ks].w, uint2{ce[ks][1].z, ce[ks][1].w});
+                        cq[k][ks] = __builtin_bit_cast(
+                            bf16x8, uint4{pack2(p0.x, p0.y), pack2(p1.x, p1.y), pack2(p2.x, p2.y), pack2(p3.x, p3.y)});
                     }
                 }
 #pragma unroll
@@ -656,7 +555,7 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
                 const int ka = 2 * J;
                 const char* buf = smem + (J & 1) * kBufBytes;
                 const char* xtb = buf + kBnBytes + kBvBytes;
-                float kl2[2][KT], kg1[2][KT];
+                float kl2[2][KT], kg1[2][KT], kgm[2][KT];
 #pragma unroll
                 for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
@@ -664,6 +563,7 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
                         const int ts = (16 * (ka + ab) + 4 * g4) / R + j;
                         kl2[ab][j] = sL2[ts];
                         kg1[ab][j] = sG1[ts];
+                        if (kDiag) kgm[ab][j] = sGam[ts];
                     }
                 // The decay factors of W: they need only the tabled log-decays, so with one
                 // key token per lane and key tile (R = 4) their exps go before the score
@@ -718,9 +618,10 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
                         for (int j = 0; j < KT; ++j) {
                             const float e = ex[k][ab][j];
                             wgt[ab][j] = e * kg1[ab][j];
-                            if (diag) {
+                            if (kDiag) {             // selects (the key token's g was read with the tables)
                                 const int ts = (16 * (ka + ab) + 4 * g4) / R + j;
-                                wgt[ab][j] = ts < tq[k] ? wgt[ab][j] : (ts == tq[k] ? e * sGam[ts] : 0.f);
+                                const float wd = ts < tq[k] ? wgt[ab][j] : (ts == tq[k] ? e * kgm[ab][j] : 0.f);
+                                wgt[ab][j] = diag ? wd : wgt[ab][j];
                             }
                         }
                     }
@@ -742,11 +643,13 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
             };
             // per key block (Q <= 64): rows RPB J .. RPB J + RPB - 1 of this wave's staged outputs
             // of the previous chunk (tile RPB J / 16)
-            const bool have_prev = kFullMode && c0 > T0;
+            // (none before the first chunk: a record count of 0 drops the stores)
+            const int nprev = c0 > T0 ? Q : 0;
             auto block_end = [&](int J) {
                 if constexpr (LY::kYStage)
-                    if (have_prev)
-                        store_rows(c0 - Q, Q, ctile<kNC>(c, RPB * J / 16), RPB * J % 16, std::integral_constant<unsigned, RPB>{});
+                    if (kFullMode)
+                        store_rows(nprev ? c0 - Q : c0, nprev, ctile<kNC>(c, RPB * J / 16), RPB * J % 16,
+                                   std::integral_constant<unsigned, RPB>{});
                 __syncthreads();
             };
             int Jb = 0;
@@ -754,7 +657,7 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
                 constexpr int K0 = decltype(mc)::value;
                 const int Je = K0 < TPC ? min(NKB, ctile<kNC>(c, K0 < TPC ? K0 : 0) / 2 + 1) : NKB;
                 if constexpr (TPC > 1 && K0 == TPC - 1)
-                    if (kFullMode && c0 + Q < T1)
+                    if (kFullMode)               // (none after the last chunk: zero records)
                         load_c(c0 + Q, std::integral_constant<int, 0>{}, std::integral_constant<int, TPC - 1>{});
                 if constexpr (K0 < TPC && kEarlyExp) {
                     // blocks before the last of tile K0, then its diagonal block
@@ -784,7 +687,6 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
             if constexpr (TPC >= 2) phase(std::integral_constant<int, 2>{});
             if constexpr (TPC >= 3) phase(std::integral_constant<int, 3>{});
             if constexpr (TPC >= 4) phase(std::integral_constant<int, 4>{});
-            pre = TPC > 1 && c0 + Q < T1;
         }
         // the last chunk's outputs
         if (kFullMode && T1 > T0) {
@@ -1024,7 +926,9 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
             __syncthreads();
             angles();
             __syncthreads();
-            // (C) the state decays over the whole chunk before its writes land; block 0
+            // (C) the next chunk's inputs (the angles no longer read this chunk's); the state
+            //     decays over the whole chunk before its writes land; block 0
+            stage_scalars(c0 + Q);
             {
                 const float f = exp2f(sMisc[0]);
 #pragma unroll
@@ -1045,7 +949,6 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
 #pragma unroll
                 for (int d = 0; d < DP; ++d) {
                     const int J = J0 + d;
-                    if (J == 0) stage_scalars(c0 + Q);        // the next chunk's inputs
                     fetch(rgB[d], rgX[d]);
                     // every LDS read of the iteration first (block J's operands, block J + 1's
                     // angles and v), then the state MFMAs, then block J + 1's tiles
@@ -1213,8 +1116,7 @@ hipError_t launch_rql(const ScanArgs& a, hipStream_t st) {
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((scan_ws_kernel<R, Q, kSummary, LAYER>), dim3(nblk), dim3(n_threads<R, Q>()), lds, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(carry_pass_kernel, dim3((kP * kN / 2 + 255) / 256, a.b * a.H), dim3(256), 0, st, a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_carry_pass(a, st)) != hipSuccess) return e;
     }
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scan_ws_kernel<R, Q, kFull, LAYER>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1234,6 +1136,11 @@ hipError_t launch_rq(const ScanArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_carry_pass(const ScanArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL(carry_pass_kernel, dim3((kP * kN / 2 + 255) / 256, a.b * a.H), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
 
 int scan_mfma_chunk(int io_bf16, int P, int N, int R, int Q) {
     if (!io_bf16 || P != kP || N != kN || !(R == 1 || R == 2 || R == 4)) return Q;
