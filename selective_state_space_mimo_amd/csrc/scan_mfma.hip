@@ -499,20 +499,23 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
                     tq[k] = t;
                     l2q[k] = sL2[t];
                     // Pairs at or past np have identity table entries, so every slice takes the
-                    // same path (a per-slice branch on np serialised the table reads); all of the
-                    // tile's table and bias reads are issued before its math.
+                    // same path (a per-slice branch on np serialised the table reads); where the
+                    // registers allow, all of the tile's table and bias reads are issued first.
+                    constexpr int RG = waves_per_simd<R, Q>() < 4 ? 4 : 1;      // slices per read group
                     uint4 ce[4][2], bi[4];
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks) {
-                        const int i0 = 16 * ks + 4 * g4;             // first pair
-                        const uint2* e = sCS + t * 64 + (i0 ^ (t & 60));   // pairs i0 .. i0 + 3
-                        ce[ks][0] = *reinterpret_cast<const uint4*>(e);
-                        ce[ks][1] = *reinterpret_cast<const uint4*>(e + 2);
-                        // a lane's rows have rank l16 % R in every tile (16 % R == 0)
-                        bi[ks] = *reinterpret_cast<const uint4*>(sCb + (l16 % R) * 64 + i0);
-                    }
+                        if (ks % RG == 0) {
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
+                            for (int u = ks; u < ks + RG; ++u) {
+                                const int i0 = 16 * u + 4 * g4;             // first pair
+                                const uint2* e = sCS + t * 64 + (i0 ^ (t & 60));   // pairs i0 .. i0 + 3
+                                ce[u][0] = *reinterpret_cast<const uint4*>(e);
+                                ce[u][1] = *reinterpret_cast<const uint4*>(e + 2);
+                                // a lane's rows have rank l16 % R in every tile (16 % R == 0)
+                                bi[u] = *reinterpret_cast<const uint4*>(sCb + (l16 % R) * 64 + i0);
+                            }
+                        }
                         const uint4 raw = __builtin_bit_cast(uint4, cq[k][ks]);
                         const float2 p0 = rot_pair(raw.x, bi[ks].x, uint2{ce[ks][0].x, ce[ks][0].y});
                         const float2 p1 = rot_pair(raw.y, bi[ks].y, uint2{ce[ks][0].z, ce[ks][0].w});
