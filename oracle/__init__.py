@@ -12,7 +12,10 @@ meet only through the seeded inputs of ``m3inputs``.
 - ``block``    the layer steps around the scan (activations, BCNorm, x lift,
                readout recombination, D skip, gate), whole sequence and one
                decode step, on top of ``ref``.
+- ``pcs``      numpy fp64: the per-coordinate selective scan (Mamba 1 preset):
+               recurrence, sum over token pairs, associative prefix form.
+- ``pcs_cpu``  plain C fp64 recurrence of the same (OpenMP over channels).
 
-Parity status of every function is pinned by ``tests/test_oracle.py``; no
+Parity status of every function is pinned by ``tests/test_oracle*.py``; no
 function here is "parity unpinned".
 """
