@@ -297,6 +297,56 @@ m3_status m3_scan_bwd(const m3_desc* d,
                       const m3_scan_grads* grads, void* workspace, size_t workspace_bytes,
                       m3_stream_t stream);
 
+/* ---- Per-coordinate selective scan (the Mamba 1 preset) -----------------------
+ *
+ * "Diagonal Equivalence in State Space Models: Characterization, Retrieval Rank,
+ * and Selective Extensions" (paperpeel.com), section 5.1 "Per-coordinate scan"
+ * and the Mamba 1 row of its table of copied-weight presets (real, static
+ * per-coordinate decay, exponential-Euler write); the exponential-Euler
+ * discretisation is that of "Mamba-3: Improved Sequence Modeling using State
+ * Space Principles", section "How Mamba gets its recurrence from a differential
+ * equation".  For every batch b, channel d (group g = d G / D of the shared B,
+ * C) and state coordinate n, with the static rate a[d, n] = -exp(A_log[d, n]):
+ *     h[n] <- exp(dt[b,t,d] a[d,n]) h[n] + dt[b,t,d] B[b,t,g,n] x[b,t,d]
+ *     y[b,t,d] = sum_n C[b,t,g,n] h[n]
+ * Each channel is a single-input, single-output core with its own N decay
+ * rates (unlike m3_scan_fwd, whose decay is one scalar per head).
+ */
+typedef struct {
+    int batch;        /* b >= 1 */
+    int seqlen;       /* L >= 0 tokens */
+    int channels;     /* D >= 1; a multiple of 8 (bf16) or 4 (f32) */
+    int ngroups;      /* G >= 1, D % G == 0; G == 1 or (D / G) % 64 == 0 */
+    int dstate;       /* N in {8, 16, 32, 64} */
+    m3_dtype io_dtype;     /* x, B, C, y */
+    int nsegments;    /* schedule: 0 = library's choice; k in 1..64 asks for k sequence
+                         segments per (batch, channel), evaluated in parallel from
+                         zero-state summaries and joined by a prefix scan of their
+                         affine maps (clamped to the number of 64-token blocks).  The
+                         result does not depend on it beyond rounding. */
+} m3_pcs_desc;
+
+/* Bytes of device workspace m3_pcs_fwd needs for *d (0 if none).
+ * Returns M3_ERR_INVALID_ARG for a NULL argument or an invalid descriptor, and
+ * M3_ERR_UNSUPPORTED for a valid one outside the supported range. */
+m3_status m3_pcs_workspace_size(const m3_pcs_desc* d, size_t* bytes);
+
+/* The per-coordinate scan over a whole sequence.
+ *   x      [b, L, D] io            dt [b, L, D] f32 (> 0, after softplus)
+ *   A_log  [D, N] f32              B, C [b, L, G, N] io
+ *   h0     [b, D, N] f32 initial state, or NULL for zero
+ *   y      [b, L, D] io (output; must not overlap any input)
+ *   h1     [b, D, N] f32 final state, or NULL; must not overlap an input or y
+ *          (so not h0 either: updating a state in place is not supported)
+ *   workspace: device buffer of at least m3_pcs_workspace_size(d) bytes (may be
+ *          NULL when that size is 0); its contents on entry do not matter; it
+ *          must not overlap any argument.
+ * With L == 0 nothing is launched except copying h0 to h1 (zeros if h0 is NULL).
+ * Errors and conventions as for m3_scan_fwd. */
+m3_status m3_pcs_fwd(const m3_pcs_desc* d, const void* x, const float* dt, const float* A_log,
+                     const void* B, const void* C, const float* h0, void* y, float* h1,
+                     void* workspace, size_t workspace_bytes, m3_stream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* m3_status_string(m3_status s);
 

@@ -13,6 +13,8 @@ not import.
     grads = scan_bwd(x, B, C, dt, lam, theta, A_log, B_bias, C_bias, init, dy,
                      dfinal=None)
 
+    y, h1 = pcs_fwd(x, dt, A_log, B, C, h0=None)     # per-coordinate scan
+
 With ``A_raw=`` (a per-token rate input [b,L,H], or [b,H] for a decode step)
 the decay rate of each token is the heavy-tail law (M3_RATE_HEAVY_TAIL) and
 ``A_log`` is not used.
@@ -23,6 +25,7 @@ import os
 import torch
 
 __all__ = ["scan_fwd", "scan_fwd_noalloc", "scan_bwd", "decode_step", "scan_workspace_size", "new_carry", "M3Error",
+           "pcs_fwd", "pcs_workspace_size", "pcs_desc", "PcsDesc",
            "LIB_PATH", "lib", "Desc", "Carry", "M3_F32", "M3_BF16", "M3_RATE_STATIC", "M3_RATE_HEAVY_TAIL"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libm3scan.so")
@@ -207,6 +210,61 @@ def scan_fwd_noalloc(x, B, C, dt, lam, theta, A_log, B_bias=None, C_bias=None, i
                                  ctypes.byref(cf) if cf is not None else None, _stream(dev))
     _check(st, "m3_scan_fwd_noalloc")
     return y, final
+
+
+class PcsDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int), ("seqlen", ctypes.c_int), ("channels", ctypes.c_int),
+                ("ngroups", ctypes.c_int), ("dstate", ctypes.c_int), ("io_dtype", ctypes.c_int),
+                ("nsegments", ctypes.c_int)]
+
+
+lib.m3_pcs_workspace_size.argtypes = [ctypes.POINTER(PcsDesc), ctypes.POINTER(_sz)]
+lib.m3_pcs_workspace_size.restype = ctypes.c_int
+lib.m3_pcs_fwd.argtypes = [ctypes.POINTER(PcsDesc)] + [_vp] * 8 + [_vp, _sz, _vp]
+lib.m3_pcs_fwd.restype = ctypes.c_int
+
+
+def pcs_desc(x, B, *, nsegments=0):
+    b, L, D = x.shape
+    G, N = B.shape[2], B.shape[3]
+    return PcsDesc(b, L, D, G, N, _dt(x), nsegments)
+
+
+def pcs_workspace_size(desc):
+    n = _sz(0)
+    _check(lib.m3_pcs_workspace_size(ctypes.byref(desc), ctypes.byref(n)), "m3_pcs_workspace_size")
+    return n.value
+
+
+def pcs_fwd(x, dt, A_log, B, C, h0=None, *, y=None, h1=True, nsegments=0, workspace=None):
+    """Per-coordinate selective scan, the Mamba 1 preset (``m3_pcs_fwd``).
+
+    x [b,L,D], B/C [b,L,G,N] (bf16 or f32, same dtype); dt [b,L,D] and A_log
+    [D,N] f32; h0 [b,D,N] f32 or None (zero).  h1: True to allocate and return
+    the final state, a tensor to write into, or False/None to skip it.
+    Returns (y, h1_or_None)."""
+    dev = x.device
+    io = x.dtype
+    desc = pcs_desc(x, B, nsegments=nsegments)
+    b, L, D = x.shape
+    N = B.shape[3]
+    if y is None:
+        y = torch.empty_like(x)
+    fin = None
+    if h1 is True:
+        fin = torch.empty((b, D, N), dtype=torch.float32, device=dev)
+    elif isinstance(h1, torch.Tensor):
+        fin = h1
+    ws_bytes = pcs_workspace_size(desc)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    st = lib.m3_pcs_fwd(ctypes.byref(desc), _ptr(x, dev, io, "x"), _ptr(dt, dev, torch.float32, "dt"),
+                        _ptr(A_log, dev, torch.float32, "A_log"), _ptr(B, dev, io, "B"), _ptr(C, dev, io, "C"),
+                        _ptr(h0, dev, torch.float32, "h0"), _ptr(y, dev, io, "y"),
+                        _ptr(fin, dev, torch.float32, "h1"),
+                        _ptr(workspace, dev, None, "workspace") if ws_bytes else None, ws_bytes, _stream(dev))
+    _check(st, "m3_pcs_fwd")
+    return y, fin
 
 
 class CarryGrad(ctypes.Structure):

@@ -609,3 +609,103 @@ m3_status m3_scan_bwd(const m3_desc* d, const void* x, const void* B, const void
 }
 
 }  // extern "C"
+
+namespace {
+
+// Checks of an m3_pcs_desc: M3_ERR_INVALID_ARG for an invalid one, M3_ERR_UNSUPPORTED
+// outside the kernels' range (state widths, channel alignment, groups split by a
+// workgroup's channel tile, more than 64 segments).
+m3_status check_pcs_desc(const m3_pcs_desc* d) {
+    if (!d) return M3_ERR_INVALID_ARG;
+    if (d->batch < 1 || d->seqlen < 0 || d->channels < 1 || d->ngroups < 1 || d->channels % d->ngroups ||
+        d->dstate < 1 || d->nsegments < 0)
+        return M3_ERR_INVALID_ARG;
+    if (d->io_dtype != M3_F32 && d->io_dtype != M3_BF16) return M3_ERR_INVALID_ARG;
+    if (!pcs_supported_state(d->dstate)) return M3_ERR_UNSUPPORTED;
+    // x, dt and y rows move in 16-byte pieces
+    if (d->channels % (d->io_dtype == M3_BF16 ? 8 : 4)) return M3_ERR_UNSUPPORTED;
+    // a workgroup's channels read one group's B and C
+    if (d->ngroups > 1 && (d->channels / d->ngroups) % pcs_channels_per_group(d->dstate)) return M3_ERR_UNSUPPORTED;
+    if (d->nsegments > 64) return M3_ERR_UNSUPPORTED;
+    return M3_OK;
+}
+
+// Segments per (batch, channel): just enough that the workgroups fill the compute
+// units' slots, at most 64 (one wave's lanes in the carry pass) and at most the number
+// of token blocks; each segment is a whole number of blocks.
+void pcs_segments(const m3_pcs_desc* d, int* nseg, int* seglen) {
+    const int TB = pcs_block_tokens();
+    const int nblocks = (d->seqlen + TB - 1) / TB;
+    int k = d->nsegments;
+    if (k == 0) {
+        const int cw = pcs_channels_per_group(d->dstate);
+        const long long wgs = (long long)d->batch * ((d->channels + cw - 1) / cw);
+        const long long slots = 256LL * pcs_groups_per_cu(d->dstate);
+        k = wgs >= slots ? 1 : (int)std::min<long long>(64, (slots + wgs - 1) / wgs);
+    }
+    k = std::max(1, std::min(k, std::max(1, nblocks)));
+    const int bps = (nblocks + k - 1) / k;   // blocks per segment
+    *seglen = std::max(1, bps) * TB;
+    *nseg = std::max(1, (d->seqlen + *seglen - 1) / *seglen);
+}
+
+PcsArgs make_pcs_args(const m3_pcs_desc* d) {
+    PcsArgs a{};
+    a.b = d->batch; a.L = d->seqlen; a.D = d->channels; a.G = d->ngroups; a.N = d->dstate;
+    a.io_bf16 = d->io_dtype == M3_BF16;
+    pcs_segments(d, &a.nseg, &a.seglen);
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+m3_status m3_pcs_workspace_size(const m3_pcs_desc* d, size_t* bytes) {
+    if (!bytes) return M3_ERR_INVALID_ARG;
+    m3_status st = check_pcs_desc(d);
+    if (st != M3_OK) return st;
+    *bytes = d->seqlen > 0 ? pcs_workspace_bytes(make_pcs_args(d)) : 0;
+    return M3_OK;
+}
+
+m3_status m3_pcs_fwd(const m3_pcs_desc* d, const void* x, const float* dt, const float* A_log, const void* B,
+                     const void* C, const float* h0, void* y, float* h1, void* workspace, size_t workspace_bytes,
+                     m3_stream_t stream) {
+    m3_status st = check_pcs_desc(d);
+    if (st != M3_OK) return st;
+    const size_t b = d->batch, L = d->seqlen, D = d->channels, G = d->ngroups, N = d->dstate,
+                 io = esize(d->io_dtype);
+    const size_t sx = b * L * D * io, sdt = b * L * D * 4, sa = D * N * 4, sbc = b * L * G * N * io, sh = b * D * N * 4;
+    if (misaligned(h0) || misaligned(h1)) return M3_ERR_ALIGNMENT;
+    const Range rh0 = rng(h0, h0 ? sh : 0), rh1 = rng(h1, h1 ? sh : 0);
+    if (overlap(rh0, rh1)) return M3_ERR_INVALID_ARG;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (L == 0) {
+        if (!h1) return M3_OK;
+        return copy_or_zero(h0, h1, sh, hs) == hipSuccess ? M3_OK : M3_ERR_HIP;
+    }
+    if (!x || !dt || !A_log || !B || !C || !y) return M3_ERR_INVALID_ARG;
+    const void* ptrs[] = {x, dt, A_log, B, C, y, workspace};
+    for (const void* p : ptrs)
+        if (misaligned(p)) return M3_ERR_ALIGNMENT;
+    const Range ry = rng(y, sx);
+    const Range ins[] = {rng(x, sx), rng(dt, sdt), rng(A_log, sa), rng(B, sbc), rng(C, sbc), rh0};
+    for (const Range& r : ins)
+        if (overlap(ry, r) || overlap(rh1, r)) return M3_ERR_INVALID_ARG;
+    if (overlap(ry, rh1)) return M3_ERR_INVALID_ARG;
+    PcsArgs a = make_pcs_args(d);
+    const size_t need = pcs_workspace_bytes(a);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return M3_ERR_INVALID_ARG;
+        const Range rw = rng(workspace, need);
+        for (const Range& r : ins)
+            if (overlap(rw, r)) return M3_ERR_INVALID_ARG;
+        if (overlap(rw, ry) || overlap(rw, rh1)) return M3_ERR_INVALID_ARG;
+    }
+    a.x = x; a.dt = dt; a.A_log = A_log; a.B = B; a.C = C; a.h0 = h0; a.y = y; a.h1 = h1;
+    a.ws = static_cast<float*>(workspace);
+    return launch_pcs(a, hs) == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
+}  // extern "C"

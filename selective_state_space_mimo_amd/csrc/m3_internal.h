@@ -115,6 +115,25 @@ size_t scan_mfma_workspace_bytes(const ScanArgs& a);
 // Pass 2 of the segmented schedule (the carry recurrence across segments).
 hipError_t launch_carry_pass(const ScanArgs& a, hipStream_t s);
 
+// Per-coordinate selective scan (pcs.hip): x, dt [b, L, D], A_log [D, N], B, C
+// [b, L, G, N], state [b, D, N] fp32; x, B, C and y in the io dtype, dt fp32.
+struct PcsArgs {
+    int b, L, D, G, N;
+    int io_bf16;
+    const void* x; const float* dt; const float* A_log; const void* B; const void* C;
+    const float* h0;        // initial state (null = zero)
+    void* y;
+    float* h1;              // final state (null = not written)
+    int nseg, seglen;       // segmented schedule: nseg segments of seglen tokens
+    float* ws;              // workspace (nseg > 1 only)
+};
+bool pcs_supported_state(int N);
+int pcs_channels_per_group(int N);   // channels per workgroup
+int pcs_groups_per_cu(int N);        // workgroups one compute unit holds at once
+int pcs_block_tokens();              // tokens per block (segments are whole blocks)
+size_t pcs_workspace_bytes(const PcsArgs& a);
+hipError_t launch_pcs(const PcsArgs& a, hipStream_t s);
+
 bool decode_fast_supported(const DecodeArgs& a);
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t s);

@@ -221,3 +221,67 @@ def test_noalloc_rejects_a_schedule_beyond_its_scratch(m3):
                                     FAKE + 5 * G4, FAKE + 6 * G4, None, None, None, FAKE + 7 * G4, None, None)
     assert st == m3.M3_ERR_TOO_LARGE == 5
     assert b"64 MiB" in m3.lib.m3_status_string(st)
+
+
+def _pcs_desc(m3, **kw):
+    d = dict(batch=2, seqlen=300, channels=128, ngroups=1, dstate=16, io_dtype=m3.M3_BF16, nsegments=0)
+    d.update(kw)
+    return m3.PcsDesc(**d)
+
+
+def _pcs(m3, d, ws_bytes=None, **kw):
+    a = dict(x=FAKE, dt=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300000, C=FAKE + 0x400000, h0=None,
+             y=FAKE + 0x500000, h1=None, ws=FAKE + 0x1000000)
+    a.update(kw)
+    n = ctypes.c_size_t(0)
+    st = m3.lib.m3_pcs_workspace_size(ctypes.byref(d), ctypes.byref(n))
+    if st != 0:
+        return st
+    return m3.lib.m3_pcs_fwd(ctypes.byref(d), a["x"], a["dt"], a["A"], a["B"], a["C"], a["h0"], a["y"], a["h1"],
+                             a["ws"], n.value if ws_bytes is None else ws_bytes, None)
+
+
+def test_pcs_entry_points_reject_bad_arguments(m3):
+    """m3_pcs_workspace_size / m3_pcs_fwd: invalid descriptors, sizes outside
+    the kernels' range, NULL / misaligned / overlapping pointers and a short
+    workspace are refused before any HIP call."""
+    n = ctypes.c_size_t(0)
+    assert m3.lib.m3_pcs_workspace_size(None, ctypes.byref(n)) == 1
+    assert m3.lib.m3_pcs_workspace_size(ctypes.byref(_pcs_desc(m3)), None) == 1
+    for bad in (dict(batch=0), dict(seqlen=-1), dict(channels=0), dict(ngroups=3), dict(dstate=0),
+                dict(io_dtype=7), dict(nsegments=-1)):
+        assert _pcs(m3, _pcs_desc(m3, **bad)) == 1, bad
+    for uns in (dict(dstate=12), dict(dstate=4), dict(dstate=128), dict(channels=132),      # 132 % 8 != 0 (bf16)
+                dict(channels=192, ngroups=2), dict(nsegments=65)):
+        assert _pcs(m3, _pcs_desc(m3, **uns)) == 2, uns
+    assert _pcs(m3, _pcs_desc(m3, channels=132, io_dtype=m3.M3_F32), y=None) == 1    # f32 rows: 132 % 4 == 0
+    d = _pcs_desc(m3)
+    assert _pcs(m3, d, C=None) == 1
+    assert _pcs(m3, d, dt=FAKE + 0x100008) == 3                                    # not 16-byte aligned
+    assert _pcs(m3, d, h1=FAKE + 0x600004) == 3
+    assert _pcs(m3, d, y=FAKE + 0x10) == 1                                         # y overlaps x
+    assert _pcs(m3, d, h1=FAKE + 0x300000) == 1                                    # h1 overlaps B
+    assert _pcs(m3, d, h0=FAKE + 0x600000, h1=FAKE + 0x600000) == 1                # state updated in place
+    # a forced segmented schedule needs a workspace that overlaps nothing
+    ds = _pcs_desc(m3, nsegments=3)
+    assert m3.lib.m3_pcs_workspace_size(ctypes.byref(ds), ctypes.byref(n)) == 0 and n.value > 0
+    assert _pcs(m3, ds, ws_bytes=16) == 1
+    assert _pcs(m3, ds, ws=None) == 1
+    assert _pcs(m3, ds, ws=FAKE + 0x200000) == 1                                   # workspace overlaps A_log
+
+
+def test_pcs_schedule_sizes(m3):
+    """The library's segment choice: none when the (batch, channel tile)
+    workgroups fill the chip, several for few long sequences; a forced count is
+    clamped to the number of 64-token blocks.  Workspace: two [b, D, nseg, N]
+    fp32 state sets and one [b, D, nseg] step sum."""
+    def ws(**kw):
+        n = ctypes.c_size_t(0)
+        assert m3.lib.m3_pcs_workspace_size(ctypes.byref(_pcs_desc(m3, **kw)), ctypes.byref(n)) == 0
+        return n.value
+    assert ws(batch=16, seqlen=2048, channels=4096) == 0
+    b, D, N = 2, 2048, 16
+    nseg = 8           # 64 workgroups of 64 channels fill 512 slots (two per compute unit) in 8 segments
+    assert ws(batch=b, seqlen=32768, channels=D) == (2 * b * D * nseg * N + b * D * nseg) * 4
+    assert ws(batch=1, seqlen=100, channels=64, nsegments=64) == (2 * 64 * 2 * 16 + 64 * 2) * 4   # 2 blocks
+    assert ws(batch=1, seqlen=0, channels=64, nsegments=5) == 0
