@@ -73,7 +73,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="scan3,decode4,scan2,scan5,scan3r,scan3q,layer3,bwd3")
+    ap.add_argument("--workloads", default="scan3,decode4,scan2,scan5,scan3r,scan3q,layer3,bwd3,pcs,pcsl")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -243,6 +243,92 @@ def run_scan(torch, m3, cfg, steps, warmup):
     del x, B, C, dt, lam, th, Ar, y, fin, init, ws
     torch.cuda.empty_cache()
     return out
+
+
+# The per-coordinate scan (Mamba 1 preset).  Its work per coordinate-step (one
+# channel, one token, one of the N state coordinates) is one exponential and four
+# other VALU operations (the exponent dt a, the write dt x B, the decay FMA, the
+# readout FMA); with the exponential at quarter rate a coordinate-step occupies 8
+# lane-cycles of a SIMD's 16, so the chip's ceiling is 256 CUs x 4 SIMDs x 16 lanes
+# x 2.4 GHz / 8 = 4915 G coordinate-steps/s.  HBM bytes per (channel, token): x and
+# y in the I/O dtype, dt f32; B and C per (group, token); the states once per stream.
+PCS_STEP_PEAK_G = 256 * 4 * 16 * 2.4 / 8
+PCS_FLOP_PER_STEP = 6          # 2 products + 2 FMAs (the exponential counted apart)
+
+
+def pcs_bytes(cfg):
+    b, L, D, G, N = cfg["batch"], cfg["seqlen"], cfg["channels"], cfg["ngroups"], cfg["dstate"]
+    io = 2 if cfg["io"] == "bf16" else 4
+    return b * L * D * (2 * io + 4) + 2 * b * L * G * N * io + D * N * 4 + 2 * b * D * N * 4
+
+
+def run_pcs(torch, m3, name, steps, warmup):
+    from m3inputs.pcs import PCS_CONFIGS, make_pcs_inputs
+    dev = torch.device("cuda:0")
+    cfg = dict(PCS_CONFIGS[name])
+    t0 = time.time()
+    d = make_pcs_inputs(**{k: v for k, v in cfg.items()}, init=True)
+    io = torch.bfloat16 if cfg["io"] == "bf16" else torch.float32
+
+    def T(a, dt):
+        return torch.from_numpy(a).to(dev).to(dt).contiguous()
+    x, B, C = T(d["x"], io), T(d["B"], io), T(d["C"], io)
+    dt, Al, h0 = T(d["dt"], torch.float32), T(d["A_log"], torch.float32), T(d["h0"], torch.float32)
+    del d
+    log("[bench] %s inputs ready in %.1fs" % (name, time.time() - t0))
+    b, L, D = x.shape
+    N = B.shape[3]
+    y = torch.empty_like(x)
+    h1 = torch.empty((b, D, N), dtype=torch.float32, device=dev)
+    desc = m3.pcs_desc(x, B)
+    ws_bytes = m3.pcs_workspace_size(desc)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def call():
+        m3.pcs_fwd(x, dt, Al, B, C, h0, y=y, h1=h1, workspace=ws)
+    ms = time_calls(torch, call, steps, warmup)
+    ms_launch = per_launch_ms(torch, call, max(3, min(steps, 10)))
+    steps_g = b * L * D * N / 1e9
+    nbytes = pcs_bytes(cfg)
+    out = {"workload": name, "batch": b, "seqlen": L, "channels": D, "dstate": N, "ngroups": cfg["ngroups"],
+           "io": cfg["io"], "segments_workspace_bytes": ws_bytes, "ms_per_call": ms, "ms_per_launch": ms_launch,
+           "tokens_per_s": b * L / (ms * 1e-3), "gsteps_per_s": steps_g / (ms_launch * 1e-3),
+           "algo_gbs": nbytes / (ms_launch * 1e-3) / 1e9, "bytes_per_call": nbytes,
+           "coordinate_steps_per_call": b * L * D * N}
+    out["alu_frac"] = out["gsteps_per_s"] / PCS_STEP_PEAK_G
+    out["hbm_frac"] = out["algo_gbs"] / PEAK_HBM_GBS
+    out["valu_tflops"] = out["gsteps_per_s"] * PCS_FLOP_PER_STEP / 1e3
+    log("[bench] %s: %.3f ms/call (%.3f ms/launch), %.2f M tok/s, %.0f Gstep/s (%.1f%% of the %.0f ALU "
+        "ceiling), %.0f GB/s (%.1f%% HBM)" % (name, ms, ms_launch, out["tokens_per_s"] / 1e6, out["gsteps_per_s"],
+                                             100 * out["alu_frac"], PCS_STEP_PEAK_G, out["algo_gbs"],
+                                             100 * out["hbm_frac"]))
+    del x, B, C, dt, Al, h0, y, h1, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def pcs_cpu_baseline(name, budget_s):
+    """The fp64 C oracle of the per-coordinate scan, as it stands, on a bounded
+    sample: every batch and token of the first k channels."""
+    from m3inputs.pcs import PCS_CONFIGS, make_pcs_inputs
+    from oracle import pcs_cpu
+    cfg = dict(PCS_CONFIGS[name])
+    cores = cpu_cores()
+    d = make_pcs_inputs(**cfg, init=True)
+    D = cfg["channels"]
+    t0 = time.time()
+    pcs_cpu.scan(d, d["h0"], 0, 8, nthreads=cores)
+    one = (time.time() - t0) / 8
+    k = int(budget_s / max(one, 1e-5))
+    k = max(cores, min(D, k - k % cores))
+    t0 = time.time()
+    pcs_cpu.scan(d, d["h0"], 0, k, nthreads=cores)
+    dt = time.time() - t0
+    toks = cfg["batch"] * cfg["seqlen"] * k / D          # whole tokens' worth of channels
+    del d
+    return {"value": toks / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "%s: channels 0..%d of %d, every batch and token (%.2f%% of the workload) in %.1f s; fp64 "
+                      "recurrence in C, channels over threads" % (name, k - 1, D, 100.0 * k / D, dt)}
 
 
 def layer_bytes(cfg):
@@ -480,7 +566,8 @@ def main():
     res = {}
     names = {"scan2": "siso_bf16_mamba2", "scan3": "mimo_bf16_prefill", "scan5": "mimo_bf16_long",
              "decode4": "mimo_bf16_decode", "scan3r": "mimo_bf16_prefill", "scan3q": "mimo_bf16_prefill",
-             "layer3": "mimo_bf16_prefill", "bwd3": "mimo_bf16_prefill", "copy": None}
+             "layer3": "mimo_bf16_prefill", "bwd3": "mimo_bf16_prefill", "copy": None, "pcs": None,
+             "pcsl": None}
     for w in wl:
         cfg = config_by_name(names[w]) if names[w] else None
         if w == "scan3r":      # the headline prefill with per-token heavy-tail rates
@@ -495,12 +582,16 @@ def main():
             res[w] = run_layer(torch, m3, cfg, args.steps, args.warmup)
         elif w.startswith("bwd"):
             res[w] = run_bwd(torch, m3, cfg, max(3, args.steps // 2), args.warmup)
+        elif w in ("pcs", "pcsl"):
+            res[w] = run_pcs(torch, m3, "pcs_balanced" if w == "pcs" else "pcs_long", args.steps, args.warmup)
         elif w.startswith("scan"):
             steps = args.steps if w != "scan5" else max(3, args.steps // 4)
             res[w] = run_scan(torch, m3, cfg, steps, args.warmup)
         else:
             res[w] = run_decode(torch, m3, cfg, args.decode_steps)
     main_w = "scan3" if "scan3" in res else [w for w in wl if w != "copy"][0] if any(w != "copy" for w in wl) else "copy"
+    if main_w in ("pcs", "pcsl"):
+        main_w = "copy" if "copy" in res else main_w
     if main_w == "copy":
         print(json.dumps({"metric": "copy calibration", "value": res["copy"]["gbs"], "unit": "GB/s"}), flush=True)
         return
@@ -566,6 +657,22 @@ def main():
                                               "algo_tflops": v["algo_tflops"], "mfma_frac": v["mfma_frac"],
                                               "algo_gbs": v["algo_gbs"], "hbm_frac": v["hbm_frac"]}
                               for v in others.values()}
+    pcs = {k: v for k, v in res.items() if k in ("pcs", "pcsl")}
+    if pcs:
+        line["pcs"] = {v["workload"]: {k2: v[k2] for k2 in ("tokens_per_s", "ms_per_call", "ms_per_launch",
+                                                              "gsteps_per_s", "alu_frac", "algo_gbs", "hbm_frac",
+                                                              "batch", "seqlen", "channels", "dstate")}
+                       for v in pcs.values()}
+        pw = pcs.get("pcs", next(iter(pcs.values())))
+        line["roofline_pcs"] = {"bound": "alu", "achieved": pw["gsteps_per_s"], "peak": PCS_STEP_PEAK_G,
+                                "unit": "Gstep/s", "frac": pw["alu_frac"], "workload": pw["workload"],
+                                "traffic": None, "algorithmic_bytes": pw["bytes_per_call"],
+                                "coordinate_steps": pw["coordinate_steps_per_call"],
+                                "hbm_achieved_gbs": pw["algo_gbs"], "hbm_frac": pw["hbm_frac"]}
+        if not args.no_cpu:
+            line["cpu_baseline_pcs"] = pcs_cpu_baseline(pw["workload"], min(args.cpu_seconds, 8.0))
+            log("[bench] pcs cpu oracle: %.1f tokens/s (%s)" % (line["cpu_baseline_pcs"]["value"],
+                                                                 line["cpu_baseline_pcs"]["sample"]))
     line["cpu_baseline"] = cpu
     s = json.dumps(line)
     print(s, flush=True)

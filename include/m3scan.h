@@ -322,7 +322,7 @@ typedef struct {
     int nsegments;    /* schedule: 0 = library's choice; k in 1..64 asks for k sequence
                          segments per (batch, channel), evaluated in parallel from
                          zero-state summaries and joined by a prefix scan of their
-                         affine maps (clamped to the number of 64-token blocks).  The
+                         affine maps (clamped to the number of 32-token blocks).  The
                          result does not depend on it beyond rounding. */
 } m3_pcs_desc;
 

@@ -612,6 +612,13 @@ m3_status m3_scan_bwd(const m3_desc* d, const void* x, const void* B, const void
 
 namespace {
 
+// Tokens per segment whose rows of x, dt, y (D elements) and of B, C (G N elements)
+// stay under 2 GiB, the reach of the kernel's 32-bit buffer offsets.
+long long pcs_max_segment_rows(const m3_pcs_desc* d) {
+    const long long row = std::max<long long>((long long)d->channels, (long long)d->ngroups * d->dstate) * 4;
+    return (1LL << 31) / row - 64;            // 64 rows of margin for the prefetch past a segment's end
+}
+
 // Checks of an m3_pcs_desc: M3_ERR_INVALID_ARG for an invalid one, M3_ERR_UNSUPPORTED
 // outside the kernels' range (state widths, channel alignment, groups split by a
 // workgroup's channel tile, more than 64 segments).
@@ -627,22 +634,29 @@ m3_status check_pcs_desc(const m3_pcs_desc* d) {
     // a workgroup's channels read one group's B and C
     if (d->ngroups > 1 && (d->channels / d->ngroups) % pcs_channels_per_group(d->dstate)) return M3_ERR_UNSUPPORTED;
     if (d->nsegments > 64) return M3_ERR_UNSUPPORTED;
+    // every segment's rows must fit the kernel's 32-bit offsets
+    const long long max_rows = pcs_max_segment_rows(d);
+    if (max_rows < 1 || (d->seqlen + max_rows - 1) / max_rows > 64) return M3_ERR_UNSUPPORTED;
     return M3_OK;
 }
 
-// Segments per (batch, channel): just enough that the workgroups fill the compute
-// units' slots, at most 64 (one wave's lanes in the carry pass) and at most the number
-// of token blocks; each segment is a whole number of blocks.
+// Segments per (batch, channel).  A segmented run costs a second pass over the
+// sequence (the summary), so it is chosen only when the (batch, channel tile) waves
+// alone would leave SIMDs idle (fewer than one wave per SIMD, 1024 SIMDs); then enough
+// segments for about four waves per SIMD, at most 64 (one wave's lanes in the carry
+// pass) and at most the number of token blocks.  Each segment is a whole number of
+// blocks, and its rows of x, dt and y stay under 2 GiB (the kernel's 32-bit offsets).
 void pcs_segments(const m3_pcs_desc* d, int* nseg, int* seglen) {
     const int TB = pcs_block_tokens();
     const int nblocks = (d->seqlen + TB - 1) / TB;
     int k = d->nsegments;
     if (k == 0) {
         const int cw = pcs_channels_per_group(d->dstate);
-        const long long wgs = (long long)d->batch * ((d->channels + cw - 1) / cw);
-        const long long slots = 256LL * pcs_groups_per_cu(d->dstate);
-        k = wgs >= slots ? 1 : (int)std::min<long long>(64, (slots + wgs - 1) / wgs);
+        const long long waves = (long long)d->batch * ((d->channels + cw - 1) / cw) * pcs_waves_per_group(d->dstate);
+        k = waves >= 1024 ? 1 : (int)std::min<long long>(64, (4096 + waves - 1) / waves);
     }
+    const long long max_rows = pcs_max_segment_rows(d);
+    k = std::max<long long>(k, (d->seqlen + max_rows - 1) / max_rows);
     k = std::max(1, std::min(k, std::max(1, nblocks)));
     const int bps = (nblocks + k - 1) / k;   // blocks per segment
     *seglen = std::max(1, bps) * TB;

@@ -125,11 +125,12 @@ struct PcsArgs {
     void* y;
     float* h1;              // final state (null = not written)
     int nseg, seglen;       // segmented schedule: nseg segments of seglen tokens
-    float* ws;              // workspace (nseg > 1 only)
+    float* ws;              // workspace (segmented schedule only)
 };
 bool pcs_supported_state(int N);
 int pcs_channels_per_group(int N);   // channels per workgroup
 int pcs_groups_per_cu(int N);        // workgroups one compute unit holds at once
+int pcs_waves_per_group(int N);
 int pcs_block_tokens();              // tokens per block (segments are whole blocks)
 size_t pcs_workspace_bytes(const PcsArgs& a);
 hipError_t launch_pcs(const PcsArgs& a, hipStream_t s);

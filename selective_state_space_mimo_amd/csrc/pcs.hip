@@ -8,18 +8,9 @@
 // coordinate n, with the static rate a[d, n] = -exp(A_log[d, n]):
 //     h[n] <- exp(dt a[d, n]) h[n] + dt B[g, n] x,      y = sum_n C[g, n] h[n].
 //
-// Work decomposition.  A workgroup (16 N threads) owns 64 consecutive channels
-// of one batch (and one sequence segment); each lane holds
-// four coordinates of one channel (a channel's lanes are consecutive), so the
-// readout is a sum over the channel's N / 4 lanes (DPP within quads, lane swaps
-// beyond).  Tokens go in blocks of 64: the block's x and dt tiles are fetched as
-// whole rows (the channels of one token are contiguous), transposed into LDS
-// (channel-major, so a lane reads four tokens per access), B and C rows are
-// staged as fp32, and the outputs leave through an LDS tile as whole rows.  The
-// next block's rows are fetched into registers while the current one computes.
-// The recurrence itself is sequential in each lane (work-optimal: N / 4
-// independent chains per lane, and enough channels to fill the chip on the
-// training shapes).
+// The recurrence is sequential in each lane (work-optimal: K independent chains
+// per lane, and enough channels to fill the chip on the training shapes); the
+// work decomposition is described at the kernel.
 //
 // Few channels and long sequences: the sequence is split into segments.  Pass 1
 // runs each segment from a zero state and records its local final state and the
@@ -36,25 +27,57 @@ namespace m3 {
 
 namespace {
 
-constexpr int kPcsTB = 64;                 // tokens per block
 constexpr int kPcsCW = 64;                 // channels per workgroup
 constexpr float kPcsLog2e = 1.4426950408889634f;
 
+// Coordinates per lane and tokens per block (the schedule; the result does not
+// depend on them beyond rounding).
+#ifndef PCS_K
+#define PCS_K 4
+#endif
+#ifndef PCS_TB
+#define PCS_TB 32
+#endif
+#ifndef PCS_STREAM
+#define PCS_STREAM 1
+#endif
+constexpr int kPcsK = PCS_K;
+constexpr int kPcsTB = PCS_TB;
+
 enum PcsMode { kPcsFull = 0, kPcsSummary = 1 };
+
+// Floats of the segmented schedule's part of the workspace (local final states and
+// incoming states [b, D, nseg, N], step sums [b, D, nseg]), rounded to 64 floats.
+size_t pcs_seg_floats(const PcsArgs& a) {
+    if (a.nseg <= 1) return 0;
+    const size_t S = (size_t)a.b * a.D * a.nseg;
+    return (2 * S * a.N + S + 63) & ~(size_t)63;
+}
 
 template <int N>
 struct PcsLayout {
-    static constexpr int LPC = N / 4;                          // lanes per channel
+    static constexpr int K = kPcsK < N ? kPcsK : N;            // coordinates per lane
+    static constexpr int LPC = N / K;                          // lanes per channel
     static constexpr int CW = kPcsCW;                          // channels per workgroup
     static constexpr int NT = CW * LPC;                        // threads per workgroup
-    static constexpr int XS = kPcsTB + 4;                      // row stride (floats) of the transposed tiles
-    static constexpr int xs = 0;                               // float [CW][XS]: x, channel-major
+    static constexpr int TB = kPcsTB;                          // tokens per block
+    static constexpr int XS = TB + 4;                          // row stride (floats) of the transposed tiles
+    static constexpr int xs = 0;                               // float [CW][XS]: x, channel-major; then y
     static constexpr int ds = xs + CW * XS * 4;                // float [CW][XS]: dt
     static constexpr int bs = ds + CW * XS * 4;                // float [TB][N]: B
-    static constexpr int cs = bs + kPcsTB * N * 4;             // float [TB][N]: C
-    static constexpr int ys = cs + kPcsTB * N * 4;             // float [TB][CW]: outputs, token-major
-    static constexpr int total = ys + kPcsTB * CW * 4;
+    static constexpr int cs = bs + TB * N * 4;                 // float [TB][N]: C
+    static constexpr int total = cs + TB * N * 4;
+    static_assert(K % 4 == 0 && N % K == 0 && LPC <= 16 && NT <= 1024, "lane layout");
 };
+
+// A buffer resource over [base, base + bytes): loads past the end read zero and stores
+// past it are dropped, so edge tiles need no branches (and the compiler can count
+// the loads and stores in flight exactly instead of waiting for all of them).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pcs_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kPcsOob = 0x7ffffff0;        // an offset past every resource's end
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -63,17 +86,28 @@ __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u 
 // the group receiving the total.
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
-    if constexpr (W >= 2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xb1, 0xf, 0xf, false));  // quad_perm 1,0,3,2
-    if constexpr (W >= 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4e, 0xf, 0xf, false));  // quad_perm 2,3,0,1
+    // (the moves carry bound_ctrl, so the compiler folds each into its add as a DPP operand)
+    if constexpr (W >= 2) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, true));  // quad_perm 1,0,3,2
+    if constexpr (W >= 4) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, true));  // quad_perm 2,3,0,1
     if constexpr (W >= 8) v += __shfl_xor(v, 4);
     if constexpr (W >= 16) v += __shfl_xor(v, 8);
     return v;
 }
 
+// Work decomposition.  A workgroup of 64 N / K threads owns 64 consecutive
+// channels of one batch (and one sequence segment); each lane holds K coordinates
+// of one channel (a channel's N / K lanes are consecutive), so the readout is a
+// sum over the channel's lanes (DPP within quads, lane swaps beyond).  Tokens go
+// in blocks of TB: the block's x and dt tiles are fetched as whole rows (the
+// channels of one token are contiguous) and transposed into LDS (channel-major,
+// so a lane reads four tokens per access); B and C rows are staged as fp32.  Each
+// channel's readout overwrites the x entry of the same token, already consumed, and
+// the block's outputs leave from that tile as whole rows.  The next block's rows
+// are fetched into registers while the current one computes.
 template <int N, int MODE, bool BF16>
 __global__ __launch_bounds__(PcsLayout<N>::NT) void pcs_kernel(PcsArgs a) {
     using LY = PcsLayout<N>;
-    constexpr int LPC = LY::LPC, CW = LY::CW, XS = LY::XS, TB = kPcsTB, kPcsThreads = LY::NT;
+    constexpr int K = LY::K, LPC = LY::LPC, CW = LY::CW, XS = LY::XS, TB = LY::TB, NT = LY::NT;
     constexpr bool kFull = MODE == kPcsFull;
     constexpr int ES = BF16 ? 2 : 4;
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -81,7 +115,6 @@ __global__ __launch_bounds__(PcsLayout<N>::NT) void pcs_kernel(PcsArgs a) {
     float* sD = reinterpret_cast<float*>(smem + LY::ds);
     float* sB = reinterpret_cast<float*>(smem + LY::bs);
     float* sC = reinterpret_cast<float*>(smem + LY::cs);
-    float* sY = reinterpret_cast<float*>(smem + LY::ys);
 
     const int tid = threadIdx.x;
     const int D = a.D, L = a.L, G = a.G, nseg = a.nseg;
@@ -94,16 +127,16 @@ __global__ __launch_bounds__(PcsLayout<N>::NT) void pcs_kernel(PcsArgs a) {
     const int g = d0 * G / D;                  // the tile's channels share one group (checked on the host)
     const int T0 = seg * a.seglen, T1 = min(L, T0 + a.seglen);
 
-    // this lane: channel c of the tile, coordinates 4 q .. 4 q + 3
+    // this lane: channel c of the tile, coordinates K q .. K q + K - 1
     const int c = tid / LPC, q = tid % LPC;
     const int d = d0 + c;
     const bool live = d < D;
-    float a2[4], h[4];
+    float a2[K], h[K];
     const size_t S = (size_t)a.b * D * nseg;
     const size_t chs = ((size_t)bi * D + (live ? d : 0)) * nseg + seg;    // (batch, channel, segment)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int n = 4 * q + m;
+    for (int m = 0; m < K; ++m) {
+        const int n = K * q + m;
         a2[m] = live ? -expf(a.A_log[(size_t)d * N + n]) * kPcsLog2e : 0.f;
         float v = 0.f;
         if (kFull && live) {
@@ -113,50 +146,55 @@ __global__ __launch_bounds__(PcsLayout<N>::NT) void pcs_kernel(PcsArgs a) {
         h[m] = v;
     }
     float dsum = 0.f;                                      // sum of the segment's steps (summary)
+    // The state and rate loads land before the first block: otherwise the wait for them,
+    // merged over the block loop, also waits for each block's prefetch as its math starts.
+    __builtin_amdgcn_s_waitcnt(0x0f70);                    // vmcnt(0)
 
     // ---- block fetch: rows of the block's tokens into registers ----
-    // x: TB rows of CW * ES bytes; dt: TB rows of CW * 4 bytes; B, C: TB rows of N * ES bytes.
-    constexpr int XP = TB * CW * ES / 16, DP = TB * CW * 4 / 16, BP = TB * N * ES / 16;   // 16-byte pieces
-    constexpr int XV = (XP + kPcsThreads - 1) / kPcsThreads;     // ... per thread
-    constexpr int DV = (DP + kPcsThreads - 1) / kPcsThreads;
-    constexpr int BV = (BP + kPcsThreads - 1) / kPcsThreads;
-    uint4 rX[XV], rD[DV], rB[BV], rC[BV];
-    const uint8_t* xg = static_cast<const uint8_t*>(a.x);
-    const uint8_t* dg = reinterpret_cast<const uint8_t*>(a.dt);
-    const uint8_t* bg = static_cast<const uint8_t*>(a.B);
-    const uint8_t* cg = static_cast<const uint8_t*>(a.C);
+    // x: TB rows of CW * ES bytes; dt: TB rows of CW * 4 bytes (16-byte pieces); B, C: TB
+    // rows of N * ES bytes (4-byte pieces).  Where a tile divides evenly among the threads
+    // (the common shapes) no thread is idle and no check is compiled.
+    constexpr int XP = TB * CW * ES / 16, DP = TB * CW * 4 / 16, BP = TB * N * ES / 4;
+    constexpr int XV = (XP + NT - 1) / NT;     // ... per thread
+    constexpr int DV = (DP + NT - 1) / NT;
+    constexpr int BV = (BP + NT - 1) / NT;
+    constexpr bool kXe = XP % NT == 0, kDe = DP % NT == 0, kBe = BP % NT == 0;
+    uint4 rX[XV], rD[DV];
+    uint32_t rB[BV], rC[BV];
+    // resources over the segment's rows (the host keeps each under 2 GiB): a row at or past
+    // T1 reads zero, and an output row there is dropped
+    const size_t row0 = (size_t)bi * L + T0;
+    const uint32_t nrow = (uint32_t)(T1 - T0);
+    const auto rx = pcs_rsrc(static_cast<const uint8_t*>(a.x) + row0 * D * ES, nrow * (uint32_t)D * ES);
+    const auto rd = pcs_rsrc(reinterpret_cast<const uint8_t*>(a.dt) + row0 * D * 4, nrow * (uint32_t)D * 4);
+    const auto rb = pcs_rsrc(static_cast<const uint8_t*>(a.B) + row0 * G * N * ES, nrow * (uint32_t)(G * N * ES));
+    const auto rc = pcs_rsrc(static_cast<const uint8_t*>(a.C) + row0 * G * N * ES, nrow * (uint32_t)(G * N * ES));
+    const auto ry = pcs_rsrc(static_cast<uint8_t*>(a.y) + row0 * D * ES, nrow * (uint32_t)D * ES);
     auto fetch = [&](int t0) {
+        const int tr = t0 - T0;                                   // the block's first row in the segment
         constexpr int XPR = CW * ES / 16;                         // 16-byte pieces per x row
 #pragma unroll
         for (int v = 0; v < XV; ++v) {
-            const int e = tid + kPcsThreads * v, r = e / XPR, k = e % XPR;
-            const int t = t0 + r, dd = d0 + k * (16 / ES);
-            uint4 z = {0u, 0u, 0u, 0u};
-            if (e < XP && t < T1 && dd < D) z = *reinterpret_cast<const uint4*>(xg + (((size_t)bi * L + t) * D + dd) * ES);
-            rX[v] = z;
+            const int e = tid + NT * v, r = e / XPR, k = e % XPR;
+            const int dd = d0 + k * (16 / ES);
+            const int o = ((kXe || e < XP) && dd < D) ? ((tr + r) * D + dd) * ES : kPcsOob;
+            rX[v] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0));
         }
         constexpr int DPR = CW * 4 / 16;
 #pragma unroll
         for (int v = 0; v < DV; ++v) {
-            const int e = tid + kPcsThreads * v, r = e / DPR, k = e % DPR;
-            const int t = t0 + r, dd = d0 + k * 4;
-            uint4 z = {0u, 0u, 0u, 0u};
-            if (e < DP && t < T1 && dd < D) z = *reinterpret_cast<const uint4*>(dg + (((size_t)bi * L + t) * D + dd) * 4);
-            rD[v] = z;
+            const int e = tid + NT * v, r = e / DPR, k = e % DPR;
+            const int dd = d0 + k * 4;
+            const int o = ((kDe || e < DP) && dd < D) ? ((tr + r) * D + dd) * 4 : kPcsOob;
+            rD[v] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, o, 0, 0));
         }
-        constexpr int BPR = N * ES / 16;
+        constexpr int BPR = N * ES / 4;
 #pragma unroll
         for (int v = 0; v < BV; ++v) {
-            const int e = tid + kPcsThreads * v, r = e / BPR, k = e % BPR;
-            const int t = t0 + r;
-            uint4 zb = {0u, 0u, 0u, 0u}, zc = {0u, 0u, 0u, 0u};
-            if (e < BP && t < T1) {
-                const size_t o = ((((size_t)bi * L + t) * G + g) * N) * ES + 16 * k;
-                zb = *reinterpret_cast<const uint4*>(bg + o);
-                if (kFull) zc = *reinterpret_cast<const uint4*>(cg + o);
-            }
-            rB[v] = zb;
-            rC[v] = zc;
+            const int e = tid + NT * v, r = e / BPR, k = e % BPR;
+            const int o = (kBe || e < BP) ? ((tr + r) * G + g) * N * ES + 4 * k : kPcsOob;
+            rB[v] = __builtin_amdgcn_raw_buffer_load_b32(rb, o, 0, 0);
+            if (kFull) rC[v] = __builtin_amdgcn_raw_buffer_load_b32(rc, o, 0, 0);
         }
     };
     // the fetched rows into the LDS tiles: x and dt transposed (channel-major), B and C as fp32
@@ -164,9 +202,9 @@ __global__ __launch_bounds__(PcsLayout<N>::NT) void pcs_kernel(PcsArgs a) {
         constexpr int XPR = CW * ES / 16;
 #pragma unroll
         for (int v = 0; v < XV; ++v) {
-            const int e = tid + kPcsThreads * v, r = e / XPR, k = e % XPR;
+            const int e = tid + NT * v, r = e / XPR, k = e % XPR;
             const int cc = k * (16 / ES);
-            if (e >= XP) break;
+            if constexpr (!kXe) if (e >= XP) break;
             if constexpr (BF16) {
                 const uint32_t w[4] = {rX[v].x, rX[v].y, rX[v].z, rX[v].w};
 #pragma unroll
@@ -184,77 +222,78 @@ __global__ __launch_bounds__(PcsLayout<N>::NT) void pcs_kernel(PcsArgs a) {
         constexpr int DPR = CW * 4 / 16;
 #pragma unroll
         for (int v = 0; v < DV; ++v) {
-            const int e = tid + kPcsThreads * v, r = e / DPR, k = e % DPR;
+            const int e = tid + NT * v, r = e / DPR, k = e % DPR;
             const int cc = k * 4;
-            if (e >= DP) break;
+            if constexpr (!kDe) if (e >= DP) break;
             sD[(cc + 0) * XS + r] = __uint_as_float(rD[v].x);
             sD[(cc + 1) * XS + r] = __uint_as_float(rD[v].y);
             sD[(cc + 2) * XS + r] = __uint_as_float(rD[v].z);
             sD[(cc + 3) * XS + r] = __uint_as_float(rD[v].w);
         }
-        constexpr int BPR = N * ES / 16;
+        constexpr int BPR = N * ES / 4;
 #pragma unroll
         for (int v = 0; v < BV; ++v) {
-            const int e = tid + kPcsThreads * v, r = e / BPR, k = e % BPR;
-            if (e < BP) {
-                const int n0 = k * (16 / ES);
-                if constexpr (BF16) {
-                    const uint32_t wb[4] = {rB[v].x, rB[v].y, rB[v].z, rB[v].w};
-                    const uint32_t wc[4] = {rC[v].x, rC[v].y, rC[v].z, rC[v].w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        sB[r * N + n0 + 2 * i] = bf16_lo(wb[i]);
-                        sB[r * N + n0 + 2 * i + 1] = bf16_hi(wb[i]);
-                        if (kFull) {
-                            sC[r * N + n0 + 2 * i] = bf16_lo(wc[i]);
-                            sC[r * N + n0 + 2 * i + 1] = bf16_hi(wc[i]);
-                        }
-                    }
-                } else {
-                    *reinterpret_cast<uint4*>(sB + r * N + n0) = rB[v];
-                    if (kFull) *reinterpret_cast<uint4*>(sC + r * N + n0) = rC[v];
-                }
+            const int e = tid + NT * v, r = e / BPR, k = e % BPR;
+            if constexpr (!kBe) if (e >= BP) break;
+            const int n0 = k * (4 / ES);
+            if constexpr (BF16) {
+                *reinterpret_cast<float2*>(sB + r * N + n0) = float2{bf16_lo(rB[v]), bf16_hi(rB[v])};
+                if (kFull) *reinterpret_cast<float2*>(sC + r * N + n0) = float2{bf16_lo(rC[v]), bf16_hi(rC[v])};
+            } else {
+                sB[r * N + n0] = __uint_as_float(rB[v]);
+                if (kFull) sC[r * N + n0] = __uint_as_float(rC[v]);
             }
         }
     };
-    // the block's outputs, whole rows of CW channels
+    // the block's outputs (in the x tile, channel-major) as whole rows of CW channels
     auto store_y = [&](int t0) {
         if constexpr (kFull) {
             constexpr int EPS = 16 / ES;                         // elements per 16-byte piece
             constexpr int YPR = CW / EPS;
+            constexpr int YP = TB * YPR;
 #pragma unroll
-            for (int v = 0; v < (TB * YPR + kPcsThreads - 1) / kPcsThreads; ++v) {
-                const int e = tid + kPcsThreads * v, r = e / YPR, k = e % YPR;
-                if (e >= TB * YPR) break;
-                const int t = t0 + r, dd = d0 + k * EPS;
-                const float* src = sY + r * CW + k * EPS;
+            for (int v = 0; v < (YP + NT - 1) / NT; ++v) {
+                const int e = tid + NT * v, r = e / YPR, k = e % YPR;
+                if constexpr (YP % NT != 0) if (e >= YP) break;
+                const int dd = d0 + k * EPS;
+                const float* src = sX + (k * EPS) * XS + r;
                 uint4 o;
                 if constexpr (BF16) {
                     uint32_t w[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         bf16x2 p;
-                        p[0] = (bf16)src[2 * i];
-                        p[1] = (bf16)src[2 * i + 1];
+                        p[0] = (bf16)src[(2 * i) * XS];
+                        p[1] = (bf16)src[(2 * i + 1) * XS];
                         w[i] = __builtin_bit_cast(uint32_t, p);
                     }
                     o = uint4{w[0], w[1], w[2], w[3]};
                 } else {
-                    o = uint4{__float_as_uint(src[0]), __float_as_uint(src[1]), __float_as_uint(src[2]), __float_as_uint(src[3])};
+                    o = uint4{__float_as_uint(src[0]), __float_as_uint(src[XS]), __float_as_uint(src[2 * XS]),
+                              __float_as_uint(src[3 * XS])};
                 }
-                if (t < T1 && dd < D) *reinterpret_cast<uint4*>(static_cast<uint8_t*>(a.y) + (((size_t)bi * L + t) * D + dd) * ES) = o;
+                const int off = dd < D ? ((t0 - T0 + r) * D + dd) * ES : kPcsOob;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), ry, off, 0, 0);
             }
         }
     };
 
     if (T0 < T1) fetch(T0);
+    if constexpr (kFull) {
+        // as many dropped stores (past the resource's end) as a block stores, so that the
+        // stores in flight at the first block's staging match those of every later block
+        // and the wait there covers only the fetch
+        constexpr int YV = (TB * CW * ES / 16 + NT - 1) / NT;
+#pragma unroll
+        for (int v = 0; v < YV; ++v) __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{0u, 0u, 0u, 0u}, ry, kPcsOob, 0, 0);
+    }
     for (int t0 = T0; t0 < T1; t0 += TB) {
         __syncthreads();                       // the previous block's tiles are consumed
         stage();
         __syncthreads();
         if (t0 + TB < T1) fetch(t0 + TB);      // the next block's rows, under this block's math
         const int nt = min(TB, T1 - t0);
-        const float* xr = sX + c * XS;
+        float* xr = sX + c * XS;
         const float* dr = sD + c * XS;
 #pragma unroll 1
         for (int t4 = 0; t4 < TB; t4 += 4) {
@@ -267,15 +306,26 @@ __global__ __launch_bounds__(PcsLayout<N>::NT) void pcs_kernel(PcsArgs a) {
                 const int t = t4 + j;
                 const float st = ds4[j];
                 const float u = st * xs4[j];
-                const float4 bv = *reinterpret_cast<const float4*>(sB + t * N + 4 * q);
-                const float b4[4] = {bv.x, bv.y, bv.z, bv.w};
+                float bk[K];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) h[m] = __builtin_amdgcn_exp2f(st * a2[m]) * h[m] + u * b4[m];
+                for (int m4 = 0; m4 < K; m4 += 4) {
+                    const float4 bv = *reinterpret_cast<const float4*>(sB + t * N + K * q + m4);
+                    bk[m4] = bv.x; bk[m4 + 1] = bv.y; bk[m4 + 2] = bv.z; bk[m4 + 3] = bv.w;
+                }
+#pragma unroll
+                for (int m = 0; m < K; ++m) h[m] = __builtin_amdgcn_exp2f(st * a2[m]) * h[m] + u * bk[m];
                 if constexpr (kFull) {
-                    const float4 cv = *reinterpret_cast<const float4*>(sC + t * N + 4 * q);
-                    float acc = cv.x * h[0] + cv.y * h[1] + cv.z * h[2] + cv.w * h[3];
+                    float acc;
+#pragma unroll
+                    for (int m4 = 0; m4 < K; m4 += 4) {
+                        const float4 cv = *reinterpret_cast<const float4*>(sC + t * N + K * q + m4);
+                        const float part = cv.x * h[m4] + cv.y * h[m4 + 1] + cv.z * h[m4 + 2] + cv.w * h[m4 + 3];
+                        acc = m4 == 0 ? part : acc + part;
+                    }
                     acc = group_sum<LPC>(acc);
-                    if (q == 0) sY[t * CW + c] = acc;
+                    // x[t] of this channel was read above by every lane of the channel (one
+                    // wave); the channel's lanes all hold the sum and write the same value
+                    xr[t] = acc;
                 } else {
                     dsum += st;
                 }
@@ -290,11 +340,188 @@ __global__ __launch_bounds__(PcsLayout<N>::NT) void pcs_kernel(PcsArgs a) {
     if constexpr (kFull) {
         if (T1 == L && a.h1)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) a.h1[((size_t)bi * D + d) * N + 4 * q + m] = h[m];
+            for (int m = 0; m < K; ++m) a.h1[((size_t)bi * D + d) * N + K * q + m] = h[m];
     } else {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) a.ws[chs * N + 4 * q + m] = h[m];
+        for (int m = 0; m < K; ++m) a.ws[chs * N + K * q + m] = h[m];
         if (q == 0) a.ws[2 * S * N + chs] = dsum;
+    }
+}
+
+// ---- streaming form, N <= 16 ------------------------------------------------------
+// One wave per workgroup; lane c owns channel d0 + c with all N coordinates, so the
+// readout is a sum inside the lane.  Per token a wave reads one 64-channel row piece of
+// x (128 bytes in bf16) and of dt and writes one of y, each a whole cache line; those
+// accesses run PF tokens ahead of the math through a ring of registers.  B and C rows are
+// the same for every lane of the wave: they come in tiles of PF tokens (one vector load
+// per lane, a tile ahead, in the same ring as x and dt), are widened to fp32 into one of
+// two LDS tiles, and each token's rows are read from there as uniform (broadcast) LDS
+// reads.  LDS reads complete in order, so their waits stay exact.  (Scalar loads would
+// deliver the rows as scalar operands, but they complete out of order: each wait for one
+// drains all of them, which defeats any prefetch.)  One wave per workgroup: no barrier.
+constexpr int kPcsPF = 16;                 // tokens in flight (the ring), and tokens per B, C tile
+
+template <int N, int MODE, bool BF16>
+__global__ __launch_bounds__(64) void pcs_stream_kernel(PcsArgs a) {
+    constexpr bool kFull = MODE == kPcsFull;
+    constexpr int ES = BF16 ? 2 : 4, PF = kPcsPF;
+    const int lane = threadIdx.x;
+    const int D = a.D, L = a.L, G = a.G, nseg = a.nseg;
+    const int ntile = (D + 63) / 64;
+    int bid = blockIdx.x;
+    const int seg = bid % nseg;
+    bid /= nseg;
+    const int tile = bid % ntile, bi = bid / ntile;
+    const int d0 = tile * 64, d = d0 + lane;
+    const int g = d0 * G / D;                  // the tile's channels share one group (checked on the host)
+    const int T0 = seg * a.seglen, T1 = min(L, T0 + a.seglen);
+    const bool live = d < D;
+
+    float a2[N], h[N];
+    const size_t S = (size_t)a.b * D * nseg;
+    const size_t chs = ((size_t)bi * D + (live ? d : 0)) * nseg + seg;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        a2[n] = live ? -expf(a.A_log[(size_t)d * N + n]) * kPcsLog2e : 0.f;
+        float v = 0.f;
+        if (kFull && live) {
+            if (seg == 0) v = a.h0 ? a.h0[((size_t)bi * D + d) * N + n] : 0.f;
+            else v = a.ws[S * N + chs * N + n];
+        }
+        h[n] = v;
+    }
+    float dsum = 0.f;
+    __builtin_amdgcn_s_waitcnt(0x0f70);                    // vmcnt(0): see the tiled kernel
+
+    // resources over the segment's rows (the host keeps each under 2 GiB); rows at or past
+    // T1 read zero (dt = 0 leaves the state unchanged) and their outputs are dropped
+    const size_t row0 = (size_t)bi * L + T0;
+    const uint32_t nrow = (uint32_t)(T1 - T0);
+    const auto rx = pcs_rsrc(static_cast<const uint8_t*>(a.x) + row0 * D * ES, nrow * (uint32_t)D * ES);
+    const auto rd = pcs_rsrc(reinterpret_cast<const uint8_t*>(a.dt) + row0 * D * 4, nrow * (uint32_t)D * 4);
+    const auto ry = pcs_rsrc(static_cast<uint8_t*>(a.y) + row0 * D * ES, nrow * (uint32_t)D * ES);
+    const int lo = live ? d * ES : kPcsOob, lod = live ? d * 4 : kPcsOob;
+    // the ring holds the loaded bits; they are converted where used, PF tokens later (a
+    // conversion at the load would wait for the load at once)
+    auto ld_x = [&](int r) -> uint32_t {
+        if constexpr (BF16) return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rx, lo + r * D * ES, 0, 0);
+        else return __builtin_amdgcn_raw_buffer_load_b32(rx, lo + r * D * 4, 0, 0);
+    };
+    auto ld_dt = [&](int r) -> uint32_t { return __builtin_amdgcn_raw_buffer_load_b32(rd, lod + r * D * 4, 0, 0); };
+    // B, C tiles: PF rows of N values of the wave's group; 16-byte pieces, lanes over (B, C)
+    const auto rb = pcs_rsrc(static_cast<const uint8_t*>(a.B) + row0 * G * N * ES, nrow * (uint32_t)(G * N * ES));
+    const auto rc = pcs_rsrc(static_cast<const uint8_t*>(a.C) + row0 * G * N * ES, nrow * (uint32_t)(G * N * ES));
+    constexpr int PPR = N * ES / 16;                       // pieces per row
+    constexpr int TP = PF * PPR;                           // pieces per tile
+    constexpr int NTEN = kFull ? 2 : 1;                    // B, and C when the readout is made
+    constexpr int TV = (TP + 63) / 64;                     // pieces per lane and tensor
+    static_assert(TP <= 64 || TP % 64 == 0, "tile pieces");
+    __shared__ __attribute__((aligned(16))) float sBC[2][2][PF][N];   // [buffer][B, C][token][n]
+    uint4 tq[NTEN][TV];
+    // with fewer pieces than lanes, lanes past them repeat a piece (same value to the same
+    // address): no lane is masked off, so no branch splits the token loop's block
+    auto fetch_tile = [&](int rt) {                        // rows rt .. rt + PF - 1
+#pragma unroll
+        for (int ten = 0; ten < NTEN; ++ten)
+#pragma unroll
+            for (int v = 0; v < TV; ++v) {
+                const int e = (lane + 64 * v) % TP, row = e / PPR, part = e % PPR;
+                const int o = ((rt + row) * G + g) * N * ES + part * 16;
+                tq[ten][v] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ten ? rc : rb, o, 0, 0));
+            }
+    };
+    auto stage_tile = [&](int buf) {
+#pragma unroll
+        for (int ten = 0; ten < NTEN; ++ten)
+#pragma unroll
+        for (int v = 0; v < TV; ++v) {
+            const int e = (lane + 64 * v) % TP, row = e / PPR, part = e % PPR;
+            const uint4 t = tq[ten][v];
+            {
+                float* dst = &sBC[buf][ten][row][part * (16 / ES)];
+                if constexpr (BF16) {
+                    reinterpret_cast<float4*>(dst)[0] = float4{bf16_lo(t.x), bf16_hi(t.x), bf16_lo(t.y), bf16_hi(t.y)};
+                    reinterpret_cast<float4*>(dst)[1] = float4{bf16_lo(t.z), bf16_hi(t.z), bf16_lo(t.w), bf16_hi(t.w)};
+                } else {
+                    *reinterpret_cast<uint4*>(dst) = t;
+                }
+            }
+        }
+    };
+
+    fetch_tile(0);                             // first in flight, so its wait below covers only it
+    uint32_t xq[PF], dq[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+        xq[j] = ld_x(j);
+        dq[j] = ld_dt(j);
+        // a dropped store (past the resource's end) per token, as the loop stores one per
+        // token: the loads and stores in flight at the loop's head are then the same on
+        // entry and on every later pass, and its waits stay PF tokens deep
+        if constexpr (kFull) __builtin_amdgcn_raw_buffer_store_b32(0u, ry, kPcsOob, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);     // in slot order, as the loop issues them
+    }
+    stage_tile(0);
+    fetch_tile(PF);                            // the next tile: in flight through the first group
+    for (int r0 = 0; r0 < (int)nrow; r0 += PF) {
+        const int buf = (r0 / PF) & 1;
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            const int r = r0 + j;
+            // take this token's x and dt out of the ring before the slot is reloaded, so that
+            // each slot keeps one register (a slot whose old and new values overlapped would
+            // be copied at the loop's end, and the copy would wait for the load)
+            uint32_t dcur, xcur;
+            asm("v_mov_b32 %0, %1" : "=v"(dcur) : "v"(dq[j]));
+            asm("v_mov_b32 %0, %1" : "=v"(xcur) : "v"(xq[j]));
+            __builtin_amdgcn_sched_barrier(0);
+            xq[j] = ld_x(r + PF);              // the ring: this slot's next token
+            dq[j] = ld_dt(r + PF);
+            float bn[N], cn[N];                // this token's rows (uniform LDS reads), issued
+#pragma unroll                                 // before the exponentials that cover them
+            for (int n4 = 0; n4 < N; n4 += 4) {
+                const float4 bv = *reinterpret_cast<const float4*>(&sBC[buf][0][j][n4]);
+                bn[n4] = bv.x; bn[n4 + 1] = bv.y; bn[n4 + 2] = bv.z; bn[n4 + 3] = bv.w;
+                if constexpr (kFull) {
+                    const float4 cv = *reinterpret_cast<const float4*>(&sBC[buf][1][j][n4]);
+                    cn[n4] = cv.x; cn[n4 + 1] = cv.y; cn[n4 + 2] = cv.z; cn[n4 + 3] = cv.w;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            const float st = __uint_as_float(dcur);
+            const float u = st * __uint_as_float(BF16 ? xcur << 16 : xcur);
+#pragma unroll
+            for (int n = 0; n < N; ++n) h[n] = __builtin_amdgcn_exp2f(st * a2[n]) * h[n] + u * bn[n];
+            if constexpr (kFull) {
+                float acc = cn[0] * h[0];
+#pragma unroll
+                for (int n = 1; n < N; ++n) acc += cn[n] * h[n];
+                if constexpr (BF16) {
+                    const bf16 yb = (bf16)acc;
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, yb), ry, lo + r * D * ES, 0, 0);
+                } else {
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), ry, lo + r * D * 4, 0, 0);
+                }
+            } else {
+                dsum += st;
+            }
+            // each token's loads and stores in order, so the waits stay one ring deep
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // the next tile (loaded through this group) into the other buffer, and the one after
+        // it on its way; one wave, in order: no barrier
+        stage_tile(buf ^ 1);
+        fetch_tile(r0 + 2 * PF);
+    }
+    if (!live) return;
+    if constexpr (kFull) {
+        if (T1 == L && a.h1)
+#pragma unroll
+            for (int n = 0; n < N; ++n) a.h1[((size_t)bi * D + d) * N + n] = h[n];
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) a.ws[chs * N + n] = h[n];
+        a.ws[2 * S * N + chs] = dsum;
     }
 }
 
@@ -340,17 +567,33 @@ __global__ __launch_bounds__(256) void pcs_carry_kernel(PcsArgs a) {
 }
 
 template <int N, bool BF16>
+hipError_t launch_pcs_stream(const PcsArgs& a, hipStream_t st) {
+    const int nblk = a.b * ((a.D + 63) / 64) * a.nseg;
+    hipError_t e;
+
+    if (a.nseg > 1) {
+        hipLaunchKernelGGL((pcs_stream_kernel<N, kPcsSummary, BF16>), dim3(nblk), dim3(64), 0, st, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const long items = (long)a.b * a.D * a.N;
+        hipLaunchKernelGGL(pcs_carry_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((pcs_stream_kernel<N, kPcsFull, BF16>), dim3(nblk), dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int N, bool BF16>
 hipError_t launch_pcs_n(const PcsArgs& a, hipStream_t st) {
     using LY = PcsLayout<N>;
     const int ntile = (a.D + LY::CW - 1) / LY::CW;
     const int nblk = a.b * ntile * a.nseg;
-    constexpr int kPcsThreads = LY::NT;
+    constexpr int kThreads = LY::NT;
     hipError_t e;
     if (a.nseg > 1) {
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pcs_kernel<N, kPcsSummary, BF16>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, LY::total);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((pcs_kernel<N, kPcsSummary, BF16>), dim3(nblk), dim3(kPcsThreads), LY::total, st, a);
+        hipLaunchKernelGGL((pcs_kernel<N, kPcsSummary, BF16>), dim3(nblk), dim3(kThreads), LY::total, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const long items = (long)a.b * a.D * a.N;
         hipLaunchKernelGGL(pcs_carry_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st, a);
@@ -359,15 +602,15 @@ hipError_t launch_pcs_n(const PcsArgs& a, hipStream_t st) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pcs_kernel<N, kPcsFull, BF16>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, LY::total);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((pcs_kernel<N, kPcsFull, BF16>), dim3(nblk), dim3(kPcsThreads), LY::total, st, a);
+    hipLaunchKernelGGL((pcs_kernel<N, kPcsFull, BF16>), dim3(nblk), dim3(kThreads), LY::total, st, a);
     return hipGetLastError();
 }
 
 template <bool BF16>
 hipError_t launch_pcs_t(const PcsArgs& a, hipStream_t st) {
     switch (a.N) {
-        case 8: return launch_pcs_n<8, BF16>(a, st);
-        case 16: return launch_pcs_n<16, BF16>(a, st);
+        case 8: return PCS_STREAM ? launch_pcs_stream<8, BF16>(a, st) : launch_pcs_n<8, BF16>(a, st);
+        case 16: return PCS_STREAM ? launch_pcs_stream<16, BF16>(a, st) : launch_pcs_n<16, BF16>(a, st);
         case 32: return launch_pcs_n<32, BF16>(a, st);
         case 64: return launch_pcs_n<64, BF16>(a, st);
         default: return hipErrorInvalidValue;
@@ -379,6 +622,16 @@ hipError_t launch_pcs_t(const PcsArgs& a, hipStream_t st) {
 bool pcs_supported_state(int N) { return N == 8 || N == 16 || N == 32 || N == 64; }
 
 int pcs_channels_per_group(int) { return kPcsCW; }
+
+int pcs_waves_per_group(int N) {
+    if (PCS_STREAM && N <= 16) return 1;
+    switch (N) {
+        case 8: return PcsLayout<8>::NT / 64;
+        case 16: return PcsLayout<16>::NT / 64;
+        case 32: return PcsLayout<32>::NT / 64;
+        default: return PcsLayout<64>::NT / 64;
+    }
+}
 
 int pcs_groups_per_cu(int N) {
     auto fit = [](int lds, int threads) { return std::max(1, std::min(163840 / lds, 2048 / threads)); };
@@ -392,11 +645,7 @@ int pcs_groups_per_cu(int N) {
 
 int pcs_block_tokens() { return kPcsTB; }
 
-size_t pcs_workspace_bytes(const PcsArgs& a) {
-    if (a.nseg <= 1) return 0;
-    const size_t S = (size_t)a.b * a.D * a.nseg;
-    return (2 * S * a.N + S) * sizeof(float);
-}
+size_t pcs_workspace_bytes(const PcsArgs& a) { return pcs_seg_floats(a) * sizeof(float); }
 
 hipError_t launch_pcs(const PcsArgs& a, hipStream_t st) {
     return a.io_bf16 ? launch_pcs_t<true>(a, st) : launch_pcs_t<false>(a, st);

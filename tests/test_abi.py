@@ -273,7 +273,7 @@ def test_pcs_entry_points_reject_bad_arguments(m3):
 def test_pcs_schedule_sizes(m3):
     """The library's segment choice: none when the (batch, channel tile)
     workgroups fill the chip, several for few long sequences; a forced count is
-    clamped to the number of 64-token blocks.  Workspace: two [b, D, nseg, N]
+    clamped to the number of 32-token blocks.  Workspace: two [b, D, nseg, N]
     fp32 state sets and one [b, D, nseg] step sum."""
     def ws(**kw):
         n = ctypes.c_size_t(0)
@@ -281,7 +281,14 @@ def test_pcs_schedule_sizes(m3):
         return n.value
     assert ws(batch=16, seqlen=2048, channels=4096) == 0
     b, D, N = 2, 2048, 16
-    nseg = 8           # 64 workgroups of 64 channels fill 512 slots (two per compute unit) in 8 segments
+    nseg = 16          # 64 workgroups of four waves: 16 segments give about four waves per SIMD
     assert ws(batch=b, seqlen=32768, channels=D) == (2 * b * D * nseg * N + b * D * nseg) * 4
-    assert ws(batch=1, seqlen=100, channels=64, nsegments=64) == (2 * 64 * 2 * 16 + 64 * 2) * 4   # 2 blocks
+    assert ws(batch=1, seqlen=100, channels=64, nsegments=64) == (2 * 64 * 4 * 16 + 64 * 4) * 4   # 4 blocks of 32
     assert ws(batch=1, seqlen=0, channels=64, nsegments=5) == 0
+    # a segment's rows must stay under 2 GiB: 2^20 tokens of 4096 channels need at least 9
+    n = ctypes.c_size_t(0)
+    assert m3.lib.m3_pcs_workspace_size(ctypes.byref(_pcs_desc(m3, batch=1, seqlen=1 << 20, channels=4096,
+                                                                nsegments=1)), ctypes.byref(n)) == 0
+    assert n.value == (2 * 4096 * 9 * 16 + 4096 * 9) * 4
+    assert m3.lib.m3_pcs_workspace_size(ctypes.byref(_pcs_desc(m3, batch=1, seqlen=1 << 23, channels=4096)),
+                                        ctypes.byref(n)) == 2     # would need more than 64 segments

@@ -93,15 +93,17 @@ def _run_and_compare(m3, inp, io, nsegments=0, label=""):
 
 SMALL = [
     # (batch, L, D, G, N, io, init, nseg)
-    (2, 200, 200, 1, 16, "bf16", False, 0),      # ragged tokens (3 blocks + 8) and channels (3 tiles + 8)
+    (2, 200, 200, 1, 16, "bf16", False, 0),      # ragged tokens (6 blocks + 8) and channels (3 tiles + 8)
     (1, 64, 64, 1, 8, "bf16", True, 0),          # one block, one tile
     (2, 130, 256, 2, 32, "bf16", True, 0),       # two groups of 128 channels
     (1, 77, 128, 1, 64, "bf16", True, 0),
     (2, 150, 100, 1, 16, "f32", True, 0),        # f32 I/O, ragged channels (100 = 64 + 36)
     (1, 65, 256, 4, 8, "f32", False, 0),         # four groups of 64 channels
     (1, 1, 64, 1, 16, "bf16", True, 0),          # a single token
-    (2, 1000, 128, 1, 16, "bf16", True, 5),      # segmented: 5 segments of 256 tokens (last one ragged)
-    (1, 640, 64, 1, 32, "f32", True, 64),        # 64 requested, clamped to 10 one-block segments
+    (2, 1000, 128, 1, 16, "bf16", True, 5),      # segmented: 5 segments of 224 tokens (last one ragged)
+    (1, 640, 64, 1, 32, "f32", True, 64),        # 64 requested, clamped to 20 one-block segments
+    (1, 3000, 64, 1, 64, "bf16", True, 64),      # 64 requested: 47 segments of 64 tokens
+    (1, 96, 128, 2, 8, "bf16", True, 3),         # three one-block segments, two groups
 ]
 
 
