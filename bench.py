@@ -35,8 +35,8 @@ PEAK_FP32_VALU_TFLOPS = 157.3 # MI355X fp32 vector: 256 CUs x 4 SIMDs x 2.4 GHz 
 CSRC = os.path.join(ROOT, "selective_state_space_mimo_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 # sources that define each measured kernel (the counters stand only while these are unchanged)
-KERNEL_SOURCES = {"scan": ("scan_mfma.hip", "m3_internal.h"), "decode": ("decode.hip", "m3_internal.h"),
-                  "bwd": ("bwd.hip", "m3_internal.h")}
+KERNEL_SOURCES = {"scan": ("scan_mfma.hip", "scan_common.h", "m3_internal.h"), "decode": ("decode.hip", "m3_internal.h"),
+                  "bwd": ("bwd.hip", "m3_internal.h"), "pcs": ("pcs.hip", "m3_internal.h")}
 
 
 def source_sha(kind):
@@ -247,12 +247,14 @@ def run_scan(torch, m3, cfg, steps, warmup):
 
 # The per-coordinate scan (Mamba 1 preset).  Its work per coordinate-step (one
 # channel, one token, one of the N state coordinates) is one exponential and four
-# other VALU operations (the exponent dt a, the write dt x B, the decay FMA, the
-# readout FMA); with the exponential at quarter rate a coordinate-step occupies 8
-# lane-cycles of a SIMD's 16, so the chip's ceiling is 256 CUs x 4 SIMDs x 16 lanes
-# x 2.4 GHz / 8 = 4915 G coordinate-steps/s.  HBM bytes per (channel, token): x and
-# y in the I/O dtype, dt f32; B and C per (group, token); the states once per stream.
-PCS_STEP_PEAK_G = 256 * 4 * 16 * 2.4 / 8
+# other fp32 VALU operations (the exponent dt a, the write dt x B, the decay
+# multiply-add, the readout multiply-add).  A SIMD retires 32 fp32 lanes per cycle
+# (the 157.3 TFLOP/s vector peak: 256 CUs x 4 SIMDs x 2.4 GHz x 32 lanes x 2 flop)
+# and transcendentals at a quarter of that, 8 lanes per cycle, so a step costs
+# 4 / 32 + 1 / 8 = 1 / 4 lane-cycle: the chip's ceiling is 256 x 4 x 2.4 GHz x 4 =
+# 9830 G coordinate-steps/s.  HBM bytes per (channel, token): x and y in the I/O
+# dtype, dt f32; B and C per (group, token); the states once per stream.
+PCS_STEP_PEAK_G = 256 * 4 * 2.4 * 4
 PCS_FLOP_PER_STEP = 6          # 2 products + 2 FMAs (the exponential counted apart)
 
 
@@ -603,7 +605,7 @@ def main():
     line = {
         "metric": "scan tokens/s (% MFMA peak) + decode state GB/s (% HBM peak), 1xMI355X",
         "value": prim.get("tokens_per_s", prim.get("gbs")),
-        "unit": "tokens/s" if main_w.startswith("scan") else "GB/s",
+        "unit": "tokens/s" if main_w.startswith(("scan", "pcs")) else "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": prim.get("ms_per_call", prim.get("ms_per_step")),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -666,7 +668,8 @@ def main():
         pw = pcs.get("pcs", next(iter(pcs.values())))
         line["roofline_pcs"] = {"bound": "alu", "achieved": pw["gsteps_per_s"], "peak": PCS_STEP_PEAK_G,
                                 "unit": "Gstep/s", "frac": pw["alu_frac"], "workload": pw["workload"],
-                                "traffic": None, "algorithmic_bytes": pw["bytes_per_call"],
+                                "traffic": measured_traffic("pcs", pw["workload"]),
+                                "algorithmic_bytes": pw["bytes_per_call"],
                                 "coordinate_steps": pw["coordinate_steps_per_call"],
                                 "hbm_achieved_gbs": pw["algo_gbs"], "hbm_frac": pw["hbm_frac"]}
         if not args.no_cpu:

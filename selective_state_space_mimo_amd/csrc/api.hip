@@ -652,8 +652,10 @@ void pcs_segments(const m3_pcs_desc* d, int* nseg, int* seglen) {
     int k = d->nsegments;
     if (k == 0) {
         const int cw = pcs_channels_per_group(d->dstate);
-        const long long waves = (long long)d->batch * ((d->channels + cw - 1) / cw) * pcs_waves_per_group(d->dstate);
-        k = waves >= 1024 ? 1 : (int)std::min<long long>(64, (4096 + waves - 1) / waves);
+        const long long tiles = (long long)d->batch * ((d->channels + cw - 1) / cw);
+        const long long waves = tiles * pcs_waves_per_group(d->dstate, false);
+        const long long seg_waves = tiles * pcs_waves_per_group(d->dstate, true);   // per segment
+        k = waves >= 1024 ? 1 : (int)std::min<long long>(64, (4096 + seg_waves - 1) / seg_waves);
     }
     const long long max_rows = pcs_max_segment_rows(d);
     k = std::max<long long>(k, (d->seqlen + max_rows - 1) / max_rows);

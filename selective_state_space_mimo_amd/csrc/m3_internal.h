@@ -130,7 +130,7 @@ struct PcsArgs {
 bool pcs_supported_state(int N);
 int pcs_channels_per_group(int N);   // channels per workgroup
 int pcs_groups_per_cu(int N);        // workgroups one compute unit holds at once
-int pcs_waves_per_group(int N);
+int pcs_waves_per_group(int N, bool segmented);
 int pcs_block_tokens();              // tokens per block (segments are whole blocks)
 size_t pcs_workspace_bytes(const PcsArgs& a);
 hipError_t launch_pcs(const PcsArgs& a, hipStream_t s);

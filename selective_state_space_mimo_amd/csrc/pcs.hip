@@ -348,24 +348,33 @@ __global__ __launch_bounds__(PcsLayout<N>::NT) void pcs_kernel(PcsArgs a) {
     }
 }
 
-// ---- streaming form, N <= 16 ------------------------------------------------------
-// One wave per workgroup; lane c owns channel d0 + c with all N coordinates, so the
-// readout is a sum inside the lane.  Per token a wave reads one 64-channel row piece of
-// x (128 bytes in bf16) and of dt and writes one of y, each a whole cache line; those
-// accesses run PF tokens ahead of the math through a ring of registers.  B and C rows are
-// the same for every lane of the wave: they come in tiles of PF tokens (one vector load
-// per lane, a tile ahead, in the same ring as x and dt), are widened to fp32 into one of
-// two LDS tiles, and each token's rows are read from there as uniform (broadcast) LDS
-// reads.  LDS reads complete in order, so their waits stay exact.  (Scalar loads would
-// deliver the rows as scalar operands, but they complete out of order: each wait for one
-// drains all of them, which defeats any prefetch.)  One wave per workgroup: no barrier.
+// ---- streaming form, N = 16 -------------------------------------------------------
+// A workgroup of NW waves owns 64 channels: lane c of every wave holds channel d0 + c,
+// wave w the coordinates w N / NW .. (w + 1) N / NW - 1.  Two waves when the channels
+// alone set the parallelism (a lone wave issues a vector instruction only every fourth
+// cycle or so; two interleave on the SIMD), one when sequence segments already give
+// every SIMD several waves (no exchange, no duplicated x and dt reads).  Per token a
+// wave reads one 64-channel row piece of x (128 bytes in bf16) and of dt, whole cache
+// lines, PF tokens ahead of the math through a ring of registers.  B and C come in tiles
+// of PF tokens (one vector load per lane, a tile ahead, in the same ring), each wave
+// widening its own half of the coordinates to fp32 into one of two LDS tiles, from which
+// each token's row is a uniform (broadcast) read.  LDS reads complete in order, so their
+// waits stay exact.  (Scalar loads would deliver the rows as scalar operands, but they
+// complete out of order: each wait for one drains all of them, defeating any prefetch.)
+// Each wave keeps its (partial) readouts of a group of PF tokens; at the group's end two
+// waves swap halves through LDS (one barrier) and each completes and stores half the
+// group's outputs; a lone wave stores them all.
 constexpr int kPcsPF = 16;                 // tokens in flight (the ring), and tokens per B, C tile
+constexpr int kPcsHalf = kPcsPF / 2;
 
-template <int N, int MODE, bool BF16>
-__global__ __launch_bounds__(64) void pcs_stream_kernel(PcsArgs a) {
+template <int N, int NW, int MODE, bool BF16>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) void pcs_stream_kernel(PcsArgs a) {
+    static_assert(NW == 1 || NW == 2, "one or two waves");
     constexpr bool kFull = MODE == kPcsFull;
-    constexpr int ES = BF16 ? 2 : 4, PF = kPcsPF;
-    const int lane = threadIdx.x;
+    constexpr int ES = BF16 ? 2 : 4, PF = kPcsPF, HF = kPcsHalf;
+    constexpr int K = N / NW;                              // coordinates per lane
+    const int lane = threadIdx.x & 63;
+    const int w = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int D = a.D, L = a.L, G = a.G, nseg = a.nseg;
     const int ntile = (D + 63) / 64;
     int bid = blockIdx.x;
@@ -376,22 +385,25 @@ __global__ __launch_bounds__(64) void pcs_stream_kernel(PcsArgs a) {
     const int g = d0 * G / D;                  // the tile's channels share one group (checked on the host)
     const int T0 = seg * a.seglen, T1 = min(L, T0 + a.seglen);
     const bool live = d < D;
+    const int n0 = w * K;                      // this wave's first coordinate
 
-    float a2[N], h[N];
+    float a2[K], h[K];
     const size_t S = (size_t)a.b * D * nseg;
     const size_t chs = ((size_t)bi * D + (live ? d : 0)) * nseg + seg;
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-        a2[n] = live ? -expf(a.A_log[(size_t)d * N + n]) * kPcsLog2e : 0.f;
+    for (int m = 0; m < K; ++m) {
+        a2[m] = live ? -expf(a.A_log[(size_t)d * N + n0 + m]) * kPcsLog2e : 0.f;
         float v = 0.f;
         if (kFull && live) {
-            if (seg == 0) v = a.h0 ? a.h0[((size_t)bi * D + d) * N + n] : 0.f;
-            else v = a.ws[S * N + chs * N + n];
+            if (seg == 0) v = a.h0 ? a.h0[((size_t)bi * D + d) * N + n0 + m] : 0.f;
+            else v = a.ws[S * N + chs * N + n0 + m];
         }
-        h[n] = v;
+        h[m] = v;
     }
     float dsum = 0.f;
-    __builtin_amdgcn_s_waitcnt(0x0f70);                    // vmcnt(0): see the tiled kernel
+    // The state and rate loads land before the loop: otherwise the wait for them, merged
+    // over the loop, would also wait for the ring's loads.
+    __builtin_amdgcn_s_waitcnt(0x0f70);                    // vmcnt(0)
 
     // resources over the segment's rows (the host keeps each under 2 GiB); rows at or past
     // T1 read zero (dt = 0 leaves the state unchanged) and their outputs are dropped
@@ -408,61 +420,63 @@ __global__ __launch_bounds__(64) void pcs_stream_kernel(PcsArgs a) {
         else return __builtin_amdgcn_raw_buffer_load_b32(rx, lo + r * D * 4, 0, 0);
     };
     auto ld_dt = [&](int r) -> uint32_t { return __builtin_amdgcn_raw_buffer_load_b32(rd, lod + r * D * 4, 0, 0); };
-    // B, C tiles: PF rows of N values of the wave's group; 16-byte pieces, lanes over (B, C)
+
+    // B, C tiles: PF rows of this wave's K values; 16-byte pieces
     const auto rb = pcs_rsrc(static_cast<const uint8_t*>(a.B) + row0 * G * N * ES, nrow * (uint32_t)(G * N * ES));
     const auto rc = pcs_rsrc(static_cast<const uint8_t*>(a.C) + row0 * G * N * ES, nrow * (uint32_t)(G * N * ES));
-    constexpr int PPR = N * ES / 16;                       // pieces per row
-    constexpr int TP = PF * PPR;                           // pieces per tile
+    constexpr int PPR = K * ES / 16;                       // pieces per row
+    static_assert(PPR >= 1, "a wave's half row is at least 16 bytes");
+    constexpr int TP = PF * PPR;                           // pieces per tile (<= 64)
     constexpr int NTEN = kFull ? 2 : 1;                    // B, and C when the readout is made
-    constexpr int TV = (TP + 63) / 64;                     // pieces per lane and tensor
-    static_assert(TP <= 64 || TP % 64 == 0, "tile pieces");
-    __shared__ __attribute__((aligned(16))) float sBC[2][2][PF][N];   // [buffer][B, C][token][n]
-    uint4 tq[NTEN][TV];
+    static_assert(TP <= 64, "tile pieces");
+    __shared__ __attribute__((aligned(16))) float sBC[NW][2][2][PF][K];  // [wave][buffer][B, C][token][m]
+    __shared__ __attribute__((aligned(16))) float sY[NW == 2 ? 2 : 1][2][64][HF];   // [buffer][from wave][lane][token]
+    uint4 tq[NTEN];
     // with fewer pieces than lanes, lanes past them repeat a piece (same value to the same
     // address): no lane is masked off, so no branch splits the token loop's block
     auto fetch_tile = [&](int rt) {                        // rows rt .. rt + PF - 1
+        const int e = lane % TP, row = e / PPR, part = e % PPR;
+        const int o = ((rt + row) * G + g) * N * ES + n0 * ES + part * 16;
 #pragma unroll
         for (int ten = 0; ten < NTEN; ++ten)
-#pragma unroll
-            for (int v = 0; v < TV; ++v) {
-                const int e = (lane + 64 * v) % TP, row = e / PPR, part = e % PPR;
-                const int o = ((rt + row) * G + g) * N * ES + part * 16;
-                tq[ten][v] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ten ? rc : rb, o, 0, 0));
-            }
+            tq[ten] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ten ? rc : rb, o, 0, 0));
     };
     auto stage_tile = [&](int buf) {
+        const int e = lane % TP, row = e / PPR, part = e % PPR;
 #pragma unroll
-        for (int ten = 0; ten < NTEN; ++ten)
-#pragma unroll
-        for (int v = 0; v < TV; ++v) {
-            const int e = (lane + 64 * v) % TP, row = e / PPR, part = e % PPR;
-            const uint4 t = tq[ten][v];
-            {
-                float* dst = &sBC[buf][ten][row][part * (16 / ES)];
-                if constexpr (BF16) {
-                    reinterpret_cast<float4*>(dst)[0] = float4{bf16_lo(t.x), bf16_hi(t.x), bf16_lo(t.y), bf16_hi(t.y)};
-                    reinterpret_cast<float4*>(dst)[1] = float4{bf16_lo(t.z), bf16_hi(t.z), bf16_lo(t.w), bf16_hi(t.w)};
-                } else {
-                    *reinterpret_cast<uint4*>(dst) = t;
-                }
+        for (int ten = 0; ten < NTEN; ++ten) {
+            const uint4 t = tq[ten];
+            float* dst = &sBC[w][buf][ten][row][part * (16 / ES)];
+            if constexpr (BF16) {
+                reinterpret_cast<float4*>(dst)[0] = float4{bf16_lo(t.x), bf16_hi(t.x), bf16_lo(t.y), bf16_hi(t.y)};
+                reinterpret_cast<float4*>(dst)[1] = float4{bf16_lo(t.z), bf16_hi(t.z), bf16_lo(t.w), bf16_hi(t.w)};
+            } else {
+                *reinterpret_cast<uint4*>(dst) = t;
             }
         }
     };
 
-    fetch_tile(0);                             // first in flight, so its wait below covers only it
+    // Prologue, in the order the loop issues the same kinds of operations, so that what is
+    // in flight at the loop's head is the same on entry and on every later pass and the
+    // compiler's waits stay a ring deep: the first tile, the ring, a group's worth of
+    // dropped stores (past the resource's end), the second tile.
+    fetch_tile(0);
     uint32_t xq[PF], dq[PF];
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
         xq[j] = ld_x(j);
         dq[j] = ld_dt(j);
-        // a dropped store (past the resource's end) per token, as the loop stores one per
-        // token: the loads and stores in flight at the loop's head are then the same on
-        // entry and on every later pass, and its waits stay PF tokens deep
-        if constexpr (kFull) __builtin_amdgcn_raw_buffer_store_b32(0u, ry, kPcsOob, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);     // in slot order, as the loop issues them
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (kFull) {
+#pragma unroll
+        for (int j = 0; j < PF / NW; ++j) __builtin_amdgcn_raw_buffer_store_b16((unsigned short)0, ry, kPcsOob, 0, 0);
     }
     stage_tile(0);
-    fetch_tile(PF);                            // the next tile: in flight through the first group
+    fetch_tile(PF);
+
+    float bn[K], cn[K];
+    float yp[PF];                              // this wave's partial readouts of the group
     for (int r0 = 0; r0 < (int)nrow; r0 += PF) {
         const int buf = (r0 / PF) & 1;
 #pragma unroll
@@ -477,39 +491,63 @@ __global__ __launch_bounds__(64) void pcs_stream_kernel(PcsArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             xq[j] = ld_x(r + PF);              // the ring: this slot's next token
             dq[j] = ld_dt(r + PF);
-            float bn[N], cn[N];                // this token's rows (uniform LDS reads), issued
-#pragma unroll                                 // before the exponentials that cover them
-            for (int n4 = 0; n4 < N; n4 += 4) {
-                const float4 bv = *reinterpret_cast<const float4*>(&sBC[buf][0][j][n4]);
-                bn[n4] = bv.x; bn[n4 + 1] = bv.y; bn[n4 + 2] = bv.z; bn[n4 + 3] = bv.w;
+#pragma unroll                                 // this token's rows, before the exponentials
+            for (int m4 = 0; m4 < K; m4 += 4) {
+                const float4 bv = *reinterpret_cast<const float4*>(&sBC[w][buf][0][j][m4]);
+                bn[m4] = bv.x; bn[m4 + 1] = bv.y; bn[m4 + 2] = bv.z; bn[m4 + 3] = bv.w;
                 if constexpr (kFull) {
-                    const float4 cv = *reinterpret_cast<const float4*>(&sBC[buf][1][j][n4]);
-                    cn[n4] = cv.x; cn[n4 + 1] = cv.y; cn[n4 + 2] = cv.z; cn[n4 + 3] = cv.w;
+                    const float4 cv = *reinterpret_cast<const float4*>(&sBC[w][buf][1][j][m4]);
+                    cn[m4] = cv.x; cn[m4 + 1] = cv.y; cn[m4 + 2] = cv.z; cn[m4 + 3] = cv.w;
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
             const float st = __uint_as_float(dcur);
             const float u = st * __uint_as_float(BF16 ? xcur << 16 : xcur);
 #pragma unroll
-            for (int n = 0; n < N; ++n) h[n] = __builtin_amdgcn_exp2f(st * a2[n]) * h[n] + u * bn[n];
+            for (int m = 0; m < K; ++m) h[m] = __builtin_amdgcn_exp2f(st * a2[m]) * h[m] + u * bn[m];
             if constexpr (kFull) {
-                float acc = cn[0] * h[0];
+                float p[4] = {cn[0] * h[0], cn[1] * h[1], cn[2] * h[2], cn[3] * h[3]};   // short chains
 #pragma unroll
-                for (int n = 1; n < N; ++n) acc += cn[n] * h[n];
-                if constexpr (BF16) {
-                    const bf16 yb = (bf16)acc;
-                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, yb), ry, lo + r * D * ES, 0, 0);
-                } else {
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), ry, lo + r * D * 4, 0, 0);
-                }
+                for (int m = 4; m < K; ++m) p[m & 3] += cn[m] * h[m];
+                yp[j] = (p[0] + p[1]) + (p[2] + p[3]);
             } else {
                 dsum += st;
             }
-            // each token's loads and stores in order, so the waits stay one ring deep
             __builtin_amdgcn_sched_barrier(0);
         }
+        auto store_y = [&](int j, float acc) {
+            const int r = r0 + j;
+            if constexpr (BF16) {
+                const bf16 yb = (bf16)acc;
+                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, yb), ry, lo + r * D * ES, 0, 0);
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), ry, lo + r * D * 4, 0, 0);
+            }
+        };
+        if constexpr (kFull && NW == 1) {
+#pragma unroll
+            for (int j = 0; j < PF; ++j) store_y(j, yp[j]);
+        } else if constexpr (kFull) {
+            // swap halves: this wave gives the other its partials of the other's half of
+            // the group's tokens (wave 0 completes tokens 0 .. HF - 1, wave 1 the rest)
+            const int give = (1 - w) * HF;
+            float4* dst = reinterpret_cast<float4*>(&sY[buf][w][lane][0]);
+#pragma unroll
+            for (int i = 0; i < HF; i += 4)
+                dst[i / 4] = float4{yp[give + i], yp[give + i + 1], yp[give + i + 2], yp[give + i + 3]};
+            __syncthreads();
+            const int keep = w * HF;
+            const float4* src = reinterpret_cast<const float4*>(&sY[buf][1 - w][lane][0]);
+#pragma unroll
+            for (int i = 0; i < HF; i += 4) {
+                const float4 o = src[i / 4];
+                const float v[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) store_y(keep + i + k, yp[keep + i + k] + v[k]);
+            }
+        }
         // the next tile (loaded through this group) into the other buffer, and the one after
-        // it on its way; one wave, in order: no barrier
+        // it on its way; each wave stages only the rows it reads: no barrier
         stage_tile(buf ^ 1);
         fetch_tile(r0 + 2 * PF);
     }
@@ -517,11 +555,11 @@ __global__ __launch_bounds__(64) void pcs_stream_kernel(PcsArgs a) {
     if constexpr (kFull) {
         if (T1 == L && a.h1)
 #pragma unroll
-            for (int n = 0; n < N; ++n) a.h1[((size_t)bi * D + d) * N + n] = h[n];
+            for (int m = 0; m < K; ++m) a.h1[((size_t)bi * D + d) * N + n0 + m] = h[m];
     } else {
 #pragma unroll
-        for (int n = 0; n < N; ++n) a.ws[chs * N + n] = h[n];
-        a.ws[2 * S * N + chs] = dsum;
+        for (int m = 0; m < K; ++m) a.ws[chs * N + n0 + m] = h[m];
+        if (w == 0) a.ws[2 * S * N + chs] = dsum;
     }
 }
 
@@ -570,15 +608,17 @@ template <int N, bool BF16>
 hipError_t launch_pcs_stream(const PcsArgs& a, hipStream_t st) {
     const int nblk = a.b * ((a.D + 63) / 64) * a.nseg;
     hipError_t e;
-
     if (a.nseg > 1) {
-        hipLaunchKernelGGL((pcs_stream_kernel<N, kPcsSummary, BF16>), dim3(nblk), dim3(64), 0, st, a);
+        // segments give the parallelism: one wave per 64 channels
+        hipLaunchKernelGGL((pcs_stream_kernel<N, 1, kPcsSummary, BF16>), dim3(nblk), dim3(64), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const long items = (long)a.b * a.D * a.N;
         hipLaunchKernelGGL(pcs_carry_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((pcs_stream_kernel<N, 1, kPcsFull, BF16>), dim3(nblk), dim3(64), 0, st, a);
+    } else {
+        hipLaunchKernelGGL((pcs_stream_kernel<N, 2, kPcsFull, BF16>), dim3(nblk), dim3(128), 0, st, a);
     }
-    hipLaunchKernelGGL((pcs_stream_kernel<N, kPcsFull, BF16>), dim3(nblk), dim3(64), 0, st, a);
     return hipGetLastError();
 }
 
@@ -609,7 +649,7 @@ hipError_t launch_pcs_n(const PcsArgs& a, hipStream_t st) {
 template <bool BF16>
 hipError_t launch_pcs_t(const PcsArgs& a, hipStream_t st) {
     switch (a.N) {
-        case 8: return PCS_STREAM ? launch_pcs_stream<8, BF16>(a, st) : launch_pcs_n<8, BF16>(a, st);
+        case 8: return launch_pcs_n<8, BF16>(a, st);
         case 16: return PCS_STREAM ? launch_pcs_stream<16, BF16>(a, st) : launch_pcs_n<16, BF16>(a, st);
         case 32: return launch_pcs_n<32, BF16>(a, st);
         case 64: return launch_pcs_n<64, BF16>(a, st);
@@ -623,8 +663,8 @@ bool pcs_supported_state(int N) { return N == 8 || N == 16 || N == 32 || N == 64
 
 int pcs_channels_per_group(int) { return kPcsCW; }
 
-int pcs_waves_per_group(int N) {
-    if (PCS_STREAM && N <= 16) return 1;
+int pcs_waves_per_group(int N, bool segmented) {
+    if (PCS_STREAM && N == 16) return segmented ? 1 : 2;   // waves per 64 channels
     switch (N) {
         case 8: return PcsLayout<8>::NT / 64;
         case 16: return PcsLayout<16>::NT / 64;

@@ -281,7 +281,7 @@ def test_pcs_schedule_sizes(m3):
         return n.value
     assert ws(batch=16, seqlen=2048, channels=4096) == 0
     b, D, N = 2, 2048, 16
-    nseg = 16          # 64 workgroups of four waves: 16 segments give about four waves per SIMD
+    nseg = 64          # 64 tiles of 64 channels, one wave each when segmented: 64 segments, four waves per SIMD
     assert ws(batch=b, seqlen=32768, channels=D) == (2 * b * D * nseg * N + b * D * nseg) * 4
     assert ws(batch=1, seqlen=100, channels=64, nsegments=64) == (2 * 64 * 4 * 16 + 64 * 4) * 4   # 4 blocks of 32
     assert ws(batch=1, seqlen=0, channels=64, nsegments=5) == 0
