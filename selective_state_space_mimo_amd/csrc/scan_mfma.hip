@@ -1052,23 +1052,57 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
     }
 }
 
-// Pass 2 of the segmented schedule: the affine carry recurrence over segments.
-// Thread = one (p, n-pair) of one stream; loops over the segments in order.
+// Pass 2 of the segmented schedule: the affine carry recurrence over segments,
 //   Hin[0]   = h0 + d_0 X_prev0^T Bt_prev0                (folded initial carry)
-//   Hin[k+1] = exp(Lam_k) Hin[k] + rot(Hloc_k, Phi_k),    Phi_{k+1} = Phi_k + dphi_k
-__global__ __launch_bounds__(256) void carry_pass_kernel(ScanArgs a) {
-    const int bh = blockIdx.y;
-    const int e = blockIdx.x * blockDim.x + threadIdx.x;     // pair element index in [0, P*N/2)
-    if (e >= kP * kN / 2) return;
+//   Hin[k+1] = exp(Lam_k) Hin[k] + rot(Hloc_k, Phi_k),    Phi_{k+1} = Phi_k + dphi_k,
+// as wave-level prefix scans ("Diagonal Equivalence in State Space Models ...", section 2.5:
+// the recurrence is an associative scan of (decay, write) pairs).  A group of W lanes (W a
+// power of two, at least the number of segments up to 64) owns one (p, n-pair) element of
+// one stream, lane k its segment k: an inclusive Kogge-Stone sum of the angle steps gives
+// each segment's Phi, the rotated local states become the writes, and an inclusive
+// Kogge-Stone composition of the affine maps (a lane combines with the lane o below it,
+// o = 1, 2, 4, ...) gives every segment's incoming state at once.  More than 64 segments
+// run as blocks of 64, each block's composition applied to the state carried out of the
+// one before.
+template <int W>
+__device__ __forceinline__ void seg_sum_scan(float& v, int k) {       // inclusive sum, angles mod 2 pi
+#pragma unroll
+    for (int o = 1; o < W; o <<= 1) {
+        const float u = __shfl_up(v, o, W);
+        if (k >= o) v = wrap_2pi(v + u);
+    }
+}
+template <int W>
+__device__ __forceinline__ void seg_affine_scan(float& A, float& B0, float& B1, int k) {
+#pragma unroll
+    for (int o = 1; o < W; o <<= 1) {
+        const float Au = __shfl_up(A, o, W), B0u = __shfl_up(B0, o, W), B1u = __shfl_up(B1, o, W);
+        if (k >= o) {                          // (earlier maps first): x -> A (Au x + Bu) + B
+            B0 = A * B0u + B0;
+            B1 = A * B1u + B1;
+            A = A * Au;
+        }
+    }
+}
+
+template <int W>
+__global__ __launch_bounds__(256) void carry_scan_kernel(ScanArgs a) {
+    constexpr int GPW = 64 / W;                                  // elements per wave
+    const int lane = threadIdx.x & 63, k_in = lane % W, grp = lane / W;
+    const long elem = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * GPW + grp;   // (stream, pair element)
+    constexpr int EPS = kP * kN / 2;                             // pair elements per stream
+    if (elem >= (long)a.b * a.H * EPS) return;                   // whole groups leave together
+    const int bh = (int)(elem / EPS), e = (int)(elem % EPS);
     const int p = e / (kN / 2), ip = e % (kN / 2), n = 2 * ip;
     const int nseg = a.nseg, np = a.np, H = a.H, L = a.L;
     const int bi = bh / H;
     const size_t S = (size_t)a.b * H * nseg;
-    float* wsHloc = a.ws;
+    const float* wsHloc = a.ws;
     float* wsHin = a.ws + S * kP * kN;
-    float* wsLam = a.ws + 2 * S * kP * kN;
-    float* wsDphi = wsLam + S;
-    float* wsPhi = wsDphi + S * np;
+    const float* wsLam = a.ws + 2 * S * kP * kN;
+    const float* wsDphi = wsLam + S;
+    float* wsPhi = a.ws + 2 * S * kP * kN + S + S * np;
+    // the folded initial carry of this element (each lane of the group computes it)
     float h0 = 0.f, h1 = 0.f;
     if (a.h0) {
         const size_t o = ((size_t)bh * kP + p) * kN + n;
@@ -1077,7 +1111,7 @@ __global__ __launch_bounds__(256) void carry_pass_kernel(ScanArgs a) {
     }
     if (a.Bp0 && a.xp0) {
         const size_t t0 = (size_t)bi * L * H + (bh % H);
-        const bool raw = a.lift != nullptr;                 // the layer's raw projections
+        const bool raw = a.lift != nullptr;                      // the layer's raw projections
         const float dt0 = raw ? softplus_f(a.dt[t0] + (a.dt_bias ? a.dt_bias[bh % H] : 0.f)) : a.dt[t0];
         const float d0 = dt0 * (1.f - (raw ? sigmoid_f(a.lam[t0]) : a.lam[t0]));
         for (int r = 0; r < a.R; ++r) {
@@ -1086,25 +1120,49 @@ __global__ __launch_bounds__(256) void carry_pass_kernel(ScanArgs a) {
             h1 += xv * ld_io(a.Bp0, ((size_t)bh * a.R + r) * kN + n + 1, 1);
         }
     }
-    float phi = (ip < np && a.phi0) ? a.phi0[(size_t)bh * np + ip] : 0.f;
-    for (int k = 0; k < nseg; ++k) {
-        const size_t ss = (size_t)bh * nseg + k;
-        const size_t o = (ss * kP + p) * kN + n;
-        wsHin[o] = h0;
-        wsHin[o + 1] = h1;
-        if (ip < np && p == 0) wsPhi[ss * np + ip] = phi;
-        const float dec = expf(wsLam[ss]);
-        float u0 = wsHloc[o], u1 = wsHloc[o + 1];
-        if (ip < np) {
-            float sn, cs;
-            sincosf(phi, &sn, &cs);
-            const float t0 = u0 * cs - u1 * sn;
-            u1 = u0 * sn + u1 * cs;
-            u0 = t0;
-            phi = wrap_2pi(phi + wsDphi[ss * np + ip]);
+    const bool turns = ip < np;
+    float phi_in = (turns && a.phi0) ? a.phi0[(size_t)bh * np + ip] : 0.f;    // angle entering the block
+    for (int k0 = 0; k0 < nseg; k0 += W) {
+        const int k = k0 + k_in;
+        const bool valid = k < nseg;
+        const size_t ss = (size_t)bh * nseg + (valid ? k : 0);
+        // segment k's angle: the carried angle plus the steps of the block's earlier segments
+        float dphi = (valid && turns) ? wsDphi[ss * np + ip] : 0.f;
+        seg_sum_scan<W>(dphi, k_in);                             // inclusive
+        float before = __shfl_up(dphi, 1, W);
+        if (k_in == 0) before = 0.f;
+        const float phi = wrap_2pi(phi_in + before);
+        // segment k's map: x -> exp(Lam_k) x + rot(Hloc_k, Phi_k)  (identity past the last segment)
+        float A = 1.f, B0 = 0.f, B1 = 0.f;
+        if (valid) {
+            const size_t o = (ss * kP + p) * kN + n;
+            A = expf(wsLam[ss]);
+            B0 = wsHloc[o];
+            B1 = wsHloc[o + 1];
+            if (turns) {
+                float sn, cs;
+                sincosf(phi, &sn, &cs);
+                const float t0 = B0 * cs - B1 * sn;
+                B1 = B0 * sn + B1 * cs;
+                B0 = t0;
+            }
         }
-        h0 = dec * h0 + u0;
-        h1 = dec * h1 + u1;
+        seg_affine_scan<W>(A, B0, B1, k_in);                     // lane k: segments k0 .. k composed
+        // incoming state of segment k: segments k0 .. k - 1 applied to the carried state
+        float Ae = __shfl_up(A, 1, W), E0 = __shfl_up(B0, 1, W), E1 = __shfl_up(B1, 1, W);
+        if (k_in == 0) { Ae = 1.f; E0 = 0.f; E1 = 0.f; }
+        if (valid) {
+            const size_t o = (ss * kP + p) * kN + n;
+            wsHin[o] = Ae * h0 + E0;
+            wsHin[o + 1] = Ae * h1 + E1;
+            if (turns && p == 0) wsPhi[ss * np + ip] = phi;
+        }
+        // the state and angle carried out of the block: its last lane's composition
+        const int last = (lane / W) * W + W - 1;
+        const float c0 = A * h0 + B0, c1 = A * h1 + B1;
+        h0 = __shfl(c0, last);
+        h1 = __shfl(c1, last);
+        phi_in = wrap_2pi(phi_in + __shfl(dphi, last));
     }
 }
 
@@ -1141,8 +1199,19 @@ hipError_t launch_rq(const ScanArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_carry_pass(const ScanArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL(carry_pass_kernel, dim3((kP * kN / 2 + 255) / 256, a.b * a.H), dim3(256), 0, st, a);
-    return hipGetLastError();
+    const long elems = (long)a.b * a.H * (kP * kN / 2);
+    auto go = [&](auto kernel, int w) {
+        const long groups_per_block = 4 * (64 / w);
+        hipLaunchKernelGGL(kernel, dim3((unsigned)((elems + groups_per_block - 1) / groups_per_block)), dim3(256), 0,
+                           st, a);
+        return hipGetLastError();
+    };
+    if (a.nseg <= 2) return go(carry_scan_kernel<2>, 2);
+    if (a.nseg <= 4) return go(carry_scan_kernel<4>, 4);
+    if (a.nseg <= 8) return go(carry_scan_kernel<8>, 8);
+    if (a.nseg <= 16) return go(carry_scan_kernel<16>, 16);
+    if (a.nseg <= 32) return go(carry_scan_kernel<32>, 32);
+    return go(carry_scan_kernel<64>, 64);
 }
 
 int scan_mfma_chunk(int io_bf16, int P, int N, int R, int Q) {

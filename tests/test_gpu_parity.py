@@ -157,6 +157,18 @@ def test_scan_segments_agree(m3):
         assert rel_l2(yk, ys[0]) < 1e-2
 
 
+@pytest.mark.parametrize("nseg", [16, 33, 100])
+def test_scan_many_segments(m3, nseg):
+    """More segments than one lane group of the carry scan holds: 16 (one group of 16
+    lanes), 33 (one 64-lane block, partly filled) and 100 (two blocks of 64, the second
+    entered with the first's carried state and angle), each against the oracle."""
+    cfg, d = make_small_case(3031 + nseg, batch=1, seqlen=2000, nheads=2, ngroups=1, headdim=64, dstate=128, rank=4,
+                             npairs=32, chunk=16, io_dtype="bf16", rms_bc=True, init_full=True)
+    yr, fr = ref_cpu.scan(d)
+    y, fin = _run_scan(m3, d, cfg, nsegments=nseg)
+    _compare(y, fin, yr, fr, "bf16", what="nseg=%d" % nseg)
+
+
 def test_long_chunk_request_is_split(m3):
     """A chunk longer than the matrix-core path's 256 rows (R = 4, Q = 128) runs
     on the small-chunk schedule (16 tokens): the same schedule, hence the same
