@@ -630,6 +630,19 @@ def main():
                                 "traffic": measured_traffic("scan", prim["workload"]),
                                 "algorithmic_flops": prim["flop_per_call"], "algorithmic_bytes": prim["bytes_per_call"],
                                 "hbm_achieved_gbs": prim["algo_gbs"], "hbm_frac": prim["hbm_frac"]}
+    if "scan5" in res and main_w != "scan5":
+        # the largest single-GPU scan (one sequence of 65536 tokens) with its own roofline
+        lw = res["scan5"]
+        bound = "hbm" if lw["hbm_frac"] >= lw["mfma_frac"] else "mfma"
+        line["roofline_long"] = {"workload": lw["workload"], "bound": bound,
+                                 "achieved": lw["algo_gbs"] if bound == "hbm" else lw["algo_tflops"],
+                                 "peak": PEAK_HBM_GBS if bound == "hbm" else PEAK_BF16_TFLOPS,
+                                 "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
+                                 "frac": lw["hbm_frac"] if bound == "hbm" else lw["mfma_frac"],
+                                 "traffic": measured_traffic("scan", lw["workload"]),
+                                 "algorithmic_bytes": lw["bytes_per_call"], "algorithmic_flops": lw["flop_per_call"],
+                                 "executed_chunk": lw["executed_chunk"], "ms_per_call": lw["ms_per_call"],
+                                 "mfma_frac": lw["mfma_frac"], "hbm_frac": lw["hbm_frac"]}
     if "decode4" in res:
         dd = res["decode4"]
         line["decode"] = {"workload": dd["workload"], "gbs": dd["gbs"], "hbm_frac": dd["hbm_frac"],
