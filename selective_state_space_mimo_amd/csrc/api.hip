@@ -166,22 +166,35 @@ hipError_t copy_or_zero(const void* src, void* dst, size_t bytes, hipStream_t s)
 // and C, dt, lambda, angular rates), its readouts and its own workspace, each part
 // starting on a 256-byte boundary.
 struct BlockWs {
+    bool fused;     // the matrix-core scan runs the layer steps itself (see m3_block_fwd)
     size_t xl, bn, cn, dt, lam, th, y, scan, scan_bytes, total;
 };
+// Whether m3_block_fwd takes the fused path for *d: the matrix-core scan lifts x and
+// activates dt, lambda, theta as it stages them and writes the recombined readout.
+bool block_fused(const m3_desc* d) {
+    if (d->seqlen < 1) return false;
+    const ScanArgs a = make_scan_args(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                      nullptr, nullptr, nullptr, nullptr);
+    return a.io_bf16 && scan_mfma_supported(a) && a.Q <= 64;
+}
 BlockWs block_ws(const m3_desc* d, int decode) {
     auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
     const size_t L = decode ? 1 : (size_t)d->seqlen;
     const size_t b = d->batch, H = d->nheads, G = d->ngroups, P = d->headdim, N = d->dstate, R = d->rank,
                  np = d->npairs, io = esize(d->io_dtype);
     BlockWs w{};
+    w.fused = !decode && block_fused(d);
+    // the fused path needs neither the lifted rows nor the activated inputs, and its readout
+    // is already recombined over the ranks
+    const size_t Rl = w.fused ? 0 : R, Ry = w.fused ? 1 : R, Lt = w.fused ? 0 : L;
     size_t o = 0;
-    w.xl = o;  o += up(b * L * H * R * P * io);
+    w.xl = o;  o += up(b * L * H * Rl * P * io);
     w.bn = o;  o += up(b * L * G * R * N * io);
     w.cn = o;  o += up(b * L * G * R * N * io);
-    w.dt = o;  o += up(b * L * H * 4);
-    w.lam = o; o += up(b * L * H * 4);
-    w.th = o;  o += up(b * L * H * np * 4);
-    w.y = o;   o += up(b * L * H * R * P * io);
+    w.dt = o;  o += up(b * Lt * H * 4);
+    w.lam = o; o += up(b * Lt * H * 4);
+    w.th = o;  o += up(b * Lt * H * np * 4);
+    w.y = o;   o += up(b * L * H * Ry * P * io);
     w.scan = o;
     w.scan_bytes = 0;
     if (!decode && L > 0) {
@@ -473,7 +486,7 @@ m3_status m3_block_fwd(const m3_desc* d, const m3_block_params* p, const void* z
     // (B and C are shared by the heads of a group).
     ScanArgs sa = make_scan_args(d, x, a.Bn, a.Cn, dt_raw, lam_raw, d->npairs ? th_raw : nullptr, A, p->B_bias,
                                  p->C_bias, init, base + w.y, final_);
-    const bool fused = sa.io_bf16 && scan_mfma_supported(sa) && sa.Q <= 64;
+    const bool fused = w.fused;
     if (fused) {
         a.xl = nullptr;
         a.dt = a.lam = a.th = nullptr;
