@@ -415,11 +415,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
     const int lo = live ? d * ES : kPcsOob, lod = live ? d * 4 : kPcsOob;
     // the ring holds the loaded bits; they are converted where used, PF tokens later (a
     // conversion at the load would wait for the load at once)
-    auto ld_x = [&](int r) -> uint32_t {
-        if constexpr (BF16) return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rx, lo + r * D * ES, 0, 0);
-        else return __builtin_amdgcn_raw_buffer_load_b32(rx, lo + r * D * 4, 0, 0);
+    // (the lane's channel as the vector offset, the token row as the scalar offset)
+    // x stays in the ring as the loaded bits (a 16-bit value for bf16: widening it to 32 bits
+    // would mask its upper half at the loop's head, where that masking waits for every load)
+    // (typed as a 16-bit float only so that no integer widening is asked for; no arithmetic
+    // is done on it)
+    using XRaw = typename std::conditional<BF16, _Float16, uint32_t>::type;
+    auto ld_x = [&](int r) -> XRaw {
+        if constexpr (BF16)
+            return __builtin_bit_cast(_Float16, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(rx, lo, r * D * ES, 0));
+        else return __builtin_amdgcn_raw_buffer_load_b32(rx, lo, r * D * 4, 0);
     };
-    auto ld_dt = [&](int r) -> uint32_t { return __builtin_amdgcn_raw_buffer_load_b32(rd, lod + r * D * 4, 0, 0); };
+    auto ld_dt = [&](int r) -> uint32_t { return __builtin_amdgcn_raw_buffer_load_b32(rd, lod, r * D * 4, 0); };
 
     // B, C tiles: PF rows of this wave's K values; 16-byte pieces
     const auto rb = pcs_rsrc(static_cast<const uint8_t*>(a.B) + row0 * G * N * ES, nrow * (uint32_t)(G * N * ES));
@@ -430,7 +437,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
     constexpr int NTEN = kFull ? 2 : 1;                    // B, and C when the readout is made
     static_assert(TP <= 64, "tile pieces");
     __shared__ __attribute__((aligned(16))) float sBC[NW][2][2][PF][K];  // [wave][buffer][B, C][token][m]
-    __shared__ __attribute__((aligned(16))) float sY[NW == 2 ? 2 : 1][2][64][HF];   // [buffer][from wave][lane][token]
+    __shared__ __attribute__((aligned(16))) float sY[NW == 2 ? 2 : 1][2][64][PF];   // [buffer][from wave][lane][token]
     uint4 tq[NTEN];
     // with fewer pieces than lanes, lanes past them repeat a piece (same value to the same
     // address): no lane is masked off, so no branch splits the token loop's block
@@ -461,7 +468,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
     // compiler's waits stay a ring deep: the first tile, the ring, a group's worth of
     // dropped stores (past the resource's end), the second tile.
     fetch_tile(0);
-    uint32_t xq[PF], dq[PF];
+    XRaw xq[PF];
+    uint32_t dq[PF];
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
         xq[j] = ld_x(j);
@@ -485,9 +493,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
             // take this token's x and dt out of the ring before the slot is reloaded, so that
             // each slot keeps one register (a slot whose old and new values overlapped would
             // be copied at the loop's end, and the copy would wait for the load)
+            // (for bf16 the copy is the widening shift: the value's bits to the upper half)
             uint32_t dcur, xcur;
             asm("v_mov_b32 %0, %1" : "=v"(dcur) : "v"(dq[j]));
-            asm("v_mov_b32 %0, %1" : "=v"(xcur) : "v"(xq[j]));
+            if constexpr (BF16) asm("v_lshlrev_b32 %0, 16, %1" : "=v"(xcur) : "v"(xq[j]));
+            else asm("v_mov_b32 %0, %1" : "=v"(xcur) : "v"(xq[j]));
             __builtin_amdgcn_sched_barrier(0);
             xq[j] = ld_x(r + PF);              // the ring: this slot's next token
             dq[j] = ld_dt(r + PF);
@@ -502,14 +512,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
             }
             __builtin_amdgcn_sched_barrier(0);
             const float st = __uint_as_float(dcur);
-            const float u = st * __uint_as_float(BF16 ? xcur << 16 : xcur);
+            const float u = st * __uint_as_float(xcur);
 #pragma unroll
             for (int m = 0; m < K; ++m) h[m] = __builtin_amdgcn_exp2f(st * a2[m]) * h[m] + u * bn[m];
             if constexpr (kFull) {
-                float p[4] = {cn[0] * h[0], cn[1] * h[1], cn[2] * h[2], cn[3] * h[3]};   // short chains
+                // partial sums: short dependency chains (four of N / 4 terms for a lone wave,
+                // whose instructions issue in order; two at half the coordinates)
+                constexpr int NP = NW == 1 ? 4 : 2;
+                float p[NP];
 #pragma unroll
-                for (int m = 4; m < K; ++m) p[m & 3] += cn[m] * h[m];
-                yp[j] = (p[0] + p[1]) + (p[2] + p[3]);
+                for (int k = 0; k < NP; ++k) p[k] = cn[k] * h[k];
+#pragma unroll
+                for (int m = NP; m < K; ++m) p[m % NP] += cn[m] * h[m];
+                if constexpr (NP == 4) yp[j] = (p[0] + p[1]) + (p[2] + p[3]);
+                else yp[j] = p[0] + p[1];
             } else {
                 dsum += st;
             }
@@ -519,31 +535,33 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
             const int r = r0 + j;
             if constexpr (BF16) {
                 const bf16 yb = (bf16)acc;
-                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, yb), ry, lo + r * D * ES, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, yb), ry, lo, r * D * ES, 0);
             } else {
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), ry, lo + r * D * 4, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), ry, lo, r * D * 4, 0);
             }
         };
         if constexpr (kFull && NW == 1) {
 #pragma unroll
             for (int j = 0; j < PF; ++j) store_y(j, yp[j]);
         } else if constexpr (kFull) {
-            // swap halves: this wave gives the other its partials of the other's half of
-            // the group's tokens (wave 0 completes tokens 0 .. HF - 1, wave 1 the rest)
-            const int give = (1 - w) * HF;
+            // both waves post all their partials; wave 0 completes tokens 0 .. HF - 1, wave 1
+            // the rest, reading both halves back at an offset of its own (the wave index is
+            // not a compile-time constant, and indexing the partials' registers by it
+            // would take a register-indexing mode switch per value)
             float4* dst = reinterpret_cast<float4*>(&sY[buf][w][lane][0]);
 #pragma unroll
-            for (int i = 0; i < HF; i += 4)
-                dst[i / 4] = float4{yp[give + i], yp[give + i + 1], yp[give + i + 2], yp[give + i + 3]};
+            for (int i = 0; i < PF; i += 4) dst[i / 4] = float4{yp[i], yp[i + 1], yp[i + 2], yp[i + 3]};
             __syncthreads();
             const int keep = w * HF;
-            const float4* src = reinterpret_cast<const float4*>(&sY[buf][1 - w][lane][0]);
+            const float4* s0 = reinterpret_cast<const float4*>(&sY[buf][0][lane][keep]);
+            const float4* s1 = reinterpret_cast<const float4*>(&sY[buf][1][lane][keep]);
 #pragma unroll
             for (int i = 0; i < HF; i += 4) {
-                const float4 o = src[i / 4];
-                const float v[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) store_y(keep + i + k, yp[keep + i + k] + v[k]);
+                const float4 u = s0[i / 4], v = s1[i / 4];
+                store_y(keep + i + 0, u.x + v.x);
+                store_y(keep + i + 1, u.y + v.y);
+                store_y(keep + i + 2, u.z + v.z);
+                store_y(keep + i + 3, u.w + v.w);
             }
         }
         // the next tile (loaded through this group) into the other buffer, and the one after
