@@ -184,9 +184,9 @@ BlockWs block_ws(const m3_desc* d, int decode) {
                  np = d->npairs, io = esize(d->io_dtype);
     BlockWs w{};
     w.fused = !decode && block_fused(d);
-    // the fused path needs neither the lifted rows nor the activated inputs, and its readout
-    // is already recombined over the ranks
-    const size_t Rl = w.fused ? 0 : R, Ry = w.fused ? 1 : R, Lt = w.fused ? 0 : L;
+    // the fused path needs neither the lifted rows nor the activated inputs nor the readouts
+    // (the scan writes the layer's output)
+    const size_t Rl = w.fused ? 0 : R, Ry = w.fused ? 0 : R, Lt = w.fused ? 0 : L;
     size_t o = 0;
     w.xl = o;  o += up(b * L * H * Rl * P * io);
     w.bn = o;  o += up(b * L * G * R * N * io);
@@ -493,13 +493,16 @@ m3_status m3_block_fwd(const m3_desc* d, const m3_block_params* p, const void* z
     }
     if (launch_block_prologue(a, hs) != hipSuccess) return M3_ERR_HIP;
     if (fused) {
+        // the scan recombines the readouts, adds the skip and applies the gate as it stores
+        // each token's row: it writes the layer's output, and no epilogue runs
         sa.lift = p->lift;
         sa.dt_bias = p->dt_bias;
-        sa.comb = p->comb;                      // y: the recombined readout [b, L, H, P]
+        sa.comb = p->comb;
+        sa.gate = z;
+        sa.dskip = p->D;
+        sa.y = out;
         sa.ws = w.scan_bytes ? reinterpret_cast<float*>(base + w.scan) : nullptr;
-        if (launch_scan_mfma(sa, hs) != hipSuccess) return M3_ERR_HIP;
-        a.R = 1;
-        a.comb = nullptr;
+        return launch_scan_mfma(sa, hs) == hipSuccess ? M3_OK : M3_ERR_HIP;
     } else {
         st = m3_scan_fwd(d, a.xl, a.Bn, a.Cn, a.dt, a.lam, d->npairs ? a.th : nullptr, A, p->B_bias, p->C_bias,
                          init, base + w.y, final_, w.scan_bytes ? base + w.scan : nullptr, w.scan_bytes, stream);

@@ -42,6 +42,10 @@ struct ScanArgs {
     // with lift: the readout weights [H, R, P]; y is then the recombined readout
     // sum_r comb[h, r] y_r, [b, L, H, P] (chunks of at most 64 tokens only)
     const float* comb;
+    // with comb and a non-null gate [b, L, H, P]: y is the layer's output, the recombined
+    // readout plus the skip dskip[h] x (dskip null: none), times silu(gate)
+    const void* gate;
+    const float* dskip;
 };
 
 // Decode-step arguments (one token, carry in place).

@@ -147,6 +147,7 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
     constexpr int TPC = NT / kNC;            // query tiles per consumer
     constexpr int RPB = 32 / kNC;            // staged output rows a consumer stores per key block
     static_assert(RPB * NKB == 16 * TPC, "a chunk's staged rows leave over its key blocks");
+    static_assert(RPB % R == 0, "a key block's staged rows are whole tokens");
     constexpr int TPL = Q > 64 ? Q / 64 : 1; // tokens per lane of the scanning wave
     constexpr int KT = R >= 4 ? 1 : 4 / R;   // key tokens among a lane's 4 rows of a score tile
     constexpr bool kEarlyExp = KT == 1;      // decay exps ahead of the score MFMAs (registers allow)
@@ -406,32 +407,6 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
             unsigned ln = lane;                               // opaque: offsets formed here
             asm volatile("" : "+v"(ln));
             ln &= 63u;
-            if constexpr (LAYER) {
-                // the layer: the R readouts of each token recombined, sum_r comb[r] y_r, one
-                // P-wide row per token (NR / R tokens, eight lanes a token)
-                const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<uint16_t*>(a.y) + ((tokbase + cst) * H + h) * kP,
-                                                            (uint32_t)nv * (uint32_t)(H * kP * 2));
-                if (ln < 8 * (NR / R)) {
-                    const unsigned qi0 = 16 * (unsigned)qt + (unsigned)r0 + R * (ln >> 3), k = ln & 7u;
-                    const float* cw = reinterpret_cast<const float*>(smem + LY::cmb);
-                    float acc[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-#pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const u32x4 v = *reinterpret_cast<const u32x4*>(ys + (qi0 + r) * 144 + k * 16);
-                        const float4 w0 = *reinterpret_cast<const float4*>(cw + r * kP + 8 * k);
-                        const float4 w1 = *reinterpret_cast<const float4*>(cw + r * kP + 8 * k + 4);
-                        acc[0] += w0.x * lo_f(v[0]); acc[1] += w0.y * hi_f(v[0]);
-                        acc[2] += w0.z * lo_f(v[1]); acc[3] += w0.w * hi_f(v[1]);
-                        acc[4] += w1.x * lo_f(v[2]); acc[5] += w1.y * hi_f(v[2]);
-                        acc[6] += w1.z * lo_f(v[3]); acc[7] += w1.w * hi_f(v[3]);
-                    }
-                    const u32x4 o = {pack2(acc[0], acc[1]), pack2(acc[2], acc[3]), pack2(acc[4], acc[5]), pack2(acc[6], acc[7])};
-                    __builtin_amdgcn_raw_buffer_store_b128(o, ro, (int)((qi0 / R) * (unsigned)(H * kP * 2) + 16 * k), 0, 0);
-                }
-                return;
-            }
             const __amdgpu_buffer_rsrc_t ry = make_rsrc(static_cast<uint16_t*>(a.y) + ((tokbase + cst) * H + h) * R * kP,
                                                         (uint32_t)nv * ysb);
             if (NR == 8 || ln < 8 * NR) {
@@ -441,6 +416,97 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
                 __builtin_amdgcn_raw_buffer_store_b128(v, ry, (int)(t * ysb + r * (kP * 2) + 16 * (ln & 7u)), 0, 0);
             }
         };
+        // (layer) Outputs leave as one P-wide row per token: the R staged readout rows
+        // recombined, sum_r comb[r] y_r, and with a gate, (that + dskip x) silu(gate).  The
+        // 16-byte pieces of a chunk's outputs of this wave are dealt to lanes: piece p (token u
+        // = p / 8 of the wave, its rows R u .. R u + R - 1 in tile order; eight pieces a token)
+        // to lane p % 64, slot p / 64.  Each lane loads the x and gate pieces of its slots
+        // with the chunk's C rows, finishes its pieces once those have landed (all lanes at
+        // once, in place: piece k of a token replaces piece k of its first staged row), and
+        // the key blocks store the finished pieces.
+        constexpr unsigned kXU = TPC * 16 / R;                // tokens of this wave's tiles
+        constexpr int kXS = (8 * kXU + 63) / 64;             // pieces per lane
+        u32x4 xpc[kXS], zpc[kXS];
+        const bool gated = LAYER && a.gate != nullptr;
+        const float dsk = LAYER && a.dskip ? a.dskip[h] : 0.f;
+        // query row of piece p's first rank
+        auto piece_row = [&](unsigned p) -> unsigned {
+            const unsigned rr = R * (p >> 3);
+            return 16u * (unsigned)ctile<kNC>(c, (int)(rr >> 4)) + (rr & 15u);
+        };
+        // x and gate pieces of the chunk at cst (nv valid tokens); pieces past the wave's
+        // outputs, rows of later tokens and every piece without a gate read zero
+        auto load_xz = [&](int cst, int nv) {
+            const uint32_t nb = gated ? (uint32_t)nv * (uint32_t)(H * kP * 2) : 0u;
+            const size_t rb = ((tokbase + cst) * H + h) * kP;
+            const __amdgpu_buffer_rsrc_t rxs = make_rsrc(static_cast<const uint16_t*>(a.x) + rb, nb);
+            const __amdgpu_buffer_rsrc_t rzs = make_rsrc(static_cast<const uint16_t*>(gated ? a.gate : a.x) + rb, nb);
+            unsigned ln = lane;                               // opaque: offsets formed here
+            asm volatile("" : "+v"(ln));
+            ln &= 63u;
+#pragma unroll
+            for (int sl = 0; sl < kXS; ++sl) {
+                const unsigned p = 64u * sl + ln;
+                const int off = p < 8u * kXU ? (int)((piece_row(p) / R) * (unsigned)(H * kP * 2) + 16u * (p & 7u)) : (int)nb;
+                xpc[sl] = __builtin_amdgcn_raw_buffer_load_b128(rxs, off, 0, 0);
+                zpc[sl] = __builtin_amdgcn_raw_buffer_load_b128(rzs, off, 0, 0);
+            }
+        };
+        // every piece of the staged chunk, in place
+        auto finish_pieces = [&]() {
+            unsigned ln = lane;                               // opaque: offsets formed here
+            asm volatile("" : "+v"(ln));
+            ln &= 63u;
+            const float* cw = reinterpret_cast<const float*>(smem + LY::cmb);
+#pragma unroll
+            for (int sl = 0; sl < kXS; ++sl) {
+                const unsigned p = 64u * sl + ln;
+                const unsigned qi0 = piece_row(p < 8u * kXU ? p : 0u), k = p & 7u;
+                float acc[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(ys + (qi0 + r) * 144 + k * 16);
+                    const float4 w0 = *reinterpret_cast<const float4*>(cw + r * kP + 8 * k);
+                    const float4 w1 = *reinterpret_cast<const float4*>(cw + r * kP + 8 * k + 4);
+                    acc[0] += w0.x * lo_f(v[0]); acc[1] += w0.y * hi_f(v[0]);
+                    acc[2] += w0.z * lo_f(v[1]); acc[3] += w0.w * hi_f(v[1]);
+                    acc[4] += w1.x * lo_f(v[2]); acc[5] += w1.y * hi_f(v[2]);
+                    acc[6] += w1.z * lo_f(v[3]); acc[7] += w1.w * hi_f(v[3]);
+                }
+                if (gated) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float xi = (i & 1) ? hi_f(xpc[sl][i / 2]) : lo_f(xpc[sl][i / 2]);
+                        const float zi = (i & 1) ? hi_f(zpc[sl][i / 2]) : lo_f(zpc[sl][i / 2]);
+                        acc[i] = (acc[i] + dsk * xi) * (zi * sigmoid_f(zi));
+                    }
+                }
+                // (the row reads of all lanes precede these writes: a wave's LDS accesses
+                // complete in order)
+                if (p < 8u * kXU)
+                    *reinterpret_cast<u32x4*>(ys + qi0 * 144 + k * 16) =
+                        u32x4{pack2(acc[0], acc[1]), pack2(acc[2], acc[3]), pack2(acc[4], acc[5]), pack2(acc[6], acc[7])};
+            }
+        };
+        // finished pieces pbeg .. pbeg + NPC - 1 (one slot) of the chunk at cst (nv valid
+        // tokens; rows of later tokens fall outside the record count)
+        auto layer_store = [&](int cst, int nv, unsigned pbeg, auto npc) {
+            constexpr unsigned NPC = decltype(npc)::value;
+            unsigned ln = lane;                               // opaque: offsets formed here
+            asm volatile("" : "+v"(ln));
+            ln &= 63u;
+            const unsigned p = (pbeg & ~63u) + ln;
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<uint16_t*>(a.y) + ((tokbase + cst) * H + h) * kP,
+                                                        (uint32_t)nv * (uint32_t)(H * kP * 2));
+            if (ln - (pbeg & 63u) < NPC && p < 8u * kXU) {
+                const unsigned qi0 = piece_row(p), k = p & 7u;
+                const u32x4 o = *reinterpret_cast<const u32x4*>(ys + qi0 * 144 + k * 16);
+                __builtin_amdgcn_raw_buffer_store_b128(o, ro, (int)((qi0 / R) * (unsigned)(H * kP * 2) + 16 * k), 0, 0);
+            }
+        };
+
         // raw C rows of tiles KB .. KE - 1 of the chunk at cst straight into the operand layout
         // (tile k, slice ks: row 16 qt + lane % 16, n = 32 ks + 8 (lane / 16) ...); rows of
         // tokens past the segment end read zero (their outputs are never stored)
@@ -475,6 +541,10 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
             //     chunk's theta and per-token inputs
             stage_theta(rgTh);
             if (kFullMode) load_c(c0, std::integral_constant<int, TPC - 1>{}, std::integral_constant<int, TPC>{});
+            // (layer) x and gate pieces of the previous chunk's outputs, stored over this
+            // chunk's key blocks (none before the first chunk: zero records)
+            if constexpr (LAYER)
+                if (kFullMode) load_xz(c0 > T0 ? c0 - Q : c0, c0 > T0 ? Q : 0);
             load_theta(c0 + Q, rgTh);
             __syncthreads();
             angles();
@@ -484,6 +554,9 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
                 else store_y(c0 - Q, Q);
             }
             __syncthreads();
+            // (layer) the previous chunk's output pieces, finished in place
+            if constexpr (LAYER)
+                if (kFullMode && c0 > T0) finish_pieces();
             // (C) C tiles: bias and turn; carry readout Y^T = exp(l_t) Hf Ct^T
             int tq[TPC];
             float l2q[TPC];
@@ -649,10 +722,16 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
             // (none before the first chunk: a record count of 0 drops the stores)
             const int nprev = c0 > T0 ? Q : 0;
             auto block_end = [&](int J) {
-                if constexpr (LY::kYStage)
+                if constexpr (LAYER) {
+                    // the tokens of rows RPB J .. RPB J + RPB - 1: pieces 8 RPB J / R ..
+                    if (kFullMode)
+                        layer_store(nprev ? c0 - Q : c0, nprev, 8u * RPB * J / R,
+                                    std::integral_constant<unsigned, 8 * RPB / R>{});
+                } else if constexpr (LY::kYStage) {
                     if (kFullMode)
                         store_rows(nprev ? c0 - Q : c0, nprev, ctile<kNC>(c, RPB * J / 16), RPB * J % 16,
                                    std::integral_constant<unsigned, RPB>{});
+                }
                 __syncthreads();
             };
             int Jb = 0;
@@ -694,7 +773,13 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
         // the last chunk's outputs
         if (kFullMode && T1 > T0) {
             const int cst = T0 + (T1 - T0 - 1) / Q * Q, nv = (T1 - T0 - 1) % Q + 1;
-            if constexpr (LY::kYStage) {
+            if constexpr (LAYER) {
+                stage_y();
+                load_xz(cst, nv);
+                finish_pieces();
+#pragma unroll
+                for (int sl = 0; sl < kXS; ++sl) layer_store(cst, nv, 64u * sl, std::integral_constant<unsigned, 64>{});
+            } else if constexpr (LY::kYStage) {
                 stage_y();
 #pragma unroll
                 for (int k = 0; k < TPC; ++k)

@@ -296,8 +296,8 @@ def test_pcs_schedule_sizes(m3):
 
 def test_layer_workspace_follows_the_path(m3):
     """m3_block_workspace_size sizes what the path taken uses: on the fused bf16
-    matrix-core path (P 64, N 128, R 4, chunk 64) only the normalised B, C, the
-    readout recombined over the ranks and the scan's own workspace; the unfused
+    matrix-core path (P 64, N 128, R 4, chunk 64) only the normalised B, C and the
+    scan's own workspace (the scan writes the layer's output itself); the unfused
     path also holds the lifted x, the activated dt / lambda / theta and R readouts."""
     n = ctypes.c_size_t(0)
     kw = dict(batch=2, seqlen=256, nheads=4, ngroups=1, headdim=64, dstate=128, rank=4, npairs=32, chunk=64,
@@ -305,7 +305,7 @@ def test_layer_workspace_follows_the_path(m3):
     assert m3.lib.m3_block_workspace_size(ctypes.byref(_desc(m3, io_dtype=m3.M3_BF16, **kw)), 0, ctypes.byref(n)) == 0
     fused = n.value
     b, L, H, P, N, R = 2, 256, 4, 64, 128, 4
-    assert fused == 2 * (b * L * R * N * 2) + b * L * H * P * 2          # Bn, Cn, recombined y (256-byte multiples)
+    assert fused == 2 * (b * L * R * N * 2)                              # Bn, Cn (256-byte multiples)
     assert m3.lib.m3_block_workspace_size(ctypes.byref(_desc(m3, io_dtype=m3.M3_F32, **kw)), 0, ctypes.byref(n)) == 0
     unfused = n.value
     assert unfused >= b * L * H * R * P * 4 * 2 + 2 * b * L * R * N * 4 + b * L * H * (2 + 32) * 4

@@ -62,6 +62,32 @@ def scan_segments(b, H, L, R, Q, nsegments):
     return max(1, -(-L // seglen)), seglen
 
 
+def _ctile(nc, c, k):
+    """Query tile k of consumer c (tiles dealt in groups of 2 nc: c and 2 nc - 1 - c)."""
+    return 2 * nc * (k >> 1) + ((2 * nc - 1 - c) if (k & 1) else c)
+
+
+def layer_pieces(R, Q, n_cons):
+    """(token of the chunk, 16-byte piece) pairs of the layer's output rows as the
+    consumers' lanes take them: piece p of consumer c (token u = p / 8 of its tiles,
+    rows R u .. R u + R - 1 in tile order) goes to lane p % 64, slot p / 64; pieces past
+    the consumer's tokens are not issued."""
+    tpc = Q * R // 16 // n_cons
+    xu = tpc * 16 // R
+    slots = (8 * xu + 63) // 64
+    out = []
+    for c in range(n_cons):
+        for sl in range(slots):
+            for ln in range(64):
+                p = 64 * sl + ln
+                if p >= 8 * xu:
+                    continue
+                rr = R * (p >> 3)
+                row = 16 * _ctile(n_cons, c, rr >> 4) + (rr & 15)
+                out.append((row // R, p & 7))
+    return out
+
+
 def replay_scan(b, L, H, G, R, Q, np_, nseg, seglen, layer=False):
     n_cons = 8 if (R == 4 and Q == 64) else 4
     n_threads = 64 * (n_cons + 4)
@@ -110,14 +136,18 @@ def replay_scan(b, L, H, G, R, Q, np_, nseg, seglen, layer=False):
                     base = Cg + (cst if nv > 0 else 0) * bstride * 2
                     t, r = qi // R, qi % R
                     _check("C rows", base, nv * bsb, t * bsb + r * (KN * 2) + 64 * ks + 16 * j4, 16, B_bytes)
-                # outputs: whole staged rows (the layer: one recombined P-wide row per token)
+                # outputs: whole staged rows (the layer: one P-wide row per token, in 16-byte
+                # pieces dealt to the consumers' lanes; the x and gate pieces are read at the
+                # same offsets of their [b, L, H, P] tensors)
                 for cst in chunks:
                     nv = max(0, min(Q, T1 - cst))
                     k8 = np.arange(8)[None, None, :]
                     tq = np.arange(Q)[:, None, None]
                     if layer:
                         base = ((tokbase + cst) * H + h) * KP * 2
-                        _check("layer y", base, nv * H * KP * 2, tq * (H * KP * 2) + 16 * k8, 16, Y_bytes)
+                        offs = np.array([t * (H * KP * 2) + 16 * k for t, k in layer_pieces(R, Q, n_cons)])
+                        for what in ("layer out", "layer x", "layer gate"):
+                            _check(what, base, nv * H * KP * 2, offs, 16, Y_bytes)
                     else:
                         rr = np.arange(R)[None, :, None]
                         base = ((tokbase + cst) * H + h) * R * KP * 2
@@ -174,6 +204,19 @@ def test_scan_resources_stay_in_their_tensors(m3, shape):
     assert ws == (0 if nseg == 1 else S * (2 * KP * KN + 1 + 2 * np_) * 4), "segment schedule differs from the library's"
     replay_scan(b, L, H, G, R, Qe, np_, nseg, seglen)
     replay_scan(b, L, H, G, R, Qe, np_, nseg, seglen, layer=True)
+
+
+@pytest.mark.parametrize("rq", [(1, 64), (2, 32), (2, 64), (4, 16), (4, 32), (4, 64)])
+def test_layer_pieces_cover_each_output_once(rq):
+    """The layer variant's lanes store every (token, 16-byte piece) of a chunk's
+    outputs exactly once, and each key block's share is whole tokens of one slot."""
+    R, Q = rq
+    n_cons = 8 if (R == 4 and Q == 64) else 4
+    pieces = layer_pieces(R, Q, n_cons)
+    assert sorted(pieces) == [(t, k) for t in range(Q) for k in range(8)]
+    rpb = 32 // n_cons
+    npc = 8 * rpb // R
+    assert 64 % npc == 0 and rpb % R == 0
 
 
 @pytest.mark.parametrize("name", ["siso_bf16_mamba2", "mimo_bf16_prefill", "mimo_bf16_long"])
