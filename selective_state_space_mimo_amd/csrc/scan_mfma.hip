@@ -480,7 +480,10 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
                     for (int i = 0; i < 8; ++i) {
                         const float xi = (i & 1) ? hi_f(xpc[sl][i / 2]) : lo_f(xpc[sl][i / 2]);
                         const float zi = (i & 1) ? hi_f(zpc[sl][i / 2]) : lo_f(zpc[sl][i / 2]);
-                        acc[i] = (acc[i] + dsk * xi) * (zi * sigmoid_f(zi));
+                        // silu(z) = z / (1 + exp(-z)) with the hardware exp2 and reciprocal
+                        // (rounded to bf16 next); a large |z| gives z or -0
+                        const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zi * kLog2e));
+                        acc[i] = (acc[i] + dsk * xi) * (zi * sg);
                     }
                 }
                 // (the row reads of all lanes precede these writes: a wave's LDS accesses
@@ -541,9 +544,10 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
             //     chunk's theta and per-token inputs
             stage_theta(rgTh);
             if (kFullMode) load_c(c0, std::integral_constant<int, TPC - 1>{}, std::integral_constant<int, TPC>{});
-            // (layer) x and gate pieces of the previous chunk's outputs, stored over this
-            // chunk's key blocks (none before the first chunk: zero records)
-            if constexpr (LAYER)
+            // (layer, one tile per consumer) x and gate pieces of the previous chunk's
+            // outputs, stored over this chunk's key blocks (none before the first chunk: zero
+            // records); with more tiles they are loaded in the previous chunk's last phase
+            if constexpr (LAYER && TPC == 1)
                 if (kFullMode) load_xz(c0 > T0 ? c0 - Q : c0, c0 > T0 ? Q : 0);
             load_theta(c0 + Q, rgTh);
             __syncthreads();
@@ -739,8 +743,12 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
                 constexpr int K0 = decltype(mc)::value;
                 const int Je = K0 < TPC ? min(NKB, ctile<kNC>(c, K0 < TPC ? K0 : 0) / 2 + 1) : NKB;
                 if constexpr (TPC > 1 && K0 == TPC - 1)
-                    if (kFullMode)               // (none after the last chunk: zero records)
+                    if (kFullMode) {             // (none after the last chunk: zero records)
                         load_c(c0 + Q, std::integral_constant<int, 0>{}, std::integral_constant<int, TPC - 1>{});
+                        // (layer) x and gate pieces of this chunk's outputs, finished at the
+                        // next chunk's start: a phase of key blocks hides their latency
+                        if constexpr (LAYER) load_xz(c0, min(Q, T1 - c0));
+                    }
                 if constexpr (K0 < TPC && kEarlyExp) {
                     // blocks before the last of tile K0, then its diagonal block
 #pragma unroll 1
@@ -775,7 +783,7 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
             const int cst = T0 + (T1 - T0 - 1) / Q * Q, nv = (T1 - T0 - 1) % Q + 1;
             if constexpr (LAYER) {
                 stage_y();
-                load_xz(cst, nv);
+                if constexpr (TPC == 1) load_xz(cst, nv);     // (else loaded in its last phase)
                 finish_pieces();
 #pragma unroll
                 for (int sl = 0; sl < kXS; ++sl) layer_store(cst, nv, 64u * sl, std::integral_constant<unsigned, 64>{});
