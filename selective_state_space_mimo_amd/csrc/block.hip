@@ -126,31 +126,47 @@ template <> struct Vec<4> {          // f32
     __device__ static T pack(const float (&f)[4]) { return T{f[0], f[1], f[2], f[3]}; }
 };
 
-// BCNorm, vectorised: G = N / V lanes per row, 64 / G rows per wave (N / V a power of
-// two dividing 64).
+// BCNorm, vectorised: G = N / V lanes per row, 64 / G rows per wave pass (N / V a power
+// of two dividing 64), kBcPasses passes per wave over consecutive rows.  B and C rows
+// alternate, and every pass covers an even number of rows, so a lane keeps one tensor
+// and one piece of the row throughout: its gains are loaded once, and all of its row
+// pieces are in flight together before any is reduced.
+constexpr int kBcPasses = 4;
 template <int V>
 __global__ __launch_bounds__(64 * kWaves) void bcnorm_vec_kernel(BlockArgs a) {
     typedef typename Vec<V>::T T;
     const int lane = threadIdx.x & 63;
     const int G = a.N / V, RPW = 64 / G;
     const long long rows = (long long)a.b * a.L * a.G * a.R;
-    const long long ri = ((long long)blockIdx.x * kWaves + (threadIdx.x >> 6)) * RPW + lane / G;
-    const bool ok = ri < 2 * rows;
-    const int which = (int)(ri & 1);
-    const size_t row = ok ? (size_t)(ri >> 1) : 0;
+    const long long r0 = ((long long)blockIdx.x * kWaves + (threadIdx.x >> 6)) * RPW * kBcPasses + lane / G;
+    const int which = (int)(r0 & 1);                          // RPW is even: the same every pass
     const int j = lane % G;                                   // piece of the row
     const T* src = reinterpret_cast<const T*>(which ? a.Craw : a.Braw);
-    float f[V];
-    Vec<V>::unpack(ok ? src[row * G + j] : T{}, f);
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < V; ++i) ss += f[i] * f[i];
-    for (int o = G >> 1; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);    // within the row's lanes
-    const float sc = 1.f / sqrtf(ss / (float)a.N + a.eps);
+    T* dst = reinterpret_cast<T*>(which ? a.Cn : a.Bn);
     const float* gain = which ? a.Cg : a.Bg;
+    float gv[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) f[i] *= sc * (gain ? gain[j * V + i] : 1.f);
-    if (ok) reinterpret_cast<T*>(which ? a.Cn : a.Bn)[row * G + j] = Vec<V>::pack(f);
+    for (int i = 0; i < V; ++i) gv[i] = gain ? gain[j * V + i] : 1.f;
+    T raw[kBcPasses];
+#pragma unroll
+    for (int k = 0; k < kBcPasses; ++k) {
+        const long long ri = r0 + (long long)k * RPW;
+        raw[k] = ri < 2 * rows ? src[(size_t)(ri >> 1) * G + j] : T{};
+    }
+#pragma unroll
+    for (int k = 0; k < kBcPasses; ++k) {
+        const long long ri = r0 + (long long)k * RPW;
+        float f[V];
+        Vec<V>::unpack(raw[k], f);
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < V; ++i) ss += f[i] * f[i];
+        for (int o = G >> 1; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);    // within the row's lanes
+        const float sc = 1.f / sqrtf(ss / (float)a.N + a.eps);
+#pragma unroll
+        for (int i = 0; i < V; ++i) f[i] *= sc * gv[i];
+        if (ri < 2 * rows) dst[(size_t)(ri >> 1) * G + j] = Vec<V>::pack(f);
+    }
 }
 
 // Per (token, head), vectorised: the lifted x (G = P / V lanes per token-head); the
@@ -233,10 +249,11 @@ hipError_t launch_block_prologue(const BlockArgs& a, hipStream_t s) {
     const long long toks = (long long)a.b * a.L * a.H;
     const int v = vec_width(a);
     if (rows > 0) {
-        if (vec_ok(a, a.N)) {
-            const int rpw = 64 / (a.N / v);
-            if (v == 8) hipLaunchKernelGGL(bcnorm_vec_kernel<8>, dim3(blocks_for((rows + rpw - 1) / rpw)), dim3(64 * kWaves), 0, s, a);
-            else hipLaunchKernelGGL(bcnorm_vec_kernel<4>, dim3(blocks_for((rows + rpw - 1) / rpw)), dim3(64 * kWaves), 0, s, a);
+        if (vec_ok(a, a.N) && a.N / v <= 32) {          // (an even number of rows per pass)
+            const long long rpw = (64 / (a.N / v)) * kBcPasses;    // rows (B and C) per wave
+            const long long waves = (rows + rpw - 1) / rpw;
+            if (v == 8) hipLaunchKernelGGL(bcnorm_vec_kernel<8>, dim3(blocks_for(waves)), dim3(64 * kWaves), 0, s, a);
+            else hipLaunchKernelGGL(bcnorm_vec_kernel<4>, dim3(blocks_for(waves)), dim3(64 * kWaves), 0, s, a);
         } else {
             hipLaunchKernelGGL(bcnorm_kernel, dim3(blocks_for(rows)), dim3(64 * kWaves), 0, s, a);
         }
