@@ -515,7 +515,8 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
         // tokens past the segment end read zero (their outputs are never stored)
         auto load_c = [&](int cst, auto kbc, auto kec) {
             constexpr int KB = decltype(kbc)::value, KE = decltype(kec)::value;
-            const int nv = max(0, min(Q, T1 - cst));
+            // (uniform; stated, so that the resource stays scalar on every path)
+            const int nv = __builtin_amdgcn_readfirstlane(max(0, min(Q, T1 - cst)));
             const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cg + (size_t)(nv > 0 ? cst : 0) * bstride, (uint32_t)nv * bsb);
             unsigned ln = lane;                               // opaque: offsets formed here
             asm volatile("" : "+v"(ln));
