@@ -36,7 +36,8 @@ CSRC = os.path.join(ROOT, "selective_state_space_mimo_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 # sources that define each measured kernel (the counters stand only while these are unchanged)
 KERNEL_SOURCES = {"scan": ("scan_mfma.hip", "scan_common.h", "m3_internal.h"), "decode": ("decode.hip", "m3_internal.h"),
-                  "bwd": ("bwd.hip", "m3_internal.h"), "pcs": ("pcs.hip", "m3_internal.h")}
+                  "bwd": ("bwd.hip", "m3_internal.h"), "pcs": ("pcs.hip", "m3_internal.h"),
+                  "layer": ("scan_mfma.hip", "scan_common.h", "m3_internal.h", "block.hip")}
 
 
 def source_sha(kind):
