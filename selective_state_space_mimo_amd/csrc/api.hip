@@ -278,7 +278,10 @@ m3_status m3_scan_workspace_size(const m3_desc* d, size_t* bytes) {
     if (d->seqlen == 0) return M3_OK;
     ScanArgs a = make_scan_args(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                 nullptr, nullptr, nullptr, nullptr);
+    // (the biases are not part of the descriptor: a shape the single-rank path takes
+    // without them gets room for either path)
     if (a.io_bf16 && scan_mfma_supported(a)) *bytes = scan_mfma_workspace_bytes(a);
+    if (scan_siso_supported(a)) *bytes = std::max(*bytes, scan_siso_workspace_bytes(a));
     return M3_OK;
 }
 
@@ -341,8 +344,9 @@ m3_status scan_fwd_impl(const m3_desc* d, const void* x, const void* B, const vo
 
     ScanArgs a = make_scan_args(d, x, B, C, dt, lam, theta, A_log, B_bias, C_bias, init, y, final_);
     hipError_t e;
-    if (a.io_bf16 && scan_mfma_supported(a)) {
-        const size_t need = scan_mfma_workspace_bytes(a);
+    const bool siso = scan_siso_supported(a);
+    if (siso || (a.io_bf16 && scan_mfma_supported(a))) {
+        const size_t need = siso ? scan_siso_workspace_bytes(a) : scan_mfma_workspace_bytes(a);
         if (use_scratch) {
             // every summary, incoming state and phase is written before it is read, so the
             // scratch needs no clearing; what a previous call left there does not matter
@@ -359,7 +363,7 @@ m3_status scan_fwd_impl(const m3_desc* d, const void* x, const void* B, const vo
                 if ((init && overlap(rw, ri[i])) || (final_ && overlap(rw, rf[i]))) return M3_ERR_INVALID_ARG;
         }
         a.ws = static_cast<float*>(workspace);
-        e = launch_scan_mfma(a, hs);
+        e = siso ? launch_scan_siso(a, hs) : launch_scan_mfma(a, hs);
     } else {
         if (scan_generic_chunk(a.P, a.N, a.R, a.np, a.Q) < 1) return M3_ERR_UNSUPPORTED;
         e = launch_scan_generic(a, hs);

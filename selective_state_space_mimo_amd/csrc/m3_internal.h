@@ -118,6 +118,11 @@ hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t s);
 size_t scan_mfma_workspace_bytes(const ScanArgs& a);
 // Pass 2 of the segmented schedule (the carry recurrence across segments).
 hipError_t launch_carry_pass(const ScanArgs& a, hipStream_t s);
+// One rank, no rotation, no bias, bf16 I/O, fp32 state, P 64, N 128, chunks of 64 tokens:
+// head-shared scores per (batch, group, chunk), then the scan per (batch, head, half of P).
+bool scan_siso_supported(const ScanArgs& a);
+size_t scan_siso_workspace_bytes(const ScanArgs& a);
+hipError_t launch_scan_siso(const ScanArgs& a, hipStream_t s);
 
 // Per-coordinate selective scan (pcs.hip): x, dt [b, L, D], A_log [D, N], B, C
 // [b, L, G, N], state [b, D, N] fp32; x, B, C and y in the io dtype, dt fp32.

@@ -11,7 +11,7 @@ import pytest
 
 from m3inputs import CONFIGS, config_by_name, make_decode_inputs, make_scan_inputs, make_small_case
 from oracle import ref_cpu
-from tests._util import host, phase_err, pooled_signed, rel_l2, to_device
+from tests._util import ROW_TOL, host, phase_err, pooled_signed, rel_l2, row_errors, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -141,6 +141,36 @@ def test_scan_mfma(m3, case):
     yr, fr = ref_cpu.scan(d)
     y, fin = _run_scan(m3, d, cfg, nsegments=nseg)
     _compare(y, fin, yr, fr, "bf16", what="mfma")
+
+
+# The single-rank path without rotation or bias (head-shared scores per batch, group and
+# chunk, then the scan per batch, head and half of P): the trapezoid term and the carries,
+# groups, ragged and short sequences, per-token rates; every output row bounded on its own.
+SISO = [
+    # L,   G, H, lam1,  init,  dyn
+    (130, 1, 4, True, False, False),
+    (200, 1, 4, False, True, False),
+    (64, 2, 4, False, True, False),
+    (1, 1, 2, False, True, False),
+    (37, 1, 3, False, False, False),
+    (300, 2, 4, False, True, True),
+    (2048, 1, 2, False, True, False),
+]
+
+
+@pytest.mark.parametrize("case", SISO, ids=lambda c: "L%d-G%d-H%d-lam1%d-init%d-dyn%d" % c)
+def test_scan_siso(m3, case):
+    L, G, H, lam1, init, dyn = case
+    _say("siso scan", case)
+    cfg, d = make_small_case(5000 + L + 7 * G + H + 3 * init + dyn, batch=2, seqlen=L, nheads=H, ngroups=G, headdim=64,
+                             dstate=128, rank=1, npairs=0, chunk=64, io_dtype="bf16", state_dtype="f32",
+                             bias=False, lam_one=lam1, rms_bc=True, init_full=init, rate_dyn=dyn)
+    yr, fr = ref_cpu.scan(d)
+    y, fin = _run_scan(m3, d, cfg)
+    _compare(y, fin, yr, fr, "bf16", what="siso")
+    er = float(row_errors(host(y), np.asarray(yr)).max())
+    _say("  siso worst row %.3e" % er)
+    assert er <= ROW_TOL
 
 
 def test_scan_segments_agree(m3):

@@ -6,7 +6,8 @@ or is dropped, so a resource may reach past its tensor (the output rows of one h
 span whole tokens of all heads); what must hold is that every offset *inside* the
 record count addresses bytes of the tensor.  The replay below restates the kernels'
 base, record-count and offset arithmetic (the matrix-core chunked scan in
-csrc/scan_mfma.hip, both per-coordinate kernels in csrc/pcs.hip) and checks it for
+csrc/scan_mfma.hip, the single-rank scan and its score pass in csrc/scan_siso.hip,
+both per-coordinate kernels in csrc/pcs.hip) and checks it for
 the edge workgroups (first and last batch, head, channel tile and segment, every
 chunk of the segment) of every shape the GPU tests and the benchmark run.  The
 segment schedule is the library's, restated here and cross-checked against the
@@ -175,6 +176,63 @@ def replay_scan(b, L, H, G, R, Q, np_, nseg, seglen, layer=False):
                         fx += TPB * xstride
 
 
+SISO_PREP_CHUNK = 10 * 1024 + 8 * 2 * 64 * 16      # score tiles and B^T operands of one chunk
+
+
+def siso_path(R, Q, np_, bias):
+    """Whether the library runs the single-rank scan (bf16, fp32 state, no rotation or bias)."""
+    return R == 1 and Q == 64 and np_ == 0 and not bias
+
+
+def replay_siso(b, L, H, G):
+    """The score pass (per batch, group and chunk) and the scan (per batch, head and half
+    of P; every chunk, and the inputs it fetches one chunk past the last)."""
+    nch = -(-L // 64)
+    lanes = np.arange(64)
+    l16, g4 = lanes & 15, lanes >> 4
+    tids = np.arange(256)
+    rowb = G * KN * 2
+    xrow = H * KP * 2
+    BC_bytes = b * L * G * KN * 2
+    X_bytes = b * L * H * KP * 2
+    T_bytes = b * L * H * 4
+    for bi in sorted({0, b - 1}):
+        for g in sorted({0, G - 1}):
+            for c in sorted({0, nch - 1}):
+                c0 = c * 64
+                nv = min(64, L - c0)
+                base = ((bi * L + c0) * G + g) * KN * 2
+                for q in range(4):
+                    offs = [(16 * q + l16) * rowb + (32 * ks + 8 * g4) * 2 for ks in range(4)]
+                    offs += [(16 * kt + l16) * rowb + (32 * ks + 8 * g4) * 2 for kt in range(q + 1) for ks in range(4)]
+                    for what in ("prep C rows", "prep B rows"):
+                        _check(what, base, nv * rowb, np.stack(offs), 16, BC_bytes)
+                    gath = [(32 * us + key) * rowb + (16 * (2 * q + j) + l16) * 2
+                            for j in range(2) for us in range(2) for key in range(32)]
+                    _check("prep B gathers", base, nv * rowb, np.asarray(gath), 2, BC_bytes)
+        for h in sorted({0, H - 1}):
+            g = h * G // H
+            tok0 = bi * L
+            for ph in (0, 1):
+                p0 = 32 * ph
+                xbase = ((tok0 * H + h) * KP + p0) * 2
+                xrec = (L - 1) * xrow + 64
+                cbase = (tok0 * G + g) * KN * 2
+                crec = (L - 1) * rowb + KN * 2
+                tbase = (tok0 * H + h) * 4
+                trec = ((L - 1) * H + 1) * 4
+                for c in sorted({0, max(0, nch - 1), nch}):
+                    c0 = c * 64
+                    _check("siso x", xbase, xrec, (c0 + (tids >> 2)) * xrow + 16 * (tids & 3), 16, X_bytes)
+                    for q in range(4):
+                        yo = [(c0 + 16 * q + l16) * xrow + (16 * pt + 4 * g4) * 2 for pt in range(2)]
+                        _check("siso y", xbase, xrec, np.stack(yo), 8, X_bytes)
+                        co = [(c0 + 16 * q + l16) * rowb + (32 * ks + 8 * g4) * 2 for ks in range(4)]
+                        _check("siso C", cbase, crec, np.stack(co), 16, BC_bytes)
+                    _check("siso dt, lam", tbase, trec, np.concatenate([(c0 + lanes) * H * 4, [(c0 + 64) * H * 4]]), 4,
+                           T_bytes)
+
+
 def _scan_ws(m3, b, L, H, G, R, Q, np_, nseg):
     d = m3.Desc(b, L, H, G, KP, KN, R, np_, Q, m3.M3_BF16, m3.M3_F32, nseg, m3.M3_RATE_STATIC)
     n = ctypes.c_size_t(0)
@@ -206,6 +264,16 @@ def test_scan_resources_stay_in_their_tensors(m3, shape):
     replay_scan(b, L, H, G, R, Qe, np_, nseg, seglen, layer=True)
 
 
+@pytest.mark.parametrize("shape", [(2, 130, 4, 1), (2, 200, 4, 1), (2, 64, 4, 2), (2, 1, 2, 1), (2, 37, 3, 1),
+                                   (2, 300, 4, 2), (2, 2048, 2, 1)], ids=lambda s: "b%d_L%d_H%d_G%d" % s)
+def test_siso_resources_stay_in_their_tensors(m3, shape):
+    """The single-rank path at the shapes its GPU parity cases run."""
+    b, L, H, G = shape
+    ws = _scan_ws(m3, b, L, H, G, 1, 64, 0, 0)
+    assert ws >= b * G * (-(-L // 64)) * SISO_PREP_CHUNK
+    replay_siso(b, L, H, G)
+
+
 @pytest.mark.parametrize("rq", [(1, 64), (2, 32), (2, 64), (4, 16), (4, 32), (4, 64)])
 def test_layer_pieces_cover_each_output_once(rq):
     """The layer variant's lanes store every (token, 16-byte piece) of a chunk's
@@ -225,9 +293,17 @@ def test_scan_resources_at_the_workloads(m3, name):
     b, L, H, G, R, np_ = cfg.batch, cfg.seqlen, cfg.nheads, cfg.ngroups, cfg.rank, cfg.npairs
     for Q in sorted({cfg.chunk, 16 if R == 4 else cfg.chunk}):
         Qe = executed_chunk(R, Q)
-        nseg, seglen = scan_segments(b, H, L, R, Qe, 0)
         ws = _scan_ws(m3, b, L, H, G, R, Q, np_, 0)
-        assert ws == (0 if nseg == 1 else b * H * nseg * (2 * KP * KN + 1 + 2 * np_) * 4)
+        nseg, seglen = scan_segments(b, H, L, R, Qe, 0)
+        seg_ws = 0 if nseg == 1 else b * H * nseg * (2 * KP * KN + 1 + 2 * np_) * 4
+        if siso_path(R, Qe, np_, False):
+            # room for either path (the descriptor does not say whether biases come)
+            assert ws == max(seg_ws, b * G * (-(-L // 64)) * SISO_PREP_CHUNK), "workspace differs from the library's"
+            replay_siso(b, L, H, G)
+            if not siso_path(R, Qe, np_, cfg.bias):
+                replay_scan(b, L, H, G, R, Qe, np_, nseg, seglen)
+            continue
+        assert ws == seg_ws
         replay_scan(b, L, H, G, R, Qe, np_, nseg, seglen)
     replay_scan(b, L, H, G, R, executed_chunk(R, cfg.chunk), np_, *scan_segments(b, H, L, R, executed_chunk(R, cfg.chunk), 0),
                 layer=True)
