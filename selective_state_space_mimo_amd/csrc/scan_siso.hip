@@ -148,8 +148,8 @@ __global__ __launch_bounds__(256) void siso_scan_kernel(ScanArgs a) {
                                                 (uint32_t)(L - 1) * brow + kN * 2);
     const __amdgpu_buffer_rsrc_t rdt = make_rsrc(a.dt + tok0 * H + h, (uint32_t)((L - 1) * H + 1) * 4u);
     const __amdgpu_buffer_rsrc_t rlm = make_rsrc(a.lam + tok0 * H + h, (uint32_t)((L - 1) * H + 1) * 4u);
-    const __amdgpu_buffer_rsrc_t rra = make_rsrc(a.A_log + (dyn_rate ? tok0 * H + h : 0),
-                                                 dyn_rate ? (uint32_t)((L - 1) * H + 1) * 4u : 0u);
+    // (static rates: the rate loads read dt again, unused)
+    const __amdgpu_buffer_rsrc_t rra = dyn_rate ? make_rsrc(a.A_log + tok0 * H + h, (uint32_t)((L - 1) * H + 1) * 4u) : rdt;
     const char* const prep = reinterpret_cast<const char*>(a.ws) + ((size_t)bi * G + g) * nch * kPrepChunkBytes;
 
     char* const sX = smem;
@@ -169,21 +169,22 @@ __global__ __launch_bounds__(256) void siso_scan_kernel(ScanArgs a) {
     auto fetch = [&](int c, In& in) {
         const int c0 = c * kSQ;
         const char* pc = prep + (size_t)min(c, nch - 1) * kPrepChunkBytes;   // (past the last chunk: unused)
+        // (every load unconditional, so that each wait counts exactly the later ones: the
+        // scalars are loaded by every wave, only wave 0 uses them; tiles past the diagonal
+        // read the diagonal tile again, and the weights zero them)
         in.x = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((c0 + (tid >> 2)) * xrow + 16 * (tid & 3)), 0, 0);
-        in.dt = in.lm = in.ra = in.dtn = in.lmn = 0.f;
-        if (q == 0) {
-            const int o = (c0 + lane) * H * 4;
-            in.dt = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdt, o, 0, 0));
-            in.lm = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rlm, o, 0, 0));
-            in.ra = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rra, o, 0, 0));
-            const int on = (c0 + kSQ) * H * 4;
-            in.dtn = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdt, on, 0, 0));
-            in.lmn = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rlm, on, 0, 0));
-        }
+        const int o = (c0 + lane) * H * 4;
+        in.dt = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdt, o, 0, 0));
+        in.lm = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rlm, o, 0, 0));
+        in.ra = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rra, o, 0, 0));
+        const int on = (c0 + kSQ) * H * 4;
+        in.dtn = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdt, on, 0, 0));
+        in.lmn = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rlm, on, 0, 0));
+        const __amdgpu_buffer_rsrc_t rp = make_rsrc(pc, (uint32_t)kPrepChunkBytes);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
-            in.s[kt] = kt <= q ? *reinterpret_cast<const f32x4*>(pc + stile(q, kt) * kSTileBytes + lane * 16)
-                               : f32x4{0.f, 0.f, 0.f, 0.f};
+            in.s[kt] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rp, stile(q, min(kt, q)) * kSTileBytes + lane * 16, 0, 0));
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
             in.c[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
@@ -192,8 +193,8 @@ __global__ __launch_bounds__(256) void siso_scan_kernel(ScanArgs a) {
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int us = 0; us < 2; ++us)
-                in.bt[j][us] = *reinterpret_cast<const bf16x8*>(pc + kSTiles * kSTileBytes +
-                                                                (((2 * q + j) * 2 + us) * 64 + lane) * 16);
+                in.bt[j][us] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                              rp, kSTiles * kSTileBytes + (((2 * q + j) * 2 + us) * 64 + lane) * 16, 0, 0));
     };
 
     // ---- the state: Hf^T tiles (n-tile 2 q + j, p-tile pt), lane: column p, rows n 4 g4 .. ----
@@ -246,20 +247,24 @@ __global__ __launch_bounds__(256) void siso_scan_kernel(ScanArgs a) {
         //     their way
         *reinterpret_cast<u32x4*>(xt + (tid >> 2) * (kPS * 2) + 16 * (tid & 3)) = cur.x;
         if (q == 0) {
-            const float rate = dyn_rate ? heavy_tail_rate(cur.ra) : -ah;
+            // (branch-free: both sides of the heavy-tail law are formed, then one is taken)
+            float inv = 1.f / (1.f - fminf(cur.ra, 0.f));
+            asm volatile("" : "+v"(inv));
+            const float ht = cur.ra >= 0.f ? 1.f + cur.ra : inv;
+            const float rate = dyn_rate ? fminf(-ht, -1e-4f) : -ah;
             const float la = cur.dt * rate;
             const float gm = cur.lm * cur.dt, dl = cur.dt * (1.f - cur.lm);
             const float l = group_scan<64>(la, lane);             // inclusive
             const float le = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), 63));
             const float dnn = cur.dtn * (1.f - cur.lmn);
-            float dn = __shfl_down(dl, 1, 64);
-            if (lane == 63) dn = dnn;
+            const float dn1 = __shfl_down(dl, 1, 64);
+            const float dn = lane == 63 ? dnn : dn1;
             const float l2 = l * kLog2e, le2 = le * kLog2e;
             tb[lane] = l2;
             tb[kSQ + lane] = gm + dn;
             tb[2 * kSQ + lane] = gm;
             tb[3 * kSQ + lane] = __builtin_amdgcn_exp2f(le2 - l2) * (gm + dn);
-            if (lane == 0) tb[4 * kSQ] = le2;
+            tb[4 * kSQ] = le2;                                    // (every lane, the same value)
         }
         fetch(c + 1, nxt);
         __syncthreads();
@@ -282,9 +287,11 @@ __global__ __launch_bounds__(256) void siso_scan_kernel(ScanArgs a) {
                 float sv[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
+                    // W from 0 / 1 masks (selects of constants): no branch per lane
                     const int u = u0 + i, t = 16 * q + l16;
+                    const float below = u < t ? 1.f : 0.f, diag = u == t ? 1.f : 0.f;
                     const float e = __builtin_amdgcn_exp2f(fminf(l2t - lv[i], 0.f));
-                    const float wt = u < t ? e * g1v[i] : (u == t ? gmv[i] : 0.f);
+                    const float wt = fmaf(e * g1v[i], below, gmv[i] * diag);
                     sv[i] = kt <= q ? cur.s[kt][i] * wt : 0.f;
                 }
                 w[2 * half] = pack2(sv[0], sv[1]);
@@ -352,11 +359,13 @@ __global__ __launch_bounds__(256) void siso_scan_kernel(ScanArgs a) {
         // (5) the snapshot for the next chunk (the other buffer: this one may still be read)
         snapshot(buf ^ 1);
     };
+    // (an odd count runs one chunk more: past the sequence every input reads zero, so it
+    // leaves the state as it is and its stores are dropped)
     In ia, ib;
     fetch(0, ia);
     for (int c = 0; c < nch; c += 2) {
         chunk(c, ia, ib);
-        if (c + 1 < nch) chunk(c + 1, ib, ia);
+        chunk(c + 1, ib, ia);
     }
 
     // ---- the final carry: the state after the last token (folded with d_L = 0) ----
