@@ -27,6 +27,8 @@
 // them (a lane's four rows of each), so weighted score tiles are B operands as they stand.
 #include "scan_common.h"
 
+#include <type_traits>
+
 namespace m3 {
 
 namespace {
@@ -41,6 +43,13 @@ constexpr size_t kPrepChunkBytes = (size_t)kSTiles * kSTileBytes + kBTBytes;   /
 
 __device__ __forceinline__ int stile(int q, int kt) { return q * (q + 1) / 2 + kt; }   // kt <= q
 
+// Workgroup i of a launch runs on XCD i % 8; consecutive logical indices (one batch's score
+// tiles, and the heads of one batch that read them) are placed on the same XCD, so that
+// each XCD's L2 holds one batch's shared operands.
+__device__ __forceinline__ int xcd_logical(int bid, int nblk) {
+    return (nblk % 8 == 0) ? (bid % 8) * (nblk / 8) + bid / 8 : bid;
+}
+
 // key of slot e (0..7) of lane group g in a 32-key step
 __device__ __forceinline__ int slot_key(int g, int e) { return (e < 4 ? 4 * g : 16 + 4 * g) + (e & 3); }
 
@@ -50,7 +59,8 @@ __global__ __launch_bounds__(256) void siso_prep_kernel(ScanArgs a) {
     const int l16 = lane & 15, g4 = lane >> 4;
     const int L = a.L, G = a.G;
     const int nch = (L + kSQ - 1) / kSQ;
-    const int c = blockIdx.x % nch, bg = blockIdx.x / nch;
+    const int lb = xcd_logical(blockIdx.x, gridDim.x);
+    const int c = lb % nch, bg = lb / nch;
     const int g = bg % G, bi = bg / G;
     const int c0 = c * kSQ;
     const int nv = min(kSQ, L - c0);
@@ -96,40 +106,44 @@ __global__ __launch_bounds__(256) void siso_prep_kernel(ScanArgs a) {
     }
 }
 
-// ---- pass 2: the scan per (batch, head, half of P) ----------------------------------------
-constexpr int kPS = 32;                                    // P columns per workgroup
-constexpr int kPT = kPS / 16;                              // P tiles per workgroup
-
-// LDS: x tiles [2][64 keys][32 p] bf16 (64-byte rows), the state snapshot [2][32 p][128 n]
-// bf16 (256-byte rows, 16-byte groups swizzled by p), per-token tables [2][4][64] fp32
-constexpr int kSXBytes = kSQ * kPS * 2;                    // 4 KiB
-constexpr int kSHBytes = kPS * kN * 2;                     // 8 KiB
+// ---- pass 2: the scan per (batch, head, PS columns of P) ----------------------------------
+// LDS: x tiles [2][64 keys][PS p] bf16, the state snapshot [2][PS p][128 n] bf16 (256-byte
+// rows, 16-byte groups swizzled by p), per-token tables [2][4][64] fp32
 constexpr int kSTBytes = 4 * kSQ * 4 + 16;                 // l2, g1, gam, v; then l2 at the chunk end
-constexpr int kSiLds = 2 * kSXBytes + 2 * kSHBytes + 2 * kSTBytes;
+template <int PS>
+constexpr int siso_lds() { return 2 * kSQ * PS * 2 + 2 * PS * kN * 2 + 2 * kSTBytes; }
 
 __device__ __forceinline__ int sh_off(int p, int grp) { return p * 256 + ((grp ^ (p & 15)) << 4); }
 
 // the x operand (column p = c0 + lane % 16, the 32-key step us in slot order) from a row-major
-// x tile by transposed reads: lane s of a 16-lane group points at key row kb + s / 4, columns
-// c0 + 4 (s % 4) .. + 3, and receives column c0 + s at keys kb .. kb + 3
+// x tile of PS columns by transposed reads: lane s of a 16-lane group points at key row
+// kb + s / 4, columns c0 + 4 (s % 4) .. + 3, and receives column c0 + s at keys kb .. kb + 3
+template <int PS>
 __device__ __forceinline__ bf16x8 x_operand(const char* tile, int c0, int us, int lane) {
     const int g = lane >> 4, s = lane & 15;
     const int kr = 32 * us + 4 * g + (s >> 2);
     const int col = c0 + 4 * (s & 3);
-    const uint2 lo = ds_tr(tile + kr * (kPS * 2) + col * 2);
-    const uint2 hi = ds_tr(tile + (kr + 16) * (kPS * 2) + col * 2);
+    const uint2 lo = ds_tr(tile + kr * (PS * 2) + col * 2);
+    const uint2 hi = ds_tr(tile + (kr + 16) * (PS * 2) + col * 2);
     return __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
 }
 
+// PS = 32 (halves of P) or 16 (quarters: twice the workgroups, for few streams)
+template <int PS>
 __global__ __launch_bounds__(256) void siso_scan_kernel(ScanArgs a) {
+    constexpr int kPS = PS, kPT = PS / 16;
+    constexpr int kSXBytes = kSQ * kPS * 2, kSHBytes = kPS * kN * 2;
+    constexpr int kXB = kPS / 2;                               // bytes of the x tile per thread
+    typedef typename std::conditional<kXB == 16, u32x4, u32x2>::type XPiece;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int q = __builtin_amdgcn_readfirstlane(tid >> 6);    // query tile, and state columns 32 q ..
     const int l16 = lane & 15, g4 = lane >> 4;
     const int L = a.L, H = a.H, G = a.G;
     const int nch = (L + kSQ - 1) / kSQ;
-    const int ph = blockIdx.x % (kP / kPS);
-    const int bh = blockIdx.x / (kP / kPS);
+    const int lb = xcd_logical(blockIdx.x, gridDim.x);
+    const int ph = lb % (kP / kPS);
+    const int bh = lb / (kP / kPS);
     const int h = bh % H, bi = bh / H;
     const int g = h * G / H;
     const int p0 = ph * kPS;
@@ -159,7 +173,7 @@ __global__ __launch_bounds__(256) void siso_scan_kernel(ScanArgs a) {
 
     // ---- the chunk's inputs, a chunk ahead ----
     struct In {
-        u32x4 x;                 // 16 bytes of the x tile: key tid / 4, columns 8 (tid % 4) ..
+        XPiece x;                // kXB bytes of the x tile: key tid / 4, bytes kXB (tid % 4) ..
         float dt, lm, ra;        // wave 0: token c0 + lane (dt, lambda, rate input)
         float dtn, lmn;          // wave 0: the token after the chunk
         f32x4 s[4];              // score tiles kt = 0 .. q of query tile q
@@ -172,7 +186,9 @@ __global__ __launch_bounds__(256) void siso_scan_kernel(ScanArgs a) {
         // (every load unconditional, so that each wait counts exactly the later ones: the
         // scalars are loaded by every wave, only wave 0 uses them; tiles past the diagonal
         // read the diagonal tile again, and the weights zero them)
-        in.x = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((c0 + (tid >> 2)) * xrow + 16 * (tid & 3)), 0, 0);
+        const int xo = (int)((c0 + (tid >> 2)) * xrow + kXB * (tid & 3));
+        if constexpr (kXB == 16) in.x = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0);
+        else in.x = __builtin_amdgcn_raw_buffer_load_b64(rx, xo, 0, 0);
         const int o = (c0 + lane) * H * 4;
         in.dt = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdt, o, 0, 0));
         in.lm = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rlm, o, 0, 0));
@@ -245,7 +261,7 @@ __global__ __launch_bounds__(256) void siso_scan_kernel(ScanArgs a) {
         float* const tb = sT + buf * kTF;
         // (1) this chunk's x tile and per-token tables into LDS; the next chunk's inputs on
         //     their way
-        *reinterpret_cast<u32x4*>(xt + (tid >> 2) * (kPS * 2) + 16 * (tid & 3)) = cur.x;
+        *reinterpret_cast<XPiece*>(xt + (tid >> 2) * (kPS * 2) + kXB * (tid & 3)) = cur.x;
         if (q == 0) {
             // (branch-free: both sides of the heavy-tail law are formed, then one is taken)
             float inv = 1.f / (1.f - fminf(cur.ra, 0.f));
@@ -317,7 +333,7 @@ __global__ __launch_bounds__(256) void siso_scan_kernel(ScanArgs a) {
 #pragma unroll
         for (int pt = 0; pt < kPT; ++pt)
 #pragma unroll
-            for (int us = 0; us < 2; ++us) xo[pt][us] = x_operand(xt, 16 * pt, us, lane);
+            for (int us = 0; us < 2; ++us) xo[pt][us] = x_operand<kPS>(xt, 16 * pt, us, lane);
 #pragma unroll
         for (int pt = 0; pt < kPT; ++pt)
 #pragma unroll
@@ -406,16 +422,22 @@ size_t scan_siso_workspace_bytes(const ScanArgs& a) {
     return (size_t)a.b * a.G * nch * kPrepChunkBytes;
 }
 
+template <int PS>
+hipError_t launch_siso_scan(const ScanArgs& a, hipStream_t st) {
+    constexpr int lds = siso_lds<PS>();
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&siso_scan_kernel<PS>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(siso_scan_kernel<PS>, dim3((unsigned)((size_t)a.b * a.H * (kP / PS))), dim3(256), lds, st, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_scan_siso(const ScanArgs& a, hipStream_t st) {
     const int nch = (a.L + kSQ - 1) / kSQ;
     hipLaunchKernelGGL(siso_prep_kernel, dim3((unsigned)((size_t)a.b * a.G * nch)), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&siso_scan_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            kSiLds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(siso_scan_kernel, dim3((unsigned)((size_t)a.b * a.H * (kP / kPS))), dim3(256), kSiLds, st, a);
-    return hipGetLastError();
+    return launch_siso_scan<32>(a, st);
 }
 
 }  // namespace m3

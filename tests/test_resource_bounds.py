@@ -187,6 +187,8 @@ def siso_path(R, Q, np_, bias):
 def replay_siso(b, L, H, G):
     """The score pass (per batch, group and chunk) and the scan (per batch, head and half
     of P; every chunk, and the inputs it fetches one chunk past the last)."""
+    PS = 32
+    xb = PS // 2                                      # bytes of the x tile per thread
     nch = -(-L // 64)
     lanes = np.arange(64)
     l16, g4 = lanes & 15, lanes >> 4
@@ -213,19 +215,19 @@ def replay_siso(b, L, H, G):
         for h in sorted({0, H - 1}):
             g = h * G // H
             tok0 = bi * L
-            for ph in (0, 1):
-                p0 = 32 * ph
+            for ph in range(KP // PS):
+                p0 = PS * ph
                 xbase = ((tok0 * H + h) * KP + p0) * 2
-                xrec = (L - 1) * xrow + 64
+                xrec = (L - 1) * xrow + PS * 2
                 cbase = (tok0 * G + g) * KN * 2
                 crec = (L - 1) * rowb + KN * 2
                 tbase = (tok0 * H + h) * 4
                 trec = ((L - 1) * H + 1) * 4
                 for c in sorted({0, max(0, nch - 1), nch}):
                     c0 = c * 64
-                    _check("siso x", xbase, xrec, (c0 + (tids >> 2)) * xrow + 16 * (tids & 3), 16, X_bytes)
+                    _check("siso x", xbase, xrec, (c0 + (tids >> 2)) * xrow + xb * (tids & 3), xb, X_bytes)
                     for q in range(4):
-                        yo = [(c0 + 16 * q + l16) * xrow + (16 * pt + 4 * g4) * 2 for pt in range(2)]
+                        yo = [(c0 + 16 * q + l16) * xrow + (16 * pt + 4 * g4) * 2 for pt in range(PS // 16)]
                         _check("siso y", xbase, xrec, np.stack(yo), 8, X_bytes)
                         co = [(c0 + 16 * q + l16) * rowb + (32 * ks + 8 * g4) * 2 for ks in range(4)]
                         _check("siso C", cbase, crec, np.stack(co), 16, BC_bytes)
