@@ -27,7 +27,6 @@
 // them (a lane's four rows of each), so weighted score tiles are B operands as they stand.
 #include "scan_common.h"
 
-#include <type_traits>
 
 namespace m3 {
 
@@ -106,41 +105,48 @@ __global__ __launch_bounds__(256) void siso_prep_kernel(ScanArgs a) {
     }
 }
 
-// ---- pass 2: the scan per (batch, head, PS columns of P) ----------------------------------
-// LDS: x tiles [2][64 keys][PS p] bf16, the state snapshot [2][PS p][128 n] bf16 (256-byte
-// rows, 16-byte groups swizzled by p), per-token tables [2][4][64] fp32
+// ---- pass 2: the scan per (batch, head, half of P) ----------------------------------------
+// Eight waves in two roles, so that each SIMD holds one of each and their dependency chains
+// overlap instead of adding up:
+//   * output waves 0-3 (wave q: query tile q): weight the score tiles, the carry readout
+//     from the state snapshot, Y^T += X^T S'^T, the output stores;
+//   * state waves 4-7 (wave 4 + q: the state's n-tiles 2 q, 2 q + 1, both P tiles): the
+//     state update Hf^T = exp(l_e) Hf^T + B^T (v x) and its bf16 snapshot for the next
+//     chunk's readout; wave 4 also scans the next chunk's decays into the token tables.
+// LDS: x tiles [2][64 keys][32 p] bf16 (64-byte rows), the state snapshot [2][32 p][128 n]
+// bf16 (256-byte rows, 16-byte groups swizzled by p), token tables [2][4][64] fp32 + the
+// chunk's total log-decay.  One barrier per chunk.
+constexpr int kPS = 32;                                    // P columns per workgroup
+constexpr int kSXBytes = kSQ * kPS * 2;                    // 4 KiB
+constexpr int kSHBytes = kPS * kN * 2;                     // 8 KiB
 constexpr int kSTBytes = 4 * kSQ * 4 + 16;                 // l2, g1, gam, v; then l2 at the chunk end
-template <int PS>
-constexpr int siso_lds() { return 2 * kSQ * PS * 2 + 2 * PS * kN * 2 + 2 * kSTBytes; }
+constexpr int kSiLds = 2 * kSXBytes + 2 * kSHBytes + 2 * kSTBytes;
+constexpr int kSiThreads = 512;
 
 __device__ __forceinline__ int sh_off(int p, int grp) { return p * 256 + ((grp ^ (p & 15)) << 4); }
 
 // the x operand (column p = c0 + lane % 16, the 32-key step us in slot order) from a row-major
-// x tile of PS columns by transposed reads: lane s of a 16-lane group points at key row
-// kb + s / 4, columns c0 + 4 (s % 4) .. + 3, and receives column c0 + s at keys kb .. kb + 3
-template <int PS>
+// x tile by transposed reads: lane s of a 16-lane group points at key row kb + s / 4, columns
+// c0 + 4 (s % 4) .. + 3, and receives column c0 + s at keys kb .. kb + 3
 __device__ __forceinline__ bf16x8 x_operand(const char* tile, int c0, int us, int lane) {
     const int g = lane >> 4, s = lane & 15;
     const int kr = 32 * us + 4 * g + (s >> 2);
     const int col = c0 + 4 * (s & 3);
-    const uint2 lo = ds_tr(tile + kr * (PS * 2) + col * 2);
-    const uint2 hi = ds_tr(tile + (kr + 16) * (PS * 2) + col * 2);
+    const uint2 lo = ds_tr(tile + kr * (kPS * 2) + col * 2);
+    const uint2 hi = ds_tr(tile + (kr + 16) * (kPS * 2) + col * 2);
     return __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
 }
 
-// PS = 32 (halves of P) or 16 (quarters: twice the workgroups, for few streams)
-template <int PS>
-__global__ __launch_bounds__(256) void siso_scan_kernel(ScanArgs a) {
-    constexpr int kPS = PS, kPT = PS / 16;
-    constexpr int kSXBytes = kSQ * kPS * 2, kSHBytes = kPS * kN * 2;
-    constexpr int kXB = kPS / 2;                               // bytes of the x tile per thread
-    typedef typename std::conditional<kXB == 16, u32x4, u32x2>::type XPiece;
+__global__ __launch_bounds__(kSiThreads) void siso_scan_kernel(ScanArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, lane = tid & 63;
-    const int q = __builtin_amdgcn_readfirstlane(tid >> 6);    // query tile, and state columns 32 q ..
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool state_role = w >= 4;
+    const int q = w & 3;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int L = a.L, H = a.H, G = a.G;
     const int nch = (L + kSQ - 1) / kSQ;
+    const int nloop = (nch + 1) & ~1;                          // (an even count: see below)
     const int lb = xcd_logical(blockIdx.x, gridDim.x);
     const int ph = lb % (kP / kPS);
     const int bh = lb / (kP / kPS);
@@ -151,60 +157,143 @@ __global__ __launch_bounds__(256) void siso_scan_kernel(ScanArgs a) {
     const float ah = dyn_rate ? 0.f : expf(a.A_log[h]);
 
     // buffer resources over the whole (batch, head) stream; tokens at or past L read zero
-    // and their stores are dropped (the host keeps every offset below 2^31)
+    // and their stores are dropped (the host keeps every offset below 2^31).  A chunk past
+    // the sequence (the loop runs an even count) reads zero everywhere: dt = 0 leaves the
+    // state as it is, and its stores are dropped.
     const uint32_t xrow = (uint32_t)H * kP * 2u, brow = (uint32_t)G * kN * 2u;
     const size_t tok0 = (size_t)bi * L;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const uint16_t*>(a.x) + (tok0 * H + h) * kP + p0,
                                                 (uint32_t)(L - 1) * xrow + kPS * 2);
-    const __amdgpu_buffer_rsrc_t ry = make_rsrc(static_cast<uint16_t*>(a.y) + (tok0 * H + h) * kP + p0,
-                                                (uint32_t)(L - 1) * xrow + kPS * 2);
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(static_cast<const uint16_t*>(a.C) + (tok0 * G + g) * kN,
-                                                (uint32_t)(L - 1) * brow + kN * 2);
-    const __amdgpu_buffer_rsrc_t rdt = make_rsrc(a.dt + tok0 * H + h, (uint32_t)((L - 1) * H + 1) * 4u);
-    const __amdgpu_buffer_rsrc_t rlm = make_rsrc(a.lam + tok0 * H + h, (uint32_t)((L - 1) * H + 1) * 4u);
-    // (static rates: the rate loads read dt again, unused)
-    const __amdgpu_buffer_rsrc_t rra = dyn_rate ? make_rsrc(a.A_log + tok0 * H + h, (uint32_t)((L - 1) * H + 1) * 4u) : rdt;
     const char* const prep = reinterpret_cast<const char*>(a.ws) + ((size_t)bi * G + g) * nch * kPrepChunkBytes;
+    auto prep_rsrc = [&](int c) { return make_rsrc(prep + (size_t)min(c, nch - 1) * kPrepChunkBytes, (uint32_t)kPrepChunkBytes); };
 
     char* const sX = smem;
     char* const sH = smem + 2 * kSXBytes;
     float* const sT = reinterpret_cast<float*>(smem + 2 * kSXBytes + 2 * kSHBytes);
     constexpr int kTF = kSTBytes / 4;                          // floats per table set
 
-    // ---- the chunk's inputs, a chunk ahead ----
+    // every wave: 8 bytes of the chunk's x tile (key tid / 8, bytes 8 (tid % 8) ..)
+    auto fetch_x = [&](int c) -> u32x2 {
+        return __builtin_amdgcn_raw_buffer_load_b64(rx, (int)((c * kSQ + (tid >> 3)) * xrow + 8 * (tid & 7)), 0, 0);
+    };
+    auto stage_x = [&](int c, const u32x2& v) {
+        *reinterpret_cast<u32x2*>(sX + (c & 1) * kSXBytes + (tid >> 3) * (kPS * 2) + 8 * (tid & 7)) = v;
+    };
+
+    if (!state_role) {
+        // =========================== output waves ===========================
+        const __amdgpu_buffer_rsrc_t ry = make_rsrc(static_cast<uint16_t*>(a.y) + (tok0 * H + h) * kP + p0,
+                                                    (uint32_t)(L - 1) * xrow + kPS * 2);
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(static_cast<const uint16_t*>(a.C) + (tok0 * G + g) * kN,
+                                                    (uint32_t)(L - 1) * brow + kN * 2);
+        struct In {
+            u32x2 x;
+            f32x4 s[4];          // score tiles kt = 0 .. q of query tile q (past q: the diagonal again)
+            bf16x8 c[4];         // C rows of query tile q (B operands, k = n)
+        };
+        auto fetch = [&](int c, In& in) {
+            const int c0 = c * kSQ;
+            in.x = fetch_x(c);
+            const __amdgpu_buffer_rsrc_t rp = prep_rsrc(c);
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+                in.s[kt] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        rp, stile(q, min(kt, q)) * kSTileBytes + lane * 16, 0, 0));
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                in.c[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          rc, (int)((c0 + 16 * q + l16) * brow + (32 * ks + 8 * g4) * 2), 0, 0));
+        };
+        auto chunk = [&](int c, In& cur, In& nxt) {
+            const int buf = c & 1, c0 = c * kSQ;
+            const char* const xt = sX + buf * kSXBytes;
+            const float* const tb = sT + buf * kTF;
+            stage_x(c, cur.x);
+            fetch(c + 1, nxt);
+            __syncthreads();
+            // weights: S'^T(u, t) = S^T(u, t) W(t, u), lane: column t = 16 q + l16, rows u
+            const float l2t = tb[16 * q + l16];
+            bf16x8 sop[2];
+#pragma unroll
+            for (int us = 0; us < 2; ++us) {
+                uint32_t wv[4];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int kt = 2 * us + half;
+                    const int u0 = 16 * kt + 4 * g4;
+                    const float4 lu = *reinterpret_cast<const float4*>(tb + u0);
+                    const float4 g1 = *reinterpret_cast<const float4*>(tb + kSQ + u0);
+                    const float4 gm = *reinterpret_cast<const float4*>(tb + 2 * kSQ + u0);
+                    const float lv[4] = {lu.x, lu.y, lu.z, lu.w}, g1v[4] = {g1.x, g1.y, g1.z, g1.w},
+                                gmv[4] = {gm.x, gm.y, gm.z, gm.w};
+                    float sv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        // W from 0 / 1 masks (selects of constants): no branch per lane
+                        const int u = u0 + i, t = 16 * q + l16;
+                        const float below = u < t ? 1.f : 0.f, diag = u == t ? 1.f : 0.f;
+                        const float e = __builtin_amdgcn_exp2f(fminf(l2t - lv[i], 0.f));
+                        const float wt = fmaf(e * g1v[i], below, gmv[i] * diag);
+                        sv[i] = kt <= q ? cur.s[kt][i] * wt : 0.f;
+                    }
+                    wv[2 * half] = pack2(sv[0], sv[1]);
+                    wv[2 * half + 1] = pack2(sv[2], sv[3]);
+                }
+                sop[us] = __builtin_bit_cast(bf16x8, uint4{wv[0], wv[1], wv[2], wv[3]});
+            }
+            // Y^T (p-tile pt, lane: column t, rows p 4 g4 ..) = exp(l_t) Hf C^T + X^T S'^T
+            const char* const hsn = sH + buf * kSHBytes;
+            const float sc = __builtin_amdgcn_exp2f(l2t);
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) {
+                f32x4 r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const bf16x8 hop = *reinterpret_cast<const bf16x8*>(hsn + sh_off(16 * pt + l16, 4 * ks + g4));
+                    r = mfma(hop, cur.c[ks], r);
+                }
+                f32x4 y = {r[0] * sc, r[1] * sc, r[2] * sc, r[3] * sc};
+#pragma unroll
+                for (int us = 0; us < 2; ++us)
+                    if (2 * us <= q) y = mfma(x_operand(xt, 16 * pt, us, lane), sop[us], y);
+                // 4 consecutive p of token t per lane (rows of tokens past L are dropped)
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])}, ry,
+                                                      (int)((c0 + 16 * q + l16) * xrow + (16 * pt + 4 * g4) * 2), 0, 0);
+            }
+        };
+        In ia, ib;
+        fetch(0, ia);
+        for (int c = 0; c < nloop; c += 2) {
+            chunk(c, ia, ib);
+            chunk(c + 1, ib, ia);
+        }
+        return;
+    }
+
+    // =========================== state waves ===========================
+    const __amdgpu_buffer_rsrc_t rdt = make_rsrc(a.dt + tok0 * H + h, (uint32_t)((L - 1) * H + 1) * 4u);
+    const __amdgpu_buffer_rsrc_t rlm = make_rsrc(a.lam + tok0 * H + h, (uint32_t)((L - 1) * H + 1) * 4u);
+    // (static rates: the rate loads read dt again, unused)
+    const __amdgpu_buffer_rsrc_t rra = dyn_rate ? make_rsrc(a.A_log + tok0 * H + h, (uint32_t)((L - 1) * H + 1) * 4u) : rdt;
     struct In {
-        XPiece x;                // kXB bytes of the x tile: key tid / 4, bytes kXB (tid % 4) ..
-        float dt, lm, ra;        // wave 0: token c0 + lane (dt, lambda, rate input)
-        float dtn, lmn;          // wave 0: the token after the chunk
-        f32x4 s[4];              // score tiles kt = 0 .. q of query tile q
-        bf16x8 c[4];             // C rows of query tile q (B operands, k = n)
+        u32x2 x;
+        float dt, lm, ra;        // token 64 (c + 1) + lane: the next chunk's (dt, lambda, rate input)
+        float dtn, lmn;          // the token after the next chunk
         bf16x8 bt[2][2];         // B^T operands of n-tiles 2 q + j, key steps us
     };
-    auto fetch = [&](int c, In& in) {
-        const int c0 = c * kSQ;
-        const char* pc = prep + (size_t)min(c, nch - 1) * kPrepChunkBytes;   // (past the last chunk: unused)
-        // (every load unconditional, so that each wait counts exactly the later ones: the
-        // scalars are loaded by every wave, only wave 0 uses them; tiles past the diagonal
-        // read the diagonal tile again, and the weights zero them)
-        const int xo = (int)((c0 + (tid >> 2)) * xrow + kXB * (tid & 3));
-        if constexpr (kXB == 16) in.x = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0);
-        else in.x = __builtin_amdgcn_raw_buffer_load_b64(rx, xo, 0, 0);
-        const int o = (c0 + lane) * H * 4;
+    // the scalars of chunk cs (the wave that scans them is a chunk ahead of the rest)
+    auto fetch_scalars = [&](int cs, In& in) {
+        const int o = (cs * kSQ + lane) * H * 4, on = (cs * kSQ + kSQ) * H * 4;
         in.dt = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdt, o, 0, 0));
         in.lm = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rlm, o, 0, 0));
         in.ra = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rra, o, 0, 0));
-        const int on = (c0 + kSQ) * H * 4;
         in.dtn = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdt, on, 0, 0));
         in.lmn = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rlm, on, 0, 0));
-        const __amdgpu_buffer_rsrc_t rp = make_rsrc(pc, (uint32_t)kPrepChunkBytes);
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-            in.s[kt] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    rp, stile(q, min(kt, q)) * kSTileBytes + lane * 16, 0, 0));
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            in.c[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      rc, (int)((c0 + 16 * q + l16) * brow + (32 * ks + 8 * g4) * 2), 0, 0));
+    };
+    auto fetch = [&](int c, In& in) {
+        in.x = fetch_x(c);
+        fetch_scalars(c + 1, in);
+        const __amdgpu_buffer_rsrc_t rp = prep_rsrc(c);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -212,16 +301,38 @@ __global__ __launch_bounds__(256) void siso_scan_kernel(ScanArgs a) {
                 in.bt[j][us] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
                                                               rp, kSTiles * kSTileBytes + (((2 * q + j) * 2 + us) * 64 + lane) * 16, 0, 0));
     };
+    // the token tables of a chunk into set tset (wave 4 only; every lane one token)
+    auto tables = [&](const In& in, int tset) {
+        float* const tb = sT + tset * kTF;
+        // (branch-free: both sides of the heavy-tail law are formed, then one is taken)
+        float inv = 1.f / (1.f - fminf(in.ra, 0.f));
+        asm volatile("" : "+v"(inv));
+        const float ht = in.ra >= 0.f ? 1.f + in.ra : inv;
+        const float rate = dyn_rate ? fminf(-ht, -1e-4f) : -ah;
+        const float la = in.dt * rate;
+        const float gm = in.lm * in.dt, dl = in.dt * (1.f - in.lm);
+        const float l = group_scan<64>(la, lane);                 // inclusive
+        const float le = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), 63));
+        const float dnn = in.dtn * (1.f - in.lmn);
+        const float dn1 = __shfl_down(dl, 1, 64);
+        const float dn = lane == 63 ? dnn : dn1;
+        const float l2 = l * kLog2e, le2 = le * kLog2e;
+        tb[lane] = l2;
+        tb[kSQ + lane] = gm + dn;
+        tb[2 * kSQ + lane] = gm;
+        tb[3 * kSQ + lane] = __builtin_amdgcn_exp2f(le2 - l2) * (gm + dn);
+        tb[4 * kSQ] = le2;                                        // (every lane, the same value)
+    };
 
-    // ---- the state: Hf^T tiles (n-tile 2 q + j, p-tile pt), lane: column p, rows n 4 g4 .. ----
-    f32x4 hs[2][kPT];
+    // the state: Hf^T tiles (n-tile 2 q + j, p-tile pt), lane: column p, rows n 4 g4 ..
+    f32x4 hs[2][2];
     {
         float d0 = 0.f;
         if (a.Bp0 && a.xp0) d0 = a.dt[tok0 * H + h] * (1.f - a.lam[tok0 * H + h]);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int pt = 0; pt < kPT; ++pt) {
+            for (int pt = 0; pt < 2; ++pt) {
                 const int p = p0 + 16 * pt + l16, n = 16 * (2 * q + j) + 4 * g4;
                 f32x4 v = {0.f, 0.f, 0.f, 0.f};
                 if (a.h0) {
@@ -239,147 +350,63 @@ __global__ __launch_bounds__(256) void siso_scan_kernel(ScanArgs a) {
             }
     }
     // snapshot of the state at a chunk's start (bf16, row p, 16-byte groups swizzled)
-    auto snapshot = [&](int buf) {
-        char* dst = sH + buf * kSHBytes;
+    auto snapshot = [&](int sbuf) {
+        char* dst = sH + sbuf * kSHBytes;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int pt = 0; pt < kPT; ++pt) {
+            for (int pt = 0; pt < 2; ++pt) {
                 const int p = 16 * pt + l16, n = 16 * (2 * q + j) + 4 * g4;
                 *reinterpret_cast<uint2*>(dst + sh_off(p, n >> 3) + (n & 7) * 2) =
                     uint2{pack2(hs[j][pt][0], hs[j][pt][1]), pack2(hs[j][pt][2], hs[j][pt][3])};
             }
     };
     snapshot(0);
-
-    // chunk c from the inputs in cur; the next chunk's inputs into nxt (the two register sets
-    // trade roles from chunk to chunk, so no copy waits for loads in flight)
+    {
+        In i0;
+        fetch_scalars(0, i0);
+        if (q == 0) tables(i0, 0);
+    }
     auto chunk = [&](int c, In& cur, In& nxt) {
         const int buf = c & 1;
-        const int c0 = c * kSQ;
-        char* const xt = sX + buf * kSXBytes;
-        float* const tb = sT + buf * kTF;
-        // (1) this chunk's x tile and per-token tables into LDS; the next chunk's inputs on
-        //     their way
-        *reinterpret_cast<XPiece*>(xt + (tid >> 2) * (kPS * 2) + kXB * (tid & 3)) = cur.x;
-        if (q == 0) {
-            // (branch-free: both sides of the heavy-tail law are formed, then one is taken)
-            float inv = 1.f / (1.f - fminf(cur.ra, 0.f));
-            asm volatile("" : "+v"(inv));
-            const float ht = cur.ra >= 0.f ? 1.f + cur.ra : inv;
-            const float rate = dyn_rate ? fminf(-ht, -1e-4f) : -ah;
-            const float la = cur.dt * rate;
-            const float gm = cur.lm * cur.dt, dl = cur.dt * (1.f - cur.lm);
-            const float l = group_scan<64>(la, lane);             // inclusive
-            const float le = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), 63));
-            const float dnn = cur.dtn * (1.f - cur.lmn);
-            const float dn1 = __shfl_down(dl, 1, 64);
-            const float dn = lane == 63 ? dnn : dn1;
-            const float l2 = l * kLog2e, le2 = le * kLog2e;
-            tb[lane] = l2;
-            tb[kSQ + lane] = gm + dn;
-            tb[2 * kSQ + lane] = gm;
-            tb[3 * kSQ + lane] = __builtin_amdgcn_exp2f(le2 - l2) * (gm + dn);
-            tb[4 * kSQ] = le2;                                    // (every lane, the same value)
-        }
+        const char* const xt = sX + buf * kSXBytes;
+        const float* const tb = sT + buf * kTF;
+        stage_x(c, cur.x);
         fetch(c + 1, nxt);
         __syncthreads();
-
-        // (2) weights: S'^T(u, t) = S^T(u, t) W(t, u), lane: column t = 16 q + l16, rows u
-        const float l2t = tb[16 * q + l16];
-        bf16x8 sop[2];
-#pragma unroll
-        for (int us = 0; us < 2; ++us) {
-            uint32_t w[4];
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int kt = 2 * us + half;
-                const int u0 = 16 * kt + 4 * g4;
-                const float4 lu = *reinterpret_cast<const float4*>(tb + u0);
-                const float4 g1 = *reinterpret_cast<const float4*>(tb + kSQ + u0);
-                const float4 gm = *reinterpret_cast<const float4*>(tb + 2 * kSQ + u0);
-                const float lv[4] = {lu.x, lu.y, lu.z, lu.w}, g1v[4] = {g1.x, g1.y, g1.z, g1.w},
-                            gmv[4] = {gm.x, gm.y, gm.z, gm.w};
-                float sv[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    // W from 0 / 1 masks (selects of constants): no branch per lane
-                    const int u = u0 + i, t = 16 * q + l16;
-                    const float below = u < t ? 1.f : 0.f, diag = u == t ? 1.f : 0.f;
-                    const float e = __builtin_amdgcn_exp2f(fminf(l2t - lv[i], 0.f));
-                    const float wt = fmaf(e * g1v[i], below, gmv[i] * diag);
-                    sv[i] = kt <= q ? cur.s[kt][i] * wt : 0.f;
-                }
-                w[2 * half] = pack2(sv[0], sv[1]);
-                w[2 * half + 1] = pack2(sv[2], sv[3]);
-            }
-            sop[us] = __builtin_bit_cast(bf16x8, uint4{w[0], w[1], w[2], w[3]});
-        }
-        // (3) Y^T (p-tile pt, lane: column t, rows p 4 g4 ..) = exp(l_t) Hf C^T + X^T S'^T
-        const char* const hsn = sH + buf * kSHBytes;
-        f32x4 yacc[kPT];
-#pragma unroll
-        for (int pt = 0; pt < kPT; ++pt) {
-            f32x4 r = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 hop = *reinterpret_cast<const bf16x8*>(hsn + sh_off(16 * pt + l16, 4 * ks + g4));
-                r = mfma(hop, cur.c[ks], r);
-            }
-            const float sc = __builtin_amdgcn_exp2f(l2t);
-            yacc[pt] = f32x4{r[0] * sc, r[1] * sc, r[2] * sc, r[3] * sc};
-        }
-        bf16x8 xo[kPT][2];
-#pragma unroll
-        for (int pt = 0; pt < kPT; ++pt)
-#pragma unroll
-            for (int us = 0; us < 2; ++us) xo[pt][us] = x_operand<kPS>(xt, 16 * pt, us, lane);
-#pragma unroll
-        for (int pt = 0; pt < kPT; ++pt)
-#pragma unroll
-            for (int us = 0; us < 2; ++us)
-                if (2 * us <= q) yacc[pt] = mfma(xo[pt][us], sop[us], yacc[pt]);
-        // outputs: 4 consecutive p of token t per lane (rows of tokens past L are dropped)
-#pragma unroll
-        for (int pt = 0; pt < kPT; ++pt)
-            __builtin_amdgcn_raw_buffer_store_b64(
-                u32x2{pack2(yacc[pt][0], yacc[pt][1]), pack2(yacc[pt][2], yacc[pt][3])}, ry,
-                (int)((c0 + 16 * q + l16) * xrow + (16 * pt + 4 * g4) * 2), 0, 0);
-        // (4) the state: Hf^T = exp(l_e) Hf^T + B^T (v x), the B operand x scaled by v per key
+        // Hf^T = exp(l_e) Hf^T + B^T (v x), the B operand x scaled by v per key
         const float fe = __builtin_amdgcn_exp2f(tb[4 * kSQ]);
-        bf16x8 vx[kPT][2];
 #pragma unroll
-        for (int us = 0; us < 2; ++us) {
-            const float4 va = *reinterpret_cast<const float4*>(tb + 3 * kSQ + 32 * us + 4 * g4);
-            const float4 vb = *reinterpret_cast<const float4*>(tb + 3 * kSQ + 32 * us + 16 + 4 * g4);
-            const float vv[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+        for (int pt = 0; pt < 2; ++pt) {
+            bf16x8 vx[2];
 #pragma unroll
-            for (int pt = 0; pt < kPT; ++pt) {
-                const uint4 raw = __builtin_bit_cast(uint4, xo[pt][us]);
+            for (int us = 0; us < 2; ++us) {
+                const float4 va = *reinterpret_cast<const float4*>(tb + 3 * kSQ + 32 * us + 4 * g4);
+                const float4 vb = *reinterpret_cast<const float4*>(tb + 3 * kSQ + 32 * us + 16 + 4 * g4);
+                const float vv[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+                const uint4 raw = __builtin_bit_cast(uint4, x_operand(xt, 16 * pt, us, lane));
                 const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
                 uint32_t o[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) o[k] = pack2(lo_f(rw[k]) * vv[2 * k], hi_f(rw[k]) * vv[2 * k + 1]);
-                vx[pt][us] = __builtin_bit_cast(bf16x8, uint4{o[0], o[1], o[2], o[3]});
+                vx[us] = __builtin_bit_cast(bf16x8, uint4{o[0], o[1], o[2], o[3]});
             }
-        }
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int pt = 0; pt < kPT; ++pt) {
+            for (int j = 0; j < 2; ++j) {
                 f32x4 v = {hs[j][pt][0] * fe, hs[j][pt][1] * fe, hs[j][pt][2] * fe, hs[j][pt][3] * fe};
 #pragma unroll
-                for (int us = 0; us < 2; ++us) v = mfma(cur.bt[j][us], vx[pt][us], v);
+                for (int us = 0; us < 2; ++us) v = mfma(cur.bt[j][us], vx[us], v);
                 hs[j][pt] = v;
             }
-        // (5) the snapshot for the next chunk (the other buffer: this one may still be read)
+        }
+        // the snapshot for the next chunk (the other buffer: this one may still be read), and
+        // the next chunk's tables (the other set: this one may still be read)
         snapshot(buf ^ 1);
+        if (q == 0) tables(cur, buf ^ 1);
     };
-    // (an odd count runs one chunk more: past the sequence every input reads zero, so it
-    // leaves the state as it is and its stores are dropped)
     In ia, ib;
     fetch(0, ia);
-    for (int c = 0; c < nch; c += 2) {
+    for (int c = 0; c < nloop; c += 2) {
         chunk(c, ia, ib);
         chunk(c + 1, ib, ia);
     }
@@ -389,20 +416,21 @@ __global__ __launch_bounds__(256) void siso_scan_kernel(ScanArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int pt = 0; pt < kPT; ++pt) {
+            for (int pt = 0; pt < 2; ++pt) {
                 const int p = p0 + 16 * pt + l16, n = 16 * (2 * q + j) + 4 * g4;
                 *reinterpret_cast<float4*>(static_cast<float*>(a.h1) + ((size_t)bh * kP + p) * kN + n) =
                     float4{hs[j][pt][0], hs[j][pt][1], hs[j][pt][2], hs[j][pt][3]};
             }
     }
     if (a.Bp1 && a.xp1) {
+        const int st = tid - 256;                                  // state-wave thread index
         const size_t t = tok0 + L - 1;
-        if (ph == 0 && tid < kN)
-            static_cast<uint16_t*>(a.Bp1)[(size_t)bh * kN + tid] =
-                static_cast<const uint16_t*>(a.B)[(t * G + g) * kN + tid];
-        if (tid < kPS)
-            static_cast<uint16_t*>(a.xp1)[(size_t)bh * kP + p0 + tid] =
-                static_cast<const uint16_t*>(a.x)[(t * H + h) * kP + p0 + tid];
+        if (ph == 0 && st < kN)
+            static_cast<uint16_t*>(a.Bp1)[(size_t)bh * kN + st] =
+                static_cast<const uint16_t*>(a.B)[(t * G + g) * kN + st];
+        if (st < kPS)
+            static_cast<uint16_t*>(a.xp1)[(size_t)bh * kP + p0 + st] =
+                static_cast<const uint16_t*>(a.x)[(t * H + h) * kP + p0 + st];
     }
 }
 
@@ -422,22 +450,16 @@ size_t scan_siso_workspace_bytes(const ScanArgs& a) {
     return (size_t)a.b * a.G * nch * kPrepChunkBytes;
 }
 
-template <int PS>
-hipError_t launch_siso_scan(const ScanArgs& a, hipStream_t st) {
-    constexpr int lds = siso_lds<PS>();
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&siso_scan_kernel<PS>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(siso_scan_kernel<PS>, dim3((unsigned)((size_t)a.b * a.H * (kP / PS))), dim3(256), lds, st, a);
-    return hipGetLastError();
-}
-
 hipError_t launch_scan_siso(const ScanArgs& a, hipStream_t st) {
     const int nch = (a.L + kSQ - 1) / kSQ;
     hipLaunchKernelGGL(siso_prep_kernel, dim3((unsigned)((size_t)a.b * a.G * nch)), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_siso_scan<32>(a, st);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&siso_scan_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kSiLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(siso_scan_kernel, dim3((unsigned)((size_t)a.b * a.H * (kP / kPS))), dim3(kSiThreads), kSiLds, st, a);
+    return hipGetLastError();
 }
 
 }  // namespace m3

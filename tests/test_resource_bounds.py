@@ -188,11 +188,11 @@ def replay_siso(b, L, H, G):
     """The score pass (per batch, group and chunk) and the scan (per batch, head and half
     of P; every chunk, and the inputs it fetches one chunk past the last)."""
     PS = 32
-    xb = PS // 2                                      # bytes of the x tile per thread
+    xb = 8                                            # bytes of the x tile per thread (512 threads)
     nch = -(-L // 64)
     lanes = np.arange(64)
     l16, g4 = lanes & 15, lanes >> 4
-    tids = np.arange(256)
+    tids = np.arange(512)
     rowb = G * KN * 2
     xrow = H * KP * 2
     BC_bytes = b * L * G * KN * 2
@@ -225,7 +225,7 @@ def replay_siso(b, L, H, G):
                 trec = ((L - 1) * H + 1) * 4
                 for c in sorted({0, max(0, nch - 1), nch}):
                     c0 = c * 64
-                    _check("siso x", xbase, xrec, (c0 + (tids >> 2)) * xrow + xb * (tids & 3), xb, X_bytes)
+                    _check("siso x", xbase, xrec, (c0 + (tids >> 3)) * xrow + xb * (tids & 7), xb, X_bytes)
                     for q in range(4):
                         yo = [(c0 + 16 * q + l16) * xrow + (16 * pt + 4 * g4) * 2 for pt in range(PS // 16)]
                         _check("siso y", xbase, xrec, np.stack(yo), 8, X_bytes)
