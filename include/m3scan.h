@@ -101,7 +101,10 @@ typedef struct {
                          k sequence segments per (batch, head) stream, evaluated in
                          parallel from zero-entry summaries (clamped to the number
                          of chunks).  The result does not depend on it beyond
-                         rounding.  Ignored by m3_decode_step. */
+                         rounding.  Ignored by m3_decode_step, and by the
+                         single-rank path (R = 1, npairs = 0, no biases, bf16 I/O,
+                         float32 state, P = 64, N = 128, Q = 64), which splits
+                         each stream's P columns instead. */
     int rate_law;     /* m3_rate_law: how the A_log argument gives the decay rate */
 } m3_desc;
 
@@ -116,8 +119,12 @@ typedef struct {
     void*  x_prev;   /* [b, H, R, P]   io_dtype: previous token's x             */
 } m3_carry;
 
-/* Bytes of device workspace m3_scan_fwd needs for *d (0 if none).
- * Returns M3_ERR_INVALID_ARG for a NULL argument or an invalid descriptor. */
+/* Bytes of device workspace m3_scan_fwd needs for *d (0 if none): the segment
+ * summaries of the segmented schedule, or for the single-rank path the chunks'
+ * head-shared score tiles (26 KiB per batch, group and chunk).  The biases are not
+ * part of *d, so a shape that takes the single-rank path without biases gets room
+ * for either.  Returns M3_ERR_INVALID_ARG for a NULL argument or an invalid
+ * descriptor. */
 m3_status m3_scan_workspace_size(const m3_desc* d, size_t* bytes);
 
 /* Chunked scan over a whole sequence.
