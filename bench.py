@@ -37,7 +37,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 # sources that define each measured kernel (the counters stand only while these are unchanged)
 KERNEL_SOURCES = {"scan": ("scan_mfma.hip", "scan_common.h", "m3_internal.h"), "decode": ("decode.hip", "m3_internal.h"),
                   "bwd": ("bwd.hip", "m3_internal.h"), "pcs": ("pcs.hip", "m3_internal.h"),
-                  "layer": ("scan_mfma.hip", "scan_common.h", "m3_internal.h", "block.hip")}
+                  "layer": ("scan_mfma.hip", "scan_common.h", "m3_internal.h", "block.hip"),
+                  "siso": ("scan_siso.hip", "scan_common.h", "m3_internal.h")}
 
 
 def source_sha(kind):

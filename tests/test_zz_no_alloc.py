@@ -1,6 +1,7 @@
 """The no-allocation scan entry point (m3_scan_fwd_noalloc, through the C ABI)
-against m3_scan_fwd on the same inputs: two calls in a row, the second with a
-smaller input, both on shapes whose segmented schedule uses the workspace.  The
+against m3_scan_fwd on the same inputs: calls in a row, each with a smaller input
+than the one before, on shapes whose schedule uses the workspace (the segmented
+schedule's summaries; the single-rank path's score tiles).  The
 two entry points run the same kernels and schedule, so their results agree bit
 for bit; both also meet the workload tolerance against the fp64 oracle."""
 import sys
@@ -27,6 +28,9 @@ def m3():
 CASES = [  # (seed, small-case kwargs): the larger first, then a smaller one with another rank and chunk
     (71, dict(batch=1, seqlen=1000, nheads=4, ngroups=1, headdim=64, dstate=128, rank=4, npairs=32, chunk=64)),
     (72, dict(batch=1, seqlen=300, nheads=2, ngroups=1, headdim=64, dstate=128, rank=2, npairs=16, chunk=32)),
+    # the single-rank path (no rotation, no bias): its workspace holds the head-shared score tiles
+    (73, dict(batch=1, seqlen=200, nheads=2, ngroups=1, headdim=64, dstate=128, rank=1, npairs=0, chunk=64,
+              bias=False)),
 ]
 
 
