@@ -541,9 +541,11 @@ m3_status m3_scan_bwd_workspace_size(const m3_desc* d, size_t* bytes) {
     m3_status st = check_desc(d, true);
     if (st != M3_OK) return st;
     if (!scan_bwd_supported(d->headdim, d->dstate, d->rank, d->npairs)) return M3_ERR_UNSUPPORTED;
+    const bool chunked = scan_bwd_chunked_eligible(d->io_dtype == M3_BF16, d->headdim, d->dstate, d->rank, d->npairs,
+                                                   d->seqlen);
     *bytes = d->seqlen == 0 ? 0
                             : scan_bwd_workspace(d->batch, d->seqlen, d->nheads, d->ngroups, d->rank, d->dstate,
-                                                 d->npairs).total;
+                                                 d->npairs, chunked).total;
     return M3_OK;
 }
 
@@ -575,7 +577,8 @@ m3_status m3_scan_bwd(const m3_desc* d, const void* x, const void* B, const void
         if (misaligned(p)) return M3_ERR_ALIGNMENT;
     // inputs (forward inputs, init carry, dy, dfinal) and outputs (every gradient, workspace)
     const size_t f4 = 4;
-    const BwdWs w = scan_bwd_workspace(d->batch, L, d->nheads, d->ngroups, d->rank, d->dstate, d->npairs);
+    const bool chunked = scan_bwd_chunked_eligible(d->io_dtype == M3_BF16, d->headdim, d->dstate, d->rank, np, L);
+    const BwdWs w = scan_bwd_workspace(d->batch, L, d->nheads, d->ngroups, d->rank, d->dstate, d->npairs, chunked);
     const size_t wsb = L > 0 ? w.total : 0;
     if (wsb > 0 && (!workspace || workspace_bytes < wsb)) return M3_ERR_INVALID_ARG;
     Range ri[4] = {};
@@ -623,6 +626,7 @@ m3_status m3_scan_bwd(const m3_desc* d, const void* x, const void* B, const void
         a.wdphi = reinterpret_cast<float*>(base + w.dphi);
         a.wdl = reinterpret_cast<float*>(base + w.dl);
         a.wdlf = reinterpret_cast<float*>(base + w.dlf);
+        a.cws = chunked ? base + w.cws : nullptr;
     }
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     return launch_scan_bwd(a, g->dB, g->dC, hs) == hipSuccess ? M3_OK : M3_ERR_HIP;

@@ -837,17 +837,24 @@ bool scan_bwd_supported(int P, int N, int R, int np) {
     return P >= 1 && P <= kPP && N >= 2 && N <= kNN && (N % 2) == 0 && R >= 1 && R <= kR4 && 2 * np <= N;
 }
 
-BwdWs scan_bwd_workspace(int b, int L, int H, int G, int R, int N, int np) {
+BwdWs scan_bwd_workspace(int b, int L, int H, int G, int R, int N, int np, bool chunked) {
     auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
     BwdWs w{};
     size_t o = 0;
     const size_t tokbc = (size_t)b * L * G * R * N, tokh = (size_t)b * L * H;
     w.accB = o; o += up(tokbc * 4);
     w.accC = o; o += up(tokbc * 4);
-    w.phi = o;  o += up(tokh * np * 4);
-    w.dphi = o; o += up(tokh * np * 4);
-    w.dl = o;   o += up(tokh * 4);
-    w.dlf = o;  o += up((size_t)b * H * 4);
+    if (chunked) {
+        // the chunked form's chunk states and phases replace the replay's per-token terms
+        w.phi = w.dphi = w.dl = w.dlf = o;
+        w.cws = o; o += up(scan_bwd_chunked_extra_bytes(b, L, H, np));
+    } else {
+        w.phi = o;  o += up(tokh * np * 4);
+        w.dphi = o; o += up(tokh * np * 4);
+        w.dl = o;   o += up(tokh * 4);
+        w.dlf = o;  o += up((size_t)b * H * 4);
+        w.cws = o;
+    }
     w.total = o;
     return w;
 }
@@ -878,7 +885,9 @@ hipError_t launch_scan_bwd(const BwdArgs& a, void* dB, void* dC, hipStream_t s) 
     if (e == hipSuccess) e = fill_zero(a.dBb, (size_t)a.H * a.R * a.N, s);
     if (e == hipSuccess) e = fill_zero(a.dCb, (size_t)a.H * a.R * a.N, s);
     if (e != hipSuccess) return e;
-    switch (a.R) {
+    if (a.cws) {
+        e = launch_scan_bwd_chunked(a, a.cws, s);
+    } else switch (a.R) {
         case 1: e = launch_r<1>(a, s); break;
         case 2: e = launch_r<2>(a, s); break;
         case 3: e = launch_r<3>(a, s); break;

@@ -1,0 +1,863 @@
+// Backward pass of the scan in chunked form on the matrix cores, for bf16 I/O at
+// P = 64, N = 128, rank 4 (the shapes of the rank-4 prefill workload).
+//
+// "Diagonal Equivalence in State Space Models: Characterization, Retrieval Rank, and
+// Selective Extensions" (paperpeel.com): section 2.4 (the chunked, state-space-duality
+// form: within a chunk the recurrence is a masked product, across chunks a state is
+// passed), section 2.5 (the adjoint recurrence: the state sensitivity runs backward
+// through the transposed transition) and appendix D.3 (a backward that keeps the
+// chunk-boundary states of the forward sweep).  The recurrence is the three-term update
+// of "Mamba-3: Improved Sequence Modeling using State Space Principles"
+// (intuitivepapers.ai), sections "How the exponential-trapezoidal update works",
+// "Computing the rotation as a data-dependent RoPE" and "MIMO: a rank-4 state update".
+//
+// Folded carry.  With delta_t = dt_t (1 - lambda_t) (so beta_t = alpha_t delta_t), the
+// folded state Hf_t = H_t + delta_{t+1} X_t^T Bt_t obeys, over a chunk of tokens c0 .. e
+// with chunk-local cumulative log-decays l_t (l_t = sum_{c0 <= k <= t} log alpha_k):
+//   H_t  = exp(l_t) Hf_in + sum_{u <= t} W(t,u) X_u^T Bt_u,
+//   W(t,u) = exp(l_t - l_u) (gamma_u + [u < t] delta_{u+1}),
+//   Hf_e = exp(l_e) Hf_in + sum_u v_u X_u^T Bt_u,   v_u = exp(l_e - l_u)(gamma_u + delta_{u+1}),
+// and y_t[r] = H_t Ct_t[r].  Its adjoint over the chunk, given Gf_out = d loss / d Hf_e
+// (from the later chunks) and dy, with rows m = (t, r), u' = (u, r'):
+//   S^T(u', m) = Bt_u' . Ct_m,  S2^T(u', m) = X_u' . dy_m,  P(t,u) = sum_{r,r'} S^T S2^T,
+//   dCt_m  = exp(l_t) Hf_in^T dy_m + sum_u' W S2^T(u', m) Bt_u',
+//   dBt_u' = v_u Gf_out^T X_u'    + sum_m  W S2^T(u', m) Ct_m,
+//   dX_u'  = v_u Gf_out Bt_u'     + sum_m  W S^T(u', m)  dy_m,
+//   Gf_in  = exp(l_e) Gf_out + sum_m exp(l_t) dy_m (x) Ct_m,
+// and the coefficient sensitivities, with Q_u = sum_r' X_u' . (Gf_out Bt_u'):
+//   d gamma_u       = sum_{t >= u} exp(l_t - l_u) P(t,u) + exp(l_e - l_u) Q_u,
+//   d delta_{u+1}   = sum_{t >  u} exp(l_t - l_u) P(t,u) + exp(l_e - l_u) Q_u,
+//   d log alpha_t   = <G_t, alpha_t Hf_{t-1}>     (G_t = d loss / d H_t)
+//                   = sum_{t' >= t} exp(l_t') <dy_t' (x) Ct_t', Hf_in> + exp(l_e) <Gf_out, Hf_in>
+//                     + sum_{t' >= t} sum_{u < t} exp(l_t' - l_u)(gamma_u + delta_{u+1}) P(t',u)
+//                     + sum_{u < t} v_u Q_u,
+// every term an inner product of the chunk's own reads and writes (the difference of all
+// reads and all writes at a token gives the same value but cancels in bf16 operands).
+// The angle's sensitivity Phi_t (the reverse running sum of each token's rotation term)
+// cancels across the sequence: the scores see only angle differences.  Rotating every
+// token from t on by eps equals turning the incoming folded state by -eps and the final
+// carry by +eps, so, per pair j (J_j a quarter turn of the pair's two columns),
+//   Phi_t[j] = Phi_L[j] - <Gf_{t-1}, J_j Hf_{t-1}>,
+//   Phi_L[j] = d phi_L[j] + <d h_L, J_j H_L> + <d B_prev,L, J_j Bt_{L-1}>.
+// The kernel sums the rotation terms inside a chunk and takes Phi at each chunk's start
+// from this identity, so rounding does not accumulate along the sequence.
+//
+// Two kernels per call, one workgroup of 8 waves per (batch, head) stream:
+//   * bwdc_state_kernel walks the chunks forward and stores each chunk's incoming folded
+//     state Hf_in (bf16, n-major) and its starting phases (fp32, wrapped into [0, 2 pi));
+//   * bwdc_main_kernel walks them backward with Gf (fp32) in matrix-core accumulators:
+//     per chunk, the score tiles S^T and S2^T, the weighted tiles (bf16 in LDS), the
+//     products above, then the per-token scalar gradients.
+// Shared B and C gradients are summed over a group's heads by fp32 atomic adds into the
+// workspace (as the token-serial backward does), converted to bf16 afterwards.
+#include "scan_common.h"
+
+namespace m3 {
+
+namespace {
+
+constexpr int kBQ = 16;                       // tokens per chunk
+constexpr int kBR = 4;                        // ranks
+constexpr int kBM = kBQ * kBR;                // rows (token, rank) per chunk
+constexpr int kBT = 512;                      // threads: 8 waves
+constexpr int kMaxPairs = 64;
+constexpr size_t kHfChunkBytes = (size_t)kN * kP * 2;   // one chunk's Hf_in, [n][p] bf16
+
+// ---- LDS layout of the main kernel (bytes) ----
+constexpr int oX = 0;                         // X    [64 m][64 p]   bf16, 128-byte rows
+constexpr int oDY = oX + kBM * kP * 2;        // dy   [64 m][64 p]
+constexpr int oB = oDY + kBM * kP * 2;        // Bt   [64 m][128 n]  256-byte rows
+constexpr int oC = oB + kBM * kN * 2;         // Ct   [64 m][128 n]
+constexpr int oG = oC + kBM * kN * 2;         // Gf_out [128 n][64 p] (bf16 copy)
+constexpr int oM1 = oG + kN * kP * 2;         // W S2^T stored as [64 m][64 u']
+constexpr int oM2 = oM1 + kBM * kBM * 2;      // W S^T  stored as [64 m][64 u']
+constexpr int oPH = oM2 + kBM * kBM * 2;      // phases [16 t][64 pair] fp32
+constexpr int oDPB = oPH + kBQ * kMaxPairs * 4;   // B side of d phi [16][64]
+constexpr int oDPC = oDPB + kBQ * kMaxPairs * 4;  // C side of d phi [16][64]
+constexpr int oPM = oDPC + kBQ * kMaxPairs * 4;   // P(t, u) [16][16]
+constexpr int oTAB = oPM + kBQ * kBQ * 4;
+
+struct Tab {
+    float l[kBQ], E[kBQ], gam[kBQ], v[kBQ], a[kBQ], u[kBQ];
+    float dl[kBQ + 1], dt[kBQ + 1], lam[kBQ + 1];   // delta, dt, lambda of tokens c0 .. c0 + 16
+    float RHp[8][kBQ];                              // per wave: <dy_t (x) Ct_t, Hf_in> of each token
+    float Qp[4][kBQ];                               // per p tile: Q_u
+    float GH[8];                                    // per wave: <Gf_out, Hf_in>
+    float TP[kBQ];                                  // sum over pairs of theta_t Phi_t
+    float dgam[kBQ], ddl[kBQ], dla[kBQ];
+    float K[kBQ][kBQ];                              // [t][u]: sum_{t' >= t} of the corner terms of column u
+    float ddl_next;                                 // d delta of token c0 + 16 from this chunk
+    float phb[kMaxPairs];                           // <Gf_in, J_j Hf_in> of each pair
+    float pend_dt, pend_lam;                        // token c0's gradients without its delta term
+    float le;
+};
+constexpr int kMainLds = oTAB + (int)sizeof(Tab);
+
+// ---- LDS layout of the state kernel ----
+constexpr int sX_ = 0;                        // X  [64 m][64 p]
+constexpr int sV_ = sX_ + kBM * kP * 2;       // v Bt [64 m][128 n]
+constexpr int sPH_ = sV_ + kBM * kN * 2;      // phases [16][64]
+constexpr int sTAB_ = sPH_ + kBQ * kMaxPairs * 4;
+constexpr int kStateLds = sTAB_ + (int)sizeof(Tab);
+
+// A-style operand: lane (g, s) reads row row0 + s, columns kbase + 8 g .. + 7 (16 bytes).
+__device__ __forceinline__ bf16x8 row_op(const char* base, int pitch, int row0, int kbase, int lane) {
+    const int g = lane >> 4, s = lane & 15;
+    return *reinterpret_cast<const bf16x8*>(base + (row0 + s) * pitch + (kbase + 8 * g) * 2);
+}
+// B-style operand from a row-major tile by transposing reads: lane (g, s) receives column
+// c0 + s at rows kbase + 8 g .. + 7 (two reads of four rows).
+__device__ __forceinline__ bf16x8 tr_op(const char* base, int pitch, int kbase, int c0, int lane) {
+    const int g = lane >> 4, s = lane & 15;
+    const char* p = base + (kbase + 8 * g + (s >> 2)) * pitch + (c0 + 4 * (s & 3)) * 2;
+    const uint2 lo = ds_tr(p);
+    const uint2 hi = ds_tr(p + 4 * pitch);
+    return __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
+}
+// Four rows kb .. kb + 3 of column c0 + s (lane (g, s); kb chosen per lane group).
+__device__ __forceinline__ void tr4(const char* base, int pitch, int kb, int c0, int lane, float out[4]) {
+    const int s = lane & 15;
+    const uint2 v = ds_tr(base + (kb + (s >> 2)) * pitch + (c0 + 4 * (s & 3)) * 2);
+    out[0] = lo_f(v.x); out[1] = hi_f(v.x); out[2] = lo_f(v.y); out[3] = hi_f(v.y);
+}
+__device__ __forceinline__ float quad_swap(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float sum16(float v) {        // over the 16 lanes of a lane group
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float sum64(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ uint2 pack4(const f32x4& v) { return uint2{pack2(v[0], v[1]), pack2(v[2], v[3])}; }
+
+// The per-token scalars of chunk [c0, c0 + 16) into the table (wave 0; lane t: token
+// c0 + t, lane 16 the token after the chunk).  Tokens at or past L have dt = 0: no decay,
+// no write.
+__device__ void chunk_scalars(const BwdArgs& a, int bi, int h, int c0, int lane, Tab* tb) {
+    const int L = a.L, H = a.H;
+    const int tok = c0 + lane;
+    const bool valid = lane <= kBQ && tok < L;
+    const size_t ti = ((size_t)bi * L + (valid ? tok : 0)) * H + h;
+    const float dt = valid ? a.dt[ti] : 0.f;
+    const float lam = valid ? a.lam[ti] : 0.f;
+    float rate = 0.f, u = 0.f;
+    if (a.rate_law) {
+        u = valid ? a.A[ti] : 0.f;
+        rate = -heavy_tail_rate(u);
+    } else {
+        rate = expf(a.A[h]);
+    }
+    const float la = -dt * rate;
+    const float gam = lam * dt, dl = dt * (1.f - lam);
+    const float l = group_scan<16>(lane < kBQ ? la : 0.f, lane);
+    const float le = __shfl(l, kBQ - 1, 64);
+    const float dn = __shfl_down(dl, 1, 64);
+    if (lane < kBQ) {
+        tb->l[lane] = l;
+        tb->E[lane] = __expf(l);
+        tb->gam[lane] = gam;
+        tb->v[lane] = __expf(fminf(le - l, 0.f)) * (gam + dn);
+        tb->a[lane] = rate;
+        tb->u[lane] = u;
+    }
+    if (lane <= kBQ) {
+        tb->dl[lane] = dl;
+        tb->dt[lane] = dt;
+        tb->lam[lane] = lam;
+    }
+    if (lane == 0) tb->le = le;
+}
+
+// Phases of the chunk's tokens (wave 1, lane j < np: pair j) from the chunk's starting
+// phase phi (wrapped): ph[t][j] = phi + sum_{k <= t} dt_k theta_k[j].  Returns the phase
+// after the chunk.
+__device__ float chunk_phases(const BwdArgs& a, int bi, int h, int c0, int j, float phi, float* ph) {
+    const int L = a.L, H = a.H, np = a.np;
+#pragma unroll 4
+    for (int t = 0; t < kBQ; ++t) {
+        const int tok = c0 + t;
+        if (tok < L) {
+            const size_t ti = ((size_t)bi * L + tok) * H + h;
+            phi = fmaf(a.dt[ti], a.theta[ti * np + j], phi);
+        }
+        ph[t * kMaxPairs + j] = phi;
+    }
+    return phi;
+}
+
+// 16 turned values of row (token, rank) at columns n0 .. n0 + 15: raw + bias, pairs
+// (2 j, 2 j + 1) with j < np rotated by the token's phases, times scale; bf16 pairs out.
+__device__ __forceinline__ void turn_piece(const uint16_t* raw, const float* bias, const float* ph, int np, int n0,
+                                           float scale, uint32_t out[8]) {
+    float v[16];
+    if (raw) {
+        const uint4 r0 = *reinterpret_cast<const uint4*>(raw + n0);
+        const uint4 r1 = *reinterpret_cast<const uint4*>(raw + n0 + 8);
+        const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { v[2 * k] = lo_f(w[k]); v[2 * k + 1] = hi_f(w[k]); }
+        if (bias) {
+#pragma unroll
+            for (int k = 0; k < 16; k += 4) {
+                const float4 b4 = *reinterpret_cast<const float4*>(bias + n0 + k);
+                v[k] += b4.x; v[k + 1] += b4.y; v[k + 2] += b4.z; v[k + 3] += b4.w;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int j = (n0 >> 1) + k;
+        float e = v[2 * k], o = v[2 * k + 1];
+        if (j < np) {
+            float sn, cs;
+            __sincosf(wrap_2pi(ph[j]), &sn, &cs);
+            const float e2 = e * cs - o * sn, o2 = e * sn + o * cs;
+            e = e2; o = o2;
+        }
+        out[k] = pack2(e * scale, o * scale);
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Forward sweep: each chunk's incoming folded state and starting phases.
+__global__ __launch_bounds__(kBT) void bwdc_state_kernel(BwdArgs a, char* hfws, float* phws, float* phl) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g4 = lane >> 4, s = lane & 15;
+    const int L = a.L, H = a.H, G = a.G, np = a.np;
+    const int bh = blockIdx.x, h = bh % H, bi = bh / H, gg = h * G / H;
+    const int nch = (L + kBQ - 1) / kBQ;
+    char* const sX = smem + sX_;
+    char* const sV = smem + sV_;
+    float* const ph = reinterpret_cast<float*>(smem + sPH_);
+    Tab* const tb = reinterpret_cast<Tab*>(smem + sTAB_);
+
+    // Hf_{-1} = H0 + delta_0 x_prev^T B_prev (the initial carry, folded); wave w owns n-tile w
+    f32x4 hf[4];
+    {
+        const int n = 16 * w + s;
+        float d0 = 0.f;
+        if (a.Bp0 && a.xp0) {
+            const size_t t0 = (size_t)bi * L * H + h;
+            d0 = a.dt[t0] * (1.f - a.lam[t0]);
+        }
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int p = 16 * pt + 4 * g4 + i;
+                float v = a.h0 ? ld_io(a.h0, ((size_t)bh * kP + p) * kN + n, a.st_bf16) : 0.f;
+                if (a.Bp0 && a.xp0)
+#pragma unroll
+                    for (int r = 0; r < kBR; ++r)
+                        v += d0 * ld_io(a.xp0, ((size_t)bh * kBR + r) * kP + p, a.io_bf16) *
+                             ld_io(a.Bp0, ((size_t)bh * kBR + r) * kN + n, a.io_bf16);
+                hf[pt][i] = v;
+            }
+    }
+    float phi = (w == 1 && lane < np && a.phi0) ? a.phi0[(size_t)bh * np + lane] : 0.f;
+
+    for (int c = 0; c < nch; ++c) {
+        const int c0 = c * kBQ;
+        if (w == 0) chunk_scalars(a, bi, h, c0, lane, tb);
+        if (w == 1 && lane < np) {
+            phi = wrap_2pi(phi);
+            phws[((size_t)bh * nch + c) * np + lane] = phi;
+            phi = chunk_phases(a, bi, h, c0, lane, phi, ph);
+        }
+        __syncthreads();
+        {
+            // X rows and v-scaled turned B rows (row m = tid / 8, piece tid % 8)
+            const int m = tid >> 3, q8 = tid & 7, t = m >> 2, r = m & 3, tok = c0 + t;
+            const bool valid = tok < L;
+            uint4 xv = {0u, 0u, 0u, 0u};
+            if (valid)
+                xv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) +
+                                                     (((size_t)bi * L + tok) * H + h) * kBR * kP + r * kP + 8 * q8);
+            *reinterpret_cast<uint4*>(sX + m * (kP * 2) + q8 * 16) = xv;
+            const uint16_t* raw = valid ? static_cast<const uint16_t*>(a.B) + (((size_t)bi * L + tok) * G + gg) * kBR * kN + r * kN
+                                        : nullptr;
+            const float* bias = a.Bb ? a.Bb + ((size_t)h * kBR + r) * kN : nullptr;
+            uint32_t o[8];
+            turn_piece(raw, bias, ph + t * kMaxPairs, np, 16 * q8, tb->v[t], o);
+            *reinterpret_cast<uint4*>(sV + m * (kN * 2) + q8 * 32) = uint4{o[0], o[1], o[2], o[3]};
+            *reinterpret_cast<uint4*>(sV + m * (kN * 2) + q8 * 32 + 16) = uint4{o[4], o[5], o[6], o[7]};
+        }
+        // the chunk's incoming state, n-major: lane writes p = 16 pt + 4 g4 .. + 3 of column n
+        {
+            char* dst = hfws + ((size_t)bh * nch + c) * kHfChunkBytes;
+            const int n = 16 * w + s;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt)
+                *reinterpret_cast<uint2*>(dst + (n * kP + 16 * pt + 4 * g4) * 2) = pack4(hf[pt]);
+        }
+        __syncthreads();
+        // Hf = exp(l_e) Hf + X^T (v Bt): rows p (A = X^T by transposing reads), columns n
+        const float fe = __expf(tb->le);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+            f32x4 acc = {hf[pt][0] * fe, hf[pt][1] * fe, hf[pt][2] * fe, hf[pt][3] * fe};
+#pragma unroll
+            for (int km = 0; km < 2; ++km)
+                acc = mfma(tr_op(sX, kP * 2, 32 * km, 16 * pt, lane), tr_op(sV, kN * 2, 32 * km, 16 * w, lane), acc);
+            hf[pt] = acc;
+        }
+        __syncthreads();
+    }
+
+    // Phi_L[j] = d phi_L[j] + <d h_L, J_j H_L> + <d B_prev,L, J_j Bt_{L-1}> (hf is H_L: delta_L = 0)
+    if (np == 0) return;
+    float* const hterm = reinterpret_cast<float*>(sV);          // [64 pairs]
+    {
+        const int n = 16 * w + s;
+        const bool odd = (s & 1) != 0;
+        float acc = 0.f;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float partner = quad_swap(hf[pt][i]);
+                const float d = a.dh1 ? a.dh1[((size_t)bh * kP + 16 * pt + 4 * g4 + i) * kN + n] : 0.f;
+                acc = fmaf(d, odd ? partner : -partner, acc);
+            }
+        acc += quad_swap(acc);
+        acc += __shfl_xor(acc, 16, 64);
+        acc += __shfl_xor(acc, 32, 64);
+        if (g4 == 0 && !odd) hterm[n >> 1] = acc;
+    }
+    __syncthreads();
+    if (tid < np) {
+        const int j = tid, tl = (L - 1) - (nch - 1) * kBQ;
+        float v = hterm[j] + (a.dphi1 ? a.dphi1[(size_t)bh * np + j] : 0.f);
+        if (a.dBp1) {
+            float sn, cs;
+            __sincosf(wrap_2pi(ph[tl * kMaxPairs + j]), &sn, &cs);
+            const size_t tok = (size_t)bi * L + (L - 1);
+#pragma unroll
+            for (int r = 0; r < kBR; ++r) {
+                const uint16_t* raw = static_cast<const uint16_t*>(a.B) + (tok * G + gg) * kBR * kN + r * kN;
+                float e = bf16_bits_to_f32(raw[2 * j]), o = bf16_bits_to_f32(raw[2 * j + 1]);
+                if (a.Bb) {
+                    e += a.Bb[((size_t)h * kBR + r) * kN + 2 * j];
+                    o += a.Bb[((size_t)h * kBR + r) * kN + 2 * j + 1];
+                }
+                const float e2 = e * cs - o * sn, o2 = e * sn + o * cs;
+                v += a.dBp1[((size_t)bh * kBR + r) * kN + 2 * j] * (-o2) + a.dBp1[((size_t)bh * kBR + r) * kN + 2 * j + 1] * e2;
+            }
+        }
+        phl[(size_t)bh * np + j] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Reverse sweep over the chunks.
+__global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* hfws, const float* phws, const float* phl) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g4 = lane >> 4, s = lane & 15;
+    const int L = a.L, H = a.H, G = a.G, np = a.np;
+    const int bh = blockIdx.x, h = bh % H, bi = bh / H, gg = h * G / H;
+    const int nch = (L + kBQ - 1) / kBQ;
+    const size_t bo = (size_t)bi * L;
+    char* const sX = smem + oX;
+    char* const sDY = smem + oDY;
+    char* const sB = smem + oB;
+    char* const sC = smem + oC;
+    char* const sG = smem + oG;
+    char* const sM1 = smem + oM1;
+    char* const sM2 = smem + oM2;
+    float* const ph = reinterpret_cast<float*>(smem + oPH);
+    float* const dphB = reinterpret_cast<float*>(smem + oDPB);
+    float* const dphC = reinterpret_cast<float*>(smem + oDPC);
+    float* const sPM = reinterpret_cast<float*>(smem + oPM);
+    Tab* const tb = reinterpret_cast<Tab*>(smem + oTAB);
+
+    // Gf = d loss / d Hf at the sequence end: the final state's sensitivity (wave w: n-tile w)
+    f32x4 gf[4];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            gf[pt][i] = a.dh1 ? a.dh1[((size_t)bh * kP + 16 * pt + 4 * g4 + i) * kN + 16 * w + s] : 0.f;
+    // Phi: the angle's sensitivity (wave 1, lane j < np), and its constant Phi_L
+    float Phi = (w == 1 && lane < np && a.dphi1) ? a.dphi1[(size_t)bh * np + lane] : 0.f;
+    const float PhiL = (w == 1 && lane < np) ? phl[(size_t)bh * np + lane] : 0.f;
+    float bbias[4] = {0.f, 0.f, 0.f, 0.f}, cbias[4] = {0.f, 0.f, 0.f, 0.f};
+    float dA_acc = 0.f;                       // static rate law: sum of d A over tokens (wave 0)
+    float pend_dt = 0.f, pend_lam = 0.f;      // token c0 + 16 of the previous iteration (wave 0, lane 0)
+
+    for (int c = nch - 1; c >= 0; --c) {
+        const int c0 = c * kBQ;
+        // ---- S0a: scalars, phases ----
+        if (w == 0) chunk_scalars(a, bi, h, c0, lane, tb);
+        if (w == 1 && lane < np) chunk_phases(a, bi, h, c0, lane, phws[((size_t)bh * nch + c) * np + lane], ph);
+        __syncthreads();
+        // ---- S0b: staging ----
+        {
+            const int m = tid >> 3, q8 = tid & 7, t = m >> 2, r = m & 3, tok = c0 + t;
+            const bool valid = tok < L;
+            const size_t xrow = ((bo + (valid ? tok : 0)) * H + h) * kBR * kP + r * kP + 8 * q8;
+            uint4 xv = {0u, 0u, 0u, 0u}, dv = {0u, 0u, 0u, 0u};
+            if (valid) {
+                xv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + xrow);
+                dv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.dy) + xrow);
+            }
+            *reinterpret_cast<uint4*>(sX + m * (kP * 2) + q8 * 16) = xv;
+            *reinterpret_cast<uint4*>(sDY + m * (kP * 2) + q8 * 16) = dv;
+            const size_t brow = ((bo + (valid ? tok : 0)) * G + gg) * kBR * kN + r * kN;
+            uint32_t o[8];
+            turn_piece(valid ? static_cast<const uint16_t*>(a.B) + brow : nullptr,
+                       a.Bb ? a.Bb + ((size_t)h * kBR + r) * kN : nullptr, ph + t * kMaxPairs, np, 16 * q8, 1.f, o);
+            *reinterpret_cast<uint4*>(sB + m * (kN * 2) + q8 * 32) = uint4{o[0], o[1], o[2], o[3]};
+            *reinterpret_cast<uint4*>(sB + m * (kN * 2) + q8 * 32 + 16) = uint4{o[4], o[5], o[6], o[7]};
+            turn_piece(valid ? static_cast<const uint16_t*>(a.C) + brow : nullptr,
+                       a.Cb ? a.Cb + ((size_t)h * kBR + r) * kN : nullptr, ph + t * kMaxPairs, np, 16 * q8, 1.f, o);
+            *reinterpret_cast<uint4*>(sC + m * (kN * 2) + q8 * 32) = uint4{o[0], o[1], o[2], o[3]};
+            *reinterpret_cast<uint4*>(sC + m * (kN * 2) + q8 * 32 + 16) = uint4{o[4], o[5], o[6], o[7]};
+        }
+        {
+            const int n = 16 * w + s;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt)
+                *reinterpret_cast<uint2*>(sG + (n * kP + 16 * pt + 4 * g4) * 2) = pack4(gf[pt]);
+        }
+        // Hf_in pieces: B operands of dy Hf_in (column n = 16 w + s, k = p) and the lane's
+        // own elements of the state tiles (for <Gf_out, Hf_in>)
+        const char* const hin = hfws + ((size_t)bh * nch + c) * kHfChunkBytes;
+        bf16x8 hop[2];
+        uint2 hown[4];
+        {
+            const int n = 16 * w + s;
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp)
+                hop[kp] = *reinterpret_cast<const bf16x8*>(hin + (n * kP + 32 * kp + 8 * g4) * 2);
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) hown[pt] = *reinterpret_cast<const uint2*>(hin + (n * kP + 16 * pt + 4 * g4) * 2);
+        }
+        __syncthreads();
+        // ---- S1: score tiles S^T, S2^T (rows u', columns m), weights, P(t, u) ----
+        {
+            const int mt = w & 3;
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const int ut = 2 * (w >> 2) + k2;
+                f32x4 st = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kn = 0; kn < 4; ++kn)
+                    st = mfma(row_op(sB, kN * 2, 16 * ut, 32 * kn, lane), row_op(sC, kN * 2, 16 * mt, 32 * kn, lane), st);
+#pragma unroll
+                for (int kp = 0; kp < 2; ++kp)
+                    s2 = mfma(row_op(sX, kP * 2, 16 * ut, 32 * kp, lane), row_op(sDY, kP * 2, 16 * mt, 32 * kp, lane), s2);
+                const int t = 4 * mt + (s >> 2), u = 4 * ut + g4;
+                float wt = 0.f;
+                if (u <= t)
+                    wt = __expf(fminf(tb->l[t] - tb->l[u], 0.f)) * (tb->gam[u] + (u < t ? tb->dl[u + 1] : 0.f));
+                const f32x4 m1 = {wt * s2[0], wt * s2[1], wt * s2[2], wt * s2[3]};
+                const f32x4 m2 = {wt * st[0], wt * st[1], wt * st[2], wt * st[3]};
+                const int m = 16 * mt + s;
+                *reinterpret_cast<uint2*>(sM1 + m * (kBM * 2) + (16 * ut + 4 * g4) * 2) = pack4(m1);
+                *reinterpret_cast<uint2*>(sM2 + m * (kBM * 2) + (16 * ut + 4 * g4) * 2) = pack4(m2);
+                float pr = st[0] * s2[0] + st[1] * s2[1] + st[2] * s2[2] + st[3] * s2[3];
+                pr += quad_swap(pr);
+                pr += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(pr), 0x4E, 0xf, 0xf, false));
+                if ((s & 3) == 0) sPM[t * kBQ + u] = pr;
+            }
+        }
+        __syncthreads();
+        // ---- S2: the products ----
+        const int nt = w, n = 16 * nt + s;
+        const bool odd = (s & 1) != 0;
+        const int pair = n >> 1;
+        const bool turns = pair < np;
+        // (a) dCt = W S2 Bt + exp(l_t) dy Hf_in   (rows m, column n)
+#pragma unroll 1
+        for (int mt = 0; mt < 4; ++mt) {
+            f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                if (2 * ks <= mt) a1 = mfma(row_op(sM1, kBM * 2, 16 * mt, 32 * ks, lane), tr_op(sB, kN * 2, 32 * ks, 16 * nt, lane), a1);
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp) a2 = mfma(row_op(sDY, kP * 2, 16 * mt, 32 * kp, lane), hop[kp], a2);
+            const int t = 4 * mt + g4, tok = c0 + t;
+            const float E = tb->E[t];
+            float dc[4], cv[4];
+            tr4(sC, kN * 2, 16 * mt + 4 * g4, 16 * nt, lane, cv);
+            float rs = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { dc[i] = fmaf(E, a2[i], a1[i]); rs = fmaf(cv[i], a2[i], rs); }
+            rs = sum16(rs);
+            if (s == 0) tb->RHp[w][t] = rs;
+            float sn = 0.f, cs = 1.f;
+            if (turns) __sincosf(wrap_2pi(ph[t * kMaxPairs + pair]), &sn, &cs);
+            float dpp = 0.f, outv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float pv = quad_swap(cv[i]), pd = quad_swap(dc[i]);
+                const float e = odd ? pv : cv[i], o = odd ? cv[i] : pv;
+                const float de = odd ? pd : dc[i], dO = odd ? dc[i] : pd;
+                dpp += -de * o + dO * e;
+                outv[i] = turns ? (odd ? -de * sn + dO * cs : de * cs + dO * sn) : dc[i];
+                cbias[i] += outv[i];
+            }
+            if (turns && !odd) dphC[t * kMaxPairs + pair] = dpp;
+            if (tok < L) {
+                float* acc = a.accC + ((bo + tok) * G + gg) * kBR * kN + n;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) unsafeAtomicAdd(acc + i * kN, outv[i]);
+            }
+        }
+        // (b) dBt = (W S2)^T Ct + v_u X Gf_out   (rows u', column n)
+#pragma unroll 1
+        for (int ut = 0; ut < 4; ++ut) {
+            f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                if (2 * ks + 1 >= ut) a1 = mfma(tr_op(sM1, kBM * 2, 32 * ks, 16 * ut, lane), tr_op(sC, kN * 2, 32 * ks, 16 * nt, lane), a1);
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp)
+                a2 = mfma(row_op(sX, kP * 2, 16 * ut, 32 * kp, lane), row_op(sG, kP * 2, 16 * nt, 32 * kp, lane), a2);
+            const int u = 4 * ut + g4, tok = c0 + u;
+            const float v = tb->v[u];
+            float db[4], bv[4];
+            tr4(sB, kN * 2, 16 * ut + 4 * g4, 16 * nt, lane, bv);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) db[i] = fmaf(v, a2[i], a1[i]);
+            if (tok == L - 1 && a.dBp1) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) db[i] += a.dBp1[((size_t)bh * kBR + i) * kN + n];
+            }
+            float sn = 0.f, cs = 1.f;
+            if (turns) __sincosf(wrap_2pi(ph[u * kMaxPairs + pair]), &sn, &cs);
+            float dpp = 0.f, outv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float pv = quad_swap(bv[i]), pd = quad_swap(db[i]);
+                const float e = odd ? pv : bv[i], o = odd ? bv[i] : pv;
+                const float de = odd ? pd : db[i], dO = odd ? db[i] : pd;
+                dpp += -de * o + dO * e;
+                outv[i] = turns ? (odd ? -de * sn + dO * cs : de * cs + dO * sn) : db[i];
+                bbias[i] += outv[i];
+            }
+            if (turns && !odd) dphB[u * kMaxPairs + pair] = dpp;
+            if (tok < L) {
+                float* acc = a.accB + ((bo + tok) * G + gg) * kBR * kN + n;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) unsafeAtomicAdd(acc + i * kN, outv[i]);
+            }
+        }
+        // (c) dX = (W S)^T dy + v_u Z, Z = Bt Gf_out^T   (rows u', column p)
+        {
+            const int pt = w & 3, p = 16 * pt + s;
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const int ut = 2 * (w >> 2) + k2;
+                f32x4 z = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kn = 0; kn < 4; ++kn)
+                    z = mfma(row_op(sB, kN * 2, 16 * ut, 32 * kn, lane), tr_op(sG, kP * 2, 32 * kn, 16 * pt, lane), z);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    if (2 * ks + 1 >= ut) a1 = mfma(tr_op(sM2, kBM * 2, 32 * ks, 16 * ut, lane), tr_op(sDY, kP * 2, 32 * ks, 16 * pt, lane), a1);
+                const int u = 4 * ut + g4, tok = c0 + u;
+                const float v = tb->v[u];
+                float xv[4];
+                tr4(sX, kP * 2, 16 * ut + 4 * g4, 16 * pt, lane, xv);
+                float q = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) q = fmaf(xv[i], z[i], q);
+                q = sum16(q);
+                if (s == 0) tb->Qp[pt][u] = q;
+                if (tok < L) {
+                    const size_t row = ((bo + tok) * H + h) * kBR * kP + p;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float dxv = fmaf(v, z[i], a1[i]);
+                        if (tok == L - 1 && a.dxp1) dxv += a.dxp1[((size_t)bh * kBR + i) * kP + p];
+                        static_cast<bf16*>(a.dx)[row + i * kP] = (bf16)dxv;
+                    }
+                }
+            }
+        }
+        // (d) <Gf_out, Hf_in>, then Gf_in = exp(l_e) Gf_out + (E dy)^T Ct
+        {
+            float gh = 0.f;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                gh = fmaf(gf[pt][0], lo_f(hown[pt].x), gh);
+                gh = fmaf(gf[pt][1], hi_f(hown[pt].x), gh);
+                gh = fmaf(gf[pt][2], lo_f(hown[pt].y), gh);
+                gh = fmaf(gf[pt][3], hi_f(hown[pt].y), gh);
+            }
+            gh = sum64(gh);
+            if (lane == 0) tb->GH[w] = gh;
+            const float fe = __expf(tb->le);
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                f32x4 acc = {gf[pt][0] * fe, gf[pt][1] * fe, gf[pt][2] * fe, gf[pt][3] * fe};
+#pragma unroll
+                for (int km = 0; km < 2; ++km) {
+                    // A = dy^T (rows p, k = m) scaled by E of each key's token: k slots 0-3 are
+                    // token 8 km + 2 g4, slots 4-7 token 8 km + 2 g4 + 1
+                    const uint4 raw = __builtin_bit_cast(uint4, tr_op(sDY, kP * 2, 32 * km, 16 * pt, lane));
+                    const float e0 = tb->E[8 * km + 2 * g4], e1 = tb->E[8 * km + 2 * g4 + 1];
+                    const uint4 sc = {pack2(lo_f(raw.x) * e0, hi_f(raw.x) * e0), pack2(lo_f(raw.y) * e0, hi_f(raw.y) * e0),
+                                      pack2(lo_f(raw.z) * e1, hi_f(raw.z) * e1), pack2(lo_f(raw.w) * e1, hi_f(raw.w) * e1)};
+                    acc = mfma(__builtin_bit_cast(bf16x8, sc), tr_op(sC, kN * 2, 32 * km, 16 * nt, lane), acc);
+                }
+                gf[pt] = acc;
+            }
+            // <Gf_in, J_j Hf_in> of pair j = n / 2 (the chunk's starting Phi is Phi_L minus it)
+            float jt = 0.f;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const float hv[4] = {lo_f(hown[pt].x), hi_f(hown[pt].x), lo_f(hown[pt].y), hi_f(hown[pt].y)};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float partner = quad_swap(hv[i]);
+                    jt = fmaf(gf[pt][i], odd ? partner : -partner, jt);
+                }
+            }
+            jt += quad_swap(jt);
+            jt += __shfl_xor(jt, 16, 64);
+            jt += __shfl_xor(jt, 32, 64);
+            if (g4 == 0 && !odd && turns) tb->phb[pair] = jt;
+        }
+        __syncthreads();
+        // ---- S3a: coefficient sensitivities (wave 0), the angle's (wave 1) ----
+        if (w == 0) {
+            const int u = lane & 15;
+            const bool ul = lane < kBQ;
+            const float lu = tb->l[u], le = tb->le;
+            const float Qu = tb->Qp[0][u] + tb->Qp[1][u] + tb->Qp[2][u] + tb->Qp[3][u];
+            float RH = 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) RH += tb->RHp[k][u];
+            float GH = 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) GH += tb->GH[k];
+            const float wv = tb->gam[u] + tb->dl[u + 1];
+            // column u: tail = sum_{t > u} exp(l_t - l_u) P(t, u); the corner terms
+            // exp(l_t' - l_u) wv_u P(t', u) summed over t' >= t, for every t > u
+            float tail = 0.f, cs = 0.f;
+            for (int t = kBQ - 1; t > u; --t) {
+                const float ep = __expf(fminf(tb->l[t] - lu, 0.f)) * sPM[t * kBQ + u];
+                tail += ep;
+                cs = fmaf(wv, ep, cs);
+                if (ul) tb->K[t][u] = cs;
+            }
+            const float diagP = sPM[u * kBQ + u];
+            const float endq = __expf(fminf(le - lu, 0.f)) * Qu;
+            const float vq = tb->v[u] * Qu;
+            // d log alpha_t (lane t = u): suffix of exp(l) RH, prefix of v Q, row t of K over u < t
+            const float erh = tb->E[u] * RH;
+            const float rv = __shfl(erh, (kBQ - 1) - u, 64);
+            const float sc = group_scan<16>(ul ? rv : 0.f, lane);
+            const float suf = __shfl(sc, (kBQ - 1) - u, 64);
+            const float pre = group_scan<16>(ul ? vq : 0.f, lane) - vq;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            float corner = 0.f;
+            for (int k = 0; k < u; ++k) corner += tb->K[u][k];
+            const float dla = suf + __expf(le) * GH + pre + corner;
+            const float dnext = tail + endq;                    // d delta of token u + 1
+            const float dprev = __shfl_up(dnext, 1, 64);        // lane u: d delta of token u (u >= 1)
+            if (ul) {
+                tb->dgam[u] = diagP + tail + endq;
+                tb->ddl[u] = u >= 1 ? dprev : 0.f;
+                tb->dla[u] = dla;
+            }
+            if (lane == kBQ - 1) tb->ddl_next = dnext;
+        }
+        if (w == 1) {
+            const bool pl = lane < np;
+            for (int t = kBQ - 1; t >= 0; --t) {
+                const int tok = c0 + t;
+                float tp = 0.f;
+                if (pl) {
+                    Phi += dphB[t * kMaxPairs + lane] + dphC[t * kMaxPairs + lane];
+                    if (tok < L) {
+                        const size_t ti = (bo + tok) * H + h;
+                        a.dtheta[ti * np + lane] = tb->dt[t] * Phi;
+                        tp = a.theta[ti * np + lane] * Phi;
+                    }
+                }
+                tp = sum64(tp);
+                if (lane == 0) tb->TP[t] = tp;
+            }
+            if (pl) Phi = PhiL - tb->phb[lane];                 // Phi at the chunk's first token
+        }
+        __syncthreads();
+        // ---- S3b: per-token outputs (wave 0, lane t) ----
+        if (w == 0) {
+            const int t = lane & 15, tok = c0 + t;
+            const float dtt = tb->dt[t], lamt = tb->lam[t], dla = tb->dla[t], dg = tb->dgam[t], dd = tb->ddl[t];
+            const float d_dt = dla * (-tb->a[t]) + dg * lamt + dd * (1.f - lamt) + tb->TP[t];
+            const float d_lam = (dg - dd) * dtt;
+            const float d_A = dla * dtt;
+            const bool valid = lane < kBQ && tok < L;
+            const size_t ti = (bo + (valid ? tok : 0)) * H + h;
+            if (valid) {
+                if (a.rate_law) {
+                    const float uu = tb->u[t];
+                    const float ht = uu >= 0.f ? 1.f + uu : 1.f / (1.f - uu);
+                    const float dht = uu >= 0.f ? 1.f : 1.f / ((1.f - uu) * (1.f - uu));
+                    a.dA[ti] = (-ht < -1e-4f) ? -d_A * dht : 0.f;
+                } else {
+                    dA_acc += d_A;
+                }
+                if (t >= 1) {
+                    a.ddt[ti] = d_dt;
+                    a.dlam[ti] = d_lam;
+                }
+            }
+            // token c0 + 16 (finished but for the delta term from this chunk's last token)
+            const float pdt = __shfl(d_dt, 0, 64), plam = __shfl(d_lam, 0, 64);
+            if (lane == 0) {
+                const int tn = c0 + kBQ;
+                if (tn < L) {
+                    const float dn = tb->ddl_next;
+                    const size_t tin = (bo + tn) * H + h;
+                    a.ddt[tin] = pend_dt + dn * (1.f - tb->lam[kBQ]);
+                    a.dlam[tin] = pend_lam - dn * tb->dt[kBQ];
+                }
+                pend_dt = pdt;
+                pend_lam = plam;
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- the initial carry: Hf_{-1} = H0 + delta_0 x_prev^T B_prev ----
+    const float d0 = tb->dl[0];
+    const int n = 16 * w + s;
+    if (a.dh0) {
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a.dh0[((size_t)bh * kP + 16 * pt + 4 * g4 + i) * kN + n] = gf[pt][i];
+    }
+    float gdot = 0.f;                          // <Gf_in, x_prev^T B_prev>
+    if (a.Bp0 && a.xp0) {
+        float bp[kBR];
+#pragma unroll
+        for (int r = 0; r < kBR; ++r) bp[r] = ld_io(a.Bp0, ((size_t)bh * kBR + r) * kN + n, a.io_bf16);
+        float xb[kBR] = {0.f, 0.f, 0.f, 0.f};  // sum_p x_prev[r][p] Gf[p][n] over the lane's p
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int p = 16 * pt + 4 * g4 + i;
+#pragma unroll
+                for (int r = 0; r < kBR; ++r) {
+                    const float xp = ld_io(a.xp0, ((size_t)bh * kBR + r) * kP + p, a.io_bf16);
+                    xb[r] = fmaf(xp, gf[pt][i], xb[r]);
+                }
+            }
+#pragma unroll
+        for (int r = 0; r < kBR; ++r) {
+            gdot = fmaf(xb[r], bp[r], gdot);
+            // d B_prev[r][n] = delta_0 sum_p x_prev[r][p] Gf[p][n]: sum over the lane groups
+            float tot = xb[r] + __shfl_xor(xb[r], 16, 64);
+            tot += __shfl_xor(tot, 32, 64);
+            if (a.dBp0 && g4 == 0) a.dBp0[((size_t)bh * kBR + r) * kN + n] = d0 * tot;
+        }
+    } else if (a.dBp0) {
+        if (g4 == 0)
+#pragma unroll
+            for (int r = 0; r < kBR; ++r) a.dBp0[((size_t)bh * kBR + r) * kN + n] = 0.f;
+    }
+    // d x_prev[r][p] = delta_0 sum_n Gf[p][n] B_prev[r][n]: per-wave partial rows in LDS
+    float* const red = reinterpret_cast<float*>(smem + oB);    // [8 waves][4 r][64 p]
+    if (a.Bp0 && a.xp0) {
+        float bp[kBR];
+#pragma unroll
+        for (int r = 0; r < kBR; ++r) bp[r] = ld_io(a.Bp0, ((size_t)bh * kBR + r) * kN + n, a.io_bf16);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < kBR; ++r) {
+                    const float v = sum16(gf[pt][i] * bp[r]);
+                    if (s == 0) red[(w * kBR + r) * kP + 16 * pt + 4 * g4 + i] = v;
+                }
+    }
+    gdot = sum64(gdot);
+    if (lane == 0) tb->GH[w] = gdot;
+    __syncthreads();
+    if (a.dxp0 && tid < kBR * kP) {
+        float v = 0.f;
+        if (a.Bp0 && a.xp0)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v += red[k * kBR * kP + tid];
+        a.dxp0[(size_t)bh * kBR * kP + tid] = d0 * v;
+    }
+    if (w == 0 && lane == 0) {
+        float GD = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) GD += tb->GH[k];
+        const size_t t0 = bo * H + h;
+        a.ddt[t0] = pend_dt + GD * (1.f - tb->lam[0]);
+        a.dlam[t0] = pend_lam - GD * tb->dt[0];
+    }
+    if (w == 0 && !a.rate_law) {
+        const float tot = sum64(lane < kBQ ? dA_acc : 0.f);
+        if (lane == 0) unsafeAtomicAdd(a.dA + h, tot * -expf(a.A[h]));
+    }
+    if (w == 1 && lane < np && a.dphi0) a.dphi0[(size_t)bh * np + lane] = Phi;
+    // bias gradients: sum over the lane groups (tokens), then over batches
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float vb = bbias[i] + __shfl_xor(bbias[i], 16, 64);
+        vb += __shfl_xor(vb, 32, 64);
+        float vc = cbias[i] + __shfl_xor(cbias[i], 16, 64);
+        vc += __shfl_xor(vc, 32, 64);
+        if (g4 == 0) {
+            if (a.dBb) unsafeAtomicAdd(a.dBb + ((size_t)h * kBR + i) * kN + n, vb);
+            if (a.dCb) unsafeAtomicAdd(a.dCb + ((size_t)h * kBR + i) * kN + n, vc);
+        }
+    }
+}
+
+}  // namespace
+
+bool scan_bwd_chunked_eligible(int io_bf16, int P, int N, int R, int np, int L) {
+    return io_bf16 && P == kP && N == kN && R == kBR && np >= 0 && np <= kMaxPairs && L >= 1;
+}
+
+size_t scan_bwd_chunked_extra_bytes(int b, int L, int H, int np) {
+    const size_t nch = (size_t)(L + kBQ - 1) / kBQ;
+    return (size_t)b * H * nch * (kHfChunkBytes + (size_t)np * 4) + (size_t)b * H * np * 4;
+}
+
+hipError_t launch_scan_bwd_chunked(const BwdArgs& a, char* extra, hipStream_t s) {
+    const size_t nch = (size_t)(a.L + kBQ - 1) / kBQ;
+    char* hfws = extra;
+    float* phws = reinterpret_cast<float*>(extra + (size_t)a.b * a.H * nch * kHfChunkBytes);
+    float* phl = phws + (size_t)a.b * a.H * nch * a.np;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwdc_state_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kStateLds);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwdc_main_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kMainLds);
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)(a.b * a.H));
+    hipLaunchKernelGGL(bwdc_state_kernel, grid, dim3(kBT), kStateLds, s, a, hfws, phws, phl);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwdc_main_kernel, grid, dim3(kBT), kMainLds, s, a, hfws, phws, phl);
+    return hipGetLastError();
+}
+
+}  // namespace m3

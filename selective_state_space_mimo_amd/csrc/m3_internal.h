@@ -93,12 +93,18 @@ struct BwdArgs {
     float* wphi; float* wdphi;         // [b, L, H, np] running angles, C side of the angle gradient
     float* wdl;                        // [b, L, H] <dy_t, y_t>
     float* wdlf;                       // [b, H] <dh_L, h_L>
+    char* cws;                         // chunked form: chunk states and phases (null: token-serial form)
 };
 struct BwdWs {
-    size_t accB, accC, phi, dphi, dl, dlf, total;   // byte offsets of the workspace parts
+    size_t accB, accC, phi, dphi, dl, dlf, cws, total;   // byte offsets of the workspace parts
 };
 bool scan_bwd_supported(int P, int N, int R, int np);
-BwdWs scan_bwd_workspace(int b, int L, int H, int G, int R, int N, int np);
+// The chunked (matrix-core) form of the backward: bf16 I/O, P 64, N 128, rank 4, at most
+// 64 rotated pairs, at least one token.  Other shapes take the token-serial form.
+bool scan_bwd_chunked_eligible(int io_bf16, int P, int N, int R, int np, int L);
+size_t scan_bwd_chunked_extra_bytes(int b, int L, int H, int np);
+hipError_t launch_scan_bwd_chunked(const BwdArgs& a, char* extra, hipStream_t s);
+BwdWs scan_bwd_workspace(int b, int L, int H, int G, int R, int N, int np, bool chunked);
 hipError_t launch_scan_bwd(const BwdArgs& a, void* dB, void* dC, hipStream_t s);
 
 // ---- host-side launchers (return hipSuccess or the launch error) ----------
