@@ -91,14 +91,14 @@ struct Tab {
     float pend_dt, pend_lam;                        // token c0's gradients without its delta term
     float le;
 };
-constexpr int kMainLds = oTAB + (int)sizeof(Tab);
+constexpr int oRAW = oTAB + (int)((sizeof(Tab) + 15) / 16 * 16);
 
 // ---- LDS layout of the state kernel ----
 constexpr int sX_ = 0;                        // X  [64 m][64 p]
 constexpr int sV_ = sX_ + kBM * kP * 2;       // v Bt [64 m][128 n]
 constexpr int sPH_ = sV_ + kBM * kN * 2;      // phases [16][64]
 constexpr int sTAB_ = sPH_ + kBQ * kMaxPairs * 4;
-constexpr int kStateLds = sTAB_ + (int)sizeof(Tab);
+constexpr int sRAW_ = sTAB_ + (int)((sizeof(Tab) + 15) / 16 * 16);
 
 // A-style operand: lane (g, s) reads row row0 + s, columns kbase + 8 g .. + 7 (16 bytes).
 __device__ __forceinline__ bf16x8 row_op(const char* base, int pitch, int row0, int kbase, int lane) {
@@ -123,31 +123,73 @@ __device__ __forceinline__ void tr4(const char* base, int pitch, int kb, int c0,
 __device__ __forceinline__ float quad_swap(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
 }
-__device__ __forceinline__ float sum16(float v) {        // over the 16 lanes of a lane group
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
+// Sum over the 16 lanes of a lane group, complete in the group's lane 15 (DPP scan).
+__device__ __forceinline__ float sum16_at15(float v) { return group_scan<16>(v, 0); }
+// Sum over the wave, in every lane.
 __device__ __forceinline__ float sum64(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(group_scan<64>(v, 0)), 63));
 }
 __device__ __forceinline__ uint2 pack4(const f32x4& v) { return uint2{pack2(v[0], v[1]), pack2(v[2], v[3])}; }
 
-// The per-token scalars of chunk [c0, c0 + 16) into the table (wave 0; lane t: token
-// c0 + t, lane 16 the token after the chunk).  Tokens at or past L have dt = 0: no decay,
-// no write.
-__device__ void chunk_scalars(const BwdArgs& a, int bi, int h, int c0, int lane, Tab* tb) {
-    const int L = a.L, H = a.H;
-    const int tok = c0 + lane;
-    const bool valid = lane <= kBQ && tok < L;
-    const size_t ti = ((size_t)bi * L + (valid ? tok : 0)) * H + h;
-    const float dt = valid ? a.dt[ti] : 0.f;
-    const float lam = valid ? a.lam[ti] : 0.f;
+// A chunk's raw per-token inputs, staged in LDS a chunk ahead of their use: dt, lambda and
+// the rate input of tokens c0 .. c0 + 16 and theta of tokens c0 .. c0 + 15 (zero past L).
+struct Raw {
+    float th[kBQ][kMaxPairs];
+    float dt[kBQ + 1], lam[kBQ + 1], ra[kBQ + 1];
+};
+struct RawRegs {
+    float th0, th1, sc;
+};
+__device__ __forceinline__ RawRegs load_raw(const BwdArgs& a, int bi, int h, int c0, int tid) {
+    const int L = a.L, H = a.H, np = a.np;
+    RawRegs r{0.f, 0.f, 0.f};
+    if (np > 0) {
+        const int e0 = tid, e1 = tid + kBT;
+        if (e0 < kBQ * np) {
+            const int t = e0 / np, j = e0 - t * np, tok = c0 + t;
+            if (tok < L) r.th0 = a.theta[(((size_t)bi * L + tok) * H + h) * np + j];
+        }
+        if (e1 < kBQ * np) {
+            const int t = e1 / np, j = e1 - t * np, tok = c0 + t;
+            if (tok < L) r.th1 = a.theta[(((size_t)bi * L + tok) * H + h) * np + j];
+        }
+    }
+    if (tid < 3 * (kBQ + 1)) {
+        const int kind = tid / (kBQ + 1), t = tid - kind * (kBQ + 1), tok = c0 + t;
+        if (tok < L) {
+            const size_t ti = ((size_t)bi * L + tok) * H + h;
+            if (kind == 0) r.sc = a.dt[ti];
+            else if (kind == 1) r.sc = a.lam[ti];
+            else if (a.rate_law) r.sc = a.A[ti];
+        }
+    }
+    return r;
+}
+__device__ __forceinline__ void store_raw(const RawRegs& r, int np, int tid, Raw* raw) {
+    if (np > 0) {
+        const int e0 = tid, e1 = tid + kBT;
+        if (e0 < kBQ * np) { const int t = e0 / np; raw->th[t][e0 - t * np] = r.th0; }
+        if (e1 < kBQ * np) { const int t = e1 / np; raw->th[t][e1 - t * np] = r.th1; }
+    }
+    if (tid < 3 * (kBQ + 1)) {
+        const int kind = tid / (kBQ + 1), t = tid - kind * (kBQ + 1);
+        (kind == 0 ? raw->dt : kind == 1 ? raw->lam : raw->ra)[t] = r.sc;
+    }
+}
+
+constexpr int kMainLds = oRAW + (int)sizeof(Raw);
+constexpr int kStateLds = sRAW_ + (int)sizeof(Raw);
+
+// The per-token scalars of the chunk into the table (wave 0; lane t: token c0 + t, lane 16
+// the token after the chunk).  Tokens at or past L have dt = 0: no decay, no write.
+__device__ void chunk_scalars(const BwdArgs& a, const Raw* raw, int h, int lane, Tab* tb) {
+    const bool in = lane <= kBQ;
+    const int li = in ? lane : 0;
+    const float dt = in ? raw->dt[li] : 0.f;
+    const float lam = in ? raw->lam[li] : 0.f;
     float rate = 0.f, u = 0.f;
     if (a.rate_law) {
-        u = valid ? a.A[ti] : 0.f;
+        u = in ? raw->ra[li] : 0.f;
         rate = -heavy_tail_rate(u);
     } else {
         rate = expf(a.A[h]);
@@ -165,7 +207,7 @@ __device__ void chunk_scalars(const BwdArgs& a, int bi, int h, int c0, int lane,
         tb->a[lane] = rate;
         tb->u[lane] = u;
     }
-    if (lane <= kBQ) {
+    if (in) {
         tb->dl[lane] = dl;
         tb->dt[lane] = dt;
         tb->lam[lane] = lam;
@@ -176,15 +218,10 @@ __device__ void chunk_scalars(const BwdArgs& a, int bi, int h, int c0, int lane,
 // Phases of the chunk's tokens (wave 1, lane j < np: pair j) from the chunk's starting
 // phase phi (wrapped): ph[t][j] = phi + sum_{k <= t} dt_k theta_k[j].  Returns the phase
 // after the chunk.
-__device__ float chunk_phases(const BwdArgs& a, int bi, int h, int c0, int j, float phi, float* ph) {
-    const int L = a.L, H = a.H, np = a.np;
-#pragma unroll 4
+__device__ float chunk_phases(const Raw* raw, int j, float phi, float* ph) {
+#pragma unroll
     for (int t = 0; t < kBQ; ++t) {
-        const int tok = c0 + t;
-        if (tok < L) {
-            const size_t ti = ((size_t)bi * L + tok) * H + h;
-            phi = fmaf(a.dt[ti], a.theta[ti * np + j], phi);
-        }
+        phi = fmaf(raw->dt[t], raw->th[t][j], phi);
         ph[t * kMaxPairs + j] = phi;
     }
     return phi;
@@ -265,16 +302,22 @@ __global__ __launch_bounds__(kBT) void bwdc_state_kernel(BwdArgs a, char* hfws, 
             }
     }
     float phi = (w == 1 && lane < np && a.phi0) ? a.phi0[(size_t)bh * np + lane] : 0.f;
+    Raw* const raw = reinterpret_cast<Raw*>(smem + sRAW_);
+    store_raw(load_raw(a, bi, h, 0, tid), np, tid, raw);
+    __syncthreads();
 
     for (int c = 0; c < nch; ++c) {
         const int c0 = c * kBQ;
-        if (w == 0) chunk_scalars(a, bi, h, c0, lane, tb);
+        if (w == 0) chunk_scalars(a, raw, h, lane, tb);
         if (w == 1 && lane < np) {
             phi = wrap_2pi(phi);
             phws[((size_t)bh * nch + c) * np + lane] = phi;
-            phi = chunk_phases(a, bi, h, c0, lane, phi, ph);
+            phi = chunk_phases(raw, lane, phi, ph);
         }
         __syncthreads();
+        const bool more = c + 1 < nch;
+        RawRegs nx{0.f, 0.f, 0.f};
+        if (more) nx = load_raw(a, bi, h, c0 + kBQ, tid);
         {
             // X rows and v-scaled turned B rows (row m = tid / 8, piece tid % 8)
             const int m = tid >> 3, q8 = tid & 7, t = m >> 2, r = m & 3, tok = c0 + t;
@@ -301,6 +344,7 @@ __global__ __launch_bounds__(kBT) void bwdc_state_kernel(BwdArgs a, char* hfws, 
                 *reinterpret_cast<uint2*>(dst + (n * kP + 16 * pt + 4 * g4) * 2) = pack4(hf[pt]);
         }
         __syncthreads();
+        if (more) store_raw(nx, np, tid, raw);
         // Hf = exp(l_e) Hf + X^T (v Bt): rows p (A = X^T by transposing reads), columns n
         const float fe = __expf(tb->le);
 #pragma unroll
@@ -396,11 +440,15 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
     float dA_acc = 0.f;                       // static rate law: sum of d A over tokens (wave 0)
     float pend_dt = 0.f, pend_lam = 0.f;      // token c0 + 16 of the previous iteration (wave 0, lane 0)
 
+    Raw* const raw = reinterpret_cast<Raw*>(smem + oRAW);
+    store_raw(load_raw(a, bi, h, (nch - 1) * kBQ, tid), np, tid, raw);
+    __syncthreads();
+
     for (int c = nch - 1; c >= 0; --c) {
         const int c0 = c * kBQ;
         // ---- S0a: scalars, phases ----
-        if (w == 0) chunk_scalars(a, bi, h, c0, lane, tb);
-        if (w == 1 && lane < np) chunk_phases(a, bi, h, c0, lane, phws[((size_t)bh * nch + c) * np + lane], ph);
+        if (w == 0) chunk_scalars(a, raw, h, lane, tb);
+        if (w == 1 && lane < np) chunk_phases(raw, lane, phws[((size_t)bh * nch + c) * np + lane], ph);
         __syncthreads();
         // ---- S0b: staging ----
         {
@@ -445,6 +493,9 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
             for (int pt = 0; pt < 4; ++pt) hown[pt] = *reinterpret_cast<const uint2*>(hin + (n * kP + 16 * pt + 4 * g4) * 2);
         }
         __syncthreads();
+        // the next chunk's raw inputs, staged in LDS once this chunk's are used (S3b)
+        RawRegs nx{0.f, 0.f, 0.f};
+        if (c > 0) nx = load_raw(a, bi, h, c0 - kBQ, tid);
         // ---- S1: score tiles S^T, S2^T (rows u', columns m), weights, P(t, u) ----
         {
             const int mt = w & 3;
@@ -495,8 +546,8 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
             float rs = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) { dc[i] = fmaf(E, a2[i], a1[i]); rs = fmaf(cv[i], a2[i], rs); }
-            rs = sum16(rs);
-            if (s == 0) tb->RHp[w][t] = rs;
+            rs = sum16_at15(rs);
+            if (s == 15) tb->RHp[w][t] = rs;
             float sn = 0.f, cs = 1.f;
             if (turns) __sincosf(wrap_2pi(ph[t * kMaxPairs + pair]), &sn, &cs);
             float dpp = 0.f, outv[4];
@@ -575,8 +626,8 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
                 float q = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) q = fmaf(xv[i], z[i], q);
-                q = sum16(q);
-                if (s == 0) tb->Qp[pt][u] = q;
+                q = sum16_at15(q);
+                if (s == 15) tb->Qp[pt][u] = q;
                 if (tok < L) {
                     const size_t row = ((bo + tok) * H + h) * kBR * kP + p;
 #pragma unroll
@@ -649,11 +700,13 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
             // column u: tail = sum_{t > u} exp(l_t - l_u) P(t, u); the corner terms
             // exp(l_t' - l_u) wv_u P(t', u) summed over t' >= t, for every t > u
             float tail = 0.f, cs = 0.f;
-            for (int t = kBQ - 1; t > u; --t) {
-                const float ep = __expf(fminf(tb->l[t] - lu, 0.f)) * sPM[t * kBQ + u];
+#pragma unroll 5
+            for (int t = kBQ - 1; t >= 1; --t) {
+                const bool act = t > u;
+                const float ep = act ? __expf(fminf(tb->l[t] - lu, 0.f)) * sPM[t * kBQ + u] : 0.f;
                 tail += ep;
                 cs = fmaf(wv, ep, cs);
-                if (ul) tb->K[t][u] = cs;
+                if (act && ul) tb->K[t][u] = cs;
             }
             const float diagP = sPM[u * kBQ + u];
             const float endq = __expf(fminf(le - lu, 0.f)) * Qu;
@@ -668,7 +721,8 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             float corner = 0.f;
-            for (int k = 0; k < u; ++k) corner += tb->K[u][k];
+#pragma unroll
+            for (int k = 0; k < kBQ - 1; ++k) corner += k < u ? tb->K[u][k] : 0.f;
             const float dla = suf + __expf(le) * GH + pre + corner;
             const float dnext = tail + endq;                    // d delta of token u + 1
             const float dprev = __shfl_up(dnext, 1, 64);        // lane u: d delta of token u (u >= 1)
@@ -680,20 +734,32 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
             if (lane == kBQ - 1) tb->ddl_next = dnext;
         }
         if (w == 1) {
+            // Phi from the chunk's end back to its start; theta_t . Phi_t per pair into the
+            // B-side table (each lane overwrites only what it has read), then row sums
             const bool pl = lane < np;
+            float* const tpt = dphB;
+#pragma unroll 4
             for (int t = kBQ - 1; t >= 0; --t) {
                 const int tok = c0 + t;
                 float tp = 0.f;
                 if (pl) {
                     Phi += dphB[t * kMaxPairs + lane] + dphC[t * kMaxPairs + lane];
-                    if (tok < L) {
-                        const size_t ti = (bo + tok) * H + h;
-                        a.dtheta[ti * np + lane] = tb->dt[t] * Phi;
-                        tp = a.theta[ti * np + lane] * Phi;
-                    }
+                    if (tok < L) a.dtheta[((bo + tok) * H + h) * np + lane] = tb->dt[t] * Phi;
+                    tp = raw->th[t][lane] * Phi;
                 }
-                tp = sum64(tp);
-                if (lane == 0) tb->TP[t] = tp;
+                tpt[t * kMaxPairs + lane] = tp;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (lane < kBQ) {
+                float acc = 0.f;
+#pragma unroll
+                for (int j = 0; j < kMaxPairs; j += 4) {
+                    const float4 q = *reinterpret_cast<const float4*>(tpt + lane * kMaxPairs + j);
+                    acc += (q.x + q.y) + (q.z + q.w);
+                }
+                tb->TP[lane] = acc;
             }
             if (pl) Phi = PhiL - tb->phb[lane];                 // Phi at the chunk's first token
         }
@@ -735,6 +801,7 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
                 pend_lam = plam;
             }
         }
+        if (c > 0) store_raw(nx, np, tid, raw);
         __syncthreads();
     }
 
@@ -789,8 +856,8 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int r = 0; r < kBR; ++r) {
-                    const float v = sum16(gf[pt][i] * bp[r]);
-                    if (s == 0) red[(w * kBR + r) * kP + 16 * pt + 4 * g4 + i] = v;
+                    const float v = sum16_at15(gf[pt][i] * bp[r]);
+                    if (s == 15) red[(w * kBR + r) * kP + 16 * pt + 4 * g4 + i] = v;
                 }
     }
     gdot = sum64(gdot);
