@@ -100,24 +100,33 @@ constexpr int sPH_ = sV_ + kBM * kN * 2;      // phases [16][64]
 constexpr int sTAB_ = sPH_ + kBQ * kMaxPairs * 4;
 constexpr int sRAW_ = sTAB_ + (int)((sizeof(Tab) + 15) / 16 * 16);
 
+// Byte offset of element (row, col) of a bf16 tile with 128- or 256-byte rows.  The 16-byte
+// groups of a row are XOR-permuted by the row (256-byte rows: by row mod 16; 128-byte rows,
+// two to a bank cycle: by (row / 2) mod 8), so that 16 consecutive rows reading one group,
+// and 4 rows reading a pair of groups (the transposing reads), fall on distinct banks.
+__device__ __forceinline__ int swz(int pitch, int row, int col) {
+    const int grp = col >> 3;
+    const int x = pitch == 256 ? (row & 15) : ((row >> 1) & 7);
+    return row * pitch + ((grp ^ x) << 4) + (col & 7) * 2;
+}
 // A-style operand: lane (g, s) reads row row0 + s, columns kbase + 8 g .. + 7 (16 bytes).
 __device__ __forceinline__ bf16x8 row_op(const char* base, int pitch, int row0, int kbase, int lane) {
     const int g = lane >> 4, s = lane & 15;
-    return *reinterpret_cast<const bf16x8*>(base + (row0 + s) * pitch + (kbase + 8 * g) * 2);
+    return *reinterpret_cast<const bf16x8*>(base + swz(pitch, row0 + s, kbase + 8 * g));
 }
 // B-style operand from a row-major tile by transposing reads: lane (g, s) receives column
 // c0 + s at rows kbase + 8 g .. + 7 (two reads of four rows).
 __device__ __forceinline__ bf16x8 tr_op(const char* base, int pitch, int kbase, int c0, int lane) {
     const int g = lane >> 4, s = lane & 15;
-    const char* p = base + (kbase + 8 * g + (s >> 2)) * pitch + (c0 + 4 * (s & 3)) * 2;
-    const uint2 lo = ds_tr(p);
-    const uint2 hi = ds_tr(p + 4 * pitch);
+    const int row = kbase + 8 * g + (s >> 2), col = c0 + 4 * (s & 3);
+    const uint2 lo = ds_tr(base + swz(pitch, row, col));
+    const uint2 hi = ds_tr(base + swz(pitch, row + 4, col));
     return __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
 }
 // Four rows kb .. kb + 3 of column c0 + s (lane (g, s); kb chosen per lane group).
 __device__ __forceinline__ void tr4(const char* base, int pitch, int kb, int c0, int lane, float out[4]) {
     const int s = lane & 15;
-    const uint2 v = ds_tr(base + (kb + (s >> 2)) * pitch + (c0 + 4 * (s & 3)) * 2);
+    const uint2 v = ds_tr(base + swz(pitch, kb + (s >> 2), c0 + 4 * (s & 3)));
     out[0] = lo_f(v.x); out[1] = hi_f(v.x); out[2] = lo_f(v.y); out[3] = hi_f(v.y);
 }
 __device__ __forceinline__ float quad_swap(float v) {
@@ -326,14 +335,14 @@ __global__ __launch_bounds__(kBT) void bwdc_state_kernel(BwdArgs a, char* hfws, 
             if (valid)
                 xv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) +
                                                      (((size_t)bi * L + tok) * H + h) * kBR * kP + r * kP + 8 * q8);
-            *reinterpret_cast<uint4*>(sX + m * (kP * 2) + q8 * 16) = xv;
+            *reinterpret_cast<uint4*>(sX + swz(kP * 2, m, 8 * q8)) = xv;
             const uint16_t* raw = valid ? static_cast<const uint16_t*>(a.B) + (((size_t)bi * L + tok) * G + gg) * kBR * kN + r * kN
                                         : nullptr;
             const float* bias = a.Bb ? a.Bb + ((size_t)h * kBR + r) * kN : nullptr;
             uint32_t o[8];
             turn_piece(raw, bias, ph + t * kMaxPairs, np, 16 * q8, tb->v[t], o);
-            *reinterpret_cast<uint4*>(sV + m * (kN * 2) + q8 * 32) = uint4{o[0], o[1], o[2], o[3]};
-            *reinterpret_cast<uint4*>(sV + m * (kN * 2) + q8 * 32 + 16) = uint4{o[4], o[5], o[6], o[7]};
+            *reinterpret_cast<uint4*>(sV + swz(kN * 2, m, 16 * q8)) = uint4{o[0], o[1], o[2], o[3]};
+            *reinterpret_cast<uint4*>(sV + swz(kN * 2, m, 16 * q8 + 8)) = uint4{o[4], o[5], o[6], o[7]};
         }
         // the chunk's incoming state, n-major: lane writes p = 16 pt + 4 g4 .. + 3 of column n
         {
@@ -460,24 +469,24 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
                 xv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + xrow);
                 dv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.dy) + xrow);
             }
-            *reinterpret_cast<uint4*>(sX + m * (kP * 2) + q8 * 16) = xv;
-            *reinterpret_cast<uint4*>(sDY + m * (kP * 2) + q8 * 16) = dv;
+            *reinterpret_cast<uint4*>(sX + swz(kP * 2, m, 8 * q8)) = xv;
+            *reinterpret_cast<uint4*>(sDY + swz(kP * 2, m, 8 * q8)) = dv;
             const size_t brow = ((bo + (valid ? tok : 0)) * G + gg) * kBR * kN + r * kN;
             uint32_t o[8];
             turn_piece(valid ? static_cast<const uint16_t*>(a.B) + brow : nullptr,
                        a.Bb ? a.Bb + ((size_t)h * kBR + r) * kN : nullptr, ph + t * kMaxPairs, np, 16 * q8, 1.f, o);
-            *reinterpret_cast<uint4*>(sB + m * (kN * 2) + q8 * 32) = uint4{o[0], o[1], o[2], o[3]};
-            *reinterpret_cast<uint4*>(sB + m * (kN * 2) + q8 * 32 + 16) = uint4{o[4], o[5], o[6], o[7]};
+            *reinterpret_cast<uint4*>(sB + swz(kN * 2, m, 16 * q8)) = uint4{o[0], o[1], o[2], o[3]};
+            *reinterpret_cast<uint4*>(sB + swz(kN * 2, m, 16 * q8 + 8)) = uint4{o[4], o[5], o[6], o[7]};
             turn_piece(valid ? static_cast<const uint16_t*>(a.C) + brow : nullptr,
                        a.Cb ? a.Cb + ((size_t)h * kBR + r) * kN : nullptr, ph + t * kMaxPairs, np, 16 * q8, 1.f, o);
-            *reinterpret_cast<uint4*>(sC + m * (kN * 2) + q8 * 32) = uint4{o[0], o[1], o[2], o[3]};
-            *reinterpret_cast<uint4*>(sC + m * (kN * 2) + q8 * 32 + 16) = uint4{o[4], o[5], o[6], o[7]};
+            *reinterpret_cast<uint4*>(sC + swz(kN * 2, m, 16 * q8)) = uint4{o[0], o[1], o[2], o[3]};
+            *reinterpret_cast<uint4*>(sC + swz(kN * 2, m, 16 * q8 + 8)) = uint4{o[4], o[5], o[6], o[7]};
         }
         {
             const int n = 16 * w + s;
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt)
-                *reinterpret_cast<uint2*>(sG + (n * kP + 16 * pt + 4 * g4) * 2) = pack4(gf[pt]);
+                *reinterpret_cast<uint2*>(sG + swz(kP * 2, n, 16 * pt + 4 * g4)) = pack4(gf[pt]);
         }
         // Hf_in pieces: B operands of dy Hf_in (column n = 16 w + s, k = p) and the lane's
         // own elements of the state tiles (for <Gf_out, Hf_in>)
@@ -516,8 +525,8 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
                 const f32x4 m1 = {wt * s2[0], wt * s2[1], wt * s2[2], wt * s2[3]};
                 const f32x4 m2 = {wt * st[0], wt * st[1], wt * st[2], wt * st[3]};
                 const int m = 16 * mt + s;
-                *reinterpret_cast<uint2*>(sM1 + m * (kBM * 2) + (16 * ut + 4 * g4) * 2) = pack4(m1);
-                *reinterpret_cast<uint2*>(sM2 + m * (kBM * 2) + (16 * ut + 4 * g4) * 2) = pack4(m2);
+                *reinterpret_cast<uint2*>(sM1 + swz(kBM * 2, m, 16 * ut + 4 * g4)) = pack4(m1);
+                *reinterpret_cast<uint2*>(sM2 + swz(kBM * 2, m, 16 * ut + 4 * g4)) = pack4(m2);
                 float pr = st[0] * s2[0] + st[1] * s2[1] + st[2] * s2[2] + st[3] * s2[3];
                 pr += quad_swap(pr);
                 pr += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(pr), 0x4E, 0xf, 0xf, false));
