@@ -618,7 +618,7 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
         // (c) dX = (W S)^T dy + v_u Z, Z = Bt Gf_out^T   (rows u', column p)
         {
             const int pt = w & 3, p = 16 * pt + s;
-#pragma unroll
+#pragma unroll 1
             for (int k2 = 0; k2 < 2; ++k2) {
                 const int ut = 2 * (w >> 2) + k2;
                 f32x4 z = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
@@ -661,7 +661,7 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
             gh = sum64(gh);
             if (lane == 0) tb->GH[w] = gh;
             const float fe = __expf(tb->le);
-#pragma unroll
+#pragma unroll 2
             for (int pt = 0; pt < 4; ++pt) {
                 f32x4 acc = {gf[pt][0] * fe, gf[pt][1] * fe, gf[pt][2] * fe, gf[pt][3] * fe};
 #pragma unroll
