@@ -71,8 +71,8 @@ constexpr int oC = oB + kBM * kN * 2;         // Ct   [64 m][128 n]
 constexpr int oG = oC + kBM * kN * 2;         // Gf_out [128 n][64 p] (bf16 copy)
 constexpr int oM1 = oG + kN * kP * 2;         // W S2^T stored as [64 m][64 u']
 constexpr int oM2 = oM1 + kBM * kBM * 2;      // W S^T  stored as [64 m][64 u']
-constexpr int oPH = oM2 + kBM * kBM * 2;      // phases [16 t][64 pair] fp32
-constexpr int oDPB = oPH + kBQ * kMaxPairs * 4;   // B side of d phi [16][64]
+constexpr int oPH = oM2 + kBM * kBM * 2;      // (cos, sin) of the phases [16 t][64 pair]
+constexpr int oDPB = oPH + kBQ * kMaxPairs * 8;   // B side of d phi [16][64]
 constexpr int oDPC = oDPB + kBQ * kMaxPairs * 4;  // C side of d phi [16][64]
 constexpr int oPM = oDPC + kBQ * kMaxPairs * 4;   // P(t, u) [16][16]
 constexpr int oTAB = oPM + kBQ * kBQ * 4;
@@ -96,8 +96,8 @@ constexpr int oRAW = oTAB + (int)((sizeof(Tab) + 15) / 16 * 16);
 // ---- LDS layout of the state kernel ----
 constexpr int sX_ = 0;                        // X  [64 m][64 p]
 constexpr int sV_ = sX_ + kBM * kP * 2;       // v Bt [64 m][128 n]
-constexpr int sPH_ = sV_ + kBM * kN * 2;      // phases [16][64]
-constexpr int sTAB_ = sPH_ + kBQ * kMaxPairs * 4;
+constexpr int sPH_ = sV_ + kBM * kN * 2;      // (cos, sin) of the phases [16][64]
+constexpr int sTAB_ = sPH_ + kBQ * kMaxPairs * 8;
 constexpr int sRAW_ = sTAB_ + (int)((sizeof(Tab) + 15) / 16 * 16);
 
 // Byte offset of element (row, col) of a bf16 tile with 128- or 256-byte rows.  The 16-byte
@@ -225,20 +225,23 @@ __device__ void chunk_scalars(const BwdArgs& a, const Raw* raw, int h, int lane,
 }
 
 // Phases of the chunk's tokens (wave 1, lane j < np: pair j) from the chunk's starting
-// phase phi (wrapped): ph[t][j] = phi + sum_{k <= t} dt_k theta_k[j].  Returns the phase
+// phase phi (wrapped): phi_t[j] = phi + sum_{k <= t} dt_k theta_k[j]; their cos and sin
+// (hardware forms of the phase wrapped into [0, 2 pi)) into the table.  Returns the phase
 // after the chunk.
-__device__ float chunk_phases(const Raw* raw, int j, float phi, float* ph) {
+__device__ float chunk_phases(const Raw* raw, int j, float phi, float2* cst) {
 #pragma unroll
     for (int t = 0; t < kBQ; ++t) {
         phi = fmaf(raw->dt[t], raw->th[t][j], phi);
-        ph[t * kMaxPairs + j] = phi;
+        float sn, cs;
+        __sincosf(wrap_2pi(phi), &sn, &cs);
+        cst[t * kMaxPairs + j] = float2{cs, sn};
     }
     return phi;
 }
 
 // 16 turned values of row (token, rank) at columns n0 .. n0 + 15: raw + bias, pairs
 // (2 j, 2 j + 1) with j < np rotated by the token's phases, times scale; bf16 pairs out.
-__device__ __forceinline__ void turn_piece(const uint16_t* raw, const float* bias, const float* ph, int np, int n0,
+__device__ __forceinline__ void turn_piece(const uint16_t* raw, const float* bias, const float2* cst, int np, int n0,
                                            float scale, uint32_t out[8]) {
     float v[16];
     if (raw) {
@@ -263,9 +266,8 @@ __device__ __forceinline__ void turn_piece(const uint16_t* raw, const float* bia
         const int j = (n0 >> 1) + k;
         float e = v[2 * k], o = v[2 * k + 1];
         if (j < np) {
-            float sn, cs;
-            __sincosf(wrap_2pi(ph[j]), &sn, &cs);
-            const float e2 = e * cs - o * sn, o2 = e * sn + o * cs;
+            const float2 c = cst[j];
+            const float e2 = e * c.x - o * c.y, o2 = e * c.y + o * c.x;
             e = e2; o = o2;
         }
         out[k] = pack2(e * scale, o * scale);
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(kBT) void bwdc_state_kernel(BwdArgs a, char* hfws, 
     const int nch = (L + kBQ - 1) / kBQ;
     char* const sX = smem + sX_;
     char* const sV = smem + sV_;
-    float* const ph = reinterpret_cast<float*>(smem + sPH_);
+    float2* const ph = reinterpret_cast<float2*>(smem + sPH_);
     Tab* const tb = reinterpret_cast<Tab*>(smem + sTAB_);
 
     // Hf_{-1} = H0 + delta_0 x_prev^T B_prev (the initial carry, folded); wave w owns n-tile w
@@ -392,8 +394,7 @@ __global__ __launch_bounds__(kBT) void bwdc_state_kernel(BwdArgs a, char* hfws, 
         const int j = tid, tl = (L - 1) - (nch - 1) * kBQ;
         float v = hterm[j] + (a.dphi1 ? a.dphi1[(size_t)bh * np + j] : 0.f);
         if (a.dBp1) {
-            float sn, cs;
-            __sincosf(wrap_2pi(ph[tl * kMaxPairs + j]), &sn, &cs);
+            const float sn = ph[tl * kMaxPairs + j].y, cs = ph[tl * kMaxPairs + j].x;
             const size_t tok = (size_t)bi * L + (L - 1);
 #pragma unroll
             for (int r = 0; r < kBR; ++r) {
@@ -429,7 +430,7 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
     char* const sG = smem + oG;
     char* const sM1 = smem + oM1;
     char* const sM2 = smem + oM2;
-    float* const ph = reinterpret_cast<float*>(smem + oPH);
+    float2* const ph = reinterpret_cast<float2*>(smem + oPH);
     float* const dphB = reinterpret_cast<float*>(smem + oDPB);
     float* const dphC = reinterpret_cast<float*>(smem + oDPC);
     float* const sPM = reinterpret_cast<float*>(smem + oPM);
@@ -539,6 +540,7 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
         const bool odd = (s & 1) != 0;
         const int pair = n >> 1;
         const bool turns = pair < np;
+        const bool wturn = 8 * nt < np;                        // any turning pair in this wave's n-tile
         // (a) dCt = W S2 Bt + exp(l_t) dy Hf_in   (rows m, column n)
 #pragma unroll 1
         for (int mt = 0; mt < 4; ++mt) {
@@ -557,19 +559,26 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
             for (int i = 0; i < 4; ++i) { dc[i] = fmaf(E, a2[i], a1[i]); rs = fmaf(cv[i], a2[i], rs); }
             rs = sum16_at15(rs);
             if (s == 15) tb->RHp[w][t] = rs;
-            float sn = 0.f, cs = 1.f;
-            if (turns) __sincosf(wrap_2pi(ph[t * kMaxPairs + pair]), &sn, &cs);
-            float dpp = 0.f, outv[4];
+            float outv[4];
+            if (wturn) {
+                const float2 cq = ph[t * kMaxPairs + pair];
+                const float cs = turns ? cq.x : 1.f, sn = turns ? cq.y : 0.f;
+                float dpp = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float pv = quad_swap(cv[i]), pd = quad_swap(dc[i]);
-                const float e = odd ? pv : cv[i], o = odd ? cv[i] : pv;
-                const float de = odd ? pd : dc[i], dO = odd ? dc[i] : pd;
-                dpp += -de * o + dO * e;
-                outv[i] = turns ? (odd ? -de * sn + dO * cs : de * cs + dO * sn) : dc[i];
-                cbias[i] += outv[i];
+                for (int i = 0; i < 4; ++i) {
+                    const float pv = quad_swap(cv[i]), pd = quad_swap(dc[i]);
+                    const float e = odd ? pv : cv[i], o = odd ? cv[i] : pv;
+                    const float de = odd ? pd : dc[i], dO = odd ? dc[i] : pd;
+                    dpp += -de * o + dO * e;
+                    outv[i] = odd ? -de * sn + dO * cs : de * cs + dO * sn;
+                }
+                if (turns && !odd) dphC[t * kMaxPairs + pair] = dpp;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) outv[i] = dc[i];
             }
-            if (turns && !odd) dphC[t * kMaxPairs + pair] = dpp;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cbias[i] += outv[i];
             if (tok < L) {
                 float* acc = a.accC + ((bo + tok) * G + gg) * kBR * kN + n;
 #pragma unroll
@@ -596,19 +605,26 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
 #pragma unroll
                 for (int i = 0; i < 4; ++i) db[i] += a.dBp1[((size_t)bh * kBR + i) * kN + n];
             }
-            float sn = 0.f, cs = 1.f;
-            if (turns) __sincosf(wrap_2pi(ph[u * kMaxPairs + pair]), &sn, &cs);
-            float dpp = 0.f, outv[4];
+            float outv[4];
+            if (wturn) {
+                const float2 cq = ph[u * kMaxPairs + pair];
+                const float cs = turns ? cq.x : 1.f, sn = turns ? cq.y : 0.f;
+                float dpp = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float pv = quad_swap(bv[i]), pd = quad_swap(db[i]);
-                const float e = odd ? pv : bv[i], o = odd ? bv[i] : pv;
-                const float de = odd ? pd : db[i], dO = odd ? db[i] : pd;
-                dpp += -de * o + dO * e;
-                outv[i] = turns ? (odd ? -de * sn + dO * cs : de * cs + dO * sn) : db[i];
-                bbias[i] += outv[i];
+                for (int i = 0; i < 4; ++i) {
+                    const float pv = quad_swap(bv[i]), pd = quad_swap(db[i]);
+                    const float e = odd ? pv : bv[i], o = odd ? bv[i] : pv;
+                    const float de = odd ? pd : db[i], dO = odd ? db[i] : pd;
+                    dpp += -de * o + dO * e;
+                    outv[i] = odd ? -de * sn + dO * cs : de * cs + dO * sn;
+                }
+                if (turns && !odd) dphB[u * kMaxPairs + pair] = dpp;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) outv[i] = db[i];
             }
-            if (turns && !odd) dphB[u * kMaxPairs + pair] = dpp;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bbias[i] += outv[i];
             if (tok < L) {
                 float* acc = a.accB + ((bo + tok) * G + gg) * kBR * kN + n;
 #pragma unroll
