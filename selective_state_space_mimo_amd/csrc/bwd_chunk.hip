@@ -129,6 +129,12 @@ __device__ __forceinline__ void tr4(const char* base, int pitch, int kb, int c0,
     const uint2 v = ds_tr(base + swz(pitch, kb + (s >> 2), c0 + 4 * (s & 3)));
     out[0] = lo_f(v.x); out[1] = hi_f(v.x); out[2] = lo_f(v.y); out[3] = hi_f(v.y);
 }
+// Workgroup barrier for LDS traffic only.  A __syncthreads() is also a release fence for
+// global memory, which waits for every store and atomic in flight; the chunk loops write
+// global memory that no wave of the workgroup reads back, so they wait for LDS only.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 __device__ __forceinline__ float quad_swap(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
 }
@@ -149,29 +155,46 @@ struct Raw {
 struct RawRegs {
     float th0, th1, sc;
 };
+// Global memory goes through buffer resources whose record counts end at the last valid
+// token, with every load, store and atomic issued unconditionally: a token past L reads
+// zero and its writes are dropped (an offset of kOOB is always out of range).  A memory
+// operation under a lane-dependent branch would make the compiler wait for every
+// operation in flight (the memory counter counts in issue order).
+constexpr int kOOB = 0x7ffffff0;
+__device__ __forceinline__ float ldf(__amdgpu_buffer_rsrc_t r, int off) {
+    return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void stf(__amdgpu_buffer_rsrc_t r, int off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+// rows of tokens c0 .. c0 + n - 1 of a [.., L, S, ...] tensor at one (batch, slot): base
+// element e0, `row` elements a token, `w` elements read per token
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tok_rsrc(const void* base, size_t e0, int esize, int n, int row, int w) {
+    const char* p = base ? static_cast<const char*>(base) + e0 * esize : nullptr;
+    return make_rsrc(p, base && n > 0 ? (uint32_t)(((n - 1) * row + w) * esize) : 0u);
+}
+
 __device__ __forceinline__ RawRegs load_raw(const BwdArgs& a, int bi, int h, int c0, int tid) {
     const int L = a.L, H = a.H, np = a.np;
+    const int nv = min(kBQ, L - c0), ns = min(kBQ + 1, L - c0);
+    const size_t t0 = ((size_t)bi * L + c0) * H + h;
     RawRegs r{0.f, 0.f, 0.f};
     if (np > 0) {
+        const __amdgpu_buffer_rsrc_t rth = tok_rsrc(a.theta, t0 * np, 4, nv, H * np, np);
         const int e0 = tid, e1 = tid + kBT;
-        if (e0 < kBQ * np) {
-            const int t = e0 / np, j = e0 - t * np, tok = c0 + t;
-            if (tok < L) r.th0 = a.theta[(((size_t)bi * L + tok) * H + h) * np + j];
-        }
-        if (e1 < kBQ * np) {
-            const int t = e1 / np, j = e1 - t * np, tok = c0 + t;
-            if (tok < L) r.th1 = a.theta[(((size_t)bi * L + tok) * H + h) * np + j];
-        }
+        const int ta = e0 / np, tb_ = e1 / np;
+        r.th0 = ldf(rth, e0 < kBQ * np ? (ta * H * np + e0 - ta * np) * 4 : kOOB);
+        r.th1 = ldf(rth, e1 < kBQ * np ? (tb_ * H * np + e1 - tb_ * np) * 4 : kOOB);
     }
-    if (tid < 3 * (kBQ + 1)) {
-        const int kind = tid / (kBQ + 1), t = tid - kind * (kBQ + 1), tok = c0 + t;
-        if (tok < L) {
-            const size_t ti = ((size_t)bi * L + tok) * H + h;
-            if (kind == 0) r.sc = a.dt[ti];
-            else if (kind == 1) r.sc = a.lam[ti];
-            else if (a.rate_law) r.sc = a.A[ti];
-        }
-    }
+    const int kind = tid / (kBQ + 1), t = tid - kind * (kBQ + 1);
+    const int off = tid < 3 * (kBQ + 1) ? t * H * 4 : kOOB;
+    const float vdt = ldf(tok_rsrc(a.dt, t0, 4, ns, H, 1), kind == 0 ? off : kOOB);
+    const float vlm = ldf(tok_rsrc(a.lam, t0, 4, ns, H, 1), kind == 1 ? off : kOOB);
+    const float vra = ldf(tok_rsrc(a.rate_law ? a.A : nullptr, t0, 4, ns, H, 1), kind == 2 ? off : kOOB);
+    r.sc = vdt + vlm + vra;
     return r;
 }
 __device__ __forceinline__ void store_raw(const RawRegs& r, int np, int tid, Raw* raw) {
@@ -186,7 +209,37 @@ __device__ __forceinline__ void store_raw(const RawRegs& r, int np, int tid, Raw
     }
 }
 
-constexpr int kMainLds = oRAW + (int)sizeof(Raw);
+constexpr int oPRE = oRAW + (int)((sizeof(Raw) + 15) / 16 * 16);   // next chunk's rows: 6 pieces x 512 threads x 16 B
+constexpr int kPreBytes = 6 * kBT * 16;
+constexpr int oBIAS = oPRE + kPreBytes;                               // B and C biases of the head [2][4][128] fp32
+constexpr int kMainLds = oBIAS + 2 * kBR * kN * 4;
+static_assert(kMainLds <= 160 * 1024, "the main kernel's LDS exceeds a compute unit's");
+
+// The rows of chunk [c0, c0 + 16) that thread tid stages (row m = tid / 8: token m / 4, rank
+// m % 4; piece tid % 8), loaded straight into LDS (buffer loads to LDS; lane i of a wave
+// writes 16 bytes at the wave's base + 16 i): x, dy (16 bytes each), B, C (32 bytes each).
+// Rows past L read zero.  Completion is awaited with the memory counter before the reads.
+__device__ __forceinline__ void prefetch_rows(const BwdArgs& a, int bi, int h, int gg, int c0, int tid, char* pre) {
+    const int L = a.L, H = a.H, G = a.G;
+    const int nv = min(kBQ, L - c0);
+    const size_t t0 = (size_t)bi * L + c0;
+    const int m = tid >> 3, q8 = tid & 7, t = m >> 2, r = m & 3, w = tid >> 6;
+    const uint32_t xb = (uint32_t)(((nv - 1) * H + 1) * kBR * kP * 2), bb = (uint32_t)(((nv - 1) * G + 1) * kBR * kN * 2);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const uint16_t*>(a.x) + (t0 * H + h) * kBR * kP, xb);
+    const __amdgpu_buffer_rsrc_t rdy = make_rsrc(static_cast<const uint16_t*>(a.dy) + (t0 * H + h) * kBR * kP, xb);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(static_cast<const uint16_t*>(a.B) + (t0 * G + gg) * kBR * kN, bb);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(static_cast<const uint16_t*>(a.C) + (t0 * G + gg) * kBR * kN, bb);
+    const int xo = (t * H * kBR * kP + r * kP + 8 * q8) * 2;
+    const int bo_ = (t * G * kBR * kN + r * kN + 16 * q8) * 2;
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    char* const base = pre + w * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(base + 0 * kBT * 16), 16, xo, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rdy, (lds_ptr)(base + 1 * kBT * 16), 16, xo, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(base + 2 * kBT * 16), 16, bo_, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(base + 3 * kBT * 16), 16, bo_ + 16, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr)(base + 4 * kBT * 16), 16, bo_, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr)(base + 5 * kBT * 16), 16, bo_ + 16, 0, 0, 0);
+}
 constexpr int kStateLds = sRAW_ + (int)sizeof(Raw);
 
 // The per-token scalars of the chunk into the table (wave 0; lane t: token c0 + t, lane 16
@@ -237,6 +290,33 @@ __device__ float chunk_phases(const Raw* raw, int j, float phi, float2* cst) {
         cst[t * kMaxPairs + j] = float2{cs, sn};
     }
     return phi;
+}
+
+// 16 turned values of a row at columns n0 .. n0 + 15 from loaded data: raw (two 16-byte
+// pieces) + bias (16 floats), pairs (2 j, 2 j + 1) with j < np turned by the token's table
+// entries, times scale; bf16 pairs out.
+__device__ __forceinline__ void turn_loaded(const uint4& r0, const uint4& r1, const float* bias, const float2* cst, int np,
+                                            int n0, float scale, uint32_t out[8]) {
+    float v[16];
+    const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) { v[2 * k] = lo_f(w[k]); v[2 * k + 1] = hi_f(w[k]); }
+#pragma unroll
+    for (int k = 0; k < 16; k += 4) {
+        const float4 b4 = *reinterpret_cast<const float4*>(bias + n0 + k);
+        v[k] += b4.x; v[k + 1] += b4.y; v[k + 2] += b4.z; v[k + 3] += b4.w;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int j = (n0 >> 1) + k;
+        float e = v[2 * k], o = v[2 * k + 1];
+        if (j < np) {
+            const float2 c = cst[j];
+            const float e2 = e * c.x - o * c.y, o2 = e * c.y + o * c.x;
+            e = e2; o = o2;
+        }
+        out[k] = pack2(e * scale, o * scale);
+    }
 }
 
 // 16 turned values of row (token, rank) at columns n0 .. n0 + 15: raw + bias, pairs
@@ -325,7 +405,7 @@ __global__ __launch_bounds__(kBT) void bwdc_state_kernel(BwdArgs a, char* hfws, 
             phws[((size_t)bh * nch + c) * np + lane] = phi;
             phi = chunk_phases(raw, lane, phi, ph);
         }
-        __syncthreads();
+        lds_barrier();
         const bool more = c + 1 < nch;
         RawRegs nx{0.f, 0.f, 0.f};
         if (more) nx = load_raw(a, bi, h, c0 + kBQ, tid);
@@ -354,7 +434,7 @@ __global__ __launch_bounds__(kBT) void bwdc_state_kernel(BwdArgs a, char* hfws, 
             for (int pt = 0; pt < 4; ++pt)
                 *reinterpret_cast<uint2*>(dst + (n * kP + 16 * pt + 4 * g4) * 2) = pack4(hf[pt]);
         }
-        __syncthreads();
+        lds_barrier();
         if (more) store_raw(nx, np, tid, raw);
         // Hf = exp(l_e) Hf + X^T (v Bt): rows p (A = X^T by transposing reads), columns n
         const float fe = __expf(tb->le);
@@ -366,7 +446,7 @@ __global__ __launch_bounds__(kBT) void bwdc_state_kernel(BwdArgs a, char* hfws, 
                 acc = mfma(tr_op(sX, kP * 2, 32 * km, 16 * pt, lane), tr_op(sV, kN * 2, 32 * km, 16 * w, lane), acc);
             hf[pt] = acc;
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // Phi_L[j] = d phi_L[j] + <d h_L, J_j H_L> + <d B_prev,L, J_j Bt_{L-1}> (hf is H_L: delta_L = 0)
@@ -451,7 +531,14 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
     float pend_dt = 0.f, pend_lam = 0.f;      // token c0 + 16 of the previous iteration (wave 0, lane 0)
 
     Raw* const raw = reinterpret_cast<Raw*>(smem + oRAW);
+    char* const pre = smem + oPRE;
+    float* const sBias = reinterpret_cast<float*>(smem + oBIAS);
     store_raw(load_raw(a, bi, h, (nch - 1) * kBQ, tid), np, tid, raw);
+    for (int i = tid; i < 2 * kBR * kN; i += kBT) {
+        const float* src = i < kBR * kN ? a.Bb : a.Cb;
+        sBias[i] = src ? src[(size_t)h * kBR * kN + (i % (kBR * kN))] : 0.f;
+    }
+    prefetch_rows(a, bi, h, gg, (nch - 1) * kBQ, tid, pre);
     __syncthreads();
 
     for (int c = nch - 1; c >= 0; --c) {
@@ -459,27 +546,25 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
         // ---- S0a: scalars, phases ----
         if (w == 0) chunk_scalars(a, raw, h, lane, tb);
         if (w == 1 && lane < np) chunk_phases(raw, lane, phws[((size_t)bh * nch + c) * np + lane], ph);
-        __syncthreads();
-        // ---- S0b: staging ----
+        lds_barrier();
+        // ---- S0b: staging (the rows were prefetched into LDS) ----
         {
-            const int m = tid >> 3, q8 = tid & 7, t = m >> 2, r = m & 3, tok = c0 + t;
-            const bool valid = tok < L;
-            const size_t xrow = ((bo + (valid ? tok : 0)) * H + h) * kBR * kP + r * kP + 8 * q8;
-            uint4 xv = {0u, 0u, 0u, 0u}, dv = {0u, 0u, 0u, 0u};
-            if (valid) {
-                xv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + xrow);
-                dv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.dy) + xrow);
-            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            const int m = tid >> 3, q8 = tid & 7, t = m >> 2, r = m & 3;
+            const uint4 xv = *reinterpret_cast<const uint4*>(pre + 0 * kBT * 16 + tid * 16);
+            const uint4 dv = *reinterpret_cast<const uint4*>(pre + 1 * kBT * 16 + tid * 16);
+            const uint4 b0 = *reinterpret_cast<const uint4*>(pre + 2 * kBT * 16 + tid * 16);
+            const uint4 b1 = *reinterpret_cast<const uint4*>(pre + 3 * kBT * 16 + tid * 16);
+            const uint4 cc0 = *reinterpret_cast<const uint4*>(pre + 4 * kBT * 16 + tid * 16);
+            const uint4 cc1 = *reinterpret_cast<const uint4*>(pre + 5 * kBT * 16 + tid * 16);
             *reinterpret_cast<uint4*>(sX + swz(kP * 2, m, 8 * q8)) = xv;
             *reinterpret_cast<uint4*>(sDY + swz(kP * 2, m, 8 * q8)) = dv;
-            const size_t brow = ((bo + (valid ? tok : 0)) * G + gg) * kBR * kN + r * kN;
+            const float keep = c0 + t < L ? 1.f : 0.f;       // rows past L: zero (the bias too)
             uint32_t o[8];
-            turn_piece(valid ? static_cast<const uint16_t*>(a.B) + brow : nullptr,
-                       a.Bb ? a.Bb + ((size_t)h * kBR + r) * kN : nullptr, ph + t * kMaxPairs, np, 16 * q8, 1.f, o);
+            turn_loaded(b0, b1, sBias + r * kN, ph + t * kMaxPairs, np, 16 * q8, keep, o);
             *reinterpret_cast<uint4*>(sB + swz(kN * 2, m, 16 * q8)) = uint4{o[0], o[1], o[2], o[3]};
             *reinterpret_cast<uint4*>(sB + swz(kN * 2, m, 16 * q8 + 8)) = uint4{o[4], o[5], o[6], o[7]};
-            turn_piece(valid ? static_cast<const uint16_t*>(a.C) + brow : nullptr,
-                       a.Cb ? a.Cb + ((size_t)h * kBR + r) * kN : nullptr, ph + t * kMaxPairs, np, 16 * q8, 1.f, o);
+            turn_loaded(cc0, cc1, sBias + kBR * kN + r * kN, ph + t * kMaxPairs, np, 16 * q8, keep, o);
             *reinterpret_cast<uint4*>(sC + swz(kN * 2, m, 16 * q8)) = uint4{o[0], o[1], o[2], o[3]};
             *reinterpret_cast<uint4*>(sC + swz(kN * 2, m, 16 * q8 + 8)) = uint4{o[4], o[5], o[6], o[7]};
         }
@@ -502,10 +587,13 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) hown[pt] = *reinterpret_cast<const uint2*>(hin + (n * kP + 16 * pt + 4 * g4) * 2);
         }
-        __syncthreads();
+        lds_barrier();
         // the next chunk's raw inputs, staged in LDS once this chunk's are used (S3b)
         RawRegs nx{0.f, 0.f, 0.f};
-        if (c > 0) nx = load_raw(a, bi, h, c0 - kBQ, tid);
+        if (c > 0) {
+            nx = load_raw(a, bi, h, c0 - kBQ, tid);
+            prefetch_rows(a, bi, h, gg, c0 - kBQ, tid, pre);
+        }
         // ---- S1: score tiles S^T, S2^T (rows u', columns m), weights, P(t, u) ----
         {
             const int mt = w & 3;
@@ -534,7 +622,7 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
                 if ((s & 3) == 0) sPM[t * kBQ + u] = pr;
             }
         }
-        __syncthreads();
+        lds_barrier();
         // ---- S2: the products ----
         const int nt = w, n = 16 * nt + s;
         const bool odd = (s & 1) != 0;
@@ -708,7 +796,7 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
             jt += __shfl_xor(jt, 32, 64);
             if (g4 == 0 && !odd && turns) tb->phb[pair] = jt;
         }
-        __syncthreads();
+        lds_barrier();
         // ---- S3a: coefficient sensitivities (wave 0), the angle's (wave 1) ----
         if (w == 0) {
             const int u = lane & 15;
@@ -788,7 +876,7 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
             }
             if (pl) Phi = PhiL - tb->phb[lane];                 // Phi at the chunk's first token
         }
-        __syncthreads();
+        lds_barrier();
         // ---- S3b: per-token outputs (wave 0, lane t) ----
         if (w == 0) {
             const int t = lane & 15, tok = c0 + t;
@@ -827,7 +915,7 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
             }
         }
         if (c > 0) store_raw(nx, np, tid, raw);
-        __syncthreads();
+        lds_barrier();
     }
 
     // ---- the initial carry: Hf_{-1} = H0 + delta_0 x_prev^T B_prev ----
