@@ -88,6 +88,57 @@ def test_scan_bwd_parity(m3, name, kw, io, final):
     _compare(g, want, d, 1e-4 if io == "f32" else 2e-2, cfg.npairs)
 
 
+# bf16 I/O at P 64, N 128, rank 4 runs the chunked matrix-core form (16-token chunks):
+# ragged and single-token lengths, chunk edges, no rotation and all 64 pairs turning,
+# heavy-tail rates, no carries, long memory over many chunks and steep decay.
+CHUNKED = [
+    ("one-token", dict(batch=1, seqlen=1, nheads=2, ngroups=1, npairs=32), True),
+    ("one-chunk-all-pairs", dict(batch=2, seqlen=16, nheads=2, ngroups=2, npairs=64), True),
+    ("chunk-plus-one", dict(batch=1, seqlen=17, nheads=3, ngroups=1, npairs=7), False),
+    ("no-rotation-no-carry", dict(batch=2, seqlen=45, nheads=2, ngroups=1, npairs=0, init_full=False, bias=False), False),
+    ("heavy-tail", dict(batch=1, seqlen=80, nheads=2, ngroups=1, npairs=32, rate_dyn=True), True),
+    ("long-memory", dict(batch=1, seqlen=300, nheads=2, ngroups=1, npairs=16, dt_scale=1e-2), True),
+    ("steep-decay", dict(batch=1, seqlen=64, nheads=2, ngroups=1, npairs=16, dt_scale=40.0), True),
+]
+
+
+@pytest.mark.parametrize("name,kw,final", CHUNKED, ids=[c[0] for c in CHUNKED])
+def test_scan_bwd_chunked_form(m3, name, kw, final):
+    _say("scan bwd chunked", name)
+    cfg, d = make_small_case(1300 + len(name), io_dtype="bf16", headdim=64, dstate=128, rank=4, rms_bc=True, **kw)
+    dy, dfin = make_cotangents(cfg, seed=41, final=final)
+    want = grad.scan_bwd(d, dy, dfin)
+    g = _run(m3, d, dy, dfin, "bf16")
+    _compare(g, want, d, 2e-2, cfg.npairs)
+    for gk, wk in (("x", "x"), ("B", "B"), ("dt", "dt")):
+        assert abs(pooled_signed(host(g[gk]), want[wk])) <= 5e-3, gk
+
+
+def test_scan_bwd_long_sequence(m3):
+    """One batch of 64 heads in one group over 16,384 tokens (1,024 chunks per stream
+    on the chunked form): the per-stream gradients (dx, dt, lambda, theta, the initial
+    carry) of sampled streams against the oracle run on those streams alone.  The
+    angle gradient is the one that would show rounding carried along the sequence."""
+    cfg = config_by_name("mimo_bf16_prefill")
+    d = make_scan_inputs(cfg, batch=1, seqlen=16384)
+    dy, dfin = make_cotangents(cfg, seed=91, batch=1, seqlen=16384)
+    _say("scan bwd long: inputs ready")
+    g = _run(m3, d, dy, dfin, "bf16")
+    for h in (0, 37):
+        s = _one_stream(d, 0, h)
+        sf = {k: v[0:1, h:h + 1] for k, v in dfin.items()}
+        want = grad.scan_bwd(s, dy[0:1, :, h:h + 1], sf)
+        errs = {"x": rel_l2(host(g["x"][0, :, h]), want["x"][0, :, 0]),
+                "dt": rel_l2(host(g["dt"][0, :, h]), want["dt"][0, :, 0]),
+                "lam": rel_l2(host(g["lam"][0, :, h]), want["lam"][0, :, 0]),
+                "theta": rel_l2(host(g["theta"][0, :, h]), want["theta"][0, :, 0])}
+        for k in ("h", "phi", "B_prev", "x_prev"):
+            errs["init." + k] = rel_l2(host(g["init"][k][0, h]), want["init"][k][0, 0])
+        _say("  stream (0, %d): " % h + " ".join("%s %.1e" % kv for kv in errs.items()))
+        for k, e in errs.items():
+            assert e <= 2e-2, (h, k, e)
+
+
 def test_scan_bwd_empty_sequence(m3):
     """L = 0: the initial carry's gradients are the final carry's sensitivities."""
     cfg, d = make_small_case(5, batch=2, seqlen=0, nheads=2, headdim=4, dstate=8, rank=2, npairs=2)
