@@ -36,7 +36,7 @@ CSRC = os.path.join(ROOT, "selective_state_space_mimo_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 # sources that define each measured kernel (the counters stand only while these are unchanged)
 KERNEL_SOURCES = {"scan": ("scan_mfma.hip", "scan_common.h", "m3_internal.h"), "decode": ("decode.hip", "m3_internal.h"),
-                  "bwd": ("bwd.hip", "m3_internal.h"), "pcs": ("pcs.hip", "m3_internal.h"),
+                  "bwd": ("bwd.hip", "bwd_chunk.hip", "scan_common.h", "m3_internal.h"), "pcs": ("pcs.hip", "m3_internal.h"),
                   "layer": ("scan_mfma.hip", "scan_common.h", "m3_internal.h", "block.hip"),
                   "siso": ("scan_siso.hip", "scan_common.h", "m3_internal.h")}
 
@@ -124,13 +124,31 @@ def scan_bytes(cfg, with_final=True):
     return total
 
 
+BWD_CHUNK = 16     # tokens per chunk of the chunked (matrix-core) backward
+
+
+def bwd_chunked(cfg):
+    """Whether the library runs the backward in its chunked matrix-core form (bf16
+    I/O, P 64, N 128, rank 4, at most 64 turning pairs)."""
+    return (cfg.io_dtype == "bf16" and cfg.headdim == 64 and cfg.dstate == 128 and cfg.rank == 4
+            and cfg.npairs <= 64)
+
+
 def bwd_flops_per_head_token(cfg):
-    """Products with the P x N state per (head, token) of the backward recurrence:
-    the readout's transpose dC = H^T dy (2 R P N), the sensitivity update G = alpha G
-    + sum_r dy_r (x) C_r (2 R P N + P N), and v = G B, w = G^T X (2 R P N each).
-    Reconstructing the forward states (4 R P N + P N more) is recomputation, not
-    credited."""
+    """Matrix work per (head, token) of the backward.
+
+    Chunked form (Q-token chunks, M = R Q rows): per chunk the score tiles
+    S^T = Bt Ct^T and X dy^T (2 M^2 (N + P)), the weighted products dCt, dBt (2 M^2 N
+    each) and dX (2 M^2 P), the state terms dy Hf_in, X Gf, Bt Gf^T and the carried
+    sensitivity update (2 M P N each), and the forward pass's state update (2 M P N):
+    2 R^2 Q (3 N + 2 P) + 10 R P N per head-token.
+
+    Token-serial form: the readout's transpose dC = H^T dy (2 R P N), the sensitivity
+    update G = alpha G + sum_r dy_r (x) C_r (2 R P N + P N), and v = G B, w = G^T X
+    (2 R P N each); reconstructing the forward states is recomputation, not credited."""
     R, N, P = cfg.rank, cfg.dstate, cfg.headdim
+    if bwd_chunked(cfg):
+        return 2 * R * R * BWD_CHUNK * (3 * N + 2 * P) + 10 * R * P * N
     return 8 * R * P * N + P * N
 
 
@@ -435,12 +453,15 @@ def run_bwd(torch, m3, cfg, steps, warmup):
            "tokens_per_s": b * L / (ms * 1e-3), "algo_tflops": flops / (ms_launch * 1e-3) / 1e12,
            "algo_gbs": nbytes / (ms_launch * 1e-3) / 1e9, "flop_per_call": flops, "bytes_per_call": nbytes,
            "workspace_bytes": ws_bytes}
+    out["chunked"] = bwd_chunked(cfg)
     out["valu_frac"] = out["algo_tflops"] / PEAK_FP32_VALU_TFLOPS
+    out["mfma_frac"] = out["algo_tflops"] / PEAK_BF16_TFLOPS
     out["hbm_frac"] = out["algo_gbs"] / PEAK_HBM_GBS
-    log("[bench] %s: %.3f ms/call, %.2f M tok/s, %.1f TFLOP/s fp32 (%.1f%% of the VALU peak), %.0f GB/s "
-        "(%.1f%% HBM), workspace %.2f GB" % (out["workload"], ms, out["tokens_per_s"] / 1e6, out["algo_tflops"],
-                                             100 * out["valu_frac"], out["algo_gbs"], 100 * out["hbm_frac"],
-                                             ws_bytes / 1e9))
+    peak = "%.1f%% of the bf16 MFMA peak" % (100 * out["mfma_frac"]) if out["chunked"] else \
+        "%.1f%% of the fp32 VALU peak" % (100 * out["valu_frac"])
+    log("[bench] %s: %.3f ms/call, %.2f M tok/s, %.1f TFLOP/s (%s), %.0f GB/s (%.1f%% HBM), workspace %.2f GB"
+        % (out["workload"], ms, out["tokens_per_s"] / 1e6, out["algo_tflops"], peak, out["algo_gbs"],
+           100 * out["hbm_frac"], ws_bytes / 1e9))
     del x, B, C, dt, lam, th, Ar, init, dyt, dft, grads, ws
     torch.cuda.empty_cache()
     return out
@@ -663,8 +684,10 @@ def main():
         bw = res["bwd3"]
         line["backward"] = {k2: bw[k2] for k2 in ("workload", "tokens_per_s", "ms_per_call", "ms_per_launch",
                                                   "algo_tflops", "algo_gbs", "hbm_frac")}
-        line["roofline_backward"] = {"bound": "alu", "achieved": bw["algo_tflops"], "peak": PEAK_FP32_VALU_TFLOPS,
-                                     "unit": "TFLOP/s", "frac": bw["valu_frac"],
+        chunked = bw["chunked"]
+        line["roofline_backward"] = {"bound": "mfma" if chunked else "alu", "achieved": bw["algo_tflops"],
+                                     "peak": PEAK_BF16_TFLOPS if chunked else PEAK_FP32_VALU_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": bw["mfma_frac"] if chunked else bw["valu_frac"],
                                      "traffic": measured_traffic("bwd", bw["workload"]),
                                      "algorithmic_flops": bw["flop_per_call"],
                                      "algorithmic_bytes": bw["bytes_per_call"]}
