@@ -284,16 +284,23 @@ typedef struct {
     m3_carry_grad dinit;   /* gradients of the initial carry (members may be NULL) */
 } m3_scan_grads;
 
-/* Bytes of device workspace m3_scan_bwd needs for *d (float32 sums of the shared B and
- * C gradients, per-token angles and replay terms). */
+/* Bytes of device workspace m3_scan_bwd needs for *d: float32 sums of the shared B and
+ * C gradients, and, for the chunked form, every 16-token chunk's incoming state (bf16,
+ * 16 KiB per (batch, head) and chunk) and phases; for the token-serial form, per-token
+ * angles and replay terms. */
 m3_status m3_scan_bwd_workspace_size(const m3_desc* d, size_t* bytes);
 
 /* Gradients of the scan.  The forward inputs are those of m3_scan_fwd (init may be
  * NULL: an all-zero carry); dy [b, L, H, R, P] io_dtype; dfinal NULL or the final
- * carry's sensitivities.  d->chunk and d->nsegments are ignored: the backward replays
- * the recurrence token by token (fp32 state in registers), so its result does not
- * depend on the forward's chunking beyond rounding.  Supported: P <= 64, N <= 128,
- * R <= 4 (M3_ERR_UNSUPPORTED otherwise).  With L == 0 the initial carry's gradients
+ * carry's sensitivities.  d->chunk and d->nsegments are ignored.  bf16 I/O at P 64,
+ * N 128, rank 4 with at most 64 turning pairs runs the chunked form on the matrix
+ * cores (16-token chunks: a forward pass stores each chunk's incoming state in the
+ * workspace, a reverse pass computes each chunk's gradients from it and the carried
+ * state sensitivity; "Diagonal Equivalence in State Space Models ...", sections 2.4,
+ * 2.5 and appendix D.3); every other supported shape replays the recurrence token by
+ * token (fp32 state in registers).  Either way the result depends on the forward's
+ * chunking only through rounding.  Supported: P <= 64, N <= 128, R <= 4
+ * (M3_ERR_UNSUPPORTED otherwise).  With L == 0 the initial carry's gradients
  * are the final carry's sensitivities and the parameter gradients are zero.
  * Asynchronous on stream; the workspace's contents on entry do not matter. */
 m3_status m3_scan_bwd(const m3_desc* d,
