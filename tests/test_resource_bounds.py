@@ -7,7 +7,8 @@ span whole tokens of all heads); what must hold is that every offset *inside* th
 record count addresses bytes of the tensor.  The replay below restates the kernels'
 base, record-count and offset arithmetic (the matrix-core chunked scan in
 csrc/scan_mfma.hip, the single-rank scan and its score pass in csrc/scan_siso.hip,
-both per-coordinate kernels in csrc/pcs.hip) and checks it for
+both per-coordinate kernels in csrc/pcs.hip, the raw loads and row prefetch of the
+backward's chunked form in csrc/bwd_chunk.hip) and checks it for
 the edge workgroups (first and last batch, head, channel tile and segment, every
 chunk of the segment) of every shape the GPU tests and the benchmark run.  The
 segment schedule is the library's, restated here and cross-checked against the
@@ -441,3 +442,68 @@ def test_the_replay_catches_a_head_offset_record_count():
     offs = (np.arange(64)[:, None] * H * np_ + np.arange(64)[None, :]) * 4     # pairs 0 .. 63
     with pytest.raises(AssertionError):
         _check("theta (planted)", base, rec, offs, 4, b * L * H * np_ * 4)
+
+
+# ---------------------------------------------------------------------------
+# backward, chunked form (csrc/bwd_chunk.hip: bf16, P 64, N 128, R 4, 16-token chunks)
+# ---------------------------------------------------------------------------
+BQ, BR = 16, 4
+
+
+def replay_bwd_chunked(b, L, H, G, np_):
+    """The raw per-token loads (theta, dt, lambda, the rate input) and the row prefetch
+    (x, dy, B, C) of every edge stream and chunk, as load_raw and prefetch_rows form
+    them: per-chunk resources whose record counts end at the chunk's last valid token."""
+    nch = -(-L // BQ)
+    tids = np.arange(512)
+    m, q8 = tids >> 3, tids & 7
+    t, r = m >> 2, m & 3
+    X_bytes = b * L * H * BR * KP * 2
+    BC_bytes = b * L * G * BR * KN * 2
+    T_bytes = b * L * H * 4
+    TH_bytes = b * L * H * np_ * 4
+    for bi in sorted({0, b - 1}):
+        for h in sorted({0, H - 1}):
+            gg = h * G // H
+            for c in sorted({0, nch - 1}):
+                c0 = c * BQ
+                nv, ns = min(BQ, L - c0), min(BQ + 1, L - c0)
+                t0 = (bi * L + c0) * H + h
+                if np_ > 0:
+                    e = np.concatenate([tids, tids + 512])
+                    e = e[e < BQ * np_]
+                    te, je = e // np_, e % np_
+                    _check("bwd theta", t0 * np_ * 4, ((nv - 1) * H * np_ + np_) * 4, (te * H * np_ + je) * 4, 4,
+                           TH_bytes)
+                ts = np.arange(BQ + 1)
+                _check("bwd dt, lambda, rate", t0 * 4, ((ns - 1) * H + 1) * 4, ts * H * 4, 4, T_bytes)
+                xbase = ((bi * L + c0) * H + h) * BR * KP * 2
+                _check("bwd x, dy rows", xbase, ((nv - 1) * H + 1) * BR * KP * 2,
+                       (t * H * BR * KP + r * KP + 8 * q8) * 2, 16, X_bytes)
+                bbase = ((bi * L + c0) * G + gg) * BR * KN * 2
+                bo = (t * G * BR * KN + r * KN + 16 * q8) * 2
+                _check("bwd B, C rows", bbase, ((nv - 1) * G + 1) * BR * KN * 2, np.concatenate([bo, bo + 16]), 16,
+                       BC_bytes)
+
+
+def _bwd_ws(m3, b, L, H, G, np_):
+    d = m3.Desc(b, L, H, G, KP, KN, BR, np_, 64, m3.M3_BF16, m3.M3_F32, 0, m3.M3_RATE_STATIC)
+    n = ctypes.c_size_t(0)
+    assert m3.lib.m3_scan_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    return n.value
+
+
+# (batch, L, heads, groups, pairs): the chunked form's GPU parity cases, the full-size,
+# all-heads and long-sequence tests
+BWD_SHAPES = [(1, 1, 2, 1, 32), (2, 16, 2, 2, 64), (1, 17, 3, 1, 7), (2, 45, 2, 1, 0), (1, 80, 2, 1, 32),
+              (1, 300, 2, 1, 16), (2, 70, 4, 1, 32), (8, 2048, 64, 1, 32), (1, 256, 64, 1, 32), (1, 16384, 64, 1, 32)]
+
+
+@pytest.mark.parametrize("shape", BWD_SHAPES, ids=lambda s: "b%d_L%d_H%d_G%d_np%d" % s)
+def test_bwd_chunked_resources_stay_in_their_tensors(m3, shape):
+    b, L, H, G, np_ = shape
+    replay_bwd_chunked(b, L, H, G, np_)
+    # the workspace holds the B, C sums and every chunk's state and phases
+    nch = -(-L // BQ)
+    need = 2 * b * L * G * BR * KN * 4 + b * H * nch * (KN * KP * 2 + np_ * 4) + b * H * np_ * 4
+    assert _bwd_ws(m3, b, L, H, G, np_) >= need
