@@ -153,7 +153,7 @@ struct Raw {
     float dt[kBQ + 1], lam[kBQ + 1], ra[kBQ + 1];
 };
 struct RawRegs {
-    float th0, th1, sc;
+    float th0, th1, sdt, slm, sra;     // (kept apart: summing them here would wait for the loads)
 };
 // Global memory goes through buffer resources whose record counts end at the last valid
 // token, with every load, store and atomic issued unconditionally: a token past L reads
@@ -181,7 +181,7 @@ __device__ __forceinline__ RawRegs load_raw(const BwdArgs& a, int bi, int h, int
     const int L = a.L, H = a.H, np = a.np;
     const int nv = min(kBQ, L - c0), ns = min(kBQ + 1, L - c0);
     const size_t t0 = ((size_t)bi * L + c0) * H + h;
-    RawRegs r{0.f, 0.f, 0.f};
+    RawRegs r{0.f, 0.f, 0.f, 0.f, 0.f};
     if (np > 0) {
         const __amdgpu_buffer_rsrc_t rth = tok_rsrc(a.theta, t0 * np, 4, nv, H * np, np);
         const int e0 = tid, e1 = tid + kBT;
@@ -194,7 +194,9 @@ __device__ __forceinline__ RawRegs load_raw(const BwdArgs& a, int bi, int h, int
     const float vdt = ldf(tok_rsrc(a.dt, t0, 4, ns, H, 1), kind == 0 ? off : kOOB);
     const float vlm = ldf(tok_rsrc(a.lam, t0, 4, ns, H, 1), kind == 1 ? off : kOOB);
     const float vra = ldf(tok_rsrc(a.rate_law ? a.A : nullptr, t0, 4, ns, H, 1), kind == 2 ? off : kOOB);
-    r.sc = vdt + vlm + vra;
+    r.sdt = vdt;
+    r.slm = vlm;
+    r.sra = vra;
     return r;
 }
 __device__ __forceinline__ void store_raw(const RawRegs& r, int np, int tid, Raw* raw) {
@@ -205,7 +207,7 @@ __device__ __forceinline__ void store_raw(const RawRegs& r, int np, int tid, Raw
     }
     if (tid < 3 * (kBQ + 1)) {
         const int kind = tid / (kBQ + 1), t = tid - kind * (kBQ + 1);
-        (kind == 0 ? raw->dt : kind == 1 ? raw->lam : raw->ra)[t] = r.sc;
+        (kind == 0 ? raw->dt : kind == 1 ? raw->lam : raw->ra)[t] = r.sdt + r.slm + r.sra;
     }
 }
 
@@ -407,7 +409,7 @@ __global__ __launch_bounds__(kBT) void bwdc_state_kernel(BwdArgs a, char* hfws, 
         }
         lds_barrier();
         const bool more = c + 1 < nch;
-        RawRegs nx{0.f, 0.f, 0.f};
+        RawRegs nx{0.f, 0.f, 0.f, 0.f, 0.f};
         if (more) nx = load_raw(a, bi, h, c0 + kBQ, tid);
         {
             // X rows and v-scaled turned B rows (row m = tid / 8, piece tid % 8)
@@ -589,7 +591,7 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
         }
         lds_barrier();
         // the next chunk's raw inputs, staged in LDS once this chunk's are used (S3b)
-        RawRegs nx{0.f, 0.f, 0.f};
+        RawRegs nx{0.f, 0.f, 0.f, 0.f, 0.f};
         if (c > 0) {
             nx = load_raw(a, bi, h, c0 - kBQ, tid);
             prefetch_rows(a, bi, h, gg, c0 - kBQ, tid, pre);
