@@ -47,7 +47,8 @@
 //     state Hf_in (bf16, n-major) and its starting phases (fp32, wrapped into [0, 2 pi));
 //   * bwdc_main_kernel walks them backward with Gf (fp32) in matrix-core accumulators:
 //     per chunk, the score tiles S^T and S2^T, the weighted tiles (bf16 in LDS), the
-//     products above, then the per-token scalar gradients.
+//     products above, then the per-token scalar gradients (waves 0 and 1; meanwhile
+//     waves 2..7 load the next chunk's x, dy, B, C rows and start phases into LDS).
 // Shared B and C gradients are summed over a group's heads by fp32 atomic adds into the
 // workspace (as the token-serial backward does), converted to bf16 afterwards.
 #include "scan_common.h"
@@ -85,7 +86,7 @@ struct Tab {
     float GH[8];                                    // per wave: <Gf_out, Hf_in>
     float TP[kBQ];                                  // sum over pairs of theta_t Phi_t
     float dgam[kBQ], ddl[kBQ], dla[kBQ];
-    float K[kBQ][kBQ];                              // [t][u]: sum_{t' >= t} of the corner terms of column u
+    alignas(16) float K[kBQ][kBQ];                              // [t][u]: sum_{t' >= t} of the corner terms of column u
     float ddl_next;                                 // d delta of token c0 + 16 from this chunk
     float phb[kMaxPairs];                           // <Gf_in, J_j Hf_in> of each pair
     float pend_dt, pend_lam;                        // token c0's gradients without its delta term
@@ -151,6 +152,7 @@ __device__ __forceinline__ uint2 pack4(const f32x4& v) { return uint2{pack2(v[0]
 struct Raw {
     float th[kBQ][kMaxPairs];
     float dt[kBQ + 1], lam[kBQ + 1], ra[kBQ + 1];
+    float phs[kMaxPairs];              // the chunk's start phases (main kernel)
 };
 struct RawRegs {
     float th0, th1, sdt, slm, sra;     // (kept apart: summing them here would wait for the loads)
@@ -221,32 +223,57 @@ static_assert(kMainLds <= 160 * 1024, "the main kernel's LDS exceeds a compute u
 // m % 4; piece tid % 8), loaded straight into LDS (buffer loads to LDS; lane i of a wave
 // writes 16 bytes at the wave's base + 16 i): x, dy (16 bytes each), B, C (32 bytes each).
 // Rows past L read zero.  Completion is awaited with the memory counter before the reads.
-__device__ __forceinline__ void prefetch_rows(const BwdArgs& a, int bi, int h, int gg, int c0, int tid, char* pre) {
+// Buffer-to-LDS loads written out, so that the compiler does not hold every later LDS access
+// of the issuing wave until they land; their waits are explicit (vmcnt(0) of the issuing waves,
+// then a barrier, before the data is read).  lds: a uniform LDS byte address (m0); each lane
+// writes its piece at lds + 16 lane (4 lane for the 4-byte form).
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(voff), "s"(r), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voff) {
+    asm volatile("buffer_load_dword %0, %1, 0 offen lds" :: "v"(voff), "s"(r), "{m0}"(lds) : "memory");
+}
+
+// The next chunk's x, dy, B and C rows as 3072 16-byte pieces, piece q landing at pre + 16 q:
+// [0, 512) x, [512, 1024) dy, [1024, 2048) B and [2048, 3072) C (piece k of thread j of a kind
+// is row j / 8, 16-byte group j % 8, first or second half of a 256-byte row).  Issued by waves
+// 2..7 (eight pieces per lane; a wave's 64 pieces of one instruction lie in one kind), while
+// waves 0 and 1 work alone on the chunk's per-token sensitivities.  Wave 2 first brings the
+// chunk's np start phases (phs, from the state pass) into raw->phs: it is its oldest load, so
+// vmcnt(8) in that wave means it has landed.
+__device__ __forceinline__ void prefetch_rows(const BwdArgs& a, int bi, int h, int gg, int c0, int tid, char* pre,
+                                              const float* phs, Raw* raw) {
     const int L = a.L, H = a.H, G = a.G;
     const int nv = min(kBQ, L - c0);
     const size_t t0 = (size_t)bi * L + c0;
-    const int m = tid >> 3, q8 = tid & 7, t = m >> 2, r = m & 3, w = tid >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6) - 2, lane = tid & 63;
     const uint32_t xb = (uint32_t)(((nv - 1) * H + 1) * kBR * kP * 2), bb = (uint32_t)(((nv - 1) * G + 1) * kBR * kN * 2);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const uint16_t*>(a.x) + (t0 * H + h) * kBR * kP, xb);
     const __amdgpu_buffer_rsrc_t rdy = make_rsrc(static_cast<const uint16_t*>(a.dy) + (t0 * H + h) * kBR * kP, xb);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(static_cast<const uint16_t*>(a.B) + (t0 * G + gg) * kBR * kN, bb);
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(static_cast<const uint16_t*>(a.C) + (t0 * G + gg) * kBR * kN, bb);
-    const int xo = (t * H * kBR * kP + r * kP + 8 * q8) * 2;
-    const int bo_ = (t * G * kBR * kN + r * kN + 16 * q8) * 2;
-    typedef __attribute__((address_space(3))) void* lds_ptr;
-    char* const base = pre + w * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(base + 0 * kBT * 16), 16, xo, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rdy, (lds_ptr)(base + 1 * kBT * 16), 16, xo, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(base + 2 * kBT * 16), 16, bo_, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(base + 3 * kBT * 16), 16, bo_ + 16, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr)(base + 4 * kBT * 16), 16, bo_, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr)(base + 5 * kBT * 16), 16, bo_ + 16, 0, 0, 0);
+    const uint32_t pre_lds = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)pre);
+    if (wv == 0)
+        lds_dma4(make_rsrc(phs, (uint32_t)a.np * 4u),
+                 __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const float*)raw->phs)),
+                 lane * 4);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int q0 = k * 384 + wv * 64;                 // the wave's first piece (uniform)
+        const int kind = q0 >> 9;
+        const int j = (q0 & 511) + lane;
+        const int m = j >> 3, q8 = j & 7, t = m >> 2, r = m & 3;
+        const int xo = (t * H * kBR * kP + r * kP + 8 * q8) * 2;
+        const int bo_ = (t * G * kBR * kN + r * kN + 16 * q8) * 2 + ((kind & 1) ? 16 : 0);
+        const __amdgpu_buffer_rsrc_t rs = kind == 0 ? rx : kind == 1 ? rdy : kind < 4 ? rb : rc;
+        lds_dma16(rs, __builtin_amdgcn_readfirstlane(pre_lds + q0 * 16), kind < 2 ? xo : bo_);
+    }
 }
 constexpr int kStateLds = sRAW_ + (int)sizeof(Raw);
 
 // The per-token scalars of the chunk into the table (wave 0; lane t: token c0 + t, lane 16
 // the token after the chunk).  Tokens at or past L have dt = 0: no decay, no write.
-__device__ void chunk_scalars(const BwdArgs& a, const Raw* raw, int h, int lane, Tab* tb) {
+__device__ void chunk_scalars(const BwdArgs& a, const Raw* raw, float rateA, int lane, Tab* tb) {
     const bool in = lane <= kBQ;
     const int li = in ? lane : 0;
     const float dt = in ? raw->dt[li] : 0.f;
@@ -256,7 +283,7 @@ __device__ void chunk_scalars(const BwdArgs& a, const Raw* raw, int h, int lane,
         u = in ? raw->ra[li] : 0.f;
         rate = -heavy_tail_rate(u);
     } else {
-        rate = expf(a.A[h]);
+        rate = rateA;
     }
     const float la = -dt * rate;
     const float gam = lam * dt, dl = dt * (1.f - lam);
@@ -284,9 +311,12 @@ __device__ void chunk_scalars(const BwdArgs& a, const Raw* raw, int h, int lane,
 // (hardware forms of the phase wrapped into [0, 2 pi)) into the table.  Returns the phase
 // after the chunk.
 __device__ float chunk_phases(const Raw* raw, int j, float phi, float2* cst) {
+    float dtv[kBQ], thv[kBQ];                 // the chunk's reads first
+#pragma unroll
+    for (int t = 0; t < kBQ; ++t) { dtv[t] = raw->dt[t]; thv[t] = raw->th[t][j]; }
 #pragma unroll
     for (int t = 0; t < kBQ; ++t) {
-        phi = fmaf(raw->dt[t], raw->th[t][j], phi);
+        phi = fmaf(dtv[t], thv[t], phi);
         float sn, cs;
         __sincosf(wrap_2pi(phi), &sn, &cs);
         cst[t * kMaxPairs + j] = float2{cs, sn};
@@ -366,6 +396,7 @@ __global__ __launch_bounds__(kBT) void bwdc_state_kernel(BwdArgs a, char* hfws, 
     const int L = a.L, H = a.H, G = a.G, np = a.np;
     const int bh = blockIdx.x, h = bh % H, bi = bh / H, gg = h * G / H;
     const int nch = (L + kBQ - 1) / kBQ;
+    const float rateA = a.rate_law ? 0.f : expf(a.A[h]);   // the static rate law's rate
     char* const sX = smem + sX_;
     char* const sV = smem + sV_;
     float2* const ph = reinterpret_cast<float2*>(smem + sPH_);
@@ -401,7 +432,7 @@ __global__ __launch_bounds__(kBT) void bwdc_state_kernel(BwdArgs a, char* hfws, 
 
     for (int c = 0; c < nch; ++c) {
         const int c0 = c * kBQ;
-        if (w == 0) chunk_scalars(a, raw, h, lane, tb);
+        if (w == 0) chunk_scalars(a, raw, rateA, lane, tb);
         if (w == 1 && lane < np) {
             phi = wrap_2pi(phi);
             phws[((size_t)bh * nch + c) * np + lane] = phi;
@@ -504,6 +535,7 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
     const int L = a.L, H = a.H, G = a.G, np = a.np;
     const int bh = blockIdx.x, h = bh % H, bi = bh / H, gg = h * G / H;
     const int nch = (L + kBQ - 1) / kBQ;
+    const float rateA = a.rate_law ? 0.f : expf(a.A[h]);   // the static rate law's rate
     const size_t bo = (size_t)bi * L;
     char* const sX = smem + oX;
     char* const sDY = smem + oDY;
@@ -540,18 +572,21 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
         const float* src = i < kBR * kN ? a.Bb : a.Cb;
         sBias[i] = src ? src[(size_t)h * kBR * kN + (i % (kBR * kN))] : 0.f;
     }
-    prefetch_rows(a, bi, h, gg, (nch - 1) * kBQ, tid, pre);
+    if (w >= 2) {
+        prefetch_rows(a, bi, h, gg, (nch - 1) * kBQ, tid, pre, phws + ((size_t)bh * nch + nch - 1) * np, raw);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();
 
     for (int c = nch - 1; c >= 0; --c) {
         const int c0 = c * kBQ;
         // ---- S0a: scalars, phases ----
-        if (w == 0) chunk_scalars(a, raw, h, lane, tb);
-        if (w == 1 && lane < np) chunk_phases(raw, lane, phws[((size_t)bh * nch + c) * np + lane], ph);
+        if (w == 0) chunk_scalars(a, raw, rateA, lane, tb);
+        if (w == 1 && lane < np) chunk_phases(raw, lane, raw->phs[lane], ph);
+        if (w >= 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the rows' loads into LDS
         lds_barrier();
         // ---- S0b: staging (the rows were prefetched into LDS) ----
         {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             const int m = tid >> 3, q8 = tid & 7, t = m >> 2, r = m & 3;
             const uint4 xv = *reinterpret_cast<const uint4*>(pre + 0 * kBT * 16 + tid * 16);
             const uint4 dv = *reinterpret_cast<const uint4*>(pre + 1 * kBT * 16 + tid * 16);
@@ -594,7 +629,6 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
         RawRegs nx{0.f, 0.f, 0.f, 0.f, 0.f};
         if (c > 0) {
             nx = load_raw(a, bi, h, c0 - kBQ, tid);
-            prefetch_rows(a, bi, h, gg, c0 - kBQ, tid, pre);
         }
         // ---- S1: score tiles S^T, S2^T (rows u', columns m), weights, P(t, u) ----
         {
@@ -800,9 +834,20 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
         }
         lds_barrier();
         // ---- S3a: coefficient sensitivities (wave 0), the angle's (wave 1) ----
+        // (this chunk's rows were staged in S0b, so the prefetch buffer is free)
+        if (w >= 2 && c > 0) prefetch_rows(a, bi, h, gg, c0 - kBQ, tid, pre, phws + ((size_t)bh * nch + c - 1) * np, raw);
         if (w == 0) {
+            // every LDS read of the phase is issued before the arithmetic that needs it
             const int u = lane & 15;
             const bool ul = lane < kBQ;
+            float lt[kBQ], pm[kBQ];
+#pragma unroll
+            for (int t = 0; t < kBQ; t += 4) {
+                const float4 q = *reinterpret_cast<const float4*>(tb->l + t);
+                lt[t] = q.x; lt[t + 1] = q.y; lt[t + 2] = q.z; lt[t + 3] = q.w;
+            }
+#pragma unroll
+            for (int t = 0; t < kBQ; ++t) pm[t] = sPM[t * kBQ + u];
             const float lu = tb->l[u], le = tb->le;
             const float Qu = tb->Qp[0][u] + tb->Qp[1][u] + tb->Qp[2][u] + tb->Qp[3][u];
             float RH = 0.f;
@@ -812,35 +857,43 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
 #pragma unroll
             for (int k = 0; k < 8; ++k) GH += tb->GH[k];
             const float wv = tb->gam[u] + tb->dl[u + 1];
+            const float diagP = sPM[u * kBQ + u];
+            const float Eu = tb->E[u], vu = tb->v[u];
             // column u: tail = sum_{t > u} exp(l_t - l_u) P(t, u); the corner terms
-            // exp(l_t' - l_u) wv_u P(t', u) summed over t' >= t, for every t > u
-            float tail = 0.f, cs = 0.f;
-#pragma unroll 5
+            // exp(l_t' - l_u) wv_u P(t', u) summed over t' >= t, for every t > u (entries with
+            // t <= u are written too and never read)
+            float tail = 0.f, cs = 0.f, kc[kBQ];
+#pragma unroll
             for (int t = kBQ - 1; t >= 1; --t) {
-                const bool act = t > u;
-                const float ep = act ? __expf(fminf(tb->l[t] - lu, 0.f)) * sPM[t * kBQ + u] : 0.f;
+                const float ep = t > u ? __expf(fminf(lt[t] - lu, 0.f)) * pm[t] : 0.f;
                 tail += ep;
                 cs = fmaf(wv, ep, cs);
-                if (act && ul) tb->K[t][u] = cs;
+                kc[t] = cs;
             }
-            const float diagP = sPM[u * kBQ + u];
+            if (ul) {
+#pragma unroll
+                for (int t = 1; t < kBQ; ++t) tb->K[t][u] = kc[t];
+            }
             const float endq = __expf(fminf(le - lu, 0.f)) * Qu;
-            const float vq = tb->v[u] * Qu;
-            // d log alpha_t (lane t = u): suffix of exp(l) RH, prefix of v Q, row t of K over u < t
-            const float erh = tb->E[u] * RH;
-            const float rv = __shfl(erh, (kBQ - 1) - u, 64);
+            const float vq = vu * Qu;
+            // d log alpha_t (lane t = u): suffix of exp(l) RH (a scan of the lanes mirrored
+            // within the row of 16), prefix of v Q, row t of K over u < t
+            const float rv = dpp_read<0x140>(Eu * RH);
             const float sc = group_scan<16>(ul ? rv : 0.f, lane);
-            const float suf = __shfl(sc, (kBQ - 1) - u, 64);
+            const float suf = dpp_read<0x140>(sc);
             const float pre = group_scan<16>(ul ? vq : 0.f, lane) - vq;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             float corner = 0.f;
 #pragma unroll
-            for (int k = 0; k < kBQ - 1; ++k) corner += k < u ? tb->K[u][k] : 0.f;
+            for (int k = 0; k < kBQ; k += 4) {
+                const float4 q = *reinterpret_cast<const float4*>(&tb->K[u][k]);
+                corner += (k < u ? q.x : 0.f) + (k + 1 < u ? q.y : 0.f) + (k + 2 < u ? q.z : 0.f) + (k + 3 < u ? q.w : 0.f);
+            }
             const float dla = suf + __expf(le) * GH + pre + corner;
             const float dnext = tail + endq;                    // d delta of token u + 1
-            const float dprev = __shfl_up(dnext, 1, 64);        // lane u: d delta of token u (u >= 1)
+            const float dprev = dpp_read<0x111>(dnext);         // lane u: d delta of token u (u >= 1)
             if (ul) {
                 tb->dgam[u] = diagP + tail + endq;
                 tb->ddl[u] = u >= 1 ? dprev : 0.f;
@@ -849,20 +902,35 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
             if (lane == kBQ - 1) tb->ddl_next = dnext;
         }
         if (w == 1) {
-            // Phi from the chunk's end back to its start; theta_t . Phi_t per pair into the
-            // B-side table (each lane overwrites only what it has read), then row sums
+            // Phi from the chunk's end back to its start (lane j < np: pair j), eight tokens'
+            // LDS reads issued at a time; theta_t . Phi_t per pair into the B-side table (lanes
+            // past np write 0; the table's rows of tokens t8 .. t8 + 7 are read before they are
+            // overwritten), d theta through a resource that ends at the last token
             const bool pl = lane < np;
             float* const tpt = dphB;
-#pragma unroll 4
-            for (int t = kBQ - 1; t >= 0; --t) {
-                const int tok = c0 + t;
-                float tp = 0.f;
-                if (pl) {
-                    Phi += dphB[t * kMaxPairs + lane] + dphC[t * kMaxPairs + lane];
-                    if (tok < L) a.dtheta[((bo + tok) * H + h) * np + lane] = tb->dt[t] * Phi;
-                    tp = raw->th[t][lane] * Phi;
+            const int dvo = pl ? lane * 4 : kOOB;                // the token's offset goes in soffset
+            const __amdgpu_buffer_rsrc_t rdt = tok_rsrc(a.dtheta, ((bo + c0) * H + h) * np, 4, min(kBQ, L - c0), H * np, np);
+            float* const dpl = dphB + lane;             // [t][pair]: B side; rows kBQ + t: C side
+            const float* const thl = &raw->th[0][lane];
+#pragma unroll
+            for (int t8 = kBQ - 8; t8 >= 0; t8 -= 8) {
+                // the eight tokens' reads first (rows t8 .. t8 + 7 are overwritten only after)
+                float ds[8], thv[8], dtv[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    ds[i] = dpl[(t8 + i) * kMaxPairs] + dpl[(kBQ + t8 + i) * kMaxPairs];
+                    thv[i] = thl[(t8 + i) * kMaxPairs];
+                    dtv[i] = tb->dt[t8 + i];
                 }
-                tpt[t * kMaxPairs + lane] = tp;
+                asm volatile("" : "+v"(thv[0]), "+v"(thv[1]), "+v"(thv[2]), "+v"(thv[3]),
+                                  "+v"(thv[4]), "+v"(thv[5]), "+v"(thv[6]), "+v"(thv[7]));   // loaded on every lane
+#pragma unroll
+                for (int i = 7; i >= 0; --i) {
+                    const int t = t8 + i;
+                    Phi += pl ? ds[i] : 0.f;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dtv[i] * Phi), rdt, dvo, t * H * np * 4, 0);
+                    dpl[t * kMaxPairs] = pl ? thv[i] * Phi : 0.f;
+                }
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -917,6 +985,7 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
             }
         }
         if (c > 0) store_raw(nx, np, tid, raw);
+        if (w == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");     // the next chunk's start phases
         lds_barrier();
     }
 

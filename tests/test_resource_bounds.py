@@ -7,8 +7,8 @@ span whole tokens of all heads); what must hold is that every offset *inside* th
 record count addresses bytes of the tensor.  The replay below restates the kernels'
 base, record-count and offset arithmetic (the matrix-core chunked scan in
 csrc/scan_mfma.hip, the single-rank scan and its score pass in csrc/scan_siso.hip,
-both per-coordinate kernels in csrc/pcs.hip, the raw loads and row prefetch of the
-backward's chunked form in csrc/bwd_chunk.hip) and checks it for
+both per-coordinate kernels in csrc/pcs.hip, the raw loads, row prefetch, start-phase
+loads and theta-gradient stores of the backward's chunked form in csrc/bwd_chunk.hip) and checks it for
 the edge workgroups (first and last batch, head, channel tile and segment, every
 chunk of the segment) of every shape the GPU tests and the benchmark run.  The
 segment schedule is the library's, restated here and cross-checked against the
@@ -450,21 +450,48 @@ def test_the_replay_catches_a_head_offset_record_count():
 BQ, BR = 16, 4
 
 
+def bwd_prefetch_pieces():
+    """The row prefetch's pieces as prefetch_rows deals them: waves 2..7 issue eight
+    16-byte loads per lane, instruction k of wave v covering pieces q0 .. q0 + 63 with
+    q0 = 384 k + 64 v; piece q is kind q // 512 (x, dy, the two halves of B, of C),
+    thread j = q % 512 of that kind (row j / 8, 16-byte group j % 8)."""
+    kinds, js = [], []
+    lane = np.arange(64)
+    for k in range(8):
+        for v in range(6):
+            q0 = 384 * k + 64 * v
+            kind = q0 >> 9
+            assert (q0 + 63) >> 9 == kind       # one kind per instruction
+            kinds.append(np.full(64, kind))
+            js.append((q0 & 511) + lane)
+    kinds, js = np.concatenate(kinds), np.concatenate(js)
+    q = kinds * 512 + js
+    assert np.array_equal(np.sort(q), np.arange(3072))   # every piece of the LDS buffer once
+    return kinds, js
+
+
 def replay_bwd_chunked(b, L, H, G, np_):
-    """The raw per-token loads (theta, dt, lambda, the rate input) and the row prefetch
-    (x, dy, B, C) of every edge stream and chunk, as load_raw and prefetch_rows form
-    them: per-chunk resources whose record counts end at the chunk's last valid token."""
+    """The raw per-token loads (theta, dt, lambda, the rate input), the row prefetch
+    (x, dy, B, C), the chunk's start phases (from the state pass's workspace) and the
+    theta-gradient stores of every edge stream and chunk, as load_raw, prefetch_rows and
+    the angle phase form them: per-chunk resources whose record counts end at the
+    chunk's last valid token."""
     nch = -(-L // BQ)
     tids = np.arange(512)
-    m, q8 = tids >> 3, tids & 7
+    kinds, js = bwd_prefetch_pieces()
+    m, q8 = js >> 3, js & 7
     t, r = m >> 2, m & 3
     X_bytes = b * L * H * BR * KP * 2
     BC_bytes = b * L * G * BR * KN * 2
     T_bytes = b * L * H * 4
     TH_bytes = b * L * H * np_ * 4
+    PH_bytes = b * H * nch * np_ * 4
+    lane = np.arange(64)
+    kOOB = 0x7ffffff0
     for bi in sorted({0, b - 1}):
         for h in sorted({0, H - 1}):
             gg = h * G // H
+            bh = bi * H + h
             for c in sorted({0, nch - 1}):
                 c0 = c * BQ
                 nv, ns = min(BQ, L - c0), min(BQ + 1, L - c0)
@@ -475,15 +502,19 @@ def replay_bwd_chunked(b, L, H, G, np_):
                     te, je = e // np_, e % np_
                     _check("bwd theta", t0 * np_ * 4, ((nv - 1) * H * np_ + np_) * 4, (te * H * np_ + je) * 4, 4,
                            TH_bytes)
+                    # d theta: voffset 4 lane (kOOB past np) plus the token's soffset
+                    vo = np.where(lane < np_, lane * 4, kOOB)
+                    offs = np.concatenate([vo + tt * H * np_ * 4 for tt in range(BQ)])
+                    _check("bwd d theta", t0 * np_ * 4, ((nv - 1) * H * np_ + np_) * 4, offs, 4, TH_bytes)
+                    _check("bwd start phases", (bh * nch + c) * np_ * 4, np_ * 4, lane * 4, 4, PH_bytes)
                 ts = np.arange(BQ + 1)
                 _check("bwd dt, lambda, rate", t0 * 4, ((ns - 1) * H + 1) * 4, ts * H * 4, 4, T_bytes)
                 xbase = ((bi * L + c0) * H + h) * BR * KP * 2
-                _check("bwd x, dy rows", xbase, ((nv - 1) * H + 1) * BR * KP * 2,
-                       (t * H * BR * KP + r * KP + 8 * q8) * 2, 16, X_bytes)
+                xo = (t * H * BR * KP + r * KP + 8 * q8) * 2
+                _check("bwd x, dy rows", xbase, ((nv - 1) * H + 1) * BR * KP * 2, xo[kinds < 2], 16, X_bytes)
                 bbase = ((bi * L + c0) * G + gg) * BR * KN * 2
-                bo = (t * G * BR * KN + r * KN + 16 * q8) * 2
-                _check("bwd B, C rows", bbase, ((nv - 1) * G + 1) * BR * KN * 2, np.concatenate([bo, bo + 16]), 16,
-                       BC_bytes)
+                bo = (t * G * BR * KN + r * KN + 16 * q8) * 2 + np.where(kinds & 1, 16, 0)
+                _check("bwd B, C rows", bbase, ((nv - 1) * G + 1) * BR * KN * 2, bo[kinds >= 2], 16, BC_bytes)
 
 
 def _bwd_ws(m3, b, L, H, G, np_):
