@@ -269,7 +269,33 @@ __device__ __forceinline__ void prefetch_rows(const BwdArgs& a, int bi, int h, i
         lds_dma16(rs, __builtin_amdgcn_readfirstlane(pre_lds + q0 * 16), kind < 2 ? xo : bo_);
     }
 }
-constexpr int kStateLds = sRAW_ + (int)sizeof(Raw);
+// The state pass's next-chunk rows: x (512 16-byte pieces), then B's first and second
+// halves (512 each); piece j of a kind is row j / 8, 16-byte group j % 8 (as above).  All
+// eight waves issue three buffer-to-LDS loads each (instruction k of wave w: pieces
+// 512 k + 64 w ..), during the chunk before the one that reads them.
+constexpr int sPRE_ = sRAW_ + (int)((sizeof(Raw) + 15) / 16 * 16);
+constexpr int sBIAS_ = sPRE_ + 3 * kBT * 16;                         // the head's B bias [4][128] fp32
+constexpr int kStateLds = sBIAS_ + kBR * kN * 4;
+static_assert(2 * kStateLds <= 160 * 1024, "two state-pass workgroups share a compute unit");
+static_assert(kBT == kBR * kN, "one bias element per thread");
+__device__ __forceinline__ void prefetch_xb(const BwdArgs& a, int bi, int h, int gg, int c0, int tid, char* pre) {
+    const int L = a.L, H = a.H, G = a.G;
+    const int nv = min(kBQ, L - c0);
+    const size_t t0 = (size_t)bi * L + c0;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const uint32_t xb = (uint32_t)(((nv - 1) * H + 1) * kBR * kP * 2), bb = (uint32_t)(((nv - 1) * G + 1) * kBR * kN * 2);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const uint16_t*>(a.x) + (t0 * H + h) * kBR * kP, xb);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(static_cast<const uint16_t*>(a.B) + (t0 * G + gg) * kBR * kN, bb);
+    const uint32_t pre_lds = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)pre);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int j = wv * 64 + lane;                      // piece of kind k
+        const int m = j >> 3, q8 = j & 7, t = m >> 2, r = m & 3;
+        const int xo = (t * H * kBR * kP + r * kP + 8 * q8) * 2;
+        const int bo_ = (t * G * kBR * kN + r * kN + 16 * q8) * 2 + (k == 2 ? 16 : 0);
+        lds_dma16(k == 0 ? rx : rb, __builtin_amdgcn_readfirstlane(pre_lds + (k * kBT + wv * 64) * 16), k == 0 ? xo : bo_);
+    }
+}
 
 // The per-token scalars of the chunk into the table (wave 0; lane t: token c0 + t, lane 16
 // the token after the chunk).  Tokens at or past L have dt = 0: no decay, no write.
@@ -427,7 +453,11 @@ __global__ __launch_bounds__(kBT) void bwdc_state_kernel(BwdArgs a, char* hfws, 
     }
     float phi = (w == 1 && lane < np && a.phi0) ? a.phi0[(size_t)bh * np + lane] : 0.f;
     Raw* const raw = reinterpret_cast<Raw*>(smem + sRAW_);
+    char* const pre = smem + sPRE_;
+    float* const sBias = reinterpret_cast<float*>(smem + sBIAS_);
     store_raw(load_raw(a, bi, h, 0, tid), np, tid, raw);
+    sBias[tid] = a.Bb ? a.Bb[(size_t)h * kBR * kN + tid] : 0.f;     // kBT == kBR * kN
+    prefetch_xb(a, bi, h, gg, 0, tid, pre);
     __syncthreads();
 
     for (int c = 0; c < nch; ++c) {
@@ -438,24 +468,21 @@ __global__ __launch_bounds__(kBT) void bwdc_state_kernel(BwdArgs a, char* hfws, 
             phws[((size_t)bh * nch + c) * np + lane] = phi;
             phi = chunk_phases(raw, lane, phi, ph);
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");             // the chunk's rows in LDS
         lds_barrier();
         const bool more = c + 1 < nch;
         RawRegs nx{0.f, 0.f, 0.f, 0.f, 0.f};
         if (more) nx = load_raw(a, bi, h, c0 + kBQ, tid);
         {
-            // X rows and v-scaled turned B rows (row m = tid / 8, piece tid % 8)
-            const int m = tid >> 3, q8 = tid & 7, t = m >> 2, r = m & 3, tok = c0 + t;
-            const bool valid = tok < L;
-            uint4 xv = {0u, 0u, 0u, 0u};
-            if (valid)
-                xv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) +
-                                                     (((size_t)bi * L + tok) * H + h) * kBR * kP + r * kP + 8 * q8);
+            // X rows and v-scaled turned B rows (row m = tid / 8, piece tid % 8); rows past L
+            // read zero and their scale v is zero
+            const int m = tid >> 3, q8 = tid & 7, t = m >> 2, r = m & 3;
+            const uint4 xv = *reinterpret_cast<const uint4*>(pre + 0 * kBT * 16 + tid * 16);
+            const uint4 b0 = *reinterpret_cast<const uint4*>(pre + 1 * kBT * 16 + tid * 16);
+            const uint4 b1 = *reinterpret_cast<const uint4*>(pre + 2 * kBT * 16 + tid * 16);
             *reinterpret_cast<uint4*>(sX + swz(kP * 2, m, 8 * q8)) = xv;
-            const uint16_t* raw = valid ? static_cast<const uint16_t*>(a.B) + (((size_t)bi * L + tok) * G + gg) * kBR * kN + r * kN
-                                        : nullptr;
-            const float* bias = a.Bb ? a.Bb + ((size_t)h * kBR + r) * kN : nullptr;
             uint32_t o[8];
-            turn_piece(raw, bias, ph + t * kMaxPairs, np, 16 * q8, tb->v[t], o);
+            turn_loaded(b0, b1, sBias + r * kN, ph + t * kMaxPairs, np, 16 * q8, tb->v[t], o);
             *reinterpret_cast<uint4*>(sV + swz(kN * 2, m, 16 * q8)) = uint4{o[0], o[1], o[2], o[3]};
             *reinterpret_cast<uint4*>(sV + swz(kN * 2, m, 16 * q8 + 8)) = uint4{o[4], o[5], o[6], o[7]};
         }
@@ -469,6 +496,7 @@ __global__ __launch_bounds__(kBT) void bwdc_state_kernel(BwdArgs a, char* hfws, 
         }
         lds_barrier();
         if (more) store_raw(nx, np, tid, raw);
+        if (more) prefetch_xb(a, bi, h, gg, c0 + kBQ, tid, pre);     // the staging reads are done
         // Hf = exp(l_e) Hf + X^T (v Bt): rows p (A = X^T by transposing reads), columns n
         const float fe = __expf(tb->le);
 #pragma unroll

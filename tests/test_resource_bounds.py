@@ -470,11 +470,26 @@ def bwd_prefetch_pieces():
     return kinds, js
 
 
+def bwd_state_prefetch_pieces():
+    """The state pass's row prefetch (prefetch_xb): all eight waves issue three 16-byte
+    loads per lane, instruction k of wave v covering pieces 512 k + 64 v .. + 63 of kind k
+    (x, the first and the second half of B), thread j = 64 v + lane of that kind."""
+    kinds, js = [], []
+    lane = np.arange(64)
+    for k in range(3):
+        for v in range(8):
+            kinds.append(np.full(64, k))
+            js.append(64 * v + lane)
+    kinds, js = np.concatenate(kinds), np.concatenate(js)
+    assert np.array_equal(np.sort(kinds * 512 + js), np.arange(1536))   # every piece once
+    return kinds, js
+
+
 def replay_bwd_chunked(b, L, H, G, np_):
     """The raw per-token loads (theta, dt, lambda, the rate input), the row prefetch
     (x, dy, B, C), the chunk's start phases (from the state pass's workspace) and the
-    theta-gradient stores of every edge stream and chunk, as load_raw, prefetch_rows and
-    the angle phase form them: per-chunk resources whose record counts end at the
+    theta-gradient stores of every edge stream and chunk, and the state pass's x and B row
+    prefetch, as load_raw, prefetch_rows, prefetch_xb and the angle phase form them: per-chunk resources whose record counts end at the
     chunk's last valid token."""
     nch = -(-L // BQ)
     tids = np.arange(512)
@@ -515,6 +530,14 @@ def replay_bwd_chunked(b, L, H, G, np_):
                 bbase = ((bi * L + c0) * G + gg) * BR * KN * 2
                 bo = (t * G * BR * KN + r * KN + 16 * q8) * 2 + np.where(kinds & 1, 16, 0)
                 _check("bwd B, C rows", bbase, ((nv - 1) * G + 1) * BR * KN * 2, bo[kinds >= 2], 16, BC_bytes)
+                # the state pass: x and B rows
+                sk, sj = bwd_state_prefetch_pieces()
+                sm, sq8 = sj >> 3, sj & 7
+                st_, sr = sm >> 2, sm & 3
+                sxo = (st_ * H * BR * KP + sr * KP + 8 * sq8) * 2
+                _check("bwd state x rows", xbase, ((nv - 1) * H + 1) * BR * KP * 2, sxo[sk == 0], 16, X_bytes)
+                sbo = (st_ * G * BR * KN + sr * KN + 16 * sq8) * 2 + np.where(sk == 2, 16, 0)
+                _check("bwd state B rows", bbase, ((nv - 1) * G + 1) * BR * KN * 2, sbo[sk >= 1], 16, BC_bytes)
 
 
 def _bwd_ws(m3, b, L, H, G, np_):
