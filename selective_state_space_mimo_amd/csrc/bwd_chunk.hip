@@ -48,7 +48,8 @@
 //   * bwdc_main_kernel walks them backward with Gf (fp32) in matrix-core accumulators:
 //     per chunk, the score tiles S^T and S2^T, the weighted tiles (bf16 in LDS), the
 //     products above, then the per-token scalar gradients (waves 0 and 1; meanwhile
-//     waves 2..7 load the next chunk's x, dy, B, C rows and start phases into LDS).
+//     waves 2..7 load the next chunk's x, dy, B, C rows and start phases into LDS); the
+//     chunk's phase table is built by waves 1..4, four tokens each.
 // Shared B and C gradients are summed over a group's heads by fp32 atomic adds into the
 // workspace (as the token-serial backward does), converted to bf16 afterwards.
 #include "scan_common.h"
@@ -350,6 +351,25 @@ __device__ float chunk_phases(const Raw* raw, int j, float phi, float2* cst) {
     return phi;
 }
 
+// Tokens T0 .. T0 + 3 of chunk_phases, for one of four waves sharing the table: the same
+// running sum up to token T0 + 3 (so the same values), the cos and sin of its last four.
+template <int T0>
+__device__ void chunk_phases4(const Raw* raw, int j, float phi, float2* cst) {
+    constexpr int TE = T0 + 4;
+    float dtv[TE], thv[TE];
+#pragma unroll
+    for (int t = 0; t < TE; ++t) { dtv[t] = raw->dt[t]; thv[t] = raw->th[t][j]; }
+#pragma unroll
+    for (int t = 0; t < TE; ++t) {
+        phi = fmaf(dtv[t], thv[t], phi);
+        if (t >= T0) {
+            float sn, cs;
+            __sincosf(wrap_2pi(phi), &sn, &cs);
+            cst[t * kMaxPairs + j] = float2{cs, sn};
+        }
+    }
+}
+
 // 16 turned values of a row at columns n0 .. n0 + 15 from loaded data: raw (two 16-byte
 // pieces) + bias (16 floats), pairs (2 j, 2 j + 1) with j < np turned by the token's table
 // entries, times scale; bf16 pairs out.
@@ -610,7 +630,13 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
         const int c0 = c * kBQ;
         // ---- S0a: scalars, phases ----
         if (w == 0) chunk_scalars(a, raw, rateA, lane, tb);
-        if (w == 1 && lane < np) chunk_phases(raw, lane, raw->phs[lane], ph);
+        if (w >= 1 && w <= 4 && lane < np) {                       // four tokens a wave
+            const float phi0 = raw->phs[lane];
+            if (w == 1) chunk_phases4<0>(raw, lane, phi0, ph);
+            else if (w == 2) chunk_phases4<4>(raw, lane, phi0, ph);
+            else if (w == 3) chunk_phases4<8>(raw, lane, phi0, ph);
+            else chunk_phases4<12>(raw, lane, phi0, ph);
+        }
         if (w >= 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the rows' loads into LDS
         lds_barrier();
         // ---- S0b: staging (the rows were prefetched into LDS) ----
