@@ -639,6 +639,19 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
         }
         if (w >= 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the rows' loads into LDS
         lds_barrier();
+        // Hf_in pieces (loaded first: they are used two phases later): B operands of dy Hf_in (column n = 16 w + s, k = p) and the lane's
+        // own elements of the state tiles (for <Gf_out, Hf_in>)
+        const char* const hin = hfws + ((size_t)bh * nch + c) * kHfChunkBytes;
+        bf16x8 hop[2];
+        uint2 hown[4];
+        {
+            const int n = 16 * w + s;
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp)
+                hop[kp] = *reinterpret_cast<const bf16x8*>(hin + (n * kP + 32 * kp + 8 * g4) * 2);
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) hown[pt] = *reinterpret_cast<const uint2*>(hin + (n * kP + 16 * pt + 4 * g4) * 2);
+        }
         // ---- S0b: staging (the rows were prefetched into LDS) ----
         {
             const int m = tid >> 3, q8 = tid & 7, t = m >> 2, r = m & 3;
@@ -665,25 +678,9 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
             for (int pt = 0; pt < 4; ++pt)
                 *reinterpret_cast<uint2*>(sG + swz(kP * 2, n, 16 * pt + 4 * g4)) = pack4(gf[pt]);
         }
-        // Hf_in pieces: B operands of dy Hf_in (column n = 16 w + s, k = p) and the lane's
-        // own elements of the state tiles (for <Gf_out, Hf_in>)
-        const char* const hin = hfws + ((size_t)bh * nch + c) * kHfChunkBytes;
-        bf16x8 hop[2];
-        uint2 hown[4];
-        {
-            const int n = 16 * w + s;
-#pragma unroll
-            for (int kp = 0; kp < 2; ++kp)
-                hop[kp] = *reinterpret_cast<const bf16x8*>(hin + (n * kP + 32 * kp + 8 * g4) * 2);
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt) hown[pt] = *reinterpret_cast<const uint2*>(hin + (n * kP + 16 * pt + 4 * g4) * 2);
-        }
         lds_barrier();
         // the next chunk's raw inputs, staged in LDS once this chunk's are used (S3b)
         RawRegs nx{0.f, 0.f, 0.f, 0.f, 0.f};
-        if (c > 0) {
-            nx = load_raw(a, bi, h, c0 - kBQ, tid);
-        }
         // ---- S1: score tiles S^T, S2^T (rows u', columns m), weights, P(t, u) ----
         {
             const int mt = w & 3;
@@ -889,6 +886,7 @@ __global__ __launch_bounds__(kBT) void bwdc_main_kernel(BwdArgs a, const char* h
         lds_barrier();
         // ---- S3a: coefficient sensitivities (wave 0), the angle's (wave 1) ----
         // (this chunk's rows were staged in S0b, so the prefetch buffer is free)
+        if (c > 0) nx = load_raw(a, bi, h, c0 - kBQ, tid);
         if (w >= 2 && c > 0) prefetch_rows(a, bi, h, gg, c0 - kBQ, tid, pre, phws + ((size_t)bh * nch + c - 1) * np, raw);
         if (w == 0) {
             // every LDS read of the phase is issued before the arithmetic that needs it
