@@ -69,7 +69,7 @@ __global__ __launch_bounds__(64 * kWaves) void prologue_kernel(BlockArgs a) {
         a.dt[ti] = softplus(a.dt_raw[ti] + (a.dt_bias ? a.dt_bias[h] : 0.f));
         a.lam[ti] = sigmoid(a.lam_raw[ti]);
     }
-    for (int i = lane; i < a.np; i += 64) a.th[(size_t)ti * a.np + i] = kPi * tanhf(a.th_raw[(size_t)ti * a.np + i]);
+    for (int i = lane; i < a.np; i += 64) a.th[(size_t)ti * a.np + i] = kPi * tanh_f(a.th_raw[(size_t)ti * a.np + i]);
     for (int p = lane; p < a.P && a.xl; p += 64) {
         const float xv = ld_io(a.x, (size_t)ti * a.P + p, a.io_bf16);
         for (int r = 0; r < a.R; ++r)
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(64 * kWaves) void prologue_vec_kernel(BlockArgs a) 
             a.dt[ti] = softplus(a.dt_raw[ti] + (a.dt_bias ? a.dt_bias[h] : 0.f));
             a.lam[ti] = sigmoid(a.lam_raw[ti]);
         }
-        for (int i = j; i < a.np; i += G) a.th[(size_t)ti * a.np + i] = kPi * tanhf(a.th_raw[(size_t)ti * a.np + i]);
+        for (int i = j; i < a.np; i += G) a.th[(size_t)ti * a.np + i] = kPi * tanh_f(a.th_raw[(size_t)ti * a.np + i]);
     }
     if (!a.xl) return;                                   // the scan lifts x itself
     float xv[V];

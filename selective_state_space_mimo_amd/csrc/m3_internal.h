@@ -175,6 +175,16 @@ __device__ __forceinline__ float heavy_tail_rate(float u) {
 // The layer's activations of its raw step, blend and angle projections.
 __device__ __forceinline__ float softplus_f(float v) { return fmaxf(v, 0.f) + log1pf(expf(-fabsf(v))); }
 __device__ __forceinline__ float sigmoid_f(float v) { return 1.f / (1.f + expf(-v)); }
+// tanh from the hardware base-2 exponential and reciprocal: tanh x = 1 - 2 / (e^{2x} + 1)
+// (exactly +-1 at the ends, where e^{2x} is 0 or infinite); below |x| = 1/16, where that
+// form cancels, the odd Taylor series x - x^3/3 + 2 x^5/15 (truncation below 3e-10).
+__device__ __forceinline__ float tanh_f(float x) {
+    const float e = __builtin_amdgcn_exp2f(x * 2.8853900817779268f);        // e^{2x} = 2^{2x log2 e}
+    const float big = 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
+    const float x2 = x * x;
+    const float small = x * fmaf(x2, fmaf(x2, 2.f / 15.f, -1.f / 3.f), 1.f);
+    return fabsf(x) < 0.0625f ? small : big;
+}
 constexpr float kPiF = 3.14159265358979f;
 // Reduce an angle into [0, 2 pi).
 __device__ __forceinline__ float wrap_2pi(float v) {

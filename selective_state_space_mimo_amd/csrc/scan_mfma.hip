@@ -263,7 +263,7 @@ __global__ __launch_bounds__((n_threads<R, Q>()), (waves_per_simd<R, Q>())) void
             if (t < Q) {
 #pragma unroll
                 for (int u = 0; u < THU; ++u)
-                    stage[(th_i + u) * (Q + 1) + t] = LAYER ? kPiF * tanhf(th[pp][u]) : th[pp][u];
+                    stage[(th_i + u) * (Q + 1) + t] = LAYER ? kPiF * tanh_f(th[pp][u]) : th[pp][u];
             }
         }
     };
